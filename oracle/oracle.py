@@ -1,0 +1,297 @@
+"""ctypes wrapper of the C oracle (fp4_oracle.c).
+
+Test infrastructure only.  Every function takes numpy arrays (or torch CPU
+tensors, converted exactly to binary32) and returns numpy arrays.  Nothing here
+touches a GPU or the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4_oracle.c")
+_LIB_DIR = os.path.join(_HERE, "_lib")
+_LIB = os.path.join(_LIB_DIR, "liboracle.so")
+
+__all__ = [
+    "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
+    "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
+    "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
+    "score_factor",
+]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no contraction of multiply-adds)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    os.makedirs(_LIB_DIR, exist_ok=True)
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wno-unused-function", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+_vp = C.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = build()
+    L = C.CDLL(path)
+    L.orc_e2m1_value.argtypes = [C.c_int]; L.orc_e2m1_value.restype = C.c_double
+    L.orc_e4m3_value.argtypes = [C.c_int]; L.orc_e4m3_value.restype = C.c_double
+    L.orc_e4m3_encode.argtypes = [C.c_double]; L.orc_e4m3_encode.restype = C.c_int
+    L.orc_e2m1_encode.argtypes = [C.c_double]; L.orc_e2m1_encode.restype = C.c_int
+    L.orc_recip.argtypes = [C.c_int]; L.orc_recip.restype = C.c_float
+    L.orc_round_fp16.argtypes = [C.c_double]; L.orc_round_fp16.restype = C.c_double
+    L.orc_score_factor.argtypes = [C.c_double, C.c_int]; L.orc_score_factor.restype = C.c_float
+    L.orc_quantize_block.argtypes = [_f32p, C.c_int, C.c_int, C.c_int, C.c_int, _u8p,
+                                     _u8p, _i8p, _vp]
+    L.orc_quantize_block.restype = C.c_int
+    L.orc_quantize.argtypes = [_f32p, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_int, C.c_int,
+                               C.c_int, C.POINTER(C.c_float), _u8p, _u8p, _vp]
+    L.orc_quantize.restype = C.c_int64
+    L.orc_dequantize.argtypes = [_u8p, _u8p, C.c_int64, C.c_int64, C.c_int, C.c_float, _f64p]
+    L.orc_dequantize.restype = None
+    L.orc_block_means.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, _f64p]
+    L.orc_block_means.restype = None
+    L.orc_topk_count.argtypes = [C.c_int, C.c_int]; L.orc_topk_count.restype = C.c_int
+    L.orc_block_topk.argtypes = [_f64p, _f64p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                 C.c_int, _i32p, _i32p]
+    L.orc_block_topk.restype = None
+    L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
+                                    C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
+                                    C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
+                                    C.c_int, _f32p, _vp, _vp, _vp]
+    L.orc_attention_fwd.restype = C.c_int
+    L.orc_attention_exact.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
+                                      C.c_int64, C.c_int, C.c_int, C.c_double, _vp, C.c_int64,
+                                      _vp, C.c_int, _f32p, _vp]
+    L.orc_attention_exact.restype = C.c_int
+    L.orc_attention_decode.argtypes = [_f32p, _f32p, _f32p, _i32p, C.c_int, C.c_int, C.c_int,
+                                       C.c_int, C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int,
+                                       C.c_int, C.c_int, _vp, C.c_int, _f32p, _vp]
+    L.orc_attention_decode.restype = C.c_int
+    L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
+    _lib = L
+    return L
+
+
+def _f32(x) -> np.ndarray:
+    """Exact binary32 copy of a numpy array or torch CPU tensor (bf16/fp16/fp32)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().orc_e4m3_value(int(byte))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def e2m1_encode(t: float) -> int:
+    return lib().orc_e2m1_encode(float(t))
+
+
+def recip(byte: int) -> float:
+    return lib().orc_recip(int(byte))
+
+
+def round_fp16(x: float) -> float:
+    return lib().orc_round_fp16(float(x))
+
+
+def score_factor(softmax_scale: float, d: int) -> float:
+    return lib().orc_score_factor(float(softmax_scale), int(d))
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def quantize_block(y, scale_search=True, fmin=-2, fmax=6, return_sse=False):
+    """Quantize 16 values; returns (codes[16] unpacked, scale byte, offset[, sse per f])."""
+    y = _f32(y).reshape(16)
+    codes = np.zeros(16, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    of = np.zeros(1, np.int8)
+    sse = np.zeros(fmax - fmin + 1, np.float32)
+    lib().orc_quantize_block(y, 1, int(scale_search), fmin, fmax, codes, sc, of, _ptr(sse))
+    out = (codes, int(sc[0]), int(of[0]))
+    return out + (sse,) if return_sse else out
+
+
+def quantize(x, block_axis=0, scale_search=True, fmin=-2, fmax=6, global_mode=0, g=1.0):
+    """Quantize a 2-D tensor. Returns dict(codes, scales, offsets, g, nonfinite_blocks)."""
+    x = _f32(x)
+    assert x.ndim == 2
+    rows, cols = x.shape
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    scales = np.zeros(rows * cols // 16, np.uint8)
+    offs = np.zeros(rows * cols // 16, np.int8)
+    gg = C.c_float(g)
+    nb = lib().orc_quantize(x, rows, cols, block_axis, int(scale_search), fmin, fmax, global_mode,
+                            C.byref(gg), codes, scales, _ptr(offs))
+    if nb < 0:
+        raise ValueError("bad quantize arguments")
+    if block_axis == 0:
+        codes = codes.reshape(rows, cols // 2)
+        scales = scales.reshape(rows, cols // 16)
+        offs = offs.reshape(rows, cols // 16)
+    else:
+        codes = codes.reshape(rows // 2, cols)
+        scales = scales.reshape(rows // 16, cols)
+        offs = offs.reshape(rows // 16, cols)
+    return dict(codes=codes, scales=scales, offsets=offs, g=gg.value, nonfinite_blocks=int(nb))
+
+
+def dequantize(codes, scales, rows, cols, block_axis=0, g=1.0):
+    out = np.zeros(rows * cols, np.float64)
+    lib().orc_dequantize(np.ascontiguousarray(codes, np.uint8).reshape(-1),
+                         np.ascontiguousarray(scales, np.uint8).reshape(-1), rows, cols,
+                         block_axis, g, out)
+    return out.reshape(rows, cols)
+
+
+def block_means(x, blk=128):
+    x = _f32(x)
+    S, d = x.shape
+    nb = (S + blk - 1) // blk
+    out = np.zeros(nb * d, np.float64)
+    lib().orc_block_means(x, S, d, blk, out)
+    return out.reshape(nb, d)
+
+
+def topk_count(pct: int, n: int) -> int:
+    return lib().orc_topk_count(int(pct), int(n))
+
+
+def block_topk(qm, km, causal, pct):
+    qm = np.ascontiguousarray(qm, np.float64)
+    km = np.ascontiguousarray(km, np.float64)
+    nqb, d = qm.shape
+    nkb = km.shape[0]
+    kmax = topk_count(pct, nkb)
+    idx = np.zeros(max(nqb * kmax, 1), np.int32)
+    cnt = np.zeros(nqb, np.int32)
+    lib().orc_block_topk(qm.reshape(-1), km.reshape(-1), nqb, nkb, d, int(causal), int(pct), kmax,
+                         idx, cnt)
+    return idx[: nqb * kmax].reshape(nqb, kmax), cnt
+
+
+def _sel(arr, dtype):
+    if arr is None:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(arr, dtype=dtype).reshape(-1))
+    return a, a.size
+
+
+def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
+                  fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
+                  with_topk=False):
+    """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
+
+    Returns (out [nh, nr, d], lse [nh, nr]) and, with with_topk, also
+    (topk_idx [nh, nqb, kmax], topk_cnt [nh, nqb])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    ra, nr = _sel(rows, np.int64)
+    ha, nh = _sel(heads, np.int32)
+    nr = nr if ra is not None else Sq
+    nh = nh if ha is not None else B * H
+    out = np.zeros(nh * nr * d, np.float32)
+    lse = np.zeros(nh * nr, np.float32)
+    nqb = (Sq + sel_block - 1) // sel_block
+    nkb = (Sk + sel_block - 1) // sel_block
+    kmax = topk_count(pct, nkb) if pct > 0 else 0
+    tidx = np.zeros(max(nh * nqb * kmax, 1), np.int32) if with_topk and pct > 0 else None
+    tcnt = np.zeros(max(nh * nqb, 1), np.int32) if with_topk and pct > 0 else None
+    rc = lib().orc_attention_fwd(q.reshape(-1), k.reshape(-1), v.reshape(-1), B, H, Hkv, Sq, Sk, d,
+                                 int(causal), float(softmax_scale), kv_tile, int(scale_search),
+                                 fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
+                                 _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
+                                 _ptr(tcnt))
+    if rc != 0:
+        raise ValueError("bad attention arguments")
+    res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))
+    if with_topk:
+        if pct > 0:
+            res += (tidx[: nh * nqb * kmax].reshape(nh, nqb, kmax), tcnt[: nh * nqb].reshape(nh, nqb))
+        else:
+            res += (None, None)
+    return res
+
+
+def attention_exact(q, k, v, causal=False, softmax_scale=0.0, rows=None, heads=None):
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    ra, nr = _sel(rows, np.int64)
+    ha, nh = _sel(heads, np.int32)
+    nr = nr if ra is not None else Sq
+    nh = nh if ha is not None else B * H
+    out = np.zeros(nh * nr * d, np.float32)
+    lse = np.zeros(nh * nr, np.float32)
+    rc = lib().orc_attention_exact(q.reshape(-1), k.reshape(-1), v.reshape(-1), B, H, Hkv, Sq, Sk, d,
+                                   int(causal), float(softmax_scale), _ptr(ra),
+                                   nr if ra is not None else 0, _ptr(ha), nh if ha is not None else 0,
+                                   out, _ptr(lse))
+    if rc != 0:
+        raise ValueError("bad attention arguments")
+    return out.reshape(nh, nr, d), lse.reshape(nh, nr)
+
+
+def attention_decode(q, k, v, ctx_len, n_sink, n_recent, softmax_scale=0.0, scale_search=True,
+                     fmin=-2, fmax=6, pairs=None):
+    """Decode oracle. q [B,Hq,d]; k/v [B,Hkv,Lcap,d] original context; ctx_len [B].
+
+    Returns (out [np, G, d], lse [np, G]) for the selected (b*Hkv+kvh) pairs."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, Hq, d = q.shape
+    Hkv, Lcap = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    cl = np.ascontiguousarray(np.asarray(ctx_len, np.int32).reshape(-1))
+    pa, npairs = _sel(pairs, np.int32)
+    npairs = npairs if pa is not None else B * Hkv
+    out = np.zeros(npairs * G * d, np.float32)
+    lse = np.zeros(npairs * G, np.float32)
+    rc = lib().orc_attention_decode(q.reshape(-1), k.reshape(-1), v.reshape(-1), cl, B, Hq, Hkv, d,
+                                    Lcap, n_sink, n_recent, float(softmax_scale), int(scale_search),
+                                    fmin, fmax, _ptr(pa), npairs if pa is not None else 0, out,
+                                    _ptr(lse))
+    if rc != 0:
+        raise ValueError("bad decode arguments")
+    return out.reshape(npairs, G, d), lse.reshape(npairs, G)

@@ -1,0 +1,159 @@
+"""Pins of the oracle's fake-quant FP4 attention forward.
+
+ScaleSearch page, Metodologia / ScaleSearchAttention (QK^T and PV on NVFP4
+operands with FP32 accumulation); ThriftAttention page, Metodologia / 2 (FP16
+path for selected block pairs, FP4 path with two-level P for the rest, both
+fused by an online softmax in the manner of FlashAttention-2).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(dtype)
+
+
+def _deq(x, axis, ss=True):
+    r = oracle.quantize(x, axis, ss)
+    return oracle.dequantize(r["codes"], r["scales"], x.shape[0], x.shape[1], axis)
+
+
+def test_two_level_p_worked_example():
+    rows = []
+    with open(os.path.join(GOLD, "two_level_p_worked.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append(line.split())
+    n = len(rows)
+    assert n == 32
+    d = 32
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, n, d), np.float32)
+    v = np.zeros((1, 1, n, d), np.float32)
+    for j, r in enumerate(rows):
+        k[0, 0, j, 0] = float(r[1])
+        v[0, 0, j, j] = 1.0
+    # preconditions: the inputs are exact in NVFP4 under ScaleSearch
+    assert np.array_equal(_deq(k[0, 0], 0), k[0, 0])
+    assert np.array_equal(_deq(v[0, 0], 1), v[0, 0])
+    assert np.array_equal(_deq(q[0, 0], 0), q[0, 0])
+    out, lse = oracle.attention_fwd(q, k, v, causal=False, softmax_scale=math.log(2.0), kv_tile=32)
+    e = np.array([np.float32(2.0) ** np.float32(float(r[1])) for r in rows], np.float64)
+    e[6] = float(np.float32(2.0 ** -0.5))
+    l = e.sum()
+    phat = np.array([float(r[5]) for r in rows])
+    expect = phat / 2688.0 / l
+    np.testing.assert_allclose(out[0, 0], expect, rtol=1e-6, atol=1e-9)
+    assert abs(lse[0, 0] - math.log(l)) < 1e-6
+
+
+def test_zero_keys_closed_form_mean_of_dequantized_v():
+    # K = 0: all scores 0, e = 1 on every visible key, P' = 2688 -> s2 = 448, code 6:
+    # every probability is exactly 1/n, so O is the mean of the dequantized V rows.
+    q = _rand((1, 1, 200, 64), 0)
+    k = torch.zeros(1, 1, 208, 64, dtype=torch.bfloat16)
+    v = _rand((1, 1, 208, 64), 1)
+    vh = _deq(v[0, 0].float().numpy(), 1)
+    out, lse = oracle.attention_fwd(q, k[:, :, :200 + 8], v, causal=False, kv_tile=64)
+    np.testing.assert_allclose(out[0], np.broadcast_to(vh.mean(0), (200, 64)), rtol=0, atol=2e-6)
+    np.testing.assert_allclose(lse[0], math.log(208), atol=1e-5)
+    # causal: row i sees i+1 keys
+    q2 = _rand((1, 1, 208, 64), 2)
+    out, _ = oracle.attention_fwd(q2, k, v, causal=True, kv_tile=64)
+    cm = np.cumsum(vh, 0) / np.arange(1, 209)[:, None]
+    np.testing.assert_allclose(out[0], cm, atol=2e-6)
+
+
+def test_causal_first_row_is_first_value_row():
+    q, k, v = _rand((1, 2, 128, 64), 3), _rand((1, 2, 128, 64), 4), _rand((1, 2, 128, 64), 5)
+    out, _ = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64, rows=[0])
+    for h in range(2):
+        vh = _deq(v[0, h].float().numpy(), 1)
+        np.testing.assert_allclose(out[h, 0], vh[0], atol=1e-7)
+
+
+def test_full_budget_equals_fp16_textbook_attention():
+    # every pair promoted: the FP16 path alone, i.e. softmax attention on fp16
+    # operands with fp16 probabilities
+    B, H, S, d = 1, 2, 256, 64
+    q, k, v = _rand((B, H, S, d), 6), _rand((B, H, S, d), 7), _rand((B, H, S, d), 8)
+    for causal in (False, True):
+        out, lse = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=128, pct=100, sel_block=128)
+        ex, exl = oracle.attention_exact(q, k, v, causal=causal)
+        qf = q.to(torch.float16).double().numpy()
+        kf = k.to(torch.float16).double().numpy()
+        vf = v.to(torch.float16).double().numpy()
+        s = np.einsum("bhid,bhjd->bhij", qf, kf) / math.sqrt(d)
+        if causal:
+            s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        ref = (p / p.sum(-1, keepdims=True)) @ vf
+        np.testing.assert_allclose(out.reshape(B, H, S, d), ref, atol=1e-3)
+        assert np.abs(out - ex).max() < 2e-3
+        np.testing.assert_allclose(lse, exl, atol=1e-5)
+
+
+def test_fp4_path_error_is_quantization_sized():
+    B, H, S, d = 1, 2, 256, 64
+    q, k, v = _rand((B, H, S, d), 9), _rand((B, H, S, d), 10), _rand((B, H, S, d), 11)
+    out, _ = oracle.attention_fwd(q, k, v, causal=False, kv_tile=64)
+    ex, _ = oracle.attention_exact(q, k, v, causal=False)
+    rel = np.linalg.norm(out - ex) / np.linalg.norm(ex)
+    assert 0.02 < rel < 0.35
+    # a partial budget lands between the FP4 path and the FP16 path
+    out50, _ = oracle.attention_fwd(q, k, v, causal=False, kv_tile=64, pct=50, sel_block=128)
+    rel50 = np.linalg.norm(out50 - ex) / np.linalg.norm(ex)
+    assert rel50 < rel
+
+
+def test_lse_consistency_with_quantized_scores():
+    B, H, S, d = 1, 1, 192, 64
+    q, k, v = _rand((B, H, S, d), 12), _rand((B, H, S, d), 13), _rand((B, H, S, d), 14)
+    out, lse = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64)
+    qh = _deq(q[0, 0].float().numpy(), 0)
+    kh = _deq(k[0, 0].float().numpy(), 0)
+    s = qh @ kh.T / math.sqrt(d)
+    for i in range(S):
+        tot = np.exp(s[i, : i + 1] - lse[0, i]).sum()
+        assert abs(tot - 1.0) < 1e-5
+
+
+def test_power_of_two_value_scaling_is_exact():
+    q, k, v = _rand((1, 1, 128, 64), 15), _rand((1, 1, 128, 64), 16), _rand((1, 1, 128, 64), 17)
+    o1, _ = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64)
+    o2, _ = oracle.attention_fwd(q, k, v * 4, causal=True, kv_tile=64)
+    np.testing.assert_allclose(o2, 4 * o1, rtol=1e-6, atol=1e-7)
+
+
+def test_key_permutation_inside_16_blocks_is_invariant():
+    # quantization blocks of K run along d (per key) and of V along 16 tokens;
+    # P's level-2 blocks are 16 keys: permuting keys inside a 16-key block changes nothing
+    q, k, v = _rand((1, 1, 96, 64), 18), _rand((1, 1, 128, 64), 19), _rand((1, 1, 128, 64), 20)
+    perm = np.arange(128)
+    rng = np.random.default_rng(0)
+    for b in range(8):
+        perm[16 * b:16 * b + 16] = 16 * b + rng.permutation(16)
+    o1, l1 = oracle.attention_fwd(q, k, v, causal=False, kv_tile=64)
+    o2, l2 = oracle.attention_fwd(q, k[:, :, perm], v[:, :, perm], causal=False, kv_tile=64)
+    np.testing.assert_allclose(o1, o2, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(l1, l2, atol=1e-6)
+
+
+def test_row_and_head_selection_consistent():
+    q, k, v = _rand((2, 2, 80, 32), 21), _rand((2, 1, 80, 32), 22), _rand((2, 1, 80, 32), 23)
+    full, lf = oracle.attention_fwd(q, k, v, causal=True, kv_tile=32)
+    part, lp = oracle.attention_fwd(q, k, v, causal=True, kv_tile=32, rows=[79, 3, 40], heads=[3, 0])
+    np.testing.assert_array_equal(part[0], full[3][[79, 3, 40]])
+    np.testing.assert_array_equal(part[1], full[0][[79, 3, 40]])
+    np.testing.assert_array_equal(lp[1], lf[0][[79, 3, 40]])
