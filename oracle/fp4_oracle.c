@@ -68,6 +68,7 @@ double orc_e4m3_value(int byte) {
    an even mantissa (even byte value) wins.  Values above 448 go to 448
    (saturation: 448 is nearest), never to NaN. */
 int orc_e4m3_encode(double v) {
+  if (v >= 448.0) return 0x7E; /* saturation (also keeps huge v out of the distance test) */
   int best = 0;
   double bd = fabs(v);
   for (int b = 1; b <= 0x7E; ++b) {
@@ -80,6 +81,7 @@ int orc_e4m3_encode(double v) {
 /* Nearest E2M1 magnitude code (0..7) to t >= 0; ties go to the even code
    (0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4); t > 6 gives 6. */
 int orc_e2m1_encode(double t) {
+  if (t >= 6.0) return 7; /* saturation: for huge t the binary64 distances would tie */
   int best = 0;
   double bd = fabs(t);
   for (int c = 1; c < 8; ++c) {

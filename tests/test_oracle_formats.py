@@ -71,6 +71,8 @@ def test_e2m1_encode_ties_and_dense_grid():
     for t, c in ties.items():
         assert oracle.e2m1_encode(t) == c, t
     assert oracle.e2m1_encode(6.0) == 7 and oracle.e2m1_encode(100.0) == 7
+    # saturation holds however large t is (binary64 distances to 4 and 6 coincide at 1e30)
+    assert oracle.e2m1_encode(1e30) == 7 and oracle.e2m1_encode(3.0e38) == 7
     rng = np.random.default_rng(0)
     ts = np.concatenate([rng.uniform(0, 7, 3000), np.arange(0, 7, 1 / 64)]).astype(np.float32)
     for t in ts:

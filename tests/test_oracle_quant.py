@@ -140,6 +140,12 @@ def test_exact_max_scaling_closed_form():
         assert sc == b and codes[5] == 0xF and codes[2] == 1
 
 
+def test_huge_values_saturate_to_six():
+    codes, sc, off = oracle.quantize_block(np.full(16, 1e30, np.float32), True)
+    assert sc == 0x7C and off == -2  # every candidate's error overflows to inf: lowest f
+    assert all(c == 7 for c in codes)
+
+
 def test_zero_and_nonfinite_blocks():
     y = np.zeros(16, np.float32)
     y[3] = -0.0
