@@ -1,0 +1,294 @@
+"""Block-scaled FP4 (NVFP4-style) attention for AMD MI355X -- Python binding.
+
+Thin ctypes layer over the C ABI in include/fp4.h (libfp4.so, hand-written HIP
+kernels for gfx950).  Functions carry the C names and only marshal arguments:
+torch tensors provide device memory, torch's current stream is the launch
+stream, and every step runs in the library's kernels.  There is no CPU
+fallback: without the native library (or a GPU) the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "load", "build", "fp4_version", "fp4_last_error", "fp4_quantize", "fp4_block_topk",
+    "fp4_attention_fwd", "fp4_attention_decode", "FP4Error", "BF16", "FP16", "FP32",
+    "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libfp4.so")
+
+BF16, FP16, FP32 = 0, 1, 2
+GLOBAL_NONE, GLOBAL_AMAX, GLOBAL_GIVEN = 0, 1, 2
+_DT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
+_TORCH_DT = {BF16: torch.bfloat16, FP16: torch.float16, FP32: torch.float32}
+
+
+class FP4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"fp4 status {status}: {msg}")
+        self.status = status
+
+
+class QuantOpts(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
+                ("f_max", C.c_int32), ("global_scale", C.c_int32), ("block_axis", C.c_int32)]
+
+
+class AttnProblem(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("B", C.c_int64), ("H", C.c_int64), ("Hkv", C.c_int64),
+                ("Sq", C.c_int64), ("Sk", C.c_int64), ("d", C.c_int64), ("dtype", C.c_int32),
+                ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("q_codes", C.c_void_p), ("q_scales", C.c_void_p), ("k_codes", C.c_void_p),
+                ("k_scales", C.c_void_p), ("v_codes", C.c_void_p), ("v_scales", C.c_void_p)]
+
+
+class AttnOpts(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("causal", C.c_int32), ("softmax_scale", C.c_float),
+                ("kv_tile", C.c_int32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
+                ("f_max", C.c_int32), ("fp16_budget_pct", C.c_int32), ("sel_block", C.c_int32),
+                ("out_dtype", C.c_int32)]
+
+
+class KVCacheStruct(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("B", C.c_int64), ("Hkv", C.c_int64), ("d", C.c_int64),
+                ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("mid_cap", C.c_int64),
+                ("k_sink", C.c_void_p), ("v_sink", C.c_void_p), ("k_codes", C.c_void_p),
+                ("k_scales", C.c_void_p), ("v_codes", C.c_void_p), ("v_scales", C.c_void_p),
+                ("k_recent", C.c_void_p), ("v_recent", C.c_void_p), ("mid_len", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def build() -> str:
+    """Compile libfp4.so for gfx950 (hipcc, in-tree)."""
+    from .buildlib import build as _b
+    return _b()
+
+
+def load():
+    """Load libfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FP4Error(-4, f"native library missing at {_LIB_PATH}; run block_scaled_fp4_amd.build()")
+    L = C.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    L.fp4_version.restype = C.c_int
+    L.fp4_last_error.restype = C.c_char_p
+    L.fp4_quantize.argtypes = [vp, i32, i64, i64, i64, C.POINTER(QuantOpts), vp, vp, vp, vp, vp, sz, vp]
+    L.fp4_quantize.restype = C.c_int
+    L.fp4_quantize_workspace_size.argtypes = [i64, i64, C.POINTER(QuantOpts)]
+    L.fp4_quantize_workspace_size.restype = sz
+    L.fp4_attention_fwd.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, vp, vp, sz, vp]
+    L.fp4_attention_fwd.restype = C.c_int
+    L.fp4_attention_fwd_workspace_size.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts)]
+    L.fp4_attention_fwd_workspace_size.restype = sz
+    L.fp4_block_topk.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, sz, vp]
+    L.fp4_block_topk.restype = C.c_int
+    L.fp4_block_topk_workspace_size.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts)]
+    L.fp4_block_topk_workspace_size.restype = sz
+    L.fp4_attention_decode.argtypes = [vp, i64, C.POINTER(KVCacheStruct), C.c_float, i32, vp, vp, vp, sz, vp]
+    L.fp4_attention_decode.restype = C.c_int
+    L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
+    L.fp4_attention_decode_workspace_size.restype = sz
+    _lib = L
+    return L
+
+
+def fp4_version() -> int:
+    return load().fp4_version()
+
+
+def fp4_last_error() -> str:
+    return load().fp4_last_error().decode()
+
+
+def _check(st: int):
+    if st != 0:
+        raise FP4Error(st, fp4_last_error())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise FP4Error(-1, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise FP4Error(-1, f"{name} must be contiguous")
+
+
+def _stream(dev):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(n, dev):
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev) if n else None
+
+
+def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True, f_min: int = -2,
+                 f_max: int = 6, global_scale: int = GLOBAL_NONE, g: torch.Tensor | None = None,
+                 with_offsets: bool = True, out=None):
+    """Quantize a 2-D tensor (bf16/fp16/fp32, contiguous rows) to NVFP4 blocks.
+
+    Returns dict(codes, scales, offsets, g); layouts as documented in fp4.h."""
+    L = load()
+    _dev(x, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if block_axis == 0:
+        cshape, sshape = (rows, cols // 2), (rows, cols // 16)
+    else:
+        cshape, sshape = (rows // 2, cols), (rows // 16, cols)
+    if out is not None:
+        codes, scales, offs = out["codes"], out["scales"], out.get("offsets")
+    else:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+        offs = torch.empty(sshape, dtype=torch.int8, device=dev) if with_offsets else None
+    if g is None and global_scale != GLOBAL_NONE:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    o = QuantOpts(C.sizeof(QuantOpts), int(bool(scale_search)), f_min, f_max, global_scale, block_axis)
+    nws = L.fp4_quantize_workspace_size(rows, cols, C.byref(o))
+    ws = _workspace(nws, dev)
+    st = L.fp4_quantize(_ptr(x), _DT[x.dtype], rows, cols, cols, C.byref(o), _ptr(codes), _ptr(scales),
+                        _ptr(offs), _ptr(g), _ptr(ws), nws, _stream(dev))
+    _check(st)
+    return dict(codes=codes, scales=scales, offsets=offs, g=g)
+
+
+def _problem(q, k, v, quant=None):
+    B, H, Sq, d = q.shape if q is not None else quant["q_shape"]
+    Hkv, Sk = (k.shape[1], k.shape[2]) if k is not None else quant["kv_shape"]
+    dt = _DT[q.dtype] if q is not None else BF16
+    P = AttnProblem(C.sizeof(AttnProblem), B, H, Hkv, Sq, Sk, d, dt, _ptr(q), _ptr(k), _ptr(v))
+    if quant is not None:
+        for name in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales"):
+            setattr(P, name, _ptr(quant[name]))
+    return P
+
+
+def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype):
+    return AttnOpts(C.sizeof(AttnOpts), int(bool(causal)), float(softmax_scale), kv_tile,
+                    int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype)
+
+
+def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile=128):
+    """Block selection alone: returns (idx [B,H,nqb,kmax], cnt [B,H,nqb])."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k")):
+        _dev(t, n)
+    P = _problem(q, k, k)
+    O = _opts(causal, 0.0, kv_tile, True, -2, 6, fp16_budget_pct, sel_block, FP32)
+    B, H, Sq = q.shape[:3]
+    Sk = k.shape[2]
+    nqb = (Sq + sel_block - 1) // sel_block
+    nkb = (Sk + sel_block - 1) // sel_block
+    kmax = (fp16_budget_pct * nkb + 99) // 100
+    idx = torch.empty((B, H, nqb, max(kmax, 1)), dtype=torch.int32, device=q.device)
+    cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=q.device)
+    nws = L.fp4_block_topk_workspace_size(C.byref(P), C.byref(O))
+    ws = _workspace(nws, q.device)
+    _check(L.fp4_block_topk(C.byref(P), C.byref(O), _ptr(idx), _ptr(cnt), _ptr(ws), nws, _stream(q.device)))
+    return idx[..., :kmax], cnt
+
+
+def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
+                      f_max=6, fp16_budget_pct=0, sel_block=128, out_dtype=BF16, quantized=None,
+                      return_lse=True, return_topk=False, workspace=None, out=None):
+    """FP4 attention forward.  q [B,H,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp16).
+
+    quantized: optional dict with q_codes..v_scales from fp4_quantize (then q/k/v
+    may be None when fp16_budget_pct == 0).  Returns (out, lse[, idx, cnt])."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    ref = q if q is not None else quantized["q_codes"]
+    dev = ref.device
+    if q is not None:
+        B, H, Sq, d = q.shape
+    else:
+        B, H, Sq, d = quantized["q_shape"]
+    P = _problem(q, k, v, quantized)
+    O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
+    idx = cnt = None
+    if return_topk and fp16_budget_pct > 0:
+        Sk = P.Sk
+        nqb = (Sq + sel_block - 1) // sel_block
+        nkb = (Sk + sel_block - 1) // sel_block
+        kmax = (fp16_budget_pct * nkb + 99) // 100
+        idx = torch.empty((B, H, nqb, kmax), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
+    nws = L.fp4_attention_fwd_workspace_size(C.byref(P), C.byref(O))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
+    _check(L.fp4_attention_fwd(C.byref(P), C.byref(O), _ptr(out), _ptr(lse), _ptr(idx), _ptr(cnt), _ptr(ws),
+                               nws, _stream(dev)))
+    return (out, lse, idx, cnt) if return_topk else (out, lse)
+
+
+def attention_fwd_workspace_bytes(q_shape, kv_shape, causal=False, kv_tile=128, fp16_budget_pct=0,
+                                  sel_block=128, prequantized=False):
+    L = load()
+    B, H, Sq, d = q_shape
+    Hkv, Sk = kv_shape
+    P = AttnProblem(C.sizeof(AttnProblem), B, H, Hkv, Sq, Sk, d, BF16)
+    if prequantized:
+        for name in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales"):
+            setattr(P, name, C.c_void_p(16))
+    O = _opts(causal, 0.0, kv_tile, True, -2, 6, fp16_budget_pct, sel_block, BF16)
+    return L.fp4_attention_fwd_workspace_size(C.byref(P), C.byref(O))
+
+
+class KVCache:
+    """Device buffers of a sink-aware mixed-precision KV cache (layouts in fp4.h)."""
+
+    def __init__(self, k_sink, v_sink, k_codes, k_scales, v_codes, v_scales, k_recent, v_recent, mid_len):
+        self.k_sink, self.v_sink = k_sink, v_sink
+        self.k_codes, self.k_scales, self.v_codes, self.v_scales = k_codes, k_scales, v_codes, v_scales
+        self.k_recent, self.v_recent = k_recent, v_recent
+        self.mid_len = mid_len
+        self.B, self.Hkv = k_codes.shape[0], k_codes.shape[1]
+        self.d = k_codes.shape[3] * 2
+        self.mid_cap = k_codes.shape[2]
+        self.n_sink = k_sink.shape[2]
+        self.n_recent = k_recent.shape[2]
+
+    def struct(self):
+        return KVCacheStruct(C.sizeof(KVCacheStruct), self.B, self.Hkv, self.d, self.n_sink, self.n_recent,
+                             self.mid_cap, _ptr(self.k_sink), _ptr(self.v_sink), _ptr(self.k_codes),
+                             _ptr(self.k_scales), _ptr(self.v_codes), _ptr(self.v_scales), _ptr(self.k_recent),
+                             _ptr(self.v_recent), _ptr(self.mid_len))
+
+
+def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, return_lse=True, workspace=None,
+                         out=None):
+    """One-token decode.  q [B,Hq,d] bf16.  Returns (out [B,Hq,d], lse [B,Hq])."""
+    L = load()
+    _dev(q, "q")
+    B, Hq, d = q.shape
+    cs = cache.struct()
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    nws = L.fp4_attention_decode_workspace_size(Hq, C.byref(cs))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
+    _check(L.fp4_attention_decode(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out), _ptr(lse),
+                                  _ptr(ws), nws, _stream(q.device)))
+    return out, lse

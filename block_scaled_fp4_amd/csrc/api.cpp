@@ -1,0 +1,351 @@
+// api.cpp -- extern "C" entry points of the FP4 library: argument validation,
+// workspace planning and kernel launches.  No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp4.h"
+#include "fp4_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return FP4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Base-2 score factor: log2(e) * scale rounded once to binary32, scale = 1/sqrt(d)
+// when the caller passes <= 0.
+float score_factor(float softmax_scale, int64_t d) {
+  double s = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)d);
+  return (float)(1.4426950408889634074 * s);
+}
+
+int check_quant_opts(const fp4_quant_opts* o) {
+  if (!o) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: opts is NULL");
+  if (o->struct_size < sizeof(fp4_quant_opts))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: opts->struct_size %u < %zu", o->struct_size,
+                sizeof(fp4_quant_opts));
+  if (o->scale_search != 0 && o->scale_search != 1)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: scale_search must be 0 or 1");
+  if (o->scale_search && (o->f_min > 0 || o->f_max < 0 || o->f_min < -8 || o->f_max > 8))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: need -8 <= f_min <= 0 <= f_max <= 8");
+  if (o->global_scale < FP4_GLOBAL_NONE || o->global_scale > FP4_GLOBAL_GIVEN)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad global_scale mode %d", o->global_scale);
+  if (o->block_axis != 0 && o->block_axis != 1)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: block_axis must be 0 or 1");
+  return FP4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct AttnPlan {
+  size_t qc, qs, kc, ks, vc, vs, qm, km, idx, cnt, total;
+  int nqb, nkb, kmax;
+  bool need_quant, need_sel;
+};
+
+AttnPlan plan_attn(const fp4_attn_problem* p, const fp4_attn_opts* o) {
+  AttnPlan P{};
+  const int64_t B = p->B, H = p->H, Hkv = p->Hkv, Sq = p->Sq, Sk = p->Sk, d = p->d;
+  P.need_quant = !(p->q_codes && p->q_scales && p->k_codes && p->k_scales && p->v_codes && p->v_scales);
+  P.need_sel = o->fp16_budget_pct > 0;
+  const int sb = o->sel_block > 0 ? o->sel_block : 128;
+  P.nqb = (int)((Sq + sb - 1) / sb);
+  P.nkb = (int)((Sk + sb - 1) / sb);
+  P.kmax = P.need_sel ? (o->fp16_budget_pct * P.nkb + 99) / 100 : 0;
+  size_t off = 0;
+  auto take = [&](size_t n) { size_t at = off; off += align256(n); return at; };
+  if (P.need_quant) {
+    P.qc = take((size_t)(B * H * Sq * d / 2));
+    P.qs = take((size_t)(B * H * Sq * d / 16));
+    P.kc = take((size_t)(B * Hkv * Sk * d / 2));
+    P.ks = take((size_t)(B * Hkv * Sk * d / 16));
+    P.vc = take((size_t)(B * Hkv * Sk * d / 2));
+    P.vs = take((size_t)(B * Hkv * Sk * d / 16));
+  }
+  if (P.need_sel) {
+    P.qm = take((size_t)(B * H * P.nqb * d) * sizeof(double));
+    P.km = take((size_t)(B * Hkv * P.nkb * d) * sizeof(double));
+    P.idx = take((size_t)(B * H * P.nqb * (P.kmax > 0 ? P.kmax : 1)) * sizeof(int32_t));
+    P.cnt = take((size_t)(B * H * P.nqb) * sizeof(int32_t));
+  }
+  P.total = off;
+  return P;
+}
+
+int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn, bool for_topk) {
+  if (!p || !o) return fail(FP4_ERR_INVALID_ARG, "%s: problem or opts is NULL", fn);
+  if (p->struct_size < sizeof(fp4_attn_problem) || o->struct_size < sizeof(fp4_attn_opts))
+    return fail(FP4_ERR_INVALID_ARG, "%s: struct_size too small", fn);
+  if (p->B < 1 || p->H < 1 || p->Hkv < 1 || p->Sq < 1 || p->Sk < 1)
+    return fail(FP4_ERR_INVALID_ARG, "%s: B, H, Hkv, Sq, Sk must be >= 1", fn);
+  if (p->H % p->Hkv) return fail(FP4_ERR_INVALID_ARG, "%s: H %% Hkv != 0", fn);
+  if (p->d != 64 && p->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim %lld not in {64,128}", fn, (long long)p->d);
+  if (p->Sk % 16) return fail(FP4_ERR_INVALID_ARG, "%s: Sk %% 16 != 0", fn);
+  if (p->dtype != FP4_BF16 && p->dtype != FP4_FP16)
+    return fail(FP4_ERR_UNSUPPORTED, "%s: q/k/v dtype must be bf16 or fp16", fn);
+  if (o->causal != 0 && o->causal != 1) return fail(FP4_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  if (o->causal && p->Sq != p->Sk) return fail(FP4_ERR_INVALID_ARG, "%s: causal needs Sq == Sk", fn);
+  if (o->kv_tile != 64 && o->kv_tile != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: kv_tile must be 64 or 128", fn);
+  if (o->fp16_budget_pct < 0 || o->fp16_budget_pct > 100)
+    return fail(FP4_ERR_INVALID_ARG, "%s: fp16_budget_pct must be in [0,100]", fn);
+  // a selection block holds whole 128-row query tiles of the kernel and whole key tiles
+  if (o->fp16_budget_pct > 0 && (o->sel_block <= 0 || o->sel_block % 128 || o->sel_block % o->kv_tile ||
+                                 o->sel_block > 4096))
+    return fail(FP4_ERR_INVALID_ARG, "%s: sel_block must be a positive multiple of 128 (<= 4096)", fn);
+  if (o->fp16_budget_pct > 0 && (p->Sk + o->sel_block - 1) / o->sel_block > 4096)
+    return fail(FP4_ERR_UNSUPPORTED, "%s: more than 4096 key blocks", fn);
+  if (o->fp16_budget_pct > 0 && (!p->q || !p->k || !p->v))
+    return fail(FP4_ERR_INVALID_ARG, "%s: the FP16 path needs the high-precision q, k, v", fn);
+  if (for_topk && o->fp16_budget_pct == 0) return fail(FP4_ERR_INVALID_ARG, "%s: fp16_budget_pct is 0", fn);
+  if (o->scale_search != 0 && o->scale_search != 1) return fail(FP4_ERR_INVALID_ARG, "%s: scale_search must be 0 or 1", fn);
+  if (o->scale_search && (o->f_min > 0 || o->f_max < 0 || o->f_min < -8 || o->f_max > 8))
+    return fail(FP4_ERR_INVALID_ARG, "%s: need -8 <= f_min <= 0 <= f_max <= 8", fn);
+  if (o->out_dtype < FP4_BF16 || o->out_dtype > FP4_FP32) return fail(FP4_ERR_INVALID_ARG, "%s: bad out_dtype", fn);
+  const bool any_codes = p->q_codes || p->q_scales || p->k_codes || p->k_scales || p->v_codes || p->v_scales;
+  const bool all_codes = p->q_codes && p->q_scales && p->k_codes && p->k_scales && p->v_codes && p->v_scales;
+  if (any_codes && !all_codes) return fail(FP4_ERR_INVALID_ARG, "%s: give all six quantized arrays or none", fn);
+  if (!all_codes && (!p->q || !p->k || !p->v)) return fail(FP4_ERR_INVALID_ARG, "%s: q, k, v are NULL", fn);
+  const void* ptrs[] = {p->q, p->k, p->v, p->q_codes, p->q_scales, p->k_codes, p->k_scales, p->v_codes, p->v_scales};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4_version(void) { return 10000; }
+
+const char* fp4_last_error(void) { return g_err; }
+
+size_t fp4_quantize_workspace_size(int64_t rows, int64_t cols, const fp4_quant_opts* opts) {
+  if (!opts || opts->global_scale != FP4_GLOBAL_AMAX || rows <= 0 || cols <= 0) return 0;
+  return (size_t)fp4i_amax_parts(rows, cols) * sizeof(float);
+}
+
+int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                 const fp4_quant_opts* opts, uint8_t* codes, uint8_t* scales, int8_t* offsets,
+                 float* g, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_quant_opts(opts);
+  if (st) return st;
+  if (dtype != FP4_BF16 && dtype != FP4_FP16 && dtype != FP4_FP32)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad dtype %d", dtype);
+  if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad shape/ld");
+  if (opts->block_axis == 0 && cols % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: cols %% 16 != 0");
+  if (opts->block_axis == 1 && rows % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: rows %% 16 != 0");
+  if (rows > 0 && cols > 0 && (!x || !codes || !scales))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: x, codes and scales must be non-NULL");
+  if ((x && !aligned16(x)) || (codes && !aligned16(codes)) || (scales && !aligned16(scales)))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: x, codes, scales must be 16-byte aligned");
+  const size_t esz = dtype == FP4_FP32 ? 4 : 2;
+  if (opts->block_axis == 0 && ld > cols && ((ld * esz) % 16))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: row stride must keep 16-byte alignment");
+  if (opts->global_scale != FP4_GLOBAL_NONE && !g)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: g is required for this global_scale mode");
+  const size_t need = fp4_quantize_workspace_size(rows, cols, opts);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(FP4_ERR_WORKSPACE, "fp4_quantize: workspace needs %zu bytes", need);
+  QuantLaunch L;
+  L.x = x;
+  L.dtype = dtype;
+  L.rows = rows;
+  L.cols = cols;
+  L.ld = ld;
+  L.axis = opts->block_axis;
+  L.search = opts->scale_search;
+  L.fmin = opts->f_min;
+  L.fmax = opts->f_max;
+  L.gmode = opts->global_scale;
+  L.codes = codes;
+  L.scales = scales;
+  L.offsets = offsets;
+  L.g = g;
+  L.amax_ws = (float*)workspace;
+  return hip_status(fp4i_launch_quantize(L, (hipStream_t)stream), "fp4_quantize launch");
+}
+
+size_t fp4_attention_fwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
+  if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
+    return 0;
+  return plan_attn(prob, opts).total;
+}
+
+size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
+  if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
+    return 0;
+  AttnPlan P = plan_attn(prob, opts);
+  if (!P.need_sel) return 0;
+  return P.total - P.qm;  // the selection part only
+}
+
+static int launch_selection(const fp4_attn_problem* p, const fp4_attn_opts* o, const AttnPlan& P, char* ws_sel,
+                            int32_t* idx, int32_t* cnt, hipStream_t s) {
+  TopkLaunch T;
+  T.q = p->q;
+  T.k = p->k;
+  T.dtype = p->dtype;
+  T.B = p->B; T.H = p->H; T.Hkv = p->Hkv; T.Sq = p->Sq; T.Sk = p->Sk; T.d = p->d;
+  T.causal = o->causal;
+  T.pct = o->fp16_budget_pct;
+  T.sel_block = o->sel_block;
+  T.nqb = P.nqb; T.nkb = P.nkb; T.kmax = P.kmax;
+  T.qmeans = (double*)(ws_sel);
+  T.kmeans = (double*)(ws_sel + (P.km - P.qm));
+  T.idx = idx ? idx : (int32_t*)(ws_sel + (P.idx - P.qm));
+  T.cnt = cnt ? cnt : (int32_t*)(ws_sel + (P.cnt - P.qm));
+  return hip_status(fp4i_launch_topk(T, s), "block selection launch");
+}
+
+int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int32_t* topk_idx,
+                   int32_t* topk_cnt, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn(prob, opts, "fp4_block_topk", true);
+  if (st) return st;
+  if (!prob->q || !prob->k) return fail(FP4_ERR_INVALID_ARG, "fp4_block_topk: q and k are required");
+  AttnPlan P = plan_attn(prob, opts);
+  size_t need = P.total - P.qm;
+  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "fp4_block_topk: workspace needs %zu bytes", need);
+  return launch_selection(prob, opts, P, (char*)workspace, topk_idx, topk_cnt, (hipStream_t)stream);
+}
+
+int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, float* lse,
+                      int32_t* topk_idx, int32_t* topk_cnt, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int st = check_attn(prob, opts, "fp4_attention_fwd", false);
+  if (st) return st;
+  if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "fp4_attention_fwd: out must be non-NULL and 16-byte aligned");
+  AttnPlan P = plan_attn(prob, opts);
+  if (workspace_bytes < P.total || (P.total && !workspace))
+    return fail(FP4_ERR_WORKSPACE, "fp4_attention_fwd: workspace needs %zu bytes", P.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t B = prob->B, H = prob->H, Hkv = prob->Hkv, Sq = prob->Sq, Sk = prob->Sk, d = prob->d;
+  const uint8_t *qc = prob->q_codes, *qs = prob->q_scales, *kc = prob->k_codes, *ks = prob->k_scales,
+                *vc = prob->v_codes, *vs = prob->v_scales;
+  if (P.need_quant) {
+    QuantLaunch L{};
+    L.dtype = prob->dtype;
+    L.search = opts->scale_search;
+    L.fmin = opts->f_min;
+    L.fmax = opts->f_max;
+    L.gmode = 0;
+    L.cols = d;
+    L.ld = d;
+    L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
+    L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
+    hipError_t e = fp4i_launch_quantize(L, s);
+    if (e == hipSuccess) {
+      L.x = prob->k; L.rows = B * Hkv * Sk;
+      L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
+      e = fp4i_launch_quantize(L, s);
+    }
+    if (e == hipSuccess) {
+      L.x = prob->v; L.axis = 1;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
+      L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
+      e = fp4i_launch_quantize(L, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "fp4_attention_fwd quantize launch");
+    qc = (uint8_t*)(ws + P.qc); qs = (uint8_t*)(ws + P.qs);
+    kc = (uint8_t*)(ws + P.kc); ks = (uint8_t*)(ws + P.ks);
+    vc = (uint8_t*)(ws + P.vc); vs = (uint8_t*)(ws + P.vs);
+  }
+  const int32_t* idx = nullptr;
+  const int32_t* cnt = nullptr;
+  if (P.need_sel) {
+    st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s);
+    if (st) return st;
+    idx = topk_idx ? topk_idx : (const int32_t*)(ws + P.idx);
+    cnt = topk_cnt ? topk_cnt : (const int32_t*)(ws + P.cnt);
+  }
+  AttnLaunch A;
+  A.B = B; A.H = H; A.Hkv = Hkv; A.Sq = Sq; A.Sk = Sk; A.d = d;
+  A.dtype = prob->dtype;
+  A.q = prob->q; A.k = prob->k; A.v = prob->v;
+  A.qc = qc; A.qs = qs; A.kc = kc; A.ks = ks; A.vc = vc; A.vs = vs;
+  A.causal = opts->causal;
+  A.c = score_factor(opts->softmax_scale, d);
+  A.kv_tile = opts->kv_tile;
+  A.pct = opts->fp16_budget_pct;
+  A.sel_block = opts->sel_block;
+  A.nqb = P.nqb;
+  A.kmax = P.kmax;
+  A.idx = idx;
+  A.cnt = cnt;
+  A.out_dtype = opts->out_dtype;
+  A.out = out;
+  A.lse = lse;
+  return hip_status(fp4i_launch_attn_fwd(A, s), "fp4_attention_fwd launch");
+}
+
+size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* c) {
+  if (!c || c->struct_size < sizeof(fp4_kv_cache) || Hq <= 0 || c->B <= 0 || c->d <= 0) return 0;
+  int64_t split_len = 0;
+  int ns = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &split_len);
+  size_t n = (size_t)(c->B * Hq) * (size_t)(ns + 1);
+  return align256(n * (size_t)c->d * sizeof(float)) + align256(n * 2 * sizeof(float));
+}
+
+int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float softmax_scale,
+                         int32_t out_dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const char* fn = "fp4_attention_decode";
+  if (!c || c->struct_size < sizeof(fp4_kv_cache)) return fail(FP4_ERR_INVALID_ARG, "%s: cache is NULL or struct_size too small", fn);
+  if (!q || !out) return fail(FP4_ERR_INVALID_ARG, "%s: q and out are required", fn);
+  if (c->B < 1 || c->Hkv < 1 || Hq < 1 || Hq % c->Hkv) return fail(FP4_ERR_INVALID_ARG, "%s: bad B/Hq/Hkv", fn);
+  if (c->d != 64 && c->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim %lld not in {64,128}", fn, (long long)c->d);
+  if (Hq / c->Hkv > 16) return fail(FP4_ERR_UNSUPPORTED, "%s: more than 16 query heads per kv head", fn);
+  if (c->n_sink < 0 || c->n_recent < 0 || c->mid_cap < 0 || c->mid_cap % 16)
+    return fail(FP4_ERR_INVALID_ARG, "%s: n_sink/n_recent must be >= 0 and mid_cap a multiple of 16", fn);
+  if (c->n_sink + c->n_recent + c->mid_cap < 1) return fail(FP4_ERR_INVALID_ARG, "%s: empty cache", fn);
+  if ((c->n_sink && (!c->k_sink || !c->v_sink)) || (c->n_recent && (!c->k_recent || !c->v_recent)))
+    return fail(FP4_ERR_INVALID_ARG, "%s: sink/recent buffers missing", fn);
+  if (c->mid_cap && (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->mid_len))
+    return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 region buffers or mid_len missing", fn);
+  if (out_dtype < FP4_BF16 || out_dtype > FP4_FP32) return fail(FP4_ERR_INVALID_ARG, "%s: bad out_dtype", fn);
+  const void* ptrs[] = {q, out, c->k_sink, c->v_sink, c->k_codes, c->k_scales, c->v_codes, c->v_scales, c->k_recent, c->v_recent};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  size_t need = fp4_attention_decode_workspace_size(Hq, c);
+  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  DecodeLaunch L;
+  L.q = q;
+  L.B = c->B; L.Hq = Hq; L.Hkv = c->Hkv; L.d = c->d;
+  L.n_sink = c->n_sink; L.n_recent = c->n_recent; L.mid_cap = c->mid_cap;
+  L.k_sink = c->k_sink; L.v_sink = c->v_sink;
+  L.kc = c->k_codes; L.ks = c->k_scales; L.vc = c->v_codes; L.vs = c->v_scales;
+  L.k_recent = c->k_recent; L.v_recent = c->v_recent;
+  L.mid_len = c->mid_len;
+  L.c = score_factor(softmax_scale, c->d);
+  L.out_dtype = out_dtype;
+  L.out = out;
+  L.lse = lse;
+  L.nsplit = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &L.split_len);
+  size_t n = (size_t)(c->B * Hq) * (size_t)(L.nsplit + 1);
+  L.part_o = (float*)workspace;
+  L.part_ml = (float*)((char*)workspace + align256(n * (size_t)c->d * sizeof(float)));
+  return hip_status(fp4i_launch_decode(L, (hipStream_t)stream), "fp4_attention_decode launch");
+}
+
+}  // extern "C"

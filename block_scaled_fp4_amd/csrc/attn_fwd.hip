@@ -1,0 +1,552 @@
+// attn_fwd.hip -- fused FP4 attention forward for gfx950 (CDNA4).
+//
+// What it computes (ScaleSearch page, Metodologia / ScaleSearchAttention:
+// QK^T and PV on NVFP4 operands with FP32 accumulation; ThriftAttention page,
+// Metodologia / 2: FP4 path with two-level quantization of P for most block
+// pairs, FP16 path for the selected ones, both merged by an online softmax):
+//   for every query row i and key tile T (kv_tile keys):
+//     x = fl32(S * c), tm = max over visible keys, e = 2^(x - tm)
+//     FP4 tile:  16-key blocks of e get s2 = E4M3(amax(e) * 448), codes
+//                RNE_E2M1(e * fl32(2688/s2)), P^ = code * s2; the tile adds
+//                (P^ V^) / 2688 with weight 2^(tm - m)
+//     FP16 tile: adds fp16(e) fp16(V) (scores from fp16 q and k)
+//     l sums the unquantized e; out = O / l.
+//
+// MI355X mapping.  gfx950's block-scaled FP4 MFMA takes power-of-two scales
+// per 32 elements, while NVFP4 scales are E4M3 per 16, so the operands are
+// dequantized exactly to fp16 (code * scale has at most 6 significant bits)
+// and run on v_mfma_f32_32x32x16_f16.  One workgroup = 4 waves = 128 query
+// rows of one (batch, head); a wave owns 32 rows.  Per key tile:
+//   - all 256 lanes dequantize the tile's K and V codes into LDS (K as
+//     [key][d], V transposed as [d][key]); the next tile's codes are fetched
+//     into registers while the current tile computes;
+//   - each wave computes S^T = K Q^T (32 keys x 32 queries per MFMA tile).  K
+//     rows are fed in a permuted order so that every lane ends up holding one
+//     query row's 16 consecutive keys: the level-2 P scale is a lane-local
+//     reduction, only the tile row maximum crosses to lane ^ 32;
+//   - P stays in registers and is the B operand of O^T += V^T P^T; V's LDS
+//     layout uses the matching key order, so P needs no shuffle.
+// The FP4 tiles run first, the FP16 tiles after (their fp16 Q fragment is
+// loaded only when a selected pair exists), as the ThriftAttention page does
+// to limit register pressure.
+#include "device_common.h"
+#include "fp4_internal.h"
+
+namespace fp4dev {
+
+// {fl32(2688 / s), s} for every positive E4M3 scale byte s, compile-time
+// correctly rounded; byte 0 (zero block) maps to {0, 0}.
+struct PScaleTable {
+  float m[128];
+  float s[128];
+  constexpr PScaleTable() : m(), s() {
+    for (int b = 0; b < 128; ++b) {
+      float v = 0.0f;
+      if (b < 8) v = (float)b / 512.0f;
+      else {
+        int e = (b >> 3) - 7, mm = b & 7;
+        v = 1.0f + (float)mm / 8.0f;
+        for (int i = 0; i < e; ++i) v *= 2.0f;
+        for (int i = 0; i > e; --i) v /= 2.0f;
+      }
+      s[b] = (b == 127) ? 0.0f : v;
+      m[b] = (b == 0 || b == 127) ? 0.0f : 2688.0f / v;
+    }
+  }
+};
+__constant__ PScaleTable kPScale = PScaleTable();
+
+constexpr int kWaves = 4;
+constexpr int kBr = 32 * kWaves;  // query rows per workgroup
+
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Position of key k (within a 32-key group) in the V^T LDS row: the 8-key
+// groups 1 and 2 trade places, matching the keys each lane holds in S^T.
+__device__ __forceinline__ int vpos(int k) { return (k & ~31) | ((k & 8) << 1) | ((k & 16) >> 1) | (k & 7); }
+
+// A-operand row of S^T for key k inside a 32-key subtile, inverse of the
+// MFMA output row -> key map key(row) = (row%4) + 4*(row/8) + 16*((row/4)%2).
+__device__ __forceinline__ int krow_of_lane(int r) { return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 4); }
+
+template <typename OT>
+__device__ __forceinline__ void store4(OT* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4_t*>(p) = float4_t{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<half_t>(half_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<half4_t*>(p) = half4_t{(half_t)a, (half_t)b, (half_t)c, (half_t)d};
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  uint2_t w;
+  w[0] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  w[1] = (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16);
+  *reinterpret_cast<uint2_t*>(p) = w;
+}
+
+// fp16 (RNE) of a bf16 or fp16 input element pair packed in a dword.
+template <typename IT>
+__device__ __forceinline__ half2_t to_half2(uint32_t w);
+template <>
+__device__ __forceinline__ half2_t to_half2<uint16_t>(uint32_t w) {
+  return half2_t{(half_t)__uint_as_float(w << 16), (half_t)__uint_as_float(w & 0xFFFF0000u)};
+}
+template <>
+__device__ __forceinline__ half2_t to_half2<half_t>(uint32_t w) {
+  return __builtin_bit_cast(half2_t, w);
+}
+
+template <int D, int BC>
+struct Smem {
+  static constexpr int KS = D + 8;   // halves per K row (16-byte pad)
+  static constexpr int VS = BC + 8;  // halves per V^T row
+  half_t k[BC * KS];
+  half_t v[D * VS];
+  float pm[128];
+  float ps[128];
+};
+
+// One tile's worth of quantized K/V held in registers between fetch and stage.
+template <int D, int BC>
+struct Fetch {
+  static constexpr int NCH = BC * D / 32;               // 16-byte chunks per operand
+  static constexpr int PER = (NCH + 255) / 256;          // chunks per thread
+  uint4_t kc[PER];
+  uint32_t ks[PER];  // two scale bytes (d blocks 2j, 2j+1)
+  uint4_t vc[PER];
+  uint4_t vs[PER];
+};
+
+struct Problem {
+  int64_t H, Hkv, Sq, Sk;
+  const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
+  const void *q, *k, *v;
+  const int32_t *idx, *cnt;
+  int causal, pct, sel_block, nqb, kmax, nqt;
+  float c;
+  void* out;
+  float* lse;
+};
+
+template <int D, int BC>
+__device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                                          const uint8_t* vs, int64_t key0, int64_t Sk) {
+  constexpr int NCH = Fetch<D, BC>::NCH;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
+    const int q = t + 256 * u;
+    if (q < NCH) {
+      // K: chunk q covers key row q/(D/32), d columns 32*(q%(D/32)) .. +32
+      const int kr = q / (D / 32), dc = q % (D / 32);
+      const int64_t key = key0 + kr;
+      if (key < Sk) {
+        F.kc[u] = *reinterpret_cast<const uint4_t*>(kc + key * (D / 2) + dc * 16);
+        F.ks[u] = *reinterpret_cast<const uint16_t*>(ks + key * (D / 16) + dc * 2);
+      } else {
+        F.kc[u] = uint4_t{0, 0, 0, 0};
+        F.ks[u] = 0;
+      }
+      // V: chunk q covers token pair row q/(D/16), columns 16*(q%(D/16)) .. +16
+      const int pr = q / (D / 16), cc = q % (D / 16);
+      const int64_t pair = key0 / 2 + pr;
+      if (2 * pair < Sk) {
+        F.vc[u] = *reinterpret_cast<const uint4_t*>(vc + pair * D + cc * 16);
+        F.vs[u] = *reinterpret_cast<const uint4_t*>(vs + (pair / 8) * D + cc * 16);
+      } else {
+        F.vc[u] = uint4_t{0, 0, 0, 0};
+        F.vs[u] = uint4_t{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ half2_t scale_pair(half2_t v, half_t s) { return v * half2_t{s, s}; }
+
+template <int D, int BC>
+__device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S) {
+  constexpr int NCH = Fetch<D, BC>::NCH;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
+    const int q = t + 256 * u;
+    if (q < NCH) {
+      const int kr = q / (D / 32), dc = q % (D / 32);
+      const half_t s0 = (half_t)e4m3_to_f32(F.ks[u] & 0xFFu), s1 = (half_t)e4m3_to_f32((F.ks[u] >> 8) & 0xFFu);
+      half8_t o[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t cw = F.kc[u][w];  // 8 codes: d = 32*dc + 8*w .. +8
+        const half_t s = w < 2 ? s0 : s1;
+        half2_t a = scale_pair(cvt_pk_f16_fp4<0>(cw), s), b = scale_pair(cvt_pk_f16_fp4<1>(cw), s);
+        half2_t c = scale_pair(cvt_pk_f16_fp4<2>(cw), s), d2 = scale_pair(cvt_pk_f16_fp4<3>(cw), s);
+        o[w] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+      }
+      half_t* dst = S.k + kr * Smem<D, BC>::KS + dc * 32;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<half8_t*>(dst + 8 * w) = o[w];
+      // V: byte j of the chunk = column 16*cc + j, tokens (2*pr, 2*pr+1)
+      const int pr = q / (D / 16), cc = q % (D / 16);
+      const int pos = vpos(2 * pr);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t cw = F.vc[u][w], sw = F.vs[u][w];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = 16 * cc + 4 * w + j;
+          const half_t s = (half_t)e4m3_to_f32((sw >> (8 * j)) & 0xFFu);
+          half2_t pv;
+          if (j == 0) pv = cvt_pk_f16_fp4<0>(cw);
+          else if (j == 1) pv = cvt_pk_f16_fp4<1>(cw);
+          else if (j == 2) pv = cvt_pk_f16_fp4<2>(cw);
+          else pv = cvt_pk_f16_fp4<3>(cw);
+          *reinterpret_cast<half2_t*>(S.v + col * Smem<D, BC>::VS + pos) = scale_pair(pv, s);
+        }
+      }
+    }
+  }
+}
+
+// FP16 path staging: original bf16/fp16 K and V of the tile, converted to fp16.
+template <int D, int BC, typename IT>
+__device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const IT* vp, int64_t key0, int64_t Sk) {
+  // K: BC rows x D; 8 elements (16 bytes) per step
+  constexpr int NK = BC * D / 8;
+  for (int q = threadIdx.x; q < NK; q += 256) {
+    const int kr = q / (D / 8), dc = q % (D / 8);
+    const int64_t key = key0 + kr;
+    uint4_t w = uint4_t{0, 0, 0, 0};
+    if (key < Sk) w = *reinterpret_cast<const uint4_t*>(kp + key * D + dc * 8);
+    half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
+    *reinterpret_cast<half8_t*>(S.k + kr * Smem<D, BC>::KS + dc * 8) =
+        half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+  }
+  // V: token pairs x 8 columns per step -> V^T
+  constexpr int NV = (BC / 2) * (D / 8);
+  for (int q = threadIdx.x; q < NV; q += 256) {
+    const int pr = q / (D / 8), cc = q % (D / 8);
+    const int64_t key = key0 + 2 * pr;
+    uint4_t w0 = uint4_t{0, 0, 0, 0}, w1 = uint4_t{0, 0, 0, 0};
+    if (key < Sk) {
+      w0 = *reinterpret_cast<const uint4_t*>(vp + key * D + cc * 8);
+      w1 = *reinterpret_cast<const uint4_t*>(vp + (key + 1) * D + cc * 8);
+    }
+    const int pos = vpos(2 * pr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half2_t a = to_half2<IT>(w0[j]), b = to_half2<IT>(w1[j]);
+      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j) * Smem<D, BC>::VS + pos) = half2_t{a[0], b[0]};
+      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j + 1) * Smem<D, BC>::VS + pos) = half2_t{a[1], b[1]};
+    }
+  }
+}
+
+// Per-wave state.
+template <int D>
+struct RowState {
+  float16_t o[D / 32];  // O^T accumulators: d rows (i%4)+8(i/4)+4(lane/32) of 32-row group, query lane%32
+  float m;              // running max (x units), shared by lanes l and l^32
+  float l;              // this lane's part of the denominator
+};
+
+// Process one tile for one wave.  fp4: two-level P; else fp16(e).
+template <int D, int BC, bool FP4, bool MASK>
+__device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
+                                          int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5;  // which 16-key half of each 32-key group this lane holds
+  constexpr int NG = BC / 32;
+  float16_t acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = float16_t{0};
+  // S^T = K Q^T
+  const int krow = krow_of_lane(lane & 31);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const half8_t a = *reinterpret_cast<const half8_t*>(S.k + (32 * g + krow) * Smem<D, BC>::KS + 16 * s + 8 * hi);
+      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[g], 0, 0, 0);
+    }
+  }
+  // x = S * c, masked keys -> -inf; lane holds keys 32g + 16*hi + i
+  float tm = -__builtin_inff();
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = acc[g][i] * c;
+      if (MASK) {
+        const int64_t key = key0 + 32 * g + 16 * hi + i;
+        if (key >= Sk || (causal && key > qrow)) x = -__builtin_inff();
+      }
+      acc[g][i] = x;
+      tm = __builtin_fmaxf(tm, x);
+    }
+  tm = __builtin_fmaxf(tm, xor32(tm));
+  const bool live = tm > -__builtin_inff();
+  const float mnew = live ? __builtin_fmaxf(R.m, tm) : R.m;
+  // e = 2^(x - tm); masked keys give 0; sum into l
+  float lsum = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float e = live ? __builtin_amdgcn_exp2f(acc[g][i] - tm) : 0.0f;
+      acc[g][i] = e;
+      lsum += e;
+    }
+  // P operands: step (g, h2) takes this lane's values i = 8*h2 .. 8*h2+7
+  half8_t pf[NG][2];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (FP4) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, acc[g][i]);
+      const uint32_t sb = f32_to_e4m3(amax * 448.0f);
+      const float M = S.pm[sb];
+      const half_t s2 = (half_t)S.ps[sb];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = acc[g][8 * h2 + i] * M;
+        uint32_t w = 0;
+        w = cvt_pk_fp4<0>(w, t[0], t[1]);
+        w = cvt_pk_fp4<1>(w, t[2], t[3]);
+        w = cvt_pk_fp4<2>(w, t[4], t[5]);
+        w = cvt_pk_fp4<3>(w, t[6], t[7]);
+        half2_t a = scale_pair(cvt_pk_f16_fp4<0>(w), s2), b = scale_pair(cvt_pk_f16_fp4<1>(w), s2);
+        half2_t cc = scale_pair(cvt_pk_f16_fp4<2>(w), s2), d2 = scale_pair(cvt_pk_f16_fp4<3>(w), s2);
+        pf[g][h2] = half8_t{a[0], a[1], b[0], b[1], cc[0], cc[1], d2[0], d2[1]};
+      }
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pf[g][h2][i] = (half_t)acc[g][8 * h2 + i];
+    }
+  }
+  // Otile^T = V^T P^T into the (now free) score accumulators, then merge
+  float16_t ot[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) ot[t] = float16_t{0};
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const half8_t a = *reinterpret_cast<const half8_t*>(S.v + (32 * t + (lane & 31)) * Smem<D, BC>::VS +
+                                                            32 * g + 16 * h2 + 8 * hi);
+        ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[g][h2], ot[t], 0, 0, 0);
+      }
+    }
+  if (live) {
+    const float alpha = __builtin_amdgcn_exp2f(R.m - mnew);  // R.m = -inf on the first live tile -> 0
+    const float w = __builtin_amdgcn_exp2f(tm - mnew) * (FP4 ? (1.0f / 2688.0f) : 1.0f);
+    const float rt = __builtin_amdgcn_exp2f(tm - mnew);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) R.o[t][i] = __builtin_fmaf(ot[t][i], w, R.o[t][i] * alpha);
+    R.l = R.l * alpha + rt * lsum;
+    R.m = mnew;
+  }
+}
+
+template <int D, int BC, typename IT, typename OT>
+__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
+  __shared__ Smem<D, BC> S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
+  // workgroup -> (batch*head, query tile): heads spread over the 8 XCDs so a
+  // head's K/V stay in one L2; heaviest (causal) query tiles first
+  const int64_t BH = gridDim.x / P.nqt;
+  int64_t bh, qrank;
+  const int64_t gi = blockIdx.x;
+  if (BH % 8 == 0) {
+    const int64_t xcd = gi % 8, slot = gi / 8, hpx = BH / 8;
+    qrank = slot / hpx;
+    bh = (slot % hpx) * 8 + xcd;
+  } else {
+    bh = gi % BH;
+    qrank = gi / BH;
+  }
+  const int qt = (int)(P.causal ? (P.nqt - 1 - qrank) : qrank);
+  const int64_t b = bh / P.H, h = bh - b * P.H, hk = h / (P.H / P.Hkv);
+  const int64_t q0 = (int64_t)qt * kBr;
+  const int64_t qrow = q0 + 32 * wave + (lane & 31);
+  const int64_t Sk = P.Sk;
+
+  if (threadIdx.x < 128) {
+    S.pm[threadIdx.x] = kPScale.m[threadIdx.x];
+    S.ps[threadIdx.x] = kPScale.s[threadIdx.x];
+  }
+  // Q^ fragment (B operand): query qrow, d = 16 s + 8 hi .. +8
+  half8_t qf[D / 16];
+  {
+    const bool ok = qrow < P.Sq;
+    const uint8_t* qcr = P.qc + (bh * P.Sq + (ok ? qrow : 0)) * (D / 2);
+    const uint8_t* qsr = P.qs + (bh * P.Sq + (ok ? qrow : 0)) * (D / 16);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t cw = ok ? *reinterpret_cast<const uint32_t*>(qcr + 8 * s + 4 * hi) : 0u;
+      const half_t sc = (half_t)e4m3_to_f32(ok ? qsr[s] : 0u);
+      half2_t a = scale_pair(cvt_pk_f16_fp4<0>(cw), sc), bb = scale_pair(cvt_pk_f16_fp4<1>(cw), sc);
+      half2_t cc = scale_pair(cvt_pk_f16_fp4<2>(cw), sc), dd = scale_pair(cvt_pk_f16_fp4<3>(cw), sc);
+      qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
+    }
+  }
+  RowState<D> R;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) R.o[t] = float16_t{0};
+  R.m = -__builtin_inff();
+  R.l = 0.0f;
+
+  const int64_t qend = q0 + kBr < P.Sq ? q0 + kBr : P.Sq;  // rows of this workgroup: [q0, qend)
+  int64_t kend = Sk;
+  if (P.causal && qend < kend) kend = qend;
+  const int ntile = (int)((kend + BC - 1) / BC);
+  // selection of this query block (sel_block is a multiple of kBr)
+  const int32_t* sel = nullptr;
+  int nsel = 0;
+  if (P.pct > 0) {
+    const int64_t qb = q0 / P.sel_block;
+    sel = P.idx + (bh * P.nqb + qb) * P.kmax;
+    nsel = P.cnt[bh * P.nqb + qb];
+  }
+  const int tiles_per_block = P.sel_block / BC;
+
+  const uint8_t* kc = P.kc + (b * P.Hkv + hk) * Sk * (D / 2);
+  const uint8_t* ks = P.ks + (b * P.Hkv + hk) * Sk * (D / 16);
+  const uint8_t* vc = P.vc + (b * P.Hkv + hk) * (Sk / 2) * D;
+  const uint8_t* vs = P.vs + (b * P.Hkv + hk) * (Sk / 16) * D;
+
+  // ---- FP4 pass: every tile not covered by a selected block
+  Fetch<D, BC> F;
+  int si = 0;  // cursor into the ascending selection list
+  auto selected = [&](int tile) {
+    if (nsel == 0) return false;
+    const int blk = tile / tiles_per_block;
+    while (si < nsel && sel[si] < blk) ++si;
+    return si < nsel && sel[si] == blk;
+  };
+  int cur = 0;
+  while (cur < ntile && selected(cur)) ++cur;
+  if (cur < ntile) fetch_fp4<D, BC>(F, kc, ks, vc, vs, (int64_t)cur * BC, Sk);
+  while (cur < ntile) {
+    int nxt = cur + 1;
+    while (nxt < ntile && selected(nxt)) ++nxt;
+    __syncthreads();  // previous tile's LDS reads are done
+    stage_fp4<D, BC>(F, S);
+    if (nxt < ntile) fetch_fp4<D, BC>(F, kc, ks, vc, vs, (int64_t)nxt * BC, Sk);
+    __syncthreads();
+    const int64_t key0 = (int64_t)cur * BC;
+    const int64_t wrow0 = q0 + 32 * wave;
+    const bool wave_dead = P.causal && key0 > wrow0 + 31;  // every key of the tile is after this wave's rows
+    if (!wave_dead) {
+      const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
+      if (need_mask) wave_tile<D, BC, true, true>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      else wave_tile<D, BC, true, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+    }
+    cur = nxt;
+  }
+
+  // ---- FP16 pass over the selected blocks
+  if (nsel > 0) {
+    // fp16 Q fragment from the original input
+    const IT* qp = reinterpret_cast<const IT*>(P.q) + bh * P.Sq * D;
+    const bool ok = qrow < P.Sq;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(qp + qrow * D + 16 * s + 8 * hi) : uint4_t{0, 0, 0, 0};
+      half2_t a = to_half2<IT>(w[0]), bb = to_half2<IT>(w[1]), cc = to_half2<IT>(w[2]), dd = to_half2<IT>(w[3]);
+      qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
+    }
+    const IT* kp = reinterpret_cast<const IT*>(P.k) + (b * P.Hkv + hk) * Sk * D;
+    const IT* vp = reinterpret_cast<const IT*>(P.v) + (b * P.Hkv + hk) * Sk * D;
+    for (int s_i = 0; s_i < nsel; ++s_i) {
+      const int blk = sel[s_i];
+      for (int tt = 0; tt < tiles_per_block; ++tt) {
+        const int tile = blk * tiles_per_block + tt;
+        if (tile >= ntile) break;
+        const int64_t key0 = (int64_t)tile * BC;
+        __syncthreads();
+        stage_fp16<D, BC, IT>(S, kp, vp, key0, Sk);
+        __syncthreads();
+        const int64_t wrow0 = q0 + 32 * wave;
+        const bool wave_dead = P.causal && key0 > wrow0 + 31;
+        if (!wave_dead) {
+          const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
+          if (need_mask) wave_tile<D, BC, false, true>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+          else wave_tile<D, BC, false, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O / l, lse
+  const float ltot = R.l + xor32(R.l);
+  if (qrow < P.Sq) {
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    OT* orow = reinterpret_cast<OT*>(P.out) + (bh * P.Sq + qrow) * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * t + 8 * j + 4 * hi;
+        store4<OT>(orow + d0, R.o[t][4 * j] * inv, R.o[t][4 * j + 1] * inv, R.o[t][4 * j + 2] * inv,
+                   R.o[t][4 * j + 3] * inv);
+      }
+    if (P.lse && hi == 0)
+      P.lse[bh * P.Sq + qrow] = ltot > 0.0f ? (R.m + __builtin_log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
+  }
+}
+
+template <int D, int BC, typename IT>
+hipError_t launch_out(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
+  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float>), grid, dim3(256), 0, st, P);
+  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t>), grid, dim3(256), 0, st, P);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t>), grid, dim3(256), 0, st, P);
+  return hipGetLastError();
+}
+
+template <int D, int BC>
+hipError_t launch_in(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
+  if (L.dtype == 1) return launch_out<D, BC, half_t>(L, P, grid, st);
+  return launch_out<D, BC, uint16_t>(L, P, grid, st);
+}
+
+}  // namespace fp4dev
+
+using namespace fp4dev;
+
+hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t st) {
+  Problem P;
+  P.H = L.H; P.Hkv = L.Hkv; P.Sq = L.Sq; P.Sk = L.Sk;
+  P.qc = L.qc; P.qs = L.qs; P.kc = L.kc; P.ks = L.ks; P.vc = L.vc; P.vs = L.vs;
+  P.q = L.q; P.k = L.k; P.v = L.v;
+  P.idx = L.idx; P.cnt = L.cnt;
+  P.causal = L.causal; P.pct = L.pct; P.sel_block = L.pct > 0 ? L.sel_block : 128;
+  P.nqb = L.nqb; P.kmax = L.kmax;
+  P.c = L.c;
+  P.out = L.out; P.lse = L.lse;
+  P.nqt = (int)((L.Sq + kBr - 1) / kBr);
+  dim3 grid((unsigned)(L.B * L.H * P.nqt));
+  if (L.d == 128) {
+    if (L.kv_tile == 128) return launch_in<128, 128>(L, P, grid, st);
+    return launch_in<128, 64>(L, P, grid, st);
+  }
+  if (L.kv_tile == 128) return launch_in<64, 128>(L, P, grid, st);
+  return launch_in<64, 64>(L, P, grid, st);
+}

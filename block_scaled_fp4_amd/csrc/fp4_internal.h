@@ -1,0 +1,87 @@
+// fp4_internal.h -- launch descriptors shared by the host API and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct QuantLaunch {
+  const void* x;
+  int dtype;  // 0 bf16, 1 fp16, 2 fp32
+  int64_t rows, cols, ld;
+  int axis;
+  int search, fmin, fmax, gmode;
+  uint8_t* codes;
+  uint8_t* scales;
+  int8_t* offsets;
+  float* g;
+  float* amax_ws;  // fp4i_amax_parts floats (mode 1)
+};
+
+int fp4i_amax_parts(int64_t rows, int64_t cols);
+hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream);
+
+struct TopkLaunch {
+  const void* q;  // [B,H,Sq,d]
+  const void* k;  // [B,Hkv,Sk,d]
+  int dtype;
+  int64_t B, H, Hkv, Sq, Sk, d;
+  int causal, pct, sel_block;
+  int nqb, nkb, kmax;
+  double* qmeans;  // [B*H, nqb, d]
+  double* kmeans;  // [B*Hkv, nkb, d]
+  int32_t* idx;    // [B*H, nqb, kmax]
+  int32_t* cnt;    // [B*H, nqb]
+};
+
+hipError_t fp4i_launch_topk(const TopkLaunch& L, hipStream_t stream);
+
+struct AttnLaunch {
+  int64_t B, H, Hkv, Sq, Sk, d;
+  int dtype;  // of q, k, v (0 bf16, 1 fp16)
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* qc;
+  const uint8_t* qs;
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  int causal;
+  float c;  // log2(e) * softmax_scale, rounded once to binary32
+  int kv_tile;
+  int pct, sel_block, nqb, kmax;
+  const int32_t* idx;  // selection (pct > 0)
+  const int32_t* cnt;
+  int out_dtype;
+  void* out;
+  float* lse;
+};
+
+hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t stream);
+
+struct DecodeLaunch {
+  const void* q;  // bf16 [B,Hq,d]
+  int64_t B, Hq, Hkv, d;
+  int n_sink, n_recent;
+  int64_t mid_cap;
+  const void* k_sink;
+  const void* v_sink;
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  const void* k_recent;
+  const void* v_recent;
+  const int32_t* mid_len;
+  float c;  // log2(e) * softmax_scale
+  int out_dtype;
+  void* out;
+  float* lse;
+  int nsplit;        // context splits per (b, kv head)
+  int64_t split_len; // tokens per split of the FP4 region (multiple of the chunk)
+  float* part_o;     // [B*Hq, nsplit+1, d]
+  float* part_ml;    // [B*Hq, nsplit+1, 2]
+};
+
+int fp4i_decode_splits(int64_t B, int64_t Hkv, int64_t mid_cap, int64_t* split_len);
+hipError_t fp4i_launch_decode(const DecodeLaunch& L, hipStream_t stream);

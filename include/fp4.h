@@ -1,0 +1,226 @@
+/*
+ * fp4.h -- C ABI of the block-scaled FP4 attention library for AMD MI355X (gfx950).
+ *
+ * The library quantizes tensors to NVFP4-style blocks (4-bit E2M1 elements,
+ * one E4M3 scale per 16 elements, optional per-tensor binary32 scale), runs a
+ * fused flash-style attention forward on those operands with two-level
+ * quantization of the probabilities and an FP16 path for selected block pairs,
+ * and decodes one token against a KV cache that keeps its first and last
+ * tokens in bf16 and the rest in NVFP4.
+ *
+ * Sources (web pages, cited by title and section):
+ *   ScaleSearch page  -- "Busca tus escalas de punto flotante por bloques":
+ *     Declaracion del Problema (NVFP4 format), Metodologia / ScaleSearch
+ *     (max-scaling and the offset search), Metodologia / ScaleSearchAttention
+ *     (NVFP4 QK^T and PV with FP32 accumulation; sink-aware cache precision).
+ *   ThriftAttention page -- Metodologia / 1 (block means, mean-dot-product
+ *     scores, top-k block pairs) and / 2 (FP16 path for the selected pairs, FP4
+ *     path with two-level P for the others, fused by an online softmax).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are device pointers owned by the caller; option structs
+ *     are host pointers.  The library never allocates, frees or retains caller
+ *     memory.  Scratch memory comes from a caller workspace whose size the
+ *     matching *_workspace_size() query returns (0 means none is needed).
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and the call returns without synchronizing.
+ *   - Arguments are validated before anything is launched.  On error nothing
+ *     runs and a negative status is returned; fp4_last_error() then returns a
+ *     message for the calling thread.  No exception or abort crosses the ABI.
+ *   - Calls that share a workspace buffer must be ordered on one stream.
+ *   - Every option struct starts with struct_size = sizeof(struct), so that
+ *     the struct can grow without breaking callers.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FP4_OK 0
+#define FP4_ERR_INVALID_ARG (-1) /* null pointer, bad shape, bad option */
+#define FP4_ERR_UNSUPPORTED (-2) /* valid request the kernels do not cover (e.g. head dim) */
+#define FP4_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the query returned */
+#define FP4_ERR_HIP (-4)         /* a HIP runtime call failed */
+
+/* element types of high-precision tensors */
+#define FP4_BF16 0
+#define FP4_FP16 1
+#define FP4_FP32 2
+
+/* per-tensor (second-level) scale modes of fp4_quantize */
+#define FP4_GLOBAL_NONE 0  /* g = 1 */
+#define FP4_GLOBAL_AMAX 1  /* g = amax(|x|) / 2688 computed on the device (2688 = 6 * 448) */
+#define FP4_GLOBAL_GIVEN 2 /* g read from *g; elements are multiplied by 1/g first */
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fp4_version(void);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* fp4_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Quantization -- ScaleSearch page, Metodologia / ScaleSearch               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct fp4_quant_opts {
+  uint32_t struct_size; /* sizeof(fp4_quant_opts) */
+  int32_t scale_search; /* 0: max-scaling only; 1: offset search */
+  int32_t f_min;        /* offset search range, -8 <= f_min <= 0 <= f_max <= 8 (default -2, 6) */
+  int32_t f_max;
+  int32_t global_scale; /* FP4_GLOBAL_* */
+  int32_t block_axis;   /* 0: blocks of 16 consecutive columns; 1: of 16 consecutive rows */
+} fp4_quant_opts;
+
+/*
+ * Quantize x [rows, cols] (row stride ld >= cols elements, dtype FP4_BF16,
+ * FP4_FP16 or FP4_FP32) into 16-element blocks.
+ *
+ * Per block: a = max|y| with y = x (or x * 1/g); scale s0 = a/6 rounded to the
+ * nearest E4M3 value (ties to even, saturating at 448).  With scale_search,
+ * candidate scale bytes s0 + f for f in [f_min, f_max] (bytes outside 0..0x7E
+ * skipped) are tried and the one with the least squared error is kept, the
+ * lowest f on ties.  Elements are |y| times the correctly rounded reciprocal
+ * of the scale, rounded to the nearest E2M1 value (ties to even); the sign bit
+ * of y is kept.  A block holding Inf/NaN gets scale byte 0x7F and zero codes.
+ *
+ * Outputs (dense, device):
+ *   block_axis 0: codes [rows, cols/2] (element 2i in the low nibble),
+ *                 scales and offsets [rows, cols/16]
+ *   block_axis 1: codes [rows/2, cols] (row 2i in the low nibble),
+ *                 scales and offsets [rows/16, cols]
+ *   offsets (nullable) receive the chosen f as int8.
+ *   g: FP4_GLOBAL_NONE -- nullable, set to 1.0 when given;
+ *      FP4_GLOBAL_AMAX -- required, receives amax/2688 (1.0 for an all-zero
+ *        tensor; NaN elements are ignored by the maximum);
+ *      FP4_GLOBAL_GIVEN -- required, read (must be finite and > 0).
+ * Requirements: cols % 16 == 0 for block_axis 0, rows % 16 == 0 for
+ * block_axis 1; x, codes, scales 16-byte aligned.  Workspace: see
+ * fp4_quantize_workspace_size (non-zero only for FP4_GLOBAL_AMAX).
+ * Dequantized value: E2M1(code) * E4M3(scale) * g.
+ */
+int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                 const fp4_quant_opts* opts, uint8_t* codes, uint8_t* scales, int8_t* offsets,
+                 float* g, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fp4_quantize_workspace_size(int64_t rows, int64_t cols, const fp4_quant_opts* opts);
+
+/* ------------------------------------------------------------------------ */
+/* Attention forward -- ScaleSearch page, Metodologia / ScaleSearchAttention; */
+/* ThriftAttention page, Metodologia / 1 and 2                               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct fp4_attn_problem {
+  uint32_t struct_size; /* sizeof(fp4_attn_problem) */
+  int64_t B, H, Hkv;    /* batch, query heads, key/value heads (H % Hkv == 0) */
+  int64_t Sq, Sk, d;    /* query / key lengths, head dimension (64 or 128) */
+  int32_t dtype;        /* FP4_BF16 or FP4_FP16 for q, k, v */
+  /* high-precision inputs, dense: q [B,H,Sq,d], k and v [B,Hkv,Sk,d].
+     Needed unless all six quantized arrays below are given; always needed
+     when fp16_budget_pct > 0 (block means and the FP16 path read them). */
+  const void* q;
+  const void* k;
+  const void* v;
+  /* optional NVFP4 operands from fp4_quantize (all six or none), dense:
+     q: codes [B,H,Sq,d/2], scales [B,H,Sq,d/16]      (blocks along d)
+     k: codes [B,Hkv,Sk,d/2], scales [B,Hkv,Sk,d/16]  (blocks along d)
+     v: codes [B,Hkv,Sk/2,d], scales [B,Hkv,Sk/16,d]  (blocks of 16 tokens)
+     When absent they are produced in the workspace with the opts' search. */
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+} fp4_attn_problem;
+
+typedef struct fp4_attn_opts {
+  uint32_t struct_size;    /* sizeof(fp4_attn_opts) */
+  int32_t causal;          /* 1: key j visible to query i iff j <= i (needs Sq == Sk) */
+  float softmax_scale;     /* <= 0 selects 1/sqrt(d) */
+  int32_t kv_tile;         /* 64 or 128 keys: the group of the row-level P scale */
+  int32_t scale_search;    /* quantization of q, k, v done inside the call */
+  int32_t f_min, f_max;
+  int32_t fp16_budget_pct; /* 0..100: share of visible key blocks per query block on the FP16 path */
+  int32_t sel_block;       /* selection block (tokens), 128; multiple of kv_tile */
+  int32_t out_dtype;       /* FP4_BF16, FP4_FP16 or FP4_FP32 */
+} fp4_attn_opts;
+
+/*
+ * out [B,H,Sq,d] = softmax(scale * q k^T) v with fake-quant NVFP4 numerics:
+ * per (query row, key tile) of kv_tile keys, x = fl32(S * log2(e) * scale),
+ * e = 2^(x - tile row max); on the FP4 path the row level maps e = 1 to 2688
+ * and each 16-key block of P takes an E4M3 scale s2 = E4M3(amax(e) * 448)
+ * with elements e * (2688/s2) rounded to E2M1; the tile adds P^ V^ / 2688.
+ * On the FP16 path (selected pairs) the tile adds fp16(e) fp16(v) using
+ * fp16(q) fp16(k) scores.  Tiles merge with an online softmax whose
+ * denominator sums the unquantized e.  lse [B,H,Sq] (nullable) receives the
+ * natural-log sum of exp of the scaled scores.
+ * Selection (fp16_budget_pct > 0): per query block i of sel_block rows, the
+ * visible key blocks j are scored by mean(q_i) . mean(k_j) in binary64 and the
+ * ceil(pct * n_i / 100) best are kept (ties: lower j).  topk_idx
+ * [B,H,ceil(Sq/sel_block),kmax] (ascending, -1 padded, kmax =
+ * ceil(pct * ceil(Sk/sel_block) / 100)) and topk_cnt [B,H,ceil(Sq/sel_block)]
+ * are written when non-null (otherwise kept in the workspace).
+ * Requirements: d in {64, 128}; Sk % 16 == 0; causal needs Sq == Sk;
+ * sel_block % kv_tile == 0; 16-byte aligned tensors.
+ */
+int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out,
+                      float* lse, int32_t* topk_idx, int32_t* topk_cnt, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+size_t fp4_attention_fwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
+
+/* Block selection alone (the first stage of fp4_attention_fwd); needs prob->q
+   and prob->k and fp16_budget_pct > 0.  Outputs as for fp4_attention_fwd. */
+int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int32_t* topk_idx,
+                   int32_t* topk_cnt, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
+
+/* ------------------------------------------------------------------------ */
+/* Decode -- ScaleSearch page, Metodologia / ScaleSearchAttention (cache)    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct fp4_kv_cache {
+  uint32_t struct_size; /* sizeof(fp4_kv_cache) */
+  int64_t B, Hkv, d;    /* batch, key/value heads, head dim (64 or 128) */
+  int32_t n_sink;       /* bf16 tokens at the start of every context */
+  int32_t n_recent;     /* bf16 tokens at the end of every context */
+  int64_t mid_cap;      /* NVFP4 capacity in tokens (multiple of 16) */
+  const void* k_sink;   /* bf16 [B,Hkv,n_sink,d] */
+  const void* v_sink;
+  const uint8_t* k_codes;  /* [B,Hkv,mid_cap,d/2]  blocks along d */
+  const uint8_t* k_scales; /* [B,Hkv,mid_cap,d/16] */
+  const uint8_t* v_codes;  /* [B,Hkv,mid_cap/2,d]  blocks of 16 tokens */
+  const uint8_t* v_scales; /* [B,Hkv,mid_cap/16,d] */
+  const void* k_recent;    /* bf16 [B,Hkv,n_recent,d], oldest first */
+  const void* v_recent;
+  const int32_t* mid_len;  /* device [B]: NVFP4 tokens in use, multiple of 16, <= mid_cap;
+                              the context of batch b is n_sink + mid_len[b] + n_recent tokens */
+} fp4_kv_cache;
+
+/*
+ * One query token per (batch, query head) against the cache: out [B,Hq,d] =
+ * softmax(scale * q K^T) V over sink (bf16), middle (dequantized NVFP4) and
+ * recent (bf16) tokens; query head h reads key/value head h / (Hq / Hkv).
+ * q is bf16 [B,Hq,d] and is not quantized.  lse [B,Hq] is nullable.
+ * mid_len values outside [0, mid_cap] are clamped and rounded down to a
+ * multiple of 16 (no out-of-range reads).  Workspace: see the query.
+ */
+int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* cache, float softmax_scale,
+                         int32_t out_dtype, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* cache);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

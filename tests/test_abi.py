@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/fp4.h declares, and rejects invalid arguments before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_scaled_fp4_amd as fp4
+    if not os.path.exists(fp4.lib_path()):
+        fp4.build()
+    return fp4.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"fp4_quantize", "fp4_attention_fwd", "fp4_attention_decode", "fp4_block_topk"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.fp4_version() == 10000
+
+
+def test_quantize_rejects_bad_arguments(L):
+    import block_scaled_fp4_amd as fp4
+    opts = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 0)
+    fake = C.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    st = L.fp4_quantize(fake, 0, 16, 40, 40, C.byref(opts), fake, fake, None, None, None, 0, None)
+    assert st == -1 and "cols" in L.fp4_last_error().decode()
+    st = L.fp4_quantize(fake, 7, 16, 32, 32, C.byref(opts), fake, fake, None, None, None, 0, None)
+    assert st == -1
+    bad = fp4.QuantOpts(4, 1, -2, 6, 0, 0)
+    assert L.fp4_quantize(fake, 0, 16, 32, 32, C.byref(bad), fake, fake, None, None, None, 0, None) == -1
+    rng = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, 1, 6, 0, 0)
+    assert L.fp4_quantize(fake, 0, 16, 32, 32, C.byref(rng), fake, fake, None, None, None, 0, None) == -1
+    ax1 = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 1)
+    assert L.fp4_quantize(fake, 0, 20, 32, 32, C.byref(ax1), fake, fake, None, None, None, 0, None) == -1
+    amax = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 1, 0)
+    need = L.fp4_quantize_workspace_size(64, 128, C.byref(amax))
+    assert need > 0
+    st = L.fp4_quantize(fake, 0, 64, 128, 128, C.byref(amax), fake, fake, None, fake, fake, need - 1, None)
+    assert st == -3
+    st = L.fp4_quantize(fake, 0, 64, 128, 128, C.byref(amax), fake, fake, None, None, fake, need, None)
+    assert st == -1  # g required
+    mis = C.c_void_p((1 << 20) + 2)
+    assert L.fp4_quantize(mis, 0, 16, 32, 32, C.byref(opts), fake, fake, None, None, None, 0, None) == -1
+
+
+def _prob(fp4, **kw):
+    f = C.c_void_p(1 << 20)
+    P = fp4.AttnProblem(C.sizeof(fp4.AttnProblem), 1, 2, 2, 256, 256, 128, 0, f, f, f)
+    for k, v in kw.items():
+        setattr(P, k, v)
+    return P
+
+
+def _opts(fp4, **kw):
+    O = fp4.AttnOpts(C.sizeof(fp4.AttnOpts), 1, 0.0, 128, 1, -2, 6, 0, 128, 2)
+    for k, v in kw.items():
+        setattr(O, k, v)
+    return O
+
+
+def test_attention_rejects_bad_arguments(L):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+
+    def call(P, O, ws_bytes=1 << 40):
+        return L.fp4_attention_fwd(C.byref(P), C.byref(O), f, None, None, None, f, ws_bytes, None)
+
+    assert call(_prob(fp4, d=96), _opts(fp4)) == -2
+    assert call(_prob(fp4, Sk=250, Sq=250), _opts(fp4)) == -1
+    assert call(_prob(fp4, Sq=128), _opts(fp4)) == -1            # causal needs Sq == Sk
+    assert call(_prob(fp4, H=3, Hkv=2), _opts(fp4)) == -1
+    assert call(_prob(fp4), _opts(fp4, kv_tile=32)) == -2
+    assert call(_prob(fp4), _opts(fp4, fp16_budget_pct=101)) == -1
+    assert call(_prob(fp4), _opts(fp4, fp16_budget_pct=10, sel_block=192)) == -1
+    assert call(_prob(fp4), _opts(fp4, fp16_budget_pct=10, sel_block=64, kv_tile=64)) == -1
+    assert call(_prob(fp4, dtype=2), _opts(fp4)) == -2
+    assert call(_prob(fp4, q_codes=f), _opts(fp4)) == -1          # partial quantized set
+    assert call(_prob(fp4), _opts(fp4), ws_bytes=0) == -3
+    assert L.fp4_attention_fwd(None, None, f, None, None, None, f, 0, None) == -1
+    assert L.fp4_block_topk(C.byref(_prob(fp4)), C.byref(_opts(fp4)), f, f, f, 1 << 30, None) == -1  # pct 0
+
+
+def test_decode_rejects_bad_arguments(L):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+    cs = fp4.KVCacheStruct(C.sizeof(fp4.KVCacheStruct), 2, 2, 128, 16, 32, 100, f, f, f, f, f, f, f, f, f)
+    assert L.fp4_attention_decode(f, 8, C.byref(cs), 0.0, 2, f, None, f, 1 << 30, None) == -1  # mid_cap % 16
+    cs.mid_cap = 96
+    assert L.fp4_attention_decode(f, 7, C.byref(cs), 0.0, 2, f, None, f, 1 << 30, None) == -1  # Hq % Hkv
+    assert L.fp4_attention_decode(f, 64, C.byref(cs), 0.0, 2, f, None, f, 1 << 30, None) == -2  # G > 16
+    cs.d = 80
+    assert L.fp4_attention_decode(f, 8, C.byref(cs), 0.0, 2, f, None, f, 1 << 30, None) == -2
+    cs.d = 128
+    need = L.fp4_attention_decode_workspace_size(8, C.byref(cs))
+    assert need > 0
+    assert L.fp4_attention_decode(f, 8, C.byref(cs), 0.0, 2, f, None, f, need - 1, None) == -3

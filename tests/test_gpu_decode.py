@@ -1,0 +1,97 @@
+"""GPU decode parity over the sink-aware mixed-precision KV cache (ScaleSearch
+page, Metodologia / ScaleSearchAttention): bf16 sink and recent tokens, NVFP4
+middle (ScaleSearch, K blocks along d, V blocks of 16 tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp4_amd import synth
+from gpu_helpers import assert_close_attn, case
+
+pytestmark = pytest.mark.gpu
+
+
+def build_cache(fp4, k, v, ctx, n_sink, n_recent, mid_cap):
+    """Fill the cache buffers on the GPU from the full bf16 context k, v [B,Hkv,L,d]."""
+    B, Hkv, Lcap, d = k.shape
+    dev = k.device
+    kc = torch.zeros((B, Hkv, mid_cap, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Hkv, mid_cap, d // 16), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((B, Hkv, mid_cap // 2, d), dtype=torch.uint8, device=dev)
+    vs = torch.zeros((B, Hkv, mid_cap // 16, d), dtype=torch.uint8, device=dev)
+    k_sink = k[:, :, :n_sink].contiguous()
+    v_sink = v[:, :, :n_sink].contiguous()
+    k_rec = torch.zeros((B, Hkv, n_recent, d), dtype=k.dtype, device=dev)
+    v_rec = torch.zeros((B, Hkv, n_recent, d), dtype=k.dtype, device=dev)
+    mids = []
+    for b in range(B):
+        L = int(ctx[b])
+        M = L - n_sink - n_recent
+        assert M >= 0 and M % 16 == 0 and M <= mid_cap
+        mids.append(M)
+        k_rec[b] = k[b, :, L - n_recent:L]
+        v_rec[b] = v[b, :, L - n_recent:L]
+        if M:
+            km = k[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
+            vm = v[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
+            rk = fp4.fp4_quantize(km, 0, True)
+            rv = fp4.fp4_quantize(vm, 1, True)
+            kc[b, :, :M] = rk["codes"].view(Hkv, M, d // 2)
+            ks[b, :, :M] = rk["scales"].view(Hkv, M, d // 16)
+            vc[b, :, :M // 2] = rv["codes"].view(Hkv, M // 2, d)
+            vs[b, :, :M // 16] = rv["scales"].view(Hkv, M // 16, d)
+    mid_len = torch.tensor(mids, dtype=torch.int32, device=dev)
+    return fp4.KVCache(k_sink, v_sink, kc, ks, vc, vs, k_rec, v_rec, mid_len)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_small_cache(gpu, d):
+    B, Hq, Hkv = 3, 8, 2
+    n_sink, n_recent, cap = 16, 32, 400
+    L = n_sink + cap + n_recent
+    q, k, v = synth.decode_context(B, Hq, Hkv, L, d)
+    ctx = [L, n_sink + n_recent + 16 * 7, n_sink + n_recent]   # full, partial, empty middle
+    case(f"decode small d={d}")
+    cache = build_cache(gpu, k.cuda(), v.cuda(), ctx, n_sink, n_recent, cap)
+    out, lse = gpu.fp4_attention_decode(q.cuda(), cache, out_dtype=gpu.FP32)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attention_decode(q, k, v, ctx, n_sink, n_recent)
+    assert_close_attn(out.cpu().numpy().reshape(-1, d), ref.reshape(-1, d), "decode small")
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(-1), rlse.reshape(-1), atol=1e-3)
+
+
+def test_gqa_group_of_one_and_sixteen(gpu):
+    for Hq, Hkv in ((4, 4), (16, 1)):
+        n_sink, n_recent, cap = 32, 64, 256
+        L = n_sink + cap + n_recent
+        q, k, v = synth.decode_context(2, Hq, Hkv, L, 128, seed=20)
+        ctx = [L, L - 128]
+        case(f"decode Hq={Hq} Hkv={Hkv}")
+        cache = build_cache(gpu, k.cuda(), v.cuda(), ctx, n_sink, n_recent, cap)
+        out, _ = gpu.fp4_attention_decode(q.cuda(), cache, out_dtype=gpu.FP32)
+        torch.cuda.synchronize()
+        ref, _ = oracle.attention_decode(q, k, v, ctx, n_sink, n_recent)
+        assert_close_attn(out.cpu().numpy().reshape(-1, 128), ref.reshape(-1, 128), f"decode G={Hq // Hkv}")
+
+
+def test_decode_workload_sampled_pairs(gpu):
+    """batch 16, 32 q heads / 8 kv heads, context 131072, d 128, sink 128 + recent 256 bf16."""
+    B, Hq, Hkv, L, d = 16, 32, 8, 131072, 128
+    n_sink, n_recent = 128, 256
+    cap = L - n_sink - n_recent
+    case("decode full workload: generating context on GPU")
+    q, k, v = synth.decode_context(B, Hq, Hkv, L, d, device="cuda")
+    ctx = [L] * B
+    cache = build_cache(gpu, k, v, ctx, n_sink, n_recent, cap)
+    case("decode full workload: kernel")
+    out, lse = gpu.fp4_attention_decode(q, cache, out_dtype=gpu.FP32)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (15, 7)]
+    G = Hq // Hkv
+    for b, hk in pairs:
+        ref, rlse = oracle.attention_decode(q[b:b + 1, hk * G:(hk + 1) * G].cpu(), k[b:b + 1, hk:hk + 1].cpu(),
+                                            v[b:b + 1, hk:hk + 1].cpu(), [L], n_sink, n_recent)
+        got = out[b, hk * G:(hk + 1) * G].cpu().numpy()
+        assert_close_attn(got, ref.reshape(G, d), f"decode pair b={b} kvh={hk}")
+        np.testing.assert_allclose(lse[b, hk * G:(hk + 1) * G].cpu().numpy(), rlse.reshape(G), atol=1e-3)

@@ -1,0 +1,92 @@
+"""GPU quantizer parity: codes, scales, offsets and the per-tensor scale must be
+bit-exact to the oracle (ScaleSearch page, Metodologia / ScaleSearch)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp4_amd import synth
+from gpu_helpers import case
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(fp4, x_cpu, axis, search, gmode=0, g=None, fmin=-2, fmax=6):
+    x = x_cpu.cuda()
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda") if g is not None else None
+    r = fp4.fp4_quantize(x, block_axis=axis, scale_search=search, f_min=fmin, f_max=fmax, global_scale=gmode, g=gt)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x_cpu, axis, search, fmin, fmax, gmode, g if g is not None else 1.0)
+    codes = r["codes"].cpu().numpy()
+    scales = r["scales"].cpu().numpy()
+    offs = r["offsets"].cpu().numpy()
+    np.testing.assert_array_equal(scales, o["scales"])
+    np.testing.assert_array_equal(offs, o["offsets"])
+    np.testing.assert_array_equal(codes, o["codes"])
+    if gmode != 0:
+        assert r["g"].item() == np.float32(o["g"])
+    return r
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("search", [False, True])
+def test_small_shapes_bit_exact(gpu, dtype, axis, search):
+    g = torch.Generator().manual_seed(11)
+    rows, cols = (48, 80) if axis == 1 else (37, 96)
+    x = (torch.randn(rows, cols, generator=g) * torch.logspace(-3, 3, cols)).to(dtype)
+    case(f"quantize small {dtype} axis={axis} search={search}")
+    _run(gpu, x, axis, search)
+
+
+@pytest.mark.parametrize("gmode", [1, 2])
+def test_global_scale_modes(gpu, gmode):
+    g = torch.Generator().manual_seed(12)
+    x = (torch.randn(64, 128, generator=g) * 30).to(torch.bfloat16)
+    case(f"quantize global mode {gmode}")
+    _run(gpu, x, 0, True, gmode=gmode, g=0.0123 if gmode == 2 else None)
+    _run(gpu, x, 1, True, gmode=gmode, g=0.0123 if gmode == 2 else None)
+
+
+def test_special_values(gpu):
+    x = torch.zeros(32, 64, dtype=torch.float32)
+    x[0, :16] = -0.0
+    x[1, 3] = float("inf")
+    x[2, 20] = float("nan")
+    x[3, :16] = torch.tensor([2.0 ** -140] * 16)          # scale underflows to 0
+    x[4, :16] = 1e30                                       # saturates at 448
+    x[5, :16] = torch.arange(16) * 0.25                    # exact grid midpoints
+    x[6, :16] = 1.0                                        # worked example -> byte 0x28
+    x[7, 16:32] = torch.tensor([6.0, -6.0] * 8) * 448      # top of the range
+    case("quantize special values")
+    r = _run(gpu, x, 0, True)
+    assert r["scales"][6, 0].item() == 0x28
+    _run(gpu, x, 0, False)
+    _run(gpu, x.t().contiguous(), 1, True)
+
+
+def test_offset_ranges(gpu):
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn(64, 64, generator=g).to(torch.bfloat16)
+    for fmin, fmax in ((-8, 8), (0, 0), (-1, 3), (0, 6)):
+        case(f"quantize offset range [{fmin},{fmax}]")
+        _run(gpu, x, 0, True, fmin=fmin, fmax=fmax)
+
+
+def test_quantizer_workload_full_size(gpu):
+    """bf16 [32768, 128] with 2% outlier channels x20, ScaleSearch, per-tensor amax scale."""
+    x = synth.quant_tensor()
+    case("quantize full workload 32768x128 bf16 amax scalesearch")
+    r = _run(gpu, x, 0, True, gmode=1)
+    # run twice: bitwise deterministic
+    r2 = gpu.fp4_quantize(x.cuda(), 0, True, -2, 6, gpu.GLOBAL_AMAX)
+    torch.cuda.synchronize()
+    assert torch.equal(r["codes"], r2["codes"]) and torch.equal(r["scales"], r2["scales"])
+
+
+def test_empty_input(gpu):
+    x = torch.zeros(0, 32, dtype=torch.bfloat16, device="cuda")
+    case("quantize empty")
+    r = gpu.fp4_quantize(x, 0, True, -2, 6, gpu.GLOBAL_AMAX)
+    torch.cuda.synchronize()
+    assert r["codes"].numel() == 0 and r["g"].item() == 1.0
