@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP4 attention hot path on one MI355X.
+
+A step is one pass of the whole forward hot path over one batch of synthetic
+input: ScaleSearch quantization of Q, K and V, block selection (means, scores,
+top-k) and the fused FP4/FP16 attention forward -- the selective workload
+B=1, H=32, S=32768, d=128, causal, top 10% of 128x128 block pairs in FP16.
+`value` is attention TFLOP/s of that step (causal convention
+4*B*H*S^2*d/2 flops).  The same JSON line carries the roofline of the dominant
+kernel (the attention kernel alone, timed with HIP events on its stream), the
+other hot-path components (8K prefill, the quantizer, FP4-KV decode) and the
+C oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP4 attention fwd TFLOP/s (S=8K/32K, d=128) + quantizer GB/s, % of roofline"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+FP16_MFMA_PEAK_TF = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(B, H, S, d, causal=True):
+    f = 4.0 * B * H * S * S * d
+    return f / 2 if causal else f
+
+
+def source_hash(name):
+    p = os.path.join(ROOT, "block_scaled_fp4_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(tag, kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    p = os.path.join(PROFILES, f"{tag}_traffic.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_hash(kernel_src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, n, warm=1):
+        torch = self.torch
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms per call
+
+
+def bench_select32k(fp4, synth, torch, steps, warmup):
+    B, H, S, d = 1, 32, 32768, 128
+    log("generating selective workload S=32768")
+    q, k, v = (t.cuda() for t in synth.prefill(S=S))
+    out = torch.empty_like(q)
+    ws_bytes = fp4.attention_fwd_workspace_bytes((B, H, S, d), (H, S), causal=True, fp16_budget_pct=10)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        fp4.fp4_attention_fwd(q, k, v, causal=True, kv_tile=128, scale_search=True, fp16_budget_pct=10,
+                              out_dtype=fp4.BF16, return_lse=False, workspace=ws, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record(st)
+    for _ in range(steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    ms = e0.elapsed_time(e1) / steps
+    flops = attn_flops(B, H, S, d)
+    # dominant kernel alone: pre-quantized operands and a precomputed selection
+    quant, sel = prequantize(fp4, q, k, v, torch, pct=10)
+    timer = Timer(torch)
+
+    def kern():
+        fp4.fp4_attention_fwd(q, k, v, causal=True, kv_tile=128, fp16_budget_pct=10, out_dtype=fp4.BF16,
+                              quantized=quant, selection=sel, return_lse=False, out=out)
+
+    kms = timer.run(kern, max(3, steps // 2))
+    return dict(ms=ms, wall=wall, flops=flops, kernel_ms=kms, q=q, k=k, v=v)
+
+
+def prequantize(fp4, q, k, v, torch, pct=0):
+    B, H, S, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    rq = fp4.fp4_quantize(q.view(-1, d), 0, True, with_offsets=False)
+    rk = fp4.fp4_quantize(k.view(-1, d), 0, True, with_offsets=False)
+    rv = fp4.fp4_quantize(v.view(-1, d), 1, True, with_offsets=False)
+    quant = dict(q_codes=rq["codes"], q_scales=rq["scales"], k_codes=rk["codes"], k_scales=rk["scales"],
+                 v_codes=rv["codes"], v_scales=rv["scales"], q_shape=(B, H, S, d), kv_shape=(Hkv, Sk))
+    sel = fp4.fp4_block_topk(q, k, True, pct, 128) if pct > 0 else None
+    if sel is not None:
+        sel = (sel[0].contiguous(), sel[1].contiguous())
+    torch.cuda.synchronize()
+    return quant, sel
+
+
+def bench_prefill8k(fp4, synth, torch, n):
+    B, H, S, d = 1, 32, 8192, 128
+    q, k, v = (t.cuda() for t in synth.prefill(S=S))
+    out = torch.empty_like(q)
+    timer = Timer(torch)
+    e2e = timer.run(lambda: fp4.fp4_attention_fwd(q, k, v, causal=True, kv_tile=128, out_dtype=fp4.BF16,
+                                                  return_lse=False, out=out), n)
+    quant, _ = prequantize(fp4, q, k, v, torch)
+    kern = timer.run(lambda: fp4.fp4_attention_fwd(None, None, None, causal=True, kv_tile=128, out_dtype=fp4.BF16,
+                                                   quantized=quant, return_lse=False, out=out), n)
+    fl = attn_flops(B, H, S, d)
+    return dict(workload="prefill B=1 H=32 S=8192 d=128 causal, ScaleSearch Q/K/V, two-level P, kv_tile 128",
+                end_to_end_ms=round(e2e, 4), end_to_end_tflops=round(fl / e2e / 1e9, 2),
+                attn_kernel_ms=round(kern, 4), attn_kernel_tflops=round(fl / kern / 1e9, 2),
+                attn_kernel_frac_fp16_mfma=round(fl / kern / 1e9 / FP16_MFMA_PEAK_TF, 4))
+
+
+def bench_quantizer(fp4, synth, torch, n):
+    rows, cols = 32768, 128
+    algo = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4  # bf16 in, codes, scales, g
+    x = synth.quant_tensor().cuda()
+    timer = Timer(torch)
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda")
+    outd = dict(codes=codes, scales=scales, offsets=None)
+    hot = timer.run(lambda: fp4.fp4_quantize(x, 0, True, -2, 6, fp4.GLOBAL_AMAX, g=g, out=outd), n)
+    # cold: rotate over 48 distinct inputs (384 MiB) so each call reads from HBM, not the 256 MB MALL
+    pool = [x.roll(i + 1, 0) for i in range(48)]
+    it = [0]
+
+    def cold_call():
+        fp4.fp4_quantize(pool[it[0] % 48], 0, True, -2, 6, fp4.GLOBAL_AMAX, g=g, out=outd)
+        it[0] += 1
+
+    cold = timer.run(cold_call, 48 * max(1, n // 8), warm=48)
+    # max-scaling only, same cold pool
+    it[0] = 0
+
+    def cold_max():
+        fp4.fp4_quantize(pool[it[0] % 48], 0, False, -2, 6, fp4.GLOBAL_AMAX, g=g, out=outd)
+        it[0] += 1
+
+    coldm = timer.run(cold_max, 48 * max(1, n // 8), warm=48)
+    del pool
+    # asymptotic: 64x rows (2M x 128 bf16 = 512 MiB)
+    big = synth.quant_tensor(rows=rows * 64).cuda()
+    bc = torch.empty((rows * 64, cols // 2), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((rows * 64, cols // 16), dtype=torch.uint8, device="cuda")
+    bo = dict(codes=bc, scales=bs, offsets=None)
+    big_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_AMAX, g=g, out=bo), max(3, n // 4))
+    big_algo = algo * 64 - 4 * 63
+    return dict(workload="bf16 [32768,128], 2% outlier channels x20, ScaleSearch f in [-2,6], per-tensor amax scale",
+                algorithmic_bytes=algo,
+                cold_us=round(cold * 1e3, 2), cold_GBps=round(algo / cold / 1e6, 1),
+                cold_frac_hbm=round(algo / cold / 1e6 / HBM_PEAK_GBS, 4),
+                hot_us=round(hot * 1e3, 2), hot_GBps=round(algo / hot / 1e6, 1),
+                max_scaling_only_cold_GBps=round(algo / coldm / 1e6, 1),
+                rows_x64_ms=round(big_ms, 4), rows_x64_GBps=round(big_algo / big_ms / 1e6, 1),
+                rows_x64_frac_hbm=round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4))
+
+
+def bench_decode(fp4, synth, torch, n):
+    B, Hq, Hkv, L, d = 16, 32, 8, 131072, 128
+    n_sink, n_recent = 128, 256
+    M = L - n_sink - n_recent
+    log("building decode cache (context 131072)")
+    q, k, v = synth.decode_context(B, Hq, Hkv, L, d, device="cuda")
+    kc = torch.empty((B, Hkv, M, d // 2), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, Hkv, M, d // 16), dtype=torch.uint8, device="cuda")
+    vc = torch.empty((B, Hkv, M // 2, d), dtype=torch.uint8, device="cuda")
+    vs = torch.empty((B, Hkv, M // 16, d), dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        km = k[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
+        vm = v[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
+        rk = fp4.fp4_quantize(km, 0, True, with_offsets=False)
+        rv = fp4.fp4_quantize(vm, 1, True, with_offsets=False)
+        kc[b] = rk["codes"].view(Hkv, M, d // 2)
+        ks[b] = rk["scales"].view(Hkv, M, d // 16)
+        vc[b] = rv["codes"].view(Hkv, M // 2, d)
+        vs[b] = rv["scales"].view(Hkv, M // 16, d)
+    cache = fp4.KVCache(k[:, :, :n_sink].contiguous(), v[:, :, :n_sink].contiguous(), kc, ks, vc, vs,
+                        k[:, :, L - n_recent:].contiguous(), v[:, :, L - n_recent:].contiguous(),
+                        torch.full((B,), M, dtype=torch.int32, device="cuda"))
+    del k, v
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    timer = Timer(torch)
+    ms = timer.run(lambda: fp4.fp4_attention_decode(q, cache, out_dtype=fp4.BF16, return_lse=False, out=out), n)
+    kv_bytes = B * Hkv * (M * (d // 2 + d // 16) * 2 + (n_sink + n_recent) * d * 2 * 2)
+    qo = B * Hq * d * 2 * 2
+    algo = kv_bytes + qo
+    return dict(workload="decode batch 16, 32 q / 8 kv heads, context 131072, d 128, 128 sink + 256 recent bf16",
+                algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(algo / ms / 1e6, 1),
+                frac_hbm=round(algo / ms / 1e6 / HBM_PEAK_GBS, 4))
+
+
+def cpu_baseline(q, k, v):
+    """The C oracle on heads 0 and 1 of the step workload: ScaleSearch
+    quantization of each head's Q/K/V, block means and top-10% selection, and
+    every query row."""
+    import numpy as np
+
+    import oracle
+    S, d = q.shape[2], q.shape[3]
+    qh, kh, vh = q[:, :2].cpu(), k[:, :2].cpu(), v[:, :2].cpu()
+    t0 = time.time()
+    oracle.attention_fwd(qh, kh, vh, causal=True, kv_tile=128, pct=10, sel_block=128)
+    dt = time.time() - t0
+    fl = 2 * attn_flops(1, 1, S, d)
+    return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
+                seconds=round(dt, 2),
+                sample=f"heads 0 and 1 of the 32K selective workload (2 of 32): ScaleSearch quantization of "
+                       f"Q/K/V, block means and top-10% selection, all {S} query rows ({fl:.3e} attention flops)")
+
+
+def pmc_mode(mode, fp4, synth, torch):
+    """Short runs for rocprofv3 --pmc: the dominant kernels and a plain copy of known size."""
+    if mode == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_mode": "copy", "bytes_read": n, "bytes_written": n}))
+        return
+    if mode == "attn":
+        q, k, v = (t.cuda() for t in synth.prefill(S=32768))
+        quant, sel = prequantize(fp4, q, k, v, torch, pct=10)
+        out = torch.empty_like(q)
+        for _ in range(3):
+            fp4.fp4_attention_fwd(q, k, v, causal=True, kv_tile=128, fp16_budget_pct=10, out_dtype=fp4.BF16,
+                                  quantized=quant, selection=sel, return_lse=False, out=out)
+        torch.cuda.synchronize()
+    elif mode == "quant":
+        x = synth.quant_tensor().cuda()
+        for _ in range(3):
+            fp4.fp4_quantize(x, 0, True, -2, 6, fp4.GLOBAL_AMAX, with_offsets=False)
+        torch.cuda.synchronize()
+    print(json.dumps({"pmc_mode": mode}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md but not run", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_fp4_amd as fp4
+    from block_scaled_fp4_amd import synth
+    if not os.path.exists(fp4.lib_path()):
+        fp4.build()
+    fp4.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.pmc_mode:
+        pmc_mode(args.pmc_mode, fp4, synth, torch)
+        return
+    res = bench_select32k(fp4, synth, torch, args.steps, args.warmup)
+    value = res["flops"] / res["ms"] / 1e9
+    kern_tf = res["flops"] / res["kernel_ms"] / 1e9
+    traffic = read_traffic("attn_fwd_select32k", "attn_fwd.hip")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "operands": "NVFP4 (E2M1 + E4M3 per 16) dequantized exactly to fp16 MFMA operands, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "selective-32K: B=1 H=32 S=32768 d=128 causal, bf16 N(0,1) with 4 K outlier "
+                               "channels x10 per head; ScaleSearch Q/K/V, two-level P, kv_tile 128, top 10% of "
+                               "128x128 block pairs per query block on the FP16 path; step = quantize + select "
+                               "+ attention",
+                   "B": 1, "H": 32, "S": 32768, "d": 128, "causal": True, "fp16_budget_pct": 10},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<128,128>",
+                     "achieved": round(kern_tf, 2), "peak": FP16_MFMA_PEAK_TF, "unit": "TFLOP/s",
+                     "frac": round(kern_tf / FP16_MFMA_PEAK_TF, 4),
+                     "kernel_ms": round(res["kernel_ms"], 4), "algorithmic_flops": res["flops"],
+                     "traffic": traffic},
+    }
+    if not args.no_components:
+        log("components: prefill 8K")
+        line["components"] = {"prefill_8k": bench_prefill8k(fp4, synth, torch, max(5, args.steps))}
+        log("components: quantizer")
+        line["components"]["quantizer"] = bench_quantizer(fp4, synth, torch, max(8, args.steps))
+        log("components: decode")
+        line["components"]["decode"] = bench_decode(fp4, synth, torch, max(5, args.steps))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(res["q"], res["k"], res["v"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

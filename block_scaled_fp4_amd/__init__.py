@@ -51,7 +51,7 @@ class AttnOpts(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("causal", C.c_int32), ("softmax_scale", C.c_float),
                 ("kv_tile", C.c_int32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
                 ("f_max", C.c_int32), ("fp16_budget_pct", C.c_int32), ("sel_block", C.c_int32),
-                ("out_dtype", C.c_int32)]
+                ("out_dtype", C.c_int32), ("selection_given", C.c_int32)]
 
 
 class KVCacheStruct(C.Structure):
@@ -182,9 +182,9 @@ def _problem(q, k, v, quant=None):
     return P
 
 
-def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype):
+def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype, given=False):
     return AttnOpts(C.sizeof(AttnOpts), int(bool(causal)), float(softmax_scale), kv_tile,
-                    int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype)
+                    int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype, int(bool(given)))
 
 
 def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile=128):
@@ -209,11 +209,12 @@ def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile
 
 def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
                       f_max=6, fp16_budget_pct=0, sel_block=128, out_dtype=BF16, quantized=None,
-                      return_lse=True, return_topk=False, workspace=None, out=None):
+                      return_lse=True, return_topk=False, workspace=None, out=None, selection=None):
     """FP4 attention forward.  q [B,H,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp16).
 
     quantized: optional dict with q_codes..v_scales from fp4_quantize (then q/k/v
-    may be None when fp16_budget_pct == 0).  Returns (out, lse[, idx, cnt])."""
+    may be None when fp16_budget_pct == 0).  selection: optional (idx, cnt) from
+    fp4_block_topk, used instead of computing one.  Returns (out, lse[, idx, cnt])."""
     L = load()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
@@ -224,12 +225,17 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
     else:
         B, H, Sq, d = quantized["q_shape"]
     P = _problem(q, k, v, quantized)
-    O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype)
+    O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype,
+              selection is not None)
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
     idx = cnt = None
-    if return_topk and fp16_budget_pct > 0:
+    if selection is not None:
+        idx, cnt = selection
+        _dev(idx, "selection idx")
+        _dev(cnt, "selection cnt")
+    elif return_topk and fp16_budget_pct > 0:
         Sk = P.Sk
         nqb = (Sq + sel_block - 1) // sel_block
         nkb = (Sk + sel_block - 1) // sel_block

@@ -69,11 +69,11 @@ AttnPlan plan_attn(const fp4_attn_problem* p, const fp4_attn_opts* o) {
   AttnPlan P{};
   const int64_t B = p->B, H = p->H, Hkv = p->Hkv, Sq = p->Sq, Sk = p->Sk, d = p->d;
   P.need_quant = !(p->q_codes && p->q_scales && p->k_codes && p->k_scales && p->v_codes && p->v_scales);
-  P.need_sel = o->fp16_budget_pct > 0;
+  P.need_sel = o->fp16_budget_pct > 0 && !o->selection_given;
   const int sb = o->sel_block > 0 ? o->sel_block : 128;
   P.nqb = (int)((Sq + sb - 1) / sb);
   P.nkb = (int)((Sk + sb - 1) / sb);
-  P.kmax = P.need_sel ? (o->fp16_budget_pct * P.nkb + 99) / 100 : 0;
+  P.kmax = o->fp16_budget_pct > 0 ? (o->fp16_budget_pct * P.nkb + 99) / 100 : 0;
   size_t off = 0;
   auto take = [&](size_t n) { size_t at = off; off += align256(n); return at; };
   if (P.need_quant) {
@@ -119,6 +119,8 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
   if (o->fp16_budget_pct > 0 && (!p->q || !p->k || !p->v))
     return fail(FP4_ERR_INVALID_ARG, "%s: the FP16 path needs the high-precision q, k, v", fn);
   if (for_topk && o->fp16_budget_pct == 0) return fail(FP4_ERR_INVALID_ARG, "%s: fp16_budget_pct is 0", fn);
+  if (o->selection_given != 0 && o->selection_given != 1)
+    return fail(FP4_ERR_INVALID_ARG, "%s: selection_given must be 0 or 1", fn);
   if (o->scale_search != 0 && o->scale_search != 1) return fail(FP4_ERR_INVALID_ARG, "%s: scale_search must be 0 or 1", fn);
   if (o->scale_search && (o->f_min > 0 || o->f_max < 0 || o->f_min < -8 || o->f_max > 8))
     return fail(FP4_ERR_INVALID_ARG, "%s: need -8 <= f_min <= 0 <= f_max <= 8", fn);
@@ -196,7 +198,9 @@ size_t fp4_attention_fwd_workspace_size(const fp4_attn_problem* prob, const fp4_
 size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
   if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
     return 0;
-  AttnPlan P = plan_attn(prob, opts);
+  fp4_attn_opts o2 = *opts;
+  o2.selection_given = 0;
+  AttnPlan P = plan_attn(prob, &o2);
   if (!P.need_sel) return 0;
   return P.total - P.qm;  // the selection part only
 }
@@ -224,9 +228,12 @@ int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int3
   int st = check_attn(prob, opts, "fp4_block_topk", true);
   if (st) return st;
   if (!prob->q || !prob->k) return fail(FP4_ERR_INVALID_ARG, "fp4_block_topk: q and k are required");
-  AttnPlan P = plan_attn(prob, opts);
+  fp4_attn_opts o2 = *opts;
+  o2.selection_given = 0;
+  AttnPlan P = plan_attn(prob, &o2);
   size_t need = P.total - P.qm;
   if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "fp4_block_topk: workspace needs %zu bytes", need);
+  if (!topk_idx || !topk_cnt) return fail(FP4_ERR_INVALID_ARG, "fp4_block_topk: topk_idx and topk_cnt are required");
   return launch_selection(prob, opts, P, (char*)workspace, topk_idx, topk_cnt, (hipStream_t)stream);
 }
 
@@ -273,7 +280,12 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   }
   const int32_t* idx = nullptr;
   const int32_t* cnt = nullptr;
-  if (P.need_sel) {
+  if (opts->fp16_budget_pct > 0 && opts->selection_given) {
+    if (!topk_idx || !topk_cnt)
+      return fail(FP4_ERR_INVALID_ARG, "fp4_attention_fwd: selection_given needs topk_idx and topk_cnt");
+    idx = topk_idx;
+    cnt = topk_cnt;
+  } else if (P.need_sel) {
     st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s);
     if (st) return st;
     idx = topk_idx ? topk_idx : (const int32_t*)(ws + P.idx);

@@ -250,15 +250,26 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const I
   }
 }
 
-// Per-wave state.
+// Per-wave state.  The output accumulator U is kept relative to a per-row
+// reference exponent `ref` (the max of the last tile merged): the true
+// unnormalized output is U * 2^ref and the denominator l * 2^ref, so the PV
+// MFMA of a tile accumulates straight into U after one rescale of U by
+// 2^(ref_old - tm).  FP4 tiles add P^ V^ (P^ is in units of 1/2688 of e);
+// the switch to FP16 tiles rescales U by 1/2688 once.
 template <int D>
 struct RowState {
-  float16_t o[D / 32];  // O^T accumulators: d rows (i%4)+8(i/4)+4(lane/32) of 32-row group, query lane%32
-  float m;              // running max (x units), shared by lanes l and l^32
+  float16_t o[D / 32];  // U^T: d rows (i%4)+8(i/4)+4(lane/32) of each 32-row group, query lane%32
+  float m;              // running max of tile maxima (x units), shared by lanes l and l^32
+  float ref;            // reference exponent of o and l
   float l;              // this lane's part of the denominator
 };
 
-// Process one tile for one wave.  fp4: two-level P; else fp16(e).
+// Tiles whose maximum is this far (in log2 units) below the running maximum
+// weigh less than 2^-64 of the row and are left out; this bounds the rescale
+// factor of U by 2^64.
+constexpr float kSkipBelow = 64.0f;
+
+// Process one tile for one wave.  FP4: two-level P; else fp16(e).
 template <int D, int BC, bool FP4, bool MASK>
 __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
                                           int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
@@ -293,22 +304,35 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       tm = __builtin_fmaxf(tm, x);
     }
   tm = __builtin_fmaxf(tm, xor32(tm));
-  const bool live = tm > -__builtin_inff();
-  const float mnew = live ? __builtin_fmaxf(R.m, tm) : R.m;
-  // e = 2^(x - tm); masked keys give 0; sum into l
+  const float mnew = __builtin_fmaxf(R.m, tm);
+  const bool use = tm > -__builtin_inff() && tm >= mnew - kSkipBelow;
+  R.m = mnew;
+  if (!__any(use)) return;  // no row of this wave takes the tile
+  // rescale U and l to the new reference tm (rows that skip keep theirs)
+  {
+    const float f = use ? __builtin_amdgcn_exp2f(R.ref - tm) : 1.0f;  // ref = -inf on the first tile -> 0
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) R.o[t][i] = R.o[t][i] * f;
+    R.l = R.l * f;
+    if (use) R.ref = tm;
+  }
+  // e = 2^(x - tm); masked keys and skipping rows give 0
   float lsum = 0.0f;
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float e = live ? __builtin_amdgcn_exp2f(acc[g][i] - tm) : 0.0f;
+      const float e = use ? __builtin_amdgcn_exp2f(acc[g][i] - tm) : 0.0f;
       acc[g][i] = e;
       lsum += e;
     }
-  // P operands: step (g, h2) takes this lane's values i = 8*h2 .. 8*h2+7
-  half8_t pf[NG][2];
+  R.l += lsum;
+  // per 32-key subtile: P operands (this lane's values i = 8*h2 .. +8), then U^T += V^T P^T
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
+    half8_t pf[2];
     if (FP4) {
       float amax = 0.0f;
 #pragma unroll
@@ -328,40 +352,22 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
         w = cvt_pk_fp4<3>(w, t[6], t[7]);
         half2_t a = scale_pair(cvt_pk_f16_fp4<0>(w), s2), b = scale_pair(cvt_pk_f16_fp4<1>(w), s2);
         half2_t cc = scale_pair(cvt_pk_f16_fp4<2>(w), s2), d2 = scale_pair(cvt_pk_f16_fp4<3>(w), s2);
-        pf[g][h2] = half8_t{a[0], a[1], b[0], b[1], cc[0], cc[1], d2[0], d2[1]};
+        pf[h2] = half8_t{a[0], a[1], b[0], b[1], cc[0], cc[1], d2[0], d2[1]};
       }
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[g][h2][i] = (half_t)acc[g][8 * h2 + i];
+        for (int i = 0; i < 8; ++i) pf[h2][i] = (half_t)acc[g][8 * h2 + i];
     }
-  }
-  // Otile^T = V^T P^T into the (now free) score accumulators, then merge
-  float16_t ot[D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) ot[t] = float16_t{0};
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
         const half8_t a = *reinterpret_cast<const half8_t*>(S.v + (32 * t + (lane & 31)) * Smem<D, BC>::VS +
                                                             32 * g + 16 * h2 + 8 * hi);
-        ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[g][h2], ot[t], 0, 0, 0);
+        R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[h2], R.o[t], 0, 0, 0);
       }
-    }
-  if (live) {
-    const float alpha = __builtin_amdgcn_exp2f(R.m - mnew);  // R.m = -inf on the first live tile -> 0
-    const float w = __builtin_amdgcn_exp2f(tm - mnew) * (FP4 ? (1.0f / 2688.0f) : 1.0f);
-    const float rt = __builtin_amdgcn_exp2f(tm - mnew);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) R.o[t][i] = __builtin_fmaf(ot[t][i], w, R.o[t][i] * alpha);
-    R.l = R.l * alpha + rt * lsum;
-    R.m = mnew;
   }
 }
 
@@ -369,15 +375,17 @@ template <int D, int BC, typename IT, typename OT>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   __shared__ Smem<D, BC> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
-  // workgroup -> (batch*head, query tile): heads spread over the 8 XCDs so a
-  // head's K/V stay in one L2; heaviest (causal) query tiles first
+  // workgroup -> (batch*head, query tile).  Workgroups go round-robin to the 8
+  // XCDs; each XCD takes whole heads, one after the other, so the workgroups
+  // resident on an XCD stream the same K/V through its L2.  Within a head the
+  // heaviest (causal) query tiles come first.
   const int64_t BH = gridDim.x / P.nqt;
   int64_t bh, qrank;
   const int64_t gi = blockIdx.x;
   if (BH % 8 == 0) {
-    const int64_t xcd = gi % 8, slot = gi / 8, hpx = BH / 8;
-    qrank = slot / hpx;
-    bh = (slot % hpx) * 8 + xcd;
+    const int64_t xcd = gi % 8, slot = gi / 8;
+    qrank = slot % P.nqt;
+    bh = (slot / P.nqt) * 8 + xcd;
   } else {
     bh = gi % BH;
     qrank = gi / BH;
@@ -411,6 +419,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) R.o[t] = float16_t{0};
   R.m = -__builtin_inff();
+  R.ref = -__builtin_inff();
   R.l = 0.0f;
 
   const int64_t qend = q0 + kBr < P.Sq ? q0 + kBr : P.Sq;  // rows of this workgroup: [q0, qend)
@@ -462,6 +471,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     cur = nxt;
   }
 
+  // FP4 tiles accumulated P^ V^ with P^ in units of e/2688
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) R.o[t][i] = R.o[t][i] * (1.0f / 2688.0f);
+
   // ---- FP16 pass over the selected blocks
   if (nsel > 0) {
     // fp16 Q fragment from the original input
@@ -509,7 +524,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
                    R.o[t][4 * j + 3] * inv);
       }
     if (P.lse && hi == 0)
-      P.lse[bh * P.Sq + qrow] = ltot > 0.0f ? (R.m + __builtin_log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
+      P.lse[bh * P.Sq + qrow] = ltot > 0.0f ? (R.ref + __builtin_log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
   }
 }
 

@@ -223,16 +223,26 @@ struct QuantArgs {
 };
 
 // Per-tensor scale factors from the partial maxima (mode 1) or *g (mode 2).
+// Every thread of the workgroup reads at most a few partials; the maximum is
+// reduced through LDS, then thread 0 forms the correctly rounded factors.
 __device__ __forceinline__ void global_factors(const QuantArgs& A, float* sh, float& ginv) {
   if (A.gmode == 0) { ginv = 1.0f; return; }
+  float a = 0.0f;
+  if (A.gmode == 1)
+    for (int i = threadIdx.x; i < A.n_part; i += blockDim.x) a = __builtin_fmaxf(a, A.amax_part[i]);
+  sh[threadIdx.x] = a;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] = __builtin_fmaxf(sh[threadIdx.x], sh[threadIdx.x + s]);
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
     float gi = 1.0f, g = 1.0f;
     if (A.gmode == 2) {
       g = *A.g;
       gi = div_rn(1.0f, g);
     } else {
-      float a = 0.0f;
-      for (int i = 0; i < A.n_part; ++i) a = __builtin_fmaxf(a, A.amax_part[i]);
+      a = sh[0];
       if (a > 0.0f && __builtin_isfinite(a)) {
         g = div_rn(a, 2688.0f);
         gi = div_rn(2688.0f, a);
@@ -242,17 +252,17 @@ __device__ __forceinline__ void global_factors(const QuantArgs& A, float* sh, fl
       }
       if (blockIdx.x == 0) *A.g = g;
     }
-    sh[0] = gi;
+    sh[256] = gi;
   }
   __syncthreads();
-  ginv = sh[0];
+  ginv = sh[256];
 }
 
 // block_axis 0: 2 lanes per 16-element block.
 template <typename T>
 __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
   __shared__ float recip[128];
-  __shared__ float sh[1];
+  __shared__ float sh[257];
   if (threadIdx.x < 128) recip[threadIdx.x] = kRecip.v[threadIdx.x];
   float ginv;
   global_factors(A, sh, ginv);
@@ -287,7 +297,7 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
 template <typename T>
 __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
   __shared__ float recip[128];
-  __shared__ float sh[1];
+  __shared__ float sh[257];
   if (threadIdx.x < 128) recip[threadIdx.x] = kRecip.v[threadIdx.x];
   float ginv;
   global_factors(A, sh, ginv);
@@ -317,17 +327,29 @@ __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
   }
 }
 
-// Partial maxima of |x| (NaN ignored) for the per-tensor scale.
+// Partial maxima of |x| (NaN ignored) for the per-tensor scale: one per
+// workgroup, grid-stride over rows with 8-element (16-byte for 2-byte types)
+// loads when rows are dense.
 template <typename T>
 __global__ void __launch_bounds__(256) amax_kernel(const T* x, int64_t rows, int64_t cols, int64_t ld,
                                                    float* part) {
   __shared__ float red[256];
   float m = 0.0f;
-  const int64_t n = rows * cols;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = i / cols, c = i - r * cols;
-    m = __builtin_fmaxf(m, __builtin_fabsf(load_elem<T>(x + r * ld + c)));
+  if (cols % 8 == 0 && ld % 8 == 0) {
+    const int64_t per_row = cols / 8, n = rows * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t r = i / per_row, c = (i - r * per_row) * 8;
+      float y[8];
+      load8<T>(x + r * ld + c, y);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(y[k]));
+    }
+  } else {
+    const int64_t n = rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+      int64_t r = i / cols, c = i - r * cols;
+      m = __builtin_fmaxf(m, __builtin_fabsf(load_elem<T>(x + r * ld + c)));
+    }
   }
   red[threadIdx.x] = m;
   __syncthreads();
@@ -345,10 +367,12 @@ __global__ void set_one_kernel(float* g) { *g = 1.0f; }
 using namespace fp4dev;
 
 int fp4i_amax_parts(int64_t rows, int64_t cols) {
+  // enough workgroups to stream the tensor at full bandwidth, few enough that
+  // every quantize workgroup can re-reduce them cheaply
   int64_t n = rows * cols;
-  int64_t p = (n + 256 * 16 - 1) / (256 * 16);
+  int64_t p = (n + 256 * 64 - 1) / (256 * 64);
   if (p < 1) p = 1;
-  if (p > 1024) p = 1024;
+  if (p > 512) p = 512;
   return (int)p;
 }
 

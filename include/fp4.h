@@ -149,6 +149,8 @@ typedef struct fp4_attn_opts {
   int32_t fp16_budget_pct; /* 0..100: share of visible key blocks per query block on the FP16 path */
   int32_t sel_block;       /* selection block (tokens), 128; multiple of kv_tile */
   int32_t out_dtype;       /* FP4_BF16, FP4_FP16 or FP4_FP32 */
+  int32_t selection_given; /* 1: topk_idx/topk_cnt are inputs (e.g. from fp4_block_topk) and
+                              no selection is computed; 0: the call computes the selection */
 } fp4_attn_opts;
 
 /*
@@ -166,7 +168,8 @@ typedef struct fp4_attn_opts {
  * ceil(pct * n_i / 100) best are kept (ties: lower j).  topk_idx
  * [B,H,ceil(Sq/sel_block),kmax] (ascending, -1 padded, kmax =
  * ceil(pct * ceil(Sk/sel_block) / 100)) and topk_cnt [B,H,ceil(Sq/sel_block)]
- * are written when non-null (otherwise kept in the workspace).
+ * are written when non-null (otherwise kept in the workspace); with
+ * opts->selection_given they are read instead and must both be non-null.
  * Requirements: d in {64, 128}; Sk % 16 == 0; causal needs Sq == Sk;
  * sel_block % kv_tile == 0; 16-byte aligned tensors.
  */
