@@ -105,12 +105,14 @@ __device__ __forceinline__ half2_t to_half2<half_t>(uint32_t w) {
   return __builtin_bit_cast(half2_t, w);
 }
 
+// LDS tiles are declared in 16-byte units so that every fragment read is a
+// single ds_read_b128 with an immediate offset.
 template <int D, int BC>
 struct Smem {
-  static constexpr int KS = D + 8;   // halves per K row (16-byte pad)
-  static constexpr int VS = BC + 8;  // halves per V^T row
-  half_t k[BC * KS];
-  half_t v[D * VS];
+  static constexpr int KS8 = D / 8 + 1;   // 16-byte units per K row (one unit of pad)
+  static constexpr int VS8 = BC / 8 + 1;  // 16-byte units per V^T row
+  half8_t k[BC * KS8];
+  half8_t v[D * VS8];
   float pm[128];
   float ps[128];
 };
@@ -172,45 +174,48 @@ __device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const uint8_t* kc, co
 
 __device__ __forceinline__ half2_t scale_pair(half2_t v, half_t s) { return v * half2_t{s, s}; }
 
+// Two E4M3 scale bytes (bits 0..15 of w) -> two fp16 values (exact).
+__device__ __forceinline__ half2_t e4m3x2_to_half2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ half2_t e4m3x2_hi_to_half2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
+// 8 E2M1 codes (one dword) times one fp16 scale -> 8 fp16 values.
+__device__ __forceinline__ half8_t deq8(uint32_t cw, half_t s) {
+  half2_t a = scale_pair(cvt_pk_f16_fp4<0>(cw), s), b = scale_pair(cvt_pk_f16_fp4<1>(cw), s);
+  half2_t c = scale_pair(cvt_pk_f16_fp4<2>(cw), s), d = scale_pair(cvt_pk_f16_fp4<3>(cw), s);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 template <int D, int BC>
 __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S) {
   constexpr int NCH = Fetch<D, BC>::NCH;
   const int t = threadIdx.x;
+  half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
 #pragma unroll
   for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
     const int q = t + 256 * u;
     if (q < NCH) {
       const int kr = q / (D / 32), dc = q % (D / 32);
-      const half_t s0 = (half_t)e4m3_to_f32(F.ks[u] & 0xFFu), s1 = (half_t)e4m3_to_f32((F.ks[u] >> 8) & 0xFFu);
-      half8_t o[4];
+      const half2_t ks2 = e4m3x2_to_half2(F.ks[u]);
+      half8_t* dst = S.k + kr * Smem<D, BC>::KS8 + dc * 4;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t cw = F.kc[u][w];  // 8 codes: d = 32*dc + 8*w .. +8
-        const half_t s = w < 2 ? s0 : s1;
-        half2_t a = scale_pair(cvt_pk_f16_fp4<0>(cw), s), b = scale_pair(cvt_pk_f16_fp4<1>(cw), s);
-        half2_t c = scale_pair(cvt_pk_f16_fp4<2>(cw), s), d2 = scale_pair(cvt_pk_f16_fp4<3>(cw), s);
-        o[w] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
-      }
-      half_t* dst = S.k + kr * Smem<D, BC>::KS + dc * 32;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) *reinterpret_cast<half8_t*>(dst + 8 * w) = o[w];
-      // V: byte j of the chunk = column 16*cc + j, tokens (2*pr, 2*pr+1)
+      for (int w = 0; w < 4; ++w) dst[w] = deq8(F.kc[u][w], w < 2 ? ks2[0] : ks2[1]);
+      // V: byte j of dword w = column 16*cc + 4*w + j, tokens (2*pr, 2*pr+1)
       const int pr = q / (D / 16), cc = q % (D / 16);
       const int pos = vpos(2 * pr);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t cw = F.vc[u][w], sw = F.vs[u][w];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = 16 * cc + 4 * w + j;
-          const half_t s = (half_t)e4m3_to_f32((sw >> (8 * j)) & 0xFFu);
-          half2_t pv;
-          if (j == 0) pv = cvt_pk_f16_fp4<0>(cw);
-          else if (j == 1) pv = cvt_pk_f16_fp4<1>(cw);
-          else if (j == 2) pv = cvt_pk_f16_fp4<2>(cw);
-          else pv = cvt_pk_f16_fp4<3>(cw);
-          *reinterpret_cast<half2_t*>(S.v + col * Smem<D, BC>::VS + pos) = scale_pair(pv, s);
-        }
+        const half2_t sa = e4m3x2_to_half2(sw), sb = e4m3x2_hi_to_half2(sw);
+        const int col = 16 * cc + 4 * w;
+        constexpr int VS2 = Smem<D, BC>::VS8 * 4;  // half2 units per V^T row
+        v2[(col + 0) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        v2[(col + 1) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        v2[(col + 2) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        v2[(col + 3) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<3>(cw), sb[1]);
       }
     }
   }
@@ -227,8 +232,7 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const I
     uint4_t w = uint4_t{0, 0, 0, 0};
     if (key < Sk) w = *reinterpret_cast<const uint4_t*>(kp + key * D + dc * 8);
     half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
-    *reinterpret_cast<half8_t*>(S.k + kr * Smem<D, BC>::KS + dc * 8) =
-        half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+    S.k[kr * Smem<D, BC>::KS8 + dc] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
   }
   // V: token pairs x 8 columns per step -> V^T
   constexpr int NV = (BC / 2) * (D / 8);
@@ -241,11 +245,13 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const I
       w1 = *reinterpret_cast<const uint4_t*>(vp + (key + 1) * D + cc * 8);
     }
     const int pos = vpos(2 * pr);
+    half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+    constexpr int VS2 = Smem<D, BC>::VS8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half2_t a = to_half2<IT>(w0[j]), b = to_half2<IT>(w1[j]);
-      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j) * Smem<D, BC>::VS + pos) = half2_t{a[0], b[0]};
-      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j + 1) * Smem<D, BC>::VS + pos) = half2_t{a[1], b[1]};
+      v2[(cc * 8 + 2 * j) * VS2 + pos / 2] = half2_t{a[0], b[0]};
+      v2[(cc * 8 + 2 * j + 1) * VS2 + pos / 2] = half2_t{a[1], b[1]};
     }
   }
 }
@@ -279,15 +285,22 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   float16_t acc[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) acc[g] = float16_t{0};
-  // S^T = K Q^T
-  const int krow = krow_of_lane(lane & 31);
+  // S^T = K Q^T; K fragments are loaded one d-step ahead of their MFMAs (the
+  // scheduling barriers keep the compiler from hoisting all of them)
+  const half8_t* kbase = S.k + krow_of_lane(lane & 31) * Smem<D, BC>::KS8 + hi;
+  half8_t kf[2][NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) kf[0][g] = kbase[32 * g * Smem<D, BC>::KS8];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
+    if (s + 1 < D / 16) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const half8_t a = *reinterpret_cast<const half8_t*>(S.k + (32 * g + krow) * Smem<D, BC>::KS + 16 * s + 8 * hi);
-      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[g], 0, 0, 0);
+      for (int g = 0; g < NG; ++g) kf[(s + 1) & 1][g] = kbase[32 * g * Smem<D, BC>::KS8 + 2 * (s + 1)];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s & 1][g], qf[s], acc[g], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // x = S * c, masked keys -> -inf; lane holds keys 32g + 16*hi + i
   float tm = -__builtin_inff();
@@ -318,13 +331,14 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
     R.l = R.l * f;
     if (use) R.ref = tm;
   }
-  // e = 2^(x - tm); masked keys and skipping rows give 0
+  // e = 2^(x - tm); masked keys give 0, rows that skip the tile subtract +inf
+  const float tme = use ? tm : __builtin_inff();
   float lsum = 0.0f;
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float e = use ? __builtin_amdgcn_exp2f(acc[g][i] - tm) : 0.0f;
+      const float e = __builtin_amdgcn_exp2f(acc[g][i] - tme);
       acc[g][i] = e;
       lsum += e;
     }
@@ -360,14 +374,17 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
 #pragma unroll
         for (int i = 0; i < 8; ++i) pf[h2][i] = (half_t)acc[g][8 * h2 + i];
     }
+    const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + 4 * g + hi;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      half8_t vf[D / 32];
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const half8_t a = *reinterpret_cast<const half8_t*>(S.v + (32 * t + (lane & 31)) * Smem<D, BC>::VS +
-                                                            32 * g + 16 * h2 + 8 * hi);
-        R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[h2], R.o[t], 0, 0, 0);
-      }
+      for (int t = 0; t < D / 32; ++t) vf[t] = vbase[32 * t * Smem<D, BC>::VS8 + 2 * h2];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t], pf[h2], R.o[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
