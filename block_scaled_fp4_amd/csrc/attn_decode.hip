@@ -27,14 +27,28 @@ constexpr int kGmax = 16;      // query heads per kv head handled by one workgro
 
 template <int D>
 struct DecSmem {
-  static constexpr int KS = D + 8;
-  static constexpr int VS = kDecTile + 8;
+  static constexpr int KS8 = D / 8 + 1;         // 16-byte units per K row (one unit of pad)
+  static constexpr int VS8 = kDecTile / 8 + 1;  // 16-byte units per V^T row
   union {
     struct {
-      half_t k[kDecTile * KS];
-      half_t v[D * VS];
+      half8_t k[kDecTile * KS8];
+      half8_t v[D * VS8];
     };
     struct {  // wave-state merge, used after the last tile
+      float red_m[4][kGmax];
+      float red_l[4][kGmax];
+      float red_o[4][kGmax][D];
+    };
+  };
+};
+
+// LDS of the FP4-region kernel: only V^T (K is consumed from registers).
+template <int D>
+struct DecSmemV {
+  static constexpr int VS8 = kDecTile / 8 + 1;
+  union {
+    half8_t v[D * VS8];
+    struct {
       float red_m[4][kGmax];
       float red_l[4][kGmax];
       float red_o[4][kGmax][D];
@@ -83,38 +97,36 @@ __device__ __forceinline__ void dec_fetch(DecFetch<D>& F, const uint8_t* kc, con
   }
 }
 
+__device__ __forceinline__ half8_t dec_deq8(uint32_t cw, half_t s) {
+  half2_t a = scale_h2(cvt_pk_f16_fp4<0>(cw), s), b = scale_h2(cvt_pk_f16_fp4<1>(cw), s);
+  half2_t c = scale_h2(cvt_pk_f16_fp4<2>(cw), s), d = scale_h2(cvt_pk_f16_fp4<3>(cw), s);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 template <int D>
 __device__ __forceinline__ void dec_stage_fp4(const DecFetch<D>& F, DecSmem<D>& S) {
+  half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+  constexpr int VS2 = DecSmem<D>::VS8 * 4;
 #pragma unroll
   for (int u = 0; u < DecFetch<D>::PER; ++u) {
     const int q = threadIdx.x + 256 * u;
     if (q < DecFetch<D>::NCH) {
       const int kr = q / (D / 32), dc = q % (D / 32);
-      const half_t s0 = (half_t)e4m3_to_f32(F.ks[u] & 0xFFu), s1 = (half_t)e4m3_to_f32((F.ks[u] >> 8) & 0xFFu);
-      half_t* dst = S.k + kr * DecSmem<D>::KS + dc * 32;
+      const half2_t ks2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.ks[u], 1.0f, false);
+      half8_t* dst = S.k + kr * DecSmem<D>::KS8 + dc * 4;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t cw = F.kc[u][w];
-        const half_t s = w < 2 ? s0 : s1;
-        half2_t a = scale_h2(cvt_pk_f16_fp4<0>(cw), s), b = scale_h2(cvt_pk_f16_fp4<1>(cw), s);
-        half2_t c = scale_h2(cvt_pk_f16_fp4<2>(cw), s), d2 = scale_h2(cvt_pk_f16_fp4<3>(cw), s);
-        *reinterpret_cast<half8_t*>(dst + 8 * w) = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
-      }
+      for (int w = 0; w < 4; ++w) dst[w] = dec_deq8(F.kc[u][w], w < 2 ? ks2[0] : ks2[1]);
       const int pr = q / (D / 16), cc = q % (D / 16);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t cw = F.vc[u][w], sw = F.vs[u][w];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = 16 * cc + 4 * w + j;
-          const half_t s = (half_t)e4m3_to_f32((sw >> (8 * j)) & 0xFFu);
-          half2_t pv;
-          if (j == 0) pv = cvt_pk_f16_fp4<0>(cw);
-          else if (j == 1) pv = cvt_pk_f16_fp4<1>(cw);
-          else if (j == 2) pv = cvt_pk_f16_fp4<2>(cw);
-          else pv = cvt_pk_f16_fp4<3>(cw);
-          *reinterpret_cast<half2_t*>(S.v + col * DecSmem<D>::VS + 2 * pr) = scale_h2(pv, s);
-        }
+        const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+        const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+        const int col = 16 * cc + 4 * w;
+        v2[(col + 0) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        v2[(col + 1) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        v2[(col + 2) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        v2[(col + 3) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
       }
     }
   }
@@ -138,7 +150,7 @@ __device__ __forceinline__ void dec_stage_bf16(DecSmem<D>& S, const uint16_t* si
       w = *reinterpret_cast<const uint4_t*>(src + dc * 8);
     }
     half2_t a = bf16x2_to_half2(w[0]), b = bf16x2_to_half2(w[1]), c = bf16x2_to_half2(w[2]), d2 = bf16x2_to_half2(w[3]);
-    *reinterpret_cast<half8_t*>(S.k + kr * DecSmem<D>::KS + dc * 8) = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+    S.k[kr * DecSmem<D>::KS8 + dc] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
   }
 }
 template <int D>
@@ -157,11 +169,13 @@ __device__ __forceinline__ void dec_stage_bf16_v(DecSmem<D>& S, const uint16_t* 
       const uint16_t* src = key + 1 < n_sink ? sink + (key + 1) * D : recent + (key + 1 - n_sink) * D;
       w1 = *reinterpret_cast<const uint4_t*>(src + cc * 8);
     }
+    half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+    constexpr int VS2 = DecSmem<D>::VS8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half2_t a = bf16x2_to_half2(w0[j]), b = bf16x2_to_half2(w1[j]);
-      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j) * DecSmem<D>::VS + 2 * pr) = half2_t{a[0], b[0]};
-      *reinterpret_cast<half2_t*>(S.v + (cc * 8 + 2 * j + 1) * DecSmem<D>::VS + 2 * pr) = half2_t{a[1], b[1]};
+      v2[(cc * 8 + 2 * j) * VS2 + pr] = half2_t{a[0], b[0]};
+      v2[(cc * 8 + 2 * j + 1) * VS2 + pr] = half2_t{a[1], b[1]};
     }
   }
 }
@@ -189,7 +203,7 @@ __device__ __forceinline__ void dec_wave_tile(const DecSmem<D>& S, const half8_t
     const int krow = kw + 8 * (m >> 2) + 4 * g + (m & 3);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const half8_t a = *reinterpret_cast<const half8_t*>(S.k + krow * DecSmem<D>::KS + 32 * s + 8 * q4);
+      const half8_t a = S.k[krow * DecSmem<D>::KS8 + 4 * s + q4];
       acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[s], acc[g], 0, 0, 0);
     }
   }
@@ -221,7 +235,7 @@ __device__ __forceinline__ void dec_wave_tile(const DecSmem<D>& S, const half8_t
   }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const half8_t a = *reinterpret_cast<const half8_t*>(S.v + (16 * t + (lane & 15)) * DecSmem<D>::VS + kw + 8 * q4);
+    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmem<D>::VS8 + kw / 8 + q4];
     R.o[t] = R.o[t] * alpha;
     R.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, R.o[t], 0, 0, 0);
   }
@@ -243,20 +257,267 @@ struct DecArgs {
   float* part_ml;
 };
 
-// grid: (B*Hkv*(nsplit+1)); split index nsplit is the bf16 part.
+// ---- FP4 region: K straight from HBM into MFMA operands, V through LDS ----
+//
+// Each wave owns 32 keys of a 128-key tile.  For S^T = K q^T on
+// v_mfma_f32_16x16x32_f16 the lanes of group q4 = lane/16 carry the d range
+// [q4*D/4, (q4+1)*D/4) over the D/32 reduction steps (the B operand q uses the
+// same d order), so one coalesced 16-byte load per lane (8 bytes for d = 64)
+// brings a key's codes for all steps and K never touches LDS.  A-row m of
+// subtile g reads key 8*(m/4) + 4*g + m%4, so each lane group ends up with 8
+// consecutive keys, the order the PV step wants.  Only V goes through LDS
+// (transposed to [d][key]), which halves LDS use and leaves room for more
+// workgroups per CU; K and V codes are prefetched two tiles ahead.
 template <int D>
-__global__ void __launch_bounds__(256, 2) decode_split_kernel(DecArgs A) {
-  __shared__ DecSmem<D> S;
+struct KRegs {
+  static constexpr int CB = D / 8;   // code bytes per lane per key (D/4 codes)
+  static constexpr int SB = D / 64;  // scale bytes per lane per key
+  uint32_t c[2][CB / 4];
+  uint32_t s[2];
+};
+
+template <int D>
+struct VRegs {
+  static constexpr int NCH = kDecTile * D / 32;  // 16-byte chunks of V codes per tile
+  static constexpr int PER = (NCH + 255) / 256;
+  uint4_t c[PER];
+  uint4_t s[PER];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k(KRegs<D>& K, const uint8_t* kc, const uint8_t* ks, int64_t key0, int64_t kend) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t key = key0 + 32 * wave + 8 * (m >> 2) + 4 * g + (m & 3);
+    if (key < kend) {
+      const uint8_t* cp = kc + key * (D / 2) + q4 * KRegs<D>::CB;
+      if (D == 128) {
+        const uint4_t w = *reinterpret_cast<const uint4_t*>(cp);
+#pragma unroll
+        for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
+        K.s[g] = *reinterpret_cast<const uint16_t*>(ks + key * (D / 16) + q4 * KRegs<D>::SB);
+      } else {
+        const uint2_t w = *reinterpret_cast<const uint2_t*>(cp);
+#pragma unroll
+        for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
+        K.s[g] = ks[key * (D / 16) + q4 * KRegs<D>::SB];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = 0;
+      K.s[g] = 0;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(VRegs<D>& V, const uint8_t* vc, const uint8_t* vs, int64_t key0, int64_t kend) {
+#pragma unroll
+  for (int u = 0; u < VRegs<D>::PER; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    if (q < VRegs<D>::NCH) {
+      const int pr = q / (D / 16), cc = q % (D / 16);
+      const int64_t pair = key0 / 2 + pr;
+      if (2 * pair < kend) {
+        V.c[u] = *reinterpret_cast<const uint4_t*>(vc + pair * D + cc * 16);
+        V.s[u] = *reinterpret_cast<const uint4_t*>(vs + (pair / 8) * D + cc * 16);
+      } else {
+        V.c[u] = uint4_t{0, 0, 0, 0};
+        V.s[u] = uint4_t{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_v(const VRegs<D>& V, DecSmemV<D>& S) {
+  half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+  constexpr int VS2 = DecSmemV<D>::VS8 * 4;
+#pragma unroll
+  for (int u = 0; u < VRegs<D>::PER; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    if (q < VRegs<D>::NCH) {
+      const int pr = q / (D / 16), cc = q % (D / 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t cw = V.c[u][w], sw = V.s[u][w];
+        const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+        const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+        const int col = 16 * cc + 4 * w;
+        v2[(col + 0) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        v2[(col + 1) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        v2[(col + 2) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        v2[(col + 3) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
+      }
+    }
+  }
+}
+
+// One wave's 32 keys: S^T from the K registers, softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void fp4_wave_tile(const DecSmemV<D>& S, const KRegs<D>& K, const half8_t (&qf)[D / 32],
+                                              DecState<D>& R, int64_t key0, int64_t kend, float c) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q4 = lane >> 4;
+  const int kw = 32 * wave;
+  float4_t acc[2] = {float4_t{0, 0, 0, 0}, float4_t{0, 0, 0, 0}};
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const half2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(K.s[g], 1.0f, false);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const half_t sv = (s >> 1) == 0 ? sc[0] : sc[1];  // scale block of d = q4*D/4 + 8*s
+      const half8_t a = dec_deq8(K.c[g][s], sv);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[s], acc[g], 0, 0, 0);
+    }
+  }
+  float x[8];
+  float tm = -__builtin_inff();
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t key = key0 + kw + 8 * q4 + 4 * g + i;
+      float v = acc[g][i] * c;
+      if (key >= kend) v = -__builtin_inff();
+      x[4 * g + i] = v;
+      tm = __builtin_fmaxf(tm, v);
+    }
+  tm = __builtin_fmaxf(tm, __shfl_xor(tm, 16, 64));
+  tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32, 64));
+  if (!(tm > -__builtin_inff())) return;
+  const float mnew = __builtin_fmaxf(R.m, tm);
+  const float alpha = __builtin_amdgcn_exp2f(R.m - mnew);
+  half8_t pf;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float e = __builtin_amdgcn_exp2f(x[j] - mnew);
+    lsum += e;
+    pf[j] = (half_t)e;
+  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmemV<D>::VS8 + kw / 8 + q4];
+    R.o[t] = R.o[t] * alpha;
+    R.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, R.o[t], 0, 0, 0);
+  }
+  R.l = R.l * alpha + lsum;
+  R.m = mnew;
+}
+
+// Merge the four waves' (m, l, O) in LDS and write this split's partial.
+template <int D, typename SM>
+__device__ __forceinline__ void write_partial(SM& S, const DecState<D>& R, const DecArgs& A, int64_t bk,
+                                              int split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q4 = lane >> 4, head = lane & 15;
   const int ns1 = A.nsplit + 1;
+  const float lh = R.l + __shfl_xor(R.l, 16, 64);
+  const float lt = lh + __shfl_xor(lh, 32, 64);
+  __syncthreads();
+  if (q4 == 0) {
+    S.red_m[wave][head] = R.m;
+    S.red_l[wave][head] = lt;
+  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S.red_o[wave][head][16 * t + 4 * q4 + i] = R.o[t][i];
+  __syncthreads();
+  const int64_t pbase = bk * A.G;
+  for (int idx = threadIdx.x; idx < A.G * D; idx += 256) {
+    const int hh = idx / D, dd = idx % D;
+    float mm = -__builtin_inff();
+    for (int w = 0; w < 4; ++w) mm = __builtin_fmaxf(mm, S.red_m[w][hh]);
+    float o = 0.0f, l = 0.0f;
+    if (mm > -__builtin_inff())
+      for (int w = 0; w < 4; ++w)
+        if (S.red_m[w][hh] > -__builtin_inff()) {
+          const float f = __builtin_amdgcn_exp2f(S.red_m[w][hh] - mm);
+          o += S.red_o[w][hh][dd] * f;
+          l += S.red_l[w][hh] * f;
+        }
+    A.part_o[((pbase + hh) * ns1 + split) * D + dd] = o;
+    if (dd == 0) {
+      A.part_ml[((pbase + hh) * ns1 + split) * 2] = mm;
+      A.part_ml[((pbase + hh) * ns1 + split) * 2 + 1] = l;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(half8_t (&qf)[D / 32], const DecArgs& A, int64_t bk) {
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, head = lane & 15;
+  const bool ok = head < A.G;
+  const uint16_t* qp = A.q + (bk * A.G + (ok ? head : 0)) * D + q4 * (D / 4);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(qp + 8 * s) : uint4_t{0, 0, 0, 0};
+    half2_t a = bf16x2_to_half2(w[0]), bb = bf16x2_to_half2(w[1]), cc = bf16x2_to_half2(w[2]), dd = bf16x2_to_half2(w[3]);
+    qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
+  }
+}
+
+// grid: (B*Hkv*nsplit); one workgroup per (batch, kv head, split of the FP4 region)
+template <int D>
+__global__ void __launch_bounds__(256, 3) decode_fp4_kernel(DecArgs A) {
+  __shared__ DecSmemV<D> S;
   const int64_t gi = blockIdx.x;
-  const int split = (int)(gi % ns1);
-  const int64_t bk = gi / ns1;  // b * Hkv + kvh
+  const int split = (int)(gi % A.nsplit);
+  const int64_t bk = gi / A.nsplit;
   const int64_t b = bk / A.Hkv;
-  const int head = lane & 15;
-  // q fragment (B operand): head lane%16 (zero beyond G), d = 32 s + 8 q4 .. +8, fp16
+  half8_t qf[D / 32];
+  load_q<D>(qf, A, bk);
+  DecState<D> R;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
+  R.m = -__builtin_inff();
+  R.l = 0.0f;
+  int64_t mlen = A.mid_len[b];
+  if (mlen < 0) mlen = 0;
+  if (mlen > A.mid_cap) mlen = A.mid_cap;
+  mlen &= ~(int64_t)15;
+  const int64_t s0 = (int64_t)split * A.split_len;
+  int64_t s1 = s0 + A.split_len;
+  if (s1 > mlen) s1 = mlen;
+  const uint8_t* kc = A.kc + bk * A.mid_cap * (D / 2);
+  const uint8_t* ks = A.ks + bk * A.mid_cap * (D / 16);
+  const uint8_t* vc = A.vc + bk * (A.mid_cap / 2) * D;
+  const uint8_t* vs = A.vs + bk * (A.mid_cap / 16) * D;
+  KRegs<D> K0, K1;
+  VRegs<D> V0, V1;
+  if (s0 < s1) { load_k<D>(K0, kc, ks, s0, s1); load_v<D>(V0, vc, vs, s0, s1); }
+  if (s0 + kDecTile < s1) { load_k<D>(K1, kc, ks, s0 + kDecTile, s1); load_v<D>(V1, vc, vs, s0 + kDecTile, s1); }
+  for (int64_t key0 = s0; key0 < s1; key0 += 2 * kDecTile) {
+    // tile key0 from buffers 0, then refill them two tiles ahead
+    __syncthreads();
+    stage_v<D>(V0, S);
+    if (key0 + 2 * kDecTile < s1) load_v<D>(V0, vc, vs, key0 + 2 * kDecTile, s1);
+    __syncthreads();
+    fp4_wave_tile<D>(S, K0, qf, R, key0, s1, A.c);
+    if (key0 + 2 * kDecTile < s1) load_k<D>(K0, kc, ks, key0 + 2 * kDecTile, s1);
+    // tile key0 + 128 from buffers 1
+    if (key0 + kDecTile < s1) {
+      __syncthreads();
+      stage_v<D>(V1, S);
+      if (key0 + 3 * kDecTile < s1) load_v<D>(V1, vc, vs, key0 + 3 * kDecTile, s1);
+      __syncthreads();
+      fp4_wave_tile<D>(S, K1, qf, R, key0 + kDecTile, s1, A.c);
+      if (key0 + 3 * kDecTile < s1) load_k<D>(K1, kc, ks, key0 + 3 * kDecTile, s1);
+    }
+  }
+  write_partial<D>(S, R, A, bk, split);
+}
+
+// grid: (B*Hkv); the bf16 sink and recent tokens, written as split index nsplit.
+template <int D>
+__global__ void __launch_bounds__(256, 2) decode_full_kernel(DecArgs A) {
+  __shared__ DecSmem<D> S;
+  const int64_t bk = blockIdx.x;  // b * Hkv + kvh
   half8_t qf[D / 32];
   {
+    // natural d order here (K comes through LDS)
+    const int lane = threadIdx.x & 63, q4 = lane >> 4, head = lane & 15;
     const bool ok = head < A.G;
     const uint16_t* qp = A.q + (bk * A.G + (ok ? head : 0)) * D;
 #pragma unroll
@@ -271,74 +532,19 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecArgs A) {
   for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
   R.m = -__builtin_inff();
   R.l = 0.0f;
-
-  if (split < A.nsplit) {
-    int64_t mlen = A.mid_len[b];
-    if (mlen < 0) mlen = 0;
-    if (mlen > A.mid_cap) mlen = A.mid_cap;
-    mlen &= ~(int64_t)15;
-    const int64_t s0 = (int64_t)split * A.split_len;
-    int64_t s1 = s0 + A.split_len;
-    if (s1 > mlen) s1 = mlen;
-    const uint8_t* kc = A.kc + bk * A.mid_cap * (D / 2);
-    const uint8_t* ks = A.ks + bk * A.mid_cap * (D / 16);
-    const uint8_t* vc = A.vc + bk * (A.mid_cap / 2) * D;
-    const uint8_t* vs = A.vs + bk * (A.mid_cap / 16) * D;
-    DecFetch<D> F;
-    if (s0 < s1) dec_fetch<D>(F, kc, ks, vc, vs, s0, s1);
-    for (int64_t key0 = s0; key0 < s1; key0 += kDecTile) {
-      __syncthreads();
-      dec_stage_fp4<D>(F, S);
-      if (key0 + kDecTile < s1) dec_fetch<D>(F, kc, ks, vc, vs, key0 + kDecTile, s1);
-      __syncthreads();
-      dec_wave_tile<D>(S, qf, R, key0, s1, A.c);
-    }
-  } else {
-    const int n_full = A.n_sink + A.n_recent;
-    const uint16_t* ksk = A.k_sink + bk * (int64_t)A.n_sink * D;
-    const uint16_t* vsk = A.v_sink + bk * (int64_t)A.n_sink * D;
-    const uint16_t* krc = A.k_recent + bk * (int64_t)A.n_recent * D;
-    const uint16_t* vrc = A.v_recent + bk * (int64_t)A.n_recent * D;
-    for (int64_t key0 = 0; key0 < n_full; key0 += kDecTile) {
-      __syncthreads();
-      dec_stage_bf16<D>(S, ksk, krc, A.n_sink, n_full, key0);
-      dec_stage_bf16_v<D>(S, vsk, vrc, A.n_sink, n_full, key0);
-      __syncthreads();
-      dec_wave_tile<D>(S, qf, R, key0, n_full, A.c);
-    }
+  const int n_full = A.n_sink + A.n_recent;
+  const uint16_t* ksk = A.k_sink + bk * (int64_t)A.n_sink * D;
+  const uint16_t* vsk = A.v_sink + bk * (int64_t)A.n_sink * D;
+  const uint16_t* krc = A.k_recent + bk * (int64_t)A.n_recent * D;
+  const uint16_t* vrc = A.v_recent + bk * (int64_t)A.n_recent * D;
+  for (int64_t key0 = 0; key0 < n_full; key0 += kDecTile) {
+    __syncthreads();
+    dec_stage_bf16<D>(S, ksk, krc, A.n_sink, n_full, key0);
+    dec_stage_bf16_v<D>(S, vsk, vrc, A.n_sink, n_full, key0);
+    __syncthreads();
+    dec_wave_tile<D>(S, qf, R, key0, n_full, A.c);
   }
-  // merge the four waves' states in LDS, then write this split's partial
-  const float lh = R.l + __shfl_xor(R.l, 16, 64);
-  const float lt = lh + __shfl_xor(lh, 32, 64);
-  __syncthreads();
-  if (q4 == 0) {
-    S.red_m[wave][head] = R.m;
-    S.red_l[wave][head] = lt;
-  }
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) S.red_o[wave][head][16 * t + 4 * q4 + i] = R.o[t][i];
-  __syncthreads();
-  const int64_t pbase = bk * A.G;  // partial rows of this (b, kvh): [G][ns1]
-  for (int idx = threadIdx.x; idx < A.G * D; idx += 256) {
-    const int hh = idx / D, dd = idx % D;
-    float mm = -__builtin_inff();
-    for (int w = 0; w < 4; ++w) mm = __builtin_fmaxf(mm, S.red_m[w][hh]);
-    float o = 0.0f;
-    if (mm > -__builtin_inff())
-      for (int w = 0; w < 4; ++w)
-        if (S.red_m[w][hh] > -__builtin_inff()) o += S.red_o[w][hh][dd] * __builtin_amdgcn_exp2f(S.red_m[w][hh] - mm);
-    A.part_o[((pbase + hh) * ns1 + split) * D + dd] = o;
-    if (dd == 0) {
-      float l = 0.0f;
-      if (mm > -__builtin_inff())
-        for (int w = 0; w < 4; ++w)
-          if (S.red_m[w][hh] > -__builtin_inff()) l += S.red_l[w][hh] * __builtin_amdgcn_exp2f(S.red_m[w][hh] - mm);
-      A.part_ml[((pbase + hh) * ns1 + split) * 2] = mm;
-      A.part_ml[((pbase + hh) * ns1 + split) * 2 + 1] = l;
-    }
-  }
+  write_partial<D>(S, R, A, bk, A.nsplit);
 }
 
 template <typename OT>
@@ -399,7 +605,9 @@ hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t st) {
   A.part_o = L.part_o;
   A.part_ml = L.part_ml;
   const int ns1 = L.nsplit + 1;
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)(L.B * L.Hkv * ns1)), dim3(256), 0, st, A);
+  if (L.nsplit > 0)
+    hipLaunchKernelGGL(decode_fp4_kernel<D>, dim3((unsigned)(L.B * L.Hkv * L.nsplit)), dim3(256), 0, st, A);
+  hipLaunchKernelGGL(decode_full_kernel<D>, dim3((unsigned)(L.B * L.Hkv)), dim3(256), 0, st, A);
   const dim3 mg((unsigned)(L.B * L.Hq));
   if (L.out_dtype == 2)
     hipLaunchKernelGGL((decode_merge_kernel<D, float>), mg, dim3(D), 0, st, L.part_o, L.part_ml, ns1, (float*)L.out, L.lse);

@@ -170,24 +170,25 @@ __device__ __forceinline__ void choose_block(const float (&y)[NH][8], int search
   }
   const int s0 = (int)e4m3_of_div6(a);
   const int lo = search ? fmin : 0, hi = search ? fmax : 0;
+  // Branch-free candidate loop (the bounds are uniform): a byte outside
+  // 0..0x7E is evaluated on a clamped byte and given an infinite error; byte 0
+  // needs no special case because its reciprocal entry is 0, which maps every
+  // element to code 0 and leaves the error |y| itself.
   float best = 0.0f;
+  bool have = false;  // a valid candidate has been seen (the first one always wins, even at inf)
   int bestf = 0;
-  bool have = false;
   uint32_t bestc[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) bestc[h] = 0;
+#pragma unroll 3
   for (int f = lo; f <= hi; ++f) {
-    int b = s0 + f;
-    if (b < 0 || b > 0x7E) continue;
+    const int b = s0 + f;
+    const bool valid = b >= 0 && b <= 0x7E;
+    const uint32_t bc = (uint32_t)(b < 0 ? 0 : (b > 0x7E ? 0x7E : b));
     float part[NH];
     uint32_t c[NH];
-    if (b == 0) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h) { part[h] = half_block_sse_zero(ay[h]); c[h] = 0; }
-    } else {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) part[h] = half_block_sse(ay[h], (uint32_t)b, recip, c[h]);
-    }
+    for (int h = 0; h < NH; ++h) part[h] = half_block_sse(ay[h], bc, recip, c[h]);
     float sse;
     if (NH == 1) {
       float other = swap_lane1(part[0]);
@@ -195,10 +196,11 @@ __device__ __forceinline__ void choose_block(const float (&y)[NH][8], int search
     } else {
       sse = part[0] + part[NH - 1];
     }
-    if (!have || sse < best) {
+    const bool better = valid && (!have || sse < best);
+    have = have || valid;
+    if (better) {
       best = sse;
       bestf = f;
-      have = true;
 #pragma unroll
       for (int h = 0; h < NH; ++h) bestc[h] = c[h];
     }
