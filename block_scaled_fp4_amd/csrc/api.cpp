@@ -103,6 +103,8 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
   if (p->H % p->Hkv) return fail(FP4_ERR_INVALID_ARG, "%s: H %% Hkv != 0", fn);
   if (p->d != 64 && p->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim %lld not in {64,128}", fn, (long long)p->d);
   if (p->Sk % 16) return fail(FP4_ERR_INVALID_ARG, "%s: Sk %% 16 != 0", fn);
+  // kernels address one head's K/V through 32-bit buffer offsets
+  if (p->Sk * p->d * 2 >= ((int64_t)1 << 31)) return fail(FP4_ERR_UNSUPPORTED, "%s: Sk * d too large", fn);
   if (p->dtype != FP4_BF16 && p->dtype != FP4_FP16)
     return fail(FP4_ERR_UNSUPPORTED, "%s: q/k/v dtype must be bf16 or fp16", fn);
   if (o->causal != 0 && o->causal != 1) return fail(FP4_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
@@ -331,6 +333,7 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float
   if (c->n_sink < 0 || c->n_recent < 0 || c->mid_cap < 0 || c->mid_cap % 16)
     return fail(FP4_ERR_INVALID_ARG, "%s: n_sink/n_recent must be >= 0 and mid_cap a multiple of 16", fn);
   if (c->n_sink + c->n_recent + c->mid_cap < 1) return fail(FP4_ERR_INVALID_ARG, "%s: empty cache", fn);
+  if (c->mid_cap * c->d / 2 >= ((int64_t)1 << 31)) return fail(FP4_ERR_UNSUPPORTED, "%s: mid_cap * d too large", fn);
   if ((c->n_sink && (!c->k_sink || !c->v_sink)) || (c->n_recent && (!c->k_recent || !c->v_recent)))
     return fail(FP4_ERR_INVALID_ARG, "%s: sink/recent buffers missing", fn);
   if (c->mid_cap && (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->mid_len))

@@ -284,48 +284,43 @@ struct VRegs {
   uint4_t s[PER];
 };
 
+// Loads go through buffer resources sized to the split's last token, so
+// tokens past it read as zero (K: masked in the scores; V: zero rows) and no
+// branch or clamp sits between loads -- several tiles stay in flight.
+struct SplitBufs {
+  rsrc_t kc, ks, vc, vs;
+};
+
 template <int D>
-__device__ __forceinline__ void load_k(KRegs<D>& K, const uint8_t* kc, const uint8_t* ks, int64_t key0, int64_t kend) {
+__device__ __forceinline__ void load_k(KRegs<D>& K, const SplitBufs& sb, int64_t key0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int64_t key = key0 + 32 * wave + 8 * (m >> 2) + 4 * g + (m & 3);
-    if (key < kend) {
-      const uint8_t* cp = kc + key * (D / 2) + q4 * KRegs<D>::CB;
-      if (D == 128) {
-        const uint4_t w = *reinterpret_cast<const uint4_t*>(cp);
+    const uint32_t key = (uint32_t)key0 + 32 * wave + 8 * (m >> 2) + 4 * g + (m & 3);
+    if (D == 128) {
+      const uint4_t w = buf_load16(sb.kc, key * (D / 2) + q4 * KRegs<D>::CB);
 #pragma unroll
-        for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
-        K.s[g] = *reinterpret_cast<const uint16_t*>(ks + key * (D / 16) + q4 * KRegs<D>::SB);
-      } else {
-        const uint2_t w = *reinterpret_cast<const uint2_t*>(cp);
-#pragma unroll
-        for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
-        K.s[g] = ks[key * (D / 16) + q4 * KRegs<D>::SB];
-      }
+      for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
+      K.s[g] = buf_load2(sb.ks, key * (D / 16) + q4 * KRegs<D>::SB);
     } else {
+      const uint2_t w = buf_load8(sb.kc, key * (D / 2) + q4 * KRegs<D>::CB);
 #pragma unroll
-      for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = 0;
-      K.s[g] = 0;
+      for (int i = 0; i < KRegs<D>::CB / 4; ++i) K.c[g][i] = w[i];
+      K.s[g] = buf_load1(sb.ks, key * (D / 16) + q4 * KRegs<D>::SB);
     }
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_v(VRegs<D>& V, const uint8_t* vc, const uint8_t* vs, int64_t key0, int64_t kend) {
+__device__ __forceinline__ void load_v(VRegs<D>& V, const SplitBufs& sb, int64_t key0) {
 #pragma unroll
   for (int u = 0; u < VRegs<D>::PER; ++u) {
     const int q = threadIdx.x + 256 * u;
-    if (q < VRegs<D>::NCH) {
+    if (VRegs<D>::NCH % 256 == 0 || q < VRegs<D>::NCH) {
       const int pr = q / (D / 16), cc = q % (D / 16);
-      const int64_t pair = key0 / 2 + pr;
-      if (2 * pair < kend) {
-        V.c[u] = *reinterpret_cast<const uint4_t*>(vc + pair * D + cc * 16);
-        V.s[u] = *reinterpret_cast<const uint4_t*>(vs + (pair / 8) * D + cc * 16);
-      } else {
-        V.c[u] = uint4_t{0, 0, 0, 0};
-        V.s[u] = uint4_t{0, 0, 0, 0};
-      }
+      const uint32_t pair = (uint32_t)(key0 / 2) + pr;
+      V.c[u] = buf_load16(sb.vc, pair * D + cc * 16);
+      V.s[u] = buf_load16(sb.vs, (pair / 8) * D + cc * 16);
     }
   }
 }
@@ -480,30 +475,40 @@ __global__ void __launch_bounds__(256, 3) decode_fp4_kernel(DecArgs A) {
   const int64_t s0 = (int64_t)split * A.split_len;
   int64_t s1 = s0 + A.split_len;
   if (s1 > mlen) s1 = mlen;
-  const uint8_t* kc = A.kc + bk * A.mid_cap * (D / 2);
-  const uint8_t* ks = A.ks + bk * A.mid_cap * (D / 16);
-  const uint8_t* vc = A.vc + bk * (A.mid_cap / 2) * D;
-  const uint8_t* vs = A.vs + bk * (A.mid_cap / 16) * D;
-  KRegs<D> K0, K1;
-  VRegs<D> V0, V1;
-  if (s0 < s1) { load_k<D>(K0, kc, ks, s0, s1); load_v<D>(V0, vc, vs, s0, s1); }
-  if (s0 + kDecTile < s1) { load_k<D>(K1, kc, ks, s0 + kDecTile, s1); load_v<D>(V1, vc, vs, s0 + kDecTile, s1); }
-  for (int64_t key0 = s0; key0 < s1; key0 += 2 * kDecTile) {
-    // tile key0 from buffers 0, then refill them two tiles ahead
-    __syncthreads();
-    stage_v<D>(V0, S);
-    if (key0 + 2 * kDecTile < s1) load_v<D>(V0, vc, vs, key0 + 2 * kDecTile, s1);
-    __syncthreads();
-    fp4_wave_tile<D>(S, K0, qf, R, key0, s1, A.c);
-    if (key0 + 2 * kDecTile < s1) load_k<D>(K0, kc, ks, key0 + 2 * kDecTile, s1);
-    // tile key0 + 128 from buffers 1
-    if (key0 + kDecTile < s1) {
+  // resources end at this split's last token s1 (a multiple of 16)
+  SplitBufs sb;
+  sb.kc = make_rsrc(A.kc + bk * A.mid_cap * (D / 2), (uint32_t)(s1 * (D / 2)));
+  sb.ks = make_rsrc(A.ks + bk * A.mid_cap * (D / 16), (uint32_t)(s1 * (D / 16)));
+  sb.vc = make_rsrc(A.vc + bk * (A.mid_cap / 2) * D, (uint32_t)((s1 / 2) * D));
+  sb.vs = make_rsrc(A.vs + bk * (A.mid_cap / 16) * D, (uint32_t)((s1 / 16) * D));
+  if (s0 < s1) {
+    // tiles start at s0 + i*128; past the last one the prefetch reloads the
+    // last tile (clamped, cached) instead of branching
+    const int64_t last = s0 + ((s1 - s0 - 1) / kDecTile) * kDecTile;
+    auto tclamp = [&](int64_t k) { return k < last ? k : last; };
+    KRegs<D> K0, K1;
+    VRegs<D> V0, V1;
+    load_k<D>(K0, sb, s0);
+    load_v<D>(V0, sb, s0);
+    load_k<D>(K1, sb, tclamp(s0 + kDecTile));
+    load_v<D>(V1, sb, tclamp(s0 + kDecTile));
+    for (int64_t key0 = s0; key0 < s1; key0 += 2 * kDecTile) {
+      // tile key0 from buffers 0, then refill them two tiles ahead
       __syncthreads();
-      stage_v<D>(V1, S);
-      if (key0 + 3 * kDecTile < s1) load_v<D>(V1, vc, vs, key0 + 3 * kDecTile, s1);
+      stage_v<D>(V0, S);
+      load_v<D>(V0, sb, tclamp(key0 + 2 * kDecTile));
       __syncthreads();
-      fp4_wave_tile<D>(S, K1, qf, R, key0 + kDecTile, s1, A.c);
-      if (key0 + 3 * kDecTile < s1) load_k<D>(K1, kc, ks, key0 + 3 * kDecTile, s1);
+      fp4_wave_tile<D>(S, K0, qf, R, key0, s1, A.c);
+      load_k<D>(K0, sb, tclamp(key0 + 2 * kDecTile));
+      // tile key0 + 128 from buffers 1
+      if (key0 + kDecTile < s1) {
+        __syncthreads();
+        stage_v<D>(V1, S);
+        load_v<D>(V1, sb, tclamp(key0 + 3 * kDecTile));
+        __syncthreads();
+        fp4_wave_tile<D>(S, K1, qf, R, key0 + kDecTile, s1, A.c);
+        load_k<D>(K1, sb, tclamp(key0 + 3 * kDecTile));
+      }
     }
   }
   write_partial<D>(S, R, A, bk, split);

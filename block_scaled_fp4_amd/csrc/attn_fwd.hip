@@ -128,6 +128,11 @@ struct Fetch {
   uint4_t vs[PER];
 };
 
+// Buffer resources of one (batch, kv head): quantized K and V.
+struct HeadBufs {
+  rsrc_t kc, ks, vc, vs;
+};
+
 struct Problem {
   int64_t H, Hkv, Sq, Sk;
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
@@ -139,35 +144,27 @@ struct Problem {
   float* lse;
 };
 
+// Tile loads go through buffer resources: keys past Sk read as zero codes
+// (their scores are masked), and no branch or clamp sits between the loads,
+// so the next tile's codes stay in flight while the current tile computes.
 template <int D, int BC>
-__device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
-                                          const uint8_t* vs, int64_t key0, int64_t Sk) {
+__device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const HeadBufs& hb, int64_t key0) {
   constexpr int NCH = Fetch<D, BC>::NCH;
   const int t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
     const int q = t + 256 * u;
-    if (q < NCH) {
+    if (NCH % 256 == 0 || q < NCH) {
       // K: chunk q covers key row q/(D/32), d columns 32*(q%(D/32)) .. +32
       const int kr = q / (D / 32), dc = q % (D / 32);
-      const int64_t key = key0 + kr;
-      if (key < Sk) {
-        F.kc[u] = *reinterpret_cast<const uint4_t*>(kc + key * (D / 2) + dc * 16);
-        F.ks[u] = *reinterpret_cast<const uint16_t*>(ks + key * (D / 16) + dc * 2);
-      } else {
-        F.kc[u] = uint4_t{0, 0, 0, 0};
-        F.ks[u] = 0;
-      }
+      const uint32_t key = (uint32_t)key0 + kr;
+      F.kc[u] = buf_load16(hb.kc, key * (D / 2) + dc * 16);
+      F.ks[u] = buf_load2(hb.ks, key * (D / 16) + dc * 2);
       // V: chunk q covers token pair row q/(D/16), columns 16*(q%(D/16)) .. +16
       const int pr = q / (D / 16), cc = q % (D / 16);
-      const int64_t pair = key0 / 2 + pr;
-      if (2 * pair < Sk) {
-        F.vc[u] = *reinterpret_cast<const uint4_t*>(vc + pair * D + cc * 16);
-        F.vs[u] = *reinterpret_cast<const uint4_t*>(vs + (pair / 8) * D + cc * 16);
-      } else {
-        F.vc[u] = uint4_t{0, 0, 0, 0};
-        F.vs[u] = uint4_t{0, 0, 0, 0};
-      }
+      const uint32_t pair = (uint32_t)(key0 / 2) + pr;
+      F.vc[u] = buf_load16(hb.vc, pair * D + cc * 16);
+      F.vs[u] = buf_load16(hb.vs, (pair / 8) * D + cc * 16);
     }
   }
 }
@@ -221,16 +218,16 @@ __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S)
   }
 }
 
-// FP16 path staging: original bf16/fp16 K and V of the tile, converted to fp16.
+// FP16 path staging: original bf16/fp16 K and V of the tile (buffer loads, so
+// keys past Sk read as zero), converted to fp16.
 template <int D, int BC, typename IT>
-__device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const IT* vp, int64_t key0, int64_t Sk) {
+__device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t vr16, int64_t key0) {
   // K: BC rows x D; 8 elements (16 bytes) per step
   constexpr int NK = BC * D / 8;
   for (int q = threadIdx.x; q < NK; q += 256) {
     const int kr = q / (D / 8), dc = q % (D / 8);
-    const int64_t key = key0 + kr;
-    uint4_t w = uint4_t{0, 0, 0, 0};
-    if (key < Sk) w = *reinterpret_cast<const uint4_t*>(kp + key * D + dc * 8);
+    const uint32_t key = (uint32_t)key0 + kr;
+    const uint4_t w = buf_load16(kr16, (key * D + dc * 8) * 2);
     half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
     S.k[kr * Smem<D, BC>::KS8 + dc] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
   }
@@ -238,12 +235,9 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, const IT* kp, const I
   constexpr int NV = (BC / 2) * (D / 8);
   for (int q = threadIdx.x; q < NV; q += 256) {
     const int pr = q / (D / 8), cc = q % (D / 8);
-    const int64_t key = key0 + 2 * pr;
-    uint4_t w0 = uint4_t{0, 0, 0, 0}, w1 = uint4_t{0, 0, 0, 0};
-    if (key < Sk) {
-      w0 = *reinterpret_cast<const uint4_t*>(vp + key * D + cc * 8);
-      w1 = *reinterpret_cast<const uint4_t*>(vp + (key + 1) * D + cc * 8);
-    }
+    const uint32_t key = (uint32_t)key0 + 2 * pr;
+    const uint4_t w0 = buf_load16(vr16, (key * D + cc * 8) * 2);
+    const uint4_t w1 = buf_load16(vr16, ((key + 1) * D + cc * 8) * 2);
     const int pos = vpos(2 * pr);
     half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
     constexpr int VS2 = Smem<D, BC>::VS8 * 4;
@@ -453,10 +447,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   }
   const int tiles_per_block = P.sel_block / BC;
 
-  const uint8_t* kc = P.kc + (b * P.Hkv + hk) * Sk * (D / 2);
-  const uint8_t* ks = P.ks + (b * P.Hkv + hk) * Sk * (D / 16);
-  const uint8_t* vc = P.vc + (b * P.Hkv + hk) * (Sk / 2) * D;
-  const uint8_t* vs = P.vs + (b * P.Hkv + hk) * (Sk / 16) * D;
+  const int64_t bhk = b * P.Hkv + hk;
+  HeadBufs hb;
+  hb.kc = make_rsrc(P.kc + bhk * Sk * (D / 2), (uint32_t)(Sk * (D / 2)));
+  hb.ks = make_rsrc(P.ks + bhk * Sk * (D / 16), (uint32_t)(Sk * (D / 16)));
+  hb.vc = make_rsrc(P.vc + bhk * (Sk / 2) * D, (uint32_t)((Sk / 2) * D));
+  hb.vs = make_rsrc(P.vs + bhk * (Sk / 16) * D, (uint32_t)((Sk / 16) * D));
 
   // ---- FP4 pass: every tile not covered by a selected block
   Fetch<D, BC> F;
@@ -469,13 +465,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   };
   int cur = 0;
   while (cur < ntile && selected(cur)) ++cur;
-  if (cur < ntile) fetch_fp4<D, BC>(F, kc, ks, vc, vs, (int64_t)cur * BC, Sk);
+  if (cur < ntile) fetch_fp4<D, BC>(F, hb, (int64_t)cur * BC);
   while (cur < ntile) {
     int nxt = cur + 1;
     while (nxt < ntile && selected(nxt)) ++nxt;
     __syncthreads();  // previous tile's LDS reads are done
     stage_fp4<D, BC>(F, S);
-    if (nxt < ntile) fetch_fp4<D, BC>(F, kc, ks, vc, vs, (int64_t)nxt * BC, Sk);
+    // always prefetch (past the last tile this is a harmless cached reload)
+    fetch_fp4<D, BC>(F, hb, (int64_t)(nxt < ntile ? nxt : cur) * BC);
     __syncthreads();
     const int64_t key0 = (int64_t)cur * BC;
     const int64_t wrow0 = q0 + 32 * wave;
@@ -505,8 +502,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
       half2_t a = to_half2<IT>(w[0]), bb = to_half2<IT>(w[1]), cc = to_half2<IT>(w[2]), dd = to_half2<IT>(w[3]);
       qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
     }
-    const IT* kp = reinterpret_cast<const IT*>(P.k) + (b * P.Hkv + hk) * Sk * D;
-    const IT* vp = reinterpret_cast<const IT*>(P.v) + (b * P.Hkv + hk) * Sk * D;
+    const rsrc_t kr16 = make_rsrc(reinterpret_cast<const IT*>(P.k) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
+    const rsrc_t vr16 = make_rsrc(reinterpret_cast<const IT*>(P.v) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
     for (int s_i = 0; s_i < nsel; ++s_i) {
       const int blk = sel[s_i];
       for (int tt = 0; tt < tiles_per_block; ++tt) {
@@ -514,7 +511,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
         if (tile >= ntile) break;
         const int64_t key0 = (int64_t)tile * BC;
         __syncthreads();
-        stage_fp16<D, BC, IT>(S, kp, vp, key0, Sk);
+        stage_fp16<D, BC, IT>(S, kr16, vr16, key0);
         __syncthreads();
         const int64_t wrow0 = q0 + 32 * wave;
         const bool wave_dead = P.causal && key0 > wrow0 + 31;
