@@ -34,23 +34,45 @@
 
 namespace fp4dev {
 
-// {fl32(2688 / s), s} for every positive E4M3 scale byte s, compile-time
-// correctly rounded; byte 0 (zero block) maps to {0, 0}.
+// Natural logarithm in double precision for compile-time tables: x = 2^k y
+// with y in [1, 2), ln y = 2 atanh((y - 1) / (y + 1)) by its power series
+// (|z| <= 1/3, so 40 terms are far past double precision).
+constexpr double ct_ln(double x) {
+  int k = 0;
+  while (x >= 2.0) { x /= 2.0; ++k; }
+  while (x < 1.0) { x *= 2.0; --k; }
+  const double z = (x - 1.0) / (x + 1.0), z2 = z * z;
+  double term = z, sum = 0.0;
+  for (int n = 0; n < 40; ++n) {
+    sum += term / (2 * n + 1);
+    term *= z2;
+  }
+  return 2.0 * sum + k * 0.69314718055994530942;
+}
+
+// Level-2 P scale data for every E4M3 scale byte s2 (compile-time):
+//   lg  = log2(2688 / s2), so the level-2 quantization input e * 2688 / s2 is
+//         formed as 2^(x - tm + lg) in one exponential;
+//   inv = s2 / 2688, which turns a block's sum of those inputs back into the
+//         sum of its unquantized e for the softmax denominator;
+//   s   = s2 itself.
+// Byte 0 (a block whose largest e is below half the smallest E4M3 step) has
+// s2 = 0: lg = 0 and inv = 1, so its inputs are the plain e (all of which
+// quantize to code 0) and its denominator sum is still the sum of e.
 struct PScaleTable {
-  float m[128];
-  float s[128];
-  constexpr PScaleTable() : m(), s() {
+  float4_t v[128];  // {lg, inv, s, 0}
+  constexpr PScaleTable() : v() {
     for (int b = 0; b < 128; ++b) {
-      float v = 0.0f;
-      if (b < 8) v = (float)b / 512.0f;
+      double s2 = 0.0;
+      if (b < 8) s2 = (double)b / 512.0;
       else {
         int e = (b >> 3) - 7, mm = b & 7;
-        v = 1.0f + (float)mm / 8.0f;
-        for (int i = 0; i < e; ++i) v *= 2.0f;
-        for (int i = 0; i > e; --i) v /= 2.0f;
+        s2 = 1.0 + (double)mm / 8.0;
+        for (int i = 0; i < e; ++i) s2 *= 2.0;
+        for (int i = 0; i > e; --i) s2 /= 2.0;
       }
-      s[b] = (b == 127) ? 0.0f : v;
-      m[b] = (b == 0 || b == 127) ? 0.0f : 2688.0f / v;
+      if (b == 0 || b == 127) v[b] = float4_t{0.0f, 1.0f, 0.0f, 0.0f};
+      else v[b] = float4_t{(float)(ct_ln(2688.0 / s2) / 0.69314718055994530942), (float)(s2 / 2688.0), (float)s2, 0.0f};
     }
   }
 };
@@ -113,8 +135,7 @@ struct Smem {
   static constexpr int VS8 = BC / 8 + 1;  // 16-byte units per V^T row
   half8_t k[BC * KS8];
   half8_t v[D * VS8];
-  float pm[128];
-  float ps[128];
+  float4_t pt[128];  // level-2 P scale data, indexed by the E4M3 byte
 };
 
 // One tile's worth of quantized K/V held in registers between fetch and stage.
@@ -250,136 +271,170 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t v
   }
 }
 
-// Per-wave state.  The output accumulator U is kept relative to a per-row
-// reference exponent `ref` (the max of the last tile merged): the true
-// unnormalized output is U * 2^ref and the denominator l * 2^ref, so the PV
-// MFMA of a tile accumulates straight into U after one rescale of U by
-// 2^(ref_old - tm).  FP4 tiles add P^ V^ (P^ is in units of 1/2688 of e);
-// the switch to FP16 tiles rescales U by 1/2688 once.
+// Per-wave state.  The output accumulator U and the denominator l are kept
+// relative to a per-row reference exponent m: the true unnormalized output is
+// U * 2^m.  m is a lazily raised running maximum: it moves only when a tile's
+// maximum exceeds it by more than kRaise, so a tile's weight r = 2^(tm - m)
+// stays <= 2^kRaise.  FP4 tiles fold r into the fp16 block scale of P^
+// (P^ r = code * fp16(s2 * r)) and add P^ V^ with P^ in units of e/2688; the
+// switch to FP16 tiles rescales U by 1/2688 once.  FP16 tiles take
+// p = 2^(x - m) = e r directly.  Either way the PV MFMA accumulates straight
+// into U.
 template <int D>
 struct RowState {
   float16_t o[D / 32];  // U^T: d rows (i%4)+8(i/4)+4(lane/32) of each 32-row group, query lane%32
-  float m;              // running max of tile maxima (x units), shared by lanes l and l^32
-  float ref;            // reference exponent of o and l
+  float m;              // reference exponent (x units), shared by lanes l and l^32
   float l;              // this lane's part of the denominator
 };
 
-// Tiles whose maximum is this far (in log2 units) below the running maximum
-// weigh less than 2^-64 of the row and are left out; this bounds the rescale
-// factor of U by 2^64.
+// The reference is raised when a tile maximum is more than 2^4 above it
+// (keeps code * s2 * r <= 2688 * 16 inside fp16); tiles more than 2^64 below
+// it weigh less than 2^-64 of the row and are left out.
+constexpr float kRaise = 4.0f;
 constexpr float kSkipBelow = 64.0f;
 
-// Process one tile for one wave.  FP4: two-level P; else fp16(e).
+__device__ __forceinline__ float max16(const float16_t& a) {
+  float m0 = __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]);
+  float m1 = __builtin_fmaxf(__builtin_fmaxf(a[3], a[4]), a[5]);
+  float m2 = __builtin_fmaxf(__builtin_fmaxf(a[6], a[7]), a[8]);
+  float m3 = __builtin_fmaxf(__builtin_fmaxf(a[9], a[10]), a[11]);
+  float m4 = __builtin_fmaxf(__builtin_fmaxf(a[12], a[13]), a[14]);
+  m0 = __builtin_fmaxf(__builtin_fmaxf(m0, m1), m2);
+  m3 = __builtin_fmaxf(__builtin_fmaxf(m3, m4), a[15]);
+  return __builtin_fmaxf(m0, m3);
+}
+
+// Process one tile for one wave.  FP4: two-level P; else fp16(2^(x - m)).
+//
+// Scores stay raw (S = q.k) until the exponential: with c > 0 the largest
+// fl32(S c) is fl32(max(S) c), so the tile maximum is taken on raw scores and
+// each exponent is one fused x*c - offset.  Each lane holds 16 consecutive
+// keys of one query row per 32-key subtile, i.e. exactly one level-2 block of
+// P, so the block scale is lane-local.
 template <int D, int BC, bool FP4, bool MASK>
 __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
                                           int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
   const int lane = threadIdx.x & 63;
   const int hi = lane >> 5;  // which 16-key half of each 32-key group this lane holds
   constexpr int NG = BC / 32;
+  constexpr int NS = D / 16;
   float16_t acc[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) acc[g] = float16_t{0};
-  // S^T = K Q^T; K fragments are loaded one d-step ahead of their MFMAs (the
-  // scheduling barriers keep the compiler from hoisting all of them)
+  float bmax[NG];
+  // ---- S^T = K Q^T, one 32-key subtile at a time; the mask-and-max of the
+  // previous subtile runs on the VALU while this subtile's MFMAs execute
   const half8_t* kbase = S.k + krow_of_lane(lane & 31) * Smem<D, BC>::KS8 + hi;
-  half8_t kf[2][NG];
+  auto mask_max = [&](int g) {
+    if (MASK) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) kf[0][g] = kbase[32 * g * Smem<D, BC>::KS8];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (s + 1 < D / 16) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) kf[(s + 1) & 1][g] = kbase[32 * g * Smem<D, BC>::KS8 + 2 * (s + 1)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s & 1][g], qf[s], acc[g], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // x = S * c, masked keys -> -inf; lane holds keys 32g + 16*hi + i
-  float tm = -__builtin_inff();
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = acc[g][i] * c;
-      if (MASK) {
+      for (int i = 0; i < 16; ++i) {
         const int64_t key = key0 + 32 * g + 16 * hi + i;
-        if (key >= Sk || (causal && key > qrow)) x = -__builtin_inff();
+        if (key >= Sk || (causal && key > qrow)) acc[g][i] = -__builtin_inff();
       }
-      acc[g][i] = x;
-      tm = __builtin_fmaxf(tm, x);
     }
-  tm = __builtin_fmaxf(tm, xor32(tm));
-  const float mnew = __builtin_fmaxf(R.m, tm);
-  const bool use = tm > -__builtin_inff() && tm >= mnew - kSkipBelow;
-  R.m = mnew;
-  if (!__any(use)) return;  // no row of this wave takes the tile
-  // rescale U and l to the new reference tm (rows that skip keep theirs)
-  {
-    const float f = use ? __builtin_amdgcn_exp2f(R.ref - tm) : 1.0f;  // ref = -inf on the first tile -> 0
+    bmax[g] = max16(acc[g]);
+  };
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    half8_t kf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = kbase[32 * g * Smem<D, BC>::KS8 + 2 * s];
+    acc[g] = float16_t{0};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[s], acc[g], 0, 0, 0);
+    if (g > 0) mask_max(g - 1);
+  }
+  mask_max(NG - 1);
+  float smax = bmax[0];
+#pragma unroll
+  for (int g = 1; g < NG; ++g) smax = __builtin_fmaxf(smax, bmax[g]);
+  smax = __builtin_fmaxf(smax, xor32(smax));
+  const float tm = smax * c;  // tile row maximum of x = fl32(S c)
+  // ---- reference update (rare after the first tiles)
+  const bool live = tm > -__builtin_inff();
+  const bool raise = live && tm > R.m + kRaise;
+  if (__any(raise)) {
+    const float f = raise ? __builtin_amdgcn_exp2f(R.m - tm) : 1.0f;  // R.m = -inf -> 0
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) R.o[t][i] = R.o[t][i] * f;
     R.l = R.l * f;
-    if (use) R.ref = tm;
+    if (raise) R.m = tm;
   }
-  // e = 2^(x - tm); masked keys give 0, rows that skip the tile subtract +inf
-  const float tme = use ? tm : __builtin_inff();
+  const bool use = live && tm >= R.m - kSkipBelow;
+  if (!__any(use)) return;  // no row of this wave takes the tile
+  // rows that skip the tile get offset -inf: every exponential below is 0
+  const float ninf = -__builtin_inff();
+  const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + hi;
   float lsum = 0.0f;
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(acc[g][i] - tme);
-      acc[g][i] = e;
-      lsum += e;
-    }
-  R.l += lsum;
-  // per 32-key subtile: P operands (this lane's values i = 8*h2 .. +8), then U^T += V^T P^T
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    half8_t pf[2];
+  // ---- P operands of subtile g (this lane's values i = 8*h2 .. +8)
+  auto make_p = [&](int g, half8_t (&pf)[2]) {
     if (FP4) {
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, acc[g][i]);
-      const uint32_t sb = f32_to_e4m3(amax * 448.0f);
-      const float M = S.pm[sb];
-      const half_t s2 = (half_t)S.ps[sb];
+      // level 2: s2 = E4M3(448 * max e) from the block maximum, then the
+      // quantization inputs t = e * 2688 / s2 = 2^(x - tm + lg)
+      const float toff = use ? -tm : ninf;
+      const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[g], c, toff));
+      const float4_t ps = S.pt[f32_to_e4m3(emax * 448.0f)];
+      const float off = use ? ps[0] - tm : ninf;
+      const half_t s2r = (half_t)(ps[2] * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf));
+      float bsum = 0.0f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         float t[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = acc[g][8 * h2 + i] * M;
+        for (int i = 0; i < 8; ++i) {
+          t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, off));
+          bsum += t[i];
+        }
         uint32_t w = 0;
         w = cvt_pk_fp4<0>(w, t[0], t[1]);
         w = cvt_pk_fp4<1>(w, t[2], t[3]);
         w = cvt_pk_fp4<2>(w, t[4], t[5]);
         w = cvt_pk_fp4<3>(w, t[6], t[7]);
-        half2_t a = scale_pair(cvt_pk_f16_fp4<0>(w), s2), b = scale_pair(cvt_pk_f16_fp4<1>(w), s2);
-        half2_t cc = scale_pair(cvt_pk_f16_fp4<2>(w), s2), d2 = scale_pair(cvt_pk_f16_fp4<3>(w), s2);
-        pf[h2] = half8_t{a[0], a[1], b[0], b[1], cc[0], cc[1], d2[0], d2[1]};
+        pf[h2] = deq8(w, s2r);
       }
+      lsum = __builtin_fmaf(bsum, ps[1], lsum);
     } else {
+      const float off = use ? -R.m : ninf;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[h2][i] = (half_t)acc[g][8 * h2 + i];
+        for (int i = 0; i < 8; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, off));
+          lsum += p;
+          pf[h2][i] = (half_t)p;
+        }
     }
-    const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + 4 * g + hi;
+  };
+  // ---- U^T += V^T P^T; P of subtile g+1 is built while subtile g's MFMAs run
+  half8_t pcur[2];
+  make_p(0, pcur);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      half8_t vf[D / 32];
+  for (int g = 0; g < NG; ++g) {
+    half8_t vf[2][D / 32];
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) vf[t] = vbase[32 * t * Smem<D, BC>::VS8 + 2 * h2];
-      __builtin_amdgcn_sched_barrier(0);
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t], pf[h2], R.o[t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < D / 32; ++t) vf[h2][t] = vbase[32 * t * Smem<D, BC>::VS8 + 4 * g + 2 * h2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+        R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h2][t], pcur[h2], R.o[t], 0, 0, 0);
+    half8_t pnext[2];
+    if (g + 1 < NG) make_p(g + 1, pnext);
+#pragma unroll
+    for (int k = 0; k < 2 * (D / 32); ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // then up to six VALU ops
+    }
+    if (g + 1 < NG) {
+      pcur[0] = pnext[0];
+      pcur[1] = pnext[1];
     }
   }
+  // FP4: lsum is in units of e (tile-local); FP16: already in units of 2^m
+  R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
 
 template <int D, int BC, typename IT, typename OT>
@@ -407,10 +462,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   const int64_t qrow = q0 + 32 * wave + (lane & 31);
   const int64_t Sk = P.Sk;
 
-  if (threadIdx.x < 128) {
-    S.pm[threadIdx.x] = kPScale.m[threadIdx.x];
-    S.ps[threadIdx.x] = kPScale.s[threadIdx.x];
-  }
+  if (threadIdx.x < 128) S.pt[threadIdx.x] = kPScale.v[threadIdx.x];
   // Q^ fragment (B operand): query qrow, d = 16 s + 8 hi .. +8
   half8_t qf[D / 16];
   {
@@ -430,7 +482,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) R.o[t] = float16_t{0};
   R.m = -__builtin_inff();
-  R.ref = -__builtin_inff();
   R.l = 0.0f;
 
   const int64_t qend = q0 + kBr < P.Sq ? q0 + kBr : P.Sq;  // rows of this workgroup: [q0, qend)
@@ -538,7 +589,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
                    R.o[t][4 * j + 3] * inv);
       }
     if (P.lse && hi == 0)
-      P.lse[bh * P.Sq + qrow] = ltot > 0.0f ? (R.ref + __builtin_log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
+      P.lse[bh * P.Sq + qrow] = ltot > 0.0f ? (R.m + __builtin_log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
   }
 }
 

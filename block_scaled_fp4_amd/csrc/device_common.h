@@ -33,12 +33,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 // Nearest E4M3 byte to v >= 0 (finite), ties to the even mantissa, saturating
 // at 0x7E = 448 (never the NaN byte 0x7F).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  if (v >= 448.0f) return 0x7Eu;
-  if (v < 0x1p-6f) return (uint32_t)__builtin_rintf(v * 512.0f);  // subnormal step 2^-9 (exact scaling)
-  uint32_t bits = __float_as_uint(v);
-  bits += 0x7FFFFu + ((bits >> 20) & 1u);  // round mantissa to 3 bits, ties to even
-  uint32_t e = (bits >> 23) - 120u;        // biased E4M3 exponent
-  uint32_t byte = (e << 3) | ((bits >> 20) & 7u);
+  // Branch-free: both the normal-range rounding and the subnormal one are
+  // formed and the right one selected; values past 448 saturate through the
+  // final minimum (their exponent field lands above 0x7E).
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);  // round mantissa to 3 bits, ties to even
+  const uint32_t normal = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);  // subnormal step 2^-9 (exact scaling)
+  const uint32_t byte = v < 0x1p-6f ? sub : normal;
   return byte > 0x7Eu ? 0x7Eu : byte;
 }
 
