@@ -128,13 +128,23 @@ __device__ __forceinline__ half2_t to_half2<half_t>(uint32_t w) {
 }
 
 // LDS tiles are declared in 16-byte units so that every fragment read is a
-// single ds_read_b128 with an immediate offset.
+// single ds_read_b128 with an immediate offset.  The LDS has 32 four-byte
+// banks.  One unit of padding per row keeps the fragment reads conflict-free;
+// V^T rows (one per d) additionally shift by vpad(d / 16) units, because the
+// staging writes of one wave span d rows 16 apart, which the row padding
+// alone maps to the same banks.  vpad never decreases, so rows never overlap.
 template <int D, int BC>
 struct Smem {
   static constexpr int KS8 = D / 8 + 1;   // 16-byte units per K row (one unit of pad)
   static constexpr int VS8 = BC / 8 + 1;  // 16-byte units per V^T row
+  static __device__ __forceinline__ constexpr int vpad(int grp) {
+    return D == 128 ? 4 * (grp >> 1) + (grp & 1) : 4 * grp;
+  }
+  // V^T row of d = r + 32 t (r < 32): vrow(r) + 32 t VS8 + vpad_t(t)
+  static __device__ __forceinline__ constexpr int vrow(int r) { return r * VS8 + vpad(r >> 4); }
+  static __device__ __forceinline__ constexpr int vpad_t(int t) { return D == 128 ? 4 * t : 8 * t; }
   half8_t k[BC * KS8];
-  half8_t v[D * VS8];
+  half8_t v[D * VS8 + 16];
   float4_t pt[128];  // level-2 P scale data, indexed by the E4M3 byte
 };
 
@@ -230,10 +240,11 @@ __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S)
         const half2_t sa = e4m3x2_to_half2(sw), sb = e4m3x2_hi_to_half2(sw);
         const int col = 16 * cc + 4 * w;
         constexpr int VS2 = Smem<D, BC>::VS8 * 4;  // half2 units per V^T row
-        v2[(col + 0) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<0>(cw), sa[0]);
-        v2[(col + 1) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<1>(cw), sa[1]);
-        v2[(col + 2) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<2>(cw), sb[0]);
-        v2[(col + 3) * VS2 + pos / 2] = scale_pair(cvt_pk_f16_fp4<3>(cw), sb[1]);
+        half2_t* dst = v2 + col * VS2 + 4 * Smem<D, BC>::vpad(cc) + pos / 2;
+        dst[0 * VS2] = scale_pair(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        dst[1 * VS2] = scale_pair(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        dst[2 * VS2] = scale_pair(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        dst[3 * VS2] = scale_pair(cvt_pk_f16_fp4<3>(cw), sb[1]);
       }
     }
   }
@@ -265,8 +276,10 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t v
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half2_t a = to_half2<IT>(w0[j]), b = to_half2<IT>(w1[j]);
-      v2[(cc * 8 + 2 * j) * VS2 + pos / 2] = half2_t{a[0], b[0]};
-      v2[(cc * 8 + 2 * j + 1) * VS2 + pos / 2] = half2_t{a[1], b[1]};
+      const int col = cc * 8 + 2 * j;
+      half2_t* dst = v2 + col * VS2 + 4 * Smem<D, BC>::vpad(col >> 4) + pos / 2;
+      dst[0] = half2_t{a[0], b[0]};
+      dst[VS2] = half2_t{a[1], b[1]};
     }
   }
 }
@@ -365,7 +378,7 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   if (!__any(use)) return;  // no row of this wave takes the tile
   // rows that skip the tile get offset -inf: every exponential below is 0
   const float ninf = -__builtin_inff();
-  const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + hi;
+  const half8_t* vbase = S.v + Smem<D, BC>::vrow(lane & 31) + hi;
   float lsum = 0.0f;
   // ---- P operands of subtile g (this lane's values i = 8*h2 .. +8)
   auto make_p = [&](int g, half8_t (&pf)[2]) {
@@ -415,7 +428,7 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) vf[h2][t] = vbase[32 * t * Smem<D, BC>::VS8 + 4 * g + 2 * h2];
+      for (int t = 0; t < D / 32; ++t) vf[h2][t] = vbase[32 * t * Smem<D, BC>::VS8 + Smem<D, BC>::vpad_t(t) + 4 * g + 2 * h2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
