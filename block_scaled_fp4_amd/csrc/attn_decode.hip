@@ -25,6 +25,17 @@ namespace fp4dev {
 constexpr int kDecTile = 128;  // keys per staged tile
 constexpr int kGmax = 16;      // query heads per kv head handled by one workgroup
 
+// V^T rows (one per d) of a staged tile: row d starts at d * VS8 + dec_vpad(d / 16)
+// 16-byte units.  The LDS has 32 four-byte banks; a wave's staging writes
+// cover d rows 16 apart, which the one-unit row padding alone puts on the
+// same banks.  The non-decreasing shift spreads them (rows never overlap);
+// fragment reads take one 16-row group per instruction, so the shift is an
+// immediate offset there.
+template <int D>
+__device__ __forceinline__ constexpr int dec_vpad(int grp) {
+  return D == 128 ? 2 * grp : 4 * grp;
+}
+
 template <int D>
 struct DecSmem {
   static constexpr int KS8 = D / 8 + 1;         // 16-byte units per K row (one unit of pad)
@@ -32,7 +43,7 @@ struct DecSmem {
   union {
     struct {
       half8_t k[kDecTile * KS8];
-      half8_t v[D * VS8];
+      half8_t v[D * VS8 + 16];
     };
     struct {  // wave-state merge, used after the last tile
       float red_m[4][kGmax];
@@ -47,7 +58,7 @@ template <int D>
 struct DecSmemV {
   static constexpr int VS8 = kDecTile / 8 + 1;
   union {
-    half8_t v[D * VS8];
+    half8_t v[D * VS8 + 16];
     struct {
       float red_m[4][kGmax];
       float red_l[4][kGmax];
@@ -123,10 +134,11 @@ __device__ __forceinline__ void dec_stage_fp4(const DecFetch<D>& F, DecSmem<D>& 
         const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
         const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
         const int col = 16 * cc + 4 * w;
-        v2[(col + 0) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
-        v2[(col + 1) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
-        v2[(col + 2) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
-        v2[(col + 3) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
+        half2_t* dst = v2 + col * VS2 + 4 * dec_vpad<D>(cc) + pr;
+        dst[0 * VS2] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        dst[1 * VS2] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        dst[2 * VS2] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        dst[3 * VS2] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
       }
     }
   }
@@ -174,8 +186,10 @@ __device__ __forceinline__ void dec_stage_bf16_v(DecSmem<D>& S, const uint16_t* 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half2_t a = bf16x2_to_half2(w0[j]), b = bf16x2_to_half2(w1[j]);
-      v2[(cc * 8 + 2 * j) * VS2 + pr] = half2_t{a[0], b[0]};
-      v2[(cc * 8 + 2 * j + 1) * VS2 + pr] = half2_t{a[1], b[1]};
+      const int col = cc * 8 + 2 * j;
+      half2_t* dst = v2 + col * VS2 + 4 * dec_vpad<D>(col >> 4) + pr;
+      dst[0] = half2_t{a[0], b[0]};
+      dst[VS2] = half2_t{a[1], b[1]};
     }
   }
 }
@@ -235,7 +249,7 @@ __device__ __forceinline__ void dec_wave_tile(const DecSmem<D>& S, const half8_t
   }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmem<D>::VS8 + kw / 8 + q4];
+    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmem<D>::VS8 + dec_vpad<D>(t) + kw / 8 + q4];
     R.o[t] = R.o[t] * alpha;
     R.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, R.o[t], 0, 0, 0);
   }
@@ -340,10 +354,11 @@ __device__ __forceinline__ void stage_v(const VRegs<D>& V, DecSmemV<D>& S) {
         const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
         const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
         const int col = 16 * cc + 4 * w;
-        v2[(col + 0) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
-        v2[(col + 1) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
-        v2[(col + 2) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
-        v2[(col + 3) * VS2 + pr] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
+        half2_t* dst = v2 + col * VS2 + 4 * dec_vpad<D>(cc) + pr;
+        dst[0 * VS2] = scale_h2(cvt_pk_f16_fp4<0>(cw), sa[0]);
+        dst[1 * VS2] = scale_h2(cvt_pk_f16_fp4<1>(cw), sa[1]);
+        dst[2 * VS2] = scale_h2(cvt_pk_f16_fp4<2>(cw), sb[0]);
+        dst[3 * VS2] = scale_h2(cvt_pk_f16_fp4<3>(cw), sb[1]);
       }
     }
   }
@@ -393,7 +408,7 @@ __device__ __forceinline__ void fp4_wave_tile(const DecSmemV<D>& S, const KRegs<
   }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmemV<D>::VS8 + kw / 8 + q4];
+    const half8_t a = S.v[(16 * t + (lane & 15)) * DecSmemV<D>::VS8 + dec_vpad<D>(t) + kw / 8 + q4];
     R.o[t] = R.o[t] * alpha;
     R.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, R.o[t], 0, 0, 0);
   }
