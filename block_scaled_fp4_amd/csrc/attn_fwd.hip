@@ -128,24 +128,43 @@ __device__ __forceinline__ half2_t to_half2<half_t>(uint32_t w) {
 }
 
 // LDS tiles are declared in 16-byte units so that every fragment read is a
-// single ds_read_b128 with an immediate offset.  The LDS has 32 four-byte
-// banks.  One unit of padding per row keeps the fragment reads conflict-free;
-// V^T rows (one per d) additionally shift by vpad(d / 16) units, because the
-// staging writes of one wave span d rows 16 apart, which the row padding
-// alone maps to the same banks.  vpad never decreases, so rows never overlap.
+// single ds_read_b128 with an immediate offset.  Bank rules of the gfx950 LDS
+// (measured with the bank-conflict counter): a 16-byte read is conflict-free
+// when each half-wave's distinct 16-byte units differ mod 32; a 4-byte write
+// when each half-wave's dwords differ mod 32; a 16-byte write when each group
+// of 8 lanes' units differ mod 8.  Rows carry one unit of padding (K and V^T
+// fragment reads), and V^T rows of d-group c = d / 16 shift by vpad(c) units
+// so that the staging writes, whose half-waves cover d-groups 32 rows apart,
+// spread over all banks.  vpad is equal within each 32-row block (reads keep
+// a lane-independent offset) and never decreases (rows never overlap).
 template <int D, int BC>
 struct Smem {
   static constexpr int KS8 = D / 8 + 1;   // 16-byte units per K row (one unit of pad)
   static constexpr int VS8 = BC / 8 + 1;  // 16-byte units per V^T row
   static __device__ __forceinline__ constexpr int vpad(int grp) {
-    return D == 128 ? 4 * (grp >> 1) + (grp & 1) : 4 * grp;
+    return D == 128 ? 4 * (grp >> 2) + ((grp >> 1) & 1) : 4 * (grp >> 1);
   }
-  // V^T row of d = r + 32 t (r < 32): vrow(r) + 32 t VS8 + vpad_t(t)
-  static __device__ __forceinline__ constexpr int vrow(int r) { return r * VS8 + vpad(r >> 4); }
-  static __device__ __forceinline__ constexpr int vpad_t(int t) { return D == 128 ? 4 * t : 8 * t; }
+  // V^T row of d = r + 32 t (r < 32): r * VS8 + vrow_t(t)
+  static __device__ __forceinline__ constexpr int vrow_t(int t) { return 32 * t * VS8 + vpad(2 * t); }
   half8_t k[BC * KS8];
   half8_t v[D * VS8 + 16];
   float4_t pt[128];  // level-2 P scale data, indexed by the E4M3 byte
+};
+
+// Which 16-byte chunk of the tile's codes each thread fetches and stages.
+// K chunk: key row kr, 32-column block dc; a group of 8 lanes takes 8 rows of
+// one block (16-byte LDS writes).  V chunk: token pair pr, 16-column block cc;
+// a half-wave takes 64/(D/16) pairs of every other block, so its d rows are
+// 32 apart (4-byte LDS writes).  Either way a wave reads whole rows of codes.
+template <int D>
+struct StageMap {
+  static constexpr int NDC = D / 32, NCC = D / 16, PPW = 64 / NCC;
+  static __device__ __forceinline__ int k_row(int wv, int l, int u) {
+    return (l & 7) + 8 * ((l >> 3) / NDC) + (64 / NDC) * (wv + 4 * u);
+  }
+  static __device__ __forceinline__ int k_dc(int l) { return (l >> 3) % NDC; }
+  static __device__ __forceinline__ int v_pair(int wv, int l, int u) { return PPW * (wv + 4 * u) + (l & 31) % PPW; }
+  static __device__ __forceinline__ int v_cc(int l) { return (l >> 5) + 2 * ((l & 31) / PPW); }
 };
 
 // One tile's worth of quantized K/V held in registers between fetch and stage.
@@ -180,19 +199,18 @@ struct Problem {
 // so the next tile's codes stay in flight while the current tile computes.
 template <int D, int BC>
 __device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const HeadBufs& hb, int64_t key0) {
-  constexpr int NCH = Fetch<D, BC>::NCH;
-  const int t = threadIdx.x;
+  using M = StageMap<D>;
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
-    const int q = t + 256 * u;
-    if (NCH % 256 == 0 || q < NCH) {
-      // K: chunk q covers key row q/(D/32), d columns 32*(q%(D/32)) .. +32
-      const int kr = q / (D / 32), dc = q % (D / 32);
+    const int kr = M::k_row(wv, l, u), dc = M::k_dc(l);
+    if (Fetch<D, BC>::NCH % 256 == 0 || kr < BC) {  // every thread has a chunk when NCH is a multiple of 256
       const uint32_t key = (uint32_t)key0 + kr;
       F.kc[u] = buf_load16(hb.kc, key * (D / 2) + dc * 16);
       F.ks[u] = buf_load2(hb.ks, key * (D / 16) + dc * 2);
-      // V: chunk q covers token pair row q/(D/16), columns 16*(q%(D/16)) .. +16
-      const int pr = q / (D / 16), cc = q % (D / 16);
+    }
+    const int pr = M::v_pair(wv, l, u), cc = M::v_cc(l);
+    if (Fetch<D, BC>::NCH % 256 == 0 || pr < BC / 2) {
       const uint32_t pair = (uint32_t)(key0 / 2) + pr;
       F.vc[u] = buf_load16(hb.vc, pair * D + cc * 16);
       F.vs[u] = buf_load16(hb.vs, (pair / 8) * D + cc * 16);
@@ -219,20 +237,21 @@ __device__ __forceinline__ half8_t deq8(uint32_t cw, half_t s) {
 
 template <int D, int BC>
 __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S) {
-  constexpr int NCH = Fetch<D, BC>::NCH;
-  const int t = threadIdx.x;
+  using M = StageMap<D>;
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
   half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
 #pragma unroll
   for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
-    const int q = t + 256 * u;
-    if (q < NCH) {
-      const int kr = q / (D / 32), dc = q % (D / 32);
+    const int kr = M::k_row(wv, l, u), dc = M::k_dc(l);
+    if (Fetch<D, BC>::NCH % 256 == 0 || kr < BC) {  // every thread has a chunk when NCH is a multiple of 256
       const half2_t ks2 = e4m3x2_to_half2(F.ks[u]);
       half8_t* dst = S.k + kr * Smem<D, BC>::KS8 + dc * 4;
 #pragma unroll
       for (int w = 0; w < 4; ++w) dst[w] = deq8(F.kc[u][w], w < 2 ? ks2[0] : ks2[1]);
-      // V: byte j of dword w = column 16*cc + 4*w + j, tokens (2*pr, 2*pr+1)
-      const int pr = q / (D / 16), cc = q % (D / 16);
+    }
+    // V: byte j of dword w = column 16*cc + 4*w + j, tokens (2*pr, 2*pr+1)
+    const int pr = M::v_pair(wv, l, u), cc = M::v_cc(l);
+    if (Fetch<D, BC>::NCH % 256 == 0 || pr < BC / 2) {
       const int pos = vpos(2 * pr);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -263,23 +282,30 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t v
     half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
     S.k[kr * Smem<D, BC>::KS8 + dc] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
   }
-  // V: token pairs x 8 columns per step -> V^T
-  constexpr int NV = (BC / 2) * (D / 8);
-  for (int q = threadIdx.x; q < NV; q += 256) {
-    const int pr = q / (D / 8), cc = q % (D / 8);
+  // V: a chunk is a token pair x 8 columns -> V^T.  As in the FP4 staging, a
+  // half-wave's chunks sit in d-groups 32 rows apart (conflict-free writes).
+  constexpr int NC8 = D / 8, PPW = 1024 / D;
+  constexpr int NV = (BC / 2) * NC8;
+  static_assert(NV % 256 == 0, "whole rounds of 256 chunks");
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6, lp = l & 31;
+  half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+  constexpr int VS2 = Smem<D, BC>::VS8 * 4;
+#pragma unroll
+  for (int it = 0; it < NV / 256; ++it) {
+    const int z = wv + 4 * it;
+    const int pr = PPW * (z >> 1) + lp % PPW;
+    const int grp = (l >> 5) + 2 * (lp / PPW);
+    const int c8 = 2 * grp + (z & 1);
     const uint32_t key = (uint32_t)key0 + 2 * pr;
-    const uint4_t w0 = buf_load16(vr16, (key * D + cc * 8) * 2);
-    const uint4_t w1 = buf_load16(vr16, ((key + 1) * D + cc * 8) * 2);
+    const uint4_t w0 = buf_load16(vr16, (key * D + c8 * 8) * 2);
+    const uint4_t w1 = buf_load16(vr16, ((key + 1) * D + c8 * 8) * 2);
     const int pos = vpos(2 * pr);
-    half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
-    constexpr int VS2 = Smem<D, BC>::VS8 * 4;
+    half2_t* dst = v2 + 8 * c8 * VS2 + 4 * Smem<D, BC>::vpad(grp) + pos / 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half2_t a = to_half2<IT>(w0[j]), b = to_half2<IT>(w1[j]);
-      const int col = cc * 8 + 2 * j;
-      half2_t* dst = v2 + col * VS2 + 4 * Smem<D, BC>::vpad(col >> 4) + pos / 2;
-      dst[0] = half2_t{a[0], b[0]};
-      dst[VS2] = half2_t{a[1], b[1]};
+      dst[(2 * j) * VS2] = half2_t{a[0], b[0]};
+      dst[(2 * j + 1) * VS2] = half2_t{a[1], b[1]};
     }
   }
 }
@@ -346,15 +372,25 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
     }
     bmax[g] = max16(acc[g]);
   };
+  // Fragment reads run kAhead MFMAs ahead of their use (LDS latency is
+  // several MFMA lengths) through a register ring; the fences keep reads and
+  // MFMAs in this order and let only ALU work (the mask-and-max of the
+  // previous subtile) move between them.
+  {
+    constexpr int NM = NG * NS, kAhead = 4, kRing = kAhead + 2;
+    half8_t ring[kRing];
+    auto kfrag = [&](int i) { return kbase[32 * (i / NS) * Smem<D, BC>::KS8 + 2 * (i % NS)]; };
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    half8_t kf[NS];
+    for (int i = 0; i < kAhead; ++i) ring[i] = kfrag(i);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kf[s] = kbase[32 * g * Smem<D, BC>::KS8 + 2 * s];
-    acc[g] = float16_t{0};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[s], acc[g], 0, 0, 0);
-    if (g > 0) mask_max(g - 1);
+    for (int i = 0; i < NM; ++i) {
+      const int g = i / NS, s = i % NS;
+      if (s == 0) acc[g] = float16_t{0};
+      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], qf[s], acc[g], 0, 0, 0);
+      if (i + kAhead < NM) ring[(i + kAhead) % kRing] = kfrag(i + kAhead);
+      if (s == 0 && g > 0) mask_max(g - 1);
+      __builtin_amdgcn_sched_barrier(0x0407);  // ALU (VALU, SALU, transcendental) may cross
+    }
   }
   mask_max(NG - 1);
   float smax = bmax[0];
@@ -378,72 +414,86 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   if (!__any(use)) return;  // no row of this wave takes the tile
   // rows that skip the tile get offset -inf: every exponential below is 0
   const float ninf = -__builtin_inff();
-  const half8_t* vbase = S.v + Smem<D, BC>::vrow(lane & 31) + hi;
+  const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + hi;
   float lsum = 0.0f;
-  // ---- P operands of subtile g (this lane's values i = 8*h2 .. +8)
-  auto make_p = [&](int g, half8_t (&pf)[2]) {
+  // ---- P operands of subtile g, built in two halves (this lane's values
+  // i = 8*h2 .. +8); prep_p forms the subtile's level-2 scale data first
+  struct PPrep {
+    float off, inv;
+    half_t s2r;
+  };
+  auto prep_p = [&](int g) {
+    PPrep q;
     if (FP4) {
       // level 2: s2 = E4M3(448 * max e) from the block maximum, then the
       // quantization inputs t = e * 2688 / s2 = 2^(x - tm + lg)
       const float toff = use ? -tm : ninf;
       const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[g], c, toff));
       const float4_t ps = S.pt[f32_to_e4m3(emax * 448.0f)];
-      const float off = use ? ps[0] - tm : ninf;
-      const half_t s2r = (half_t)(ps[2] * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf));
-      float bsum = 0.0f;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, off));
-          bsum += t[i];
-        }
-        uint32_t w = 0;
-        w = cvt_pk_fp4<0>(w, t[0], t[1]);
-        w = cvt_pk_fp4<1>(w, t[2], t[3]);
-        w = cvt_pk_fp4<2>(w, t[4], t[5]);
-        w = cvt_pk_fp4<3>(w, t[6], t[7]);
-        pf[h2] = deq8(w, s2r);
-      }
-      lsum = __builtin_fmaf(bsum, ps[1], lsum);
+      q.off = use ? ps[0] - tm : ninf;
+      q.inv = ps[1];
+      q.s2r = (half_t)(ps[2] * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf));
     } else {
-      const float off = use ? -R.m : ninf;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, off));
-          lsum += p;
-          pf[h2][i] = (half_t)p;
-        }
+      q.off = use ? -R.m : ninf;
+      q.inv = 1.0f;
+      q.s2r = (half_t)1.0f;
     }
+    return q;
   };
-  // ---- U^T += V^T P^T; P of subtile g+1 is built while subtile g's MFMAs run
-  half8_t pcur[2];
-  make_p(0, pcur);
+  auto make_half = [&](int g, int h2, const PPrep& q, half8_t& pf) {
+    float t[8], bsum = 0.0f;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    half8_t vf[2][D / 32];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) vf[h2][t] = vbase[32 * t * Smem<D, BC>::VS8 + Smem<D, BC>::vpad_t(t) + 4 * g + 2 * h2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h2][t], pcur[h2], R.o[t], 0, 0, 0);
-    half8_t pnext[2];
-    if (g + 1 < NG) make_p(g + 1, pnext);
-#pragma unroll
-    for (int k = 0; k < 2 * (D / 32); ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // then up to six VALU ops
+    for (int i = 0; i < 8; ++i) {
+      t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, q.off));
+      bsum += t[i];
     }
-    if (g + 1 < NG) {
-      pcur[0] = pnext[0];
-      pcur[1] = pnext[1];
+    if (FP4) {
+      uint32_t w = 0;
+      w = cvt_pk_fp4<0>(w, t[0], t[1]);
+      w = cvt_pk_fp4<1>(w, t[2], t[3]);
+      w = cvt_pk_fp4<2>(w, t[4], t[5]);
+      w = cvt_pk_fp4<3>(w, t[6], t[7]);
+      pf = deq8(w, q.s2r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[i] = (half_t)t[i];
+    }
+    lsum = __builtin_fmaf(bsum, q.inv, lsum);
+  };
+  // ---- U^T += V^T P^T with V fragments through the same kind of ring; the P
+  // halves of subtile g+1 are built between subtile g's MFMAs.
+  {
+    constexpr int NT = D / 32, NPV = 2 * NT, NM = NG * NPV, kAhead = 4, kRing = kAhead + 1;
+    half8_t ring[kRing];
+    // MFMA i: subtile g = i / NPV, h2 = (i % NPV) / NT, t = i % NT
+    auto vfrag = [&](int i) {
+      const int g = i / NPV, h2 = (i % NPV) / NT, t = i % NT;
+      return vbase[Smem<D, BC>::vrow_t(t) + 4 * g + 2 * h2];
+    };
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) ring[i] = vfrag(i);
+    half8_t pcur[2], pnext[2];
+    {
+      const PPrep q0 = prep_p(0);
+      make_half(0, 0, q0, pcur[0]);
+      make_half(0, 1, q0, pcur[1]);
+    }
+    PPrep qn;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int g = i / NPV, k = i % NPV, h2 = k / NT, t = k % NT;
+      R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], pcur[h2], R.o[t], 0, 0, 0);
+      if (i + kAhead < NM) ring[(i + kAhead) % kRing] = vfrag(i + kAhead);
+      if (g + 1 < NG) {
+        if (k == 0) qn = prep_p(g + 1);
+        if (k == 1) make_half(g + 1, 0, qn, pnext[0]);
+        if (k == NPV / 2 + 1) make_half(g + 1, 1, qn, pnext[1]);
+        if (k == NPV - 1) {
+          pcur[0] = pnext[0];
+          pcur[1] = pnext[1];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // FP4: lsum is in units of e (tile-local); FP16: already in units of 2^m
