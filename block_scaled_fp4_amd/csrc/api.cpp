@@ -317,7 +317,8 @@ size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* c) {
   if (!c || c->struct_size < sizeof(fp4_kv_cache) || Hq <= 0 || c->B <= 0 || c->d <= 0) return 0;
   int64_t split_len = 0;
   int ns = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &split_len);
-  size_t n = (size_t)(c->B * Hq) * (size_t)(ns + 1);
+  int nf = fp4i_decode_full_splits((int64_t)c->n_sink + c->n_recent);
+  size_t n = (size_t)(c->B * Hq) * (size_t)(ns + nf);
   return align256(n * (size_t)c->d * sizeof(float)) + align256(n * 2 * sizeof(float));
 }
 
@@ -357,7 +358,8 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float
   L.out = out;
   L.lse = lse;
   L.nsplit = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &L.split_len);
-  size_t n = (size_t)(c->B * Hq) * (size_t)(L.nsplit + 1);
+  L.nfull = fp4i_decode_full_splits((int64_t)c->n_sink + c->n_recent);
+  size_t n = (size_t)(c->B * Hq) * (size_t)(L.nsplit + L.nfull);
   L.part_o = (float*)workspace;
   L.part_ml = (float*)((char*)workspace + align256(n * (size_t)c->d * sizeof(float)));
   return hip_status(fp4i_launch_decode(L, (hipStream_t)stream), "fp4_attention_decode launch");

@@ -125,6 +125,9 @@ __device__ __forceinline__ uint4_t buf_load16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint2_t buf_load8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }

@@ -78,10 +78,12 @@ struct DecodeLaunch {
   void* out;
   float* lse;
   int nsplit;        // context splits per (b, kv head)
+  int nfull;         // full-precision (sink + recent) workgroups per (b, kv head)
   int64_t split_len; // tokens per split of the FP4 region (multiple of the chunk)
-  float* part_o;     // [B*Hq, nsplit+1, d]
-  float* part_ml;    // [B*Hq, nsplit+1, 2]
+  float* part_o;     // [B*Hq, nsplit+nfull, d]
+  float* part_ml;    // [B*Hq, nsplit+nfull, 2]
 };
 
 int fp4i_decode_splits(int64_t B, int64_t Hkv, int64_t mid_cap, int64_t* split_len);
+int fp4i_decode_full_splits(int64_t n_full);
 hipError_t fp4i_launch_decode(const DecodeLaunch& L, hipStream_t stream);
