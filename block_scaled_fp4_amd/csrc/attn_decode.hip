@@ -18,9 +18,9 @@
 //     loads D/16 consecutive channels of four token pairs and a 4x4 byte
 //     transpose (v_perm_b32) turns them into one dword of 8 consecutive
 //     tokens per channel -- exactly an A-operand row of the PV product;
-//   - a small kernel reads the bf16 sink and recent tokens (128 per
-//     workgroup); the waves of a workgroup merge their (m, l, O) in LDS and a
-//     third kernel merges the partials of all workgroups.
+//   - extra workgroups of the same launch read the bf16 sink and recent
+//     tokens (128 per workgroup); the waves of a workgroup merge their
+//     (m, l, O) in LDS and a second kernel merges the workgroups' partials.
 // Probabilities enter the PV product as fp16 (q, K, V and P are not
 // re-quantized; P rounding is within the tolerance of the plain definition).
 #include "device_common.h"
@@ -70,7 +70,7 @@ struct DecArgs {
   int64_t Hq, Hkv, nbk;  // nbk = B * Hkv
   int G, n_sink, n_recent;
   int64_t mid_cap, split_len;
-  int nsplit, ns1;  // FP4 splits; partials per row (FP4 splits + full-precision splits)
+  int nsplit, nfull, ns1;  // FP4 splits, full-precision workgroups, partials per row (their sum)
   const uint16_t *k_sink, *v_sink, *k_recent, *v_recent;
   const uint8_t *kc, *ks, *vc, *vs;
   const int32_t* mid_len;
@@ -339,16 +339,47 @@ __device__ __forceinline__ void write_partial(DecRed<D>& S, const DecState<D>& R
   }
 }
 
-// grid: B*Hkv*nsplit; one workgroup per split of the FP4 region of a
-// (batch, kv head), partial index = split.
+// Workgroup f of a (batch, kv head) over its full-precision tokens
+// [128 f, 128 f + 128), one step per wave; partial index nsplit + f.
 template <int D>
-__global__ void __launch_bounds__(64 * kDecWaves, 3) decode_fp4_kernel(DecArgs A) {
+__device__ __forceinline__ void full_workgroup(DecRed<D>& S, const DecArgs& A, int64_t bk, int f, int wave) {
+  half8_t qf[D / 32];
+  load_q<D>(qf, A, bk);
+  DecState<D> R;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
+  R.m = -__builtin_inff();
+  R.l = 0.0f;
+  const uint32_t n_full = (uint32_t)(A.n_sink + A.n_recent);
+  const uint32_t key0 = (uint32_t)(kStep * kDecWaves * f + kStep * wave);
+  if (key0 < n_full) {
+    const uint16_t* ksk = A.k_sink + bk * (int64_t)A.n_sink * D;
+    const uint16_t* vsk = A.v_sink + bk * (int64_t)A.n_sink * D;
+    const uint16_t* krc = A.k_recent + bk * (int64_t)A.n_recent * D;
+    const uint16_t* vrc = A.v_recent + bk * (int64_t)A.n_recent * D;
+    bf16_step<D>(ksk, krc, vsk, vrc, A.n_sink, n_full, qf, R, key0, A.c);
+  }
+  write_partial<D>(S, R, A, bk, A.nsplit + f);
+}
+
+// grid: B*Hkv*nfull workgroups over the full-precision (bf16 sink + recent)
+// tokens, then B*Hkv*nsplit over the splits of the FP4 region of each
+// (batch, kv head) (partial index = split).
+template <int D>
+__global__ void __launch_bounds__(64 * kDecWaves, 3) decode_kernel(DecArgs A) {
   __shared__ DecRed<D> S;
-  const int64_t gi = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t nfw = A.nbk * A.nfull;
+  if ((int64_t)blockIdx.x < nfw) {
+    // (its own scope, returning: the two kinds of workgroup share no
+    // registers, so the rare bf16 one does not raise the kernel's count)
+    full_workgroup<D>(S, A, (int64_t)blockIdx.x / A.nfull, (int)((int64_t)blockIdx.x % A.nfull), wave);
+    return;
+  }
+  const int64_t gi = (int64_t)blockIdx.x - nfw;
   const int64_t bk = gi / A.nsplit;
   const int split = (int)(gi % A.nsplit);
   const int64_t b = bk / A.Hkv;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   half8_t qf[D / 32];
   load_q<D>(qf, A, bk);
   DecState<D> R;
@@ -397,34 +428,6 @@ __global__ void __launch_bounds__(64 * kDecWaves, 3) decode_fp4_kernel(DecArgs A
   write_partial<D>(S, R, A, bk, split);
 }
 
-// grid: B*Hkv*nfull; workgroup f of a (batch, kv head) reads full-precision
-// tokens [128 f, 128 f + 128) (one step per wave), partial index nsplit + f.
-template <int D>
-__global__ void __launch_bounds__(64 * kDecWaves) decode_full_kernel(DecArgs A, int nfull) {
-  __shared__ DecRed<D> S;
-  const int64_t gi = blockIdx.x;
-  const int64_t bk = gi / nfull;
-  const int f = (int)(gi % nfull);
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  half8_t qf[D / 32];
-  load_q<D>(qf, A, bk);
-  DecState<D> R;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
-  R.m = -__builtin_inff();
-  R.l = 0.0f;
-  const uint32_t n_full = (uint32_t)(A.n_sink + A.n_recent);
-  const uint32_t key0 = (uint32_t)(kStep * kDecWaves * f + kStep * wave);
-  if (key0 < n_full) {
-    const uint16_t* ksk = A.k_sink + bk * (int64_t)A.n_sink * D;
-    const uint16_t* vsk = A.v_sink + bk * (int64_t)A.n_sink * D;
-    const uint16_t* krc = A.k_recent + bk * (int64_t)A.n_recent * D;
-    const uint16_t* vrc = A.v_recent + bk * (int64_t)A.n_recent * D;
-    bf16_step<D>(ksk, krc, vsk, vrc, A.n_sink, n_full, qf, R, key0, A.c);
-  }
-  write_partial<D>(S, R, A, bk, A.nsplit + f);
-}
-
 template <typename OT>
 __device__ __forceinline__ void store1(OT* p, float v);
 template <>
@@ -445,18 +448,20 @@ __global__ void __launch_bounds__(128) decode_merge_kernel(const float* part_o, 
   const int64_t row = blockIdx.x;  // (b*Hkv + kvh) * G + g  ==  b*Hq + h
   const int dd = threadIdx.x;
   const float* ml = part_ml + row * ns1 * 2;
+  // (unrolled, loads unconditional, so that several partials are in flight at
+  // once; an empty partial has m = -inf, l = 0, o = 0 and weight 0)
   float mm = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < ns1; ++s) mm = __builtin_fmaxf(mm, ml[2 * s]);
   float o = 0.0f, l = 0.0f;
-  if (mm > -__builtin_inff())
+  if (mm > -__builtin_inff()) {
+#pragma unroll 8
     for (int s = 0; s < ns1; ++s) {
-      const float m = ml[2 * s];
-      if (m > -__builtin_inff()) {
-        const float w = __builtin_amdgcn_exp2f(m - mm);
-        o += part_o[(row * ns1 + s) * D + dd] * w;
-        l += ml[2 * s + 1] * w;
-      }
+      const float w = __builtin_amdgcn_exp2f(ml[2 * s] - mm);
+      o += part_o[(row * ns1 + s) * D + dd] * w;
+      l += ml[2 * s + 1] * w;
     }
+  }
   store1<OT>(out + row * D + dd, l > 0.0f ? o / l : 0.0f);
   if (lse && dd == 0) lse[row] = l > 0.0f ? (mm + __builtin_log2f(l)) * 0.69314718055994531f : -__builtin_inff();
 }
@@ -474,6 +479,7 @@ hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t st) {
   A.mid_cap = L.mid_cap;
   A.split_len = L.split_len;
   A.nsplit = L.nsplit;
+  A.nfull = L.nfull;
   A.ns1 = L.nsplit + L.nfull;
   A.k_sink = (const uint16_t*)L.k_sink;
   A.v_sink = (const uint16_t*)L.v_sink;
@@ -485,11 +491,7 @@ hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t st) {
   A.part_o = L.part_o;
   A.part_ml = L.part_ml;
   const int ns1 = A.ns1;
-  if (L.nfull > 0)
-    hipLaunchKernelGGL(decode_full_kernel<D>, dim3((unsigned)(L.B * L.Hkv * L.nfull)), dim3(64 * kDecWaves), 0, st, A,
-                       L.nfull);
-  if (L.nsplit > 0)
-    hipLaunchKernelGGL(decode_fp4_kernel<D>, dim3((unsigned)(L.B * L.Hkv * L.nsplit)), dim3(64 * kDecWaves), 0, st, A);
+  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)(L.B * L.Hkv * ns1)), dim3(64 * kDecWaves), 0, st, A);
   const dim3 mg((unsigned)(L.B * L.Hq));
   if (L.out_dtype == 2)
     hipLaunchKernelGGL((decode_merge_kernel<D, float>), mg, dim3(D), 0, st, L.part_o, L.part_ml, ns1, (float*)L.out, L.lse);
