@@ -7,10 +7,13 @@
 //
 // The kernel is VALU-bound with the search on (9 candidates x 16 elements per
 // block), HBM-bound without it.  Layout choices:
-//   block_axis 0 (blocks along the contiguous dimension): two lanes share a
-//     block, 8 elements each, so one 16-byte load per lane covers a bf16 block
-//     half and a wavefront reads 2 KiB of contiguous input; the partial error
-//     sums of the two lanes meet through a DPP quad permute.
+//   block_axis 0 (blocks along the contiguous dimension): one lane per block,
+//     two 16-byte loads for bf16, so a wavefront reads 2 KiB of contiguous
+//     input and writes 512 contiguous code bytes; the default offset range is
+//     fully unrolled and each candidate is a straight run of multiplies,
+//     hardware E2M1 converts (there and back),
+//     fused error terms, squares and the fixed sum tree; the codes of the
+//     chosen scale are formed once at the end.
 //   block_axis 1 (blocks along rows, e.g. V along tokens): one lane per block,
 //     consecutive lanes take consecutive columns, so each of the 16 row loads
 //     of a wavefront is one contiguous 128-byte (bf16) segment.
@@ -22,11 +25,14 @@
 
 namespace fp4dev {
 
-// Reciprocals of every scale byte, correctly rounded binary32, built at
-// compile time (the compiler evaluates 1.0f / s exactly under IEEE rules).
-struct RecipTable {
-  float v[128];
-  constexpr RecipTable() : v() {
+// Scale and reciprocal of every scale byte: {s, fl32(1/s)} with the
+// reciprocal correctly rounded (the compiler evaluates 1.0f / s exactly under
+// IEEE rules at compile time).  Byte 0 maps to {0, 0}: every element then
+// rounds to code 0 and its error is the element itself; byte 0x7F (NaN) is
+// never a candidate.
+struct ScaleTable {
+  float2_t v[128];
+  constexpr ScaleTable() : v() {
     for (int b = 0; b < 128; ++b) {
       float s = 0.0f;
       if (b < 8) s = (float)b / 512.0f;
@@ -36,11 +42,11 @@ struct RecipTable {
         for (int i = 0; i < e; ++i) s *= 2.0f;
         for (int i = 0; i > e; --i) s /= 2.0f;
       }
-      v[b] = (b == 0 || b == 127) ? 0.0f : 1.0f / s;
+      v[b] = (b == 0 || b == 127) ? float2_t{0.0f, 0.0f} : float2_t{s, 1.0f / s};
     }
   }
 };
-__constant__ RecipTable kRecip = RecipTable();
+__constant__ ScaleTable kScaleTab = ScaleTable();
 
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p);
@@ -53,9 +59,9 @@ __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 
 // Load 8 consecutive elements (16-byte aligned for 2-byte types) as binary32.
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&y)[8]);
+__device__ __forceinline__ void load8(const T* p, float* y);
 template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&y)[8]) {
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* y) {
   uint4_t w = *reinterpret_cast<const uint4_t*>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -64,21 +70,22 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&y)[8]
   }
 }
 template <>
-__device__ __forceinline__ void load8<half_t>(const half_t* p, float (&y)[8]) {
+__device__ __forceinline__ void load8<half_t>(const half_t* p, float* y) {
   half8_t w = *reinterpret_cast<const half8_t*>(p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = (float)w[i];
 }
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&y)[8]) {
+__device__ __forceinline__ void load8<float>(const float* p, float* y) {
   float4_t a = *reinterpret_cast<const float4_t*>(p);
   float4_t b = *reinterpret_cast<const float4_t*>(p + 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) { y[i] = a[i]; y[4 + i] = b[i]; }
 }
 
-// Convert 8 non-negative values to 8 E2M1 codes packed in one dword.
-__device__ __forceinline__ uint32_t pack8(const float (&t)[8]) {
+// 8 values -> 8 E2M1 codes in one dword (nearest, ties to the even code,
+// saturating at 6; the magnitude is rounded, the sign follows the value).
+__device__ __forceinline__ uint32_t pack8(const float* t) {
   uint32_t w = 0;
   w = cvt_pk_fp4<0>(w, t[0], t[1]);
   w = cvt_pk_fp4<1>(w, t[2], t[3]);
@@ -88,240 +95,262 @@ __device__ __forceinline__ uint32_t pack8(const float (&t)[8]) {
 }
 
 // E2M1 values of the 8 codes in a dword.
-__device__ __forceinline__ void unpack8(uint32_t w, float (&v)[8]) {
+__device__ __forceinline__ void unpack8(uint32_t w, float* v) {
   float2_t a = cvt_pk_f32_fp4<0>(w), b = cvt_pk_f32_fp4<1>(w);
   float2_t c = cvt_pk_f32_fp4<2>(w), d = cvt_pk_f32_fp4<3>(w);
   v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
   v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
 }
 
-// Sum of 8 squared errors by the fixed pairwise tree (elements 0..7 of a half block).
-__device__ __forceinline__ float tree8(const float (&q)[8]) {
-  float a0 = q[0] + q[1], a1 = q[2] + q[3], a2 = q[4] + q[5], a3 = q[6] + q[7];
-  float b0 = a0 + a1, b1 = a2 + a3;
-  return b0 + b1;
-}
-
-// Squared error of 8 elements |y| for scale byte b (b > 0), and their codes.
-__device__ __forceinline__ float half_block_sse(const float (&ay)[8], uint32_t b, const float* recip,
-                                                uint32_t& codes) {
-  float s = e4m3_to_f32(b);
-  float r = recip[b];
-  float t[8];
+// Squared error of one 16-element block y for the scale {s, r}.  Values
+// keep their sign throughout: y - v*s has the magnitude of |y| - |v|*s (v has
+// the sign of y, or is zero), so the squares are those of the definition.
+// The sum follows the fixed pairwise tree (0+1, 2+3, ..., then pairs of
+// pairs); the product v*s is exact, so fmaf rounds once, like the plain
+// difference.
+__device__ __forceinline__ float block_sse(const float (&y)[16], float2_t sr) {
+  float t[16], v[16], q[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = ay[i] * r;
-  codes = pack8(t);
-  float v[8], q[8];
-  unpack8(codes, v);
+  for (int i = 0; i < 16; ++i) t[i] = y[i] * sr[1];
+  unpack8(pack8(t), v);
+  unpack8(pack8(t + 8), v + 8);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float e = __builtin_fmaf(-v[i], s, ay[i]);  // |y| - v*s: the product is exact, one rounding
+  for (int i = 0; i < 16; ++i) {
+    const float e = __builtin_fmaf(-v[i], sr[0], y[i]);
     q[i] = e * e;
   }
-  return tree8(q);
+  float l1[8], l2[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) l1[k] = q[2 * k] + q[2 * k + 1];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) l2[k] = l1[2 * k] + l1[2 * k + 1];
+  return (l2[0] + l2[1]) + (l2[2] + l2[3]);
 }
 
-__device__ __forceinline__ float half_block_sse_zero(const float (&ay)[8]) {
-  float q[8];
+// Codes of one block for the reciprocal r (two dwords, element 2i in the low nibble).
+__device__ __forceinline__ void block_codes(const float (&y)[16], float r, uint32_t (&c)[2]) {
+  float t[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = ay[i] * ay[i];
-  return tree8(q);
+  for (int i = 0; i < 16; ++i) t[i] = y[i] * r;
+  c[0] = pack8(t);
+  c[1] = pack8(t + 8);
 }
 
-// Sign bits of 8 elements placed at bit 3 of each nibble.
-__device__ __forceinline__ uint32_t sign_nibbles(const float (&y)[8]) {
-  uint32_t m = 0;
+// Sign bits of 16 values at bit 3 of each nibble (two dwords).
+__device__ __forceinline__ void sign_nibbles(const float (&y)[16], uint32_t (&m)[2]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m |= (__float_as_uint(y[i]) >> 31) << (4 * i + 3);
-  return m;
-}
-
-// Choose the scale of one block held as NH halves of 8 elements per lane
-// (NH = 1: the other half is on lane ^ 1; NH = 2: the whole block on this lane).
-// Returns the scale byte, the offset and the packed codes (one dword per half).
-template <int NH>
-__device__ __forceinline__ void choose_block(const float (&y)[NH][8], int search, int fmin, int fmax,
-                                             const float* recip, uint32_t (&codes)[NH],
-                                             uint32_t& scale, int& off) {
-  float ay[NH][8];
-  float a = 0.0f;
-  bool bad = false;
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w = 0;
 #pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ay[h][i] = __builtin_fabsf(y[h][i]);
-      bad |= !__builtin_isfinite(y[h][i]);
-      a = __builtin_fmaxf(a, ay[h][i]);
-    }
-  if (NH == 1) {
-    a = __builtin_fmaxf(a, swap_lane1(a));
-    bad |= swap_lane1_u((uint32_t)bad) != 0u;
+    for (int i = 0; i < 8; ++i) w |= (__float_as_uint(y[8 * h + i]) >> 31) << (4 * i + 3);
+    m[h] = w;
   }
-  uint32_t sgn[NH];
+}
+
+// One candidate of the offset search: a byte outside 0..0x7E is evaluated on
+// byte 0 and can never win.  The comparison runs on the error's bit pattern
+// (non-negative floats order like their bits) against a running best that
+// starts above every float, so the first valid candidate wins even with an
+// infinite error, and later ones only when strictly smaller: ties keep the
+// lowest offset.
+__device__ __forceinline__ void try_offset(const float (&y)[16], int s0, int f, const float2_t* tab,
+                                           uint32_t& best, int& bestf) {
+  const int b = s0 + f;
+  const bool valid = (unsigned)b <= 0x7Eu;
+  const float sse = block_sse(y, tab[valid ? b : 0]);
+  const uint32_t key = valid ? __float_as_uint(sse) : 0xFFFFFFFFu;
+  const bool better = key < best;
+  best = better ? key : best;
+  bestf = better ? f : bestf;
+}
+
+// Quantize one block of 16 scaled values.  Returns the scale byte, the offset
+// and the codes (two dwords, element 2i in the low nibble).  The default
+// search range [-2, 6] is fully unrolled; other ranges loop.
+__device__ __forceinline__ void quantize_block(const float (&y)[16], int search, int fmin, int fmax,
+                                               const float2_t* tab, uint32_t (&codes)[2], uint32_t& scale,
+                                               int& off) {
+  // a = max |y|; a non-finite element makes the maximum of the magnitude bits
+  // reach the exponent-all-ones range
+  uint32_t abits = 0;
 #pragma unroll
-  for (int h = 0; h < NH; ++h) sgn[h] = sign_nibbles(y[h]);
-  if (bad || a == 0.0f) {
-#pragma unroll
-    for (int h = 0; h < NH; ++h) codes[h] = sgn[h];
-    scale = bad ? 0x7Fu : 0u;
+  for (int i = 0; i < 16; ++i) abits = __builtin_elementwise_max(abits, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+  uint32_t sgn[2];
+  sign_nibbles(y, sgn);
+  if (abits >= 0x7F800000u || abits == 0u) {
+    codes[0] = sgn[0];
+    codes[1] = sgn[1];
+    scale = abits ? 0x7Fu : 0u;
     off = 0;
     return;
   }
-  const int s0 = (int)e4m3_of_div6(a);
-  const int lo = search ? fmin : 0, hi = search ? fmax : 0;
-  // Branch-free candidate loop (the bounds are uniform): a byte outside
-  // 0..0x7E is evaluated on a clamped byte and given an infinite error; byte 0
-  // needs no special case because its reciprocal entry is 0, which maps every
-  // element to code 0 and leaves the error |y| itself.
-  float best = 0.0f;
-  bool have = false;  // a valid candidate has been seen (the first one always wins, even at inf)
+  const int s0 = (int)e4m3_of_div6(__uint_as_float(abits));
+  uint32_t best = 0xFFFFFFFFu;
   int bestf = 0;
-  uint32_t bestc[NH];
+  if (search && fmin == -2 && fmax == 6) {
 #pragma unroll
-  for (int h = 0; h < NH; ++h) bestc[h] = 0;
-#pragma unroll 3
-  for (int f = lo; f <= hi; ++f) {
-    const int b = s0 + f;
-    const bool valid = b >= 0 && b <= 0x7E;
-    const uint32_t bc = (uint32_t)(b < 0 ? 0 : (b > 0x7E ? 0x7E : b));
-    float part[NH];
-    uint32_t c[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) part[h] = half_block_sse(ay[h], bc, recip, c[h]);
-    float sse;
-    if (NH == 1) {
-      float other = swap_lane1(part[0]);
-      sse = part[0] + other;  // elements 0..7 tree + elements 8..15 tree (commutative)
-    } else {
-      sse = part[0] + part[NH - 1];
-    }
-    const bool better = valid && (!have || sse < best);
-    have = have || valid;
-    if (better) {
-      best = sse;
-      bestf = f;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) bestc[h] = c[h];
-    }
+    for (int f = -2; f <= 6; ++f) try_offset(y, s0, f, tab, best, bestf);
+  } else if (search) {
+    for (int f = fmin; f <= fmax; ++f) try_offset(y, s0, f, tab, best, bestf);
   }
-#pragma unroll
-  for (int h = 0; h < NH; ++h) codes[h] = bestc[h] | sgn[h];
+  // (without the search the only candidate, s0 itself, is always valid)
   scale = (uint32_t)(s0 + bestf);
   off = bestf;
+  block_codes(y, tab[scale][1], codes);
+  codes[0] |= sgn[0];
+  codes[1] |= sgn[1];
 }
 
 struct QuantArgs {
   const void* x;
   int64_t rows, cols, ld;
-  uint32_t* codes;  // axis 0: as dwords; axis 1: bytes via codes8
-  uint8_t* codes8;
+  uint2_t* codes;   // axis 0: one 8-byte pair of dwords per block
+  uint8_t* codes8;  // axis 1: bytes
   uint8_t* scales;
   int8_t* offsets;
-  float* g;          // per-tensor scale output/input (may be null for mode 0)
+  float* g;                // per-tensor scale output/input (may be null for mode 0)
   const float* amax_part;  // partial maxima (mode 1)
   int n_part;
   int search, fmin, fmax, gmode;
 };
 
-// Per-tensor scale factors from the partial maxima (mode 1) or *g (mode 2).
-// Every thread of the workgroup reads at most a few partials; the maximum is
-// reduced through LDS, then thread 0 forms the correctly rounded factors.
-__device__ __forceinline__ void global_factors(const QuantArgs& A, float* sh, float& ginv) {
-  if (A.gmode == 0) { ginv = 1.0f; return; }
-  float a = 0.0f;
-  if (A.gmode == 1)
-    for (int i = threadIdx.x; i < A.n_part; i += blockDim.x) a = __builtin_fmaxf(a, A.amax_part[i]);
-  sh[threadIdx.x] = a;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) sh[threadIdx.x] = __builtin_fmaxf(sh[threadIdx.x], sh[threadIdx.x + s]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    float gi = 1.0f, g = 1.0f;
-    if (A.gmode == 2) {
-      g = *A.g;
-      gi = div_rn(1.0f, g);
-    } else {
-      a = sh[0];
-      if (a > 0.0f && __builtin_isfinite(a)) {
-        g = div_rn(a, 2688.0f);
-        gi = div_rn(2688.0f, a);
-      } else if (a > 0.0f) {  // infinite amax: g = inf, every finite element scales to 0
-        g = __builtin_inff();
-        gi = 0.0f;
-      }
-      if (blockIdx.x == 0) *A.g = g;
-    }
-    sh[256] = gi;
-  }
-  __syncthreads();
-  ginv = sh[256];
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, k, 64));
+  return v;
 }
 
-// block_axis 0: 2 lanes per 16-element block.
+// Per-tensor encode factor from the partial maxima (mode 1) or *g (mode 2):
+// every thread reads a few partials, waves reduce with cross-lane moves and
+// one LDS exchange joins the waves.  The first workgroup writes g (mode 1).
+__device__ __forceinline__ float global_factor(const QuantArgs& A, float* sh) {
+  if (A.gmode == 0) return 1.0f;
+  if (A.gmode == 2) return div_rn(1.0f, *A.g);
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < A.n_part; i += blockDim.x) a = __builtin_fmaxf(a, A.amax_part[i]);
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = sh[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) a = __builtin_fmaxf(a, sh[w]);
+  float g = 1.0f, gi = 1.0f;
+  if (a > 0.0f && __builtin_isfinite(a)) {
+    g = div_rn(a, 2688.0f);
+    gi = div_rn(2688.0f, a);
+  } else if (a > 0.0f) {  // infinite amax: g = inf, every finite element scales to 0
+    g = __builtin_inff();
+    gi = 0.0f;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *A.g = g;
+  return gi;
+}
+
+// One block of 16 consecutive elements as raw 16-byte words (bf16/fp16: 2,
+// fp32: 4), loaded ahead of its use.
+template <typename T>
+struct RawBlock {
+  static constexpr int N = sizeof(T) * 16 / 16;
+  uint4_t w[N];
+};
+template <typename T>
+__device__ __forceinline__ void load_raw(RawBlock<T>& R, const T* p) {
+#pragma unroll
+  for (int i = 0; i < RawBlock<T>::N; ++i) R.w[i] = reinterpret_cast<const uint4_t*>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void raw_to_f32(const RawBlock<T>& R, float (&y)[16]);
+template <>
+__device__ __forceinline__ void raw_to_f32<uint16_t>(const RawBlock<uint16_t>& R, float (&y)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = R.w[i >> 2][i & 3];
+    y[2 * i] = __uint_as_float(w << 16);
+    y[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void raw_to_f32<half_t>(const RawBlock<half_t>& R, float (&y)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = R.w[i >> 2][i & 3];
+    const half2_t h = __builtin_bit_cast(half2_t, w);
+    y[2 * i] = (float)h[0];
+    y[2 * i + 1] = (float)h[1];
+  }
+}
+template <>
+__device__ __forceinline__ void raw_to_f32<float>(const RawBlock<float>& R, float (&y)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = __uint_as_float(R.w[i >> 2][i & 3]);
+}
+
+// block_axis 0: one lane per 16-element block; a wavefront reads 64
+// consecutive blocks (2 KiB of bf16) and writes their 512 code bytes.  The
+// grid is a few workgroups per CU that stride over the blocks, each lane
+// loading its next block while it searches the current one.
 template <typename T>
 __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
-  __shared__ float recip[128];
-  __shared__ float sh[257];
-  if (threadIdx.x < 128) recip[threadIdx.x] = kRecip.v[threadIdx.x];
-  float ginv;
-  global_factors(A, sh, ginv);
+  __shared__ float2_t tab[128];
+  __shared__ float sh[8];
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const float ginv = global_factor(A, sh);
   __syncthreads();
   const int64_t bpr = A.cols / 16;  // blocks per row
-  const int64_t nhalf = A.rows * bpr * 2;
+  const int64_t nb = A.rows * bpr;
   const T* x = reinterpret_cast<const T*>(A.x);
-  for (int64_t hi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; hi - (threadIdx.x & 1) < nhalf;
-       hi += (int64_t)gridDim.x * blockDim.x) {
-    // both lanes of a pair stay in the loop together (nhalf is even)
-    const int64_t blk = hi >> 1;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  auto src = [&](int64_t blk) {
     const int64_t r = blk / bpr, cb = blk - r * bpr;
-    const int part = (int)(hi & 1);
-    float y[1][8];
-    load8<T>(x + r * A.ld + cb * 16 + part * 8, y[0]);
+    return x + r * A.ld + cb * 16;
+  };
+  int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  RawBlock<T> raw;
+  if (blk < nb) load_raw<T>(raw, src(blk));
+  for (; blk < nb; blk += stride) {
+    float y[16];
+    raw_to_f32<T>(raw, y);
+    if (blk + stride < nb) load_raw<T>(raw, src(blk + stride));
     if (A.gmode != 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[0][i] = y[0][i] * ginv;
+      for (int i = 0; i < 16; ++i) y[i] = y[i] * ginv;
     }
-    uint32_t codes[1], scale;
+    uint32_t codes[2], scale;
     int off;
-    choose_block<1>(y, A.search, A.fmin, A.fmax, recip, codes, scale, off);
-    A.codes[hi] = codes[0];
-    if (part == 0) {
-      A.scales[blk] = (uint8_t)scale;
-      if (A.offsets) A.offsets[blk] = (int8_t)off;
-    }
+    quantize_block(y, A.search, A.fmin, A.fmax, tab, codes, scale, off);
+    A.codes[blk] = uint2_t{codes[0], codes[1]};
+    A.scales[blk] = (uint8_t)scale;
+    if (A.offsets) A.offsets[blk] = (int8_t)off;
   }
 }
 
-// block_axis 1: one lane per block of 16 rows of one column.
+// block_axis 1: one lane per block of 16 rows of one column; consecutive
+// lanes take consecutive columns, so each row load of a wavefront is one
+// contiguous segment.
 template <typename T>
 __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
-  __shared__ float recip[128];
-  __shared__ float sh[257];
-  if (threadIdx.x < 128) recip[threadIdx.x] = kRecip.v[threadIdx.x];
-  float ginv;
-  global_factors(A, sh, ginv);
+  __shared__ float2_t tab[128];
+  __shared__ float sh[8];
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const float ginv = global_factor(A, sh);
   __syncthreads();
   const int64_t nb = (A.rows / 16) * A.cols;
   const T* x = reinterpret_cast<const T*>(A.x);
   for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nb;
        blk += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rb = blk / A.cols, c = blk - rb * A.cols;
-    float y[2][8];
+    float y[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      float v = load_elem<T>(x + (rb * 16 + k) * A.ld + c);
-      y[k >> 3][k & 7] = A.gmode != 0 ? v * ginv : v;
+      const float v = load_elem<T>(x + (rb * 16 + k) * A.ld + c);
+      y[k] = A.gmode != 0 ? v * ginv : v;
     }
     uint32_t codes[2], scale;
     int off;
-    choose_block<2>(y, A.search, A.fmin, A.fmax, recip, codes, scale, off);
+    quantize_block(y, A.search, A.fmin, A.fmax, tab, codes, scale, off);
     // row pair (2i, 2i+1) -> byte i of the block's 8 bytes, at codes8[(rb*8+i)*cols + c]
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t byte = (codes[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const uint32_t byte = (codes[i >> 2] >> (8 * (i & 3))) & 0xFFu;
       A.codes8[(rb * 8 + i) * A.cols + c] = (uint8_t)byte;
     }
     A.scales[blk] = (uint8_t)scale;
@@ -330,16 +359,29 @@ __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
 }
 
 // Partial maxima of |x| (NaN ignored) for the per-tensor scale: one per
-// workgroup, grid-stride over rows with 8-element (16-byte for 2-byte types)
-// loads when rows are dense.
+// workgroup.  Dense rows are read as 16-byte chunks, four per thread in flight.
 template <typename T>
 __global__ void __launch_bounds__(256) amax_kernel(const T* x, int64_t rows, int64_t cols, int64_t ld,
                                                    float* part) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   float m = 0.0f;
   if (cols % 8 == 0 && ld % 8 == 0) {
     const int64_t per_row = cols / 8, n = rows * per_row;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+      float y[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t j = i + u * stride, r = j / per_row, c = (j - r * per_row) * 8;
+        load8<T>(x + r * ld + c, y[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(y[u][k]));
+    }
+    for (; i < n; i += stride) {
       const int64_t r = i / per_row, c = (i - r * per_row) * 8;
       float y[8];
       load8<T>(x + r * ld + c, y);
@@ -353,13 +395,11 @@ __global__ void __launch_bounds__(256) amax_kernel(const T* x, int64_t rows, int
       m = __builtin_fmaxf(m, __builtin_fabsf(load_elem<T>(x + r * ld + c)));
     }
   }
-  red[threadIdx.x] = m;
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] = __builtin_fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+  if (threadIdx.x == 0)
+    part[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
 __global__ void set_one_kernel(float* g) { *g = 1.0f; }
@@ -372,9 +412,9 @@ int fp4i_amax_parts(int64_t rows, int64_t cols) {
   // enough workgroups to stream the tensor at full bandwidth, few enough that
   // every quantize workgroup can re-reduce them cheaply
   int64_t n = rows * cols;
-  int64_t p = (n + 256 * 64 - 1) / (256 * 64);
+  int64_t p = (n + 256 * 32 - 1) / (256 * 32);
   if (p < 1) p = 1;
-  if (p > 512) p = 512;
+  if (p > 1024) p = 1024;
   return (int)p;
 }
 
@@ -384,7 +424,7 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   A.rows = L.rows;
   A.cols = L.cols;
   A.ld = L.ld;
-  A.codes = reinterpret_cast<uint32_t*>(L.codes);
+  A.codes = reinterpret_cast<uint2_t*>(L.codes);
   A.codes8 = L.codes;
   A.scales = L.scales;
   A.offsets = L.offsets;
@@ -413,9 +453,9 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   } else if (L.gmode == 0 && L.g) {
     hipLaunchKernelGGL(set_one_kernel, dim3(1), dim3(1), 0, stream, L.g);
   }
-  int64_t work = L.axis == 0 ? L.rows * (L.cols / 16) * 2 : (L.rows / 16) * L.cols;
+  int64_t work = L.axis == 0 ? L.rows * (L.cols / 16) : (L.rows / 16) * L.cols;
   int64_t grid = (work + 255) / 256;
-  if (grid > 65536) grid = 65536;
+  if (grid > 2048) grid = 2048;  // 8 workgroups per CU, striding over the blocks
   if (grid < 1) grid = 1;
   if (L.axis == 0) {
     if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis0_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
