@@ -28,7 +28,9 @@
 //     layout uses the matching key order, so P needs no shuffle.
 // The FP4 tiles run first, the FP16 tiles after (their fp16 Q fragment is
 // loaded only when a selected pair exists), as the ThriftAttention page does
-// to limit register pressure.
+// to limit register pressure.  A wave raises its issue priority while it runs
+// an MFMA loop, so that on a SIMD shared by two workgroups the MFMA stream
+// of one wave keeps going while the other wave's softmax fills the VALU.
 #include "device_common.h"
 #include "fp4_internal.h"
 
@@ -382,6 +384,9 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
     auto kfrag = [&](int i) { return kbase[32 * (i / NS) * Smem<D, BC>::KS8 + 2 * (i % NS)]; };
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) ring[i] = kfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int g = i / NS, s = i % NS;
@@ -392,6 +397,9 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       __builtin_amdgcn_sched_barrier(0x0407);  // ALU (VALU, SALU, transcendental) may cross
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
   mask_max(NG - 1);
   float smax = bmax[0];
 #pragma unroll
@@ -479,6 +487,9 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       make_half(0, 1, q0, pcur[1]);
     }
     PPrep qn;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int g = i / NPV, k = i % NPV, h2 = k / NT, t = k % NT;
@@ -496,6 +507,9 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
   // FP4: lsum is in units of e (tile-local); FP16: already in units of 2^m
   R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
