@@ -158,6 +158,17 @@ def bench_prefill8k(fp4, synth, torch, n):
                 attn_kernel_frac_fp16_mfma=round(fl / kern / 1e9 / FP16_MFMA_PEAK_TF, 4))
 
 
+# The quantizer's search is bound by plain VALU work: per element and offset
+# candidate one multiply (element times reciprocal scale), one E2M1 convert
+# there and back (a packed pair per instruction: half an instruction each),
+# one fused error term, one square and one tree addition -- 5 lane operations,
+# 45 per element for the 9 offsets.  The ALU peak is one lane operation per
+# lane per clock: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T lane-ops/s
+# (the published 157.3 TFLOP/s fp32 counts an FMA as two).
+QUANT_LANE_OPS_PER_ELEM = 45
+VALU_PEAK_TOPS = 78.6
+
+
 def bench_quantizer(fp4, synth, torch, n):
     rows, cols = 32768, 128
     algo = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4  # bf16 in, codes, scales, g
@@ -193,7 +204,14 @@ def bench_quantizer(fp4, synth, torch, n):
     bo = dict(codes=bc, scales=bs, offsets=None)
     big_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_AMAX, g=g, out=bo), max(3, n // 4))
     big_algo = algo * 64 - 4 * 63
+    alu_tops = rows * 64 * cols * QUANT_LANE_OPS_PER_ELEM / big_ms / 1e9
+    cold_gbps = algo / cold / 1e6
     return dict(workload="bf16 [32768,128], 2% outlier channels x20, ScaleSearch f in [-2,6], per-tensor amax scale",
+                roofline={"bound": "alu", "achieved": round(alu_tops, 2), "peak": VALU_PEAK_TOPS,
+                          "unit": "T lane-ops/s", "frac": round(alu_tops / VALU_PEAK_TOPS, 4),
+                          "note": "64x rows, algorithmic 45 lane-ops per element",
+                          "hbm_frac_cold": round(cold_gbps / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("quantizer_32768x128", "quantize.hip")},
                 algorithmic_bytes=algo,
                 cold_us=round(cold * 1e3, 2), cold_GBps=round(algo / cold / 1e6, 1),
                 cold_frac_hbm=round(algo / cold / 1e6 / HBM_PEAK_GBS, 4),
@@ -232,9 +250,13 @@ def bench_decode(fp4, synth, torch, n):
     kv_bytes = B * Hkv * (M * (d // 2 + d // 16) * 2 + (n_sink + n_recent) * d * 2 * 2)
     qo = B * Hq * d * 2 * 2
     algo = kv_bytes + qo
+    gbps = algo / ms / 1e6
     return dict(workload="decode batch 16, 32 q / 8 kv heads, context 131072, d 128, 128 sink + 256 recent bf16",
-                algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(algo / ms / 1e6, 1),
-                frac_hbm=round(algo / ms / 1e6 / HBM_PEAK_GBS, 4))
+                algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
+                frac_hbm=round(gbps / HBM_PEAK_GBS, 4),
+                roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("decode_b16_ctx131072", "attn_decode.hip")})
 
 
 def cpu_baseline(q, k, v):
@@ -275,6 +297,8 @@ def pmc_mode(mode, fp4, synth, torch):
             fp4.fp4_attention_fwd(q, k, v, causal=True, kv_tile=128, fp16_budget_pct=10, out_dtype=fp4.BF16,
                                   quantized=quant, selection=sel, return_lse=False, out=out)
         torch.cuda.synchronize()
+    elif mode == "decode":
+        bench_decode(fp4, synth, torch, 3)
     elif mode == "quant":
         x = synth.quant_tensor().cuda()
         for _ in range(3):
@@ -290,7 +314,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
-    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy"], default=None)
+    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy", "decode"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
