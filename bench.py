@@ -16,6 +16,7 @@ C oracle timed on a bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -259,6 +260,35 @@ def bench_decode(fp4, synth, torch, n):
                           "traffic": read_traffic("decode_b16_ctx131072", "attn_decode.hip")})
 
 
+def bench_kv_append(fp4, torch, n):
+    """Quantize-on-write of 16 tokens per (batch, kv head) into the decode workload's cache."""
+    B, Hkv, d, n_recent, cap = 16, 8, 128, 256, 130688
+    g = torch.Generator(device="cuda").manual_seed(60)
+    kr = torch.randn(B, Hkv, n_recent, d, generator=g, device="cuda").to(torch.bfloat16)
+    vr = torch.randn(B, Hkv, n_recent, d, generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(B, Hkv, 16, d, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(B, Hkv, 16, d, generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, Hkv, cap, d // 16), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((B, Hkv, cap // 2, d), dtype=torch.uint8, device="cuda")
+    vs = torch.zeros((B, Hkv, cap // 16, d), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros((B, Hkv, 128, d), dtype=torch.bfloat16, device="cuda")
+    calls = n + 4
+    ml = torch.full((B,), cap - 16 * calls, dtype=torch.int32, device="cuda")  # room for every call
+    cache = fp4.KVCache(sink, sink, kc, ks, vc, vs, kr, vr, ml)
+    ws = torch.empty(fp4.load().fp4_kv_cache_append_workspace_size(ctypes.byref(cache.struct())), dtype=torch.uint8,
+                     device="cuda")
+    timer = Timer(torch)
+    ms = timer.run(lambda: fp4.fp4_kv_cache_append(cache, kn, vn, workspace=ws), n, warm=2)
+    # read the window and the new tokens once, write the window and the NVFP4 group once
+    algo = B * Hkv * ((n_recent + 16) * d * 2 * 2 + n_recent * d * 2 * 2 + 16 * (d // 2 + d // 16) * 2)
+    gbps = algo / ms / 1e6
+    return dict(workload="append 16 tokens to batch 16 x 8 kv heads, d 128, 256-token bf16 window, ScaleSearch",
+                algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
+                roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": None})
+
+
 def cpu_baseline(q, k, v):
     """The C oracle on heads 0 and 1 of the step workload: ScaleSearch
     quantization of each head's Q/K/V, block means and top-10% selection, and
@@ -369,6 +399,8 @@ def main():
         line["components"]["quantizer"] = bench_quantizer(fp4, synth, torch, max(8, args.steps))
         log("components: decode")
         line["components"]["decode"] = bench_decode(fp4, synth, torch, max(5, args.steps))
+        log("components: kv append")
+        line["components"]["kv_append"] = bench_kv_append(fp4, torch, max(10, args.steps))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(res["q"], res["k"], res["v"])

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "load", "build", "fp4_version", "fp4_last_error", "fp4_quantize", "fp4_block_topk",
-    "fp4_attention_fwd", "fp4_attention_decode", "FP4Error", "BF16", "FP16", "FP32",
+    "fp4_attention_fwd", "fp4_attention_decode", "fp4_kv_cache_append", "FP4Error", "BF16", "FP16", "FP32",
     "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
 ]
 
@@ -102,6 +102,10 @@ def load():
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
+    L.fp4_kv_cache_append.argtypes = [C.POINTER(KVCacheStruct), vp, vp, i32, vp, vp, sz, vp]
+    L.fp4_kv_cache_append.restype = C.c_int
+    L.fp4_kv_cache_append_workspace_size.argtypes = [C.POINTER(KVCacheStruct)]
+    L.fp4_kv_cache_append_workspace_size.restype = sz
     _lib = L
     return L
 
@@ -298,3 +302,20 @@ def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, r
     _check(L.fp4_attention_decode(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out), _ptr(lse),
                                   _ptr(ws), nws, _stream(q.device)))
     return out, lse
+
+
+def fp4_kv_cache_append(cache: KVCache, k_new, v_new, workspace=None):
+    """Quantize-on-write: append k_new, v_new (bf16 [B,Hkv,n_new,d], n_new a
+    multiple of 16) to the cache in place.  Returns overflow [B] int32 (1 where
+    the NVFP4 region had no room and the batch was left unchanged)."""
+    L = load()
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    n_new = int(k_new.shape[2])
+    cs = cache.struct()
+    overflow = torch.empty((cache.B,), dtype=torch.int32, device=k_new.device)
+    nws = L.fp4_kv_cache_append_workspace_size(C.byref(cs))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, k_new.device)
+    _check(L.fp4_kv_cache_append(C.byref(cs), _ptr(k_new), _ptr(v_new), n_new, _ptr(overflow), _ptr(ws), nws,
+                                 _stream(k_new.device)))
+    return overflow

@@ -365,4 +365,43 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float
   return hip_status(fp4i_launch_decode(L, (hipStream_t)stream), "fp4_attention_decode launch");
 }
 
+size_t fp4_kv_cache_append_workspace_size(const fp4_kv_cache* c) {
+  if (!c || c->struct_size < sizeof(fp4_kv_cache) || c->B <= 0 || c->Hkv <= 0 || c->d <= 0 || c->n_recent < 0)
+    return 0;
+  return fp4i_kv_append_workspace(c->B, c->Hkv, c->n_recent, c->d);
+}
+
+int fp4_kv_cache_append(const fp4_kv_cache* c, const void* k_new, const void* v_new, int32_t n_new,
+                        int32_t* overflow, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "fp4_kv_cache_append";
+  if (!c || c->struct_size < sizeof(fp4_kv_cache)) return fail(FP4_ERR_INVALID_ARG, "%s: cache is NULL or struct_size too small", fn);
+  if (c->B < 1 || c->Hkv < 1) return fail(FP4_ERR_INVALID_ARG, "%s: bad B/Hkv", fn);
+  if (c->d != 64 && c->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim %lld not in {64,128}", fn, (long long)c->d);
+  if (n_new <= 0 || n_new % 16) return fail(FP4_ERR_INVALID_ARG, "%s: n_new must be a positive multiple of 16", fn);
+  if (c->n_recent < 0 || c->mid_cap < 16 || c->mid_cap % 16)
+    return fail(FP4_ERR_INVALID_ARG, "%s: need n_recent >= 0 and a NVFP4 capacity that is a positive multiple of 16", fn);
+  if (c->mid_cap * c->d / 2 >= ((int64_t)1 << 31)) return fail(FP4_ERR_UNSUPPORTED, "%s: mid_cap * d too large", fn);
+  if (!k_new || !v_new) return fail(FP4_ERR_INVALID_ARG, "%s: k_new and v_new are required", fn);
+  if (c->n_recent && (!c->k_recent || !c->v_recent)) return fail(FP4_ERR_INVALID_ARG, "%s: recent buffers missing", fn);
+  if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->mid_len)
+    return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 region buffers or mid_len missing", fn);
+  const void* ptrs[] = {k_new, v_new, c->k_recent, c->v_recent, c->k_codes, c->k_scales, c->v_codes, c->v_scales};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  const size_t need = fp4_kv_cache_append_workspace_size(c);
+  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  KvAppendLaunch L;
+  L.B = c->B; L.Hkv = c->Hkv; L.d = c->d; L.mid_cap = c->mid_cap;
+  L.n_recent = c->n_recent; L.n_new = n_new;
+  L.k_new = k_new; L.v_new = v_new;
+  L.k_recent = const_cast<void*>(c->k_recent);
+  L.v_recent = const_cast<void*>(c->v_recent);
+  L.kc = const_cast<uint8_t*>(c->k_codes); L.ks = const_cast<uint8_t*>(c->k_scales);
+  L.vc = const_cast<uint8_t*>(c->v_codes); L.vs = const_cast<uint8_t*>(c->v_scales);
+  L.mid_len = const_cast<int32_t*>(c->mid_len);
+  L.overflow = overflow;
+  L.ws = workspace;
+  return hip_status(fp4i_launch_kv_append(L, (hipStream_t)stream), "fp4_kv_cache_append launch");
+}
+
 }  // extern "C"

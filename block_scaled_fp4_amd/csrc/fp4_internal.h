@@ -85,5 +85,21 @@ struct DecodeLaunch {
 };
 
 int fp4i_decode_splits(int64_t B, int64_t Hkv, int64_t mid_cap, int64_t* split_len);
+
+struct KvAppendLaunch {
+  int64_t B, Hkv, d, mid_cap;
+  int n_recent, n_new;
+  const void* k_new;  // bf16 [B,Hkv,n_new,d]
+  const void* v_new;
+  void* k_recent;     // bf16 [B,Hkv,n_recent,d]
+  void* v_recent;
+  uint8_t *kc, *ks, *vc, *vs;
+  int32_t* mid_len;
+  int32_t* overflow;  // nullable
+  void* ws;
+};
+
+size_t fp4i_kv_append_workspace(int64_t B, int64_t Hkv, int64_t n_recent, int64_t d);
+hipError_t fp4i_launch_kv_append(const KvAppendLaunch& L, hipStream_t stream);
 int fp4i_decode_full_splits(int64_t n_full);
 hipError_t fp4i_launch_decode(const DecodeLaunch& L, hipStream_t stream);

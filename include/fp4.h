@@ -222,6 +222,36 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* cache, f
 
 size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* cache);
 
+/* ------------------------------------------------------------------------ */
+/* Cache append -- ScaleSearch page, Metodologia / ScaleSearchAttention      */
+/* (the middle of the cache is NVFP4 with ScaleSearch, its first and last   */
+/* blocks full precision)                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Quantize-on-write: appends n_new tokens (a multiple of 16) per (batch, kv
+ * head).  For every batch b the recent window followed by the new tokens is a
+ * sequence T of n_recent + n_new tokens; its first n_new tokens move into the
+ * NVFP4 region at token mid_len[b] (K quantized per token in blocks of 16
+ * channels, V in blocks of 16 tokens per channel, both with ScaleSearch over
+ * offsets [-2, 6] and no per-tensor scale, exactly as fp4_quantize), the
+ * recent window becomes the last n_recent tokens of T (oldest first), and
+ * mid_len[b] becomes mid_len[b] + n_new (mid_len is first clamped to
+ * [0, mid_cap] and rounded down to a multiple of 16, as the decode reads it).
+ * A batch whose NVFP4 region has no room for n_new more tokens is left
+ * unchanged; overflow [B] (device, nullable) receives 1 for such a batch, 0
+ * otherwise.  The sink is never touched.
+ * k_new, v_new: bf16 [B,Hkv,n_new,d], dense, 16-byte aligned.  The cache's
+ * recent buffers, NVFP4 arrays and mid_len are written in place (the const
+ * qualifiers of fp4_kv_cache do not apply to this call).  Calls on one cache
+ * must be ordered on one stream.  Workspace: see the query (a copy of the
+ * windows and one int per batch).
+ */
+int fp4_kv_cache_append(const fp4_kv_cache* cache, const void* k_new, const void* v_new, int32_t n_new,
+                        int32_t* overflow, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fp4_kv_cache_append_workspace_size(const fp4_kv_cache* cache);
+
 #ifdef __cplusplus
 }
 #endif

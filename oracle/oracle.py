@@ -21,7 +21,7 @@ __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
-    "score_factor",
+    "score_factor", "kv_append",
 ]
 
 
@@ -295,3 +295,48 @@ def attention_decode(q, k, v, ctx_len, n_sink, n_recent, softmax_scale=0.0, scal
     if rc != 0:
         raise ValueError("bad decode arguments")
     return out.reshape(npairs, G, d), lse.reshape(npairs, G)
+
+
+def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, k_new, v_new):
+    """Quantize-on-write append (the cache's middle is NVFP4 with ScaleSearch,
+    its first and last blocks full precision: ScaleSearch page, Metodologia /
+    ScaleSearchAttention).  Steps, per batch b:
+      1. T = recent window followed by the new tokens (oldest first);
+      2. m = mid_len[b] clamped to [0, mid_cap] and rounded down to a multiple
+         of 16; if m + n_new > mid_cap the batch is left unchanged (flag 1);
+      3. the first n_new tokens of T are quantized exactly as quantize() does
+         for a cache middle region -- K row by row in blocks of 16 channels,
+         V in blocks of 16 tokens per channel, ScaleSearch [-2, 6], g = 1 --
+         and written at tokens m .. m + n_new;
+      4. the window becomes the last n_recent tokens of T; mid_len[b] = m + n_new.
+    Arrays are numpy (k/v bf16 values as float32, codes/scales uint8, mid_len
+    int32) with the layouts of fp4.h; copies are returned:
+    (k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, overflow)."""
+    kr, vr = _f32(k_recent).copy(), _f32(v_recent).copy()
+    kn, vn = _f32(k_new), _f32(v_new)
+    kc, ks = np.array(k_codes, np.uint8), np.array(k_scales, np.uint8)
+    vc, vs = np.array(v_codes, np.uint8), np.array(v_scales, np.uint8)
+    ml = np.array(mid_len, np.int32).reshape(-1).copy()
+    B, Hkv, n_new, d = kn.shape
+    n_recent = kr.shape[2]
+    mid_cap = kc.shape[2]
+    assert n_new % 16 == 0 and n_new > 0
+    over = np.zeros(B, np.int32)
+    for b in range(B):
+        m = int(min(max(int(ml[b]), 0), mid_cap)) // 16 * 16
+        if m + n_new > mid_cap:
+            over[b] = 1
+            continue
+        for h in range(Hkv):
+            tk = np.concatenate([kr[b, h], kn[b, h]], axis=0)
+            tv = np.concatenate([vr[b, h], vn[b, h]], axis=0)
+            rk = quantize(tk[:n_new], 0, True, -2, 6)
+            rv = quantize(tv[:n_new], 1, True, -2, 6)
+            kc[b, h, m:m + n_new] = rk["codes"]
+            ks[b, h, m:m + n_new] = rk["scales"]
+            vc[b, h, m // 2:(m + n_new) // 2] = rv["codes"]
+            vs[b, h, m // 16:(m + n_new) // 16] = rv["scales"]
+            kr[b, h] = tk[n_new:]
+            vr[b, h] = tv[n_new:]
+        ml[b] = m + n_new
+    return kr, vr, kc, ks, vc, vs, ml, over

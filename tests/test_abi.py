@@ -108,3 +108,23 @@ def test_decode_rejects_bad_arguments(L):
     need = L.fp4_attention_decode_workspace_size(8, C.byref(cs))
     assert need > 0
     assert L.fp4_attention_decode(f, 8, C.byref(cs), 0.0, 2, f, None, f, need - 1, None) == -3
+
+
+def test_kv_append_rejects_bad_arguments(L):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+    cs = fp4.KVCacheStruct(C.sizeof(fp4.KVCacheStruct), 2, 2, 128, 16, 32, 96, f, f, f, f, f, f, f, f, f)
+    need = L.fp4_kv_cache_append_workspace_size(C.byref(cs))
+    assert need >= 2 * 2 * 2 * 32 * 128 * 2  # two window copies (K, V) in bf16
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 24, None, f, need, None) == -1   # not a multiple of 16
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 0, None, f, need, None) == -1
+    assert L.fp4_kv_cache_append(C.byref(cs), None, f, 16, None, f, need, None) == -1
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, need - 1, None) == -3
+    cs.mid_cap = 100
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, need, None) == -1  # capacity % 16
+    cs.mid_cap = 96
+    cs.d = 96
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, need, None) == -2
+    cs.d = 128
+    cs.mid_len = None
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, need, None) == -1
