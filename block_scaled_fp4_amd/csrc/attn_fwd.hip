@@ -83,7 +83,14 @@ __constant__ PScaleTable kPScale = PScaleTable();
 constexpr int kWaves = 4;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Value of lane ^ 32, with v_permlane32_swap (a VALU op: no LDS round trip).
+// Called with the same register as both operands, the swap returns the
+// lower half's values in the upper lanes of the first result and the upper
+// half's values in the lower lanes of the second.
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // Position of key k (within a 32-key group) in the V^T LDS row: the 8-key
 // groups 1 and 2 trade places, matching the keys each lane holds in S^T.
