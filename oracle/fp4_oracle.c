@@ -311,6 +311,21 @@ void orc_block_means(const float* x, int64_t S, int d, int blk, double* means) {
   }
 }
 
+/* Sum of each block of `blk` consecutive tokens of x [S][d] (the last block
+   may be short), in binary64 over ascending tokens: the numerators of
+   orc_block_means, kept by a cache so that appends can extend them. */
+void orc_block_sums(const float* x, int64_t S, int d, int blk, double* sums) {
+  int64_t nb = (S + blk - 1) / blk;
+  for (int64_t ib = 0; ib < nb; ++ib) {
+    int64_t t0 = ib * blk, t1 = t0 + blk < S ? t0 + blk : S;
+    for (int c = 0; c < d; ++c) {
+      double s = 0.0;
+      for (int64_t t = t0; t < t1; ++t) s += (double)x[t * d + c];
+      sums[ib * d + c] = s;
+    }
+  }
+}
+
 /* Number of selected key blocks for a query block that sees n key blocks:
    ceil(pct * n / 100) in integers. */
 int orc_topk_count(int pct, int n) { return (pct * n + 99) / 100; }
@@ -630,13 +645,24 @@ int orc_attention_exact(const float* q, const float* k, const float* v, int B, i
    softmax attention over that dequantized cache.
    q [B][Hq][d]; k, v [B][Hkv][Lcap][d] hold the original context.
    pairs (n_pairs of them, NULL = all) picks flattened b*Hkv+kvh pairs; out is
-   [n_pairs][Hq/Hkv][d], lse [n_pairs][Hq/Hkv] (natural log).  Returns 0, or -1
-   on bad arguments. */
+   [n_pairs][Hq/Hkv][d], lse [n_pairs][Hq/Hkv] (natural log).
+   With pct > 0 (ThriftAttention page, Metodologia / 1 and / 2, applied to
+   decode; reading: the query block of a kv head is its G query tokens, and the
+   cache keeps a full-precision copy of the middle beside the NVFP4 one), the
+   middle is cut into blocks of sel_blk tokens from its first token (the last
+   one may be short), each block j is scored by mean(q over the G heads) .
+   mean(K block j) in binary64 (orc_block_means / orc_block_topk order), and
+   the ceil(pct * n / 100) best blocks take their original K and V instead of
+   the dequantized ones.  sel_idx [n_pairs][kmax] (ascending, -1 padded) and
+   sel_cnt [n_pairs] (nullable) receive the choice.  Returns 0, or -1 on bad
+   arguments. */
 int orc_attention_decode(const float* q, const float* k, const float* v, const int32_t* ctx_len,
                          int B, int Hq, int Hkv, int d, int64_t Lcap, int n_sink, int n_recent,
                          double softmax_scale, int scale_search, int fmin, int fmax,
-                         const int* pairs, int n_pairs, float* out, float* lse) {
+                         const int* pairs, int n_pairs, float* out, float* lse,
+                         int pct, int sel_blk, int kmax, int32_t* sel_idx, int32_t* sel_cnt) {
   if (Hq % Hkv || d % 16) return -1;
+  if (pct < 0 || pct > 100 || (pct > 0 && sel_blk < 1)) return -1;
   int G = Hq / Hkv;
   double sc = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)d);
   int np = pairs ? n_pairs : B * Hkv;
@@ -657,6 +683,37 @@ int orc_attention_decode(const float* q, const float* k, const float* v, const i
       memcpy(Kt + (int64_t)n_sink * d, Kq, sizeof(double) * (size_t)(M * d));
       memcpy(Vt + (int64_t)n_sink * d, Vq, sizeof(double) * (size_t)(M * d));
       free(Kq); free(Vq);
+    }
+    /* Selective promotion: the middle's key blocks of sel_blk tokens are
+       scored against the mean of the group's G query vectors and the best
+       ceil(pct * n / 100) are read from the full-precision copy. */
+    if (pct > 0) {
+      int nb = (int)((M + sel_blk - 1) / sel_blk);
+      int k_b = orc_topk_count(pct, nb);
+      if (k_b > kmax) { free(Kt); free(Vt); return -1; }
+      int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(kmax > 0 ? kmax : 1));
+      int32_t cnt = 0;
+      for (int w = 0; w < kmax; ++w) idx[w] = -1;
+      if (nb > 0) {
+        double* km = (double*)malloc(sizeof(double) * (size_t)nb * d);
+        double* qm = (double*)malloc(sizeof(double) * (size_t)d);
+        orc_block_means(kb + (int64_t)n_sink * d, M, d, sel_blk, km);
+        for (int dd = 0; dd < d; ++dd) {
+          double s = 0.0;
+          for (int g = 0; g < G; ++g) s += (double)q[((int64_t)b * Hq + hk * G + g) * d + dd];
+          qm[dd] = s / (double)G;
+        }
+        orc_block_topk(qm, km, 1, nb, d, 0, pct, kmax > 0 ? kmax : 1, idx, &cnt);
+        for (int w = 0; w < cnt; ++w) {
+          int64_t t0 = n_sink + (int64_t)idx[w] * sel_blk;
+          int64_t t1 = t0 + sel_blk < n_sink + M ? t0 + sel_blk : n_sink + M;
+          for (int64_t t = t0 * d; t < t1 * d; ++t) { Kt[t] = kb[t]; Vt[t] = vb[t]; }
+        }
+        free(km); free(qm);
+      }
+      if (sel_idx) memcpy(sel_idx + (int64_t)pi * kmax, idx, sizeof(int32_t) * (size_t)kmax);
+      if (sel_cnt) sel_cnt[pi] = cnt;
+      free(idx);
     }
 #pragma omp parallel for schedule(static)
     for (int g = 0; g < G; ++g) {

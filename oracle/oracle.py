@@ -21,7 +21,7 @@ __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
-    "score_factor", "kv_append",
+    "score_factor", "kv_append", "block_sums",
 ]
 
 
@@ -87,8 +87,11 @@ def lib():
     L.orc_attention_exact.restype = C.c_int
     L.orc_attention_decode.argtypes = [_f32p, _f32p, _f32p, _i32p, C.c_int, C.c_int, C.c_int,
                                        C.c_int, C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int,
-                                       C.c_int, C.c_int, _vp, C.c_int, _f32p, _vp]
+                                       C.c_int, C.c_int, _vp, C.c_int, _f32p, _vp, C.c_int,
+                                       C.c_int, C.c_int, _vp, _vp]
     L.orc_attention_decode.restype = C.c_int
+    L.orc_block_sums.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, _f64p]
+    L.orc_block_sums.restype = None
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
     _lib = L
     return L
@@ -274,11 +277,28 @@ def attention_exact(q, k, v, causal=False, softmax_scale=0.0, rows=None, heads=N
     return out.reshape(nh, nr, d), lse.reshape(nh, nr)
 
 
+def block_sums(x, blk=128):
+    """Binary64 sums over blocks of blk tokens of x [S, d] (ascending tokens)."""
+    x = _f32(x)
+    S, d = x.shape
+    nb = (S + blk - 1) // blk
+    out = np.zeros(max(nb * d, 1), np.float64)
+    lib().orc_block_sums(x, S, d, blk, out)
+    return out[: nb * d].reshape(nb, d)
+
+
 def attention_decode(q, k, v, ctx_len, n_sink, n_recent, softmax_scale=0.0, scale_search=True,
-                     fmin=-2, fmax=6, pairs=None):
+                     fmin=-2, fmax=6, pairs=None, pct=0, sel_block=128, kmax=None,
+                     with_selection=False):
     """Decode oracle. q [B,Hq,d]; k/v [B,Hkv,Lcap,d] original context; ctx_len [B].
 
-    Returns (out [np, G, d], lse [np, G]) for the selected (b*Hkv+kvh) pairs."""
+    pct > 0 promotes the best ceil(pct * n / 100) middle blocks of sel_block
+    tokens per (batch, kv head) to full precision (scored by the mean of the
+    group's queries against the block's mean key).  kmax (default: from the
+    longest middle) is the row length of the selection output.
+
+    Returns (out [np, G, d], lse [np, G]) for the selected (b*Hkv+kvh) pairs,
+    and with with_selection also (sel_idx [np, kmax], sel_cnt [np])."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, Hq, d = q.shape
     Hkv, Lcap = k.shape[1], k.shape[2]
@@ -288,16 +308,26 @@ def attention_decode(q, k, v, ctx_len, n_sink, n_recent, softmax_scale=0.0, scal
     npairs = npairs if pa is not None else B * Hkv
     out = np.zeros(npairs * G * d, np.float32)
     lse = np.zeros(npairs * G, np.float32)
+    if kmax is None:
+        mmax = max(int(cl.max()) - n_sink - n_recent, 0)
+        kmax = topk_count(pct, (mmax + sel_block - 1) // sel_block) if pct > 0 else 0
+    sidx = np.zeros(max(npairs * kmax, 1), np.int32)
+    scnt = np.zeros(max(npairs, 1), np.int32)
     rc = lib().orc_attention_decode(q.reshape(-1), k.reshape(-1), v.reshape(-1), cl, B, Hq, Hkv, d,
                                     Lcap, n_sink, n_recent, float(softmax_scale), int(scale_search),
                                     fmin, fmax, _ptr(pa), npairs if pa is not None else 0, out,
-                                    _ptr(lse))
+                                    _ptr(lse), int(pct), int(sel_block), int(kmax), _ptr(sidx),
+                                    _ptr(scnt))
     if rc != 0:
         raise ValueError("bad decode arguments")
-    return out.reshape(npairs, G, d), lse.reshape(npairs, G)
+    res = (out.reshape(npairs, G, d), lse.reshape(npairs, G))
+    if with_selection:
+        res += (sidx[: npairs * kmax].reshape(npairs, kmax), scnt[:npairs])
+    return res
 
 
-def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, k_new, v_new):
+def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, k_new, v_new,
+              k_mid=None, v_mid=None, k_sum=None, sel_block=128):
     """Quantize-on-write append (the cache's middle is NVFP4 with ScaleSearch,
     its first and last blocks full precision: ScaleSearch page, Metodologia /
     ScaleSearchAttention).  Steps, per batch b:
@@ -311,7 +341,13 @@ def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len,
       4. the window becomes the last n_recent tokens of T; mid_len[b] = m + n_new.
     Arrays are numpy (k/v bf16 values as float32, codes/scales uint8, mid_len
     int32) with the layouts of fp4.h; copies are returned:
-    (k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, overflow)."""
+    (k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len, overflow).
+    With the full-precision copy of the middle (k_mid, v_mid [B,Hkv,mid_cap,d]
+    and the binary64 key-block sums k_sum [B,Hkv,ceil(mid_cap/sel_block),d];
+    ThriftAttention page, Significado: both copies kept), step 3 also writes
+    the tokens unquantized at m .. m + n_new and adds each one, in order, to
+    the sum of its block (a block's sum starts from zero at its first token);
+    the three updated copies follow the tuple above."""
     kr, vr = _f32(k_recent).copy(), _f32(v_recent).copy()
     kn, vn = _f32(k_new), _f32(v_new)
     kc, ks = np.array(k_codes, np.uint8), np.array(k_scales, np.uint8)
@@ -321,6 +357,10 @@ def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len,
     n_recent = kr.shape[2]
     mid_cap = kc.shape[2]
     assert n_new % 16 == 0 and n_new > 0
+    dual = k_mid is not None
+    if dual:
+        km, vm = _f32(k_mid).copy(), _f32(v_mid).copy()
+        ksum = np.array(k_sum, np.float64)
     over = np.zeros(B, np.int32)
     for b in range(B):
         m = int(min(max(int(ml[b]), 0), mid_cap)) // 16 * 16
@@ -330,6 +370,14 @@ def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len,
         for h in range(Hkv):
             tk = np.concatenate([kr[b, h], kn[b, h]], axis=0)
             tv = np.concatenate([vr[b, h], vn[b, h]], axis=0)
+            if dual:
+                km[b, h, m:m + n_new] = tk[:n_new]
+                vm[b, h, m:m + n_new] = tv[:n_new]
+                for t in range(n_new):
+                    j = (m + t) // sel_block
+                    if (m + t) % sel_block == 0:
+                        ksum[b, h, j] = 0.0
+                    ksum[b, h, j] = ksum[b, h, j] + tk[t].astype(np.float64)
             rk = quantize(tk[:n_new], 0, True, -2, 6)
             rv = quantize(tv[:n_new], 1, True, -2, 6)
             kc[b, h, m:m + n_new] = rk["codes"]
@@ -339,4 +387,6 @@ def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len,
             kr[b, h] = tk[n_new:]
             vr[b, h] = tv[n_new:]
         ml[b] = m + n_new
+    if dual:
+        return kr, vr, kc, ks, vc, vs, ml, over, km, vm, ksum
     return kr, vr, kc, ks, vc, vs, ml, over

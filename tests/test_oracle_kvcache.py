@@ -128,3 +128,44 @@ def test_appended_values_dequantize_close_to_the_tokens():
     ek = np.sqrt(((kh - k[0, 0]) ** 2).sum()) / np.sqrt((k[0, 0] ** 2).sum())
     ev = np.sqrt(((vh - v[0, 0]) ** 2).sum()) / np.sqrt((v[0, 0] ** 2).sum())
     assert ek < 0.15 and ev < 0.15
+
+
+def test_append_keeps_the_full_precision_copy_and_block_sums():
+    """With the dual cache (ThriftAttention page, Significado), appends write
+    the tokens unquantized beside the NVFP4 copy and extend the key-block sums;
+    after any sequence of appends the sums equal the block sums of the copy
+    computed in one go (orc_block_sums), block boundaries every 128 tokens from
+    the first middle token."""
+    B, H, d, n_sink, n_recent, cap = 2, 2, 64, 16, 32, 320
+    M0, M1 = 112, 304  # start mid-block, end in a short last block
+    L = n_sink + M1 + n_recent
+    k, v = _context(B, H, L, d, seed=5)
+    kr, vr, kc, ks, vc, vs, ml = _direct_cache(k, v, n_sink, M0, n_recent, cap)
+    nbc = (cap + 127) // 128
+    km = np.zeros((B, H, cap, d), np.float32)
+    vm = np.zeros((B, H, cap, d), np.float32)
+    ksum = np.full((B, H, nbc, d), np.nan)  # blocks never written must not be read
+    km[:, :, :M0] = k[:, :, n_sink:n_sink + M0]
+    vm[:, :, :M0] = v[:, :, n_sink:n_sink + M0]
+    for b in range(B):
+        for h in range(H):
+            ksum[b, h, :1] = oracle.block_sums(km[b, h, :M0])[:1]  # block 0 holds 112 tokens
+    state = (kr, vr, kc, ks, vc, vs, ml)
+    dual = (km, vm, ksum)
+    pos, step = n_sink + M0 + n_recent, 16
+    while pos < L:
+        kn, vn = k[:, :, pos:pos + step], v[:, :, pos:pos + step]
+        out = oracle.kv_append(*state, kn, vn, *dual)
+        assert not out[7].any()
+        state, dual = out[:7], out[8:]
+        pos += step
+        step = 48 if step == 16 else 16
+    km, vm, ksum = dual
+    np.testing.assert_array_equal(km[:, :, :M1], k[:, :, n_sink:n_sink + M1])
+    np.testing.assert_array_equal(vm[:, :, :M1], v[:, :, n_sink:n_sink + M1])
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(ksum[b, h, :3], oracle.block_sums(k[b, h, n_sink:n_sink + M1]))
+    want = _direct_cache(k, v, n_sink, M1, n_recent, cap)
+    for got, ref in zip(state, want):
+        np.testing.assert_array_equal(got, ref)
