@@ -15,8 +15,8 @@ import torch
 
 __all__ = [
     "load", "build", "fp4_version", "fp4_last_error", "fp4_quantize", "fp4_block_topk",
-    "fp4_attention_fwd", "fp4_attention_decode", "fp4_kv_cache_append", "FP4Error", "BF16", "FP16", "FP32",
-    "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
+    "fp4_attention_fwd", "fp4_attention_decode", "fp4_kv_cache_append", "fp4_kv_block_sums", "decode_sel_kmax",
+    "FP4Error", "BF16", "FP16", "FP32", "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,7 +59,8 @@ class KVCacheStruct(C.Structure):
                 ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("mid_cap", C.c_int64),
                 ("k_sink", C.c_void_p), ("v_sink", C.c_void_p), ("k_codes", C.c_void_p),
                 ("k_scales", C.c_void_p), ("v_codes", C.c_void_p), ("v_scales", C.c_void_p),
-                ("k_recent", C.c_void_p), ("v_recent", C.c_void_p), ("mid_len", C.c_void_p)]
+                ("k_recent", C.c_void_p), ("v_recent", C.c_void_p), ("mid_len", C.c_void_p),
+                ("k_mid", C.c_void_p), ("v_mid", C.c_void_p), ("k_sum", C.c_void_p)]
 
 
 _lib = None
@@ -102,6 +103,13 @@ def load():
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
+    L.fp4_attention_decode_selective.argtypes = [vp, i64, C.POINTER(KVCacheStruct), i32, C.c_float, i32, vp, vp,
+                                                 vp, vp, vp, sz, vp]
+    L.fp4_attention_decode_selective.restype = C.c_int
+    L.fp4_attention_decode_selective_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct), i32]
+    L.fp4_attention_decode_selective_workspace_size.restype = sz
+    L.fp4_kv_block_sums.argtypes = [C.POINTER(KVCacheStruct), vp]
+    L.fp4_kv_block_sums.restype = C.c_int
     L.fp4_kv_cache_append.argtypes = [C.POINTER(KVCacheStruct), vp, vp, i32, vp, vp, sz, vp]
     L.fp4_kv_cache_append.restype = C.c_int
     L.fp4_kv_cache_append_workspace_size.argtypes = [C.POINTER(KVCacheStruct)]
@@ -267,9 +275,15 @@ def attention_fwd_workspace_bytes(q_shape, kv_shape, causal=False, kv_tile=128, 
 
 
 class KVCache:
-    """Device buffers of a sink-aware mixed-precision KV cache (layouts in fp4.h)."""
+    """Device buffers of a sink-aware mixed-precision KV cache (layouts in fp4.h).
 
-    def __init__(self, k_sink, v_sink, k_codes, k_scales, v_codes, v_scales, k_recent, v_recent, mid_len):
+    k_mid, v_mid (bf16 [B,Hkv,mid_cap,d]) and k_sum (float64
+    [B,Hkv,ceil(mid_cap/128),d]) are the optional full-precision copy of the
+    middle that selective decode reads."""
+
+    def __init__(self, k_sink, v_sink, k_codes, k_scales, v_codes, v_scales, k_recent, v_recent, mid_len,
+                 k_mid=None, v_mid=None, k_sum=None):
+        self.k_mid, self.v_mid, self.k_sum = k_mid, v_mid, k_sum
         self.k_sink, self.v_sink = k_sink, v_sink
         self.k_codes, self.k_scales, self.v_codes, self.v_scales = k_codes, k_scales, v_codes, v_scales
         self.k_recent, self.v_recent = k_recent, v_recent
@@ -284,12 +298,22 @@ class KVCache:
         return KVCacheStruct(C.sizeof(KVCacheStruct), self.B, self.Hkv, self.d, self.n_sink, self.n_recent,
                              self.mid_cap, _ptr(self.k_sink), _ptr(self.v_sink), _ptr(self.k_codes),
                              _ptr(self.k_scales), _ptr(self.v_codes), _ptr(self.v_scales), _ptr(self.k_recent),
-                             _ptr(self.v_recent), _ptr(self.mid_len))
+                             _ptr(self.v_recent), _ptr(self.mid_len), _ptr(self.k_mid), _ptr(self.v_mid),
+                             _ptr(self.k_sum))
+
+
+def decode_sel_kmax(mid_cap, fp16_budget_pct):
+    """Row length of the selective decode's selection output."""
+    nbc = (mid_cap + 127) // 128
+    return (fp16_budget_pct * nbc + 99) // 100
 
 
 def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, return_lse=True, workspace=None,
-                         out=None):
-    """One-token decode.  q [B,Hq,d] bf16.  Returns (out [B,Hq,d], lse [B,Hq])."""
+                         out=None, fp16_budget_pct=0, return_selection=False):
+    """One-token decode.  q [B,Hq,d] bf16.  Returns (out [B,Hq,d], lse [B,Hq]),
+    and with return_selection also (sel_idx [B,Hkv,kmax], sel_cnt [B,Hkv]).
+    fp16_budget_pct > 0 runs the selective decode (needs the cache's
+    full-precision copy)."""
     L = load()
     _dev(q, "q")
     B, Hq, d = q.shape
@@ -297,11 +321,34 @@ def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, r
     if out is None:
         out = torch.empty((B, Hq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
-    nws = L.fp4_attention_decode_workspace_size(Hq, C.byref(cs))
-    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
-    _check(L.fp4_attention_decode(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out), _ptr(lse),
-                                  _ptr(ws), nws, _stream(q.device)))
+    pct = int(fp16_budget_pct)
+    sidx = scnt = None
+    if return_selection:
+        kmax = decode_sel_kmax(cache.mid_cap, pct) if pct > 0 else 0
+        sidx = torch.empty((cache.B, cache.Hkv, kmax), dtype=torch.int32, device=q.device)
+        scnt = torch.zeros((cache.B, cache.Hkv), dtype=torch.int32, device=q.device)
+    if pct == 0:
+        nws = L.fp4_attention_decode_workspace_size(Hq, C.byref(cs))
+        ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
+        _check(L.fp4_attention_decode(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out),
+                                      _ptr(lse), _ptr(ws), nws, _stream(q.device)))
+    else:
+        nws = L.fp4_attention_decode_selective_workspace_size(Hq, C.byref(cs), pct)
+        ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
+        _check(L.fp4_attention_decode_selective(_ptr(q), Hq, C.byref(cs), pct, float(softmax_scale), out_dtype,
+                                                _ptr(out), _ptr(lse), _ptr(sidx if sidx is not None and sidx.numel() else None),
+                                                _ptr(scnt), _ptr(ws), nws, _stream(q.device)))
+    if return_selection:
+        return out, lse, sidx, scnt
     return out, lse
+
+
+def fp4_kv_block_sums(cache: KVCache):
+    """(Re)compute cache.k_sum from cache.k_mid over the tokens in use."""
+    L = load()
+    cs = cache.struct()
+    dev = cache.k_mid.device if cache.k_mid is not None else torch.device("cuda")
+    _check(L.fp4_kv_block_sums(C.byref(cs), _stream(dev)))
 
 
 def fp4_kv_cache_append(cache: KVCache, k_new, v_new, workspace=None):

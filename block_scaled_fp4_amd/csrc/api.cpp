@@ -313,19 +313,52 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   return hip_status(fp4i_launch_attn_fwd(A, s), "fp4_attention_fwd launch");
 }
 
-size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* c) {
-  if (!c || c->struct_size < sizeof(fp4_kv_cache) || Hq <= 0 || c->B <= 0 || c->d <= 0) return 0;
+}  // extern "C"
+
+namespace {
+
+// Workspace plan of a decode call: partials, then (with a budget) the
+// selection's keys, indices, counts and block mask.
+struct DecodePlan {
+  int nsplit = 0, nfull = 0, nprom = 0, kmax = 0, nbc = 0, nbw = 0;
   int64_t split_len = 0;
-  int ns = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &split_len);
-  int nf = fp4i_decode_full_splits((int64_t)c->n_sink + c->n_recent);
-  size_t n = (size_t)(c->B * Hq) * (size_t)(ns + nf);
-  return align256(n * (size_t)c->d * sizeof(float)) + align256(n * 2 * sizeof(float));
+  size_t part_o = 0, part_ml = 0, keys = 0, idx = 0, cnt = 0, mask = 0, total = 0;
+};
+
+DecodePlan decode_plan(int64_t Hq, const fp4_kv_cache* c, int pct) {
+  DecodePlan P;
+  P.nsplit = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &P.split_len);
+  P.nfull = fp4i_decode_full_splits((int64_t)c->n_sink + c->n_recent);
+  if (pct > 0) {
+    P.nbc = (int)((c->mid_cap + kDecSelBlock - 1) / kDecSelBlock);
+    P.kmax = (pct * P.nbc + 99) / 100;
+    P.nprom = (P.kmax + 3) / 4;
+    P.nbw = (P.nbc + 31) / 32;
+  }
+  const size_t n = (size_t)(c->B * Hq) * (size_t)(P.nsplit + P.nfull + P.nprom);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  P.part_o = take(n * (size_t)c->d * sizeof(float));
+  P.part_ml = take(n * 2 * sizeof(float));
+  if (pct > 0) {
+    const size_t nbk = (size_t)(c->B * c->Hkv);
+    P.keys = take(nbk * (size_t)(P.nbc > 0 ? P.nbc : 1) * sizeof(uint64_t));
+    P.idx = take(nbk * (size_t)(P.kmax > 0 ? P.kmax : 1) * sizeof(int32_t));
+    P.cnt = take(nbk * sizeof(int32_t));
+    P.mask = take(nbk * (size_t)(P.nbw > 0 ? P.nbw : 1) * sizeof(uint32_t));
+  }
+  P.total = off;
+  return P;
 }
 
-int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float softmax_scale,
-                         int32_t out_dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  const char* fn = "fp4_attention_decode";
+bool decode_args_ok(int64_t Hq, const fp4_kv_cache* c) {
+  return c && c->struct_size >= sizeof(fp4_kv_cache) && Hq > 0 && c->B > 0 && c->Hkv > 0 && c->d > 0 &&
+         c->mid_cap >= 0;
+}
+
+int decode_impl(const char* fn, const void* q, int64_t Hq, const fp4_kv_cache* c, int pct, float softmax_scale,
+                int32_t out_dtype, void* out, float* lse, int32_t* sel_idx, int32_t* sel_cnt, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (!c || c->struct_size < sizeof(fp4_kv_cache)) return fail(FP4_ERR_INVALID_ARG, "%s: cache is NULL or struct_size too small", fn);
   if (!q || !out) return fail(FP4_ERR_INVALID_ARG, "%s: q and out are required", fn);
   if (c->B < 1 || c->Hkv < 1 || Hq < 1 || Hq % c->Hkv) return fail(FP4_ERR_INVALID_ARG, "%s: bad B/Hq/Hkv", fn);
@@ -340,12 +373,19 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float
   if (c->mid_cap && (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->mid_len))
     return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 region buffers or mid_len missing", fn);
   if (out_dtype < FP4_BF16 || out_dtype > FP4_FP32) return fail(FP4_ERR_INVALID_ARG, "%s: bad out_dtype", fn);
-  const void* ptrs[] = {q, out, c->k_sink, c->v_sink, c->k_codes, c->k_scales, c->v_codes, c->v_scales, c->k_recent, c->v_recent};
+  if (pct < 0 || pct > 100) return fail(FP4_ERR_INVALID_ARG, "%s: fp16_budget_pct must be in [0, 100]", fn);
+  if (pct > 0 && c->mid_cap > 0 && (!c->k_mid || !c->v_mid || !c->k_sum))
+    return fail(FP4_ERR_INVALID_ARG, "%s: a budget > 0 needs the full-precision copy (k_mid, v_mid, k_sum)", fn);
+  const void* ptrs[] = {q, out, c->k_sink, c->v_sink, c->k_codes, c->k_scales, c->v_codes, c->v_scales, c->k_recent,
+                        c->v_recent, pct > 0 ? c->k_mid : nullptr, pct > 0 ? c->v_mid : nullptr,
+                        pct > 0 ? (const void*)c->k_sum : nullptr};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-  size_t need = fp4_attention_decode_workspace_size(Hq, c);
-  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  DecodeLaunch L;
+  const DecodePlan P = decode_plan(Hq, c, pct);
+  if (workspace_bytes < P.total || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, P.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  DecodeLaunch L{};
   L.q = q;
   L.B = c->B; L.Hq = Hq; L.Hkv = c->Hkv; L.d = c->d;
   L.n_sink = c->n_sink; L.n_recent = c->n_recent; L.mid_cap = c->mid_cap;
@@ -357,12 +397,75 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float
   L.out_dtype = out_dtype;
   L.out = out;
   L.lse = lse;
-  L.nsplit = fp4i_decode_splits(c->B, c->Hkv, c->mid_cap, &L.split_len);
-  L.nfull = fp4i_decode_full_splits((int64_t)c->n_sink + c->n_recent);
-  size_t n = (size_t)(c->B * Hq) * (size_t)(L.nsplit + L.nfull);
-  L.part_o = (float*)workspace;
-  L.part_ml = (float*)((char*)workspace + align256(n * (size_t)c->d * sizeof(float)));
-  return hip_status(fp4i_launch_decode(L, (hipStream_t)stream), "fp4_attention_decode launch");
+  L.nsplit = P.nsplit;
+  L.split_len = P.split_len;
+  L.nfull = P.nfull;
+  L.part_o = (float*)(ws + P.part_o);
+  L.part_ml = (float*)(ws + P.part_ml);
+  if (pct > 0) {
+    DecSelectLaunch S{};
+    S.q = q;
+    S.k_sum = c->k_sum;
+    S.mid_len = c->mid_len;
+    S.B = c->B; S.Hq = Hq; S.Hkv = c->Hkv; S.d = c->d; S.mid_cap = c->mid_cap;
+    S.pct = pct; S.kmax = P.kmax; S.nbc = P.nbc; S.nbw = P.nbw;
+    S.keys = (uint64_t*)(ws + P.keys);
+    S.idx = sel_idx ? sel_idx : (int32_t*)(ws + P.idx);
+    S.cnt = sel_cnt ? sel_cnt : (int32_t*)(ws + P.cnt);
+    S.mask = (uint32_t*)(ws + P.mask);
+    hipError_t e = fp4i_launch_decode_select(S, st);
+    if (e != hipSuccess) return hip_status(e, "decode selection launch");
+    L.k_mid = c->k_mid;
+    L.v_mid = c->v_mid;
+    L.sel_idx = S.idx;
+    L.sel_mask = S.mask;
+    L.kmax = P.kmax;
+    L.nprom = P.nprom;
+    L.nbw = P.nbw;
+  }
+  return hip_status(fp4i_launch_decode(L, st), "fp4_attention_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* c) {
+  if (!decode_args_ok(Hq, c)) return 0;
+  return decode_plan(Hq, c, 0).total;
+}
+
+int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* c, float softmax_scale,
+                         int32_t out_dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return decode_impl("fp4_attention_decode", q, Hq, c, 0, softmax_scale, out_dtype, out, lse, nullptr, nullptr,
+                     workspace, workspace_bytes, stream);
+}
+
+size_t fp4_attention_decode_selective_workspace_size(int64_t Hq, const fp4_kv_cache* c, int32_t pct) {
+  if (!decode_args_ok(Hq, c) || pct < 0 || pct > 100) return 0;
+  return decode_plan(Hq, c, pct).total;
+}
+
+int fp4_attention_decode_selective(const void* q, int64_t Hq, const fp4_kv_cache* c, int32_t fp16_budget_pct,
+                                   float softmax_scale, int32_t out_dtype, void* out, float* lse, int32_t* sel_idx,
+                                   int32_t* sel_cnt, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("fp4_attention_decode_selective", q, Hq, c, fp16_budget_pct, softmax_scale, out_dtype, out,
+                     lse, sel_idx, sel_cnt, workspace, workspace_bytes, stream);
+}
+
+int fp4_kv_block_sums(const fp4_kv_cache* c, void* stream) {
+  const char* fn = "fp4_kv_block_sums";
+  if (!c || c->struct_size < sizeof(fp4_kv_cache)) return fail(FP4_ERR_INVALID_ARG, "%s: cache is NULL or struct_size too small", fn);
+  if (c->B < 1 || c->Hkv < 1) return fail(FP4_ERR_INVALID_ARG, "%s: bad B/Hkv", fn);
+  if (c->d != 64 && c->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim %lld not in {64,128}", fn, (long long)c->d);
+  if (c->mid_cap < 0 || c->mid_cap % 16) return fail(FP4_ERR_INVALID_ARG, "%s: mid_cap must be a multiple of 16", fn);
+  if (c->mid_cap == 0) return FP4_OK;
+  if (!c->k_mid || !c->k_sum || !c->mid_len) return fail(FP4_ERR_INVALID_ARG, "%s: k_mid, k_sum and mid_len are required", fn);
+  if (!aligned16(c->k_mid) || !aligned16(c->k_sum)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return hip_status(fp4i_launch_kv_block_sums(c->k_mid, c->mid_len, const_cast<double*>(c->k_sum), c->B, c->Hkv,
+                                              c->mid_cap, c->d, (hipStream_t)stream),
+                    "fp4_kv_block_sums launch");
 }
 
 size_t fp4_kv_cache_append_workspace_size(const fp4_kv_cache* c) {
@@ -385,7 +488,10 @@ int fp4_kv_cache_append(const fp4_kv_cache* c, const void* k_new, const void* v_
   if (c->n_recent && (!c->k_recent || !c->v_recent)) return fail(FP4_ERR_INVALID_ARG, "%s: recent buffers missing", fn);
   if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->mid_len)
     return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 region buffers or mid_len missing", fn);
-  const void* ptrs[] = {k_new, v_new, c->k_recent, c->v_recent, c->k_codes, c->k_scales, c->v_codes, c->v_scales};
+  const int ndual = (c->k_mid ? 1 : 0) + (c->v_mid ? 1 : 0) + (c->k_sum ? 1 : 0);
+  if (ndual != 0 && ndual != 3) return fail(FP4_ERR_INVALID_ARG, "%s: give all of k_mid, v_mid, k_sum or none", fn);
+  const void* ptrs[] = {k_new, v_new, c->k_recent, c->v_recent, c->k_codes, c->k_scales, c->v_codes, c->v_scales,
+                        c->k_mid, c->v_mid, c->k_sum};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
   const size_t need = fp4_kv_cache_append_workspace_size(c);
@@ -401,6 +507,9 @@ int fp4_kv_cache_append(const fp4_kv_cache* c, const void* k_new, const void* v_
   L.mid_len = const_cast<int32_t*>(c->mid_len);
   L.overflow = overflow;
   L.ws = workspace;
+  L.k_mid = const_cast<void*>(c->k_mid);
+  L.v_mid = const_cast<void*>(c->v_mid);
+  L.k_sum = const_cast<double*>(c->k_sum);
   return hip_status(fp4i_launch_kv_append(L, (hipStream_t)stream), "fp4_kv_cache_append launch");
 }
 

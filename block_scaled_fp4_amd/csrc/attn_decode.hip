@@ -20,7 +20,12 @@
 //     tokens per channel -- exactly an A-operand row of the PV product;
 //   - extra workgroups of the same launch read the bf16 sink and recent
 //     tokens (128 per workgroup); the waves of a workgroup merge their
-//     (m, l, O) in LDS and a second kernel merges the workgroups' partials.
+//     (m, l, O) in LDS and a second kernel merges the workgroups' partials;
+//   - with selective promotion (ThriftAttention page, Metodologia / 2, in
+//     decode) a selection kernel first picks middle blocks of 128 tokens;
+//     further workgroups read those blocks from the full-precision copy (one
+//     block per wave), and the FP4 waves skip them: their loads fall past the
+//     buffer resources' ends (no memory access) and their keys are masked.
 // Probabilities enter the PV product as fp16 (q, K, V and P are not
 // re-quantized; P rounding is within the tolerance of the plain definition).
 #include "device_common.h"
@@ -77,6 +82,11 @@ struct DecArgs {
   float c;
   float* part_o;
   float* part_ml;
+  // selective promotion: workgroups of four promoted blocks (one per wave)
+  const uint16_t *k_mid, *v_mid;  // full-precision copy of the middle
+  const int32_t* sel_idx;         // [nbk, kmax] promoted blocks, -1 padded
+  const uint32_t* sel_mask;       // [nbk, nbw] bit j: block j promoted (null: none)
+  int kmax, nprom, nbw;
 };
 
 struct SplitBufs {
@@ -362,9 +372,40 @@ __device__ __forceinline__ void full_workgroup(DecRed<D>& S, const DecArgs& A, i
   write_partial<D>(S, R, A, bk, A.nsplit + f);
 }
 
+// Workgroup f of the promoted blocks of a (batch, kv head): wave w reads
+// promoted block sel_idx[4 f + w] (128 tokens, fewer for a short last block)
+// from the full-precision copy; partial index nsplit + nfull + f.
+template <int D>
+__device__ __forceinline__ void promoted_workgroup(DecRed<D>& S, const DecArgs& A, int64_t bk, int f, int wave) {
+  half8_t qf[D / 32];
+  load_q<D>(qf, A, bk);
+  DecState<D> R;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
+  R.m = -__builtin_inff();
+  R.l = 0.0f;
+  const int slot = 4 * f + wave;
+  const int j = slot < A.kmax ? A.sel_idx[bk * A.kmax + slot] : -1;
+  if (j >= 0) {
+    int64_t mlen = A.mid_len[bk / A.Hkv];
+    if (mlen < 0) mlen = 0;
+    if (mlen > A.mid_cap) mlen = A.mid_cap;
+    mlen &= ~(int64_t)15;
+    const int64_t t0 = (int64_t)j * (kStep * kDecWaves);
+    const int64_t rest = mlen - t0;
+    const uint32_t n = (uint32_t)(rest < kStep * kDecWaves ? (rest > 0 ? rest : 0) : kStep * kDecWaves);
+    const uint16_t* kb = A.k_mid + (bk * A.mid_cap + t0) * D;
+    const uint16_t* vb = A.v_mid + (bk * A.mid_cap + t0) * D;
+    for (uint32_t key0 = 0; key0 < n; key0 += kStep) bf16_step<D>(kb, kb, vb, vb, 0, n, qf, R, key0, A.c);
+  }
+  write_partial<D>(S, R, A, bk, A.nsplit + A.nfull + f);
+}
+
 // grid: B*Hkv*nfull workgroups over the full-precision (bf16 sink + recent)
-// tokens, then B*Hkv*nsplit over the splits of the FP4 region of each
-// (batch, kv head) (partial index = split).
+// tokens, B*Hkv*nprom over the promoted middle blocks, then B*Hkv*nsplit over
+// the splits of the FP4 region of each (batch, kv head) (partial index =
+// split).  (The short promoted workgroups go before the long splits: the
+// other order measured 10% slower.)
 template <int D>
 __global__ void __launch_bounds__(64 * kDecWaves, 3) decode_kernel(DecArgs A) {
   __shared__ DecRed<D> S;
@@ -376,7 +417,13 @@ __global__ void __launch_bounds__(64 * kDecWaves, 3) decode_kernel(DecArgs A) {
     full_workgroup<D>(S, A, (int64_t)blockIdx.x / A.nfull, (int)((int64_t)blockIdx.x % A.nfull), wave);
     return;
   }
-  const int64_t gi = (int64_t)blockIdx.x - nfw;
+  const int64_t npw = A.nbk * A.nprom;
+  if ((int64_t)blockIdx.x - nfw < npw) {
+    const int64_t gp = (int64_t)blockIdx.x - nfw;
+    promoted_workgroup<D>(S, A, gp / A.nprom, (int)(gp % A.nprom), wave);
+    return;
+  }
+  const int64_t gi = (int64_t)blockIdx.x - nfw - npw;
   const int64_t bk = gi / A.nsplit;
   const int split = (int)(gi % A.nsplit);
   const int64_t b = bk / A.Hkv;
@@ -405,6 +452,20 @@ __global__ void __launch_bounds__(64 * kDecWaves, 3) decode_kernel(DecArgs A) {
     sb.ks = make_rsrc(A.ks + bk * A.mid_cap * (D / 16), (uint32_t)(s1 * (D / 16)));
     sb.vc = make_rsrc(A.vc + bk * (A.mid_cap / 2) * D, (uint32_t)((s1 / 2) * D));
     sb.vs = make_rsrc(A.vs + bk * (A.mid_cap / 16) * D, (uint32_t)((s1 / 16) * D));
+    // steps of promoted blocks load from key kOOB instead: every offset then
+    // lies at or past 2^28 (scales) or 2^31 (codes), beyond the resources'
+    // ends (mid_cap * D / 2 < 2^31), so nothing is read and zeros come back;
+    // their keys are masked
+    constexpr uint32_t kOOB = (1u << 31) / (D / 2);
+    const uint32_t* smask = A.sel_mask ? A.sel_mask + bk * A.nbw : nullptr;
+    auto promoted = [&](uint32_t key) {
+      if (!smask) return false;
+      const uint32_t blk = key / (kStep * kDecWaves);
+      const uint32_t word = (uint32_t)__builtin_amdgcn_readfirstlane((int)smask[blk >> 5]);  // wave-uniform
+      return ((word >> (blk & 31u)) & 1u) != 0u;
+    };
+    auto at = [&](uint32_t key) { return promoted(key) ? kOOB : key; };
+    auto stop = [&](uint32_t key) { return promoted(key) ? key : (uint32_t)we; };
     const uint32_t kend = (uint32_t)we;
     // steps start at ws + 32 i; prefetches past the last one reload it
     // (cached) instead of branching
@@ -412,17 +473,17 @@ __global__ void __launch_bounds__(64 * kDecWaves, 3) decode_kernel(DecArgs A) {
     auto clampk = [&](uint32_t k) { return k < last ? k : last; };
     KStep<D> K0, K1, K2;
     VStep<D> V0, V1, V2;
-    load_fp4<D>(K0, V0, sb, (uint32_t)ws);
-    load_fp4<D>(K1, V1, sb, clampk((uint32_t)ws + kStep));
+    load_fp4<D>(K0, V0, sb, at((uint32_t)ws));
+    load_fp4<D>(K1, V1, sb, at(clampk((uint32_t)ws + kStep)));
     for (uint32_t key0 = (uint32_t)ws; key0 < kend; key0 += 3 * kStep) {
-      load_fp4<D>(K2, V2, sb, clampk(key0 + 2 * kStep));
-      fp4_step<D>(K0, V0, qf, R, key0, kend, A.c);
+      load_fp4<D>(K2, V2, sb, at(clampk(key0 + 2 * kStep)));
+      fp4_step<D>(K0, V0, qf, R, key0, stop(key0), A.c);
       if (key0 + kStep >= kend) break;
-      load_fp4<D>(K0, V0, sb, clampk(key0 + 3 * kStep));
-      fp4_step<D>(K1, V1, qf, R, key0 + kStep, kend, A.c);
+      load_fp4<D>(K0, V0, sb, at(clampk(key0 + 3 * kStep)));
+      fp4_step<D>(K1, V1, qf, R, key0 + kStep, stop(key0 + kStep), A.c);
       if (key0 + 2 * kStep >= kend) break;
-      load_fp4<D>(K1, V1, sb, clampk(key0 + 4 * kStep));
-      fp4_step<D>(K2, V2, qf, R, key0 + 2 * kStep, kend, A.c);
+      load_fp4<D>(K1, V1, sb, at(clampk(key0 + 4 * kStep)));
+      fp4_step<D>(K2, V2, qf, R, key0 + 2 * kStep, stop(key0 + 2 * kStep), A.c);
     }
   }
   write_partial<D>(S, R, A, bk, split);
@@ -480,7 +541,6 @@ hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t st) {
   A.split_len = L.split_len;
   A.nsplit = L.nsplit;
   A.nfull = L.nfull;
-  A.ns1 = L.nsplit + L.nfull;
   A.k_sink = (const uint16_t*)L.k_sink;
   A.v_sink = (const uint16_t*)L.v_sink;
   A.k_recent = (const uint16_t*)L.k_recent;
@@ -490,6 +550,14 @@ hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t st) {
   A.c = L.c;
   A.part_o = L.part_o;
   A.part_ml = L.part_ml;
+  A.k_mid = (const uint16_t*)L.k_mid;
+  A.v_mid = (const uint16_t*)L.v_mid;
+  A.sel_idx = L.sel_idx;
+  A.sel_mask = L.sel_mask;
+  A.kmax = L.kmax;
+  A.nprom = L.nprom;
+  A.nbw = L.nbw;
+  A.ns1 = L.nsplit + L.nfull + L.nprom;
   const int ns1 = A.ns1;
   hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)(L.B * L.Hkv * ns1)), dim3(64 * kDecWaves), 0, st, A);
   const dim3 mg((unsigned)(L.B * L.Hq));

@@ -22,6 +22,7 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef double double2_t __attribute__((ext_vector_type(2)));
 
 // E4M3 byte (0..0x7E) -> binary32 value, from the field layout: exponent field
 // e (bias 7) and 3-bit mantissa m; e = 0 is subnormal m * 2^-9.

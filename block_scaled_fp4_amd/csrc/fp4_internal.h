@@ -80,11 +80,35 @@ struct DecodeLaunch {
   int nsplit;        // context splits per (b, kv head)
   int nfull;         // full-precision (sink + recent) workgroups per (b, kv head)
   int64_t split_len; // tokens per split of the FP4 region (multiple of the chunk)
-  float* part_o;     // [B*Hq, nsplit+nfull, d]
-  float* part_ml;    // [B*Hq, nsplit+nfull, 2]
+  float* part_o;     // [B*Hq, nsplit+nfull+nprom, d]
+  float* part_ml;    // [B*Hq, nsplit+nfull+nprom, 2]
+  // selective promotion (nprom = 0: none)
+  const void* k_mid;         // bf16 [B,Hkv,mid_cap,d]
+  const void* v_mid;
+  const int32_t* sel_idx;    // [B*Hkv, kmax]
+  const uint32_t* sel_mask;  // [B*Hkv, nbw] bit j: middle block j promoted
+  int kmax, nprom, nbw;      // nprom = ceil(kmax / 4) workgroups of promoted blocks
 };
 
 int fp4i_decode_splits(int64_t B, int64_t Hkv, int64_t mid_cap, int64_t* split_len);
+
+// Selection of the promoted middle blocks for decode.
+struct DecSelectLaunch {
+  const void* q;         // bf16 [B,Hq,d]
+  const double* k_sum;   // [B*Hkv, nbc, d]
+  const int32_t* mid_len;
+  int64_t B, Hq, Hkv, d, mid_cap;
+  int pct, kmax, nbc, nbw;
+  uint64_t* keys;        // [B*Hkv, nbc] workspace
+  int32_t* idx;          // [B*Hkv, kmax]
+  int32_t* cnt;          // [B*Hkv]
+  uint32_t* mask;        // [B*Hkv, nbw]
+};
+
+constexpr int kDecSelBlock = 128;  // tokens per selection block of the middle
+hipError_t fp4i_launch_decode_select(const DecSelectLaunch& L, hipStream_t stream);
+hipError_t fp4i_launch_kv_block_sums(const void* k_mid, const int32_t* mid_len, double* k_sum, int64_t B,
+                                     int64_t Hkv, int64_t mid_cap, int64_t d, hipStream_t stream);
 
 struct KvAppendLaunch {
   int64_t B, Hkv, d, mid_cap;
@@ -97,6 +121,9 @@ struct KvAppendLaunch {
   int32_t* mid_len;
   int32_t* overflow;  // nullable
   void* ws;
+  void* k_mid;        // full-precision copy of the middle (nullable, with v_mid and k_sum)
+  void* v_mid;
+  double* k_sum;
 };
 
 size_t fp4i_kv_append_workspace(int64_t B, int64_t Hkv, int64_t n_recent, int64_t d);

@@ -20,6 +20,12 @@
 //   2. kv_append_commit_kernel: window from the workspace, mid_len and flags.
 // Launch 1 also keeps each batch's mid_len in the workspace: every workgroup
 // of launch 2 decides on that copy, while one of them updates mid_len.
+// With the cache's full-precision copy of the middle (the dual cache of the
+// ThriftAttention page, Significado), the quantizing lanes of launch 1 also
+// write their tokens unquantized, and one more workgroup per (batch, kv head)
+// extends the binary64 key-block sums: one lane per channel adds the moved
+// tokens in order (sequential, so the sums equal a one-pass sum over each
+// block's tokens).
 #include "device_common.h"
 #include "fp4_internal.h"
 #include "quant_core.h"
@@ -42,6 +48,11 @@ struct AppendArgs {
   uint16_t* ws_k;                // [B,Hkv,n_recent,d] new window
   uint16_t* ws_v;
   int32_t* snap;                 // [B] mid_len as launch 1 read it
+  uint16_t* k_mid;               // bf16 [B,Hkv,mid_cap,d] (nullable: no dual copy)
+  uint16_t* v_mid;
+  double* k_sum;                 // [B,Hkv,nbc,d]
+  int nbc;                       // ceil(mid_cap / kDecSelBlock)
+  int nsum;                      // 1 with the dual copy (its sums workgroup), else 0
 };
 
 // mid_len as the decode kernel reads it: clamped to [0, mid_cap], multiple of 16.
@@ -58,21 +69,42 @@ __device__ __forceinline__ const uint16_t* seq_row(const uint16_t* recent, const
   return t < A.n_recent ? recent + (bk * A.n_recent + t) * A.d : fresh + (bk * A.n_new + (t - A.n_recent)) * A.d;
 }
 
-// grid: B*Hkv*(ngroups + ncopy).  Workgroups (bk, g < ngroups) quantize
-// group g; workgroups (bk, ngroups + c) copy window chunk c (kCopyTok tokens
-// of the new window) into the workspace.
+// grid: B*Hkv*(ngroups + ncopy + nsum).  Workgroups (bk, g < ngroups)
+// quantize group g; workgroups (bk, ngroups + c) copy window chunk c
+// (kCopyTok tokens of the new window) into the workspace; with the dual copy
+// workgroup (bk, ngroups + ncopy) extends the key-block sums.
 __global__ void __launch_bounds__(256) kv_append_quant_kernel(AppendArgs A) {
   __shared__ float2_t tab[128];
   if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
   __syncthreads();
   const int64_t gi = blockIdx.x;
-  const int g = (int)(gi % (A.ngroups + A.ncopy));
-  const int64_t bk = gi / (A.ngroups + A.ncopy);
+  const int per = A.ngroups + A.ncopy + A.nsum;
+  const int g = (int)(gi % per);
+  const int64_t bk = gi / per;
   const int64_t b = bk / A.Hkv;
   if (g == 0 && bk % A.Hkv == 0 && threadIdx.x == 0) A.snap[b] = A.mid_len[b];
   const int64_t mid = used_mid(A, b);
   if (mid + A.n_new > A.mid_cap) return;  // no room: the batch stays as it is
   const int d = (int)A.d;
+  if (g == A.ngroups + A.ncopy) {
+    // key-block sums: lane c adds channel c of the moved tokens T[0, n_new)
+    const int c = threadIdx.x;
+    if (c < d) {
+      double* sums = A.k_sum + bk * (int64_t)A.nbc * d + c;
+      int64_t j = mid / kDecSelBlock;
+      double acc = mid % kDecSelBlock == 0 ? 0.0 : sums[j * d];
+      for (int t = 0; t < A.n_new; ++t) {
+        if (t > 0 && (mid + t) % kDecSelBlock == 0) {
+          sums[j * d] = acc;
+          ++j;
+          acc = 0.0;
+        }
+        acc = __dadd_rn(acc, (double)bf16_to_f32(seq_row(A.k_recent, A.k_new, A, bk, t)[c]));
+      }
+      sums[j * d] = acc;
+    }
+    return;
+  }
   if (g >= A.ngroups) {
     // new window: T[n_new + j] for j in this chunk, 16 bytes per step
     const int64_t per_tok = d / 8;  // 16-byte chunks per token
@@ -106,6 +138,12 @@ __global__ void __launch_bounds__(256) kv_append_quant_kernel(AppendArgs A) {
     const int64_t row = bk * A.mid_cap + dst_tok + tk;
     *reinterpret_cast<uint2_t*>(A.kc + row * (d / 2) + 8 * cb) = uint2_t{codes[0], codes[1]};
     A.ks[row * (d / 16) + cb] = (uint8_t)scale;
+    if (A.k_mid) {
+      const uint4_t* s4 = reinterpret_cast<const uint4_t*>(src);
+      uint4_t* d4 = reinterpret_cast<uint4_t*>(A.k_mid + row * d + 16 * cb);
+      d4[0] = s4[0];
+      d4[1] = s4[1];
+    }
   } else if (tid < nkb + d) {
     // V: channel c of the 16 tokens
     const int c = tid - nkb;
@@ -120,6 +158,11 @@ __global__ void __launch_bounds__(256) kv_append_quant_kernel(AppendArgs A) {
     for (int i = 0; i < 8; ++i)
       A.vc[(bk * (A.mid_cap / 2) + dst_tok / 2 + i) * d + c] = (uint8_t)((codes[i >> 2] >> (8 * (i & 3))) & 0xFFu);
     A.vs[(bk * (A.mid_cap / 16) + dst_tok / 16) * d + c] = (uint8_t)scale;
+    if (A.v_mid) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        A.v_mid[(bk * A.mid_cap + dst_tok + k) * d + c] = seq_row(A.v_recent, A.v_new, A, bk, t0 + k)[c];
+    }
   }
 }
 
@@ -152,9 +195,50 @@ __global__ void __launch_bounds__(256) kv_append_commit_kernel(AppendArgs A) {
   }
 }
 
+// grid: B*Hkv*nbc; block: d lanes, one channel each.  Block j's sum over its
+// tokens below mid_len, ascending (0 for a block with none).
+__global__ void __launch_bounds__(128) kv_block_sums_kernel(const uint16_t* k_mid, const int32_t* mid_len,
+                                                            double* k_sum, int64_t Hkv, int64_t mid_cap, int d,
+                                                            int nbc) {
+  const int64_t gi = blockIdx.x;
+  const int64_t bk = gi / nbc;
+  const int j = (int)(gi % nbc);
+  const int c = threadIdx.x;
+  if (c >= d) return;
+  int64_t M = mid_len[bk / Hkv];
+  if (M < 0) M = 0;
+  if (M > mid_cap) M = mid_cap;
+  M &= ~(int64_t)15;
+  const int64_t t0 = (int64_t)j * kDecSelBlock;
+  int64_t n = M - t0;
+  if (n < 0) n = 0;
+  if (n > kDecSelBlock) n = kDecSelBlock;
+  const uint16_t* p = k_mid + (bk * mid_cap + t0) * d + c;
+  double s = 0.0;
+  int64_t t = 0;
+  for (; t + 8 <= n; t += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (double)bf16_to_f32(p[(t + u) * d]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = __dadd_rn(s, v[u]);
+  }
+  for (; t < n; ++t) s = __dadd_rn(s, (double)bf16_to_f32(p[t * d]));
+  k_sum[(bk * nbc + j) * d + c] = s;
+}
+
 }  // namespace fp4dev
 
 using namespace fp4dev;
+
+hipError_t fp4i_launch_kv_block_sums(const void* k_mid, const int32_t* mid_len, double* k_sum, int64_t B,
+                                     int64_t Hkv, int64_t mid_cap, int64_t d, hipStream_t st) {
+  const int nbc = (int)((mid_cap + kDecSelBlock - 1) / kDecSelBlock);
+  if (nbc == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_block_sums_kernel, dim3((unsigned)(B * Hkv * nbc)), dim3(128), 0, st,
+                     (const uint16_t*)k_mid, mid_len, k_sum, Hkv, mid_cap, (int)d, nbc);
+  return hipGetLastError();
+}
 
 size_t fp4i_kv_append_workspace(int64_t B, int64_t Hkv, int64_t n_recent, int64_t d) {
   const size_t win = (size_t)(B * Hkv * n_recent * d) * 2;  // bf16 bytes of one window copy
@@ -183,8 +267,13 @@ hipError_t fp4i_launch_kv_append(const KvAppendLaunch& L, hipStream_t st) {
   A.ws_k = (uint16_t*)L.ws;
   A.ws_v = (uint16_t*)((char*)L.ws + a);
   A.snap = (int32_t*)((char*)L.ws + 2 * a);
-  hipLaunchKernelGGL(kv_append_quant_kernel, dim3((unsigned)(L.B * L.Hkv * (A.ngroups + A.ncopy))), dim3(256), 0, st,
-                     A);
+  A.k_mid = (uint16_t*)L.k_mid;
+  A.v_mid = (uint16_t*)L.v_mid;
+  A.k_sum = L.k_sum;
+  A.nbc = (int)((L.mid_cap + kDecSelBlock - 1) / kDecSelBlock);
+  A.nsum = L.k_mid ? 1 : 0;
+  hipLaunchKernelGGL(kv_append_quant_kernel, dim3((unsigned)(L.B * L.Hkv * (A.ngroups + A.ncopy + A.nsum))), dim3(256),
+                     0, st, A);
   const int nc = A.ncopy > 0 ? A.ncopy : 1;
   hipLaunchKernelGGL(kv_append_commit_kernel, dim3((unsigned)(L.B * L.Hkv * nc)), dim3(256), 0, st, A);
   return hipGetLastError();

@@ -206,7 +206,20 @@ typedef struct fp4_kv_cache {
   const void* v_recent;
   const int32_t* mid_len;  /* device [B]: NVFP4 tokens in use, multiple of 16, <= mid_cap;
                               the context of batch b is n_sink + mid_len[b] + n_recent tokens */
+  /* Optional full-precision copy of the middle (the dual cache of the
+     ThriftAttention page, Significado: an FP16 and an FP4 copy side by side):
+     all three pointers or none.  Read by fp4_attention_decode_selective with a
+     budget > 0; fp4_kv_cache_append keeps them up to date when present. */
+  const void* k_mid;       /* bf16 [B,Hkv,mid_cap,d]: the middle tokens unquantized */
+  const void* v_mid;       /* bf16 [B,Hkv,mid_cap,d] */
+  const double* k_sum;     /* [B,Hkv,ceil(mid_cap/128),d]: binary64 sum of each block of
+                              FP4_DECODE_SEL_BLOCK k_mid tokens counted from the first middle
+                              token (the last block in use may be short), added in ascending
+                              token order */
 } fp4_kv_cache;
+
+/* tokens per selection block of the cache middle */
+#define FP4_DECODE_SEL_BLOCK 128
 
 /*
  * One query token per (batch, query head) against the cache: out [B,Hq,d] =
@@ -221,6 +234,40 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* cache, f
                          size_t workspace_bytes, void* stream);
 
 size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* cache);
+
+/*
+ * Decode with selective promotion (ThriftAttention page, Metodologia / 1 and
+ * / 2, applied to one query token).  For every (batch, kv head) the middle is
+ * cut into blocks of FP4_DECODE_SEL_BLOCK tokens from its first token (the
+ * last one may be short: n_b = ceil(mid_len[b] / 128) blocks).  Block j is
+ * scored by qbar . (k_sum[j] / tokens in j) in binary64, ascending channels,
+ * where qbar is the mean of the kv head's G query vectors (reading: the query
+ * block of a kv head is the G query tokens that read it).  The
+ * ceil(fp16_budget_pct * n_b / 100) best blocks (ties: lower j) are read from
+ * k_mid / v_mid, every other middle block from the NVFP4 copy; sink and recent
+ * tokens as in fp4_attention_decode, and probabilities as there.
+ * fp16_budget_pct 0..100; 0 is fp4_attention_decode (the dual pointers are
+ * then not read).  sel_idx [B,Hkv,kmax] (ascending, -1 padded; kmax =
+ * ceil(pct * ceil(mid_cap/128) / 100)) and sel_cnt [B,Hkv] receive the choice
+ * when non-null.  k_sum must hold the sums of the tokens in use (see
+ * fp4_kv_block_sums); NaN sums give an unspecified choice.  Workspace: see
+ * the query (it depends on the budget).
+ */
+int fp4_attention_decode_selective(const void* q, int64_t Hq, const fp4_kv_cache* cache, int32_t fp16_budget_pct,
+                                   float softmax_scale, int32_t out_dtype, void* out, float* lse, int32_t* sel_idx,
+                                   int32_t* sel_cnt, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fp4_attention_decode_selective_workspace_size(int64_t Hq, const fp4_kv_cache* cache,
+                                                     int32_t fp16_budget_pct);
+
+/*
+ * (Re)computes cache->k_sum from cache->k_mid: for every (batch, kv head) and
+ * block j < ceil(mid_cap/128), the binary64 sum over ascending tokens of the
+ * block's tokens below mid_len[b] (0.0 for a block with none).  For a cache
+ * whose middle was filled without fp4_kv_cache_append.  k_sum is written in
+ * place.  No workspace.
+ */
+int fp4_kv_block_sums(const fp4_kv_cache* cache, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Cache append -- ScaleSearch page, Metodologia / ScaleSearchAttention      */
@@ -240,7 +287,10 @@ size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* cache
  * [0, mid_cap] and rounded down to a multiple of 16, as the decode reads it).
  * A batch whose NVFP4 region has no room for n_new more tokens is left
  * unchanged; overflow [B] (device, nullable) receives 1 for such a batch, 0
- * otherwise.  The sink is never touched.
+ * otherwise.  The sink is never touched.  With the cache's full-precision
+ * copy, the moved tokens are also written unquantized to k_mid / v_mid and
+ * added, in token order, to the k_sum of their block (a block's sum restarts
+ * from zero at its first token).
  * k_new, v_new: bf16 [B,Hkv,n_new,d], dense, 16-byte aligned.  The cache's
  * recent buffers, NVFP4 arrays and mid_len are written in place (the const
  * qualifiers of fp4_kv_cache do not apply to this call).  Calls on one cache

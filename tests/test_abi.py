@@ -128,3 +128,36 @@ def test_kv_append_rejects_bad_arguments(L):
     cs.d = 128
     cs.mid_len = None
     assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, need, None) == -1
+
+
+def test_selective_decode_and_block_sums_reject_bad_arguments(L):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+    cs = fp4.KVCacheStruct(C.sizeof(fp4.KVCacheStruct), 2, 2, 128, 16, 32, 256, f, f, f, f, f, f, f, f, f,
+                           f, f, f)
+    base = L.fp4_attention_decode_workspace_size(8, C.byref(cs))
+    need = L.fp4_attention_decode_selective_workspace_size(8, C.byref(cs), 10)
+    assert need > base > 0  # selection keys, indices, counts and mask on top of the partials
+    assert L.fp4_attention_decode_selective_workspace_size(8, C.byref(cs), 101) == 0
+    assert L.fp4_attention_decode_selective_workspace_size(8, C.byref(cs), 0) == base
+
+    def call(pct, nbytes=need):
+        return L.fp4_attention_decode_selective(f, 8, C.byref(cs), pct, 0.0, 2, f, None, None, None, f, nbytes, None)
+
+    assert call(-1) == -1 and call(101) == -1
+    assert call(10, need - 1) == -3
+    cs.k_sum = None
+    assert call(10) == -1  # the budget needs the full-precision copy
+    assert L.fp4_kv_block_sums(C.byref(cs), None) == -1
+    cs.k_sum = C.c_void_p((1 << 20) + 8)
+    assert call(10) == -1  # 16-byte alignment
+    assert L.fp4_kv_block_sums(C.byref(cs), None) == -1
+    cs.k_sum = f
+    cs.mid_cap = 100
+    assert L.fp4_kv_block_sums(C.byref(cs), None) == -1
+    cs.mid_cap = 256
+    cs.d = 96
+    assert L.fp4_kv_block_sums(C.byref(cs), None) == -2
+    cs.d = 128
+    cs.v_mid = None
+    assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, 1 << 30, None) == -1  # all three or none

@@ -7,42 +7,9 @@ import torch
 
 import oracle
 from block_scaled_fp4_amd import synth
-from gpu_helpers import assert_close_attn, case
+from gpu_helpers import assert_close_attn, build_cache, case
 
 pytestmark = pytest.mark.gpu
-
-
-def build_cache(fp4, k, v, ctx, n_sink, n_recent, mid_cap):
-    """Fill the cache buffers on the GPU from the full bf16 context k, v [B,Hkv,L,d]."""
-    B, Hkv, Lcap, d = k.shape
-    dev = k.device
-    kc = torch.zeros((B, Hkv, mid_cap, d // 2), dtype=torch.uint8, device=dev)
-    ks = torch.zeros((B, Hkv, mid_cap, d // 16), dtype=torch.uint8, device=dev)
-    vc = torch.zeros((B, Hkv, mid_cap // 2, d), dtype=torch.uint8, device=dev)
-    vs = torch.zeros((B, Hkv, mid_cap // 16, d), dtype=torch.uint8, device=dev)
-    k_sink = k[:, :, :n_sink].contiguous()
-    v_sink = v[:, :, :n_sink].contiguous()
-    k_rec = torch.zeros((B, Hkv, n_recent, d), dtype=k.dtype, device=dev)
-    v_rec = torch.zeros((B, Hkv, n_recent, d), dtype=k.dtype, device=dev)
-    mids = []
-    for b in range(B):
-        L = int(ctx[b])
-        M = L - n_sink - n_recent
-        assert M >= 0 and M % 16 == 0 and M <= mid_cap
-        mids.append(M)
-        k_rec[b] = k[b, :, L - n_recent:L]
-        v_rec[b] = v[b, :, L - n_recent:L]
-        if M:
-            km = k[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
-            vm = v[b, :, n_sink:n_sink + M].contiguous().view(Hkv * M, d)
-            rk = fp4.fp4_quantize(km, 0, True)
-            rv = fp4.fp4_quantize(vm, 1, True)
-            kc[b, :, :M] = rk["codes"].view(Hkv, M, d // 2)
-            ks[b, :, :M] = rk["scales"].view(Hkv, M, d // 16)
-            vc[b, :, :M // 2] = rv["codes"].view(Hkv, M // 2, d)
-            vs[b, :, :M // 16] = rv["scales"].view(Hkv, M // 16, d)
-    mid_len = torch.tensor(mids, dtype=torch.int32, device=dev)
-    return fp4.KVCache(k_sink, v_sink, kc, ks, vc, vs, k_rec, v_rec, mid_len)
 
 
 @pytest.mark.parametrize("d", [64, 128])
