@@ -222,7 +222,7 @@ def bench_quantizer(fp4, synth, torch, n):
                 rows_x64_frac_hbm=round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4))
 
 
-def bench_decode(fp4, synth, torch, n):
+def bench_decode(fp4, synth, torch, n, selective=True):
     B, Hq, Hkv, L, d = 16, 32, 8, 131072, 128
     n_sink, n_recent = 128, 256
     M = L - n_sink - n_recent
@@ -241,9 +241,14 @@ def bench_decode(fp4, synth, torch, n):
         ks[b] = rk["scales"].view(Hkv, M, d // 16)
         vc[b] = rv["codes"].view(Hkv, M // 2, d)
         vs[b] = rv["scales"].view(Hkv, M // 16, d)
+    # the dual cache's full-precision copy of the middle and its key-block sums
+    k_mid = k[:, :, n_sink:n_sink + M].contiguous()
+    v_mid = v[:, :, n_sink:n_sink + M].contiguous()
+    k_sum = torch.empty((B, Hkv, (M + 127) // 128, d), dtype=torch.float64, device="cuda")
     cache = fp4.KVCache(k[:, :, :n_sink].contiguous(), v[:, :, :n_sink].contiguous(), kc, ks, vc, vs,
                         k[:, :, L - n_recent:].contiguous(), v[:, :, L - n_recent:].contiguous(),
-                        torch.full((B,), M, dtype=torch.int32, device="cuda"))
+                        torch.full((B,), M, dtype=torch.int32, device="cuda"), k_mid, v_mid, k_sum)
+    fp4.fp4_kv_block_sums(cache)
     del k, v
     out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
     timer = Timer(torch)
@@ -252,12 +257,31 @@ def bench_decode(fp4, synth, torch, n):
     qo = B * Hq * d * 2 * 2
     algo = kv_bytes + qo
     gbps = algo / ms / 1e6
-    return dict(workload="decode batch 16, 32 q / 8 kv heads, context 131072, d 128, 128 sink + 256 recent bf16",
-                algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
-                frac_hbm=round(gbps / HBM_PEAK_GBS, 4),
-                roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbps / HBM_PEAK_GBS, 4),
-                          "traffic": read_traffic("decode_b16_ctx131072", "attn_decode.hip")})
+    res = dict(workload="decode batch 16, 32 q / 8 kv heads, context 131072, d 128, 128 sink + 256 recent bf16",
+               algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
+               frac_hbm=round(gbps / HBM_PEAK_GBS, 4),
+               roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic("decode_b16_ctx131072", "attn_decode.hip")})
+    if not selective:
+        return res
+    # selective promotion, 10% of the middle blocks per (batch, kv head) from the full-precision copy
+    pct = 10
+    nb = (M + 127) // 128
+    kp = (pct * nb + 99) // 100
+    ms_sel = timer.run(lambda: fp4.fp4_attention_decode(q, cache, out_dtype=fp4.BF16, return_lse=False, out=out,
+                                                        fp16_budget_pct=pct), n)
+    sel_kv = B * Hkv * ((nb - kp) * 128 * (d // 2 + d // 16) * 2 + kp * 128 * d * 2 * 2
+                        + (n_sink + n_recent) * d * 2 * 2 + nb * d * 8)
+    algo_sel = sel_kv + qo
+    gb_sel = algo_sel / ms_sel / 1e6
+    res["selective_10pct"] = dict(
+        workload="the same decode, 10% of the 128-token middle blocks per (batch, kv head) promoted to the "
+                 "bf16 copy (scores, selection, decode, merge)",
+        algorithmic_bytes=algo_sel, us=round(ms_sel * 1e3, 2), GBps=round(gb_sel, 1),
+        frac_hbm=round(gb_sel / HBM_PEAK_GBS, 4),
+        bf16_decode_equivalent_bytes=B * Hkv * L * d * 2 * 2 + qo)
+    return res
 
 
 def bench_kv_append(fp4, torch, n):
@@ -328,7 +352,7 @@ def pmc_mode(mode, fp4, synth, torch):
                                   quantized=quant, selection=sel, return_lse=False, out=out)
         torch.cuda.synchronize()
     elif mode == "decode":
-        bench_decode(fp4, synth, torch, 3)
+        bench_decode(fp4, synth, torch, 3, selective=False)
     elif mode == "quant":
         x = synth.quant_tensor().cuda()
         for _ in range(3):

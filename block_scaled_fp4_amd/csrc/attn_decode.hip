@@ -258,10 +258,12 @@ __device__ __forceinline__ void bf16_step(const uint16_t* ksk, const uint16_t* k
   for (int g = 0; g < 2; ++g) {
     const uint32_t key = key0 + krow(m, g);
     const bool ok = key < n_full;
-    const uint16_t* src = full_row<D>(ksk, krc, n_sink, ok ? key : 0u) + q4 * (D / 4);
+    const uint16_t* src = full_row<D>(ksk, krc, n_sink, ok ? key : 0u) + 8 * q4;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(src + 8 * s) : uint4_t{0, 0, 0, 0};
+      // reduction order of the bf16 tokens: lane group q4, step s -> d = 8 (q4 + 4 s) .. +8,
+      // so the four lane groups read 64 contiguous bytes of a key row per load
+      const uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(src + 32 * s) : uint4_t{0, 0, 0, 0};
       const half2_t a = bf16x2_to_half2(w[0]), b = bf16x2_to_half2(w[1]);
       const half2_t cc = bf16x2_to_half2(w[2]), dd = bf16x2_to_half2(w[3]);
       acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(half8_t{a[0], a[1], b[0], b[1], cc[0], cc[1], dd[0], dd[1]},
@@ -297,15 +299,16 @@ __device__ __forceinline__ void bf16_step(const uint16_t* ksk, const uint16_t* k
   for (int t = 0; t < D / 16; ++t) R.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[t], pf, R.o[t], 0, 0, 0);
 }
 
-// q fragments in the K reduction order: lane group q4, step s -> d = q4*D/4 + 8*s .. +8.
-template <int D>
+// q fragments in the K reduction order: lane group q4, step s -> d = q4*D/4 + 8*s .. +8
+// for the NVFP4 keys (FULL false), d = 8 (q4 + 4 s) .. +8 for the bf16 ones.
+template <int D, bool FULL = false>
 __device__ __forceinline__ void load_q(half8_t (&qf)[D / 32], const DecArgs& A, int64_t bk) {
   const int lane = threadIdx.x & 63, q4 = lane >> 4, head = lane & 15;
   const bool ok = head < A.G;
-  const uint16_t* qp = A.q + (bk * A.G + (ok ? head : 0)) * D + q4 * (D / 4);
+  const uint16_t* qp = A.q + (bk * A.G + (ok ? head : 0)) * D + (FULL ? 8 * q4 : q4 * (D / 4));
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
-    uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(qp + 8 * s) : uint4_t{0, 0, 0, 0};
+    uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(qp + (FULL ? 32 : 8) * s) : uint4_t{0, 0, 0, 0};
     half2_t a = bf16x2_to_half2(w[0]), bb = bf16x2_to_half2(w[1]), cc = bf16x2_to_half2(w[2]), dd = bf16x2_to_half2(w[3]);
     qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
   }
@@ -354,7 +357,7 @@ __device__ __forceinline__ void write_partial(DecRed<D>& S, const DecState<D>& R
 template <int D>
 __device__ __forceinline__ void full_workgroup(DecRed<D>& S, const DecArgs& A, int64_t bk, int f, int wave) {
   half8_t qf[D / 32];
-  load_q<D>(qf, A, bk);
+  load_q<D, true>(qf, A, bk);
   DecState<D> R;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
@@ -378,7 +381,7 @@ __device__ __forceinline__ void full_workgroup(DecRed<D>& S, const DecArgs& A, i
 template <int D>
 __device__ __forceinline__ void promoted_workgroup(DecRed<D>& S, const DecArgs& A, int64_t bk, int f, int wave) {
   half8_t qf[D / 32];
-  load_q<D>(qf, A, bk);
+  load_q<D, true>(qf, A, bk);
   DecState<D> R;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) R.o[t] = float4_t{0, 0, 0, 0};
