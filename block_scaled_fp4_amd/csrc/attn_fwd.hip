@@ -401,7 +401,7 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], qf[s], acc[g], 0, 0, 0);
       if (i + kAhead < NM) ring[(i + kAhead) % kRing] = kfrag(i + kAhead);
       if (s == 0 && g > 0) mask_max(g - 1);
-      __builtin_amdgcn_sched_barrier(0x0407);  // ALU (VALU, SALU, transcendental) may cross
+      __builtin_amdgcn_sched_barrier(0x0406);  // VALU, SALU and transcendental ops may cross (not MFMA, not LDS)
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -432,22 +432,38 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   const half8_t* vbase = S.v + (lane & 31) * Smem<D, BC>::VS8 + hi;
   float lsum = 0.0f;
   // ---- P operands of subtile g, built in two halves (this lane's values
-  // i = 8*h2 .. +8); prep_p forms the subtile's level-2 scale data first
+  // i = 8*h2 .. +8).  The subtile's level-2 scale data comes from the LDS
+  // table (lookup, issued a subtile ahead of its use) and is then combined
+  // with the row's offsets (finalize).
+  struct PRaw {
+    float lg, inv, s;
+  };
   struct PPrep {
     float off, inv;
     half_t s2r;
   };
-  auto prep_p = [&](int g) {
-    PPrep q;
+  auto lookup = [&](int g) {
+    PRaw r{0.0f, 1.0f, 0.0f};
     if (FP4) {
-      // level 2: s2 = E4M3(448 * max e) from the block maximum, then the
-      // quantization inputs t = e * 2688 / s2 = 2^(x - tm + lg)
+      // level 2: s2 = E4M3(448 * max e) from the block maximum
       const float toff = use ? -tm : ninf;
       const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[g], c, toff));
       const float4_t ps = S.pt[f32_to_e4m3(emax * 448.0f)];
-      q.off = use ? ps[0] - tm : ninf;
-      q.inv = ps[1];
-      q.s2r = (half_t)(ps[2] * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf));
+      r.lg = ps[0];
+      r.inv = ps[1];
+      r.s = ps[2];
+    }
+    return r;
+  };
+  // this row's weight of the tile relative to its reference, 2^(tm - m)
+  const float rr = FP4 ? __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : 1.0f;
+  auto finalize = [&](const PRaw& r) {
+    PPrep q;
+    if (FP4) {
+      // the quantization inputs t = e * 2688 / s2 = 2^(x - tm + lg)
+      q.off = use ? r.lg - tm : ninf;
+      q.inv = r.inv;
+      q.s2r = (half_t)(r.s * rr);
     } else {
       q.off = use ? -R.m : ninf;
       q.inv = 1.0f;
@@ -488,12 +504,13 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) ring[i] = vfrag(i);
     half8_t pcur[2], pnext[2];
-    {
-      const PPrep q0 = prep_p(0);
-      make_half(0, 0, q0, pcur[0]);
-      make_half(0, 1, q0, pcur[1]);
-    }
-    PPrep qn;
+    // the level-2 scale data of subtile g + 2 is looked up (an LDS read) a
+    // whole subtile before its use, so that no wait drains the V ring
+    PRaw rn = lookup(0);
+    PPrep qn = finalize(rn);
+    make_half(0, 0, qn, pcur[0]);
+    make_half(0, 1, qn, pcur[1]);
+    if (NG > 1) rn = lookup(1);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -503,8 +520,11 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
       R.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], pcur[h2], R.o[t], 0, 0, 0);
       if (i + kAhead < NM) ring[(i + kAhead) % kRing] = vfrag(i + kAhead);
       if (g + 1 < NG) {
-        if (k == 0) qn = prep_p(g + 1);
-        if (k == 1) make_half(g + 1, 0, qn, pnext[0]);
+        if (k == 1) {
+          qn = finalize(rn);
+          make_half(g + 1, 0, qn, pnext[0]);
+          if (g + 2 < NG) rn = lookup(g + 2);
+        }
         if (k == NPV / 2 + 1) make_half(g + 1, 1, qn, pnext[1]);
         if (k == NPV - 1) {
           pcur[0] = pnext[0];
