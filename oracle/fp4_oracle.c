@@ -294,6 +294,35 @@ void orc_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* Incoherence processing ([ScaleSearch] Metodologia / ScaleSearchAttention:  */
+/* Hadamard transforms of Q and K before quantization)                       */
+/* ------------------------------------------------------------------------ */
+
+/* Each row v of x [rows][n] (n a power of two) becomes H_n (s o v) / sqrt(n):
+   s_j = -1 where bit j of signs (32 bits per word) is set, else +1 (the sign
+   flip is exact); H_n is the Sylvester Hadamard matrix, applied by butterfly
+   stages of span h = 1, 2, 4, ..., n/2, each pair (i, i+h) with bit h of i
+   clear becoming (a + b, a - b) in binary32; then every element is
+   multiplied by the binary32 value of 1/sqrt(n).  The rotation R =
+   diag(s) H_n / sqrt(n) is orthogonal, so (Q R)(K R)^T = Q K^T. */
+void orc_hadamard_rows(float* x, int64_t rows, int n, const uint32_t* signs) {
+  const float c = (float)(1.0 / sqrt((double)n));
+  for (int64_t r = 0; r < rows; ++r) {
+    float* v = x + r * n;
+    for (int j = 0; j < n; ++j)
+      if (signs && ((signs[j >> 5] >> (j & 31)) & 1u)) v[j] = -v[j];
+    for (int h = 1; h < n; h <<= 1)
+      for (int i = 0; i < n; ++i)
+        if (!(i & h)) {
+          float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+    for (int j = 0; j < n; ++j) v[j] = v[j] * c;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Block selection ([Thrift] Metodologia / 1)                                */
 /* ------------------------------------------------------------------------ */
 
@@ -523,7 +552,13 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
                       int64_t Sq, int64_t Sk, int d, int causal, double softmax_scale, int kv_tile,
                       int scale_search, int fmin, int fmax, int pct, int sel_block,
                       const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
-                      float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt) {
+                      float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt,
+                      const float* q_fp4, const float* k_fp4) {
+  /* q_fp4, k_fp4 (nullable, same layout as q, k): what the FP4 path
+     quantizes, e.g. Q and K after incoherence processing; the FP16 path and
+     the block means always use q and k. */
+  if (!q_fp4) q_fp4 = q;
+  if (!k_fp4) k_fp4 = k;
   if (d % 16 || Sk % 16 || kv_tile % 16 || H % Hkv) return -1;
   if (causal && Sq != Sk) return -1;
   if (pct > 0 && sel_block % kv_tile) return -1;
@@ -538,7 +573,9 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
     const float* qb = q + ((int64_t)b * H + h) * Sq * d;
     const float* kb = k + ((int64_t)b * Hkv + hk) * Sk * d;
     const float* vb = v + ((int64_t)b * Hkv + hk) * Sk * d;
-    double* Kh = quant_dequant(kb, Sk, d, 0, scale_search, fmin, fmax);
+    const float* qbr = q_fp4 + ((int64_t)b * H + h) * Sq * d;
+    const float* kbr = k_fp4 + ((int64_t)b * Hkv + hk) * Sk * d;
+    double* Kh = quant_dequant(kbr, Sk, d, 0, scale_search, fmin, fmax);
     double* Vh = quant_dequant(vb, Sk, d, 1, scale_search, fmin, fmax);
     double *K16 = NULL, *V16 = NULL;
     int32_t* sidx = NULL;
@@ -567,7 +604,7 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
       double* qh = (double*)malloc(sizeof(double) * (size_t)d);
       double* q16 = (double*)malloc(sizeof(double) * (size_t)d);
       for (int blk = 0; blk < d / 16; ++blk) {
-        orc_quantize_block(qb + i * d + blk * 16, 1, scale_search, fmin, fmax, cd, &sc, &of, NULL);
+        orc_quantize_block(qbr + i * d + blk * 16, 1, scale_search, fmin, fmax, cd, &sc, &of, NULL);
         for (int t = 0; t < 16; ++t) qh[blk * 16 + t] = orc_e2m1_value(cd[t]) * orc_e4m3_value(sc);
       }
       for (int dd = 0; dd < d; ++dd) q16[dd] = orc_round_fp16(qb[i * d + dd]);

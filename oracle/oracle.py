@@ -21,7 +21,7 @@ __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
-    "score_factor", "kv_append", "block_sums",
+    "score_factor", "kv_append", "block_sums", "hadamard_rows",
 ]
 
 
@@ -79,8 +79,10 @@ def lib():
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
-                                    C.c_int, _f32p, _vp, _vp, _vp]
+                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp]
     L.orc_attention_fwd.restype = C.c_int
+    L.orc_hadamard_rows.argtypes = [_f32p, C.c_int64, C.c_int, _vp]
+    L.orc_hadamard_rows.restype = None
     L.orc_attention_exact.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                       C.c_int64, C.c_int, C.c_int, C.c_double, _vp, C.c_int64,
                                       _vp, C.c_int, _f32p, _vp]
@@ -156,6 +158,19 @@ def quantize_block(y, scale_search=True, fmin=-2, fmax=6, return_sse=False):
     return out + (sse,) if return_sse else out
 
 
+def hadamard_rows(x, signs=None):
+    """Incoherence processing of the rows of x [..., n] (n a power of two):
+    H_n (s o row) / sqrt(n) in binary32 (orc_hadamard_rows); signs is a
+    sequence of 32-bit words, bit j set negating element j first."""
+    x = _f32(x).copy()
+    n = x.shape[-1]
+    sg = None if signs is None else np.ascontiguousarray(np.asarray(signs, np.uint32).reshape(-1))
+    if sg is not None:
+        assert sg.size * 32 >= n
+    lib().orc_hadamard_rows(x.reshape(-1), x.size // n, n, _ptr(sg))
+    return x
+
+
 def quantize(x, block_axis=0, scale_search=True, fmin=-2, fmax=6, global_mode=0, g=1.0):
     """Quantize a 2-D tensor. Returns dict(codes, scales, offsets, g, nonfinite_blocks)."""
     x = _f32(x)
@@ -223,14 +238,22 @@ def _sel(arr, dtype):
 
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
-                  with_topk=False):
+                  with_topk=False, hadamard=False, signs=None):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
+
+    hadamard: the FP4 path quantizes Q and K after incoherence processing
+    (hadamard_rows with the given signs); the FP16 path and the block means
+    use the original Q and K.
 
     Returns (out [nh, nr, d], lse [nh, nr]) and, with with_topk, also
     (topk_idx [nh, nqb, kmax], topk_cnt [nh, nqb])."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, H, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
+    qr = kr = None
+    if hadamard:
+        qr = np.ascontiguousarray(hadamard_rows(q, signs).reshape(-1))
+        kr = np.ascontiguousarray(hadamard_rows(k, signs).reshape(-1))
     ra, nr = _sel(rows, np.int64)
     ha, nh = _sel(heads, np.int32)
     nr = nr if ra is not None else Sq
@@ -246,7 +269,7 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
                                  int(causal), float(softmax_scale), kv_tile, int(scale_search),
                                  fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
                                  _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
-                                 _ptr(tcnt))
+                                 _ptr(tcnt), _ptr(qr), _ptr(kr))
     if rc != 0:
         raise ValueError("bad attention arguments")
     res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))
