@@ -36,7 +36,8 @@ class FP4Error(RuntimeError):
 
 class QuantOpts(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
-                ("f_max", C.c_int32), ("global_scale", C.c_int32), ("block_axis", C.c_int32)]
+                ("f_max", C.c_int32), ("global_scale", C.c_int32), ("block_axis", C.c_int32),
+                ("hadamard", C.c_int32), ("hadamard_signs", C.c_uint32 * 4)]
 
 
 class AttnProblem(C.Structure):
@@ -51,7 +52,16 @@ class AttnOpts(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("causal", C.c_int32), ("softmax_scale", C.c_float),
                 ("kv_tile", C.c_int32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
                 ("f_max", C.c_int32), ("fp16_budget_pct", C.c_int32), ("sel_block", C.c_int32),
-                ("out_dtype", C.c_int32), ("selection_given", C.c_int32)]
+                ("out_dtype", C.c_int32), ("selection_given", C.c_int32), ("hadamard_qk", C.c_int32),
+                ("hadamard_signs", C.c_uint32 * 4)]
+
+
+def _sign_words(signs):
+    """Sign bits of the incoherence rotation as four 32-bit words (None: no flips)."""
+    w = (C.c_uint32 * 4)()
+    for i, v in enumerate(list(signs or [])[:4]):
+        w[i] = int(v) & 0xFFFFFFFF
+    return w
 
 
 class KVCacheStruct(C.Structure):
@@ -154,10 +164,12 @@ def _workspace(n, dev):
 
 def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True, f_min: int = -2,
                  f_max: int = 6, global_scale: int = GLOBAL_NONE, g: torch.Tensor | None = None,
-                 with_offsets: bool = True, out=None):
+                 with_offsets: bool = True, out=None, hadamard: bool = False, hadamard_signs=None):
     """Quantize a 2-D tensor (bf16/fp16/fp32, contiguous rows) to NVFP4 blocks.
 
-    Returns dict(codes, scales, offsets, g); layouts as documented in fp4.h."""
+    hadamard rotates each row first (incoherence processing; hadamard_signs:
+    up to four 32-bit words of sign bits).  Returns dict(codes, scales,
+    offsets, g); layouts as documented in fp4.h."""
     L = load()
     _dev(x, "x")
     rows, cols = x.shape
@@ -174,7 +186,8 @@ def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True
         offs = torch.empty(sshape, dtype=torch.int8, device=dev) if with_offsets else None
     if g is None and global_scale != GLOBAL_NONE:
         g = torch.empty(1, dtype=torch.float32, device=dev)
-    o = QuantOpts(C.sizeof(QuantOpts), int(bool(scale_search)), f_min, f_max, global_scale, block_axis)
+    o = QuantOpts(C.sizeof(QuantOpts), int(bool(scale_search)), f_min, f_max, global_scale, block_axis,
+                  int(bool(hadamard)), _sign_words(hadamard_signs))
     nws = L.fp4_quantize_workspace_size(rows, cols, C.byref(o))
     ws = _workspace(nws, dev)
     st = L.fp4_quantize(_ptr(x), _DT[x.dtype], rows, cols, cols, C.byref(o), _ptr(codes), _ptr(scales),
@@ -194,9 +207,11 @@ def _problem(q, k, v, quant=None):
     return P
 
 
-def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype, given=False):
+def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype, given=False,
+          hadamard=False, hadamard_signs=None):
     return AttnOpts(C.sizeof(AttnOpts), int(bool(causal)), float(softmax_scale), kv_tile,
-                    int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype, int(bool(given)))
+                    int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype, int(bool(given)),
+                    int(bool(hadamard)), _sign_words(hadamard_signs))
 
 
 def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile=128):
@@ -221,8 +236,12 @@ def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile
 
 def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
                       f_max=6, fp16_budget_pct=0, sel_block=128, out_dtype=BF16, quantized=None,
-                      return_lse=True, return_topk=False, workspace=None, out=None, selection=None):
+                      return_lse=True, return_topk=False, workspace=None, out=None, selection=None,
+                      hadamard=False, hadamard_signs=None):
     """FP4 attention forward.  q [B,H,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp16).
+
+    hadamard: Q and K are quantized after the incoherence rotation (with
+    hadamard_signs); the scores are unchanged in exact arithmetic.
 
     quantized: optional dict with q_codes..v_scales from fp4_quantize (then q/k/v
     may be None when fp16_budget_pct == 0).  selection: optional (idx, cnt) from
@@ -238,7 +257,7 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
         B, H, Sq, d = quantized["q_shape"]
     P = _problem(q, k, v, quantized)
     O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype,
-              selection is not None)
+              selection is not None, hadamard, hadamard_signs)
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None

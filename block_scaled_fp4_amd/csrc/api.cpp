@@ -51,8 +51,18 @@ int check_quant_opts(const fp4_quant_opts* o) {
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad global_scale mode %d", o->global_scale);
   if (o->block_axis != 0 && o->block_axis != 1)
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: block_axis must be 0 or 1");
+  if (o->hadamard != 0 && o->hadamard != 1) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: hadamard must be 0 or 1");
+  if (o->hadamard && o->block_axis != 0)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: hadamard needs block_axis 0");
+  if (o->hadamard && o->global_scale == FP4_GLOBAL_AMAX)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: hadamard with FP4_GLOBAL_AMAX is not supported");
   return FP4_OK;
 }
+
+bool hadamard_size(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128; }
+
+// binary32 1/sqrt(n) for the incoherence rotation, rounded once from binary64
+float hadamard_scale(int64_t n) { return (float)(1.0 / std::sqrt((double)n)); }
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -131,6 +141,9 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
   const bool all_codes = p->q_codes && p->q_scales && p->k_codes && p->k_scales && p->v_codes && p->v_scales;
   if (any_codes && !all_codes) return fail(FP4_ERR_INVALID_ARG, "%s: give all six quantized arrays or none", fn);
   if (!all_codes && (!p->q || !p->k || !p->v)) return fail(FP4_ERR_INVALID_ARG, "%s: q, k, v are NULL", fn);
+  if (o->hadamard_qk != 0 && o->hadamard_qk != 1) return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk must be 0 or 1", fn);
+  if (o->hadamard_qk && all_codes)
+    return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk applies to the call's own quantization (no pre-quantized operands)", fn);
   const void* ptrs[] = {p->q, p->k, p->v, p->q_codes, p->q_scales, p->k_codes, p->k_scales, p->v_codes, p->v_scales};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
@@ -160,6 +173,8 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad shape/ld");
   if (opts->block_axis == 0 && cols % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: cols %% 16 != 0");
   if (opts->block_axis == 1 && rows % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: rows %% 16 != 0");
+  if (opts->hadamard && !hadamard_size(cols))
+    return fail(FP4_ERR_UNSUPPORTED, "fp4_quantize: hadamard needs cols in {16, 32, 64, 128}");
   if (rows > 0 && cols > 0 && (!x || !codes || !scales))
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: x, codes and scales must be non-NULL");
   if ((x && !aligned16(x)) || (codes && !aligned16(codes)) || (scales && !aligned16(scales)))
@@ -172,7 +187,7 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   const size_t need = fp4_quantize_workspace_size(rows, cols, opts);
   if (workspace_bytes < need || (need && !workspace))
     return fail(FP4_ERR_WORKSPACE, "fp4_quantize: workspace needs %zu bytes", need);
-  QuantLaunch L;
+  QuantLaunch L{};
   L.x = x;
   L.dtype = dtype;
   L.rows = rows;
@@ -188,6 +203,9 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   L.offsets = offsets;
   L.g = g;
   L.amax_ws = (float*)workspace;
+  L.hadamard = opts->hadamard;
+  for (int i = 0; i < 4; ++i) L.hsigns[i] = opts->hadamard_signs[i];
+  L.hscale = hadamard_scale(cols);
   return hip_status(fp4i_launch_quantize(L, (hipStream_t)stream), "fp4_quantize launch");
 }
 
@@ -264,6 +282,9 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
     L.ld = d;
     L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
     L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
+    L.hadamard = opts->hadamard_qk;  // Q and K only; V is never rotated
+    for (int i = 0; i < 4; ++i) L.hsigns[i] = opts->hadamard_signs[i];
+    L.hscale = hadamard_scale(d);
     hipError_t e = fp4i_launch_quantize(L, s);
     if (e == hipSuccess) {
       L.x = prob->k; L.rows = B * Hkv * Sk;
@@ -271,7 +292,7 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
       e = fp4i_launch_quantize(L, s);
     }
     if (e == hipSuccess) {
-      L.x = prob->v; L.axis = 1;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
+      L.x = prob->v; L.axis = 1; L.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
       L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
       e = fp4i_launch_quantize(L, s);
     }

@@ -14,6 +14,9 @@ struct QuantLaunch {
   int8_t* offsets;
   float* g;
   float* amax_ws;  // fp4i_amax_parts floats (mode 1)
+  int hadamard;            // rotate rows (axis 0) before quantizing
+  uint32_t hsigns[4];      // sign bits of the rotation
+  float hscale;            // binary32 1/sqrt(cols)
 };
 
 int fp4i_amax_parts(int64_t rows, int64_t cols);

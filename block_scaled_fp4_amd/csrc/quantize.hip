@@ -37,7 +37,41 @@ struct QuantArgs {
   const float* amax_part;  // partial maxima (mode 1)
   int n_part;
   int search, fmin, fmax, gmode;
+  uint32_t hsigns[4];  // incoherence processing: sign bits and 1/sqrt(cols)
+  float hscale;
 };
+
+// Incoherence processing of one row held by the bpr = cols/16 consecutive
+// lanes of its blocks (ScaleSearch page, Metodologia / ScaleSearchAttention):
+// signs, then the Hadamard butterflies of span 1, 2, 4, 8 inside the lane and
+// 16, 32, 64 across lanes (lane ^ 1, 2, 4), each pair (a, b) -> (a + b, a - b)
+// in binary32, then the 1/sqrt(cols) multiply.  All lanes of a row are active
+// together (rows are whole in the grid-stride loop).
+__device__ __forceinline__ void hadamard_block(float (&y)[16], const QuantArgs& A, int64_t cb, int bpr) {
+  const uint32_t sm = (A.hsigns[cb >> 1] >> ((cb & 1) * 16)) & 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((sm >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!(i & h)) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+  const int lane = threadIdx.x;
+  for (int hb = 1; hb < bpr; hb <<= 1) {
+    const bool upper = (lane & hb) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float o = __shfl_xor(y[i], hb, 64);
+      y[i] = upper ? o - y[i] : y[i] + o;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = y[i] * A.hscale;
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -113,7 +147,7 @@ __device__ __forceinline__ void raw_to_f32<float>(const RawBlock<float>& R, floa
 // consecutive blocks (2 KiB of bf16) and writes their 512 code bytes.  The
 // grid is a few workgroups per CU that stride over the blocks, each lane
 // loading its next block while it searches the current one.
-template <typename T>
+template <typename T, bool HAD>
 __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
   __shared__ float2_t tab[128];
   __shared__ float sh[8];
@@ -135,6 +169,7 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
     float y[16];
     raw_to_f32<T>(raw, y);
     if (blk + stride < nb) load_raw<T>(raw, src(blk + stride));
+    if (HAD) hadamard_block(y, A, blk % bpr, (int)bpr);
     if (A.gmode != 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = y[i] * ginv;
@@ -282,10 +317,16 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   int64_t grid = (work + 255) / 256;
   if (grid > 2048) grid = 2048;  // 8 workgroups per CU, striding over the blocks
   if (grid < 1) grid = 1;
-  if (L.axis == 0) {
-    if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis0_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
-    else if (L.dtype == 1) hipLaunchKernelGGL(quantize_axis0_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
-    else hipLaunchKernelGGL(quantize_axis0_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
+  for (int i = 0; i < 4; ++i) A.hsigns[i] = L.hsigns[i];
+  A.hscale = L.hscale;
+  if (L.axis == 0 && L.hadamard) {
+    if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis0_kernel<uint16_t, true>), dim3(grid), dim3(256), 0, stream, A);
+    else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis0_kernel<half_t, true>), dim3(grid), dim3(256), 0, stream, A);
+    else hipLaunchKernelGGL((quantize_axis0_kernel<float, true>), dim3(grid), dim3(256), 0, stream, A);
+  } else if (L.axis == 0) {
+    if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis0_kernel<uint16_t, false>), dim3(grid), dim3(256), 0, stream, A);
+    else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis0_kernel<half_t, false>), dim3(grid), dim3(256), 0, stream, A);
+    else hipLaunchKernelGGL((quantize_axis0_kernel<float, false>), dim3(grid), dim3(256), 0, stream, A);
   } else {
     if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis1_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
     else if (L.dtype == 1) hipLaunchKernelGGL(quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);

@@ -75,6 +75,16 @@ typedef struct fp4_quant_opts {
   int32_t f_max;
   int32_t global_scale; /* FP4_GLOBAL_* */
   int32_t block_axis;   /* 0: blocks of 16 consecutive columns; 1: of 16 consecutive rows */
+  /* Incoherence processing (ScaleSearch page, Metodologia / ScaleSearchAttention:
+     Hadamard transforms before quantization, following QuIP#).  1: every row
+     is first replaced by H_n (s o row) / sqrt(n), n = cols, s_j = -1 where bit
+     j of hadamard_signs is set (bit j % 32 of word j / 32), H_n the Sylvester
+     Hadamard matrix applied by binary32 butterfly stages of span 1, 2, 4, ...
+     (pair (i, i+h) -> (a + b, a - b)), then a multiply by the binary32 value
+     of 1/sqrt(n).  Needs block_axis 0, cols in {16, 32, 64, 128} and a global
+     scale mode other than FP4_GLOBAL_AMAX.  0: off. */
+  int32_t hadamard;
+  uint32_t hadamard_signs[4];
 } fp4_quant_opts;
 
 /*
@@ -151,6 +161,11 @@ typedef struct fp4_attn_opts {
   int32_t out_dtype;       /* FP4_BF16, FP4_FP16 or FP4_FP32 */
   int32_t selection_given; /* 1: topk_idx/topk_cnt are inputs (e.g. from fp4_block_topk) and
                               no selection is computed; 0: the call computes the selection */
+  int32_t hadamard_qk;     /* 1: the call quantizes Q and K after the rotation of fp4_quant_opts'
+                              hadamard (n = d) with these signs; QK^T is kept, the FP16 path
+                              and the block means use the original Q and K.  Needs the call
+                              to quantize (no pre-quantized operands). */
+  uint32_t hadamard_signs[4];
 } fp4_attn_opts;
 
 /*

@@ -161,3 +161,26 @@ def test_selective_decode_and_block_sums_reject_bad_arguments(L):
     cs.d = 128
     cs.v_mid = None
     assert L.fp4_kv_cache_append(C.byref(cs), f, f, 16, None, f, 1 << 30, None) == -1  # all three or none
+
+
+def test_hadamard_options_are_validated(L):
+    import block_scaled_fp4_amd as fp4
+    fake = C.c_void_p(1 << 20)
+
+    def q(cols, axis=0, gmode=0, had=1, rows=32):
+        o = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, gmode, axis, had)
+        return L.fp4_quantize(fake, 0, rows, cols, cols, C.byref(o), fake, fake, None, fake, fake, 1 << 20, None)
+
+    assert q(128, axis=1) == -1          # rows of blocks only
+    assert q(48) == -2                   # not a power of two
+    assert q(256) == -2                  # wider than one 8-lane row group
+    assert q(128, gmode=1) == -1         # amax of the rotated tensor is not formed
+    assert q(128, had=2) == -1
+    f = C.c_void_p(1 << 20)
+
+    def call(P, O):
+        return L.fp4_attention_fwd(C.byref(P), C.byref(O), f, None, None, None, f, 1 << 40, None)
+
+    quant = dict(q_codes=f, q_scales=f, k_codes=f, k_scales=f, v_codes=f, v_scales=f)
+    assert call(_prob(fp4, **quant), _opts(fp4, hadamard_qk=1)) == -1
+    assert call(_prob(fp4), _opts(fp4, hadamard_qk=3)) == -1
