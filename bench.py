@@ -205,6 +205,14 @@ def bench_quantizer(fp4, synth, torch, n):
     bo = dict(codes=bc, scales=bs, offsets=None)
     big_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_AMAX, g=g, out=bo), max(3, n // 4))
     big_algo = algo * 64 - 4 * 63
+    # the same with incoherence processing (rotation fused into the quantizer; a given
+    # per-tensor scale, since the amax of the rotated tensor is not formed)
+    g.fill_(0.01)
+    had_signs = [0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0xD1B54A32]
+    big_had_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_GIVEN, g=g, out=bo, hadamard=True,
+                                                    hadamard_signs=had_signs), max(3, n // 4))
+    big_given_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_GIVEN, g=g, out=bo),
+                             max(3, n // 4))
     alu_tops = rows * 64 * cols * QUANT_LANE_OPS_PER_ELEM / big_ms / 1e9
     cold_gbps = algo / cold / 1e6
     return dict(workload="bf16 [32768,128], 2% outlier channels x20, ScaleSearch f in [-2,6], per-tensor amax scale",
@@ -219,7 +227,9 @@ def bench_quantizer(fp4, synth, torch, n):
                 hot_us=round(hot * 1e3, 2), hot_GBps=round(algo / hot / 1e6, 1),
                 max_scaling_only_cold_GBps=round(algo / coldm / 1e6, 1),
                 rows_x64_ms=round(big_ms, 4), rows_x64_GBps=round(big_algo / big_ms / 1e6, 1),
-                rows_x64_frac_hbm=round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4))
+                rows_x64_frac_hbm=round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4),
+                rows_x64_given_scale_ms=round(big_given_ms, 4),
+                rows_x64_hadamard_given_scale_ms=round(big_had_ms, 4))
 
 
 def bench_decode(fp4, synth, torch, n, selective=True):
