@@ -449,7 +449,7 @@ static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss,
 static void attn_row(const double* qh, const double* q16, const double* Kh, const double* Vh,
                      const double* K16, const double* V16, int64_t Sk, int d, int64_t i,
                      int causal, float c, int kv_tile, const int32_t* sel, int nsel, int sel_block,
-                     float* out, float* lse) {
+                     int single_level, float* out, float* lse) {
   int64_t ntiles = (Sk + kv_tile - 1) / kv_tile;
   double* Oacc = (double*)calloc((size_t)d, sizeof(double));
   double* Ot = (double*)malloc(sizeof(double) * (size_t)d);
@@ -496,14 +496,19 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
         float amax = 0.0f;
         for (int j = b0; j < b1; ++j)
           if (e[j] > amax) amax = e[j];
-        float a448 = amax * 448.0f;
-        int s2 = orc_e4m3_encode((double)a448);
+        /* two-level: the row level maps e = 1 to 2688, so the block scale is
+           E4M3(amax * 2688 / 6) = E4M3(amax * 448) and the element factor
+           fl32(2688 / s2); single level (Attn-QAT page, Metodologia / B: no
+           two-level step): the block scale is E4M3(fl32(amax / 6)) and the
+           element factor the correctly rounded reciprocal R(s2), as in the
+           quantizer */
+        int s2 = single_level ? orc_e4m3_encode((double)(amax / 6.0f)) : orc_e4m3_encode((double)(amax * 448.0f));
         if (s2 == 0) {
           for (int j = b0; j < b1; ++j) P[j] = 0.0;
           continue;
         }
         float s2f = (float)orc_e4m3_value(s2);
-        float M = 2688.0f / s2f;
+        float M = single_level ? orc_recip(s2) : 2688.0f / s2f;
         for (int j = b0; j < b1; ++j) {
           float t = e[j] * M;
           int code = orc_e2m1_encode((double)t);
@@ -516,7 +521,7 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
     for (int j = 0; j < n; ++j)
       if (P[j] != 0.0)
         for (int dd = 0; dd < d; ++dd) O[dd] += P[j] * VV[(t0 + j) * d + dd];
-    if (!promoted)
+    if (!promoted && !single_level)
       for (int dd = 0; dd < d; ++dd) O[dd] /= 2688.0;
     Os[T] = O;
     tms[T] = tm;
@@ -546,14 +551,15 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
    rows (n_rows of them, NULL = all) picks the query rows; heads (n_heads, NULL
    = all) picks flattened b*H+h heads.  out is [n_heads][n_rows][d], lse
    [n_heads][n_rows] (nullable); topk_idx [n_heads][nqb][kmax] and topk_cnt
-   [n_heads][nqb] (nullable) receive the selection. Returns 0, or -1 on bad
-   arguments. */
+   [n_heads][nqb] (nullable) receive the selection.  single_level quantizes P
+   with the NVFP4 block scale alone (no row level; the Attn-QAT page removes
+   the two-level step).  Returns 0, or -1 on bad arguments. */
 int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int H, int Hkv,
                       int64_t Sq, int64_t Sk, int d, int causal, double softmax_scale, int kv_tile,
                       int scale_search, int fmin, int fmax, int pct, int sel_block,
                       const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
                       float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt,
-                      const float* q_fp4, const float* k_fp4) {
+                      const float* q_fp4, const float* k_fp4, int single_level) {
   /* q_fp4, k_fp4 (nullable, same layout as q, k): what the FP4 path
      quantizes, e.g. Q and K after incoherence processing; the FP16 path and
      the block means always use q and k. */
@@ -615,7 +621,7 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
         sel = sidx + (int64_t)qbk * kmax;
         nsel = scnt[qbk];
       }
-      attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block,
+      attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block, single_level,
                out + ((int64_t)hi * nr + ri) * d, lse ? lse + (int64_t)hi * nr + ri : NULL);
       free(qh); free(q16);
     }

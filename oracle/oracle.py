@@ -79,7 +79,7 @@ def lib():
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
-                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp]
+                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int]
     L.orc_attention_fwd.restype = C.c_int
     L.orc_hadamard_rows.argtypes = [_f32p, C.c_int64, C.c_int, _vp]
     L.orc_hadamard_rows.restype = None
@@ -238,12 +238,13 @@ def _sel(arr, dtype):
 
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
-                  with_topk=False, hadamard=False, signs=None):
+                  with_topk=False, hadamard=False, signs=None, single_level_p=False):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
 
     hadamard: the FP4 path quantizes Q and K after incoherence processing
     (hadamard_rows with the given signs); the FP16 path and the block means
-    use the original Q and K.
+    use the original Q and K.  single_level_p quantizes P with the block
+    scale alone, E4M3(amax(e)/6) per 16 keys, without the row level.
 
     Returns (out [nh, nr, d], lse [nh, nr]) and, with with_topk, also
     (topk_idx [nh, nqb, kmax], topk_cnt [nh, nqb])."""
@@ -269,7 +270,7 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
                                  int(causal), float(softmax_scale), kv_tile, int(scale_search),
                                  fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
                                  _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
-                                 _ptr(tcnt), _ptr(qr), _ptr(kr))
+                                 _ptr(tcnt), _ptr(qr), _ptr(kr), int(bool(single_level_p)))
     if rc != 0:
         raise ValueError("bad attention arguments")
     res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))

@@ -157,3 +157,49 @@ def test_row_and_head_selection_consistent():
     np.testing.assert_array_equal(part[0], full[3][[79, 3, 40]])
     np.testing.assert_array_equal(part[1], full[0][[79, 3, 40]])
     np.testing.assert_array_equal(lp[1], lf[0][[79, 3, 40]])
+
+
+# ---- single-level P (Attn-QAT page, Metodologia / B: FP4 attention without the
+# two-level step): P takes only the NVFP4 block scale E4M3(amax(e)/6)
+
+def test_single_level_p_zero_keys_closed_form():
+    """K = 0: every e = 1, so each block's scale is E4M3(1/6) = 0x23 =
+    0.171875 and t = 1 * R(0x23) = 5.818 rounds to code 6: every weight is
+    6 * 0.171875 = 1.03125 against a denominator of n, so O is 1.03125 times
+    the mean of the dequantized V rows (the two-level P gives exactly the
+    mean: its row level maps e = 1 to 2688 = 6 * 448)."""
+    q = _rand((1, 1, 64, 64), 10)
+    k = torch.zeros(1, 1, 192, 64, dtype=torch.bfloat16)
+    v = _rand((1, 1, 192, 64), 11)
+    vh = _deq(v[0, 0].float().numpy(), 1)
+    out, lse = oracle.attention_fwd(q, k, v, kv_tile=64, single_level_p=True)
+    np.testing.assert_allclose(out[0], np.broadcast_to(1.03125 * vh.mean(0), (64, 64)), rtol=0, atol=2e-6)
+    np.testing.assert_allclose(lse[0], math.log(192), atol=1e-5)  # the denominator sums the unquantized e
+
+
+def test_single_level_p_worked_example():
+    """Scores built so that e is a power of two (softmax scale ln 2 makes the
+    score factor exactly 1; q = 4 e_0 and k_j = -a_j e_0 quantize exactly under
+    ScaleSearch).  One 16-key block with e = 1, 1/2, 1/4, 1/16, 1/256 and
+    eleven keys at e = 1/256: s2 = E4M3(1/6) = 0.171875, R(s2) = fl32(1/s2)
+    = 5.8181815, so t = 5.818, 2.909, 1.4545, 0.3636, 0.0227 -> E2M1 6, 3,
+    1.5, 0.5, 0 -> P^ = 1.03125, 0.515625, 0.2578125, 0.0859375, 0."""
+    d = 16
+    x = [0, -1, -2, -4] + [-8] * 12             # tile-row maximum 0
+    q = torch.zeros(1, 1, 1, d)
+    q[0, 0, 0, 0] = 4.0
+    k = torch.zeros(1, 1, 16, d)
+    for j, xj in enumerate(x):
+        k[0, 0, j, 0] = xj / 4.0
+    v = _rand((1, 1, 16, d), 12)  # any values: the check goes through the dequantized V
+    vh = _deq(v[0, 0].float().numpy(), 1)
+    out, lse = oracle.attention_fwd(q.to(torch.bfloat16), k.to(torch.bfloat16), v, kv_tile=64,
+                                    softmax_scale=float(np.float32(math.log(2.0))), single_level_p=True)
+    e = np.array([2.0 ** xj for xj in x])
+    p_hat = np.array([1.03125, 0.515625, 0.2578125, 0.0859375] + [0.0] * 12)
+    want = (p_hat[:, None] * vh).sum(0) / e.sum()
+    np.testing.assert_allclose(out[0, 0], want, rtol=0, atol=1e-6)
+    # the two-level P of the same scores keeps e = 1/2 and 1/4 exactly (s2 = 448)
+    two, _ = oracle.attention_fwd(q.to(torch.bfloat16), k.to(torch.bfloat16), v, kv_tile=64,
+                                  softmax_scale=float(np.float32(math.log(2.0))))
+    assert np.abs(two[0, 0] - want).max() > 1e-3
