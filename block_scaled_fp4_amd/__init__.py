@@ -53,7 +53,7 @@ class AttnOpts(C.Structure):
                 ("kv_tile", C.c_int32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
                 ("f_max", C.c_int32), ("fp16_budget_pct", C.c_int32), ("sel_block", C.c_int32),
                 ("out_dtype", C.c_int32), ("selection_given", C.c_int32), ("hadamard_qk", C.c_int32),
-                ("hadamard_signs", C.c_uint32 * 4)]
+                ("hadamard_signs", C.c_uint32 * 4), ("p_single_level", C.c_int32)]
 
 
 def _sign_words(signs):
@@ -208,10 +208,10 @@ def _problem(q, k, v, quant=None):
 
 
 def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype, given=False,
-          hadamard=False, hadamard_signs=None):
+          hadamard=False, hadamard_signs=None, single_level_p=False):
     return AttnOpts(C.sizeof(AttnOpts), int(bool(causal)), float(softmax_scale), kv_tile,
                     int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype, int(bool(given)),
-                    int(bool(hadamard)), _sign_words(hadamard_signs))
+                    int(bool(hadamard)), _sign_words(hadamard_signs), int(bool(single_level_p)))
 
 
 def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile=128):
@@ -237,8 +237,11 @@ def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile
 def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
                       f_max=6, fp16_budget_pct=0, sel_block=128, out_dtype=BF16, quantized=None,
                       return_lse=True, return_topk=False, workspace=None, out=None, selection=None,
-                      hadamard=False, hadamard_signs=None):
+                      hadamard=False, hadamard_signs=None, single_level_p=False):
     """FP4 attention forward.  q [B,H,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp16).
+
+    single_level_p: P is quantized with the NVFP4 block scale alone (no row
+    level).
 
     hadamard: Q and K are quantized after the incoherence rotation (with
     hadamard_signs); the scores are unchanged in exact arithmetic.
@@ -257,7 +260,7 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
         B, H, Sq, d = quantized["q_shape"]
     P = _problem(q, k, v, quantized)
     O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype,
-              selection is not None, hadamard, hadamard_signs)
+              selection is not None, hadamard, hadamard_signs, single_level_p)
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None

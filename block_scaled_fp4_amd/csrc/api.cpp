@@ -142,6 +142,8 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
   if (any_codes && !all_codes) return fail(FP4_ERR_INVALID_ARG, "%s: give all six quantized arrays or none", fn);
   if (!all_codes && (!p->q || !p->k || !p->v)) return fail(FP4_ERR_INVALID_ARG, "%s: q, k, v are NULL", fn);
   if (o->hadamard_qk != 0 && o->hadamard_qk != 1) return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk must be 0 or 1", fn);
+  if (o->p_single_level != 0 && o->p_single_level != 1)
+    return fail(FP4_ERR_INVALID_ARG, "%s: p_single_level must be 0 or 1", fn);
   if (o->hadamard_qk && all_codes)
     return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk applies to the call's own quantization (no pre-quantized operands)", fn);
   const void* ptrs[] = {p->q, p->k, p->v, p->q_codes, p->q_scales, p->k_codes, p->k_scales, p->v_codes, p->v_scales};
@@ -323,6 +325,7 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   A.c = score_factor(opts->softmax_scale, d);
   A.kv_tile = opts->kv_tile;
   A.pct = opts->fp16_budget_pct;
+  A.single_p = opts->p_single_level;
   A.sel_block = opts->sel_block;
   A.nqb = P.nqb;
   A.kmax = P.kmax;

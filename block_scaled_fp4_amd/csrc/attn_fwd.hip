@@ -11,6 +11,9 @@
 //                (P^ V^) / 2688 with weight 2^(tm - m)
 //     FP16 tile: adds fp16(e) fp16(V) (scores from fp16 q and k)
 //     l sums the unquantized e; out = O / l.
+//   Single-level P (Attn-QAT page, Metodologia / B, option): the FP4 tile's
+//   blocks take s2 = E4M3(amax(e) / 6) and codes RNE_E2M1(e / s2) directly,
+//   and the tile adds P^ V^ (no row level).
 //
 // MI355X mapping.  gfx950's block-scaled FP4 MFMA takes power-of-two scales
 // per 32 elements, while NVFP4 scales are E4M3 per 16, so the operands are
@@ -79,6 +82,28 @@ struct PScaleTable {
   }
 };
 __constant__ PScaleTable kPScale = PScaleTable();
+
+// Single-level P (Attn-QAT page, Metodologia / B: no two-level step): the
+// block scale is s2 = E4M3(max e / 6) itself, so lg = log2(1 / s2), inv = s2
+// and s = s2; the tile adds P^ V^ with P^ in units of e.
+struct PScaleTable1 {
+  float4_t v[128];  // {lg, inv, s, 0}
+  constexpr PScaleTable1() : v() {
+    for (int b = 0; b < 128; ++b) {
+      double s2 = 0.0;
+      if (b < 8) s2 = (double)b / 512.0;
+      else {
+        int e = (b >> 3) - 7, mm = b & 7;
+        s2 = 1.0 + (double)mm / 8.0;
+        for (int i = 0; i < e; ++i) s2 *= 2.0;
+        for (int i = 0; i > e; --i) s2 /= 2.0;
+      }
+      if (b == 0 || b == 127) v[b] = float4_t{0.0f, 1.0f, 0.0f, 0.0f};
+      else v[b] = float4_t{(float)(ct_ln(1.0 / s2) / 0.69314718055994530942), (float)s2, (float)s2, 0.0f};
+    }
+  }
+};
+__constant__ PScaleTable1 kPScale1 = PScaleTable1();
 
 constexpr int kWaves = 4;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
@@ -198,6 +223,7 @@ struct Problem {
   const void *q, *k, *v;
   const int32_t *idx, *cnt;
   int causal, pct, sel_block, nqb, kmax, nqt;
+  int single_p;  // 1: single-level P
   float c;
   void* out;
   float* lse;
@@ -324,8 +350,9 @@ __device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t v
 // U * 2^m.  m is a lazily raised running maximum: it moves only when a tile's
 // maximum exceeds it by more than kRaise, so a tile's weight r = 2^(tm - m)
 // stays <= 2^kRaise.  FP4 tiles fold r into the fp16 block scale of P^
-// (P^ r = code * fp16(s2 * r)) and add P^ V^ with P^ in units of e/2688; the
-// switch to FP16 tiles rescales U by 1/2688 once.  FP16 tiles take
+// (P^ r = code * fp16(s2 * r)) and add P^ V^ with P^ in units of e/2688 (of
+// e with single-level P); the switch to FP16 tiles rescales U to units of e
+// once.  FP16 tiles take
 // p = 2^(x - m) = e r directly.  Either way the PV MFMA accumulates straight
 // into U.
 template <int D>
@@ -359,7 +386,7 @@ __device__ __forceinline__ float max16(const float16_t& a) {
 // each exponent is one fused x*c - offset.  Each lane holds 16 consecutive
 // keys of one query row per 32-key subtile, i.e. exactly one level-2 block of
 // P, so the block scale is lane-local.
-template <int D, int BC, bool FP4, bool MASK>
+template <int D, int BC, bool FP4, bool MASK, bool SINGLE>
 __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
                                           int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
   const int lane = threadIdx.x & 63;
@@ -445,10 +472,12 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   auto lookup = [&](int g) {
     PRaw r{0.0f, 1.0f, 0.0f};
     if (FP4) {
-      // level 2: s2 = E4M3(448 * max e) from the block maximum
+      // level 2: s2 = E4M3(448 * max e) from the block maximum (single
+      // level: s2 = E4M3(max e / 6))
       const float toff = use ? -tm : ninf;
       const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[g], c, toff));
-      const float4_t ps = S.pt[f32_to_e4m3(emax * 448.0f)];
+      const uint32_t byte = f32_to_e4m3(SINGLE ? div6_rn(emax) : emax * 448.0f);
+      const float4_t ps = S.pt[byte];
       r.lg = ps[0];
       r.inv = ps[1];
       r.s = ps[2];
@@ -541,7 +570,7 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
 
-template <int D, int BC, typename IT, typename OT>
+template <int D, int BC, typename IT, typename OT, bool SINGLE>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   __shared__ Smem<D, BC> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
@@ -566,7 +595,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   const int64_t qrow = q0 + 32 * wave + (lane & 31);
   const int64_t Sk = P.Sk;
 
-  if (threadIdx.x < 128) S.pt[threadIdx.x] = kPScale.v[threadIdx.x];
+  if (threadIdx.x < 128) S.pt[threadIdx.x] = SINGLE ? kPScale1.v[threadIdx.x] : kPScale.v[threadIdx.x];
   // Q^ fragment (B operand): query qrow, d = 16 s + 8 hi .. +8
   half8_t qf[D / 16];
   {
@@ -634,17 +663,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     const bool wave_dead = P.causal && key0 > wrow0 + 31;  // every key of the tile is after this wave's rows
     if (!wave_dead) {
       const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
-      if (need_mask) wave_tile<D, BC, true, true>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-      else wave_tile<D, BC, true, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      if (need_mask) wave_tile<D, BC, true, true, SINGLE>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      else wave_tile<D, BC, true, false, SINGLE>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
     }
     cur = nxt;
   }
 
-  // FP4 tiles accumulated P^ V^ with P^ in units of e/2688
+  // FP4 tiles accumulated P^ V^ with P^ in units of e/2688 (two-level) or of e
+  const float to_e = SINGLE ? 1.0f : 1.0f / 2688.0f;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) R.o[t][i] = R.o[t][i] * (1.0f / 2688.0f);
+    for (int i = 0; i < 16; ++i) R.o[t][i] = R.o[t][i] * to_e;
 
   // ---- FP16 pass over the selected blocks
   if (nsel > 0) {
@@ -672,8 +702,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
         const bool wave_dead = P.causal && key0 > wrow0 + 31;
         if (!wave_dead) {
           const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
-          if (need_mask) wave_tile<D, BC, false, true>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-          else wave_tile<D, BC, false, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+          if (need_mask) wave_tile<D, BC, false, true, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+          else wave_tile<D, BC, false, false, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
         }
       }
     }
@@ -697,18 +727,23 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   }
 }
 
-template <int D, int BC, typename IT>
+template <int D, int BC, typename IT, bool SINGLE>
 hipError_t launch_out(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
-  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float>), grid, dim3(256), 0, st, P);
-  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t>), grid, dim3(256), 0, st, P);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t>), grid, dim3(256), 0, st, P);
+  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float, SINGLE>), grid, dim3(256), 0, st, P);
+  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t, SINGLE>), grid, dim3(256), 0, st, P);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t, SINGLE>), grid, dim3(256), 0, st, P);
   return hipGetLastError();
 }
 
 template <int D, int BC>
 hipError_t launch_in(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
-  if (L.dtype == 1) return launch_out<D, BC, half_t>(L, P, grid, st);
-  return launch_out<D, BC, uint16_t>(L, P, grid, st);
+  // single-level P: bf16 or fp16 in, every output type
+  if (L.single_p) {
+    if (L.dtype == 1) return launch_out<D, BC, half_t, true>(L, P, grid, st);
+    return launch_out<D, BC, uint16_t, true>(L, P, grid, st);
+  }
+  if (L.dtype == 1) return launch_out<D, BC, half_t, false>(L, P, grid, st);
+  return launch_out<D, BC, uint16_t, false>(L, P, grid, st);
 }
 
 }  // namespace fp4dev
@@ -722,6 +757,7 @@ hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t st) {
   P.q = L.q; P.k = L.k; P.v = L.v;
   P.idx = L.idx; P.cnt = L.cnt;
   P.causal = L.causal; P.pct = L.pct; P.sel_block = L.pct > 0 ? L.sel_block : 128;
+  P.single_p = L.single_p;
   P.nqb = L.nqb; P.kmax = L.kmax;
   P.c = L.c;
   P.out = L.out; P.lse = L.lse;

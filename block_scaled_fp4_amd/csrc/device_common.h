@@ -67,6 +67,17 @@ __device__ __forceinline__ uint32_t e4m3_of_div6(float a) {
   return b;
 }
 
+// Correctly rounded binary32 a / 6 for normal a (three operations: a product
+// with the rounded reciprocal, the exact remainder by a fused multiply-add, one
+// fused correction).  Checked against IEEE division for every binary32 in
+// 22 binades on the host (the check is in the CPU test suite).
+__device__ __forceinline__ float div6_rn(float a) {
+  const float r = 1.0f / 6.0f;
+  const float q1 = a * r;
+  const float rem = __builtin_fmaf(-q1, 6.0f, a);
+  return __builtin_fmaf(rem, r, q1);
+}
+
 // Two binary32 values t0, t1 >= 0 -> byte (code(t1) << 4) | code(t0) written
 // into byte `sel` of `old`; codes are nearest E2M1 (ties to even), saturating.
 template <int SEL>

@@ -53,6 +53,7 @@ struct AttnLaunch {
   float c;  // log2(e) * softmax_scale, rounded once to binary32
   int kv_tile;
   int pct, sel_block, nqb, kmax;
+  int single_p;        // 1: single-level P
   const int32_t* idx;  // selection (pct > 0)
   const int32_t* cnt;
   int out_dtype;

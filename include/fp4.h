@@ -166,6 +166,10 @@ typedef struct fp4_attn_opts {
                               and the block means use the original Q and K.  Needs the call
                               to quantize (no pre-quantized operands). */
   uint32_t hadamard_signs[4];
+  int32_t p_single_level;  /* 1: the FP4 path quantizes P with the NVFP4 block scale alone,
+                              s2 = E4M3(amax(e) / 6) per 16 keys and codes RNE_E2M1(e / s2)
+                              (Attn-QAT page, Metodologia / B: no two-level step); 0: the
+                              two-level P above */
 } fp4_attn_opts;
 
 /*

@@ -149,3 +149,20 @@ def test_deterministic(gpu):
     b, _ = gpu.fp4_attention_fwd(qc, kc, vc, causal=True, fp16_budget_pct=10, out_dtype=gpu.FP32)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,kv_tile,causal,pct", [(64, 64, False, 0), (128, 128, True, 0), (128, 128, True, 25),
+                                                  (128, 64, False, 0)])
+def test_single_level_p(gpu, d, kv_tile, causal, pct):
+    """Single-level P (Attn-QAT page, Metodologia / B: no two-level step)
+    against the oracle's single-level numerics."""
+    q, k, v = synth.qkv(1, 2, 320, d, torch.bfloat16, seed=60 + d, k_outliers=4)
+    case(f"single-level P d={d} kv_tile={kv_tile} causal={causal} pct={pct}")
+    out, lse = gpu.fp4_attention_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, kv_tile=kv_tile,
+                                     fp16_budget_pct=pct, out_dtype=gpu.FP32, single_level_p=True)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=kv_tile, pct=pct, single_level_p=True)
+    assert_close_attn(out.cpu().numpy().reshape(-1, d), ref.reshape(-1, d), "single-level P")
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(-1), rlse.reshape(-1), atol=1e-3)
+    two, _ = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=kv_tile, pct=pct)
+    assert np.abs(two - ref).max() > 1e-3  # the two schemes differ: the test tells them apart
