@@ -449,8 +449,14 @@ static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss,
 static void attn_row(const double* qh, const double* q16, const double* Kh, const double* Vh,
                      const double* K16, const double* V16, int64_t Sk, int d, int64_t i,
                      int causal, float c, int kv_tile, const int32_t* sel, int nsel, int sel_block,
-                     int single_level, float* out, float* lse) {
+                     int single_level, float* out, float* lse, double* Prow, double* Phrow) {
+  /* Prow, Phrow (nullable, Sk entries): the row's normalized probabilities,
+     e * 2^(tm - m) / l, and the normalized weights the output uses, the same
+     with P^ in place of e (divided by 2688 on two-level FP4 tiles); zero on
+     masked keys.  Used by the training oracle. */
   int64_t ntiles = (Sk + kv_tile - 1) / kv_tile;
+  float* erow = Prow ? (float*)calloc((size_t)Sk, sizeof(float)) : NULL;
+  double* qrow = Prow ? (double*)calloc((size_t)Sk, sizeof(double)) : NULL;
   double* Oacc = (double*)calloc((size_t)d, sizeof(double));
   double* Ot = (double*)malloc(sizeof(double) * (size_t)d);
   float* x = (float*)malloc(sizeof(float) * (size_t)kv_tile);
@@ -523,6 +529,11 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
         for (int dd = 0; dd < d; ++dd) O[dd] += P[j] * VV[(t0 + j) * d + dd];
     if (!promoted && !single_level)
       for (int dd = 0; dd < d; ++dd) O[dd] /= 2688.0;
+    if (erow)
+      for (int j = 0; j < n; ++j) {
+        erow[t0 + j] = e[j];
+        qrow[t0 + j] = (!promoted && !single_level) ? P[j] / 2688.0 : P[j];
+      }
     Os[T] = O;
     tms[T] = tm;
     ls[T] = lsum;
@@ -539,6 +550,19 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
   }
   for (int dd = 0; dd < d; ++dd) out[dd] = nt ? (float)(Oacc[dd] / l) : 0.0f;
   if (lse) *lse = nt ? (float)(((double)m + log2(l)) * 0.69314718055994530942) : -INFINITY;
+  if (Prow) {
+    for (int64_t j = 0; j < Sk; ++j) { Prow[j] = 0.0; Phrow[j] = 0.0; }
+    for (T = 0; T < nt; ++T) {
+      double r = exp2((double)tms[T] - (double)m);
+      int64_t t0 = T * kv_tile, t1 = t0 + kv_tile < Sk ? t0 + kv_tile : Sk;
+      if (t1 > last + 1) t1 = last + 1;
+      for (int64_t j = t0; j < t1; ++j) {
+        Prow[j] = (double)erow[j] * r / l;
+        Phrow[j] = qrow[j] * r / l;
+      }
+    }
+    free(erow); free(qrow);
+  }
   (void)isfp4;
   free(isfp4); free(Os); free(ls); free(tms); free(P); free(e); free(x); free(Ot); free(Oacc);
 }
@@ -553,13 +577,17 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
    [n_heads][n_rows] (nullable); topk_idx [n_heads][nqb][kmax] and topk_cnt
    [n_heads][nqb] (nullable) receive the selection.  single_level quantizes P
    with the NVFP4 block scale alone (no row level; the Attn-QAT page removes
-   the two-level step).  Returns 0, or -1 on bad arguments. */
+   the two-level step).  probs and probs_hat (nullable, both or neither,
+   [n_heads][n_rows][Sk]) receive every row's normalized probabilities and the
+   normalized weights the output uses (see attn_row).  Returns 0, or -1 on bad
+   arguments. */
 int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int H, int Hkv,
                       int64_t Sq, int64_t Sk, int d, int causal, double softmax_scale, int kv_tile,
                       int scale_search, int fmin, int fmax, int pct, int sel_block,
                       const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
                       float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt,
-                      const float* q_fp4, const float* k_fp4, int single_level) {
+                      const float* q_fp4, const float* k_fp4, int single_level,
+                      double* probs, double* probs_hat) {
   /* q_fp4, k_fp4 (nullable, same layout as q, k): what the FP4 path
      quantizes, e.g. Q and K after incoherence processing; the FP16 path and
      the block means always use q and k. */
@@ -622,7 +650,9 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
         nsel = scnt[qbk];
       }
       attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block, single_level,
-               out + ((int64_t)hi * nr + ri) * d, lse ? lse + (int64_t)hi * nr + ri : NULL);
+               out + ((int64_t)hi * nr + ri) * d, lse ? lse + (int64_t)hi * nr + ri : NULL,
+               probs ? probs + ((int64_t)hi * nr + ri) * Sk : NULL,
+               probs ? probs_hat + ((int64_t)hi * nr + ri) * Sk : NULL);
       free(qh); free(q16);
     }
     free(Kh); free(Vh); free(K16); free(V16); free(sidx); free(scnt);

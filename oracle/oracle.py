@@ -7,6 +7,7 @@ touches a GPU or the GPU library.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 import subprocess
 
@@ -21,7 +22,7 @@ __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
-    "score_factor", "kv_append", "block_sums", "hadamard_rows",
+    "score_factor", "kv_append", "block_sums", "hadamard_rows", "attention_train",
 ]
 
 
@@ -79,7 +80,7 @@ def lib():
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
-                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int]
+                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _vp]
     L.orc_attention_fwd.restype = C.c_int
     L.orc_hadamard_rows.argtypes = [_f32p, C.c_int64, C.c_int, _vp]
     L.orc_hadamard_rows.restype = None
@@ -238,13 +239,16 @@ def _sel(arr, dtype):
 
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
-                  with_topk=False, hadamard=False, signs=None, single_level_p=False):
+                  with_topk=False, hadamard=False, signs=None, single_level_p=False, with_probs=False):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
 
     hadamard: the FP4 path quantizes Q and K after incoherence processing
     (hadamard_rows with the given signs); the FP16 path and the block means
     use the original Q and K.  single_level_p quantizes P with the block
     scale alone, E4M3(amax(e)/6) per 16 keys, without the row level.
+    with_probs also returns every row's normalized probabilities P and the
+    normalized weights P^ the output uses (float64 [nh, nr, Sk] each), after
+    the other results.
 
     Returns (out [nh, nr, d], lse [nh, nr]) and, with with_topk, also
     (topk_idx [nh, nqb, kmax], topk_cnt [nh, nqb])."""
@@ -264,16 +268,21 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
     nqb = (Sq + sel_block - 1) // sel_block
     nkb = (Sk + sel_block - 1) // sel_block
     kmax = topk_count(pct, nkb) if pct > 0 else 0
+    probs = np.zeros(nh * nr * Sk, np.float64) if with_probs else None
+    probs_hat = np.zeros(nh * nr * Sk, np.float64) if with_probs else None
     tidx = np.zeros(max(nh * nqb * kmax, 1), np.int32) if with_topk and pct > 0 else None
     tcnt = np.zeros(max(nh * nqb, 1), np.int32) if with_topk and pct > 0 else None
     rc = lib().orc_attention_fwd(q.reshape(-1), k.reshape(-1), v.reshape(-1), B, H, Hkv, Sq, Sk, d,
                                  int(causal), float(softmax_scale), kv_tile, int(scale_search),
                                  fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
                                  _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
-                                 _ptr(tcnt), _ptr(qr), _ptr(kr), int(bool(single_level_p)))
+                                 _ptr(tcnt), _ptr(qr), _ptr(kr), int(bool(single_level_p)),
+                                 _ptr(probs), _ptr(probs_hat))
     if rc != 0:
         raise ValueError("bad attention arguments")
     res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))
+    if with_probs:
+        return res + (probs.reshape(nh, nr, Sk), probs_hat.reshape(nh, nr, Sk))
     if with_topk:
         if pct > 0:
             res += (tidx[: nh * nqb * kmax].reshape(nh, nqb, kmax), tcnt[: nh * nqb].reshape(nh, nqb))
@@ -414,3 +423,56 @@ def kv_append(k_recent, v_recent, k_codes, k_scales, v_codes, v_scales, mid_len,
     if dual:
         return kr, vr, kc, ks, vc, vs, ml, over, km, vm, ksum
     return kr, vr, kc, ks, vc, vs, ml, over
+
+
+def attention_train(q, k, v, dout, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
+                    fmin=-2, fmax=6, single_level_p=False):
+    """One training step of FP4 attention with quantization-aware training
+    (Attn-QAT page, Metodologia / A and B): the forward of attention_fwd (no
+    FP16 path) plus
+
+      O' = P V^, the high-precision output (normalized probabilities P, not
+           their FP4 version P^), kept for the backward;
+      dV = P^T dO      (P recomputed in FP4, as the forward used it)
+      dP = dO V^T
+      D  = rowsum(dO * O')   (= rowsum(P * dP): the identity holds for P, not P^)
+      dS = s * P * (dP - D)  with s = c ln 2, c the binary32 score factor
+      dQ = dS K^,  dK = dS^T Q^  (summed over the query heads of a kv head)
+
+    Q^, K^, V^ are the fake-quantized operands and the quantizers pass the
+    gradient straight through (dQ is the gradient of Q^, and so on).  Float64
+    throughout.  Returns dict(out, lse, out_hp, dq, dk, dv)."""
+    q32, k32, v32 = _f32(q), _f32(k), _f32(v)
+    do = _f32(dout).astype(np.float64)
+    B, H, Sq, d = q32.shape
+    Hkv, Sk = k32.shape[1], k32.shape[2]
+    G = H // Hkv
+    out, lse, P, Ph = attention_fwd(q32, k32, v32, causal=causal, softmax_scale=softmax_scale, kv_tile=kv_tile,
+                                    scale_search=scale_search, fmin=fmin, fmax=fmax,
+                                    single_level_p=single_level_p, with_probs=True)
+    P = P.reshape(B, H, Sq, Sk)
+    Ph = Ph.reshape(B, H, Sq, Sk)
+    s = float(score_factor(softmax_scale, d)) * math.log(2.0)
+
+    def fq(x, axis):
+        r = quantize(x, axis, scale_search, fmin, fmax)
+        return dequantize(r["codes"], r["scales"], x.shape[0], x.shape[1], axis)
+
+    out_hp = np.zeros((B, H, Sq, d))
+    dq = np.zeros((B, H, Sq, d))
+    dk = np.zeros((B, Hkv, Sk, d))
+    dv = np.zeros((B, Hkv, Sk, d))
+    for b in range(B):
+        kh = [fq(k32[b, j], 0) for j in range(Hkv)]
+        vh = [fq(v32[b, j], 1) for j in range(Hkv)]
+        for h in range(H):
+            j = h // G
+            qh = fq(q32[b, h], 0)
+            out_hp[b, h] = P[b, h] @ vh[j]
+            dv[b, j] += Ph[b, h].T @ do[b, h]
+            dP = do[b, h] @ vh[j].T
+            D = (do[b, h] * out_hp[b, h]).sum(axis=1)
+            dS = s * P[b, h] * (dP - D[:, None])
+            dq[b, h] = dS @ kh[j]
+            dk[b, j] += dS.T @ qh
+    return dict(out=out.reshape(B, H, Sq, d), lse=lse.reshape(B, H, Sq), out_hp=out_hp, dq=dq, dk=dk, dv=dv)
