@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "load", "build", "fp4_version", "fp4_last_error", "fp4_quantize", "fp4_block_topk",
     "fp4_attention_fwd", "fp4_attention_decode", "fp4_kv_cache_append", "fp4_kv_block_sums", "decode_sel_kmax",
+    "fp4_attention_fwd_train", "fp4_attention_bwd",
     "FP4Error", "BF16", "FP16", "FP32", "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
 ]
 
@@ -113,6 +114,12 @@ def load():
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
+    L.fp4_attention_fwd_train.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, vp, sz, vp]
+    L.fp4_attention_fwd_train.restype = C.c_int
+    L.fp4_attention_bwd.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fp4_attention_bwd.restype = C.c_int
+    L.fp4_attention_bwd_workspace_size.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts)]
+    L.fp4_attention_bwd_workspace_size.restype = sz
     L.fp4_attention_decode_selective.argtypes = [vp, i64, C.POINTER(KVCacheStruct), i32, C.c_float, i32, vp, vp,
                                                  vp, vp, vp, sz, vp]
     L.fp4_attention_decode_selective.restype = C.c_int
@@ -281,6 +288,50 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
     _check(L.fp4_attention_fwd(C.byref(P), C.byref(O), _ptr(out), _ptr(lse), _ptr(idx), _ptr(cnt), _ptr(ws),
                                nws, _stream(dev)))
     return (out, lse, idx, cnt) if return_topk else (out, lse)
+
+
+def fp4_attention_fwd_train(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
+                            f_max=6, out_dtype=FP32, single_level_p=False, workspace=None):
+    """Training forward: (out, out_hp, lse) -- out and lse as fp4_attention_fwd,
+    out_hp the high-precision output O' kept for the backward."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    B, H, Sq, d = q.shape
+    P = _problem(q, k, v)
+    O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, 0, 128, out_dtype,
+              single_level_p=single_level_p)
+    out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
+    out_hp = torch.empty_like(out)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    nws = L.fp4_attention_fwd_workspace_size(C.byref(P), C.byref(O))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
+    _check(L.fp4_attention_fwd_train(C.byref(P), C.byref(O), _ptr(out), _ptr(out_hp), _ptr(lse), _ptr(ws), nws,
+                                     _stream(q.device)))
+    return out, out_hp, lse
+
+
+def fp4_attention_bwd(q, k, v, out_hp, lse, dout, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
+                      f_min=-2, f_max=6, single_level_p=False, workspace=None):
+    """Training backward: (dq, dk, dv) in float32 from fp4_attention_fwd_train's
+    out_hp and lse and the output gradient dout (q's dtype)."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out_hp, "out_hp"), (lse, "lse"), (dout, "dout")):
+        _dev(t, n)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    hp_dtype = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}[out_hp.dtype]
+    P = _problem(q, k, v)
+    O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, 0, 128, hp_dtype,
+              single_level_p=single_level_p)
+    dq = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, Sk, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, Sk, d), dtype=torch.float32, device=q.device)
+    nws = L.fp4_attention_bwd_workspace_size(C.byref(P), C.byref(O))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, q.device)
+    _check(L.fp4_attention_bwd(C.byref(P), C.byref(O), _ptr(out_hp), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(ws), nws, _stream(q.device)))
+    return dq, dk, dv
 
 
 def attention_fwd_workspace_bytes(q_shape, kv_shape, causal=False, kv_tile=128, fp16_budget_pct=0,

@@ -259,12 +259,16 @@ int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int3
   return launch_selection(prob, opts, P, (char*)workspace, topk_idx, topk_cnt, (hipStream_t)stream);
 }
 
-int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, float* lse,
-                      int32_t* topk_idx, int32_t* topk_cnt, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  int st = check_attn(prob, opts, "fp4_attention_fwd", false);
-  if (st) return st;
-  if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "fp4_attention_fwd: out must be non-NULL and 16-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// The forward: quantization and selection into the workspace when needed, then
+// the attention kernel for `out`, and with out_hp the same kernel with
+// unquantized P on the FP4 tiles for the high-precision output.
+int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, void* out_hp,
+                       float* lse, int32_t* topk_idx, int32_t* topk_cnt, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   AttnPlan P = plan_attn(prob, opts);
   if (workspace_bytes < P.total || (P.total && !workspace))
     return fail(FP4_ERR_WORKSPACE, "fp4_attention_fwd: workspace needs %zu bytes", P.total);
@@ -311,7 +315,7 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
     idx = topk_idx;
     cnt = topk_cnt;
   } else if (P.need_sel) {
-    st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s);
+    const int st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s);
     if (st) return st;
     idx = topk_idx ? topk_idx : (const int32_t*)(ws + P.idx);
     cnt = topk_cnt ? topk_cnt : (const int32_t*)(ws + P.cnt);
@@ -325,7 +329,7 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   A.c = score_factor(opts->softmax_scale, d);
   A.kv_tile = opts->kv_tile;
   A.pct = opts->fp16_budget_pct;
-  A.single_p = opts->p_single_level;
+  A.p_mode = opts->p_single_level ? 1 : 0;
   A.sel_block = opts->sel_block;
   A.nqb = P.nqb;
   A.kmax = P.kmax;
@@ -334,7 +338,109 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   A.out_dtype = opts->out_dtype;
   A.out = out;
   A.lse = lse;
-  return hip_status(fp4i_launch_attn_fwd(A, s), "fp4_attention_fwd launch");
+  const int st2 = hip_status(fp4i_launch_attn_fwd(A, s), "fp4_attention_fwd launch");
+  if (st2 || !out_hp) return st2;
+  A.p_mode = 2;
+  A.out = out_hp;
+  A.lse = nullptr;
+  return hip_status(fp4i_launch_attn_fwd(A, s), "fp4_attention_fwd_train launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, float* lse,
+                      int32_t* topk_idx, int32_t* topk_cnt, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int st = check_attn(prob, opts, "fp4_attention_fwd", false);
+  if (st) return st;
+  if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "fp4_attention_fwd: out must be non-NULL and 16-byte aligned");
+  return attention_fwd_impl(prob, opts, out, nullptr, lse, topk_idx, topk_cnt, workspace, workspace_bytes, stream);
+}
+
+size_t fp4_attention_bwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
+  if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
+    return 0;
+  const AttnPlan P = plan_attn(prob, opts);
+  AttnBwdLaunch L{};
+  L.B = prob->B; L.H = prob->H; L.Hkv = prob->Hkv; L.Sq = prob->Sq; L.Sk = prob->Sk; L.d = prob->d;
+  return align256(P.total) + fp4i_attn_bwd_workspace(L);
+}
+
+int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, const void* out_hp, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const char* fn = "fp4_attention_bwd";
+  int st = check_attn(prob, opts, fn, false);
+  if (st) return st;
+  if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_UNSUPPORTED, "%s: training has no FP16 path (fp16_budget_pct must be 0)", fn);
+  if (opts->hadamard_qk) return fail(FP4_ERR_UNSUPPORTED, "%s: the rotation is not supported in training", fn);
+  if (!out_hp || !lse || !dout || !dq || !dk || !dv) return fail(FP4_ERR_INVALID_ARG, "%s: out_hp, lse, dout, dq, dk, dv are required", fn);
+  const void* ptrs[] = {out_hp, lse, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if (prob->Sk > 65536) return fail(FP4_ERR_UNSUPPORTED, "%s: Sk above 65536", fn);
+  const size_t need = fp4_attention_bwd_workspace_size(prob, opts);
+  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  const AttnPlan P = plan_attn(prob, opts);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t B = prob->B, H = prob->H, Hkv = prob->Hkv, Sq = prob->Sq, Sk = prob->Sk, d = prob->d;
+  const uint8_t *qc = prob->q_codes, *qs = prob->q_scales, *kc = prob->k_codes, *ks = prob->k_scales,
+                *vc = prob->v_codes, *vs = prob->v_scales;
+  if (P.need_quant) {  // the forward's quantization, repeated
+    QuantLaunch L{};
+    L.dtype = prob->dtype;
+    L.search = opts->scale_search;
+    L.fmin = opts->f_min;
+    L.fmax = opts->f_max;
+    L.cols = d;
+    L.ld = d;
+    L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
+    L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
+    hipError_t e = fp4i_launch_quantize(L, s);
+    if (e == hipSuccess) {
+      L.x = prob->k; L.rows = B * Hkv * Sk;
+      L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
+      e = fp4i_launch_quantize(L, s);
+    }
+    if (e == hipSuccess) {
+      L.x = prob->v; L.axis = 1;
+      L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
+      e = fp4i_launch_quantize(L, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "fp4_attention_bwd quantize launch");
+    qc = (uint8_t*)(ws + P.qc); qs = (uint8_t*)(ws + P.qs);
+    kc = (uint8_t*)(ws + P.kc); ks = (uint8_t*)(ws + P.ks);
+    vc = (uint8_t*)(ws + P.vc); vs = (uint8_t*)(ws + P.vs);
+  }
+  AttnBwdLaunch L{};
+  L.B = B; L.H = H; L.Hkv = Hkv; L.Sq = Sq; L.Sk = Sk; L.d = d;
+  L.dtype = prob->dtype;
+  L.hp_dtype = opts->out_dtype;
+  L.qc = qc; L.qs = qs; L.kc = kc; L.ks = ks; L.vc = vc; L.vs = vs;
+  L.dout = dout;
+  L.out_hp = out_hp;
+  L.lse = lse;
+  L.causal = opts->causal;
+  L.kv_tile = opts->kv_tile;
+  L.single = opts->p_single_level;
+  L.c = score_factor(opts->softmax_scale, d);
+  L.dq = dq; L.dk = dk; L.dv = dv;
+  L.ws = ws + align256(P.total);
+  return hip_status(fp4i_launch_attn_bwd(L, s), "fp4_attention_bwd launch");
+}
+
+int fp4_attention_fwd_train(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, void* out_hp,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "fp4_attention_fwd_train";
+  int st = check_attn(prob, opts, fn, false);
+  if (st) return st;
+  if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_UNSUPPORTED, "%s: training has no FP16 path (fp16_budget_pct must be 0)", fn);
+  if (!out || !out_hp || !lse || !aligned16(out) || !aligned16(out_hp))
+    return fail(FP4_ERR_INVALID_ARG, "%s: out, out_hp and lse are required (16-byte aligned)", fn);
+  return attention_fwd_impl(prob, opts, out, out_hp, lse, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -223,7 +223,6 @@ struct Problem {
   const void *q, *k, *v;
   const int32_t *idx, *cnt;
   int causal, pct, sel_block, nqb, kmax, nqt;
-  int single_p;  // 1: single-level P
   float c;
   void* out;
   float* lse;
@@ -570,7 +569,10 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
 
-template <int D, int BC, typename IT, typename OT, bool SINGLE>
+// PM: P on the FP4 tiles -- 0 two-level, 1 single-level, 2 unquantized
+// (fp16 probabilities with the FP4 operands: the high-precision output O' of
+// training, Attn-QAT page, Metodologia / A).
+template <int D, int BC, typename IT, typename OT, int PM>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   __shared__ Smem<D, BC> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
@@ -595,7 +597,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   const int64_t qrow = q0 + 32 * wave + (lane & 31);
   const int64_t Sk = P.Sk;
 
-  if (threadIdx.x < 128) S.pt[threadIdx.x] = SINGLE ? kPScale1.v[threadIdx.x] : kPScale.v[threadIdx.x];
+  if (threadIdx.x < 128) S.pt[threadIdx.x] = PM == 1 ? kPScale1.v[threadIdx.x] : kPScale.v[threadIdx.x];
   // Q^ fragment (B operand): query qrow, d = 16 s + 8 hi .. +8
   half8_t qf[D / 16];
   {
@@ -663,14 +665,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     const bool wave_dead = P.causal && key0 > wrow0 + 31;  // every key of the tile is after this wave's rows
     if (!wave_dead) {
       const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
-      if (need_mask) wave_tile<D, BC, true, true, SINGLE>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-      else wave_tile<D, BC, true, false, SINGLE>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      if (need_mask) wave_tile<D, BC, PM != 2, true, PM == 1>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      else wave_tile<D, BC, PM != 2, false, PM == 1>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
     }
     cur = nxt;
   }
 
   // FP4 tiles accumulated P^ V^ with P^ in units of e/2688 (two-level) or of e
-  const float to_e = SINGLE ? 1.0f : 1.0f / 2688.0f;
+  const float to_e = PM == 0 ? 1.0f / 2688.0f : 1.0f;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -727,23 +729,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   }
 }
 
-template <int D, int BC, typename IT, bool SINGLE>
+template <int D, int BC, typename IT, int PM>
 hipError_t launch_out(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
-  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float, SINGLE>), grid, dim3(256), 0, st, P);
-  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t, SINGLE>), grid, dim3(256), 0, st, P);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t, SINGLE>), grid, dim3(256), 0, st, P);
+  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float, PM>), grid, dim3(256), 0, st, P);
+  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t, PM>), grid, dim3(256), 0, st, P);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t, PM>), grid, dim3(256), 0, st, P);
   return hipGetLastError();
 }
 
 template <int D, int BC>
 hipError_t launch_in(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
-  // single-level P: bf16 or fp16 in, every output type
-  if (L.single_p) {
-    if (L.dtype == 1) return launch_out<D, BC, half_t, true>(L, P, grid, st);
-    return launch_out<D, BC, uint16_t, true>(L, P, grid, st);
+  // P mode x input type x output type
+  if (L.p_mode == 1) {
+    if (L.dtype == 1) return launch_out<D, BC, half_t, 1>(L, P, grid, st);
+    return launch_out<D, BC, uint16_t, 1>(L, P, grid, st);
   }
-  if (L.dtype == 1) return launch_out<D, BC, half_t, false>(L, P, grid, st);
-  return launch_out<D, BC, uint16_t, false>(L, P, grid, st);
+  if (L.p_mode == 2) {
+    if (L.dtype == 1) return launch_out<D, BC, half_t, 2>(L, P, grid, st);
+    return launch_out<D, BC, uint16_t, 2>(L, P, grid, st);
+  }
+  if (L.dtype == 1) return launch_out<D, BC, half_t, 0>(L, P, grid, st);
+  return launch_out<D, BC, uint16_t, 0>(L, P, grid, st);
 }
 
 }  // namespace fp4dev
@@ -757,7 +763,6 @@ hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t st) {
   P.q = L.q; P.k = L.k; P.v = L.v;
   P.idx = L.idx; P.cnt = L.cnt;
   P.causal = L.causal; P.pct = L.pct; P.sel_block = L.pct > 0 ? L.sel_block : 128;
-  P.single_p = L.single_p;
   P.nqb = L.nqb; P.kmax = L.kmax;
   P.c = L.c;
   P.out = L.out; P.lse = L.lse;

@@ -1,0 +1,359 @@
+// attn_train.hip -- backward of FP4 attention for quantization-aware training
+// (Attn-QAT page, Metodologia / A: the probabilities are recomputed in FP4 in
+// the backward, as the forward used them; the row term of the softmax
+// gradient uses the high-precision output O' kept by the forward).
+//
+// With fake-quantized operands Q^, K^, V^ (NVFP4, straight-through), the
+// normalized probabilities P = 2^(x - lse2) (x = fl32(S c), S = Q^ K^T) and the
+// normalized FP4 weights P^ the forward's output used (tile-local
+// quantization of e = 2^(x - tm), rescaled by 2^(tm - lse2)):
+//   dV = P^T dO,  dS = s P * (dO V^T - D),  D = rowsum(dO * O'),
+//   dQ = dS K^,   dK = dS^T Q^,             s = c ln 2.
+// The score-sized matrices are materialized (one float per query/key pair
+// for P, then dS in place, one for P^), so the workspace grows with
+// B H Sq Sk; the products are batched fp32 GEMMs (64 x 64 tiles, LDS
+// staged), and the query heads of a kv head are consecutive rows of one GEMM
+// for dK and dV.
+#include "device_common.h"
+#include "fp4_internal.h"
+
+namespace fp4dev {
+
+// ---- operands in fp32 ----------------------------------------------------
+
+// NVFP4 rows with blocks along the row (Q, K): codes [rows, d/2], scales
+// [rows, d/16] -> fp32 [rows, d].  One thread per 8 codes (4 bytes).
+__global__ void __launch_bounds__(256) dequant_rows_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                           int64_t rows, int d, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of 8 elements
+  const int64_t n = rows * (d / 8);
+  if (i >= n) return;
+  const int64_t r = i / (d / 8);
+  const int c8 = (int)(i % (d / 8));
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (d / 2) + 4 * c8);
+  const float s = e4m3_to_f32(scales[r * (d / 16) + c8 / 2]);
+  float* o = out + r * d + 8 * c8;
+  const float2_t v0 = cvt_pk_f32_fp4<0>(w), v1 = cvt_pk_f32_fp4<1>(w);
+  const float2_t v2 = cvt_pk_f32_fp4<2>(w), v3 = cvt_pk_f32_fp4<3>(w);
+  *reinterpret_cast<float4_t*>(o) = float4_t{v0[0] * s, v0[1] * s, v1[0] * s, v1[1] * s};
+  *reinterpret_cast<float4_t*>(o + 4) = float4_t{v2[0] * s, v2[1] * s, v3[0] * s, v3[1] * s};
+}
+
+// NVFP4 with blocks of 16 rows (V): codes [rows/2, d] (row 2i in the low
+// nibble), scales [rows/16, d] -> fp32 [rows, d].  One thread per row pair
+// and column.
+__global__ void __launch_bounds__(256) dequant_cols_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                           int64_t rows, int d, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (rows / 2) * d;
+  if (i >= n) return;
+  const int64_t pr = i / d;
+  const int c = (int)(i % d);
+  const uint32_t b = codes[pr * d + c];
+  const float s = e4m3_to_f32(scales[(pr / 8) * d + c]);
+  const float2_t v = cvt_pk_f32_fp4<0>(b);
+  out[(2 * pr) * d + c] = v[0] * s;
+  out[(2 * pr + 1) * d + c] = v[1] * s;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <>
+__device__ __forceinline__ float to_f32<half_t>(half_t v) { return (float)v; }
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+template <typename T>
+__global__ void __launch_bounds__(256) to_f32_kernel(const T* x, int64_t n, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = to_f32<T>(x[i]);
+}
+
+// D[row] = sum_d dO[row][d] O'[row][d], one wave per row.
+template <typename TO>
+__global__ void __launch_bounds__(256) row_dot_kernel(const float* dout, const TO* ohp, int64_t rows, int d,
+                                                      float* D) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float s = 0.0f;
+  for (int c = lane; c < d; c += 64) s = __builtin_fmaf(dout[row * d + c], to_f32<TO>(ohp[row * d + c]), s);
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
+  if (lane == 0) D[row] = s;
+}
+
+// ---- probabilities --------------------------------------------------------
+
+// Per E4M3 byte of the P block scale: {factor, s2} with factor the element
+// multiplier of the quantization input (two-level: fl32(2688 / s2); single
+// level: the correctly rounded 1 / s2), as the forward's definition.
+struct TrainPTable {
+  float2_t two[128];
+  float2_t one[128];
+  constexpr TrainPTable() : two(), one() {
+    for (int b = 0; b < 128; ++b) {
+      double s2 = 0.0;
+      if (b < 8) s2 = (double)b / 512.0;
+      else {
+        int e = (b >> 3) - 7, mm = b & 7;
+        s2 = 1.0 + (double)mm / 8.0;
+        for (int i = 0; i < e; ++i) s2 *= 2.0;
+        for (int i = 0; i > e; --i) s2 /= 2.0;
+      }
+      const bool ok = b != 0 && b != 127;
+      two[b] = ok ? float2_t{(float)(2688.0 / s2), (float)s2} : float2_t{0.0f, 0.0f};
+      one[b] = ok ? float2_t{(float)(1.0 / s2), (float)s2} : float2_t{0.0f, 0.0f};
+    }
+  }
+};
+__constant__ TrainPTable kTrainP = TrainPTable();
+
+struct ProbArgs {
+  float* S;      // [rows][Sk]: the scores in, the probabilities P out (in place)
+  float* Phat;   // [rows][Sk]: the normalized FP4 weights P^
+  const float* lse;
+  int64_t rows, Sq, Sk;
+  int kv_tile, causal, single;
+  float c;
+};
+
+// One workgroup per query row; a thread takes 16 consecutive keys (one P
+// block).  Pass 1: block maxima of x = fl32(S c) into LDS; pass 2: the tile
+// maximum tm from its blocks, e = 2^(x - tm), the block scale and codes, and
+// P = 2^(x - lse2), P^ = v s2 2^(tm - lse2) (/2688 two-level).
+__global__ void __launch_bounds__(256) probs_kernel(ProbArgs A) {
+  extern __shared__ float bmax[];  // Sk / 16
+  const int64_t row = blockIdx.x;
+  const int64_t q = row % A.Sq;
+  const int64_t nvis = A.causal ? (q + 1 < A.Sk ? q + 1 : A.Sk) : A.Sk;
+  const int nblk = (int)(A.Sk / 16);
+  float* srow = A.S + row * A.Sk;
+  float* prow = A.Phat + row * A.Sk;
+  const float lse2 = A.lse[row] * 1.4426950408889634f;
+  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = 16 * (int64_t)b + i;
+      if (j < nvis) m = __builtin_fmaxf(m, srow[j] * A.c);
+    }
+    bmax[b] = m;
+  }
+  __syncthreads();
+  const int bpt = A.kv_tile / 16;  // blocks per tile
+  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
+    const int t0 = (b / bpt) * bpt;
+    float tm = -__builtin_inff();
+    for (int k = 0; k < bpt && t0 + k < nblk; ++k) tm = __builtin_fmaxf(tm, bmax[t0 + k]);  // (a short last tile)
+    float x[16], e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = 16 * (int64_t)b + i;
+      x[i] = j < nvis ? srow[j] * A.c : -__builtin_inff();
+      e[i] = __builtin_amdgcn_exp2f(x[i] - tm);  // masked: 0 (tm finite on a visible tile)
+    }
+    float pv[16], ph[16];
+    if (bmax[b] == -__builtin_inff()) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = ph[i] = 0.0f;
+    } else {
+      const float emax = __builtin_amdgcn_exp2f(bmax[b] - tm);
+      const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
+      const float2_t fs = A.single ? kTrainP.one[byte] : kTrainP.two[byte];
+      const float w = __builtin_amdgcn_exp2f(tm - lse2) * (A.single ? 1.0f : 1.0f / 2688.0f);
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = e[i] * fs[0];
+      uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        cw[h] = cvt_pk_fp4<0>(cw[h], t[8 * h + 0], t[8 * h + 1]);
+        cw[h] = cvt_pk_fp4<1>(cw[h], t[8 * h + 2], t[8 * h + 3]);
+        cw[h] = cvt_pk_fp4<2>(cw[h], t[8 * h + 4], t[8 * h + 5]);
+        cw[h] = cvt_pk_fp4<3>(cw[h], t[8 * h + 6], t[8 * h + 7]);
+      }
+      float cv[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float2_t a0 = cvt_pk_f32_fp4<0>(cw[h]), a1 = cvt_pk_f32_fp4<1>(cw[h]);
+        const float2_t a2 = cvt_pk_f32_fp4<2>(cw[h]), a3 = cvt_pk_f32_fp4<3>(cw[h]);
+        cv[8 * h + 0] = a0[0]; cv[8 * h + 1] = a0[1]; cv[8 * h + 2] = a1[0]; cv[8 * h + 3] = a1[1];
+        cv[8 * h + 4] = a2[0]; cv[8 * h + 5] = a2[1]; cv[8 * h + 6] = a3[0]; cv[8 * h + 7] = a3[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        ph[i] = cv[i] * fs[1] * w;  // code value times s2 is exact; one rounding for the weight
+        pv[i] = __builtin_amdgcn_exp2f(x[i] - lse2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      *reinterpret_cast<float4_t*>(srow + 16 * (int64_t)b + i) = float4_t{pv[i], pv[i + 1], pv[i + 2], pv[i + 3]};
+      *reinterpret_cast<float4_t*>(prow + 16 * (int64_t)b + i) = float4_t{ph[i], ph[i + 1], ph[i + 2], ph[i + 3]};
+    }
+  }
+}
+
+// ---- batched fp32 GEMM ----------------------------------------------------
+
+struct GemmArgs {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t M, N, K, lda, ldb, ldc, sA, sB, sC;
+  int gA, gB;          // batch z reads A batch z / gA and B batch z / gB
+  float alpha;         // epilogue 1: C = alpha * C * (acc - D[z][row])
+  const float* D;
+};
+
+// C[z] = op(A) op(B): op(A) is M x K (TA: A stored K x M), op(B) is K x N (TB:
+// B stored N x K).  64 x 64 tile per workgroup, 16-deep k slices through LDS,
+// 4 x 4 outputs per thread.
+template <bool TA, bool TB, int EPI>
+__global__ void __launch_bounds__(256) sgemm_kernel(GemmArgs g) {
+  __shared__ float As[16][68];
+  __shared__ float Bs[16][68];
+  const int64_t z = blockIdx.z;
+  const float* A = g.A + (z / g.gA) * g.sA;
+  const float* B = g.B + (z / g.gB) * g.sB;
+  float* C = g.C + z * g.sC;
+  const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int64_t k0 = 0; k0 < g.K; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      const int mm = TA ? (e & 63) : (e >> 4), ka = TA ? (e >> 6) : (e & 15);
+      const int64_t gm = m0 + mm, gk = k0 + ka;
+      As[ka][mm] = (gm < g.M && gk < g.K) ? (TA ? A[gk * g.lda + gm] : A[gm * g.lda + gk]) : 0.0f;
+      const int nn = TB ? (e >> 4) : (e & 63), kb = TB ? (e & 15) : (e >> 6);
+      const int64_t gn = n0 + nn, gkb = k0 + kb;
+      Bs[kb][nn] = (gn < g.N && gkb < g.K) ? (TB ? B[gn * g.ldb + gkb] : B[gkb * g.ldb + gn]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float4_t a = *reinterpret_cast<const float4_t*>(&As[kk][4 * ty]);
+      const float4_t b = *reinterpret_cast<const float4_t*>(&Bs[kk][4 * tx]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = m0 + 4 * ty + i;
+    if (r >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t cidx = n0 + 4 * tx + j;
+      if (cidx >= g.N) continue;
+      float* p = C + r * g.ldc + cidx;
+      if (EPI == 0) *p = acc[i][j];
+      else *p = g.alpha * *p * (acc[i][j] - g.D[z * g.M + r]);
+    }
+  }
+}
+
+template <bool TA, bool TB, int EPI>
+hipError_t gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  const dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)batch);
+  hipLaunchKernelGGL((sgemm_kernel<TA, TB, EPI>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace fp4dev
+
+using namespace fp4dev;
+
+size_t fp4i_attn_bwd_workspace(const AttnBwdLaunch& L) {
+  auto a = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  const size_t nq = (size_t)(L.B * L.H * L.Sq), nk = (size_t)(L.B * L.Hkv * L.Sk);
+  return a(nq * L.d * 4) * 2 + a(nk * L.d * 4) * 2 + a(nq * 4) + a(nq * (size_t)L.Sk * 4) * 2;
+}
+
+hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
+  auto a = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  const int64_t B = L.B, H = L.H, Hkv = L.Hkv, Sq = L.Sq, Sk = L.Sk, d = L.d, G = H / Hkv;
+  const size_t nq = (size_t)(B * H * Sq), nk = (size_t)(B * Hkv * Sk);
+  char* w = (char*)L.ws;
+  float* qh = (float*)w; w += a(nq * d * 4);
+  float* dof = (float*)w; w += a(nq * d * 4);
+  float* kh = (float*)w; w += a(nk * d * 4);
+  float* vh = (float*)w; w += a(nk * d * 4);
+  float* Dv = (float*)w; w += a(nq * 4);
+  float* Sb = (float*)w; w += a(nq * (size_t)Sk * 4);
+  float* Ph = (float*)w;
+  auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
+  // operands
+  hipLaunchKernelGGL(dequant_rows_kernel, blocks((int64_t)nq * d / 8), dim3(256), 0, st, L.qc, L.qs, (int64_t)nq,
+                     (int)d, qh);
+  hipLaunchKernelGGL(dequant_rows_kernel, blocks((int64_t)nk * d / 8), dim3(256), 0, st, L.kc, L.ks, (int64_t)nk,
+                     (int)d, kh);
+  hipLaunchKernelGGL(dequant_cols_kernel, blocks((int64_t)nk / 2 * d), dim3(256), 0, st, L.vc, L.vs, (int64_t)nk,
+                     (int)d, vh);
+  if (L.dtype == 1)
+    hipLaunchKernelGGL(to_f32_kernel<half_t>, blocks((int64_t)nq * d), dim3(256), 0, st, (const half_t*)L.dout,
+                       (int64_t)nq * d, dof);
+  else
+    hipLaunchKernelGGL(to_f32_kernel<uint16_t>, blocks((int64_t)nq * d), dim3(256), 0, st, (const uint16_t*)L.dout,
+                       (int64_t)nq * d, dof);
+  const dim3 rd((unsigned)((nq + 3) / 4));
+  if (L.hp_dtype == 2) hipLaunchKernelGGL(row_dot_kernel<float>, rd, dim3(256), 0, st, dof, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  else if (L.hp_dtype == 1) hipLaunchKernelGGL(row_dot_kernel<half_t>, rd, dim3(256), 0, st, dof, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  else hipLaunchKernelGGL(row_dot_kernel<uint16_t>, rd, dim3(256), 0, st, dof, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  // S = Q^ K^T per query head (K^ of its kv head)
+  GemmArgs g{};
+  g.A = qh; g.lda = d; g.sA = Sq * d; g.gA = 1;
+  g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
+  g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
+  g.M = Sq; g.N = Sk; g.K = d;
+  hipError_t e = gemm<false, true, 0>(g, B * H, st);
+  if (e != hipSuccess) return e;
+  // P and P^
+  ProbArgs pa;
+  pa.S = Sb; pa.Phat = Ph; pa.lse = L.lse;
+  pa.rows = (int64_t)nq; pa.Sq = Sq; pa.Sk = Sk;
+  pa.kv_tile = L.kv_tile; pa.causal = L.causal; pa.single = L.single; pa.c = L.c;
+  hipLaunchKernelGGL(probs_kernel, dim3((unsigned)nq), dim3(256), (size_t)(Sk / 16) * 4, st, pa);
+  // dV = P^T dO over the G query heads of each kv head
+  g = GemmArgs{};
+  g.A = Ph; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
+  g.B = dof; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
+  g.C = L.dv; g.ldc = d; g.sC = Sk * d;
+  g.M = Sk; g.N = d; g.K = G * Sq;
+  if ((e = gemm<true, false, 0>(g, B * Hkv, st)) != hipSuccess) return e;
+  // dS = s P (dO V^T - D), written over P
+  g = GemmArgs{};
+  g.A = dof; g.lda = d; g.sA = Sq * d; g.gA = 1;
+  g.B = vh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
+  g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
+  g.M = Sq; g.N = Sk; g.K = d;
+  g.alpha = L.c * 0.69314718055994531f;
+  g.D = Dv;
+  if ((e = gemm<false, true, 1>(g, B * H, st)) != hipSuccess) return e;
+  // dQ = dS K^
+  g = GemmArgs{};
+  g.A = Sb; g.lda = Sk; g.sA = Sq * Sk; g.gA = 1;
+  g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
+  g.C = L.dq; g.ldc = d; g.sC = Sq * d;
+  g.M = Sq; g.N = d; g.K = Sk;
+  if ((e = gemm<false, false, 0>(g, B * H, st)) != hipSuccess) return e;
+  // dK = dS^T Q^ over the G query heads of each kv head
+  g = GemmArgs{};
+  g.A = Sb; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
+  g.B = qh; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
+  g.C = L.dk; g.ldc = d; g.sC = Sk * d;
+  g.M = Sk; g.N = d; g.K = G * Sq;
+  return gemm<true, false, 0>(g, B * Hkv, st);
+}

@@ -53,7 +53,7 @@ struct AttnLaunch {
   float c;  // log2(e) * softmax_scale, rounded once to binary32
   int kv_tile;
   int pct, sel_block, nqb, kmax;
-  int single_p;        // 1: single-level P
+  int p_mode;          // P on the FP4 tiles: 0 two-level, 1 single-level, 2 unquantized (O')
   const int32_t* idx;  // selection (pct > 0)
   const int32_t* cnt;
   int out_dtype;
@@ -62,6 +62,24 @@ struct AttnLaunch {
 };
 
 hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t stream);
+
+// Backward of the FP4 attention (training).
+struct AttnBwdLaunch {
+  int64_t B, H, Hkv, Sq, Sk, d;
+  int dtype;       // of dout (0 bf16, 1 fp16)
+  int hp_dtype;    // of out_hp (0 bf16, 1 fp16, 2 fp32)
+  const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
+  const void* dout;
+  const void* out_hp;
+  const float* lse;
+  int causal, kv_tile, single;
+  float c;
+  float *dq, *dk, *dv;
+  void* ws;
+};
+
+size_t fp4i_attn_bwd_workspace(const AttnBwdLaunch& L);
+hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t stream);
 
 struct DecodeLaunch {
   const void* q;  // bf16 [B,Hq,d]

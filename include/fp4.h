@@ -206,6 +206,41 @@ int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int3
 size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
 
 /* ------------------------------------------------------------------------ */
+/* Training -- Attn-QAT page, Metodologia / A (principles: P recomputed in    */
+/* FP4 in the backward; a high-precision output O' for the softmax gradient) */
+/* and / B (fake-quantized forward)                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Training forward: out and lse exactly as fp4_attention_fwd, and out_hp
+ * [B,H,Sq,d] (opts->out_dtype) the high-precision output O' = P V^: the same
+ * scores and softmax, with the probabilities themselves (as fp16 operands of
+ * the product, not their FP4 version) weighting the fake-quantized V.  Needs
+ * fp16_budget_pct == 0.  lse is required.  Workspace: fp4_attention_fwd's.
+ */
+int fp4_attention_fwd_train(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, void* out_hp,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training backward with straight-through fake quantization: given dout
+ * [B,H,Sq,d] (prob->dtype), out_hp and lse from fp4_attention_fwd_train with
+ * the same problem and opts, writes the binary32 gradients
+ *   dv [B,Hkv,Sk,d] = P^T dO        (P^ the FP4 weights the forward used,
+ *                                     recomputed in FP4)
+ *   dq [B,H,Sq,d]   = dS K^,  dk [B,Hkv,Sk,d] = dS^T Q^ (summed over the
+ *                    query heads of each kv head),
+ *   dS = c ln2 * P * (dO V^T - rowsum(dO * O')),  P = 2^(x - lse log2 e),
+ * with Q^, K^, V^ the NVFP4 operands of the forward (quantized again here
+ * unless given).  Needs fp16_budget_pct == 0, no rotation, Sk <= 65536.  The
+ * workspace holds two binary32 matrices of B*H*Sq*Sk scores (see the query).
+ */
+int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, const void* out_hp, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+size_t fp4_attention_bwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
+
+/* ------------------------------------------------------------------------ */
 /* Decode -- ScaleSearch page, Metodologia / ScaleSearchAttention (cache)    */
 /* ------------------------------------------------------------------------ */
 
