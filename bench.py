@@ -294,6 +294,37 @@ def bench_decode(fp4, synth, torch, n, selective=True):
     return res
 
 
+def bench_train(fp4, synth, torch, n):
+    """Training step of the FP4 attention (Attn-QAT): forward with O' and the
+    straight-through backward, B=1 H=32 S=4096 d=128 causal."""
+    S, H, d = 4096, 32, 128
+    q, k, v = synth.qkv(1, H, S, d, torch.bfloat16, seed=0, k_outliers=4, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    do = torch.randn(1, H, S, d, generator=g, device="cuda").to(torch.bfloat16)
+    timer = Timer(torch)
+    fwd = [None]
+
+    def f():
+        fwd[0] = fp4.fp4_attention_fwd_train(q, k, v, causal=True)
+
+    ms_f = timer.run(f, n)
+    out, out_hp, lse = fwd[0]
+    ws = torch.empty(fp4.load().fp4_attention_bwd_workspace_size(
+        ctypes.byref(fp4._problem(q, k, v)),
+        ctypes.byref(fp4._opts(True, 0.0, 128, True, -2, 6, 0, 128, fp4.FP32))), dtype=torch.uint8, device="cuda")
+    ms_b = timer.run(lambda: fp4.fp4_attention_bwd(q, k, v, out_hp, lse, do, causal=True, workspace=ws), n)
+    fl_f = attn_flops(1, H, S, d)          # one attention forward (FA convention, causal half)
+    fl_b = 2.5 * fl_f                       # five score-sized products: S again, dP, dV, dQ, dK
+    return dict(workload="training step B=1 H=32 S=4096 d=128 causal, bf16, ScaleSearch Q/K/V, two-level P",
+                forward_ms=round(ms_f, 4),
+                forward_note="quantization of Q/K/V and two attention passes (FP4 output and O')",
+                forward_tflops=round(2 * fl_f / ms_f / 1e9, 1),
+                backward_ms=round(ms_b, 4), backward_tflops=round(fl_b / ms_b / 1e9, 1),
+                backward_roofline={"bound": "fp32", "achieved": round(fl_b / ms_b / 1e9, 1), "peak": 157.3,
+                                   "unit": "TFLOP/s", "frac": round(fl_b / ms_b / 1e9 / 157.3, 4),
+                                   "note": "causal half counted; products skip the tiles above the diagonal"})
+
+
 def bench_kv_append(fp4, torch, n):
     """Quantize-on-write of 16 tokens per (batch, kv head) into the decode workload's cache."""
     B, Hkv, d, n_recent, cap = 16, 8, 128, 256, 130688
@@ -435,6 +466,8 @@ def main():
         line["components"]["decode"] = bench_decode(fp4, synth, torch, max(5, args.steps))
         log("components: kv append")
         line["components"]["kv_append"] = bench_kv_append(fp4, torch, max(10, args.steps))
+        log("components: training step")
+        line["components"]["train"] = bench_train(fp4, synth, torch, max(3, args.steps // 3))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(res["q"], res["k"], res["v"])

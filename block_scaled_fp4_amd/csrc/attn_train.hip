@@ -207,6 +207,13 @@ struct GemmArgs {
   int gA, gB;          // batch z reads A batch z / gA and B batch z / gB
   float alpha;         // epilogue 1: C = alpha * C * (acc - D[z][row])
   const float* D;
+  // causal structure (the score matrix is zero above the diagonal):
+  // 1: C is queries x keys -- tiles entirely above the diagonal are skipped;
+  // 2: K runs over keys (dS K^) -- the k loop stops after the tile's last query;
+  // 3: M runs over keys, K over stacked query rows of Sq each (P^T dO, dS^T Q^)
+  //    -- k slices whose queries all precede the tile's first key are skipped.
+  int causal;
+  int64_t Sq;
 };
 
 // C[z] = op(A) op(B): op(A) is M x K (TA: A stored K x M), op(B) is K x N (TB:
@@ -221,22 +228,25 @@ __global__ void __launch_bounds__(256) sgemm_kernel(GemmArgs g) {
   const float* B = g.B + (z / g.gB) * g.sB;
   float* C = g.C + z * g.sC;
   const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  if (g.causal == 1 && n0 > m0 + 63) return;  // every key after every query of the tile
+  const int64_t kend = g.causal == 2 && m0 + 64 < g.K ? m0 + 64 : g.K;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int64_t k0 = 0; k0 < g.K; k0 += 16) {
+  for (int64_t k0 = 0; k0 < kend; k0 += 16) {
+    if (g.causal == 3 && (k0 % g.Sq) + 15 < m0) continue;  // (uniform: the same for the whole workgroup)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = threadIdx.x + 256 * u;
       const int mm = TA ? (e & 63) : (e >> 4), ka = TA ? (e >> 6) : (e & 15);
       const int64_t gm = m0 + mm, gk = k0 + ka;
-      As[ka][mm] = (gm < g.M && gk < g.K) ? (TA ? A[gk * g.lda + gm] : A[gm * g.lda + gk]) : 0.0f;
+      As[ka][mm] = (gm < g.M && gk < kend) ? (TA ? A[gk * g.lda + gm] : A[gm * g.lda + gk]) : 0.0f;
       const int nn = TB ? (e >> 4) : (e & 63), kb = TB ? (e & 15) : (e >> 6);
       const int64_t gn = n0 + nn, gkb = k0 + kb;
-      Bs[kb][nn] = (gn < g.N && gkb < g.K) ? (TB ? B[gn * g.ldb + gkb] : B[gkb * g.ldb + gn]) : 0.0f;
+      Bs[kb][nn] = (gn < g.N && gkb < kend) ? (TB ? B[gn * g.ldb + gkb] : B[gkb * g.ldb + gn]) : 0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -318,6 +328,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
   g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
   g.M = Sq; g.N = Sk; g.K = d;
+  g.causal = L.causal ? 1 : 0;
   hipError_t e = gemm<false, true, 0>(g, B * H, st);
   if (e != hipSuccess) return e;
   // P and P^
@@ -332,6 +343,8 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.B = dof; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
   g.C = L.dv; g.ldc = d; g.sC = Sk * d;
   g.M = Sk; g.N = d; g.K = G * Sq;
+  g.causal = L.causal ? 3 : 0;
+  g.Sq = Sq;
   if ((e = gemm<true, false, 0>(g, B * Hkv, st)) != hipSuccess) return e;
   // dS = s P (dO V^T - D), written over P
   g = GemmArgs{};
@@ -341,6 +354,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.M = Sq; g.N = Sk; g.K = d;
   g.alpha = L.c * 0.69314718055994531f;
   g.D = Dv;
+  g.causal = L.causal ? 1 : 0;  // skipped tiles keep P = 0, which is dS there
   if ((e = gemm<false, true, 1>(g, B * H, st)) != hipSuccess) return e;
   // dQ = dS K^
   g = GemmArgs{};
@@ -348,6 +362,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
   g.C = L.dq; g.ldc = d; g.sC = Sq * d;
   g.M = Sq; g.N = d; g.K = Sk;
+  g.causal = L.causal ? 2 : 0;
   if ((e = gemm<false, false, 0>(g, B * H, st)) != hipSuccess) return e;
   // dK = dS^T Q^ over the G query heads of each kv head
   g = GemmArgs{};
@@ -355,5 +370,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.B = qh; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
   g.C = L.dk; g.ldc = d; g.sC = Sk * d;
   g.M = Sk; g.N = d; g.K = G * Sq;
+  g.causal = L.causal ? 3 : 0;
+  g.Sq = Sq;
   return gemm<true, false, 0>(g, B * Hkv, st);
 }
