@@ -420,6 +420,94 @@ typedef struct {
 } tile_acc;
 
 /* Quantize a dense [S][d] slice and return its binary64 dequantized copy. */
+/* ------------------------------------------------------------------------ */
+/* MXFP4: E2M1 elements with one power-of-two (E8M0) scale per 32 elements,  */
+/* the classic block floating point the ScaleSearch page contrasts NVFP4     */
+/* with (Declaracion del Problema: a scale fixed by the block maximum, no    */
+/* mantissa bits).  Scale rule of the OCP microscaling format: shared        */
+/* exponent floor(log2(amax)) - 2 (2 = the exponent of E2M1's largest value),*/
+/* elements rounded to nearest E2M1 (ties to the even code) with saturation  */
+/* at 6 -- values in [6, 8) times the scale clip to 6.                       */
+/* ------------------------------------------------------------------------ */
+
+/* Scale byte (biased by 127) of a block with maximum magnitude a, the
+   shared exponent clamped to [-127, 127]; 0 for a = 0 (every code is then
+   0), 0xFF for a non-finite maximum. */
+int orc_mx_scale_byte(double a) {
+  if (!(a == a) || a == INFINITY) return 0xFF;
+  if (a == 0.0) return 0;
+  int ex;
+  frexp(a, &ex);            /* a = m 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1 */
+  int shared = ex - 1 - 2;
+  if (shared < -127) shared = -127;
+  if (shared > 127) shared = 127;
+  return shared + 127;
+}
+
+/* Blocks of 32 along block_axis (0: columns, 1: rows); codes packed like
+   orc_quantize's (element or row 2i in the low nibble); scales [rows][cols/32]
+   or [rows/32][cols]. */
+void orc_mx_quantize(const float* x, int64_t rows, int64_t cols, int block_axis, uint8_t* codes, uint8_t* scales) {
+  int64_t nb = block_axis == 0 ? rows * (cols / 32) : (rows / 32) * cols;
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    double y[32];
+    int64_t idx[32];
+    for (int t = 0; t < 32; ++t) {
+      int64_t r, c;
+      if (block_axis == 0) { r = blk / (cols / 32); c = (blk % (cols / 32)) * 32 + t; }
+      else { r = (blk / cols) * 32 + t; c = blk % cols; }
+      idx[t] = r * cols + c;
+      y[t] = x[idx[t]];
+    }
+    double a = 0.0;
+    int nonfinite = 0;
+    for (int t = 0; t < 32; ++t) {
+      if (!isfinite(y[t])) nonfinite = 1;
+      else if (fabs(y[t]) > a) a = fabs(y[t]);
+    }
+    int sb = nonfinite ? 0xFF : orc_mx_scale_byte(a);
+    double X = ldexp(1.0, sb - 127);
+    scales[blk] = (uint8_t)sb;
+    for (int t = 0; t < 32; ++t) {
+      int code = 0;
+      if (sb != 0xFF) code = orc_e2m1_encode(fabs(y[t]) / X);  /* (a zero block: every t is 0) */
+      if (sb != 0xFF && signbit(y[t])) code |= 8;
+      int64_t r = idx[t] / cols, c = idx[t] % cols;
+      int64_t byte, shift;
+      if (block_axis == 0) { byte = r * (cols / 2) + c / 2; shift = (c & 1) * 4; }
+      else { byte = (r / 2) * cols + c; shift = (r & 1) * 4; }
+      codes[byte] = (uint8_t)((codes[byte] & ~(0xF << shift)) | (code << shift));
+    }
+  }
+}
+
+void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int block_axis,
+                       double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int code, sb;
+      if (block_axis == 0) {
+        code = (codes[r * (cols / 2) + c / 2] >> ((c & 1) * 4)) & 0xF;
+        sb = scales[r * (cols / 32) + c / 32];
+      } else {
+        code = (codes[(r / 2) * cols + c] >> ((r & 1) * 4)) & 0xF;
+        sb = scales[(r / 32) * cols + c];
+      }
+      out[r * cols + c] = sb == 0xFF ? NAN : orc_e2m1_value(code) * ldexp(1.0, sb - 127);
+    }
+}
+
+static double* mx_quant_dequant(const float* x, int64_t S, int d, int axis) {
+  uint8_t* codes = (uint8_t*)calloc((size_t)(S * d / 2), 1);
+  uint8_t* scales = (uint8_t*)calloc((size_t)(S * d / 32), 1);
+  double* out = (double*)malloc(sizeof(double) * (size_t)(S * d));
+  orc_mx_quantize(x, S, d, axis, codes, scales);
+  orc_mx_dequantize(codes, scales, S, d, axis, out);
+  free(codes);
+  free(scales);
+  return out;
+}
+
 static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss, int fmin, int fmax) {
   uint8_t* codes = (uint8_t*)calloc((size_t)(S * d / 2), 1);
   uint8_t* scales = (uint8_t*)calloc((size_t)(S * d / 16), 1);
@@ -449,7 +537,10 @@ static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss,
 static void attn_row(const double* qh, const double* q16, const double* Kh, const double* Vh,
                      const double* K16, const double* V16, int64_t Sk, int d, int64_t i,
                      int causal, float c, int kv_tile, const int32_t* sel, int nsel, int sel_block,
-                     int single_level, float* out, float* lse, double* Prow, double* Phrow) {
+                     int pmode, float* out, float* lse, double* Prow, double* Phrow) {
+  /* pmode: P on the FP4 tiles -- 0 two-level NVFP4, 1 single-level NVFP4,
+     2 MXFP4 (32-key blocks, power-of-two scale by the OCP rule) */
+  const int single_level = pmode != 0;
   /* Prow, Phrow (nullable, Sk entries): the row's normalized probabilities,
      e * 2^(tm - m) / l, and the normalized weights the output uses, the same
      with P^ in place of e (divided by 2688 on two-level FP4 tiles); zero on
@@ -496,6 +587,16 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
     }
     if (promoted) {
       for (int j = 0; j < n; ++j) P[j] = orc_round_fp16((double)e[j]);
+    } else if (pmode == 2) {
+      for (int b0 = 0; b0 < n; b0 += 32) {
+        int b1 = b0 + 32 < n ? b0 + 32 : n;
+        float amax = 0.0f;
+        for (int j = b0; j < b1; ++j)
+          if (e[j] > amax) amax = e[j];
+        int sb = orc_mx_scale_byte((double)amax);
+        double X = ldexp(1.0, sb - 127);
+        for (int j = b0; j < b1; ++j) P[j] = kE2M1[orc_e2m1_encode((double)e[j] / X)] * X;
+      }
     } else {
       for (int b0 = 0; b0 < n; b0 += 16) {
         int b1 = b0 + 16 < n ? b0 + 16 : n;
@@ -587,7 +688,11 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
                       const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
                       float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt,
                       const float* q_fp4, const float* k_fp4, int single_level,
-                      double* probs, double* probs_hat) {
+                      double* probs, double* probs_hat, int mx) {
+  /* mx: Q, K (blocks of 32 along d), V (blocks of 32 tokens) and P (blocks of
+     32 keys) in MXFP4 instead of NVFP4 (scale_search does not apply) */
+  const int pmode = mx ? 2 : (single_level ? 1 : 0);
+  if (mx && (d % 32 || Sk % 32 || kv_tile % 32)) return -1;
   /* q_fp4, k_fp4 (nullable, same layout as q, k): what the FP4 path
      quantizes, e.g. Q and K after incoherence processing; the FP16 path and
      the block means always use q and k. */
@@ -609,8 +714,9 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
     const float* vb = v + ((int64_t)b * Hkv + hk) * Sk * d;
     const float* qbr = q_fp4 + ((int64_t)b * H + h) * Sq * d;
     const float* kbr = k_fp4 + ((int64_t)b * Hkv + hk) * Sk * d;
-    double* Kh = quant_dequant(kbr, Sk, d, 0, scale_search, fmin, fmax);
-    double* Vh = quant_dequant(vb, Sk, d, 1, scale_search, fmin, fmax);
+    double* Kh = mx ? mx_quant_dequant(kbr, Sk, d, 0) : quant_dequant(kbr, Sk, d, 0, scale_search, fmin, fmax);
+    double* Vh = mx ? mx_quant_dequant(vb, Sk, d, 1) : quant_dequant(vb, Sk, d, 1, scale_search, fmin, fmax);
+    double* Qmx = mx ? mx_quant_dequant(qbr, Sq, d, 0) : NULL;
     double *K16 = NULL, *V16 = NULL;
     int32_t* sidx = NULL;
     int32_t* scnt = NULL;
@@ -637,9 +743,13 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
       int8_t of;
       double* qh = (double*)malloc(sizeof(double) * (size_t)d);
       double* q16 = (double*)malloc(sizeof(double) * (size_t)d);
-      for (int blk = 0; blk < d / 16; ++blk) {
-        orc_quantize_block(qbr + i * d + blk * 16, 1, scale_search, fmin, fmax, cd, &sc, &of, NULL);
-        for (int t = 0; t < 16; ++t) qh[blk * 16 + t] = orc_e2m1_value(cd[t]) * orc_e4m3_value(sc);
+      if (mx) {
+        for (int dd = 0; dd < d; ++dd) qh[dd] = Qmx[i * d + dd];
+      } else {
+        for (int blk = 0; blk < d / 16; ++blk) {
+          orc_quantize_block(qbr + i * d + blk * 16, 1, scale_search, fmin, fmax, cd, &sc, &of, NULL);
+          for (int t = 0; t < 16; ++t) qh[blk * 16 + t] = orc_e2m1_value(cd[t]) * orc_e4m3_value(sc);
+        }
       }
       for (int dd = 0; dd < d; ++dd) q16[dd] = orc_round_fp16(qb[i * d + dd]);
       const int32_t* sel = NULL;
@@ -649,13 +759,13 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
         sel = sidx + (int64_t)qbk * kmax;
         nsel = scnt[qbk];
       }
-      attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block, single_level,
+      attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block, pmode,
                out + ((int64_t)hi * nr + ri) * d, lse ? lse + (int64_t)hi * nr + ri : NULL,
                probs ? probs + ((int64_t)hi * nr + ri) * Sk : NULL,
                probs ? probs_hat + ((int64_t)hi * nr + ri) * Sk : NULL);
       free(qh); free(q16);
     }
-    free(Kh); free(Vh); free(K16); free(V16); free(sidx); free(scnt);
+    free(Kh); free(Vh); free(Qmx); free(K16); free(V16); free(sidx); free(scnt);
   }
   return 0;
 }

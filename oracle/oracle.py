@@ -22,7 +22,8 @@ __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
-    "score_factor", "kv_append", "block_sums", "hadamard_rows", "attention_train",
+    "score_factor", "kv_append", "block_sums", "hadamard_rows", "attention_train", "mx_quantize",
+    "mx_dequantize", "mx_scale_byte",
 ]
 
 
@@ -80,8 +81,13 @@ def lib():
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
-                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _vp]
+                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int]
     L.orc_attention_fwd.restype = C.c_int
+    L.orc_mx_scale_byte.argtypes = [C.c_double]; L.orc_mx_scale_byte.restype = C.c_int
+    L.orc_mx_quantize.argtypes = [_f32p, C.c_int64, C.c_int64, C.c_int, _u8p, _u8p]
+    L.orc_mx_quantize.restype = None
+    L.orc_mx_dequantize.argtypes = [_u8p, _u8p, C.c_int64, C.c_int64, C.c_int, _f64p]
+    L.orc_mx_dequantize.restype = None
     L.orc_hadamard_rows.argtypes = [_f32p, C.c_int64, C.c_int, _vp]
     L.orc_hadamard_rows.restype = None
     L.orc_attention_exact.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
@@ -172,6 +178,30 @@ def hadamard_rows(x, signs=None):
     return x
 
 
+def mx_quantize(x, block_axis=0):
+    """MXFP4 quantization (orc_mx_quantize): blocks of 32, E8M0 scale bytes.
+    Returns dict(codes, scales) with layouts like quantize()'s (scales per 32)."""
+    x = _f32(x)
+    assert x.ndim == 2
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2) if block_axis == 0 else (rows // 2, cols), np.uint8)
+    scales = np.zeros((rows, cols // 32) if block_axis == 0 else (rows // 32, cols), np.uint8)
+    lib().orc_mx_quantize(np.ascontiguousarray(x).reshape(-1), rows, cols, block_axis, codes.reshape(-1),
+                          scales.reshape(-1))
+    return dict(codes=codes, scales=scales)
+
+
+def mx_dequantize(codes, scales, rows, cols, block_axis=0):
+    out = np.zeros(rows * cols, np.float64)
+    lib().orc_mx_dequantize(np.ascontiguousarray(codes, np.uint8).reshape(-1),
+                            np.ascontiguousarray(scales, np.uint8).reshape(-1), rows, cols, block_axis, out)
+    return out.reshape(rows, cols)
+
+
+def mx_scale_byte(a: float) -> int:
+    return lib().orc_mx_scale_byte(float(a))
+
+
 def quantize(x, block_axis=0, scale_search=True, fmin=-2, fmax=6, global_mode=0, g=1.0):
     """Quantize a 2-D tensor. Returns dict(codes, scales, offsets, g, nonfinite_blocks)."""
     x = _f32(x)
@@ -239,14 +269,17 @@ def _sel(arr, dtype):
 
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
-                  with_topk=False, hadamard=False, signs=None, single_level_p=False, with_probs=False):
+                  with_topk=False, hadamard=False, signs=None, single_level_p=False, with_probs=False,
+                  mx=False):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
 
     hadamard: the FP4 path quantizes Q and K after incoherence processing
     (hadamard_rows with the given signs); the FP16 path and the block means
     use the original Q and K.  single_level_p quantizes P with the block
     scale alone, E4M3(amax(e)/6) per 16 keys, without the row level.
-    with_probs also returns every row's normalized probabilities P and the
+    mx: the MXFP4 variant (mx_quantize for Q, K, V; P in 32-key blocks with
+    the same power-of-two scale rule).  with_probs also returns every row's
+    normalized probabilities P and the
     normalized weights P^ the output uses (float64 [nh, nr, Sk] each), after
     the other results.
 
@@ -277,7 +310,7 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
                                  fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
                                  _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
                                  _ptr(tcnt), _ptr(qr), _ptr(kr), int(bool(single_level_p)),
-                                 _ptr(probs), _ptr(probs_hat))
+                                 _ptr(probs), _ptr(probs_hat), int(bool(mx)))
     if rc != 0:
         raise ValueError("bad attention arguments")
     res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))
