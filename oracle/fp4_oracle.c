@@ -579,6 +579,10 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
       x[j] = S * c;
       if (x[j] > tm) tm = x[j];
     }
+    /* MXFP4 tiles take the power of two at or above the tile maximum as their
+       reference (the row level of P can only be a power of two with E8M0
+       block scales): e = 2^(x - ceil(tm)) in (1/2, 1] at the maximum */
+    if (pmode == 2 && !promoted) tm = ceilf(tm);
     double lsum = 0.0;
     for (int j = 0; j < n; ++j) {
       float z = x[j] - tm;

@@ -141,3 +141,24 @@ def test_smallest_scale_is_a_real_scale():
     r = oracle.mx_quantize(y, 0)
     assert r["scales"][0, 0] == 0 and (r["codes"][0, 0] & 0xF) == 6
     assert oracle.mx_dequantize(r["codes"], r["scales"], 1, 32, 0)[0, 0] == 2.0 ** -125
+
+
+def test_attention_reference_is_the_power_of_two_above_the_tile_maximum():
+    """A tile maximum of 0.5 (score factor 1): the MXFP4 tile reference is
+    ceil(0.5) = 1, so e = 2^-0.5 and 2^-1.5 for scores 0.5 and -0.5; the block
+    maximum 0.7071 has exponent -1, scale 2^-3, t = 5.66 -> 6 (P^ 0.75) and
+    t = 2.83 -> 3 (P^ 0.375).  The denominator sums the e."""
+    d = 32
+    q = torch.zeros(1, 1, 1, d)
+    q[0, 0, 0, 0] = 4.0
+    k = torch.zeros(1, 1, 32, d)
+    k[0, 0, :, 0] = -8.0          # x = -32: e ~ 1e-10, code 0
+    k[0, 0, 0, 0] = 0.125         # x = 0.5
+    k[0, 0, 1, 0] = -0.125        # x = -0.5
+    v = _rand((1, 1, 32, d), 5)
+    out, _ = oracle.attention_fwd(q.to(torch.bfloat16), k.to(torch.bfloat16), v, kv_tile=64,
+                                  softmax_scale=float(np.float32(math.log(2.0))), mx=True)
+    vh = _mxdeq(v[0, 0].float().numpy(), 1)
+    e0, e1 = 2.0 ** -0.5, 2.0 ** -1.5
+    want = (0.75 * vh[0] + 0.375 * vh[1]) / (e0 + e1 + 30 * 2.0 ** -33)
+    np.testing.assert_allclose(out[0, 0], want, atol=1e-6)
