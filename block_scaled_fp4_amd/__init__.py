@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "load", "build", "fp4_version", "fp4_last_error", "fp4_quantize", "fp4_block_topk",
     "fp4_attention_fwd", "fp4_attention_decode", "fp4_kv_cache_append", "fp4_kv_block_sums", "decode_sel_kmax",
-    "fp4_attention_fwd_train", "fp4_attention_bwd",
+    "fp4_attention_fwd_train", "fp4_attention_bwd", "fp4_mx_quantize", "fp4_attention_fwd_mx",
     "FP4Error", "BF16", "FP16", "FP32", "GLOBAL_NONE", "GLOBAL_AMAX", "GLOBAL_GIVEN", "KVCache", "lib_path",
 ]
 
@@ -114,6 +114,12 @@ def load():
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
+    L.fp4_mx_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
+    L.fp4_mx_quantize.restype = C.c_int
+    L.fp4_attention_fwd_mx.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, sz, vp]
+    L.fp4_attention_fwd_mx.restype = C.c_int
+    L.fp4_attention_fwd_mx_workspace_size.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts)]
+    L.fp4_attention_fwd_mx_workspace_size.restype = sz
     L.fp4_attention_fwd_train.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, vp, sz, vp]
     L.fp4_attention_fwd_train.restype = C.c_int
     L.fp4_attention_bwd.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -203,6 +209,24 @@ def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True
     return dict(codes=codes, scales=scales, offsets=offs, g=g)
 
 
+def fp4_mx_quantize(x: torch.Tensor, block_axis: int = 0):
+    """MXFP4 quantization of a 2-D tensor (blocks of 32, E8M0 scales).
+    Returns dict(codes, scales)."""
+    L = load()
+    _dev(x, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if block_axis == 0:
+        cshape, sshape = (rows, cols // 2), (rows, cols // 32)
+    else:
+        cshape, sshape = (rows // 2, cols), (rows // 32, cols)
+    codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    _check(L.fp4_mx_quantize(_ptr(x), _DT[x.dtype], rows, cols, cols, block_axis, _ptr(codes), _ptr(scales),
+                             _stream(dev)))
+    return dict(codes=codes, scales=scales)
+
+
 def _problem(q, k, v, quant=None):
     B, H, Sq, d = q.shape if q is not None else quant["q_shape"]
     Hkv, Sk = (k.shape[1], k.shape[2]) if k is not None else quant["kv_shape"]
@@ -288,6 +312,29 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
     _check(L.fp4_attention_fwd(C.byref(P), C.byref(O), _ptr(out), _ptr(lse), _ptr(idx), _ptr(cnt), _ptr(ws),
                                nws, _stream(dev)))
     return (out, lse, idx, cnt) if return_topk else (out, lse)
+
+
+def fp4_attention_fwd_mx(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, out_dtype=BF16, quantized=None,
+                         return_lse=True, workspace=None, out=None):
+    """MXFP4 attention forward (blocks of 32, power-of-two scales, P quantized
+    per 32 keys against the tile reference ceil(max x)).  q [B,H,Sq,d], k/v
+    [B,Hkv,Sk,d]; quantized: optional dict with q_codes..v_scales from
+    fp4_mx_quantize plus q_shape/kv_shape.  Returns (out, lse)."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    ref = q if q is not None else quantized["q_codes"]
+    dev = ref.device
+    B, H, Sq, d = q.shape if q is not None else quantized["q_shape"]
+    P = _problem(q, k, v, quantized)
+    O = _opts(causal, softmax_scale, kv_tile, False, -2, 6, 0, 128, out_dtype, False)
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
+    nws = L.fp4_attention_fwd_mx_workspace_size(C.byref(P), C.byref(O))
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
+    _check(L.fp4_attention_fwd_mx(C.byref(P), C.byref(O), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(dev)))
+    return out, lse
 
 
 def fp4_attention_fwd_train(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,

@@ -211,6 +211,23 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   return hip_status(fp4i_launch_quantize(L, (hipStream_t)stream), "fp4_quantize launch");
 }
 
+int fp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld, int32_t block_axis,
+                    uint8_t* codes, uint8_t* scales, void* stream) {
+  const char* fn = "fp4_mx_quantize";
+  if (dtype != FP4_BF16 && dtype != FP4_FP16 && dtype != FP4_FP32) return fail(FP4_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (block_axis != 0 && block_axis != 1) return fail(FP4_ERR_INVALID_ARG, "%s: block_axis must be 0 or 1", fn);
+  if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "%s: bad shape/ld", fn);
+  if (block_axis == 0 && cols % 32) return fail(FP4_ERR_INVALID_ARG, "%s: cols %% 32 != 0", fn);
+  if (block_axis == 1 && rows % 32) return fail(FP4_ERR_INVALID_ARG, "%s: rows %% 32 != 0", fn);
+  if (rows > 0 && cols > 0 && (!x || !codes || !scales)) return fail(FP4_ERR_INVALID_ARG, "%s: x, codes, scales required", fn);
+  if ((x && !aligned16(x)) || (codes && !aligned16(codes)))
+    return fail(FP4_ERR_INVALID_ARG, "%s: x and codes must be 16-byte aligned", fn);
+  const size_t esz = dtype == FP4_FP32 ? 4 : 2;
+  if (block_axis == 0 && ld > cols && ((ld * esz) % 16)) return fail(FP4_ERR_INVALID_ARG, "%s: row stride must keep 16-byte alignment", fn);
+  return hip_status(fp4i_launch_mx_quantize(x, dtype, rows, cols, ld, block_axis, codes, scales, (hipStream_t)stream),
+                    "fp4_mx_quantize launch");
+}
+
 size_t fp4_attention_fwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
   if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
     return 0;
@@ -357,6 +374,56 @@ int fp4_attention_fwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, v
   if (st) return st;
   if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "fp4_attention_fwd: out must be non-NULL and 16-byte aligned");
   return attention_fwd_impl(prob, opts, out, nullptr, lse, topk_idx, topk_cnt, workspace, workspace_bytes, stream);
+}
+
+size_t fp4_attention_fwd_mx_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {
+  if (!prob || !opts || prob->struct_size < sizeof(fp4_attn_problem) || opts->struct_size < sizeof(fp4_attn_opts))
+    return 0;
+  if (prob->q_codes && prob->q_scales && prob->k_codes && prob->k_scales && prob->v_codes && prob->v_scales) return 0;
+  const size_t nq = (size_t)(prob->B * prob->H * prob->Sq * prob->d), nk = (size_t)(prob->B * prob->Hkv * prob->Sk * prob->d);
+  return align256(nq / 2) + align256(nq / 32) + 2 * (align256(nk / 2) + align256(nk / 32));
+}
+
+int fp4_attention_fwd_mx(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "fp4_attention_fwd_mx";
+  int st = check_attn(prob, opts, fn, false);
+  if (st) return st;
+  if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_INVALID_ARG, "%s: no FP16 path (fp16_budget_pct must be 0)", fn);
+  if (opts->hadamard_qk) return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk must be 0", fn);
+  if (prob->Sk % 32) return fail(FP4_ERR_INVALID_ARG, "%s: Sk %% 32 != 0", fn);
+  if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "%s: out must be non-NULL and 16-byte aligned", fn);
+  const size_t need = fp4_attention_fwd_mx_workspace_size(prob, opts);
+  if (workspace_bytes < need || (need && !workspace)) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t B = prob->B, H = prob->H, Hkv = prob->Hkv, Sq = prob->Sq, Sk = prob->Sk, d = prob->d;
+  MxAttnLaunch A;
+  A.qc = prob->q_codes; A.qs = prob->q_scales; A.kc = prob->k_codes; A.ks = prob->k_scales;
+  A.vc = prob->v_codes; A.vs = prob->v_scales;
+  if (need) {
+    char* ws = (char*)workspace;
+    const size_t nq = (size_t)(B * H * Sq * d), nk = (size_t)(B * Hkv * Sk * d);
+    uint8_t* qc = (uint8_t*)ws;
+    uint8_t* qs = qc + align256(nq / 2);
+    uint8_t* kc = qs + align256(nq / 32);
+    uint8_t* ks = kc + align256(nk / 2);
+    uint8_t* vc = ks + align256(nk / 32);
+    uint8_t* vs = vc + align256(nk / 2);
+    hipError_t e = fp4i_launch_mx_quantize(prob->q, prob->dtype, B * H * Sq, d, d, 0, qc, qs, s);
+    if (e == hipSuccess) e = fp4i_launch_mx_quantize(prob->k, prob->dtype, B * Hkv * Sk, d, d, 0, kc, ks, s);
+    // V blocks run along tokens; 32-token blocks never straddle heads (Sk % 32 == 0)
+    if (e == hipSuccess) e = fp4i_launch_mx_quantize(prob->v, prob->dtype, B * Hkv * Sk, d, d, 1, vc, vs, s);
+    if (e != hipSuccess) return hip_status(e, "fp4_attention_fwd_mx quantize launch");
+    A.qc = qc; A.qs = qs; A.kc = kc; A.ks = ks; A.vc = vc; A.vs = vs;
+  }
+  A.B = B; A.H = H; A.Hkv = Hkv; A.Sq = Sq; A.Sk = Sk; A.d = d;
+  A.causal = opts->causal;
+  A.c = score_factor(opts->softmax_scale, d);
+  A.kv_tile = opts->kv_tile;
+  A.out_dtype = opts->out_dtype;
+  A.out = out;
+  A.lse = lse;
+  return hip_status(fp4i_launch_attn_mx(A, s), "fp4_attention_fwd_mx launch");
 }
 
 size_t fp4_attention_bwd_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts) {

@@ -20,7 +20,24 @@ struct QuantLaunch {
 };
 
 int fp4i_amax_parts(int64_t rows, int64_t cols);
+hipError_t fp4i_launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream);
+
+// MXFP4 attention forward: Q, K codes [.., d/2] with E8M0 scales [.., d/32]
+// (blocks along d), V codes [.., Sk/2, d] with scales [.., Sk/32, d] (blocks
+// along tokens); Sk % 32 == 0.
+struct MxAttnLaunch {
+  int64_t B, H, Hkv, Sq, Sk, d;
+  const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
+  int causal;
+  float c;  // log2(e) * softmax_scale
+  int kv_tile;
+  int out_dtype;
+  void* out;
+  float* lse;
+};
+hipError_t fp4i_launch_attn_mx(const MxAttnLaunch& L, hipStream_t stream);
 
 struct TopkLaunch {
   const void* q;  // [B,H,Sq,d]

@@ -264,6 +264,94 @@ __global__ void __launch_bounds__(256) amax_kernel(const T* x, int64_t rows, int
 
 __global__ void set_one_kernel(float* g) { *g = 1.0f; }
 
+// ---- MXFP4: E2M1 elements, one power-of-two (E8M0) scale per 32 ----------
+// (the block floating point the ScaleSearch page contrasts NVFP4 with,
+// Declaracion del Problema), scale rule of the OCP microscaling format:
+// shared exponent floor(log2(amax)) - 2, clamped to [-127, 127], elements
+// RNE-rounded to E2M1 with saturation at 6 (so [6, 8) x scale clips to 6).
+
+struct MxArgs {
+  const void* x;
+  int64_t rows, cols, ld;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+// 32 values -> 16 code bytes (4 dwords, element 2i in the low nibble) and the
+// scale byte.
+__device__ __forceinline__ void mx_block(const float (&y)[32], uint32_t (&c)[4], uint32_t& sb) {
+  uint32_t abits = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) abits = __builtin_elementwise_max(abits, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+  uint32_t sgn[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) sgn[i >> 3] |= (__float_as_uint(y[i]) >> 31) << (4 * (i & 7) + 3);
+  if (abits >= 0x7F800000u) {  // Inf or NaN in the block
+    sb = 0xFFu;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c[w] = 0u;
+    return;
+  }
+  int shared = -127;
+  if (abits) {
+    shared = __builtin_amdgcn_frexp_expf(__uint_as_float(abits)) - 3;  // floor(log2 a) - 2
+    shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
+  }
+  sb = (uint32_t)(shared + 127);
+  float t[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) t[i] = __builtin_ldexpf(__builtin_fabsf(y[i]), -shared);  // exact: power of two
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t v = 0;
+    v = cvt_pk_fp4<0>(v, t[8 * w + 0], t[8 * w + 1]);
+    v = cvt_pk_fp4<1>(v, t[8 * w + 2], t[8 * w + 3]);
+    v = cvt_pk_fp4<2>(v, t[8 * w + 4], t[8 * w + 5]);
+    v = cvt_pk_fp4<3>(v, t[8 * w + 6], t[8 * w + 7]);
+    c[w] = v | sgn[w];
+  }
+}
+
+// One lane per block of 32 consecutive elements of a row.
+template <typename T>
+__global__ void __launch_bounds__(256) mx_quantize_axis0_kernel(MxArgs A) {
+  const int64_t bpr = A.cols / 32;
+  const int64_t nb = A.rows * bpr;
+  const T* x = reinterpret_cast<const T*>(A.x);
+  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nb; blk += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = blk / bpr, cb = blk - r * bpr;
+    const T* src = x + r * A.ld + cb * 32;
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load8<T>(src + 8 * i, y + 8 * i);
+    uint32_t c[4], sb;
+    mx_block(y, c, sb);
+    *reinterpret_cast<uint4_t*>(A.codes + r * (A.cols / 2) + cb * 16) = uint4_t{c[0], c[1], c[2], c[3]};
+    A.scales[blk] = (uint8_t)sb;
+  }
+}
+
+// One lane per block of 32 rows of one column (consecutive lanes, consecutive
+// columns).
+template <typename T>
+__global__ void __launch_bounds__(256) mx_quantize_axis1_kernel(MxArgs A) {
+  const int64_t nb = (A.rows / 32) * A.cols;
+  const T* x = reinterpret_cast<const T*>(A.x);
+  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nb; blk += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rb = blk / A.cols, c = blk - rb * A.cols;
+    float y[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) y[k] = load_elem<T>(x + (rb * 32 + k) * A.ld + c);
+    uint32_t cw[4], sb;
+    mx_block(y, cw, sb);
+    // row pair (2i, 2i+1) -> byte i of the block's 16 bytes, at codes[(rb*16 + i)*cols + c]
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      A.codes[(rb * 16 + i) * A.cols + c] = (uint8_t)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    A.scales[blk] = (uint8_t)sb;
+  }
+}
+
 }  // namespace fp4dev
 
 using namespace fp4dev;
@@ -331,6 +419,26 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
     if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis1_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
     else if (L.dtype == 1) hipLaunchKernelGGL(quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
     else hipLaunchKernelGGL(quantize_axis1_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
+  }
+  return hipGetLastError();
+}
+
+hipError_t fp4i_launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  MxArgs A;
+  A.x = x; A.rows = rows; A.cols = cols; A.ld = ld; A.codes = codes; A.scales = scales;
+  const int64_t work = axis == 0 ? rows * (cols / 32) : (rows / 32) * cols;
+  if (work == 0) return hipSuccess;
+  int64_t grid = (work + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  if (axis == 0) {
+    if (dtype == 0) hipLaunchKernelGGL(mx_quantize_axis0_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
+    else if (dtype == 1) hipLaunchKernelGGL(mx_quantize_axis0_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
+    else hipLaunchKernelGGL(mx_quantize_axis0_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
+  } else {
+    if (dtype == 0) hipLaunchKernelGGL(mx_quantize_axis1_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
+    else if (dtype == 1) hipLaunchKernelGGL(mx_quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
+    else hipLaunchKernelGGL(mx_quantize_axis1_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
   }
   return hipGetLastError();
 }

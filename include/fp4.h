@@ -120,6 +120,23 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
 
 size_t fp4_quantize_workspace_size(int64_t rows, int64_t cols, const fp4_quant_opts* opts);
 
+/*
+ * MXFP4 variant: E2M1 elements with one power-of-two scale per 32 elements
+ * (the block floating point the ScaleSearch page contrasts NVFP4 with,
+ * Declaracion del Problema; the operand format of gfx950's FP4 matrix
+ * instructions).  Scale byte = E8M0 (value 2^(byte - 127)) with the OCP
+ * microscaling rule: exponent floor(log2(amax)) - 2 clamped to [-127, 127]
+ * (byte 0 for an all-zero block, 0xFF for a block holding Inf/NaN, whose
+ * codes are then 0); elements |x| / 2^exponent rounded to the nearest E2M1
+ * value (ties to the even code, saturating at 6), sign bit copied.
+ * Layouts as fp4_quantize with blocks of 32: block_axis 0 -> codes
+ * [rows, cols/2], scales [rows, cols/32]; block_axis 1 -> codes
+ * [rows/2, cols], scales [rows/32, cols].  No offset search, no per-tensor
+ * scale, no workspace.
+ */
+int fp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld, int32_t block_axis,
+                    uint8_t* codes, uint8_t* scales, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Attention forward -- ScaleSearch page, Metodologia / ScaleSearchAttention; */
 /* ThriftAttention page, Metodologia / 1 and 2                               */
@@ -204,6 +221,28 @@ int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int3
                    int32_t* topk_cnt, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
+
+/*
+ * MXFP4 variant of the forward (blocks of 32 with power-of-two scales, the
+ * format the ScaleSearch page contrasts NVFP4 with, Declaracion del Problema;
+ * gfx950's FP4 matrix instructions take its scales natively).  Q and K are
+ * quantized with fp4_mx_quantize along d, V along tokens; per (query row, key
+ * tile) x = fl32(S * log2(e) * scale), the tile reference is ceil(max x) (a
+ * power of two that the E8M0 block scales can carry), e = 2^(x - ceil(max
+ * x)), and each 32-key block of e is quantized by the rule of
+ * fp4_mx_quantize; the tile adds P^ V^, tiles merge by online softmax over
+ * the unquantized e.  Uses prob (q, k, v, or all six operands from
+ * fp4_mx_quantize: q codes [B,H,Sq,d/2] scales [B,H,Sq,d/32], k codes
+ * [B,Hkv,Sk,d/2] scales [B,Hkv,Sk,d/32], v codes [B,Hkv,Sk/2,d] scales
+ * [B,Hkv,Sk/32,d]) and opts' causal, softmax_scale, kv_tile and out_dtype;
+ * fp16_budget_pct and hadamard_qk must be 0, p_single_level and the scale
+ * search fields are ignored.  Requirements as fp4_attention_fwd with
+ * Sk % 32 == 0.  out, lse as fp4_attention_fwd.
+ */
+int fp4_attention_fwd_mx(const fp4_attn_problem* prob, const fp4_attn_opts* opts, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fp4_attention_fwd_mx_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
 
 /* ------------------------------------------------------------------------ */
 /* Training -- Attn-QAT page, Metodologia / A (principles: P recomputed in    */

@@ -184,3 +184,27 @@ def test_hadamard_options_are_validated(L):
     quant = dict(q_codes=f, q_scales=f, k_codes=f, k_scales=f, v_codes=f, v_scales=f)
     assert call(_prob(fp4, **quant), _opts(fp4, hadamard_qk=1)) == -1
     assert call(_prob(fp4), _opts(fp4, hadamard_qk=3)) == -1
+
+
+def test_mx_entry_points_validate(L):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+    assert L.fp4_mx_quantize(f, 0, 16, 48, 48, 0, f, f, None) == -1      # cols % 32
+    assert L.fp4_mx_quantize(f, 0, 48, 32, 32, 1, f, f, None) == -1      # rows % 32 along rows
+    assert L.fp4_mx_quantize(f, 5, 32, 32, 32, 0, f, f, None) == -1      # dtype
+    assert L.fp4_mx_quantize(f, 0, 32, 32, 32, 2, f, f, None) == -1      # axis
+    assert L.fp4_mx_quantize(C.c_void_p((1 << 20) + 4), 0, 32, 32, 32, 0, f, f, None) == -1
+
+    def call(P, O, ws=1 << 40):
+        return L.fp4_attention_fwd_mx(C.byref(P), C.byref(O), f, None, f, ws, None)
+
+    assert call(_prob(fp4, Sq=272, Sk=272), _opts(fp4)) == -1                  # Sk % 32
+    assert call(_prob(fp4), _opts(fp4, fp16_budget_pct=10)) == -1              # no FP16 path
+    assert call(_prob(fp4), _opts(fp4, hadamard_qk=1)) == -1
+    assert call(_prob(fp4, d=96), _opts(fp4)) == -2
+    need = L.fp4_attention_fwd_mx_workspace_size(C.byref(_prob(fp4)), C.byref(_opts(fp4)))
+    nq = 2 * 256 * 128
+    assert need >= nq // 2 + nq // 32 + 2 * (nq // 2 + nq // 32)
+    assert call(_prob(fp4), _opts(fp4), need - 1) == -3
+    quant = dict(q_codes=f, q_scales=f, k_codes=f, k_scales=f, v_codes=f, v_scales=f)
+    assert L.fp4_attention_fwd_mx_workspace_size(C.byref(_prob(fp4, **quant)), C.byref(_opts(fp4))) == 0
