@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "FP4 attention fwd TFLOP/s (S=8K/32K, d=128) + quantizer GB/s, % of roofline"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 FP16_MFMA_PEAK_TF = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+FP4_MFMA_PEAK_TF = 10100.0  # MI355X dense FP4 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -325,6 +326,39 @@ def bench_train(fp4, synth, torch, n):
                                    "note": "causal half counted; products skip the tiles above the diagonal"})
 
 
+def bench_mx(fp4, synth, torch, n):
+    """MXFP4 variant of the prefill (blocks of 32, power-of-two scales) on the
+    block-scaled FP4 matrix instructions: B=1 H=32 d=128 causal at S=8192 and
+    32768, kv_tile 64 and 128; end to end (MX quantization of Q/K/V plus the
+    attention) and the attention kernel alone."""
+    res = {}
+    timer = Timer(torch)
+    for S in (8192, 32768):
+        B, H, d = 1, 32, 128
+        q, k, v = (t.cuda() for t in synth.prefill(S=S))
+        out = torch.empty_like(q)
+        fl = attn_flops(B, H, S, d)
+        mq = fp4.fp4_mx_quantize(q.view(-1, d), 0)
+        mk = fp4.fp4_mx_quantize(k.view(-1, d), 0)
+        mv = fp4.fp4_mx_quantize(v.view(-1, d), 1)
+        quant = dict(q_codes=mq["codes"], q_scales=mq["scales"], k_codes=mk["codes"], k_scales=mk["scales"],
+                     v_codes=mv["codes"], v_scales=mv["scales"], q_shape=(B, H, S, d), kv_shape=(k.shape[1], S))
+        r = {}
+        for kvt in (64, 128):
+            e2e = timer.run(lambda: fp4.fp4_attention_fwd_mx(q, k, v, causal=True, kv_tile=kvt, out_dtype=fp4.BF16,
+                                                             return_lse=False, out=out), n)
+            kern = timer.run(lambda: fp4.fp4_attention_fwd_mx(None, None, None, causal=True, kv_tile=kvt,
+                                                              out_dtype=fp4.BF16, quantized=quant, return_lse=False,
+                                                              out=out), n)
+            r[f"kv_tile_{kvt}"] = dict(end_to_end_ms=round(e2e, 4), end_to_end_tflops=round(fl / e2e / 1e9, 1),
+                                       attn_kernel_ms=round(kern, 4), attn_kernel_tflops=round(fl / kern / 1e9, 1),
+                                       attn_kernel_frac_fp4_mfma=round(fl / kern / 1e9 / FP4_MFMA_PEAK_TF, 4))
+        res[f"S{S}"] = r
+        del q, k, v, out, quant, mq, mk, mv
+    res["workload"] = "MXFP4 prefill B=1 H=32 d=128 causal, bf16 inputs as the prefill workload, no FP16 path"
+    return res
+
+
 def bench_kv_append(fp4, torch, n):
     """Quantize-on-write of 16 tokens per (batch, kv head) into the decode workload's cache."""
     B, Hkv, d, n_recent, cap = 16, 8, 128, 256, 130688
@@ -466,6 +500,8 @@ def main():
         line["components"]["decode"] = bench_decode(fp4, synth, torch, max(5, args.steps))
         log("components: kv append")
         line["components"]["kv_append"] = bench_kv_append(fp4, torch, max(10, args.steps))
+        log("components: MXFP4 prefill")
+        line["components"]["mxfp4"] = bench_mx(fp4, synth, torch, max(5, args.steps))
         log("components: training step")
         line["components"]["train"] = bench_train(fp4, synth, torch, max(3, args.steps // 3))
     if not args.no_cpu_baseline:
