@@ -11,13 +11,15 @@
 //   dQ = dS K^,   dK = dS^T Q^,             s = c ln 2.
 // The score-sized matrices are materialized (one float per query/key pair
 // for P, then dS in place, one for P^), so the workspace grows with
-// B H Sq Sk; the products are batched fp32 GEMMs (64 x 64 tiles, LDS
-// staged), and the query heads of a kv head are consecutive rows of one GEMM
-// for dK and dV.
+// B H Sq Sk; the products are batched GEMMs on the bf16 MFMA with binary32
+// accuracy (128 x 128 tiles, LDS staged), and the query heads of a kv head
+// are consecutive rows of one GEMM for dK and dV.
 #include "device_common.h"
 #include "fp4_internal.h"
 
 namespace fp4dev {
+
+constexpr int kGT = 128;  // output tile (M and N) of the products
 
 // ---- operands in fp32 ----------------------------------------------------
 
@@ -121,7 +123,7 @@ struct ProbArgs {
 };
 
 // One workgroup per query row; a thread takes 16 consecutive keys (one P
-// block).  Pass 1: block maxima of x = fl32(S c) into LDS; pass 2: the tile
+// block) up to the row's last key the products read.  Pass 1: block maxima of x = fl32(S c) into LDS; pass 2: the tile
 // maximum tm from its blocks, e = 2^(x - tm), the block scale and codes, and
 // P = 2^(x - lse2), P^ = v s2 2^(tm - lse2) (/2688 two-level).
 __global__ void __launch_bounds__(256) probs_kernel(ProbArgs A) {
@@ -129,7 +131,11 @@ __global__ void __launch_bounds__(256) probs_kernel(ProbArgs A) {
   const int64_t row = blockIdx.x;
   const int64_t q = row % A.Sq;
   const int64_t nvis = A.causal ? (q + 1 < A.Sk ? q + 1 : A.Sk) : A.Sk;
-  const int nblk = (int)(A.Sk / 16);
+  // Under the causal mask the products read a row only up to the end of its
+  // kGT-key tile (they skip the tiles above the diagonal): entries past it are
+  // neither written nor read.
+  const int64_t jend = A.causal && (q / kGT + 1) * kGT < A.Sk ? (q / kGT + 1) * kGT : A.Sk;
+  const int nblk = (int)(jend / 16);
   float* srow = A.S + row * A.Sk;
   float* prow = A.Phat + row * A.Sk;
   const float lse2 = A.lse[row] * 1.4426950408889634f;
@@ -197,7 +203,16 @@ __global__ void __launch_bounds__(256) probs_kernel(ProbArgs A) {
   }
 }
 
-// ---- batched fp32 GEMM ----------------------------------------------------
+// ---- batched GEMM on the bf16 MFMA -----------------------------------------
+//
+// The products keep binary32 accuracy on the bf16 matrix instructions: an
+// operand whose values are bf16 numbers (the dequantized NVFP4 Q^, K^, V^ --
+// an E2M1 value times an E4M3 scale has at most 6 significant bits -- and dO
+// given in bf16) goes in as it is; an fp32 operand (P^, dS, dO given in
+// fp16) is split as x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi),
+// |r| <= 2^-17 |x|, and each product takes hi.hi + hi.lo + lo.hi (the lo.lo
+// term is below 2^-16 of the product).  Products are exact in the MFMA and
+// accumulate in fp32.
 
 struct GemmArgs {
   const float* A;
@@ -216,69 +231,180 @@ struct GemmArgs {
   int64_t Sq;
 };
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kGK = 32;   // k slice
+constexpr int kGRow = kGK + 8;  // LDS row: 32 bf16 + 8 of padding (80 bytes)
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite values only
+}
+
+// 4 fp32 -> 4 bf16 hi (and lo when SPLIT), packed two per dword
+template <bool SPLIT>
+__device__ __forceinline__ void split4(const float4_t& x, uint2_t& hi, uint2_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = bf16_rne_bits(x[i]);
+    l[i] = SPLIT ? bf16_rne_bits(x[i] - __uint_as_float(h[i] << 16)) : 0u;  // the difference is exact
+  }
+  hi = uint2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = uint2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// One operand's slice: kGT rows (m or n) x kGK k, 16 values per thread.
+// KC (k contiguous in memory, element (r, k) at X[r*ld + k]): thread t reads
+// row t/8 + 32i, k 4(t%8)..+3.  RC (rows contiguous, element (r, k) at
+// X[k*ld + r]): thread t reads rows 4(t%32)..+3 at k 4(t/32)+i and
+// transposes in registers.
+template <bool RC>
+struct OpSlice {
+  float4_t v[4];
+  __device__ __forceinline__ void load(const float* X, int64_t ld, int64_t r0, int64_t rows, int64_t k0, int64_t kend) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!RC) {
+        const int64_t r = r0 + t / 8 + 32 * i, k = k0 + 4 * (t % 8);
+        v[i] = (r < rows && k < kend) ? *reinterpret_cast<const float4_t*>(X + r * ld + k) : float4_t{0, 0, 0, 0};
+      } else {
+        const int64_t r = r0 + 4 * (t % 32), k = k0 + 4 * (t / 32) + i;
+        v[i] = (r < rows && k < kend) ? *reinterpret_cast<const float4_t*>(X + k * ld + r) : float4_t{0, 0, 0, 0};
+      }
+    }
+  }
+  template <bool SPLIT>
+  __device__ __forceinline__ void store(uint16_t* hiS, uint16_t* loS) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4_t x;
+      int r, k;
+      if (!RC) {
+        x = v[i];
+        r = t / 8 + 32 * i;
+        k = 4 * (t % 8);
+      } else {
+        x = float4_t{v[0][i], v[1][i], v[2][i], v[3][i]};  // row 4(t%32)+i, k 4(t/32)..+3
+        r = 4 * (t % 32) + i;
+        k = 4 * (t / 32);
+      }
+      uint2_t h, l;
+      split4<SPLIT>(x, h, l);
+      *reinterpret_cast<uint2_t*>(hiS + r * kGRow + k) = h;
+      if (SPLIT) *reinterpret_cast<uint2_t*>(loS + r * kGRow + k) = l;
+    }
+  }
+};
+
+__device__ __forceinline__ float16_t mfma_bf16(const uint4_t& a, const uint4_t& b, const float16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
 // C[z] = op(A) op(B): op(A) is M x K (TA: A stored K x M), op(B) is K x N (TB:
-// B stored N x K).  64 x 64 tile per workgroup, 16-deep k slices through LDS,
-// 4 x 4 outputs per thread.
-template <bool TA, bool TB, int EPI>
-__global__ void __launch_bounds__(256) sgemm_kernel(GemmArgs g) {
-  __shared__ float As[16][68];
-  __shared__ float Bs[16][68];
+// B stored N x K).  128 x 128 tile per workgroup (4 waves of 64 x 64, each
+// 2 x 2 products of 32 x 32), 32-deep k slices through LDS; the next slice's
+// loads are in flight while the current one computes.
+template <bool TA, bool TB, int EPI, bool SA, bool SB>
+__global__ void __launch_bounds__(256) mgemm_kernel(GemmArgs g) {
+  __shared__ uint16_t Ah[kGT * kGRow], Bh[kGT * kGRow];
+  __shared__ uint16_t Al[SA ? kGT * kGRow : 1], Bl[SB ? kGT * kGRow : 1];
   const int64_t z = blockIdx.z;
   const float* A = g.A + (z / g.gA) * g.sA;
   const float* B = g.B + (z / g.gB) * g.sB;
   float* C = g.C + z * g.sC;
-  const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-  if (g.causal == 1 && n0 > m0 + 63) return;  // every key after every query of the tile
-  const int64_t kend = g.causal == 2 && m0 + 64 < g.K ? m0 + 64 : g.K;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4];
+  const int64_t m0 = (int64_t)blockIdx.y * kGT, n0 = (int64_t)blockIdx.x * kGT;
+  if (g.causal == 1 && n0 > m0 + kGT - 1) return;  // every key after every query of the tile
+  const int64_t kend = g.causal == 2 && m0 + kGT < g.K ? m0 + kGT : g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5, r32 = lane & 31;
+  float16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int64_t k0 = 0; k0 < kend; k0 += 16) {
-    if (g.causal == 3 && (k0 % g.Sq) + 15 < m0) continue;  // (uniform: the same for the whole workgroup)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int mm = TA ? (e & 63) : (e >> 4), ka = TA ? (e >> 6) : (e & 15);
-      const int64_t gm = m0 + mm, gk = k0 + ka;
-      As[ka][mm] = (gm < g.M && gk < kend) ? (TA ? A[gk * g.lda + gm] : A[gm * g.lda + gk]) : 0.0f;
-      const int nn = TB ? (e >> 4) : (e & 63), kb = TB ? (e & 15) : (e >> 6);
-      const int64_t gn = n0 + nn, gkb = k0 + kb;
-      Bs[kb][nn] = (gn < g.N && gkb < kend) ? (TB ? B[gn * g.ldb + gkb] : B[gkb * g.ldb + gn]) : 0.0f;
+    for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{0};
+  // first slice that is not all zero (mode 3: queries of the slice all before the tile's first key)
+  auto skip = [&](int64_t k0) { return g.causal == 3 && (k0 % g.Sq) + kGK - 1 < m0; };
+  OpSlice<TA> sa;      // A rows are m: contiguous along m when A is stored K x M
+  OpSlice<!TB> sb;     // B rows are n: contiguous along n when B is stored K x N
+  int64_t k0 = 0;
+  while (k0 < kend && skip(k0)) k0 += kGK;
+  if (k0 < kend) {
+    sa.load(A, g.lda, m0, g.M, k0, kend);
+    sb.load(B, g.ldb, n0, g.N, k0, kend);
+  }
+  while (k0 < kend) {
+    __syncthreads();  // the previous slice's LDS reads are done
+    sa.template store<SA>(Ah, Al);
+    sb.template store<SB>(Bh, Bl);
+    int64_t kn = k0 + kGK;
+    while (kn < kend && skip(kn)) kn += kGK;
+    if (kn < kend) {
+      sa.load(A, g.lda, m0, g.M, kn, kend);
+      sb.load(B, g.ldb, n0, g.N, kn, kend);
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float4_t a = *reinterpret_cast<const float4_t*>(&As[kk][4 * ty]);
-      const float4_t b = *reinterpret_cast<const float4_t*>(&Bs[kk][4 * tx]);
+    for (int kk = 0; kk < kGK / 16; ++kk) {
+      const int ko = 16 * kk + 8 * hi;
+      uint4_t ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i) {
+        const int ra = (2 * wm + i) * 32 + r32, rb = (2 * wn + i) * 32 + r32;
+        ah[i] = *reinterpret_cast<const uint4_t*>(Ah + ra * kGRow + ko);
+        bh[i] = *reinterpret_cast<const uint4_t*>(Bh + rb * kGRow + ko);
+        if (SA) al[i] = *reinterpret_cast<const uint4_t*>(Al + ra * kGRow + ko);
+        if (SB) bl[i] = *reinterpret_cast<const uint4_t*>(Bl + rb * kGRow + ko);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
+          if (SB) acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
+          if (SA) acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
+        }
     }
-    __syncthreads();
+    k0 = kn;
   }
+  // C layout of a 32 x 32 product: lane column r32, rows 8(v/4) + 4 hi + v%4
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = m0 + 4 * ty + i;
-    if (r >= g.M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t cidx = n0 + 4 * tx + j;
-      if (cidx >= g.N) continue;
-      float* p = C + r * g.ldc + cidx;
-      if (EPI == 0) *p = acc[i][j];
-      else *p = g.alpha * *p * (acc[i][j] - g.D[z * g.M + r]);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + (2 * wn + j) * 32 + r32;
+      if (col >= g.N) continue;
+      const int64_t rb = m0 + (2 * wm + i) * 32 + 4 * hi;
+      if (EPI == 1) {  // every load first, then the stores: the reads of P stay in flight together
+        float pv[16], dv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rb + 8 * (v / 4) + (v % 4);
+          pv[v] = row < g.M ? C[row * g.ldc + col] : 0.0f;
+          dv[v] = row < g.M ? g.D[z * g.M + row] : 0.0f;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rb + 8 * (v / 4) + (v % 4);
+          if (row < g.M) C[row * g.ldc + col] = g.alpha * pv[v] * (acc[i][j][v] - dv[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rb + 8 * (v / 4) + (v % 4);
+          if (row < g.M) C[row * g.ldc + col] = acc[i][j][v];
+        }
+      }
     }
-  }
 }
 
-template <bool TA, bool TB, int EPI>
+template <bool TA, bool TB, int EPI, bool SA, bool SB>
 hipError_t gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
-  const dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)batch);
-  hipLaunchKernelGGL((sgemm_kernel<TA, TB, EPI>), grid, dim3(256), 0, st, g);
+  const dim3 grid((unsigned)((g.N + kGT - 1) / kGT), (unsigned)((g.M + kGT - 1) / kGT), (unsigned)batch);
+  hipLaunchKernelGGL((mgemm_kernel<TA, TB, EPI, SA, SB>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
@@ -296,6 +422,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   auto a = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const int64_t B = L.B, H = L.H, Hkv = L.Hkv, Sq = L.Sq, Sk = L.Sk, d = L.d, G = H / Hkv;
   const size_t nq = (size_t)(B * H * Sq), nk = (size_t)(B * Hkv * Sk);
+  const bool fp16_do = L.dtype == 1;  // dO in fp16 is not a bf16 number: split it
   char* w = (char*)L.ws;
   float* qh = (float*)w; w += a(nq * d * 4);
   float* dof = (float*)w; w += a(nq * d * 4);
@@ -329,7 +456,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
   g.M = Sq; g.N = Sk; g.K = d;
   g.causal = L.causal ? 1 : 0;
-  hipError_t e = gemm<false, true, 0>(g, B * H, st);
+  hipError_t e = gemm<false, true, 0, false, false>(g, B * H, st);
   if (e != hipSuccess) return e;
   // P and P^
   ProbArgs pa;
@@ -345,7 +472,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.M = Sk; g.N = d; g.K = G * Sq;
   g.causal = L.causal ? 3 : 0;
   g.Sq = Sq;
-  if ((e = gemm<true, false, 0>(g, B * Hkv, st)) != hipSuccess) return e;
+  if ((e = (fp16_do ? gemm<true, false, 0, true, true>(g, B * Hkv, st) : gemm<true, false, 0, true, false>(g, B * Hkv, st))) != hipSuccess) return e;
   // dS = s P (dO V^T - D), written over P
   g = GemmArgs{};
   g.A = dof; g.lda = d; g.sA = Sq * d; g.gA = 1;
@@ -355,7 +482,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.alpha = L.c * 0.69314718055994531f;
   g.D = Dv;
   g.causal = L.causal ? 1 : 0;  // skipped tiles keep P = 0, which is dS there
-  if ((e = gemm<false, true, 1>(g, B * H, st)) != hipSuccess) return e;
+  if ((e = (fp16_do ? gemm<false, true, 1, true, false>(g, B * H, st) : gemm<false, true, 1, false, false>(g, B * H, st))) != hipSuccess) return e;
   // dQ = dS K^
   g = GemmArgs{};
   g.A = Sb; g.lda = Sk; g.sA = Sq * Sk; g.gA = 1;
@@ -363,7 +490,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.C = L.dq; g.ldc = d; g.sC = Sq * d;
   g.M = Sq; g.N = d; g.K = Sk;
   g.causal = L.causal ? 2 : 0;
-  if ((e = gemm<false, false, 0>(g, B * H, st)) != hipSuccess) return e;
+  if ((e = gemm<false, false, 0, true, false>(g, B * H, st)) != hipSuccess) return e;
   // dK = dS^T Q^ over the G query heads of each kv head
   g = GemmArgs{};
   g.A = Sb; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
@@ -372,5 +499,5 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.M = Sk; g.N = d; g.K = G * Sq;
   g.causal = L.causal ? 3 : 0;
   g.Sq = Sq;
-  return gemm<true, false, 0>(g, B * Hkv, st);
+  return gemm<true, false, 0, true, false>(g, B * Hkv, st);
 }

@@ -27,6 +27,8 @@ def _close_grad(got, ref, what):
     (256, 64, 2, 2, True, 128, False, torch.bfloat16),
     (208, 128, 4, 2, False, 64, False, torch.bfloat16),   # ragged length, GQA
     (192, 128, 2, 1, True, 64, True, torch.float16),      # single-level P, fp16 inputs
+    (1040, 128, 2, 2, True, 128, False, torch.bfloat16),  # several 128-tiles of every product, ragged tail
+    (336, 64, 4, 1, False, 128, False, torch.float16),    # fp16 dO split in both GEMMs that read it, G = 4
 ])
 def test_train_step(gpu, S, d, H, Hkv, causal, kv_tile, single, dt):
     q, k, v = synth.qkv(1, H, S, d, dt, seed=120 + S, Hkv=Hkv, k_outliers=2)
