@@ -9,11 +9,11 @@
 // quantization of e = 2^(x - tm), rescaled by 2^(tm - lse2)):
 //   dV = P^T dO,  dS = s P * (dO V^T - D),  D = rowsum(dO * O'),
 //   dQ = dS K^,   dK = dS^T Q^,             s = c ln 2.
-// The score-sized matrices are materialized (one float per query/key pair
-// for P, then dS in place, one for P^), so the workspace grows with
-// B H Sq Sk; the products are batched GEMMs on the bf16 MFMA with binary32
-// accuracy (128 x 128 tiles, LDS staged), and the query heads of a kv head
-// are consecutive rows of one GEMM for dK and dV.
+// One pass recomputes the scores and writes P^ and dS (one float per
+// query/key pair each, so the workspace grows with B H Sq Sk); dV, dQ and dK
+// are batched GEMMs on the bf16 MFMA with binary32 accuracy (128 x 128 tiles,
+// LDS staged), the query heads of a kv head being consecutive rows of one
+// GEMM for dK and dV.
 #include "device_common.h"
 #include "fp4_internal.h"
 
@@ -113,96 +113,6 @@ struct TrainPTable {
 };
 __constant__ TrainPTable kTrainP = TrainPTable();
 
-struct ProbArgs {
-  float* S;      // [rows][Sk]: the scores in, the probabilities P out (in place)
-  float* Phat;   // [rows][Sk]: the normalized FP4 weights P^
-  const float* lse;
-  int64_t rows, Sq, Sk;
-  int kv_tile, causal, single;
-  float c;
-};
-
-// One workgroup per query row; a thread takes 16 consecutive keys (one P
-// block) up to the row's last key the products read.  Pass 1: block maxima of x = fl32(S c) into LDS; pass 2: the tile
-// maximum tm from its blocks, e = 2^(x - tm), the block scale and codes, and
-// P = 2^(x - lse2), P^ = v s2 2^(tm - lse2) (/2688 two-level).
-__global__ void __launch_bounds__(256) probs_kernel(ProbArgs A) {
-  extern __shared__ float bmax[];  // Sk / 16
-  const int64_t row = blockIdx.x;
-  const int64_t q = row % A.Sq;
-  const int64_t nvis = A.causal ? (q + 1 < A.Sk ? q + 1 : A.Sk) : A.Sk;
-  // Under the causal mask the products read a row only up to the end of its
-  // kGT-key tile (they skip the tiles above the diagonal): entries past it are
-  // neither written nor read.
-  const int64_t jend = A.causal && (q / kGT + 1) * kGT < A.Sk ? (q / kGT + 1) * kGT : A.Sk;
-  const int nblk = (int)(jend / 16);
-  float* srow = A.S + row * A.Sk;
-  float* prow = A.Phat + row * A.Sk;
-  const float lse2 = A.lse[row] * 1.4426950408889634f;
-  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t j = 16 * (int64_t)b + i;
-      if (j < nvis) m = __builtin_fmaxf(m, srow[j] * A.c);
-    }
-    bmax[b] = m;
-  }
-  __syncthreads();
-  const int bpt = A.kv_tile / 16;  // blocks per tile
-  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
-    const int t0 = (b / bpt) * bpt;
-    float tm = -__builtin_inff();
-    for (int k = 0; k < bpt && t0 + k < nblk; ++k) tm = __builtin_fmaxf(tm, bmax[t0 + k]);  // (a short last tile)
-    float x[16], e[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t j = 16 * (int64_t)b + i;
-      x[i] = j < nvis ? srow[j] * A.c : -__builtin_inff();
-      e[i] = __builtin_amdgcn_exp2f(x[i] - tm);  // masked: 0 (tm finite on a visible tile)
-    }
-    float pv[16], ph[16];
-    if (bmax[b] == -__builtin_inff()) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = ph[i] = 0.0f;
-    } else {
-      const float emax = __builtin_amdgcn_exp2f(bmax[b] - tm);
-      const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
-      const float2_t fs = A.single ? kTrainP.one[byte] : kTrainP.two[byte];
-      const float w = __builtin_amdgcn_exp2f(tm - lse2) * (A.single ? 1.0f : 1.0f / 2688.0f);
-      float t[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t[i] = e[i] * fs[0];
-      uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        cw[h] = cvt_pk_fp4<0>(cw[h], t[8 * h + 0], t[8 * h + 1]);
-        cw[h] = cvt_pk_fp4<1>(cw[h], t[8 * h + 2], t[8 * h + 3]);
-        cw[h] = cvt_pk_fp4<2>(cw[h], t[8 * h + 4], t[8 * h + 5]);
-        cw[h] = cvt_pk_fp4<3>(cw[h], t[8 * h + 6], t[8 * h + 7]);
-      }
-      float cv[16];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float2_t a0 = cvt_pk_f32_fp4<0>(cw[h]), a1 = cvt_pk_f32_fp4<1>(cw[h]);
-        const float2_t a2 = cvt_pk_f32_fp4<2>(cw[h]), a3 = cvt_pk_f32_fp4<3>(cw[h]);
-        cv[8 * h + 0] = a0[0]; cv[8 * h + 1] = a0[1]; cv[8 * h + 2] = a1[0]; cv[8 * h + 3] = a1[1];
-        cv[8 * h + 4] = a2[0]; cv[8 * h + 5] = a2[1]; cv[8 * h + 6] = a3[0]; cv[8 * h + 7] = a3[1];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ph[i] = cv[i] * fs[1] * w;  // code value times s2 is exact; one rounding for the weight
-        pv[i] = __builtin_amdgcn_exp2f(x[i] - lse2);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      *reinterpret_cast<float4_t*>(srow + 16 * (int64_t)b + i) = float4_t{pv[i], pv[i + 1], pv[i + 2], pv[i + 3]};
-      *reinterpret_cast<float4_t*>(prow + 16 * (int64_t)b + i) = float4_t{ph[i], ph[i + 1], ph[i + 2], ph[i + 3]};
-    }
-  }
-}
-
 // ---- batched GEMM on the bf16 MFMA -----------------------------------------
 //
 // The products keep binary32 accuracy on the bf16 matrix instructions: an
@@ -220,10 +130,7 @@ struct GemmArgs {
   float* C;
   int64_t M, N, K, lda, ldb, ldc, sA, sB, sC;
   int gA, gB;          // batch z reads A batch z / gA and B batch z / gB
-  float alpha;         // epilogue 1: C = alpha * C * (acc - D[z][row])
-  const float* D;
   // causal structure (the score matrix is zero above the diagonal):
-  // 1: C is queries x keys -- tiles entirely above the diagonal are skipped;
   // 2: K runs over keys (dS K^) -- the k loop stops after the tile's last query;
   // 3: M runs over keys, K over stacked query rows of Sq each (P^T dO, dS^T Q^)
   //    -- k slices whose queries all precede the tile's first key are skipped.
@@ -308,7 +215,7 @@ __device__ __forceinline__ float16_t mfma_bf16(const uint4_t& a, const uint4_t& 
 // B stored N x K).  128 x 128 tile per workgroup (4 waves of 64 x 64, each
 // 2 x 2 products of 32 x 32), 32-deep k slices through LDS; the next slice's
 // loads are in flight while the current one computes.
-template <bool TA, bool TB, int EPI, bool SA, bool SB>
+template <bool TA, bool TB, bool SA, bool SB>
 __global__ void __launch_bounds__(256) mgemm_kernel(GemmArgs g) {
   __shared__ uint16_t Ah[kGT * kGRow], Bh[kGT * kGRow];
   __shared__ uint16_t Al[SA ? kGT * kGRow : 1], Bl[SB ? kGT * kGRow : 1];
@@ -317,7 +224,6 @@ __global__ void __launch_bounds__(256) mgemm_kernel(GemmArgs g) {
   const float* B = g.B + (z / g.gB) * g.sB;
   float* C = g.C + z * g.sC;
   const int64_t m0 = (int64_t)blockIdx.y * kGT, n0 = (int64_t)blockIdx.x * kGT;
-  if (g.causal == 1 && n0 > m0 + kGT - 1) return;  // every key after every query of the tile
   const int64_t kend = g.causal == 2 && m0 + kGT < g.K ? m0 + kGT : g.K;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5, r32 = lane & 31;
@@ -378,34 +284,199 @@ __global__ void __launch_bounds__(256) mgemm_kernel(GemmArgs g) {
       const int64_t col = n0 + (2 * wn + j) * 32 + r32;
       if (col >= g.N) continue;
       const int64_t rb = m0 + (2 * wm + i) * 32 + 4 * hi;
-      if (EPI == 1) {  // every load first, then the stores: the reads of P stay in flight together
-        float pv[16], dv[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = rb + 8 * (v / 4) + (v % 4);
-          pv[v] = row < g.M ? C[row * g.ldc + col] : 0.0f;
-          dv[v] = row < g.M ? g.D[z * g.M + row] : 0.0f;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = rb + 8 * (v / 4) + (v % 4);
-          if (row < g.M) C[row * g.ldc + col] = g.alpha * pv[v] * (acc[i][j][v] - dv[v]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = rb + 8 * (v / 4) + (v % 4);
-          if (row < g.M) C[row * g.ldc + col] = acc[i][j][v];
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = rb + 8 * (v / 4) + (v % 4);
+        if (row < g.M) C[row * g.ldc + col] = acc[i][j][v];
       }
     }
 }
 
-template <bool TA, bool TB, int EPI, bool SA, bool SB>
+template <bool TA, bool TB, bool SA, bool SB>
 hipError_t gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
   const dim3 grid((unsigned)((g.N + kGT - 1) / kGT), (unsigned)((g.M + kGT - 1) / kGT), (unsigned)batch);
-  hipLaunchKernelGGL((mgemm_kernel<TA, TB, EPI, SA, SB>), grid, dim3(256), 0, st, g);
+  hipLaunchKernelGGL((mgemm_kernel<TA, TB, SA, SB>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
+}
+
+// ---- scores, probabilities and dS in one pass -------------------------------
+//
+// One workgroup per 128 query rows (4 waves x 32) of a head, looping over the
+// key tiles the rows see.  Per tile the waves compute S^T = K^ Q^T and
+// dP^T = V^ dO^T on the bf16 MFMA (K^ and V^ rows fed in the permuted order
+// that leaves each lane 16 consecutive keys of its query: one P block per
+// lane), then the forward's tile-local P^ (the block scale from the block
+// maximum, the tile maximum over kv_tile keys), P = 2^(x - lse2) and
+// dS = s P (dP - D), and write P^ and dS.  Rows are written up to the end of
+// the diagonal tile under the causal mask (the products read no further).
+
+struct SdpArgs {
+  const float *q, *k, *v, *dout, *D, *lse;
+  float *Ph, *dS;
+  int64_t H, G, Sq, Sk;
+  int kv_tile, causal, single, nqt;
+  float c, alpha;
+};
+
+__device__ __forceinline__ int sdp_krow(int r) { return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 4); }
+
+__device__ __forceinline__ float sdp_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// 8 consecutive fp32 of a row -> 8 bf16 (hi, and lo when SPLIT) for an MFMA operand
+template <bool SPLIT>
+__device__ __forceinline__ void frag8(const float* p, bool ok, uint4_t& hi, uint4_t& lo) {
+  const float4_t a = ok ? *reinterpret_cast<const float4_t*>(p) : float4_t{0, 0, 0, 0};
+  const float4_t b = ok ? *reinterpret_cast<const float4_t*>(p + 4) : float4_t{0, 0, 0, 0};
+  uint2_t ha, la, hb, lb;
+  split4<SPLIT>(a, ha, la);
+  split4<SPLIT>(b, hb, lb);
+  hi = uint4_t{ha[0], ha[1], hb[0], hb[1]};
+  lo = uint4_t{la[0], la[1], lb[0], lb[1]};
+}
+
+template <int D, bool SPLIT_DO>
+__global__ void __launch_bounds__(256, 2) sdp_kernel(SdpArgs A) {
+  constexpr int ROW = D + 8;  // bf16 per LDS row (16 bytes of padding)
+  __shared__ uint16_t Ks[kGT * ROW], Vs[kGT * ROW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+  const int64_t BH = gridDim.x / A.nqt;
+  const int64_t gi = blockIdx.x;
+  const int64_t bh = gi % BH, qrank = gi / BH;
+  const int qt = (int)(A.causal ? A.nqt - 1 - qrank : qrank);  // heaviest causal rows first
+  const int64_t b = bh / A.H, h = bh - b * A.H;
+  const int64_t bhk = b * (A.H / A.G) + h / A.G;
+  const int64_t q = (int64_t)qt * kGT + 32 * wave + r32;
+  const bool qok = q < A.Sq;
+  const int64_t qidx = bh * A.Sq + (qok ? q : 0);
+  // B operands (this lane's query, d = 16 s + 8 hi .. + 8): Q^ and dO
+  uint4_t qf[D / 16], df[D / 16], dl[SPLIT_DO ? D / 16 : 1];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    uint4_t unused;
+    frag8<false>(A.q + qidx * D + 16 * s + 8 * hi, qok, qf[s], unused);
+    frag8<SPLIT_DO>(A.dout + qidx * D + 16 * s + 8 * hi, qok, df[s], dl[SPLIT_DO ? s : 0]);
+  }
+  const float lse2 = qok ? A.lse[qidx] * 1.4426950408889634f : 0.0f;
+  const float Dq = qok ? A.D[qidx] : 0.0f;
+  const int64_t qend = ((int64_t)qt + 1) * kGT;
+  const int64_t kend = A.causal && qend < A.Sk ? qend : A.Sk;
+  const int ntile = (int)((kend + kGT - 1) / kGT);
+  const float* kb = A.k + bhk * A.Sk * D;
+  const float* vb = A.v + bhk * A.Sk * D;
+  const int krow = sdp_krow(r32);
+  for (int t = 0; t < ntile; ++t) {
+    const int64_t key0 = (int64_t)t * kGT;
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll 4
+    for (int u = 0; u < kGT * D / 4 / 256; ++u) {
+      const int f = threadIdx.x + 256 * u;
+      const int r = f / (D / 4), c4 = f % (D / 4);
+      const bool ok = key0 + r < A.Sk;
+      const float4_t kx = ok ? *reinterpret_cast<const float4_t*>(kb + (key0 + r) * D + 4 * c4) : float4_t{0, 0, 0, 0};
+      const float4_t vx = ok ? *reinterpret_cast<const float4_t*>(vb + (key0 + r) * D + 4 * c4) : float4_t{0, 0, 0, 0};
+      uint2_t kh, vh, unused;
+      split4<false>(kx, kh, unused);  // K^ and V^ are bf16 numbers: exact
+      split4<false>(vx, vh, unused);
+      *reinterpret_cast<uint2_t*>(Ks + r * ROW + 4 * c4) = kh;
+      *reinterpret_cast<uint2_t*>(Vs + r * ROW + 4 * c4) = vh;
+    }
+    __syncthreads();
+    // S^T for the tile's four 32-key subtiles
+    float16_t sacc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sacc[g] = float16_t{0};
+      const uint16_t* ka = Ks + (32 * g + krow) * ROW + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        sacc[g] = mfma_bf16(*reinterpret_cast<const uint4_t*>(ka + 16 * s), qf[s], sacc[g]);
+    }
+    // x = fl32(S c) on visible keys, block and tile maxima
+    float bmax[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t key = key0 + 32 * g + 16 * hi + i;
+        const bool vis = key < A.Sk && (!A.causal || key <= q);
+        sacc[g][i] = vis ? sacc[g][i] * A.c : -__builtin_inff();
+        m = __builtin_fmaxf(m, sacc[g][i]);
+      }
+      bmax[g] = m;
+    }
+    float tmv[4];
+    if (A.kv_tile == 128) {
+      float m = __builtin_fmaxf(__builtin_fmaxf(bmax[0], bmax[1]), __builtin_fmaxf(bmax[2], bmax[3]));
+      m = __builtin_fmaxf(m, sdp_xor32(m));
+      tmv[0] = tmv[1] = tmv[2] = tmv[3] = m;
+    } else {
+      float m0 = __builtin_fmaxf(bmax[0], bmax[1]), m1 = __builtin_fmaxf(bmax[2], bmax[3]);
+      m0 = __builtin_fmaxf(m0, sdp_xor32(m0));
+      m1 = __builtin_fmaxf(m1, sdp_xor32(m1));
+      tmv[0] = tmv[1] = m0;
+      tmv[2] = tmv[3] = m1;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t kb0 = key0 + 32 * g + 16 * hi;  // this lane's P block
+      // dP^T of the subtile
+      float16_t dp = float16_t{0};
+      const uint16_t* va = Vs + (32 * g + krow) * ROW + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const uint4_t a = *reinterpret_cast<const uint4_t*>(va + 16 * s);
+        dp = mfma_bf16(a, df[s], dp);
+        if (SPLIT_DO) dp = mfma_bf16(a, dl[s], dp);
+      }
+      float pv[16], ph[16];
+      const float tm = tmv[g];
+      if (bmax[g] == -__builtin_inff()) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = ph[i] = 0.0f;
+      } else {
+        const float emax = __builtin_amdgcn_exp2f(bmax[g] - tm);
+        const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
+        const float2_t fs = A.single ? kTrainP.one[byte] : kTrainP.two[byte];
+        const float w = __builtin_amdgcn_exp2f(tm - lse2) * (A.single ? 1.0f : 1.0f / 2688.0f);
+        float tq[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tq[i] = __builtin_amdgcn_exp2f(sacc[g][i] - tm) * fs[0];  // masked: 0
+        uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          cw[hh] = cvt_pk_fp4<0>(cw[hh], tq[8 * hh + 0], tq[8 * hh + 1]);
+          cw[hh] = cvt_pk_fp4<1>(cw[hh], tq[8 * hh + 2], tq[8 * hh + 3]);
+          cw[hh] = cvt_pk_fp4<2>(cw[hh], tq[8 * hh + 4], tq[8 * hh + 5]);
+          cw[hh] = cvt_pk_fp4<3>(cw[hh], tq[8 * hh + 6], tq[8 * hh + 7]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float2_t a0 = cvt_pk_f32_fp4<0>(cw[hh]), a1 = cvt_pk_f32_fp4<1>(cw[hh]);
+          const float2_t a2 = cvt_pk_f32_fp4<2>(cw[hh]), a3 = cvt_pk_f32_fp4<3>(cw[hh]);
+          const float cv[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ph[8 * hh + i] = cv[i] * fs[1] * w;  // code value times s2 is exact
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(sacc[g][i] - lse2);
+      }
+      if (qok && kb0 < A.Sk) {
+        float* php = A.Ph + qidx * A.Sk + kb0;
+        float* dsp = A.dS + qidx * A.Sk + kb0;
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          *reinterpret_cast<float4_t*>(php + i) = float4_t{ph[i], ph[i + 1], ph[i + 2], ph[i + 3]};
+          *reinterpret_cast<float4_t*>(dsp + i) =
+              float4_t{A.alpha * pv[i] * (dp[i] - Dq), A.alpha * pv[i + 1] * (dp[i + 1] - Dq),
+                       A.alpha * pv[i + 2] * (dp[i + 2] - Dq), A.alpha * pv[i + 3] * (dp[i + 3] - Dq)};
+        }
+      }
+    }
+  }
 }
 
 }  // namespace fp4dev
@@ -449,40 +520,34 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   if (L.hp_dtype == 2) hipLaunchKernelGGL(row_dot_kernel<float>, rd, dim3(256), 0, st, dof, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
   else if (L.hp_dtype == 1) hipLaunchKernelGGL(row_dot_kernel<half_t>, rd, dim3(256), 0, st, dof, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
   else hipLaunchKernelGGL(row_dot_kernel<uint16_t>, rd, dim3(256), 0, st, dof, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
-  // S = Q^ K^T per query head (K^ of its kv head)
-  GemmArgs g{};
-  g.A = qh; g.lda = d; g.sA = Sq * d; g.gA = 1;
-  g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
-  g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
-  g.M = Sq; g.N = Sk; g.K = d;
-  g.causal = L.causal ? 1 : 0;
-  hipError_t e = gemm<false, true, 0, false, false>(g, B * H, st);
+  // P^ and dS = s P (dO V^T - D) from the scores, in one pass
+  SdpArgs sa;
+  sa.q = qh; sa.k = kh; sa.v = vh; sa.dout = dof; sa.D = Dv; sa.lse = L.lse;
+  sa.Ph = Ph; sa.dS = Sb;
+  sa.H = H; sa.G = G; sa.Sq = Sq; sa.Sk = Sk;
+  sa.kv_tile = L.kv_tile; sa.causal = L.causal; sa.single = L.single;
+  sa.nqt = (int)((Sq + kGT - 1) / kGT);
+  sa.c = L.c;
+  sa.alpha = L.c * 0.69314718055994531f;
+  const dim3 sgrid((unsigned)(B * H * sa.nqt));
+  if (d == 128) {
+    if (fp16_do) hipLaunchKernelGGL((sdp_kernel<128, true>), sgrid, dim3(256), 0, st, sa);
+    else hipLaunchKernelGGL((sdp_kernel<128, false>), sgrid, dim3(256), 0, st, sa);
+  } else {
+    if (fp16_do) hipLaunchKernelGGL((sdp_kernel<64, true>), sgrid, dim3(256), 0, st, sa);
+    else hipLaunchKernelGGL((sdp_kernel<64, false>), sgrid, dim3(256), 0, st, sa);
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // P and P^
-  ProbArgs pa;
-  pa.S = Sb; pa.Phat = Ph; pa.lse = L.lse;
-  pa.rows = (int64_t)nq; pa.Sq = Sq; pa.Sk = Sk;
-  pa.kv_tile = L.kv_tile; pa.causal = L.causal; pa.single = L.single; pa.c = L.c;
-  hipLaunchKernelGGL(probs_kernel, dim3((unsigned)nq), dim3(256), (size_t)(Sk / 16) * 4, st, pa);
   // dV = P^T dO over the G query heads of each kv head
-  g = GemmArgs{};
+  GemmArgs g{};
   g.A = Ph; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
   g.B = dof; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
   g.C = L.dv; g.ldc = d; g.sC = Sk * d;
   g.M = Sk; g.N = d; g.K = G * Sq;
   g.causal = L.causal ? 3 : 0;
   g.Sq = Sq;
-  if ((e = (fp16_do ? gemm<true, false, 0, true, true>(g, B * Hkv, st) : gemm<true, false, 0, true, false>(g, B * Hkv, st))) != hipSuccess) return e;
-  // dS = s P (dO V^T - D), written over P
-  g = GemmArgs{};
-  g.A = dof; g.lda = d; g.sA = Sq * d; g.gA = 1;
-  g.B = vh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
-  g.C = Sb; g.ldc = Sk; g.sC = Sq * Sk;
-  g.M = Sq; g.N = Sk; g.K = d;
-  g.alpha = L.c * 0.69314718055994531f;
-  g.D = Dv;
-  g.causal = L.causal ? 1 : 0;  // skipped tiles keep P = 0, which is dS there
-  if ((e = (fp16_do ? gemm<false, true, 1, true, false>(g, B * H, st) : gemm<false, true, 1, false, false>(g, B * H, st))) != hipSuccess) return e;
+  if ((e = (fp16_do ? gemm<true, false, true, true>(g, B * Hkv, st) : gemm<true, false, true, false>(g, B * Hkv, st))) != hipSuccess) return e;
   // dQ = dS K^
   g = GemmArgs{};
   g.A = Sb; g.lda = Sk; g.sA = Sq * Sk; g.gA = 1;
@@ -490,7 +555,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.C = L.dq; g.ldc = d; g.sC = Sq * d;
   g.M = Sq; g.N = d; g.K = Sk;
   g.causal = L.causal ? 2 : 0;
-  if ((e = gemm<false, false, 0, true, false>(g, B * H, st)) != hipSuccess) return e;
+  if ((e = gemm<false, false, true, false>(g, B * H, st)) != hipSuccess) return e;
   // dK = dS^T Q^ over the G query heads of each kv head
   g = GemmArgs{};
   g.A = Sb; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
@@ -499,5 +564,5 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   g.M = Sk; g.N = d; g.K = G * Sq;
   g.causal = L.causal ? 3 : 0;
   g.Sq = Sq;
-  return gemm<true, false, 0, true, false>(g, B * Hkv, st);
+  return gemm<true, false, true, false>(g, B * Hkv, st);
 }
