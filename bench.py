@@ -49,10 +49,10 @@ def source_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(tag, kernel_src):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
-    when the summary is missing or was taken on a different kernel source."""
-    p = os.path.join(PROFILES, f"{tag}_traffic.txt")
+def read_profile(name, kernel_src, key):
+    """A figure from a committed rocprofv3 --pmc summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    p = os.path.join(PROFILES, name)
     if not os.path.exists(p):
         return None
     kv = {}
@@ -63,9 +63,14 @@ def read_traffic(tag, kernel_src):
     if kv.get("kernel_source_sha256_16") != source_hash(kernel_src):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(tag, kernel_src):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy)."""
+    return read_profile(f"{tag}_traffic.txt", kernel_src, "hbm_bytes_per_launch")
 
 
 class Timer:
@@ -88,6 +93,21 @@ class Timer:
         e1.record(s)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms per call
+
+    def each(self, fn, n, warm=1):
+        """Per-call durations (ms), one event pair per call on the launch stream."""
+        torch = self.torch
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(s)
+            fn()
+            b.record(s)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
 
 
 def bench_select32k(fp4, synth, torch, steps, warmup):
@@ -125,7 +145,9 @@ def bench_select32k(fp4, synth, torch, steps, warmup):
                               quantized=quant, selection=sel, return_lse=False, out=out)
 
     kms = timer.run(kern, max(3, steps // 2))
-    return dict(ms=ms, wall=wall, flops=flops, kernel_ms=kms, q=q, k=k, v=v)
+    per = timer.each(kern, max(5, steps))
+    pct = {f"p{p}": round(per[min(len(per) - 1, (len(per) * p) // 100)], 4) for p in (10, 50, 90)}
+    return dict(ms=ms, wall=wall, flops=flops, kernel_ms=kms, kernel_ms_pct=pct, q=q, k=k, v=v)
 
 
 def prequantize(fp4, q, k, v, torch, pct=0):
@@ -316,14 +338,20 @@ def bench_train(fp4, synth, torch, n):
     ms_b = timer.run(lambda: fp4.fp4_attention_bwd(q, k, v, out_hp, lse, do, causal=True, workspace=ws), n)
     fl_f = attn_flops(1, H, S, d)          # one attention forward (FA convention, causal half)
     fl_b = 2.5 * fl_f                       # five score-sized products: S again, dP, dV, dQ, dK
+    # the backward writes P^ and dS (fp32, causal half plus the diagonal tiles) and reads them in
+    # the dV, dK and dQ products
+    score_bytes = 4.0 * H * (S * S / 2 + S * 64)
     return dict(workload="training step B=1 H=32 S=4096 d=128 causal, bf16, ScaleSearch Q/K/V, two-level P",
                 forward_ms=round(ms_f, 4),
                 forward_note="quantization of Q/K/V and two attention passes (FP4 output and O')",
                 forward_tflops=round(2 * fl_f / ms_f / 1e9, 1),
                 backward_ms=round(ms_b, 4), backward_tflops=round(fl_b / ms_b / 1e9, 1),
-                backward_roofline={"bound": "fp32", "achieved": round(fl_b / ms_b / 1e9, 1), "peak": 157.3,
-                                   "unit": "TFLOP/s", "frac": round(fl_b / ms_b / 1e9 / 157.3, 4),
-                                   "note": "causal half counted; products skip the tiles above the diagonal"})
+                backward_roofline={"bound": "mfma", "achieved": round(fl_b / ms_b / 1e9, 1),
+                                   "peak": FP16_MFMA_PEAK_TF, "unit": "TFLOP/s",
+                                   "frac": round(fl_b / ms_b / 1e9 / FP16_MFMA_PEAK_TF, 4),
+                                   "note": "bf16 MFMA (fp32 operands split in two bf16 terms); causal half "
+                                           "counted; the materialized P^ and dS make it HBM-bound"},
+                backward_score_traffic_gbs=round(5 * score_bytes / ms_b / 1e6, 1))
 
 
 def bench_mx(fp4, synth, torch, n):
@@ -488,8 +516,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<128,128>",
                      "achieved": round(kern_tf, 2), "peak": FP16_MFMA_PEAK_TF, "unit": "TFLOP/s",
                      "frac": round(kern_tf / FP16_MFMA_PEAK_TF, 4),
-                     "kernel_ms": round(res["kernel_ms"], 4), "algorithmic_flops": res["flops"],
-                     "traffic": traffic},
+                     "kernel_ms": round(res["kernel_ms"], 4), "kernel_ms_per_launch": res["kernel_ms_pct"],
+                     "algorithmic_flops": res["flops"], "traffic": traffic,
+                     "mfma_busy": read_profile("attn_fwd_select32k_mfma.txt", "attn_fwd.hip", "mfma_busy_frac")},
     }
     if not args.no_components:
         log("components: prefill 8K")
