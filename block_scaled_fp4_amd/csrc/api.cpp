@@ -1,10 +1,12 @@
 // api.cpp -- extern "C" entry points of the FP4 library: argument validation,
-// workspace planning and kernel launches.  No allocation, no synchronization.
+// workspace planning and kernel launches.  No allocation; no synchronization
+// unless FP4_SYNC_CHECK is set.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/fp4.h"
@@ -14,11 +16,21 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Debug switches read from the environment at every call (set and unset at will):
+// FP4_LOG=1 reports each launch and each error on stderr; FP4_SYNC_CHECK=1
+// waits for the device after each launch, so a fault inside a kernel is
+// returned as FP4_ERR_HIP by the call that launched it.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+  if (env_on("FP4_LOG")) std::fprintf(stderr, "[fp4] error %d: %s\n", code, g_err);
   return code;
 }
 
@@ -65,7 +77,12 @@ bool hadamard_size(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128
 float hadamard_scale(int64_t n) { return (float)(1.0 / std::sqrt((double)n)); }
 
 int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess && env_on("FP4_SYNC_CHECK")) {
+    e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipGetLastError();
+  }
   if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (env_on("FP4_LOG")) std::fprintf(stderr, "[fp4] %s: ok\n", what);
   return ok();
 }
 

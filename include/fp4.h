@@ -30,6 +30,11 @@
  *   - Calls that share a workspace buffer must be ordered on one stream.
  *   - Every option struct starts with struct_size = sizeof(struct), so that
  *     the struct can grow without breaking callers.
+ *   - Debug switches, read from the environment at every call: FP4_LOG=1
+ *     prints each launch and each error on stderr; FP4_SYNC_CHECK=1 waits for
+ *     the device after each launch (hipDeviceSynchronize), so an error raised
+ *     while a kernel runs is returned as FP4_ERR_HIP by the call that launched
+ *     it instead of surfacing at a later call.
  */
 #ifndef FP4_H
 #define FP4_H

@@ -208,3 +208,16 @@ def test_mx_entry_points_validate(L):
     assert call(_prob(fp4), _opts(fp4), need - 1) == -3
     quant = dict(q_codes=f, q_scales=f, k_codes=f, k_scales=f, v_codes=f, v_scales=f)
     assert L.fp4_attention_fwd_mx_workspace_size(C.byref(_prob(fp4, **quant)), C.byref(_opts(fp4))) == 0
+
+
+def test_log_switch_reports_errors(L, capfd, monkeypatch):
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+    opts = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 0)
+    monkeypatch.setenv("FP4_LOG", "1")
+    assert L.fp4_quantize(f, 0, 16, 40, 40, C.byref(opts), f, f, None, None, None, 0, None) == -1
+    err = capfd.readouterr().err
+    assert "[fp4] error -1" in err and "cols" in err
+    monkeypatch.setenv("FP4_LOG", "0")
+    assert L.fp4_quantize(f, 0, 16, 40, 40, C.byref(opts), f, f, None, None, None, 0, None) == -1
+    assert "[fp4]" not in capfd.readouterr().err
