@@ -338,9 +338,6 @@ def bench_train(fp4, synth, torch, n):
     ms_b = timer.run(lambda: fp4.fp4_attention_bwd(q, k, v, out_hp, lse, do, causal=True, workspace=ws), n)
     fl_f = attn_flops(1, H, S, d)          # one attention forward (FA convention, causal half)
     fl_b = 2.5 * fl_f                       # five score-sized products: S again, dP, dV, dQ, dK
-    # the backward writes P^ and dS (fp32, causal half plus the diagonal tiles) and reads them in
-    # the dV, dK and dQ products
-    score_bytes = 4.0 * H * (S * S / 2 + S * 64)
     return dict(workload="training step B=1 H=32 S=4096 d=128 causal, bf16, ScaleSearch Q/K/V, two-level P",
                 forward_ms=round(ms_f, 4),
                 forward_note="quantization of Q/K/V and two attention passes (FP4 output and O')",
@@ -350,8 +347,8 @@ def bench_train(fp4, synth, torch, n):
                                    "peak": FP16_MFMA_PEAK_TF, "unit": "TFLOP/s",
                                    "frac": round(fl_b / ms_b / 1e9 / FP16_MFMA_PEAK_TF, 4),
                                    "note": "bf16 MFMA (fp32 operands split in two bf16 terms); causal half "
-                                           "counted; the materialized P^ and dS make it HBM-bound"},
-                backward_score_traffic_gbs=round(5 * score_bytes / ms_b / 1e6, 1))
+                                           "counted; scores recomputed in the dK/dV and the dQ kernels, none "
+                                           "stored"})
 
 
 def bench_mx(fp4, synth, torch, n):

@@ -464,7 +464,6 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
   const void* ptrs[] = {out_hp, lse, dout, dq, dk, dv};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-  if (prob->Sk > 65536) return fail(FP4_ERR_UNSUPPORTED, "%s: Sk above 65536", fn);
   const size_t need = fp4_attention_bwd_workspace_size(prob, opts);
   if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   const AttnPlan P = plan_attn(prob, opts);

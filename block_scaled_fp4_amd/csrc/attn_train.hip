@@ -9,17 +9,18 @@
 // quantization of e = 2^(x - tm), rescaled by 2^(tm - lse2)):
 //   dV = P^T dO,  dS = s P * (dO V^T - D),  D = rowsum(dO * O'),
 //   dQ = dS K^,   dK = dS^T Q^,             s = c ln 2.
-// One pass recomputes the scores and writes P^ and dS (one float per
-// query/key pair each, so the workspace grows with B H Sq Sk); dV, dQ and dK
-// are batched GEMMs on the bf16 MFMA with binary32 accuracy (128 x 128 tiles,
-// LDS staged), the query heads of a kv head being consecutive rows of one
-// GEMM for dK and dV.
+// Nothing score-sized is stored: one kernel per key tile recomputes the
+// scores, P, P^ and dS for every query that sees the tile and accumulates dK
+// and dV (summed over the query heads of a kv head); one kernel per query
+// tile recomputes the scores, P and dS and accumulates dQ.  The products run
+// on the bf16 MFMA with binary32 accuracy; the workspace holds fp32 copies of
+// the operands and D only.
 #include "device_common.h"
 #include "fp4_internal.h"
 
 namespace fp4dev {
 
-constexpr int kGT = 128;  // output tile (M and N) of the products
+constexpr int kGT = 128;  // query rows per dQ workgroup, keys per dK/dV workgroup
 
 // ---- operands in fp32 ----------------------------------------------------
 
@@ -113,7 +114,7 @@ struct TrainPTable {
 };
 __constant__ TrainPTable kTrainP = TrainPTable();
 
-// ---- batched GEMM on the bf16 MFMA -----------------------------------------
+// ---- binary32 products on the bf16 MFMA --------------------------------------
 //
 // The products keep binary32 accuracy on the bf16 matrix instructions: an
 // operand whose values are bf16 numbers (the dequantized NVFP4 Q^, K^, V^ --
@@ -124,24 +125,7 @@ __constant__ TrainPTable kTrainP = TrainPTable();
 // term is below 2^-16 of the product).  Products are exact in the MFMA and
 // accumulate in fp32.
 
-struct GemmArgs {
-  const float* A;
-  const float* B;
-  float* C;
-  int64_t M, N, K, lda, ldb, ldc, sA, sB, sC;
-  int gA, gB;          // batch z reads A batch z / gA and B batch z / gB
-  // causal structure (the score matrix is zero above the diagonal):
-  // 2: K runs over keys (dS K^) -- the k loop stops after the tile's last query;
-  // 3: M runs over keys, K over stacked query rows of Sq each (P^T dO, dS^T Q^)
-  //    -- k slices whose queries all precede the tile's first key are skipped.
-  int causal;
-  int64_t Sq;
-};
-
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-constexpr int kGK = 32;   // k slice
-constexpr int kGRow = kGK + 8;  // LDS row: 32 bf16 + 8 of padding (80 bytes)
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -161,168 +145,9 @@ __device__ __forceinline__ void split4(const float4_t& x, uint2_t& hi, uint2_t& 
   lo = uint2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
 }
 
-// One operand's slice: kGT rows (m or n) x kGK k, 16 values per thread.
-// KC (k contiguous in memory, element (r, k) at X[r*ld + k]): thread t reads
-// row t/8 + 32i, k 4(t%8)..+3.  RC (rows contiguous, element (r, k) at
-// X[k*ld + r]): thread t reads rows 4(t%32)..+3 at k 4(t/32)+i and
-// transposes in registers.
-template <bool RC>
-struct OpSlice {
-  float4_t v[4];
-  __device__ __forceinline__ void load(const float* X, int64_t ld, int64_t r0, int64_t rows, int64_t k0, int64_t kend) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!RC) {
-        const int64_t r = r0 + t / 8 + 32 * i, k = k0 + 4 * (t % 8);
-        v[i] = (r < rows && k < kend) ? *reinterpret_cast<const float4_t*>(X + r * ld + k) : float4_t{0, 0, 0, 0};
-      } else {
-        const int64_t r = r0 + 4 * (t % 32), k = k0 + 4 * (t / 32) + i;
-        v[i] = (r < rows && k < kend) ? *reinterpret_cast<const float4_t*>(X + k * ld + r) : float4_t{0, 0, 0, 0};
-      }
-    }
-  }
-  template <bool SPLIT>
-  __device__ __forceinline__ void store(uint16_t* hiS, uint16_t* loS) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4_t x;
-      int r, k;
-      if (!RC) {
-        x = v[i];
-        r = t / 8 + 32 * i;
-        k = 4 * (t % 8);
-      } else {
-        x = float4_t{v[0][i], v[1][i], v[2][i], v[3][i]};  // row 4(t%32)+i, k 4(t/32)..+3
-        r = 4 * (t % 32) + i;
-        k = 4 * (t / 32);
-      }
-      uint2_t h, l;
-      split4<SPLIT>(x, h, l);
-      *reinterpret_cast<uint2_t*>(hiS + r * kGRow + k) = h;
-      if (SPLIT) *reinterpret_cast<uint2_t*>(loS + r * kGRow + k) = l;
-    }
-  }
-};
-
 __device__ __forceinline__ float16_t mfma_bf16(const uint4_t& a, const uint4_t& b, const float16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
-}
-
-// C[z] = op(A) op(B): op(A) is M x K (TA: A stored K x M), op(B) is K x N (TB:
-// B stored N x K).  128 x 128 tile per workgroup (4 waves of 64 x 64, each
-// 2 x 2 products of 32 x 32), 32-deep k slices through LDS; the next slice's
-// loads are in flight while the current one computes.
-template <bool TA, bool TB, bool SA, bool SB>
-__global__ void __launch_bounds__(256) mgemm_kernel(GemmArgs g) {
-  __shared__ uint16_t Ah[kGT * kGRow], Bh[kGT * kGRow];
-  __shared__ uint16_t Al[SA ? kGT * kGRow : 1], Bl[SB ? kGT * kGRow : 1];
-  const int64_t z = blockIdx.z;
-  const float* A = g.A + (z / g.gA) * g.sA;
-  const float* B = g.B + (z / g.gB) * g.sB;
-  float* C = g.C + z * g.sC;
-  const int64_t m0 = (int64_t)blockIdx.y * kGT, n0 = (int64_t)blockIdx.x * kGT;
-  const int64_t kend = g.causal == 2 && m0 + kGT < g.K ? m0 + kGT : g.K;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, hi = lane >> 5, r32 = lane & 31;
-  float16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{0};
-  // first slice that is not all zero (mode 3: queries of the slice all before the tile's first key)
-  auto skip = [&](int64_t k0) { return g.causal == 3 && (k0 % g.Sq) + kGK - 1 < m0; };
-  OpSlice<TA> sa;      // A rows are m: contiguous along m when A is stored K x M
-  OpSlice<!TB> sb;     // B rows are n: contiguous along n when B is stored K x N
-  int64_t k0 = 0;
-  while (k0 < kend && skip(k0)) k0 += kGK;
-  if (k0 < kend) {
-    sa.load(A, g.lda, m0, g.M, k0, kend);
-    sb.load(B, g.ldb, n0, g.N, k0, kend);
-  }
-  while (k0 < kend) {
-    __syncthreads();  // the previous slice's LDS reads are done
-    sa.template store<SA>(Ah, Al);
-    sb.template store<SB>(Bh, Bl);
-    int64_t kn = k0 + kGK;
-    while (kn < kend && skip(kn)) kn += kGK;
-    if (kn < kend) {
-      sa.load(A, g.lda, m0, g.M, kn, kend);
-      sb.load(B, g.ldb, n0, g.N, kn, kend);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kGK / 16; ++kk) {
-      const int ko = 16 * kk + 8 * hi;
-      uint4_t ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = (2 * wm + i) * 32 + r32, rb = (2 * wn + i) * 32 + r32;
-        ah[i] = *reinterpret_cast<const uint4_t*>(Ah + ra * kGRow + ko);
-        bh[i] = *reinterpret_cast<const uint4_t*>(Bh + rb * kGRow + ko);
-        if (SA) al[i] = *reinterpret_cast<const uint4_t*>(Al + ra * kGRow + ko);
-        if (SB) bl[i] = *reinterpret_cast<const uint4_t*>(Bl + rb * kGRow + ko);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
-          if (SB) acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
-          if (SA) acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
-        }
-    }
-    k0 = kn;
-  }
-  // C layout of a 32 x 32 product: lane column r32, rows 8(v/4) + 4 hi + v%4
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + (2 * wn + j) * 32 + r32;
-      if (col >= g.N) continue;
-      const int64_t rb = m0 + (2 * wm + i) * 32 + 4 * hi;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = rb + 8 * (v / 4) + (v % 4);
-        if (row < g.M) C[row * g.ldc + col] = acc[i][j][v];
-      }
-    }
-}
-
-template <bool TA, bool TB, bool SA, bool SB>
-hipError_t gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
-  const dim3 grid((unsigned)((g.N + kGT - 1) / kGT), (unsigned)((g.M + kGT - 1) / kGT), (unsigned)batch);
-  hipLaunchKernelGGL((mgemm_kernel<TA, TB, SA, SB>), grid, dim3(256), 0, st, g);
-  return hipGetLastError();
-}
-
-// ---- scores, probabilities and dS in one pass -------------------------------
-//
-// One workgroup per 128 query rows (4 waves x 32) of a head, looping over the
-// key tiles the rows see.  Per tile the waves compute S^T = K^ Q^T and
-// dP^T = V^ dO^T on the bf16 MFMA (K^ and V^ rows fed in the permuted order
-// that leaves each lane 16 consecutive keys of its query: one P block per
-// lane), then the forward's tile-local P^ (the block scale from the block
-// maximum, the tile maximum over kv_tile keys), P = 2^(x - lse2) and
-// dS = s P (dP - D), and write P^ and dS.  Rows are written up to the end of
-// the diagonal tile under the causal mask (the products read no further).
-
-struct SdpArgs {
-  const float *q, *k, *v, *dout, *D, *lse;
-  float *Ph, *dS;
-  int64_t H, G, Sq, Sk;
-  int kv_tile, causal, single, nqt;
-  float c, alpha;
-};
-
-__device__ __forceinline__ int sdp_krow(int r) { return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 4); }
-
-__device__ __forceinline__ float sdp_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 // 8 consecutive fp32 of a row -> 8 bf16 (hi, and lo when SPLIT) for an MFMA operand
@@ -337,10 +162,297 @@ __device__ __forceinline__ void frag8(const float* p, bool ok, uint4_t& hi, uint
   lo = uint4_t{la[0], la[1], lb[0], lb[1]};
 }
 
+// ---- dK and dV without materialized scores ---------------------------------
+//
+// One workgroup per 128-key tile of a kv head (4 waves x 32 keys), looping
+// over 32-query blocks of the G query heads that read it.  The wave keeps its
+// keys' K^ and V^ as B operands in registers and recomputes S = Q^ K^T and
+// dP = dO V^T with Q and dO rows fed in the order krow2 (bits 2 and 3 of the
+// row swapped), which leaves lane (key, h) holding queries 8h..8h+7 and
+// 16+8h..16+8h+7: exactly the k order of the A operand of dV += P^T dO and
+// dK += dS^T Q^.  P^ is quantized as in the forward: the 16-key block maximum
+// is a reduction over one 16-lane DPP row, the tile maximum over kv_tile keys
+// goes through LDS across waves.
+
+struct KvArgs {
+  const float *q, *k, *v, *dout, *D, *lse;
+  float *dk, *dv;
+  int64_t H, G, Sq, Sk;
+  int kv_tile, causal, single, nkt;
+  float c, alpha;
+};
+
+__device__ __forceinline__ int krow2(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __builtin_fmaxf(v, o);
+}
+
+// maximum over the 16 lanes of a DPP row (mirror, half mirror, then the two quad swaps)
+__device__ __forceinline__ float rowmax16(float v) {
+  v = dpp_max<0x140>(v);
+  v = dpp_max<0x141>(v);
+  v = dpp_max<0xB1>(v);
+  return dpp_max<0x4E>(v);
+}
+
+// 8 fp32 -> 8 bf16 (hi, and lo when SPLIT) as one MFMA operand
+template <bool SPLIT>
+__device__ __forceinline__ void pack8(const float* x, uint4_t& hi, uint4_t& lo) {
+  uint2_t ha, la, hb, lb;
+  split4<SPLIT>(float4_t{x[0], x[1], x[2], x[3]}, ha, la);
+  split4<SPLIT>(float4_t{x[4], x[5], x[6], x[7]}, hb, lb);
+  hi = uint4_t{ha[0], ha[1], hb[0], hb[1]};
+  lo = uint4_t{la[0], la[1], lb[0], lb[1]};
+}
+
 template <int D, bool SPLIT_DO>
-__global__ void __launch_bounds__(256, 2) sdp_kernel(SdpArgs A) {
-  constexpr int ROW = D + 8;  // bf16 per LDS row (16 bytes of padding)
-  __shared__ uint16_t Ks[kGT * ROW], Vs[kGT * ROW];
+__global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
+  constexpr int QB = 32;        // queries per step
+  constexpr int RA = D + 8;     // [query][d] rows, bf16
+  constexpr int RB = QB + 8;    // [d][query] rows, bf16
+  __shared__ uint16_t Qa[QB * RA], Oa[QB * RA], Qb[D * RB], Ob[D * RB];
+  __shared__ uint16_t Oal[SPLIT_DO ? QB * RA : 1], Obl[SPLIT_DO ? D * RB : 1];
+  __shared__ __align__(16) float lse_s[QB];
+  __shared__ __align__(16) float D_s[QB];
+  __shared__ __align__(16) float tmx[8][QB];  // block maxima: [2 wave + row of the wave][query]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+  const int64_t BHkv = gridDim.x / A.nkt;
+  const int64_t bhk = blockIdx.x % BHkv;
+  const int kt = (int)(blockIdx.x / BHkv);  // key tile 0 sees the most queries under the causal mask
+  const int64_t Hkv = A.H / A.G;
+  const int64_t b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int64_t key0 = (int64_t)kt * kGT;
+  const int64_t key = key0 + 32 * wave + r32;
+  const bool kok = key < A.Sk;
+  uint4_t kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    uint4_t unused;
+    frag8<false>(A.k + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, kf[s], unused);
+    frag8<false>(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, vf[s], unused);
+  }
+  float16_t dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) dvacc[t] = dkacc[t] = float16_t{0};
+  __shared__ float2_t ptab[128];  // the P-scale table of the chosen scheme
+  if (threadIdx.x < 128) ptab[threadIdx.x] = A.single ? kTrainP.one[threadIdx.x] : kTrainP.two[threadIdx.x];
+  const int64_t qstart = A.causal ? key0 : 0;  // earlier queries see none of these keys
+  const int nqb = qstart < A.Sq ? (int)((A.Sq - qstart + QB - 1) / QB) : 0;
+  const int nsteps = (int)A.G * nqb;  // (query head, query block) pairs
+  const int qr = krow2(r32);  // the Q / dO row this lane feeds to the score products
+  // query of value v of this lane in the score layout
+  auto qof = [&](int v) { return (v & 7) + 8 * hi + 16 * (v >> 3); };
+  // staging: thread (query group, d group) moves 4 queries x 4 d of Q^ (op 0) and dO (op 1);
+  // with d = 128 every thread takes both operands, with d = 64 half the threads each
+  constexpr int NT = 2 * D;
+  constexpr int NOP = NT == 256 ? 2 : 1;
+  float4_t fx[NOP][4];
+  float fl = 0.0f, fd = 0.0f;
+  auto fetch = [&](int step) {
+    const int64_t bh = b * A.H + hk * A.G + step / nqb;
+    const int64_t q0 = qstart + (int64_t)(step % nqb) * QB;
+#pragma unroll
+    for (int o = 0; o < NOP; ++o) {
+      const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
+      const int t = (int)(threadIdx.x % NT);
+      const int qg = t % 8, dg = t / 8;
+      const float* src = op == 0 ? A.q : A.dout;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t qq = q0 + 4 * qg + i;
+        fx[o][i] = qq < A.Sq ? *reinterpret_cast<const float4_t*>(src + (bh * A.Sq + qq) * D + 4 * dg)
+                             : float4_t{0, 0, 0, 0};
+      }
+    }
+    if (threadIdx.x < QB) {
+      const int64_t qq = q0 + threadIdx.x;
+      const bool ok = qq < A.Sq;
+      fl = ok ? A.lse[bh * A.Sq + qq] * 1.4426950408889634f : 0.0f;
+      fd = ok ? A.D[bh * A.Sq + qq] : 0.0f;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int o = 0; o < NOP; ++o) {
+      const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
+      const int t = (int)(threadIdx.x % NT);
+      const int qg = t % 8, dg = t / 8;
+      const bool split = SPLIT_DO && op == 1;
+      uint16_t* ra = op == 0 ? Qa : Oa;
+      uint16_t* rb = op == 0 ? Qb : Ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2_t h, l;
+        if (split) split4<true>(fx[o][i], h, l);
+        else split4<false>(fx[o][i], h, l);
+        *reinterpret_cast<uint2_t*>(ra + (4 * qg + i) * RA + 4 * dg) = h;
+        if (SPLIT_DO && split) *reinterpret_cast<uint2_t*>(Oal + (4 * qg + i) * RA + 4 * dg) = l;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2_t h, l;
+        const float4_t y = float4_t{fx[o][0][j], fx[o][1][j], fx[o][2][j], fx[o][3][j]};
+        if (split) split4<true>(y, h, l);
+        else split4<false>(y, h, l);
+        *reinterpret_cast<uint2_t*>(rb + (4 * dg + j) * RB + 4 * qg) = h;
+        if (SPLIT_DO && split) *reinterpret_cast<uint2_t*>(Obl + (4 * dg + j) * RB + 4 * qg) = l;
+      }
+    }
+    if (threadIdx.x < QB) {
+      lse_s[threadIdx.x] = fl;
+      D_s[threadIdx.x] = fd;
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    {
+      const int64_t q0 = qstart + (int64_t)(step % nqb) * QB;
+      __syncthreads();  // the previous step's LDS reads are done
+      stage();
+      if (step + 1 < nsteps) fetch(step + 1);  // in flight during this step's products
+      __syncthreads();
+      // S = Q^ K^T and dP = dO V^T (lane: key r32 of the wave, the 16 queries qof(v)); both
+      // products are issued before the softmax so the matrix cores run under it
+      float16_t sacc = float16_t{0}, dp = float16_t{0};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        sacc = mfma_bf16(*reinterpret_cast<const uint4_t*>(Qa + qr * RA + 16 * s + 8 * hi), kf[s], sacc);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oa + qr * RA + 16 * s + 8 * hi), vf[s], dp);
+        if (SPLIT_DO) dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oal + qr * RA + 16 * s + 8 * hi), vf[s], dp);
+      }
+      float x[16], bm[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t qq = q0 + qof(v);
+        const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
+        x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+        bm[v] = rowmax16(x[v]);  // this query's 16-key block
+      }
+      // block maxima of the tile: one writer per DPP row (entry 2 wave + row of the wave)
+      if ((r32 & 15) == 0) {
+        float* dst = &tmx[2 * wave + (r32 >> 4)][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          *reinterpret_cast<float4_t*>(dst + 8 * hi + 16 * h) = float4_t{bm[8 * h], bm[8 * h + 1], bm[8 * h + 2], bm[8 * h + 3]};
+          *reinterpret_cast<float4_t*>(dst + 8 * hi + 16 * h + 4) =
+              float4_t{bm[8 * h + 4], bm[8 * h + 5], bm[8 * h + 6], bm[8 * h + 7]};
+        }
+      }
+      __syncthreads();
+      float ph[16], ds[16];
+      {
+        // tile maximum per query over the kv_tile keys' blocks, and the row statistics
+        const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
+        const int ne = A.kv_tile == 128 ? 8 : 4;
+        float tm[16], l2[16], dd[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qb = 8 * hi + 16 * h;
+          float4_t a = *reinterpret_cast<const float4_t*>(&tmx[e0][qb]);
+          float4_t c = *reinterpret_cast<const float4_t*>(&tmx[e0][qb + 4]);
+          for (int e = 1; e < ne; ++e) {
+            const float4_t a2 = *reinterpret_cast<const float4_t*>(&tmx[e0 + e][qb]);
+            const float4_t c2 = *reinterpret_cast<const float4_t*>(&tmx[e0 + e][qb + 4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              a[j] = __builtin_fmaxf(a[j], a2[j]);
+              c[j] = __builtin_fmaxf(c[j], c2[j]);
+            }
+          }
+          const float4_t la = *reinterpret_cast<const float4_t*>(&lse_s[qb]);
+          const float4_t lc = *reinterpret_cast<const float4_t*>(&lse_s[qb + 4]);
+          const float4_t da = *reinterpret_cast<const float4_t*>(&D_s[qb]);
+          const float4_t dc = *reinterpret_cast<const float4_t*>(&D_s[qb + 4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            tm[8 * h + j] = a[j]; tm[8 * h + 4 + j] = c[j];
+            l2[8 * h + j] = la[j]; l2[8 * h + 4 + j] = lc[j];
+            dd[8 * h + j] = da[j]; dd[8 * h + 4 + j] = dc[j];
+          }
+        }
+        float t[16], f1[16], wv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // a block with no visible key gets scale 0 (t = 0, P^ = 0); tm is then finite or the
+          // whole row of the tile is masked, where every factor below is 0
+          const bool live = bm[v] != -__builtin_inff();
+          const float emax = live ? __builtin_amdgcn_exp2f(bm[v] - tm[v]) : 0.0f;
+          const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
+          const float2_t fs = ptab[byte];
+          const float w = live ? __builtin_amdgcn_exp2f(tm[v] - l2[v]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
+          t[v] = live ? __builtin_amdgcn_exp2f(x[v] - tm[v]) * fs[0] : 0.0f;
+          f1[v] = fs[1];
+          wv[v] = w;
+          ds[v] = A.alpha * __builtin_amdgcn_exp2f(x[v] - l2[v]) * (dp[v] - dd[v]);  // P masked: 0
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
+          ph[v] = cv[0] * f1[v] * wv[v];  // code value times s2 is exact; one rounding for the weight
+          ph[v + 1] = cv[1] * f1[v + 1] * wv[v + 1];
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q^: A = this lane's values (k-step ks: values 8 ks .. 8 ks + 7)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4_t pa, pl, da, dl;
+        pack8<true>(ph + 8 * ks, pa, pl);
+        pack8<true>(ds + 8 * ks, da, dl);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
+          const uint4_t ob = *reinterpret_cast<const uint4_t*>(Ob + row);
+          const uint4_t qb = *reinterpret_cast<const uint4_t*>(Qb + row);
+          dvacc[t] = mfma_bf16(pa, ob, dvacc[t]);
+          dvacc[t] = mfma_bf16(pl, ob, dvacc[t]);
+          if (SPLIT_DO) dvacc[t] = mfma_bf16(pa, *reinterpret_cast<const uint4_t*>(Obl + row), dvacc[t]);
+          dkacc[t] = mfma_bf16(da, qb, dkacc[t]);
+          dkacc[t] = mfma_bf16(dl, qb, dkacc[t]);
+        }
+      }
+    }
+  }
+  // dV and dK: lane holds column d = 32 t + r32, rows (keys) 8 (v/4) + 4 h + v%4 of the wave's 32
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t kk = key0 + 32 * wave + 8 * (v / 4) + 4 * hi + (v % 4);
+      if (kk < A.Sk) {
+        A.dv[(bhk * A.Sk + kk) * D + 32 * t + r32] = dvacc[t][v];
+        A.dk[(bhk * A.Sk + kk) * D + 32 * t + r32] = dkacc[t][v];
+      }
+    }
+}
+
+// ---- dQ without materialized scores -----------------------------------------
+//
+// One workgroup per 128 query rows (4 waves x 32), looping over 64-key tiles.
+// Per 32-key subtile the wave recomputes S^T = K^ Q^T and dP^T = V^ dO^T with
+// K^ and V^ rows fed in the krow2 order, so that lane (query, h) holds keys
+// 8h..8h+7 and 16+8h..16+8h+7 -- the k order of the B operand of
+// dQ^T += K^T dS^T -- forms dS = s P (dP - D) with P = 2^(x - lse2) (dQ needs
+// no P^), and accumulates dQ^T with K^T staged transposed in LDS.
+
+struct QArgs {
+  const float *q, *k, *v, *dout, *D, *lse;
+  float* dq;
+  int64_t H, G, Sq, Sk;
+  int causal, nqt;
+  float c, alpha;
+};
+
+template <int D, bool SPLIT_DO>
+__global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
+  constexpr int KT = 64;       // keys per tile
+  constexpr int RA = D + 8;    // [key][d] rows, bf16
+  constexpr int RT = KT + 8;   // [d][key] rows, bf16
+  __shared__ uint16_t Ka[KT * RA], Va[KT * RA], Kt[D * RT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
   const int64_t BH = gridDim.x / A.nqt;
   const int64_t gi = blockIdx.x;
@@ -351,7 +463,6 @@ __global__ void __launch_bounds__(256, 2) sdp_kernel(SdpArgs A) {
   const int64_t q = (int64_t)qt * kGT + 32 * wave + r32;
   const bool qok = q < A.Sq;
   const int64_t qidx = bh * A.Sq + (qok ? q : 0);
-  // B operands (this lane's query, d = 16 s + 8 hi .. + 8): Q^ and dO
   uint4_t qf[D / 16], df[D / 16], dl[SPLIT_DO ? D / 16 : 1];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
@@ -361,121 +472,93 @@ __global__ void __launch_bounds__(256, 2) sdp_kernel(SdpArgs A) {
   }
   const float lse2 = qok ? A.lse[qidx] * 1.4426950408889634f : 0.0f;
   const float Dq = qok ? A.D[qidx] : 0.0f;
+  float16_t acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = float16_t{0};
   const int64_t qend = ((int64_t)qt + 1) * kGT;
   const int64_t kend = A.causal && qend < A.Sk ? qend : A.Sk;
-  const int ntile = (int)((kend + kGT - 1) / kGT);
+  const int ntile = (int)((kend + KT - 1) / KT);
   const float* kb = A.k + bhk * A.Sk * D;
   const float* vb = A.v + bhk * A.Sk * D;
-  const int krow = sdp_krow(r32);
-  for (int t = 0; t < ntile; ++t) {
-    const int64_t key0 = (int64_t)t * kGT;
+  const int kr = krow2(r32);
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int64_t key0 = (int64_t)tile * KT;
     __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll 4
-    for (int u = 0; u < kGT * D / 4 / 256; ++u) {
-      const int f = threadIdx.x + 256 * u;
-      const int r = f / (D / 4), c4 = f % (D / 4);
-      const bool ok = key0 + r < A.Sk;
-      const float4_t kx = ok ? *reinterpret_cast<const float4_t*>(kb + (key0 + r) * D + 4 * c4) : float4_t{0, 0, 0, 0};
-      const float4_t vx = ok ? *reinterpret_cast<const float4_t*>(vb + (key0 + r) * D + 4 * c4) : float4_t{0, 0, 0, 0};
-      uint2_t kh, vh, unused;
-      split4<false>(kx, kh, unused);  // K^ and V^ are bf16 numbers: exact
-      split4<false>(vx, vh, unused);
-      *reinterpret_cast<uint2_t*>(Ks + r * ROW + 4 * c4) = kh;
-      *reinterpret_cast<uint2_t*>(Vs + r * ROW + 4 * c4) = vh;
+    {
+      // K^ and V^ rows as [key][d]; K^ also as [d][key]: thread (key group, d group) moves 4 x 4
+      const int t = threadIdx.x;
+#pragma unroll
+      for (int u = 0; u < KT * D / 16 / 256; ++u) {
+        const int id = t + 256 * u;
+        const int kg = id % (KT / 4), dg = id / (KT / 4);
+        float4_t xk[4], xv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t kk = key0 + 4 * kg + i;
+          const bool ok = kk < A.Sk;
+          xk[i] = ok ? *reinterpret_cast<const float4_t*>(kb + kk * D + 4 * dg) : float4_t{0, 0, 0, 0};
+          xv[i] = ok ? *reinterpret_cast<const float4_t*>(vb + kk * D + 4 * dg) : float4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint2_t hk, hv, unused;
+          split4<false>(xk[i], hk, unused);  // K^ and V^ are bf16 numbers: exact
+          split4<false>(xv[i], hv, unused);
+          *reinterpret_cast<uint2_t*>(Ka + (4 * kg + i) * RA + 4 * dg) = hk;
+          *reinterpret_cast<uint2_t*>(Va + (4 * kg + i) * RA + 4 * dg) = hv;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint2_t hk, unused;
+          split4<false>(float4_t{xk[0][j], xk[1][j], xk[2][j], xk[3][j]}, hk, unused);
+          *reinterpret_cast<uint2_t*>(Kt + (4 * dg + j) * RT + 4 * kg) = hk;
+        }
+      }
     }
     __syncthreads();
-    // S^T for the tile's four 32-key subtiles
-    float16_t sacc[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      sacc[g] = float16_t{0};
-      const uint16_t* ka = Ks + (32 * g + krow) * ROW + 8 * hi;
+    for (int g = 0; g < KT / 32; ++g) {
+      float16_t s = float16_t{0}, dp = float16_t{0};
+      const uint16_t* ka = Ka + (32 * g + kr) * RA + 8 * hi;
+      const uint16_t* va = Va + (32 * g + kr) * RA + 8 * hi;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        sacc[g] = mfma_bf16(*reinterpret_cast<const uint4_t*>(ka + 16 * s), qf[s], sacc[g]);
-    }
-    // x = fl32(S c) on visible keys, block and tile maxima
-    float bmax[4];
+      for (int k = 0; k < D / 16; ++k) s = mfma_bf16(*reinterpret_cast<const uint4_t*>(ka + 16 * k), qf[k], s);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float m = -__builtin_inff();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t key = key0 + 32 * g + 16 * hi + i;
-        const bool vis = key < A.Sk && (!A.causal || key <= q);
-        sacc[g][i] = vis ? sacc[g][i] * A.c : -__builtin_inff();
-        m = __builtin_fmaxf(m, sacc[g][i]);
+      for (int k = 0; k < D / 16; ++k) {
+        const uint4_t a = *reinterpret_cast<const uint4_t*>(va + 16 * k);
+        dp = mfma_bf16(a, df[k], dp);
+        if (SPLIT_DO) dp = mfma_bf16(a, dl[k], dp);
       }
-      bmax[g] = m;
-    }
-    float tmv[4];
-    if (A.kv_tile == 128) {
-      float m = __builtin_fmaxf(__builtin_fmaxf(bmax[0], bmax[1]), __builtin_fmaxf(bmax[2], bmax[3]));
-      m = __builtin_fmaxf(m, sdp_xor32(m));
-      tmv[0] = tmv[1] = tmv[2] = tmv[3] = m;
-    } else {
-      float m0 = __builtin_fmaxf(bmax[0], bmax[1]), m1 = __builtin_fmaxf(bmax[2], bmax[3]);
-      m0 = __builtin_fmaxf(m0, sdp_xor32(m0));
-      m1 = __builtin_fmaxf(m1, sdp_xor32(m1));
-      tmv[0] = tmv[1] = m0;
-      tmv[2] = tmv[3] = m1;
-    }
+      float ds[16];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t kb0 = key0 + 32 * g + 16 * hi;  // this lane's P block
-      // dP^T of the subtile
-      float16_t dp = float16_t{0};
-      const uint16_t* va = Vs + (32 * g + krow) * ROW + 8 * hi;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const uint4_t a = *reinterpret_cast<const uint4_t*>(va + 16 * s);
-        dp = mfma_bf16(a, df[s], dp);
-        if (SPLIT_DO) dp = mfma_bf16(a, dl[s], dp);
+      for (int v = 0; v < 16; ++v) {
+        const int64_t key = key0 + 32 * g + (v & 7) + 8 * hi + 16 * (v >> 3);
+        const bool vis = qok && key < A.Sk && (!A.causal || key <= q);
+        const float x = vis ? s[v] * A.c : -__builtin_inff();
+        ds[v] = A.alpha * __builtin_amdgcn_exp2f(x - lse2) * (dp[v] - Dq);  // P masked: 0
       }
-      float pv[16], ph[16];
-      const float tm = tmv[g];
-      if (bmax[g] == -__builtin_inff()) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = ph[i] = 0.0f;
-      } else {
-        const float emax = __builtin_amdgcn_exp2f(bmax[g] - tm);
-        const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
-        const float2_t fs = A.single ? kTrainP.one[byte] : kTrainP.two[byte];
-        const float w = __builtin_amdgcn_exp2f(tm - lse2) * (A.single ? 1.0f : 1.0f / 2688.0f);
-        float tq[16];
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4_t da, dlo;
+        pack8<true>(ds + 8 * ks, da, dlo);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tq[i] = __builtin_amdgcn_exp2f(sacc[g][i] - tm) * fs[0];  // masked: 0
-        uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          cw[hh] = cvt_pk_fp4<0>(cw[hh], tq[8 * hh + 0], tq[8 * hh + 1]);
-          cw[hh] = cvt_pk_fp4<1>(cw[hh], tq[8 * hh + 2], tq[8 * hh + 3]);
-          cw[hh] = cvt_pk_fp4<2>(cw[hh], tq[8 * hh + 4], tq[8 * hh + 5]);
-          cw[hh] = cvt_pk_fp4<3>(cw[hh], tq[8 * hh + 6], tq[8 * hh + 7]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const float2_t a0 = cvt_pk_f32_fp4<0>(cw[hh]), a1 = cvt_pk_f32_fp4<1>(cw[hh]);
-          const float2_t a2 = cvt_pk_f32_fp4<2>(cw[hh]), a3 = cvt_pk_f32_fp4<3>(cw[hh]);
-          const float cv[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ph[8 * hh + i] = cv[i] * fs[1] * w;  // code value times s2 is exact
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(sacc[g][i] - lse2);
-      }
-      if (qok && kb0 < A.Sk) {
-        float* php = A.Ph + qidx * A.Sk + kb0;
-        float* dsp = A.dS + qidx * A.Sk + kb0;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          *reinterpret_cast<float4_t*>(php + i) = float4_t{ph[i], ph[i + 1], ph[i + 2], ph[i + 3]};
-          *reinterpret_cast<float4_t*>(dsp + i) =
-              float4_t{A.alpha * pv[i] * (dp[i] - Dq), A.alpha * pv[i + 1] * (dp[i + 1] - Dq),
-                       A.alpha * pv[i + 2] * (dp[i + 2] - Dq), A.alpha * pv[i + 3] * (dp[i + 3] - Dq)};
+        for (int t = 0; t < D / 32; ++t) {
+          const uint4_t a = *reinterpret_cast<const uint4_t*>(Kt + (32 * t + r32) * RT + 32 * g + 16 * ks + 8 * hi);
+          acc[t] = mfma_bf16(a, da, acc[t]);
+          acc[t] = mfma_bf16(a, dlo, acc[t]);
         }
       }
     }
+  }
+  // dQ^T: lane column = this query, rows d = 32 t + 8 (v/4) + 4 h + v%4
+  if (qok) {
+    float* dst = A.dq + (bh * A.Sq + q) * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4_t*>(dst + 32 * t + 8 * j + 4 * hi) =
+            float4_t{acc[t][4 * j], acc[t][4 * j + 1], acc[t][4 * j + 2], acc[t][4 * j + 3]};
   }
 }
 
@@ -486,7 +569,7 @@ using namespace fp4dev;
 size_t fp4i_attn_bwd_workspace(const AttnBwdLaunch& L) {
   auto a = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t nq = (size_t)(L.B * L.H * L.Sq), nk = (size_t)(L.B * L.Hkv * L.Sk);
-  return a(nq * L.d * 4) * 2 + a(nk * L.d * 4) * 2 + a(nq * 4) + a(nq * (size_t)L.Sk * 4) * 2;
+  return a(nq * L.d * 4) * 2 + a(nk * L.d * 4) * 2 + a(nq * 4);
 }
 
 hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
@@ -499,9 +582,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   float* dof = (float*)w; w += a(nq * d * 4);
   float* kh = (float*)w; w += a(nk * d * 4);
   float* vh = (float*)w; w += a(nk * d * 4);
-  float* Dv = (float*)w; w += a(nq * 4);
-  float* Sb = (float*)w; w += a(nq * (size_t)Sk * 4);
-  float* Ph = (float*)w;
+  float* Dv = (float*)w;
   auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
   // operands
   hipLaunchKernelGGL(dequant_rows_kernel, blocks((int64_t)nq * d / 8), dim3(256), 0, st, L.qc, L.qs, (int64_t)nq,
@@ -520,49 +601,42 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   if (L.hp_dtype == 2) hipLaunchKernelGGL(row_dot_kernel<float>, rd, dim3(256), 0, st, dof, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
   else if (L.hp_dtype == 1) hipLaunchKernelGGL(row_dot_kernel<half_t>, rd, dim3(256), 0, st, dof, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
   else hipLaunchKernelGGL(row_dot_kernel<uint16_t>, rd, dim3(256), 0, st, dof, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
-  // P^ and dS = s P (dO V^T - D) from the scores, in one pass
-  SdpArgs sa;
-  sa.q = qh; sa.k = kh; sa.v = vh; sa.dout = dof; sa.D = Dv; sa.lse = L.lse;
-  sa.Ph = Ph; sa.dS = Sb;
-  sa.H = H; sa.G = G; sa.Sq = Sq; sa.Sk = Sk;
-  sa.kv_tile = L.kv_tile; sa.causal = L.causal; sa.single = L.single;
-  sa.nqt = (int)((Sq + kGT - 1) / kGT);
-  sa.c = L.c;
-  sa.alpha = L.c * 0.69314718055994531f;
-  const dim3 sgrid((unsigned)(B * H * sa.nqt));
+  const float alpha = L.c * 0.69314718055994531f;  // s = c ln 2
+  // dQ per 128 query rows
+  QArgs qa;
+  qa.q = qh; qa.k = kh; qa.v = vh; qa.dout = dof; qa.D = Dv; qa.lse = L.lse;
+  qa.dq = L.dq;
+  qa.H = H; qa.G = G; qa.Sq = Sq; qa.Sk = Sk;
+  qa.causal = L.causal;
+  qa.nqt = (int)((Sq + kGT - 1) / kGT);
+  qa.c = L.c;
+  qa.alpha = alpha;
+  const dim3 qgrid((unsigned)(B * H * qa.nqt));
   if (d == 128) {
-    if (fp16_do) hipLaunchKernelGGL((sdp_kernel<128, true>), sgrid, dim3(256), 0, st, sa);
-    else hipLaunchKernelGGL((sdp_kernel<128, false>), sgrid, dim3(256), 0, st, sa);
+    if (fp16_do) hipLaunchKernelGGL((bwd_q_kernel<128, true>), qgrid, dim3(256), 0, st, qa);
+    else hipLaunchKernelGGL((bwd_q_kernel<128, false>), qgrid, dim3(256), 0, st, qa);
   } else {
-    if (fp16_do) hipLaunchKernelGGL((sdp_kernel<64, true>), sgrid, dim3(256), 0, st, sa);
-    else hipLaunchKernelGGL((sdp_kernel<64, false>), sgrid, dim3(256), 0, st, sa);
+    if (fp16_do) hipLaunchKernelGGL((bwd_q_kernel<64, true>), qgrid, dim3(256), 0, st, qa);
+    else hipLaunchKernelGGL((bwd_q_kernel<64, false>), qgrid, dim3(256), 0, st, qa);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dV = P^T dO over the G query heads of each kv head
-  GemmArgs g{};
-  g.A = Ph; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
-  g.B = dof; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
-  g.C = L.dv; g.ldc = d; g.sC = Sk * d;
-  g.M = Sk; g.N = d; g.K = G * Sq;
-  g.causal = L.causal ? 3 : 0;
-  g.Sq = Sq;
-  if ((e = (fp16_do ? gemm<true, false, true, true>(g, B * Hkv, st) : gemm<true, false, true, false>(g, B * Hkv, st))) != hipSuccess) return e;
-  // dQ = dS K^
-  g = GemmArgs{};
-  g.A = Sb; g.lda = Sk; g.sA = Sq * Sk; g.gA = 1;
-  g.B = kh; g.ldb = d; g.sB = Sk * d; g.gB = (int)G;
-  g.C = L.dq; g.ldc = d; g.sC = Sq * d;
-  g.M = Sq; g.N = d; g.K = Sk;
-  g.causal = L.causal ? 2 : 0;
-  if ((e = gemm<false, false, true, false>(g, B * H, st)) != hipSuccess) return e;
-  // dK = dS^T Q^ over the G query heads of each kv head
-  g = GemmArgs{};
-  g.A = Sb; g.lda = Sk; g.sA = G * Sq * Sk; g.gA = 1;
-  g.B = qh; g.ldb = d; g.sB = G * Sq * d; g.gB = 1;
-  g.C = L.dk; g.ldc = d; g.sC = Sk * d;
-  g.M = Sk; g.N = d; g.K = G * Sq;
-  g.causal = L.causal ? 3 : 0;
-  g.Sq = Sq;
-  return gemm<true, false, true, false>(g, B * Hkv, st);
+  // dK and dV per key tile, over the G query heads of each kv head
+  KvArgs ka;
+  ka.q = qh; ka.k = kh; ka.v = vh; ka.dout = dof; ka.D = Dv; ka.lse = L.lse;
+  ka.dk = L.dk; ka.dv = L.dv;
+  ka.H = H; ka.G = G; ka.Sq = Sq; ka.Sk = Sk;
+  ka.kv_tile = L.kv_tile; ka.causal = L.causal; ka.single = L.single;
+  ka.nkt = (int)((Sk + kGT - 1) / kGT);
+  ka.c = L.c;
+  ka.alpha = alpha;
+  const dim3 kgrid((unsigned)(B * Hkv * ka.nkt));
+  if (d == 128) {
+    if (fp16_do) hipLaunchKernelGGL((bwd_kv_kernel<128, true>), kgrid, dim3(256), 0, st, ka);
+    else hipLaunchKernelGGL((bwd_kv_kernel<128, false>), kgrid, dim3(256), 0, st, ka);
+  } else {
+    if (fp16_do) hipLaunchKernelGGL((bwd_kv_kernel<64, true>), kgrid, dim3(256), 0, st, ka);
+    else hipLaunchKernelGGL((bwd_kv_kernel<64, false>), kgrid, dim3(256), 0, st, ka);
+  }
+  return hipGetLastError();
 }

@@ -221,3 +221,17 @@ def test_log_switch_reports_errors(L, capfd, monkeypatch):
     monkeypatch.setenv("FP4_LOG", "0")
     assert L.fp4_quantize(f, 0, 16, 40, 40, C.byref(opts), f, f, None, None, None, 0, None) == -1
     assert "[fp4]" not in capfd.readouterr().err
+
+
+def test_backward_workspace_is_linear_in_length(L):
+    """The backward recomputes the scores: its workspace holds per-row operand copies only."""
+    import block_scaled_fp4_amd as fp4
+    sizes = []
+    for S in (4096, 8192, 131072):
+        P = _prob(fp4, Sq=S, Sk=S, H=32, Hkv=32)
+        sizes.append(L.fp4_attention_bwd_workspace_size(C.byref(P), C.byref(_opts(fp4))))
+    assert sizes[1] <= 2 * sizes[0] + 4096
+    assert sizes[2] <= 32 * sizes[0] + 65536
+    n = 32 * 131072 * 128
+    # fp32 copies of Q^, K^, V^, dO, the row term D, and the NVFP4 codes + scales of Q, K, V
+    assert sizes[2] < n * 4 * 4 + 32 * 131072 * 4 + 3 * n * 9 // 16 + 65536
