@@ -165,14 +165,16 @@ __device__ __forceinline__ void frag8(const float* p, bool ok, uint4_t& hi, uint
 // ---- dK and dV without materialized scores ---------------------------------
 //
 // One workgroup per 128-key tile of a kv head (4 waves x 32 keys), looping
-// over 32-query blocks of the G query heads that read it.  The wave keeps its
-// keys' K^ and V^ as B operands in registers and recomputes S = Q^ K^T and
-// dP = dO V^T with Q and dO rows fed in the order krow2 (bits 2 and 3 of the
-// row swapped), which leaves lane (key, h) holding queries 8h..8h+7 and
-// 16+8h..16+8h+7: exactly the k order of the A operand of dV += P^T dO and
-// dK += dS^T Q^.  P^ is quantized as in the forward: the 16-key block maximum
-// is a reduction over one 16-lane DPP row, the tile maximum over kv_tile keys
-// goes through LDS across waves.
+// over 32-query blocks of the G query heads that read it, in two passes that
+// each fit two waves per SIMD: the dV pass needs P^ (block and tile maxima),
+// the dK pass needs P and dP.  The wave keeps its keys' K^ (and V^) as B
+// operands in registers and recomputes S = Q^ K^T (and dP = dO V^T) with Q
+// and dO rows fed in the order krow2 (bits 2 and 3 of the row swapped), which
+// leaves lane (key, h) holding queries 8h..8h+7 and 16+8h..16+8h+7: exactly
+// the k order of the A operand of dV += P^T dO and dK += dS^T Q^.  P^ is
+// quantized as in the forward: the 16-key block maximum is a reduction over
+// one 16-lane DPP row, the tile maximum over kv_tile keys goes through LDS
+// across waves.
 
 struct KvArgs {
   const float *q, *k, *v, *dout, *D, *lse;
@@ -208,16 +210,21 @@ __device__ __forceinline__ void pack8(const float* x, uint4_t& hi, uint4_t& lo) 
   lo = uint4_t{la[0], la[1], lb[0], lb[1]};
 }
 
-template <int D, bool SPLIT_DO>
-__global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
+template <int D, bool SPLIT_DO, int MODE>  // MODE 0: dV, 1: dK
+__global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
+  constexpr bool DV = MODE == 0;
+  constexpr bool SPL = SPLIT_DO;
   constexpr int QB = 32;        // queries per step
   constexpr int RA = D + 8;     // [query][d] rows, bf16
   constexpr int RB = QB + 8;    // [d][query] rows, bf16
-  __shared__ uint16_t Qa[QB * RA], Oa[QB * RA], Qb[D * RB], Ob[D * RB];
-  __shared__ uint16_t Oal[SPLIT_DO ? QB * RA : 1], Obl[SPLIT_DO ? D * RB : 1];
+  // dV: Q^ as [query][d] (scores), dO as [d][query] (product B operand);
+  // dK: Q^ in both layouts, dO as [query][d] (dP)
+  __shared__ uint16_t Qa[QB * RA], Xb[D * RB];
+  __shared__ uint16_t Oa[DV ? 1 : QB * RA], Oal[!DV && SPL ? QB * RA : 1], Xbl[DV && SPL ? D * RB : 1];
   __shared__ __align__(16) float lse_s[QB];
   __shared__ __align__(16) float D_s[QB];
-  __shared__ __align__(16) float tmx[8][QB];  // block maxima: [2 wave + row of the wave][query]
+  __shared__ __align__(16) float tmx[DV ? 8 : 1][QB];  // block maxima: [2 wave + row of the wave][query]
+  __shared__ float2_t ptab[DV ? 128 : 1];             // the P-scale table of the chosen scheme
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
   const int64_t BHkv = gridDim.x / A.nkt;
   const int64_t bhk = blockIdx.x % BHkv;
@@ -227,24 +234,22 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
   const int64_t key0 = (int64_t)kt * kGT;
   const int64_t key = key0 + 32 * wave + r32;
   const bool kok = key < A.Sk;
-  uint4_t kf[D / 16], vf[D / 16];
+  uint4_t kf[D / 16], vf[DV ? 1 : D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     uint4_t unused;
     frag8<false>(A.k + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, kf[s], unused);
-    frag8<false>(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, vf[s], unused);
+    if (!DV) frag8<false>(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, vf[DV ? 0 : s], unused);
   }
-  float16_t dvacc[D / 32], dkacc[D / 32];
+  float16_t acc[D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) dvacc[t] = dkacc[t] = float16_t{0};
-  __shared__ float2_t ptab[128];  // the P-scale table of the chosen scheme
-  if (threadIdx.x < 128) ptab[threadIdx.x] = A.single ? kTrainP.one[threadIdx.x] : kTrainP.two[threadIdx.x];
+  for (int t = 0; t < D / 32; ++t) acc[t] = float16_t{0};
+  if (DV && threadIdx.x < 128) ptab[threadIdx.x] = A.single ? kTrainP.one[threadIdx.x] : kTrainP.two[threadIdx.x];
   const int64_t qstart = A.causal ? key0 : 0;  // earlier queries see none of these keys
   const int nqb = qstart < A.Sq ? (int)((A.Sq - qstart + QB - 1) / QB) : 0;
   const int nsteps = (int)A.G * nqb;  // (query head, query block) pairs
   const int qr = krow2(r32);  // the Q / dO row this lane feeds to the score products
-  // query of value v of this lane in the score layout
-  auto qof = [&](int v) { return (v & 7) + 8 * hi + 16 * (v >> 3); };
+  auto qof = [&](int v) { return (v & 7) + 8 * hi + 16 * (v >> 3); };  // query of value v
   // staging: thread (query group, d group) moves 4 queries x 4 d of Q^ (op 0) and dO (op 1);
   // with d = 128 every thread takes both operands, with d = 64 half the threads each
   constexpr int NT = 2 * D;
@@ -271,7 +276,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
       const int64_t qq = q0 + threadIdx.x;
       const bool ok = qq < A.Sq;
       fl = ok ? A.lse[bh * A.Sq + qq] * 1.4426950408889634f : 0.0f;
-      fd = ok ? A.D[bh * A.Sq + qq] : 0.0f;
+      fd = ok && !DV ? A.D[bh * A.Sq + qq] : 0.0f;
     }
   };
   auto stage = [&]() {
@@ -280,25 +285,30 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
       const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
       const int t = (int)(threadIdx.x % NT);
       const int qg = t % 8, dg = t / 8;
-      const bool split = SPLIT_DO && op == 1;
-      uint16_t* ra = op == 0 ? Qa : Oa;
-      uint16_t* rb = op == 0 ? Qb : Ob;
+      const bool split = SPL && op == 1;
+      // [query][d] image: Q^ always, dO for dK; [d][query] image: dO for dV, Q^ for dK
+      uint16_t* ra = op == 0 ? Qa : (DV ? nullptr : Oa);
+      uint16_t* rb = (op == 1) == DV ? Xb : nullptr;
+      if (ra) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint2_t h, l;
-        if (split) split4<true>(fx[o][i], h, l);
-        else split4<false>(fx[o][i], h, l);
-        *reinterpret_cast<uint2_t*>(ra + (4 * qg + i) * RA + 4 * dg) = h;
-        if (SPLIT_DO && split) *reinterpret_cast<uint2_t*>(Oal + (4 * qg + i) * RA + 4 * dg) = l;
+        for (int i = 0; i < 4; ++i) {
+          uint2_t h, l;
+          if (split) split4<true>(fx[o][i], h, l);
+          else split4<false>(fx[o][i], h, l);
+          *reinterpret_cast<uint2_t*>(ra + (4 * qg + i) * RA + 4 * dg) = h;
+          if (!DV && SPL && split) *reinterpret_cast<uint2_t*>(Oal + (4 * qg + i) * RA + 4 * dg) = l;
+        }
       }
+      if (rb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2_t h, l;
-        const float4_t y = float4_t{fx[o][0][j], fx[o][1][j], fx[o][2][j], fx[o][3][j]};
-        if (split) split4<true>(y, h, l);
-        else split4<false>(y, h, l);
-        *reinterpret_cast<uint2_t*>(rb + (4 * dg + j) * RB + 4 * qg) = h;
-        if (SPLIT_DO && split) *reinterpret_cast<uint2_t*>(Obl + (4 * dg + j) * RB + 4 * qg) = l;
+        for (int j = 0; j < 4; ++j) {
+          uint2_t h, l;
+          const float4_t y = float4_t{fx[o][0][j], fx[o][1][j], fx[o][2][j], fx[o][3][j]};
+          if (split) split4<true>(y, h, l);
+          else split4<false>(y, h, l);
+          *reinterpret_cast<uint2_t*>(rb + (4 * dg + j) * RB + 4 * qg) = h;
+          if (DV && SPL && split) *reinterpret_cast<uint2_t*>(Xbl + (4 * dg + j) * RB + 4 * qg) = l;
+        }
       }
     }
     if (threadIdx.x < QB) {
@@ -308,34 +318,37 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
   };
   if (nsteps > 0) fetch(0);
   for (int step = 0; step < nsteps; ++step) {
-    {
-      const int64_t q0 = qstart + (int64_t)(step % nqb) * QB;
-      __syncthreads();  // the previous step's LDS reads are done
-      stage();
-      if (step + 1 < nsteps) fetch(step + 1);  // in flight during this step's products
-      __syncthreads();
-      // S = Q^ K^T and dP = dO V^T (lane: key r32 of the wave, the 16 queries qof(v)); both
-      // products are issued before the softmax so the matrix cores run under it
-      float16_t sacc = float16_t{0}, dp = float16_t{0};
+    const int64_t q0 = qstart + (int64_t)(step % nqb) * QB;
+    __syncthreads();  // the previous step's LDS reads are done
+    stage();
+    if (step + 1 < nsteps) fetch(step + 1);  // in flight during this step's products
+    __syncthreads();
+    // S = Q^ K^T (and dP = dO V^T): lane holds key r32 of the wave and the 16 queries qof(v)
+    float16_t sacc = float16_t{0}, dp = float16_t{0};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        sacc = mfma_bf16(*reinterpret_cast<const uint4_t*>(Qa + qr * RA + 16 * s + 8 * hi), kf[s], sacc);
+    for (int s = 0; s < D / 16; ++s)
+      sacc = mfma_bf16(*reinterpret_cast<const uint4_t*>(Qa + qr * RA + 16 * s + 8 * hi), kf[s], sacc);
+    if (!DV) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oa + qr * RA + 16 * s + 8 * hi), vf[s], dp);
-        if (SPLIT_DO) dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oal + qr * RA + 16 * s + 8 * hi), vf[s], dp);
+        dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oa + qr * RA + 16 * s + 8 * hi), vf[DV ? 0 : s], dp);
+        if (SPL) dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oal + qr * RA + 16 * s + 8 * hi), vf[DV ? 0 : s], dp);
       }
-      float x[16], bm[16];
+    }
+    float x[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t qq = q0 + qof(v);
-        const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
-        x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
-        bm[v] = rowmax16(x[v]);  // this query's 16-key block
-      }
-      // block maxima of the tile: one writer per DPP row (entry 2 wave + row of the wave)
-      if ((r32 & 15) == 0) {
-        float* dst = &tmx[2 * wave + (r32 >> 4)][0];
+    for (int v = 0; v < 16; ++v) {
+      const int64_t qq = q0 + qof(v);
+      const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
+      x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+    }
+    float w16[16];  // the A operand values of this step: P^ (dV) or dS (dK)
+    if (DV) {
+      float bm[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) bm[v] = rowmax16(x[v]);  // this query's 16-key block
+      if ((r32 & 15) == 0) {  // one writer per DPP row: entry 2 wave + row of the wave
+        float* dst = &tmx[DV ? 2 * wave + (r32 >> 4) : 0][0];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           *reinterpret_cast<float4_t*>(dst + 8 * hi + 16 * h) = float4_t{bm[8 * h], bm[8 * h + 1], bm[8 * h + 2], bm[8 * h + 3]};
@@ -344,89 +357,89 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(KvArgs A) {
         }
       }
       __syncthreads();
-      float ph[16], ds[16];
-      {
-        // tile maximum per query over the kv_tile keys' blocks, and the row statistics
-        const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
-        const int ne = A.kv_tile == 128 ? 8 : 4;
-        float tm[16], l2[16], dd[16];
+      // tile maximum per query over the kv_tile keys' blocks
+      const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
+      const int ne = A.kv_tile == 128 ? 8 : 4;
+      float tm[16], l2[16];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int qb = 8 * hi + 16 * h;
-          float4_t a = *reinterpret_cast<const float4_t*>(&tmx[e0][qb]);
-          float4_t c = *reinterpret_cast<const float4_t*>(&tmx[e0][qb + 4]);
-          for (int e = 1; e < ne; ++e) {
-            const float4_t a2 = *reinterpret_cast<const float4_t*>(&tmx[e0 + e][qb]);
-            const float4_t c2 = *reinterpret_cast<const float4_t*>(&tmx[e0 + e][qb + 4]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              a[j] = __builtin_fmaxf(a[j], a2[j]);
-              c[j] = __builtin_fmaxf(c[j], c2[j]);
-            }
-          }
-          const float4_t la = *reinterpret_cast<const float4_t*>(&lse_s[qb]);
-          const float4_t lc = *reinterpret_cast<const float4_t*>(&lse_s[qb + 4]);
-          const float4_t da = *reinterpret_cast<const float4_t*>(&D_s[qb]);
-          const float4_t dc = *reinterpret_cast<const float4_t*>(&D_s[qb + 4]);
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 8 * hi + 16 * h;
+        float4_t a = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 : 0][qb]);
+        float4_t c = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 : 0][qb + 4]);
+        for (int e = 1; e < ne; ++e) {
+          const float4_t a2 = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 + e : 0][qb]);
+          const float4_t c2 = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 + e : 0][qb + 4]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            tm[8 * h + j] = a[j]; tm[8 * h + 4 + j] = c[j];
-            l2[8 * h + j] = la[j]; l2[8 * h + 4 + j] = lc[j];
-            dd[8 * h + j] = da[j]; dd[8 * h + 4 + j] = dc[j];
+            a[j] = __builtin_fmaxf(a[j], a2[j]);
+            c[j] = __builtin_fmaxf(c[j], c2[j]);
           }
         }
-        float t[16], f1[16], wv[16];
+        const float4_t la = *reinterpret_cast<const float4_t*>(&lse_s[qb]);
+        const float4_t lc = *reinterpret_cast<const float4_t*>(&lse_s[qb + 4]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // a block with no visible key gets scale 0 (t = 0, P^ = 0); tm is then finite or the
-          // whole row of the tile is masked, where every factor below is 0
-          const bool live = bm[v] != -__builtin_inff();
-          const float emax = live ? __builtin_amdgcn_exp2f(bm[v] - tm[v]) : 0.0f;
-          const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
-          const float2_t fs = ptab[byte];
-          const float w = live ? __builtin_amdgcn_exp2f(tm[v] - l2[v]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
-          t[v] = live ? __builtin_amdgcn_exp2f(x[v] - tm[v]) * fs[0] : 0.0f;
-          f1[v] = fs[1];
-          wv[v] = w;
-          ds[v] = A.alpha * __builtin_amdgcn_exp2f(x[v] - l2[v]) * (dp[v] - dd[v]);  // P masked: 0
-        }
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
-          ph[v] = cv[0] * f1[v] * wv[v];  // code value times s2 is exact; one rounding for the weight
-          ph[v + 1] = cv[1] * f1[v + 1] * wv[v + 1];
+        for (int j = 0; j < 4; ++j) {
+          tm[8 * h + j] = a[j]; tm[8 * h + 4 + j] = c[j];
+          l2[8 * h + j] = la[j]; l2[8 * h + 4 + j] = lc[j];
         }
       }
-      // dV += P^T dO and dK += dS^T Q^: A = this lane's values (k-step ks: values 8 ks .. 8 ks + 7)
+      float t[16], f1[16], wv[16];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4_t pa, pl, da, dl;
-        pack8<true>(ph + 8 * ks, pa, pl);
-        pack8<true>(ds + 8 * ks, da, dl);
+      for (int v = 0; v < 16; ++v) {
+        // a block with no visible key gets scale 0 (t = 0, P^ = 0)
+        const bool live = bm[v] != -__builtin_inff();
+        const float emax = live ? __builtin_amdgcn_exp2f(bm[v] - tm[v]) : 0.0f;
+        const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
+        const float2_t fs = ptab[DV ? byte : 0];
+        wv[v] = live ? __builtin_amdgcn_exp2f(tm[v] - l2[v]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
+        t[v] = live ? __builtin_amdgcn_exp2f(x[v] - tm[v]) * fs[0] : 0.0f;
+        f1[v] = fs[1];
+      }
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
-          const uint4_t ob = *reinterpret_cast<const uint4_t*>(Ob + row);
-          const uint4_t qb = *reinterpret_cast<const uint4_t*>(Qb + row);
-          dvacc[t] = mfma_bf16(pa, ob, dvacc[t]);
-          dvacc[t] = mfma_bf16(pl, ob, dvacc[t]);
-          if (SPLIT_DO) dvacc[t] = mfma_bf16(pa, *reinterpret_cast<const uint4_t*>(Obl + row), dvacc[t]);
-          dkacc[t] = mfma_bf16(da, qb, dkacc[t]);
-          dkacc[t] = mfma_bf16(dl, qb, dkacc[t]);
+      for (int v = 0; v < 16; v += 2) {
+        const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
+        w16[v] = cv[0] * f1[v] * wv[v];  // code value times s2 is exact; one rounding for the weight
+        w16[v + 1] = cv[1] * f1[v + 1] * wv[v + 1];
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 8 * hi + 16 * h;
+        const float4_t la = *reinterpret_cast<const float4_t*>(&lse_s[qb]);
+        const float4_t lc = *reinterpret_cast<const float4_t*>(&lse_s[qb + 4]);
+        const float4_t da = *reinterpret_cast<const float4_t*>(&D_s[qb]);
+        const float4_t dc = *reinterpret_cast<const float4_t*>(&D_s[qb + 4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w16[8 * h + j] = A.alpha * __builtin_amdgcn_exp2f(x[8 * h + j] - la[j]) * (dp[8 * h + j] - da[j]);
+          w16[8 * h + 4 + j] = A.alpha * __builtin_amdgcn_exp2f(x[8 * h + 4 + j] - lc[j]) * (dp[8 * h + 4 + j] - dc[j]);
         }
       }
     }
+    // acc += w^T X: A = this lane's values (k-step ks: values 8 ks .. 8 ks + 7), B = the
+    // [d][query] image (dO for dV, Q^ for dK)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4_t wa, wl;
+      pack8<true>(w16 + 8 * ks, wa, wl);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
+        const uint4_t xb = *reinterpret_cast<const uint4_t*>(Xb + row);
+        acc[t] = mfma_bf16(wa, xb, acc[t]);
+        acc[t] = mfma_bf16(wl, xb, acc[t]);
+        if (DV && SPL) acc[t] = mfma_bf16(wa, *reinterpret_cast<const uint4_t*>(Xbl + row), acc[t]);
+      }
+    }
   }
-  // dV and dK: lane holds column d = 32 t + r32, rows (keys) 8 (v/4) + 4 h + v%4 of the wave's 32
+  // lane holds column d = 32 t + r32, rows (keys) 8 (v/4) + 4 h + v%4 of the wave's 32
+  float* out = DV ? A.dv : A.dk;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t kk = key0 + 32 * wave + 8 * (v / 4) + 4 * hi + (v % 4);
-      if (kk < A.Sk) {
-        A.dv[(bhk * A.Sk + kk) * D + 32 * t + r32] = dvacc[t][v];
-        A.dk[(bhk * A.Sk + kk) * D + 32 * t + r32] = dkacc[t][v];
-      }
+      if (kk < A.Sk) out[(bhk * A.Sk + kk) * D + 32 * t + r32] = acc[t][v];
     }
 }
 
@@ -632,11 +645,21 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   ka.alpha = alpha;
   const dim3 kgrid((unsigned)(B * Hkv * ka.nkt));
   if (d == 128) {
-    if (fp16_do) hipLaunchKernelGGL((bwd_kv_kernel<128, true>), kgrid, dim3(256), 0, st, ka);
-    else hipLaunchKernelGGL((bwd_kv_kernel<128, false>), kgrid, dim3(256), 0, st, ka);
+    if (fp16_do) {
+      hipLaunchKernelGGL((bwd_kv_kernel<128, true, 0>), kgrid, dim3(256), 0, st, ka);
+      hipLaunchKernelGGL((bwd_kv_kernel<128, true, 1>), kgrid, dim3(256), 0, st, ka);
+    } else {
+      hipLaunchKernelGGL((bwd_kv_kernel<128, false, 0>), kgrid, dim3(256), 0, st, ka);
+      hipLaunchKernelGGL((bwd_kv_kernel<128, false, 1>), kgrid, dim3(256), 0, st, ka);
+    }
   } else {
-    if (fp16_do) hipLaunchKernelGGL((bwd_kv_kernel<64, true>), kgrid, dim3(256), 0, st, ka);
-    else hipLaunchKernelGGL((bwd_kv_kernel<64, false>), kgrid, dim3(256), 0, st, ka);
+    if (fp16_do) {
+      hipLaunchKernelGGL((bwd_kv_kernel<64, true, 0>), kgrid, dim3(256), 0, st, ka);
+      hipLaunchKernelGGL((bwd_kv_kernel<64, true, 1>), kgrid, dim3(256), 0, st, ka);
+    } else {
+      hipLaunchKernelGGL((bwd_kv_kernel<64, false, 0>), kgrid, dim3(256), 0, st, ka);
+      hipLaunchKernelGGL((bwd_kv_kernel<64, false, 1>), kgrid, dim3(256), 0, st, ka);
+    }
   }
   return hipGetLastError();
 }
