@@ -13,8 +13,8 @@
 // scores, P, P^ and dS for every query that sees the tile and accumulates dK
 // and dV (summed over the query heads of a kv head); one kernel per query
 // tile recomputes the scores, P and dS and accumulates dQ.  The products run
-// on the bf16 MFMA with binary32 accuracy; the workspace holds fp32 copies of
-// the operands and D only.
+// on the bf16 MFMA with binary32 accuracy; the workspace holds bf16 copies of
+// the operands (exact) and D only.
 #include "device_common.h"
 #include "fp4_internal.h"
 
@@ -22,12 +22,20 @@ namespace fp4dev {
 
 constexpr int kGT = 128;  // query rows per dQ workgroup, keys per dK/dV workgroup
 
-// ---- operands in fp32 ----------------------------------------------------
+// ---- operands in bf16 -------------------------------------------------------
+//
+// The dequantized NVFP4 operands are bf16 numbers (an E2M1 value times an
+// E4M3 scale has at most 6 significant bits, within bf16's exponent range),
+// so their bf16 copies are exact: the top half of the binary32 pattern.
+
+__device__ __forceinline__ uint32_t bf16x2_exact(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
 
 // NVFP4 rows with blocks along the row (Q, K): codes [rows, d/2], scales
-// [rows, d/16] -> fp32 [rows, d].  One thread per 8 codes (4 bytes).
+// [rows, d/16] -> bf16 [rows, d].  One thread per 8 codes (4 bytes).
 __global__ void __launch_bounds__(256) dequant_rows_kernel(const uint8_t* codes, const uint8_t* scales,
-                                                           int64_t rows, int d, float* out) {
+                                                           int64_t rows, int d, uint16_t* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of 8 elements
   const int64_t n = rows * (d / 8);
   if (i >= n) return;
@@ -35,18 +43,18 @@ __global__ void __launch_bounds__(256) dequant_rows_kernel(const uint8_t* codes,
   const int c8 = (int)(i % (d / 8));
   const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (d / 2) + 4 * c8);
   const float s = e4m3_to_f32(scales[r * (d / 16) + c8 / 2]);
-  float* o = out + r * d + 8 * c8;
   const float2_t v0 = cvt_pk_f32_fp4<0>(w), v1 = cvt_pk_f32_fp4<1>(w);
   const float2_t v2 = cvt_pk_f32_fp4<2>(w), v3 = cvt_pk_f32_fp4<3>(w);
-  *reinterpret_cast<float4_t*>(o) = float4_t{v0[0] * s, v0[1] * s, v1[0] * s, v1[1] * s};
-  *reinterpret_cast<float4_t*>(o + 4) = float4_t{v2[0] * s, v2[1] * s, v3[0] * s, v3[1] * s};
+  *reinterpret_cast<uint4_t*>(out + r * d + 8 * c8) =
+      uint4_t{bf16x2_exact(v0[0] * s, v0[1] * s), bf16x2_exact(v1[0] * s, v1[1] * s),
+              bf16x2_exact(v2[0] * s, v2[1] * s), bf16x2_exact(v3[0] * s, v3[1] * s)};
 }
 
 // NVFP4 with blocks of 16 rows (V): codes [rows/2, d] (row 2i in the low
-// nibble), scales [rows/16, d] -> fp32 [rows, d].  One thread per row pair
+// nibble), scales [rows/16, d] -> bf16 [rows, d].  One thread per row pair
 // and column.
 __global__ void __launch_bounds__(256) dequant_cols_kernel(const uint8_t* codes, const uint8_t* scales,
-                                                           int64_t rows, int d, float* out) {
+                                                           int64_t rows, int d, uint16_t* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (rows / 2) * d;
   if (i >= n) return;
@@ -55,8 +63,9 @@ __global__ void __launch_bounds__(256) dequant_cols_kernel(const uint8_t* codes,
   const uint32_t b = codes[pr * d + c];
   const float s = e4m3_to_f32(scales[(pr / 8) * d + c]);
   const float2_t v = cvt_pk_f32_fp4<0>(b);
-  out[(2 * pr) * d + c] = v[0] * s;
-  out[(2 * pr + 1) * d + c] = v[1] * s;
+  const uint32_t pk = bf16x2_exact(v[0] * s, v[1] * s);
+  out[(2 * pr) * d + c] = (uint16_t)pk;
+  out[(2 * pr + 1) * d + c] = (uint16_t)(pk >> 16);
 }
 
 template <typename T>
@@ -68,21 +77,30 @@ __device__ __forceinline__ float to_f32<half_t>(half_t v) { return (float)v; }
 template <>
 __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 
-template <typename T>
-__global__ void __launch_bounds__(256) to_f32_kernel(const T* x, int64_t n, float* out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = to_f32<T>(x[i]);
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite values only
 }
 
-// D[row] = sum_d dO[row][d] O'[row][d], one wave per row.
-template <typename TO>
-__global__ void __launch_bounds__(256) row_dot_kernel(const float* dout, const TO* ohp, int64_t rows, int d,
-                                                      float* D) {
+// fp16 dO is not a bf16 number: x = hi + lo exactly with hi = bf16(x), lo = bf16(x - hi)
+// (11 significant bits fit in two bf16 terms of 8)
+__global__ void __launch_bounds__(256) split_f16_kernel(const half_t* x, int64_t n, uint16_t* hi, uint16_t* lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = (float)x[i];
+  const uint32_t h = bf16_rne_bits(v);
+  hi[i] = (uint16_t)h;
+  lo[i] = (uint16_t)bf16_rne_bits(v - __uint_as_float(h << 16));
+}
+
+// D[row] = sum_d dO[row][d] O'[row][d] in binary32, one wave per row.
+template <typename TD, typename TO>
+__global__ void __launch_bounds__(256) row_dot_kernel(const TD* dout, const TO* ohp, int64_t rows, int d, float* D) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   float s = 0.0f;
-  for (int c = lane; c < d; c += 64) s = __builtin_fmaf(dout[row * d + c], to_f32<TO>(ohp[row * d + c]), s);
+  for (int c = lane; c < d; c += 64) s = __builtin_fmaf(to_f32<TD>(dout[row * d + c]), to_f32<TO>(ohp[row * d + c]), s);
 #pragma unroll
   for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
   if (lane == 0) D[row] = s;
@@ -127,11 +145,6 @@ __constant__ TrainPTable kTrainP = TrainPTable();
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite values only
-}
-
 // 4 fp32 -> 4 bf16 hi (and lo when SPLIT), packed two per dword
 template <bool SPLIT>
 __device__ __forceinline__ void split4(const float4_t& x, uint2_t& hi, uint2_t& lo) {
@@ -150,16 +163,19 @@ __device__ __forceinline__ float16_t mfma_bf16(const uint4_t& a, const uint4_t& 
                                                  0, 0, 0);
 }
 
-// 8 consecutive fp32 of a row -> 8 bf16 (hi, and lo when SPLIT) for an MFMA operand
-template <bool SPLIT>
-__device__ __forceinline__ void frag8(const float* p, bool ok, uint4_t& hi, uint4_t& lo) {
-  const float4_t a = ok ? *reinterpret_cast<const float4_t*>(p) : float4_t{0, 0, 0, 0};
-  const float4_t b = ok ? *reinterpret_cast<const float4_t*>(p + 4) : float4_t{0, 0, 0, 0};
-  uint2_t ha, la, hb, lb;
-  split4<SPLIT>(a, ha, la);
-  split4<SPLIT>(b, hb, lb);
-  hi = uint4_t{ha[0], ha[1], hb[0], hb[1]};
-  lo = uint4_t{la[0], la[1], lb[0], lb[1]};
+// 8 consecutive bf16 of a row as one MFMA operand (zero when !ok)
+__device__ __forceinline__ uint4_t fragb(const uint16_t* p, bool ok) {
+  return ok ? *reinterpret_cast<const uint4_t*>(p) : uint4_t{0, 0, 0, 0};
+}
+
+// 4 x 4 transpose of 16-bit elements: in[i] holds elements (i, 0..3), out[j] elements (0..3, j)
+__device__ __forceinline__ void transpose4x4_16(const uint2_t (&in)[4], uint2_t (&out)[4]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {  // columns 2w and 2w+1
+    const uint32_t a = in[0][w], b = in[1][w], c = in[2][w], d = in[3][w];
+    out[2 * w] = uint2_t{__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(d, c, 0x05040100u)};
+    out[2 * w + 1] = uint2_t{__builtin_amdgcn_perm(b, a, 0x07060302u), __builtin_amdgcn_perm(d, c, 0x07060302u)};
+  }
 }
 
 // ---- dK and dV without materialized scores ---------------------------------
@@ -177,7 +193,8 @@ __device__ __forceinline__ void frag8(const float* p, bool ok, uint4_t& hi, uint
 // across waves.
 
 struct KvArgs {
-  const float *q, *k, *v, *dout, *D, *lse;
+  const uint16_t *q, *k, *v, *doh, *dol;  // bf16 [rows][d]; dol: the low terms of an fp16 dO
+  const float *D, *lse;
   float *dk, *dv;
   int64_t H, G, Sq, Sk;
   int kv_tile, causal, single, nkt;
@@ -237,9 +254,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
   uint4_t kf[D / 16], vf[DV ? 1 : D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    uint4_t unused;
-    frag8<false>(A.k + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, kf[s], unused);
-    if (!DV) frag8<false>(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok, vf[DV ? 0 : s], unused);
+    kf[s] = fragb(A.k + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok);
+    if (!DV) vf[DV ? 0 : s] = fragb(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok);
   }
   float16_t acc[D / 32];
 #pragma unroll
@@ -250,11 +266,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
   const int nsteps = (int)A.G * nqb;  // (query head, query block) pairs
   const int qr = krow2(r32);  // the Q / dO row this lane feeds to the score products
   auto qof = [&](int v) { return (v & 7) + 8 * hi + 16 * (v >> 3); };  // query of value v
-  // staging: thread (query group, d group) moves 4 queries x 4 d of Q^ (op 0) and dO (op 1);
-  // with d = 128 every thread takes both operands, with d = 64 half the threads each
+  // staging: thread (query group, d group) moves 4 queries x 4 d of Q^ (op 0) and dO (op 1, with
+  // its low terms when split); with d = 128 every thread takes both operands, with d = 64 half each
   constexpr int NT = 2 * D;
   constexpr int NOP = NT == 256 ? 2 : 1;
-  float4_t fx[NOP][4];
+  uint2_t fx[NOP][4], fxl[SPL ? 4 : 1];
   float fl = 0.0f, fd = 0.0f;
   auto fetch = [&](int step) {
     const int64_t bh = b * A.H + hk * A.G + step / nqb;
@@ -264,12 +280,14 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
       const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
       const int t = (int)(threadIdx.x % NT);
       const int qg = t % 8, dg = t / 8;
-      const float* src = op == 0 ? A.q : A.dout;
+      const uint16_t* src = op == 0 ? A.q : A.doh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t qq = q0 + 4 * qg + i;
-        fx[o][i] = qq < A.Sq ? *reinterpret_cast<const float4_t*>(src + (bh * A.Sq + qq) * D + 4 * dg)
-                             : float4_t{0, 0, 0, 0};
+        const bool ok = qq < A.Sq;
+        fx[o][i] = ok ? *reinterpret_cast<const uint2_t*>(src + (bh * A.Sq + qq) * D + 4 * dg) : uint2_t{0, 0};
+        if (SPL && op == 1)
+          fxl[SPL ? i : 0] = ok ? *reinterpret_cast<const uint2_t*>(A.dol + (bh * A.Sq + qq) * D + 4 * dg) : uint2_t{0, 0};
       }
     }
     if (threadIdx.x < QB) {
@@ -285,29 +303,26 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
       const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
       const int t = (int)(threadIdx.x % NT);
       const int qg = t % 8, dg = t / 8;
-      const bool split = SPL && op == 1;
       // [query][d] image: Q^ always, dO for dK; [d][query] image: dO for dV, Q^ for dK
       uint16_t* ra = op == 0 ? Qa : (DV ? nullptr : Oa);
       uint16_t* rb = (op == 1) == DV ? Xb : nullptr;
       if (ra) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint2_t h, l;
-          if (split) split4<true>(fx[o][i], h, l);
-          else split4<false>(fx[o][i], h, l);
-          *reinterpret_cast<uint2_t*>(ra + (4 * qg + i) * RA + 4 * dg) = h;
-          if (!DV && SPL && split) *reinterpret_cast<uint2_t*>(Oal + (4 * qg + i) * RA + 4 * dg) = l;
+          *reinterpret_cast<uint2_t*>(ra + (4 * qg + i) * RA + 4 * dg) = fx[o][i];
+          if (!DV && SPL && op == 1) *reinterpret_cast<uint2_t*>(Oal + (4 * qg + i) * RA + 4 * dg) = fxl[SPL ? i : 0];
         }
       }
       if (rb) {
+        uint2_t tr[4];
+        transpose4x4_16(fx[o], tr);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint2_t h, l;
-          const float4_t y = float4_t{fx[o][0][j], fx[o][1][j], fx[o][2][j], fx[o][3][j]};
-          if (split) split4<true>(y, h, l);
-          else split4<false>(y, h, l);
-          *reinterpret_cast<uint2_t*>(rb + (4 * dg + j) * RB + 4 * qg) = h;
-          if (DV && SPL && split) *reinterpret_cast<uint2_t*>(Xbl + (4 * dg + j) * RB + 4 * qg) = l;
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2_t*>(rb + (4 * dg + j) * RB + 4 * qg) = tr[j];
+        if (DV && SPL && op == 1) {
+          uint2_t trl[4];
+          transpose4x4_16(*reinterpret_cast<const uint2_t(*)[4]>(fxl), trl);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2_t*>(Xbl + (4 * dg + j) * RB + 4 * qg) = trl[j];
         }
       }
     }
@@ -453,7 +468,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
 // no P^), and accumulates dQ^T with K^T staged transposed in LDS.
 
 struct QArgs {
-  const float *q, *k, *v, *dout, *D, *lse;
+  const uint16_t *q, *k, *v, *doh, *dol;
+  const float *D, *lse;
   float* dq;
   int64_t H, G, Sq, Sk;
   int causal, nqt;
@@ -469,8 +485,8 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
   const int64_t BH = gridDim.x / A.nqt;
   const int64_t gi = blockIdx.x;
-  const int64_t bh = gi % BH, qrank = gi / BH;
-  const int qt = (int)(A.causal ? A.nqt - 1 - qrank : qrank);  // heaviest causal rows first
+  const int64_t bh = gi % BH, qrank = gi / BH;  // heads interleaved, the heaviest causal rows first
+  const int qt = (int)(A.causal ? A.nqt - 1 - qrank : qrank);
   const int64_t b = bh / A.H, h = bh - b * A.H;
   const int64_t bhk = b * (A.H / A.G) + h / A.G;
   const int64_t q = (int64_t)qt * kGT + 32 * wave + r32;
@@ -479,9 +495,9 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
   uint4_t qf[D / 16], df[D / 16], dl[SPLIT_DO ? D / 16 : 1];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    uint4_t unused;
-    frag8<false>(A.q + qidx * D + 16 * s + 8 * hi, qok, qf[s], unused);
-    frag8<SPLIT_DO>(A.dout + qidx * D + 16 * s + 8 * hi, qok, df[s], dl[SPLIT_DO ? s : 0]);
+    qf[s] = fragb(A.q + qidx * D + 16 * s + 8 * hi, qok);
+    df[s] = fragb(A.doh + qidx * D + 16 * s + 8 * hi, qok);
+    if (SPLIT_DO) dl[SPLIT_DO ? s : 0] = fragb(A.dol + qidx * D + 16 * s + 8 * hi, qok);
   }
   const float lse2 = qok ? A.lse[qidx] * 1.4426950408889634f : 0.0f;
   const float Dq = qok ? A.D[qidx] : 0.0f;
@@ -491,8 +507,8 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
   const int64_t qend = ((int64_t)qt + 1) * kGT;
   const int64_t kend = A.causal && qend < A.Sk ? qend : A.Sk;
   const int ntile = (int)((kend + KT - 1) / KT);
-  const float* kb = A.k + bhk * A.Sk * D;
-  const float* vb = A.v + bhk * A.Sk * D;
+  const uint16_t* kb = A.k + bhk * A.Sk * D;
+  const uint16_t* vb = A.v + bhk * A.Sk * D;
   const int kr = krow2(r32);
   for (int tile = 0; tile < ntile; ++tile) {
     const int64_t key0 = (int64_t)tile * KT;
@@ -504,28 +520,23 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
       for (int u = 0; u < KT * D / 16 / 256; ++u) {
         const int id = t + 256 * u;
         const int kg = id % (KT / 4), dg = id / (KT / 4);
-        float4_t xk[4], xv[4];
+        uint2_t xk[4], xv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t kk = key0 + 4 * kg + i;
           const bool ok = kk < A.Sk;
-          xk[i] = ok ? *reinterpret_cast<const float4_t*>(kb + kk * D + 4 * dg) : float4_t{0, 0, 0, 0};
-          xv[i] = ok ? *reinterpret_cast<const float4_t*>(vb + kk * D + 4 * dg) : float4_t{0, 0, 0, 0};
+          xk[i] = ok ? *reinterpret_cast<const uint2_t*>(kb + kk * D + 4 * dg) : uint2_t{0, 0};
+          xv[i] = ok ? *reinterpret_cast<const uint2_t*>(vb + kk * D + 4 * dg) : uint2_t{0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint2_t hk, hv, unused;
-          split4<false>(xk[i], hk, unused);  // K^ and V^ are bf16 numbers: exact
-          split4<false>(xv[i], hv, unused);
-          *reinterpret_cast<uint2_t*>(Ka + (4 * kg + i) * RA + 4 * dg) = hk;
-          *reinterpret_cast<uint2_t*>(Va + (4 * kg + i) * RA + 4 * dg) = hv;
+          *reinterpret_cast<uint2_t*>(Ka + (4 * kg + i) * RA + 4 * dg) = xk[i];
+          *reinterpret_cast<uint2_t*>(Va + (4 * kg + i) * RA + 4 * dg) = xv[i];
         }
+        uint2_t tr[4];
+        transpose4x4_16(xk, tr);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint2_t hk, unused;
-          split4<false>(float4_t{xk[0][j], xk[1][j], xk[2][j], xk[3][j]}, hk, unused);
-          *reinterpret_cast<uint2_t*>(Kt + (4 * dg + j) * RT + 4 * kg) = hk;
-        }
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2_t*>(Kt + (4 * dg + j) * RT + 4 * kg) = tr[j];
       }
     }
     __syncthreads();
@@ -582,7 +593,8 @@ using namespace fp4dev;
 size_t fp4i_attn_bwd_workspace(const AttnBwdLaunch& L) {
   auto a = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t nq = (size_t)(L.B * L.H * L.Sq), nk = (size_t)(L.B * L.Hkv * L.Sk);
-  return a(nq * L.d * 4) * 2 + a(nk * L.d * 4) * 2 + a(nq * 4);
+  // bf16 Q^, K^, V^; the two bf16 terms of an fp16 dO; D
+  return a(nq * L.d * 2) * 3 + a(nk * L.d * 2) * 2 + a(nq * 4);
 }
 
 hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
@@ -591,10 +603,11 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   const size_t nq = (size_t)(B * H * Sq), nk = (size_t)(B * Hkv * Sk);
   const bool fp16_do = L.dtype == 1;  // dO in fp16 is not a bf16 number: split it
   char* w = (char*)L.ws;
-  float* qh = (float*)w; w += a(nq * d * 4);
-  float* dof = (float*)w; w += a(nq * d * 4);
-  float* kh = (float*)w; w += a(nk * d * 4);
-  float* vh = (float*)w; w += a(nk * d * 4);
+  uint16_t* qh = (uint16_t*)w; w += a(nq * d * 2);
+  uint16_t* doh = (uint16_t*)w; w += a(nq * d * 2);
+  uint16_t* dol = (uint16_t*)w; w += a(nq * d * 2);
+  uint16_t* kh = (uint16_t*)w; w += a(nk * d * 2);
+  uint16_t* vh = (uint16_t*)w; w += a(nk * d * 2);
   float* Dv = (float*)w;
   auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
   // operands
@@ -604,20 +617,30 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
                      (int)d, kh);
   hipLaunchKernelGGL(dequant_cols_kernel, blocks((int64_t)nk / 2 * d), dim3(256), 0, st, L.vc, L.vs, (int64_t)nk,
                      (int)d, vh);
-  if (L.dtype == 1)
-    hipLaunchKernelGGL(to_f32_kernel<half_t>, blocks((int64_t)nq * d), dim3(256), 0, st, (const half_t*)L.dout,
-                       (int64_t)nq * d, dof);
-  else
-    hipLaunchKernelGGL(to_f32_kernel<uint16_t>, blocks((int64_t)nq * d), dim3(256), 0, st, (const uint16_t*)L.dout,
-                       (int64_t)nq * d, dof);
+  const uint16_t* dO_hi = (const uint16_t*)L.dout;  // a bf16 dO is used as it is
+  const uint16_t* dO_lo = nullptr;
+  if (fp16_do) {
+    hipLaunchKernelGGL(split_f16_kernel, blocks((int64_t)nq * d), dim3(256), 0, st, (const half_t*)L.dout,
+                       (int64_t)nq * d, doh, dol);
+    dO_hi = doh;
+    dO_lo = dol;
+  }
   const dim3 rd((unsigned)((nq + 3) / 4));
-  if (L.hp_dtype == 2) hipLaunchKernelGGL(row_dot_kernel<float>, rd, dim3(256), 0, st, dof, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
-  else if (L.hp_dtype == 1) hipLaunchKernelGGL(row_dot_kernel<half_t>, rd, dim3(256), 0, st, dof, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
-  else hipLaunchKernelGGL(row_dot_kernel<uint16_t>, rd, dim3(256), 0, st, dof, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  if (fp16_do) {
+    const half_t* dO = (const half_t*)L.dout;
+    if (L.hp_dtype == 2) hipLaunchKernelGGL((row_dot_kernel<half_t, float>), rd, dim3(256), 0, st, dO, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
+    else if (L.hp_dtype == 1) hipLaunchKernelGGL((row_dot_kernel<half_t, half_t>), rd, dim3(256), 0, st, dO, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+    else hipLaunchKernelGGL((row_dot_kernel<half_t, uint16_t>), rd, dim3(256), 0, st, dO, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  } else {
+    const uint16_t* dO = (const uint16_t*)L.dout;
+    if (L.hp_dtype == 2) hipLaunchKernelGGL((row_dot_kernel<uint16_t, float>), rd, dim3(256), 0, st, dO, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
+    else if (L.hp_dtype == 1) hipLaunchKernelGGL((row_dot_kernel<uint16_t, half_t>), rd, dim3(256), 0, st, dO, (const half_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+    else hipLaunchKernelGGL((row_dot_kernel<uint16_t, uint16_t>), rd, dim3(256), 0, st, dO, (const uint16_t*)L.out_hp, (int64_t)nq, (int)d, Dv);
+  }
   const float alpha = L.c * 0.69314718055994531f;  // s = c ln 2
   // dQ per 128 query rows
   QArgs qa;
-  qa.q = qh; qa.k = kh; qa.v = vh; qa.dout = dof; qa.D = Dv; qa.lse = L.lse;
+  qa.q = qh; qa.k = kh; qa.v = vh; qa.doh = dO_hi; qa.dol = dO_lo; qa.D = Dv; qa.lse = L.lse;
   qa.dq = L.dq;
   qa.H = H; qa.G = G; qa.Sq = Sq; qa.Sk = Sk;
   qa.causal = L.causal;
@@ -636,7 +659,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   // dK and dV per key tile, over the G query heads of each kv head
   KvArgs ka;
-  ka.q = qh; ka.k = kh; ka.v = vh; ka.dout = dof; ka.D = Dv; ka.lse = L.lse;
+  ka.q = qh; ka.k = kh; ka.v = vh; ka.doh = dO_hi; ka.dol = dO_lo; ka.D = Dv; ka.lse = L.lse;
   ka.dk = L.dk; ka.dv = L.dv;
   ka.H = H; ka.G = G; ka.Sq = Sq; ka.Sk = Sk;
   ka.kv_tile = L.kv_tile; ka.causal = L.causal; ka.single = L.single;
