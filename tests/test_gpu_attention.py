@@ -166,3 +166,29 @@ def test_single_level_p(gpu, d, kv_tile, causal, pct):
     np.testing.assert_allclose(lse.cpu().numpy().reshape(-1), rlse.reshape(-1), atol=1e-3)
     two, _ = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=kv_tile, pct=pct)
     assert np.abs(two - ref).max() > 1e-3  # the two schemes differ: the test tells them apart
+
+
+@pytest.mark.parametrize("single", [False, True])
+def test_peaked_scores_move_the_reference(gpu, single):
+    """Scores that jump by tens of binades between tiles.  Keys 20 and 300 lie
+    along a direction u that every query shares, 40 and about 100 binades above
+    the rest: rows that see key 300 raise their running reference at its tile,
+    and later tiles fall more than 2^64 below it and are left out.  Those rows
+    are one-hot in the quantized operands too (key 300 gets e = 1, P^ = 1
+    exactly), so the comparison does not hinge on ulp-level rounding near a
+    code boundary."""
+    q, k, v = synth.qkv(1, 2, 640, 128, seed=131)
+    u = torch.ones(128) / 128 ** 0.5
+    q = (q.float() + 2.0 * u).to(torch.bfloat16)
+    k = k.float()
+    k[:, :, 20] = 160.0 * u
+    k[:, :, 300] = 400.0 * u
+    k = k.to(torch.bfloat16)
+    case(f"attn peaked scores S=640 single_level={single}")
+    for causal in (True, False):
+        out, lse = gpu.fp4_attention_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, out_dtype=gpu.FP32,
+                                         single_level_p=single)
+        torch.cuda.synchronize()
+        ref, rlse = oracle.attention_fwd(q, k, v, causal=causal, single_level_p=single)
+        assert_close_attn(out.cpu().numpy().reshape(ref.shape), ref, "peaked scores")
+        np.testing.assert_allclose(lse.cpu().numpy().reshape(rlse.shape), rlse, atol=1e-3)
