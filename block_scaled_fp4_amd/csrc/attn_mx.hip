@@ -238,23 +238,27 @@ __device__ __forceinline__ void mx_wave_tile(const MxSmem<D, BC>& S, const uint4
   float lsum = 0.0f;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    float e[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][i], c, off));
-      lsum += e[i];
-    }
     float em = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[g], c, off));
     em = __builtin_fmaxf(em, xor32(em));
     int sh = em > 0.0f ? __builtin_amdgcn_frexp_expf(em) - 3 : -127;  // floor(log2 max e) - 2
     sh = sh < -127 ? -127 : sh;
+    // the quantization inputs t = e / 2^sh come out of one exp2: the reference and the shift
+    // are integers, so off - sh is exact; the denominator takes the block sum of t times 2^sh
+    const float offs = off - (float)sh;
+    float t[16], bs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][i], c, offs));
+      bs += t[i];
+    }
+    lsum += __builtin_ldexpf(bs, sh);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t w = 0;
-      w = cvt_pk_fp4<0>(w, __builtin_ldexpf(e[8 * h + 0], -sh), __builtin_ldexpf(e[8 * h + 1], -sh));
-      w = cvt_pk_fp4<1>(w, __builtin_ldexpf(e[8 * h + 2], -sh), __builtin_ldexpf(e[8 * h + 3], -sh));
-      w = cvt_pk_fp4<2>(w, __builtin_ldexpf(e[8 * h + 4], -sh), __builtin_ldexpf(e[8 * h + 5], -sh));
-      w = cvt_pk_fp4<3>(w, __builtin_ldexpf(e[8 * h + 6], -sh), __builtin_ldexpf(e[8 * h + 7], -sh));
+      w = cvt_pk_fp4<0>(w, t[8 * h + 0], t[8 * h + 1]);
+      w = cvt_pk_fp4<1>(w, t[8 * h + 2], t[8 * h + 3]);
+      w = cvt_pk_fp4<2>(w, t[8 * h + 4], t[8 * h + 5]);
+      w = cvt_pk_fp4<3>(w, t[8 * h + 6], t[8 * h + 7]);
       pc[g][h] = w;
     }
     int sb = sh + 127 + rexp;  // the tile weight rides on the block scale
