@@ -186,11 +186,13 @@ def bench_prefill8k(fp4, synth, torch, n):
 # candidate one multiply (element times reciprocal scale), one E2M1 convert
 # there and back (a packed pair per instruction: half an instruction each),
 # one fused error term, one square and one tree addition -- 5 lane operations,
-# 45 per element for the 9 offsets.  The ALU peak is one lane operation per
-# lane per clock: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T lane-ops/s
-# (the published 157.3 TFLOP/s fp32 counts an FMA as two).
+# 45 per element for the 9 offsets.  The ALU peak: an unpacked 32-bit VALU
+# instruction processes 16 lanes per clock on each SIMD (a wave of 64 in 4
+# clocks): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.  (The
+# published 157.3 TFLOP/s fp32 counts an FMA as two flops and packed FP32 as
+# two lanes; packed FP32 is not used here.)
 QUANT_LANE_OPS_PER_ELEM = 45
-VALU_PEAK_TOPS = 78.6
+VALU_PEAK_TOPS = 39.3
 
 
 def bench_quantizer(fp4, synth, torch, n):
