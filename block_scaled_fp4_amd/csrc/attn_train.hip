@@ -217,6 +217,22 @@ __device__ __forceinline__ float rowmax16(float v) {
   return dpp_max<0x4E>(v);
 }
 
+// lane n of each 16-lane DPP row, broadcast to the row
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+
+// dst[k][n] = src[k] of lane n of this lane's row, for n = 0..15
+template <int N = 0>
+__device__ __forceinline__ void row_bcast_all(const float (&src)[4], float (&dst)[4][16]) {
+  if constexpr (N < 16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k][N] = row_bcast<N>(src[k]);
+    row_bcast_all<N + 1>(src, dst);
+  }
+}
+
 // 8 fp32 -> 8 bf16 (hi, and lo when SPLIT) as one MFMA operand
 template <bool SPLIT>
 __device__ __forceinline__ void pack8(const float* x, uint4_t& hi, uint4_t& lo) {
@@ -372,49 +388,36 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
         }
       }
       __syncthreads();
-      // tile maximum per query over the kv_tile keys' blocks
+      // The scale data of a (query, 16-key block) is the same in all 16 lanes of the block's DPP
+      // row: lane i of each row works it out for value i (query qof(i)), then each value is
+      // broadcast across the row.
       const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
       const int ne = A.kv_tile == 128 ? 8 : 4;
-      float tm[16], l2[16];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qb = 8 * hi + 16 * h;
-        float4_t a = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 : 0][qb]);
-        float4_t c = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 : 0][qb + 4]);
-        for (int e = 1; e < ne; ++e) {
-          const float4_t a2 = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 + e : 0][qb]);
-          const float4_t c2 = *reinterpret_cast<const float4_t*>(&tmx[DV ? e0 + e : 0][qb + 4]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a[j] = __builtin_fmaxf(a[j], a2[j]);
-            c[j] = __builtin_fmaxf(c[j], c2[j]);
-          }
-        }
-        const float4_t la = *reinterpret_cast<const float4_t*>(&lse_s[qb]);
-        const float4_t lc = *reinterpret_cast<const float4_t*>(&lse_s[qb + 4]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          tm[8 * h + j] = a[j]; tm[8 * h + 4 + j] = c[j];
-          l2[8 * h + j] = la[j]; l2[8 * h + 4 + j] = lc[j];
-        }
-      }
-      float t[16], f1[16], wv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // a block with no visible key gets scale 0 (t = 0, P^ = 0)
-        const bool live = bm[v] != -__builtin_inff();
-        const float emax = live ? __builtin_amdgcn_exp2f(bm[v] - tm[v]) : 0.0f;
+      float sd[4];  // this lane's value: tile maximum, element factor, s2, tile weight
+      {
+        const int qi = qof(r32 & 15);
+        const float bmi = tmx[2 * wave + (r32 >> 4)][qi];
+        float tmi = tmx[e0][qi];
+        for (int e = 1; e < ne; ++e) tmi = __builtin_fmaxf(tmi, tmx[e0 + e][qi]);
+        const bool live = bmi != -__builtin_inff();  // a block with no visible key gets scale 0
+        const float emax = live ? __builtin_amdgcn_exp2f(bmi - tmi) : 0.0f;
         const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
         const float2_t fs = ptab[DV ? byte : 0];
-        wv[v] = live ? __builtin_amdgcn_exp2f(tm[v] - l2[v]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
-        t[v] = live ? __builtin_amdgcn_exp2f(x[v] - tm[v]) * fs[0] : 0.0f;
-        f1[v] = fs[1];
+        sd[0] = live ? tmi : 0.0f;
+        sd[1] = fs[0];
+        sd[2] = fs[1];
+        sd[3] = live ? __builtin_amdgcn_exp2f(tmi - lse_s[qi]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
       }
+      float bc[4][16];
+      row_bcast_all(sd, bc);
+      float t[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t[v] = bm[v] != -__builtin_inff() ? __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v] : 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
         const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
-        w16[v] = cv[0] * f1[v] * wv[v];  // code value times s2 is exact; one rounding for the weight
-        w16[v + 1] = cv[1] * f1[v + 1] * wv[v + 1];
+        w16[v] = cv[0] * bc[2][v] * bc[3][v];  // code value times s2 is exact; one rounding for the weight
+        w16[v + 1] = cv[1] * bc[2][v + 1] * bc[3][v + 1];
       }
     } else {
 #pragma unroll
