@@ -137,11 +137,11 @@ __constant__ TrainPTable kTrainP = TrainPTable();
 // The products keep binary32 accuracy on the bf16 matrix instructions: an
 // operand whose values are bf16 numbers (the dequantized NVFP4 Q^, K^, V^ --
 // an E2M1 value times an E4M3 scale has at most 6 significant bits -- and dO
-// given in bf16) goes in as it is; an fp32 operand (P^, dS, dO given in
-// fp16) is split as x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi),
-// |r| <= 2^-17 |x|, and each product takes hi.hi + hi.lo + lo.hi (the lo.lo
-// term is below 2^-16 of the product).  Products are exact in the MFMA and
-// accumulate in fp32.
+// given in bf16) goes in as it is; an fp32 operand (P^, dS) is split as
+// x = hi + lo + r with |r| <= 2^-16 |x| (see pack8), and an fp16 dO exactly
+// as hi + lo; each product takes hi.B + lo.B (with an fp16 dO on the other
+// side, hi.lo too; the dropped lo.lo term is below 2^-14 of the product).
+// Products are exact in the MFMA and accumulate in fp32.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -233,14 +233,29 @@ __device__ __forceinline__ void row_bcast_all(const float (&src)[4], float (&dst
   }
 }
 
-// 8 fp32 -> 8 bf16 (hi, and lo when SPLIT) as one MFMA operand
+// 8 fp32 -> 8 bf16 (hi, and lo when SPLIT) as one MFMA operand.  Without the
+// split the values are bf16 numbers and hi is exact.  With it, hi is x cut to
+// its top 16 bits (exact difference x - hi, below 2^-7 |x|) and lo that
+// difference rounded to bf16, so |x - hi - lo| <= 2^-16 |x|.
 template <bool SPLIT>
 __device__ __forceinline__ void pack8(const float* x, uint4_t& hi, uint4_t& lo) {
-  uint2_t ha, la, hb, lb;
-  split4<SPLIT>(float4_t{x[0], x[1], x[2], x[3]}, ha, la);
-  split4<SPLIT>(float4_t{x[4], x[5], x[6], x[7]}, hb, lb);
-  hi = uint4_t{ha[0], ha[1], hb[0], hb[1]};
-  lo = uint4_t{la[0], la[1], lb[0], lb[1]};
+  if (!SPLIT) {
+    uint2_t ha, la, hb, lb;
+    split4<false>(float4_t{x[0], x[1], x[2], x[3]}, ha, la);
+    split4<false>(float4_t{x[4], x[5], x[6], x[7]}, hb, lb);
+    hi = uint4_t{ha[0], ha[1], hb[0], hb[1]};
+    lo = uint4_t{0u, 0u, 0u, 0u};
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = __float_as_uint(x[2 * j]), b = __float_as_uint(x[2 * j + 1]);
+    hi[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // top halves of a (low) and b (high)
+    const uint32_t ra = __float_as_uint(x[2 * j] - __uint_as_float(a & 0xFFFF0000u));
+    const uint32_t rb = __float_as_uint(x[2 * j + 1] - __uint_as_float(b & 0xFFFF0000u));
+    const uint32_t qa = ra + 0x7FFFu + ((ra >> 16) & 1u), qb = rb + 0x7FFFu + ((rb >> 16) & 1u);
+    lo[j] = __builtin_amdgcn_perm(qb, qa, 0x07060302u);
+  }
 }
 
 template <int D, bool SPLIT_DO, int MODE>  // MODE 0: dV, 1: dK
