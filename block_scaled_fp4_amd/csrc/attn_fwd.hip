@@ -500,14 +500,16 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
     return q;
   };
   auto make_half = [&](int g, int h2, const PPrep& q, half8_t& pf) {
-    float t[8], bsum = 0.0f;
+    float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, q.off));
-      bsum += t[i];
-    }
+    for (int i = 0; i < 8; ++i) t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g][8 * h2 + i], c, q.off));
+    float bsum = t[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) bsum += t[i];
     if (FP4) {
-      uint32_t w = 0;
+      // every byte of w is written below: its start value only lends the
+      // register (t[0]'s, free once its pair is converted)
+      uint32_t w = __float_as_uint(t[0]);
       w = cvt_pk_fp4<0>(w, t[0], t[1]);
       w = cvt_pk_fp4<1>(w, t[2], t[3]);
       w = cvt_pk_fp4<2>(w, t[4], t[5]);

@@ -31,18 +31,15 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return __uint_as_float((((b >> 3) + 120u) << 23) | ((b & 7u) << 20));
 }
 
-// Nearest E4M3 byte to v >= 0 (finite), ties to the even mantissa, saturating
-// at 0x7E = 448 (never the NaN byte 0x7F).
+// Nearest E4M3 byte to v >= +0, ties to the even mantissa, saturating at
+// 0x7E = 448 (never the NaN byte 0x7F).  gfx950's fp8 convert rounds to
+// nearest even into the OCP E4M3 format, subnormals included, and agrees with
+// that rounding on every binary32 in [0, 464]; past 464 it returns the NaN
+// code instead of saturating, so the input is first bounded by 448.  The mask
+// keeps the byte inside the 128-entry scale tables.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  // Branch-free: both the normal-range rounding and the subnormal one are
-  // formed and the right one selected; values past 448 saturate through the
-  // final minimum (their exponent field lands above 0x7E).
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);  // round mantissa to 3 bits, ties to even
-  const uint32_t normal = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-  const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);  // subnormal step 2^-9 (exact scaling)
-  const uint32_t byte = v < 0x1p-6f ? sub : normal;
-  return byte > 0x7Eu ? 0x7Eu : byte;
+  const float b = __builtin_fminf(v, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(b, 0.0f, 0, false) & 0x7Fu;
 }
 
 // Nearest E4M3 byte to the exact quotient a/6 (a >= 0 finite).  Exactly the

@@ -276,8 +276,10 @@ int fp4_attention_fwd_train(const fp4_attn_problem* prob, const fp4_attn_opts* o
  *   dS = c ln2 * P * (dO V^T - rowsum(dO * O')),  P = 2^(x - lse log2 e),
  * with Q^, K^, V^ the NVFP4 operands of the forward (quantized again here
  * unless given).  Needs fp16_budget_pct == 0 and no rotation.  The scores
- * are recomputed, never stored: the workspace holds binary32 copies of Q^,
- * K^, V^ and dO and one float per query row (see the query).
+ * are recomputed, never stored: the workspace holds bfloat16 copies of Q^,
+ * K^ and V^ (exact, as every E2M1 x E4M3 product has at most six significant
+ * bits), dO as one bfloat16 term or, for binary16 dO, as two bfloat16 terms
+ * whose sum is exact, and one float per query row (see the query).
  */
 int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, const void* out_hp, const float* lse,
                       const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
