@@ -45,8 +45,14 @@ def attn_flops(B, H, S, d, causal=True):
 
 
 def source_hash(name):
-    p = os.path.join(ROOT, "block_scaled_fp4_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of a kernel's source file followed by every
+    header of the library sources, so that a change to shared device code
+    also marks the counter summaries taken before it as stale."""
+    csrc = os.path.join(ROOT, "block_scaled_fp4_amd", "csrc")
+    h = hashlib.sha256(open(os.path.join(csrc, name), "rb").read())
+    for hdr in sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
+        h.update(open(os.path.join(csrc, hdr), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_profile(name, kernel_src, key):
