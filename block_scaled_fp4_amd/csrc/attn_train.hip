@@ -382,11 +382,18 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
       }
     }
     float x[16];
+    // every (key, query) pair of the wave's step visible: no mask (the common case)
+    const int64_t wkey1 = key0 + 32 * wave + 31;  // the wave's last key
+    if (wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t qq = q0 + qof(v);
-      const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
-      x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+      for (int v = 0; v < 16; ++v) x[v] = sacc[v] * A.c;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t qq = q0 + qof(v);
+        const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
+        x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+      }
     }
     float w16[16];  // the A operand values of this step: P^ (dV) or dS (dK)
     if (DV) {
@@ -572,12 +579,21 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
         if (SPLIT_DO) dp = mfma_bf16(a, dl[k], dp);
       }
       float ds[16];
+      // every (key, query) pair of the wave's subtile visible: no mask (the common case; with
+      // the split dO the second copy of the loop would not fit the registers)
+      const int64_t skey1 = key0 + 32 * g + 31, wq0 = q - r32;
+      if (!SPLIT_DO && wq0 + 32 <= A.Sq && skey1 < A.Sk && (!A.causal || skey1 <= wq0)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t key = key0 + 32 * g + (v & 7) + 8 * hi + 16 * (v >> 3);
-        const bool vis = qok && key < A.Sk && (!A.causal || key <= q);
-        const float x = vis ? s[v] * A.c : -__builtin_inff();
-        ds[v] = A.alpha * __builtin_amdgcn_exp2f(x - lse2) * (dp[v] - Dq);  // P masked: 0
+        for (int v = 0; v < 16; ++v)
+          ds[v] = A.alpha * __builtin_amdgcn_exp2f(s[v] * A.c - lse2) * (dp[v] - Dq);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t key = key0 + 32 * g + (v & 7) + 8 * hi + 16 * (v >> 3);
+          const bool vis = qok && key < A.Sk && (!A.causal || key <= q);
+          const float x = vis ? s[v] * A.c : -__builtin_inff();
+          ds[v] = A.alpha * __builtin_amdgcn_exp2f(x - lse2) * (dp[v] - Dq);  // P masked: 0
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
