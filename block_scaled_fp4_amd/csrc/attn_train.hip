@@ -224,13 +224,21 @@ __device__ __forceinline__ float row_bcast(float x) {
 }
 
 // dst[k][n] = src[k] of lane n of this lane's row, for n = 0..15
-template <int N = 0>
-__device__ __forceinline__ void row_bcast_all(const float (&src)[4], float (&dst)[4][16]) {
+template <int K, int N = 0>
+__device__ __forceinline__ void row_bcast_all(const float (&src)[K], float (&dst)[K][16]) {
   if constexpr (N < 16) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dst[k][N] = row_bcast<N>(src[k]);
-    row_bcast_all<N + 1>(src, dst);
+    for (int k = 0; k < K; ++k) dst[k][N] = row_bcast<N>(src[k]);
+    row_bcast_all<K, N + 1>(src, dst);
   }
+}
+
+// Two binary32 values -> two bf16 (round to nearest even) in one dword, low
+// half first: gfx950's packed convert.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
 }
 
 // 8 fp32 -> 8 bf16 (hi, and lo when SPLIT) as one MFMA operand.  Without the
@@ -251,10 +259,7 @@ __device__ __forceinline__ void pack8(const float* x, uint4_t& hi, uint4_t& lo) 
   for (int j = 0; j < 4; ++j) {
     const uint32_t a = __float_as_uint(x[2 * j]), b = __float_as_uint(x[2 * j + 1]);
     hi[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // top halves of a (low) and b (high)
-    const uint32_t ra = __float_as_uint(x[2 * j] - __uint_as_float(a & 0xFFFF0000u));
-    const uint32_t rb = __float_as_uint(x[2 * j + 1] - __uint_as_float(b & 0xFFFF0000u));
-    const uint32_t qa = ra + 0x7FFFu + ((ra >> 16) & 1u), qb = rb + 0x7FFFu + ((rb >> 16) & 1u);
-    lo[j] = __builtin_amdgcn_perm(qb, qa, 0x07060302u);
+    lo[j] = bf16x2_rne(x[2 * j] - __uint_as_float(a & 0xFFFF0000u), x[2 * j + 1] - __uint_as_float(b & 0xFFFF0000u));
   }
 }
 
@@ -415,7 +420,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
       // broadcast across the row.
       const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
       const int ne = A.kv_tile == 128 ? 8 : 4;
-      float sd[4];  // this lane's value: tile maximum, element factor, s2, tile weight
+      float sd[3];  // this lane's value: tile maximum, element factor, s2 times the tile weight
       {
         const int qi = qof(r32 & 15);
         const float bmi = tmx[2 * wave + (r32 >> 4)][qi];
@@ -427,10 +432,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
         const float2_t fs = ptab[DV ? byte : 0];
         sd[0] = live ? tmi : 0.0f;
         sd[1] = fs[0];
-        sd[2] = fs[1];
-        sd[3] = live ? __builtin_amdgcn_exp2f(tmi - lse_s[qi]) * (A.single ? 1.0f : 1.0f / 2688.0f) : 0.0f;
+        sd[2] = live ? fs[1] * (__builtin_amdgcn_exp2f(tmi - lse_s[qi]) * (A.single ? 1.0f : 1.0f / 2688.0f)) : 0.0f;
       }
-      float bc[4][16];
+      float bc[3][16];
       row_bcast_all(sd, bc);
       float t[16];
 #pragma unroll
@@ -438,8 +442,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
         const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
-        w16[v] = cv[0] * bc[2][v] * bc[3][v];  // code value times s2 is exact; one rounding for the weight
-        w16[v + 1] = cv[1] * bc[2][v + 1] * bc[3][v + 1];
+        w16[v] = cv[0] * bc[2][v];  // (s2 times the weight is rounded once, then the product)
+        w16[v + 1] = cv[1] * bc[2][v + 1];
       }
     } else {
 #pragma unroll
