@@ -65,6 +65,31 @@ def test_special_values(gpu):
     _run(gpu, x.t().contiguous(), 1, True)
 
 
+def test_scale_rounding_boundaries(gpu):
+    """Blocks whose amax / 6 sits on or next to an E4M3 rounding point: ties
+    between normal neighbours (even mantissa wins), ties in the subnormal
+    range (steps of 2^-9), and the band between 448 and the next would-be
+    step, where the scale byte saturates at 0x7E."""
+    e4m3 = [k / 512 for k in range(8)] + [(1 + m / 8) * 2.0 ** e for e in range(-6, 9) for m in range(8)]
+    e4m3 = sorted(v for v in e4m3 if v <= 448)
+    mids = [(a + b) / 2 for a, b in zip(e4m3, e4m3[1:])]
+    picks = mids[:10] + mids[50:60] + mids[-10:] + [448.0, 452.0, 456.0, 460.0, 464.0, 466.0, 470.0, 480.0]
+    amax = []
+    for m in picks:  # the midpoint itself and its binary32 neighbours, times 6 (exact in binary32 or next to it)
+        f = np.float32(m * 6)
+        amax += [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(0))]
+    x = torch.zeros(len(amax), 32, dtype=torch.float32)
+    g = torch.Generator().manual_seed(21)
+    for i, a in enumerate(amax):
+        row = torch.rand(32, generator=g) * float(a)
+        row[i % 16] = float(a)
+        row[16 + (i * 7) % 16] = -float(a)
+        x[i] = row
+    case("quantize E4M3 rounding boundaries")
+    _run(gpu, x, 0, True)
+    _run(gpu, x, 0, False)
+
+
 def test_offset_ranges(gpu):
     g = torch.Generator().manual_seed(13)
     x = torch.randn(64, 64, generator=g).to(torch.bfloat16)
