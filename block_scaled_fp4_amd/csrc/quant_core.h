@@ -68,7 +68,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float* y) {
 // 8 values -> 8 E2M1 codes in one dword (nearest, ties to the even code,
 // saturating at 6; the magnitude is rounded, the sign follows the value).
 __device__ __forceinline__ uint32_t pack8(const float* t) {
-  uint32_t w = 0;
+  // every byte of w is written below: its start value only lends a register
+  // (t[0]'s, dead once its pair is converted in the callers)
+  uint32_t w = __float_as_uint(t[0]);
   w = cvt_pk_fp4<0>(w, t[0], t[1]);
   w = cvt_pk_fp4<1>(w, t[2], t[3]);
   w = cvt_pk_fp4<2>(w, t[4], t[5]);
