@@ -389,7 +389,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
     float x[16];
     // every (key, query) pair of the wave's step visible: no mask (the common case)
     const int64_t wkey1 = key0 + 32 * wave + 31;  // the wave's last key
-    if (wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0)) {
+    const bool full = wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0);
+    if (full) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) x[v] = sacc[v] * A.c;
     } else {
@@ -437,8 +438,14 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
       float bc[3][16];
       row_bcast_all(sd, bc);
       float t[16];
+      if (full) {  // no block is empty
 #pragma unroll
-      for (int v = 0; v < 16; ++v) t[v] = bm[v] != -__builtin_inff() ? __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v] : 0.0f;
+        for (int v = 0; v < 16; ++v) t[v] = __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          t[v] = bm[v] != -__builtin_inff() ? __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v] : 0.0f;
+      }
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
         const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
