@@ -632,6 +632,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     const int64_t qb = q0 / P.sel_block;
     sel = P.idx + (bh * P.nqb + qb) * P.kmax;
     nsel = P.cnt[bh * P.nqb + qb];
+    nsel = nsel < 0 ? 0 : (nsel > P.kmax ? P.kmax : nsel);  // a given count never reaches the padding
   }
   const int tiles_per_block = P.sel_block / BC;
 
@@ -642,9 +643,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   hb.vc = make_rsrc(P.vc + bhk * (Sk / 2) * D, (uint32_t)((Sk / 2) * D));
   hb.vs = make_rsrc(P.vs + bhk * (Sk / 16) * D, (uint32_t)((Sk / 16) * D));
 
-  // ---- FP4 pass: every tile not covered by a selected block
+  // ---- FP4 pass: every tile not covered by a selected block.  A block
+  // counts as selected when its index exceeds every list entry before it (the
+  // whole list, for the ascending lists the selection kernel writes); the FP16
+  // pass below takes exactly these entries, so a given list that is unsorted
+  // or repeats an index never counts a key twice or skips it.
   Fetch<D, BC> F;
-  int si = 0;  // cursor into the ascending selection list
+  int si = 0;  // cursor into the selection list
   auto selected = [&](int tile) {
     if (nsel == 0) return false;
     const int blk = tile / tiles_per_block;
@@ -693,8 +698,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     }
     const rsrc_t kr16 = make_rsrc(reinterpret_cast<const IT*>(P.k) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
     const rsrc_t vr16 = make_rsrc(reinterpret_cast<const IT*>(P.v) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
+    int prev = -1;  // entries not above every earlier entry are skipped (negative ones included)
     for (int s_i = 0; s_i < nsel; ++s_i) {
       const int blk = sel[s_i];
+      if (blk <= prev) continue;
+      prev = blk;
       for (int tt = 0; tt < tiles_per_block; ++tt) {
         const int tile = blk * tiles_per_block + tt;
         if (tile >= ntile) break;

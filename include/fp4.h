@@ -211,6 +211,12 @@ typedef struct fp4_attn_opts {
  * ceil(pct * ceil(Sk/sel_block) / 100)) and topk_cnt [B,H,ceil(Sq/sel_block)]
  * are written when non-null (otherwise kept in the workspace); with
  * opts->selection_given they are read instead and must both be non-null.
+ * A given selection should list, per query block, distinct visible key-block
+ * indices in ascending order with topk_cnt <= kmax.  What the kernel does with
+ * any other list: topk_cnt is clamped to [0, kmax]; of the first topk_cnt
+ * entries, only those greater than every entry before them are promoted
+ * (negative, repeated and out-of-order entries are ignored), and indices at or
+ * past ceil(Sk/sel_block) are ignored.  So no key is ever counted twice.
  * Requirements: d in {64, 128}; Sk % 16 == 0; causal needs Sq == Sk;
  * sel_block % kv_tile == 0; 16-byte aligned tensors.
  */

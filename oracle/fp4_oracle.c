@@ -520,6 +520,58 @@ static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss,
   return out;
 }
 
+/* Open decisions of one 16-key block of P (see attn_row): e[n] the block's
+   unquantized e, P[n] its weights, V its dequantized value rows [n][d],
+   amax, s2 and M the block maximum, scale byte and element factor.  Returns
+   the bound in the block's own weight units (before the tile weight and the
+   division by l). */
+static double block_ambiguity(const float* e, const double* P, int n, const double* V, int d, float amax,
+                              int s2, float M, float tm, int single_level, const double* tie) {
+  double vmax[16];
+  for (int j = 0; j < n; ++j) {
+    vmax[j] = 0.0;
+    for (int dd = 0; dd < d; ++dd)
+      if (fabs(V[j * d + dd]) > vmax[j]) vmax[j] = fabs(V[j * d + dd]);
+  }
+  const double s2d = orc_e4m3_value(s2);
+  const double lg = s2 ? log2((double)M) : 0.0;
+  /* (a) codes near an E2M1 midpoint under the chosen scale */
+  double codes = 0.0;
+  if (s2) {
+    for (int j = 0; j < n; ++j) {
+      if (e[j] <= 0.0f) continue;
+      const double z = log2((double)e[j]);
+      const double eps = tie[0] + tie[1] * (fabs((double)tm) + fabs(lg) + fabs(z));
+      const double t = (double)(e[j] * M);
+      const int c0 = orc_e2m1_encode(t);
+      const int lo = orc_e2m1_encode(t * (1.0 - eps)), hi = orc_e2m1_encode(t * (1.0 + eps));
+      double dv = fabs(kE2M1[lo] - kE2M1[c0]);
+      if (fabs(kE2M1[hi] - kE2M1[c0]) > dv) dv = fabs(kE2M1[hi] - kE2M1[c0]);
+      codes += dv * s2d * vmax[j];
+    }
+  }
+  /* (b) a neighbouring scale byte: the whole block requantized under it */
+  double scale = 0.0;
+  if (amax > 0.0f) {
+    const double ain = single_level ? (double)(amax / 6.0f) : (double)(amax * 448.0f);
+    const double eps = tie[0] + tie[1] * (fabs((double)tm) + fabs(lg) + fabs(log2((double)amax)));
+    const int alts[2] = {orc_e4m3_encode(ain * (1.0 - eps)), orc_e4m3_encode(ain * (1.0 + eps))};
+    for (int a = 0; a < 2; ++a) {
+      const int sa = alts[a];
+      if (sa == s2) continue;
+      const double sad = orc_e4m3_value(sa);
+      const float Ma = sa ? (single_level ? orc_recip(sa) : 2688.0f / (float)sad) : 0.0f;
+      double dev = 0.0;
+      for (int j = 0; j < n; ++j) {
+        const double pa = sa ? kE2M1[orc_e2m1_encode((double)(e[j] * Ma))] * sad : 0.0;
+        dev += fabs(pa - P[j]) * vmax[j];
+      }
+      if (dev > scale) scale = dev;
+    }
+  }
+  return codes > scale ? codes : scale;
+}
+
 /* Fake-quant FP4 attention forward for one query row.
    FP4 tile (keys t0..t1-1 visible to row i):
      S_j   = Q^_i . K^_j, exact products, rounded once to binary32
@@ -533,11 +585,32 @@ static double* quant_dequant(const float* x, int64_t S, int d, int axis, int ss,
    FP16 tile (a selected block pair): S_j from fp16(Q).fp16(K) rounded once
      to binary32, same x, tm, e; O += fp16(e) fp16(V), l += sum e.
    Tiles are merged with weights 2^(tm - m), m = max over tiles of tm; the
-   output is O / l and lse = (m + log2 l) ln 2.  The merge order is free. */
+   output is O / l and lse = (m + log2 l) ln 2.  The merge order is free.
+
+   Rounding ambiguity (tie, amb; both nullable).  The codes and block scales
+   of P are integers decided by binary32 values t = e * 2688 / s2 and
+   amax * 448 (single level: e / s2 and amax / 6).  An evaluation of the
+   same real quantity in another order of binary32 operations (a fused
+   exponent, another exp2) lands within a small relative distance of these
+   values, and where a value lies that close to a rounding boundary either
+   decision is a correct rounding.  With tie = {a, b}, a decision counts as
+   open when moving its input by the relative slack
+     eps = a + b (|tm| + |lg| + |z|),
+   (z = x - tm of the element, or of the block maximum for the scale; lg =
+   log2 of the element factor: 2688 / s2, or 1 / s2 single-level) changes it.
+   *amb receives an upper bound on how far the row's output can move, in
+   max-abs over d, when open decisions go the other way: per block, the
+   larger of (a) the sum over keys with an open code of |v(alt) - v(code)|
+   s2 max_c |V^_j[c]| and (b) the change of the whole block under an open
+   neighbouring scale byte, weighted like the tile's output and divided by
+   l (which sums the unquantized e, so it does not move).  FP16 tiles and the
+   MXFP4 mode contribute nothing (their P has no such codes here, or is not
+   covered). */
 static void attn_row(const double* qh, const double* q16, const double* Kh, const double* Vh,
                      const double* K16, const double* V16, int64_t Sk, int d, int64_t i,
                      int causal, float c, int kv_tile, const int32_t* sel, int nsel, int sel_block,
-                     int pmode, float* out, float* lse, double* Prow, double* Phrow) {
+                     int pmode, float* out, float* lse, double* Prow, double* Phrow,
+                     const double* tie, double* amb) {
   /* pmode: P on the FP4 tiles -- 0 two-level NVFP4, 1 single-level NVFP4,
      2 MXFP4 (32-key blocks, power-of-two scale by the OCP rule) */
   const int single_level = pmode != 0;
@@ -559,6 +632,7 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
   double* ls = (double*)malloc(sizeof(double) * (size_t)ntiles);
   double** Os = (double**)calloc((size_t)ntiles, sizeof(double*));
   int* isfp4 = (int*)malloc(sizeof(int) * (size_t)ntiles);
+  double* ambs = (double*)calloc((size_t)ntiles, sizeof(double));
   float m = -INFINITY;
   int64_t T;
   for (T = 0; T < ntiles; ++T) {
@@ -625,6 +699,8 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
           int code = orc_e2m1_encode((double)t);
           P[j] = kE2M1[code] * (double)s2f;
         }
+        if (tie) ambs[T] += block_ambiguity(e + b0, P + b0, b1 - b0, Vh + (t0 + b0) * d, d, amax, s2, M,
+                                            tm, single_level, tie);
       }
     }
     const double* VV = promoted ? V16 : Vh;
@@ -646,13 +722,15 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
     if (tm > m) m = tm;
   }
   int64_t nt = T;
-  double l = 0.0;
+  double l = 0.0, am = 0.0;
   for (T = 0; T < nt; ++T) {
     double r = exp2((double)tms[T] - (double)m);
     l += r * ls[T];
+    am += r * ambs[T];
     for (int dd = 0; dd < d; ++dd) Oacc[dd] += r * Os[T][dd];
     free(Os[T]);
   }
+  if (amb) *amb = nt ? am / (single_level ? 1.0 : 2688.0) / l : 0.0;
   for (int dd = 0; dd < d; ++dd) out[dd] = nt ? (float)(Oacc[dd] / l) : 0.0f;
   if (lse) *lse = nt ? (float)(((double)m + log2(l)) * 0.69314718055994530942) : -INFINITY;
   if (Prow) {
@@ -669,7 +747,7 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
     free(erow); free(qrow);
   }
   (void)isfp4;
-  free(isfp4); free(Os); free(ls); free(tms); free(P); free(e); free(x); free(Ot); free(Oacc);
+  free(isfp4); free(ambs); free(Os); free(ls); free(tms); free(P); free(e); free(x); free(Ot); free(Oacc);
 }
 
 /* Forward FP4 attention over q [B][H][Sq][d], k and v [B][Hkv][Sk][d]
@@ -684,15 +762,16 @@ static void attn_row(const double* qh, const double* q16, const double* Kh, cons
    with the NVFP4 block scale alone (no row level; the Attn-QAT page removes
    the two-level step).  probs and probs_hat (nullable, both or neither,
    [n_heads][n_rows][Sk]) receive every row's normalized probabilities and the
-   normalized weights the output uses (see attn_row).  Returns 0, or -1 on bad
-   arguments. */
+   normalized weights the output uses (see attn_row).  tie (nullable, {a, b})
+   and amb (nullable, [n_heads][n_rows]) give every row's rounding-ambiguity
+   bound (see attn_row).  Returns 0, or -1 on bad arguments. */
 int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int H, int Hkv,
                       int64_t Sq, int64_t Sk, int d, int causal, double softmax_scale, int kv_tile,
                       int scale_search, int fmin, int fmax, int pct, int sel_block,
                       const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
                       float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt,
                       const float* q_fp4, const float* k_fp4, int single_level,
-                      double* probs, double* probs_hat, int mx) {
+                      double* probs, double* probs_hat, int mx, const double* tie, double* amb) {
   /* mx: Q, K (blocks of 32 along d), V (blocks of 32 tokens) and P (blocks of
      32 keys) in MXFP4 instead of NVFP4 (scale_search does not apply) */
   const int pmode = mx ? 2 : (single_level ? 1 : 0);
@@ -766,7 +845,8 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
       attn_row(qh, q16, Kh, Vh, K16, V16, Sk, d, i, causal, c, kv_tile, sel, nsel, sel_block, pmode,
                out + ((int64_t)hi * nr + ri) * d, lse ? lse + (int64_t)hi * nr + ri : NULL,
                probs ? probs + ((int64_t)hi * nr + ri) * Sk : NULL,
-               probs ? probs_hat + ((int64_t)hi * nr + ri) * Sk : NULL);
+               probs ? probs_hat + ((int64_t)hi * nr + ri) * Sk : NULL,
+               amb ? tie : NULL, amb ? amb + (int64_t)hi * nr + ri : NULL);
       free(qh); free(q16);
     }
     free(Kh); free(Vh); free(Qmx); free(K16); free(V16); free(sidx); free(scnt);

@@ -81,7 +81,8 @@ def lib():
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
-                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int]
+                                    C.c_int, _f32p, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int,
+                                    _vp, _vp]
     L.orc_attention_fwd.restype = C.c_int
     L.orc_mx_scale_byte.argtypes = [C.c_double]; L.orc_mx_scale_byte.restype = C.c_int
     L.orc_mx_quantize.argtypes = [_f32p, C.c_int64, C.c_int64, C.c_int, _u8p, _u8p]
@@ -270,7 +271,7 @@ def _sel(arr, dtype):
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
                   with_topk=False, hadamard=False, signs=None, single_level_p=False, with_probs=False,
-                  mx=False):
+                  mx=False, tie_slack=None):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
 
     hadamard: the FP4 path quantizes Q and K after incoherence processing
@@ -282,6 +283,12 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
     normalized probabilities P and the
     normalized weights P^ the output uses (float64 [nh, nr, Sk] each), after
     the other results.
+
+    tie_slack = (a, b): also return, last, every row's rounding-ambiguity
+    bound amb [nh, nr] (float64): how far the row's output (max-abs over d)
+    can move when a P code or block scale whose binary32 input lies within the
+    relative slack a + b (|tm| + |lg| + |z|) of a rounding boundary is decided
+    the other way (see attn_row in fp4_oracle.c).
 
     Returns (out [nh, nr, d], lse [nh, nr]) and, with with_topk, also
     (topk_idx [nh, nqb, kmax], topk_cnt [nh, nqb])."""
@@ -305,22 +312,26 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
     probs_hat = np.zeros(nh * nr * Sk, np.float64) if with_probs else None
     tidx = np.zeros(max(nh * nqb * kmax, 1), np.int32) if with_topk and pct > 0 else None
     tcnt = np.zeros(max(nh * nqb, 1), np.int32) if with_topk and pct > 0 else None
+    tie = np.ascontiguousarray(np.asarray(tie_slack, np.float64)) if tie_slack is not None else None
+    amb = np.zeros(nh * nr, np.float64) if tie_slack is not None else None
     rc = lib().orc_attention_fwd(q.reshape(-1), k.reshape(-1), v.reshape(-1), B, H, Hkv, Sq, Sk, d,
                                  int(causal), float(softmax_scale), kv_tile, int(scale_search),
                                  fmin, fmax, int(pct), sel_block, _ptr(ra), nr if ra is not None else 0,
                                  _ptr(ha), nh if ha is not None else 0, out, _ptr(lse), _ptr(tidx),
                                  _ptr(tcnt), _ptr(qr), _ptr(kr), int(bool(single_level_p)),
-                                 _ptr(probs), _ptr(probs_hat), int(bool(mx)))
+                                 _ptr(probs), _ptr(probs_hat), int(bool(mx)), _ptr(tie), _ptr(amb))
     if rc != 0:
         raise ValueError("bad attention arguments")
     res = (out.reshape(nh, nr, d), lse.reshape(nh, nr))
     if with_probs:
-        return res + (probs.reshape(nh, nr, Sk), probs_hat.reshape(nh, nr, Sk))
-    if with_topk:
+        res += (probs.reshape(nh, nr, Sk), probs_hat.reshape(nh, nr, Sk))
+    elif with_topk:
         if pct > 0:
             res += (tidx[: nh * nqb * kmax].reshape(nh, nqb, kmax), tcnt[: nh * nqb].reshape(nh, nqb))
         else:
             res += (None, None)
+    if tie_slack is not None:
+        res += (amb.reshape(nh, nr),)
     return res
 
 

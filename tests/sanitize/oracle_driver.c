@@ -24,7 +24,8 @@ int orc_attention_fwd(const float* q, const float* k, const float* v, int B, int
                       int d, int causal, double softmax_scale, int kv_tile, int scale_search, int fmin, int fmax,
                       int pct, int sel_block, const int64_t* rows, int64_t n_rows, const int* heads, int n_heads,
                       float* out, float* lse, int32_t* topk_idx, int32_t* topk_cnt, const float* q_fp4,
-                      const float* k_fp4, int single_level, double* probs, double* probs_hat, int mx);
+                      const float* k_fp4, int single_level, double* probs, double* probs_hat, int mx,
+                      const double* tie, double* amb);
 int orc_attention_exact(const float* q, const float* k, const float* v, int B, int H, int Hkv, int64_t Sq,
                         int64_t Sk, int d, int causal, double softmax_scale, const int64_t* rows, int64_t n_rows,
                         const int* heads, int n_heads, float* out, float* lse);
@@ -101,16 +102,18 @@ int main(void) {
   double* probs = malloc(sizeof(double) * (size_t)(B * H * S * S));
   double* probs_hat = malloc(sizeof(double) * (size_t)(B * H * S * S));
   int32_t tidx[2 * 2 * 2], tcnt[2 * 2];
+  const double tie[2] = {1e-6, 1e-7};
+  double* amb = malloc(sizeof(double) * (size_t)(B * H * S));
   CHECK(orc_attention_fwd(q, k, v, B, H, Hkv, S, S, d, 1, 0.0, 64, 1, -2, 6, 50, 128, NULL, 0, NULL, 0, out, lse,
-                          tidx, tcnt, NULL, NULL, 0, NULL, NULL, 0) == 0);
+                          tidx, tcnt, NULL, NULL, 0, NULL, NULL, 0, tie, amb) == 0);
   CHECK(orc_attention_fwd(q, k, v, B, H, Hkv, S, S, d, 0, 0.0, 128, 1, -2, 6, 0, 128, NULL, 0, NULL, 0, out, lse,
-                          NULL, NULL, NULL, NULL, 1, probs, probs_hat, 0) == 0);
+                          NULL, NULL, NULL, NULL, 1, probs, probs_hat, 0, tie, amb) == 0);
   CHECK(orc_attention_fwd(q, k, v, B, H, Hkv, S, S, d, 1, 0.0, 64, 0, 0, 0, 0, 128, NULL, 0, NULL, 0, out, lse,
-                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 1) == 0);
+                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 1, NULL, NULL) == 0);
   const int64_t rows[3] = {0, 77, 159};
   const int heads[1] = {1};
   CHECK(orc_attention_fwd(q, k, v, B, H, Hkv, S, S, d, 1, 0.2, 128, 1, -2, 6, 0, 128, rows, 3, heads, 1, out, lse,
-                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 0) == 0);
+                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 0, NULL, NULL) == 0);
   CHECK(orc_attention_exact(q, k, v, B, H, Hkv, S, S, d, 1, 0.0, rows, 3, NULL, 0, out, lse) == 0);
   /* decode over a cache with sink, middle and recent tokens, with and without promotion */
   const int Bd = 2, Hq = 4, Hk = 2;
@@ -129,9 +132,9 @@ int main(void) {
   /* rejected arguments */
   CHECK(orc_quantize(x, R, 40, 0, 1, -2, 6, 0, NULL, codes, scales, NULL) < 0);
   CHECK(orc_attention_fwd(q, k, v, B, H, Hkv, S, S, d, 1, 0.0, 48, 0, 0, 0, 0, 128, NULL, 0, NULL, 0, out, lse,
-                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 1) != 0);
+                          NULL, NULL, NULL, NULL, 0, NULL, NULL, 1, NULL, NULL) != 0);
   free(x); free(codes); free(scales); free(offs); free(deq); free(qm); free(km);
-  free(q); free(k); free(v); free(out); free(lse); free(probs); free(probs_hat);
+  free(q); free(k); free(v); free(out); free(lse); free(probs); free(probs_hat); free(amb);
   free(dq); free(dk); free(dv); free(dout); free(dlse);
   printf("oracle driver ok\n");
   return 0;

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 from block_scaled_fp4_amd import synth
-from gpu_helpers import assert_close_attn, case
+from gpu_helpers import TIE_SLACK, assert_close_attn, assert_close_attn_rows, case
+import mix_closed_form as mcf
 
 pytestmark = pytest.mark.gpu
 
@@ -21,20 +22,20 @@ def _gpu(fp4, q, k, v, **kw):
     return out.cpu().numpy(), lse.cpu().numpy(), idx, cnt
 
 
-def _check(fp4, q, k, v, causal, kv_tile, search, pct=0, rows=None, heads=None, softmax_scale=0.0):
+def _check(fp4, q, k, v, causal, kv_tile, search, pct=0, rows=None, heads=None, softmax_scale=0.0, sel_block=128):
     B, H, Sq, d = q.shape
     out, lse, idx, cnt = _gpu(fp4, q, k, v, causal=causal, kv_tile=kv_tile, scale_search=search,
-                              fp16_budget_pct=pct, softmax_scale=softmax_scale)
-    ref, rlse = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=kv_tile, scale_search=search, pct=pct,
-                                     sel_block=128, rows=rows, heads=heads,
-                                     softmax_scale=float(np.float32(softmax_scale)))
+                              fp16_budget_pct=pct, softmax_scale=softmax_scale, sel_block=sel_block)
+    ref, rlse, amb = oracle.attention_fwd(q, k, v, causal=causal, kv_tile=kv_tile, scale_search=search, pct=pct,
+                                          sel_block=sel_block, rows=rows, heads=heads,
+                                          softmax_scale=float(np.float32(softmax_scale)), tie_slack=TIE_SLACK)
     got = out.reshape(B * H, Sq, d)
     gl = lse.reshape(B * H, Sq)
     if heads is not None:
         got, gl = got[heads], gl[heads]
     if rows is not None:
         got, gl = got[:, rows], gl[:, rows]
-    assert_close_attn(got, ref)
+    assert_close_attn_rows(got, ref, amb)
     np.testing.assert_allclose(gl, rlse, atol=1e-3)
     return out, idx, cnt
 
@@ -69,11 +70,63 @@ def test_fp16_inputs_and_custom_scale(gpu):
 
 
 @pytest.mark.parametrize("pct", [10, 30, 100])
-def test_selective_fp16_path(gpu, pct):
-    q, k, v = synth.qkv(1, 2, 1024 + 64, 128, seed=8, k_outliers=4)
-    case(f"attn selective pct={pct} S=1088 causal")
-    out, idx, cnt = _check(gpu, q, k, v, causal=True, kv_tile=128, search=True, pct=pct)
-    assert idx is not None and cnt is not None
+@pytest.mark.parametrize("sel_block", [128, 256])
+@pytest.mark.parametrize("kv_tile", [64, 128])
+@pytest.mark.parametrize("d", [64, 128])
+def test_selective_fp16_path(gpu, d, kv_tile, sel_block, pct):
+    """Random inputs with the FP16 path on: head dims 64 and 128, key tiles of
+    64 (two tiles per 128-token selection block) and 128, selection blocks of
+    128 and 256 tokens (two query tiles of the kernel share a selection row)."""
+    q, k, v = synth.qkv(1, 2, 1024 + 64, d, seed=8 + d, k_outliers=4)
+    case(f"attn selective d={d} kv_tile={kv_tile} sel_block={sel_block} pct={pct} S=1088 causal")
+    out, idx, cnt = _check(gpu, q, k, v, causal=True, kv_tile=kv_tile, search=True, pct=pct, sel_block=sel_block)
+    _, _, ridx, rcnt = oracle.attention_fwd(q, k, v, causal=True, kv_tile=kv_tile, pct=pct, sel_block=sel_block,
+                                            rows=[0], with_topk=True)
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(ridx.shape), ridx)
+    np.testing.assert_array_equal(cnt.cpu().numpy().reshape(rcnt.shape), rcnt)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sel_block,pct", [(128, 10), (128, 34), (256, 50)])
+@pytest.mark.parametrize("kv_tile", [64, 128])
+@pytest.mark.parametrize("d", [64, 128])
+def test_partial_budget_mix_closed_form(gpu, d, kv_tile, sel_block, pct, causal):
+    """The FP4/FP16 mix against its closed form (tests/mix_closed_form.py):
+    scores constant inside every key tile make P quantization lossless, so the
+    output is softmax attention over fp16(V) on the selected blocks' keys and
+    the dequantized V elsewhere.  A wrong tile -> block map, a shifted block or
+    FP4 weights in other units move it by 3e-2 or more in relative L2."""
+    H, S = 2, 960  # 7.5 selection blocks of 128
+    q, k, v, a = mcf.construct(H, S, d, kv_tile, seed=pct + kv_tile + d)
+    assert mcf.operands_exact(q, k)
+    scale = 0.25 / d
+    case(f"attn mix closed form d={d} kv_tile={kv_tile} sel_block={sel_block} pct={pct} causal={causal}")
+    out, lse, idx, cnt = _gpu(gpu, q, k, v, causal=causal, kv_tile=kv_tile, fp16_budget_pct=pct,
+                              sel_block=sel_block, softmax_scale=scale)
+    want, wlse = mcf.expected(q, k, v, a, causal, pct, sel_block, scale, kv_tile)
+    assert_close_attn(out.reshape(H, S, d), want, "mix vs closed form")
+    np.testing.assert_allclose(lse.reshape(H, S), wlse, atol=1e-4)
+    ref, _ = oracle.attention_fwd(q, k, v, causal=causal, softmax_scale=scale, kv_tile=kv_tile, pct=pct,
+                                  sel_block=sel_block)
+    assert_close_attn(out.reshape(H, S, d), ref, "mix vs oracle")
+    idx, cnt = idx.cpu().numpy().reshape(H, -1, idx.shape[-1]), cnt.cpu().numpy().reshape(H, -1)
+    for h in range(H):
+        for i, s in enumerate(mcf.selection(a[h], S, causal, pct, sel_block)):
+            assert cnt[h, i] == len(s) and list(idx[h, i, : cnt[h, i]]) == s
+
+
+@pytest.mark.parametrize("kv_tile", [64, 128])
+def test_partial_budget_zero_keys(gpu, kv_tile):
+    """K = 0 at a partial budget: ties promote the lowest visible blocks, and
+    every row is the mean of fp16(V) over their keys and of V^ elsewhere."""
+    H, S, d, pct = 1, 640, 128, 34
+    q, k, v, a = mcf.construct(H, S, d, kv_tile, seed=3, zero_keys=True)
+    case(f"attn mix zero keys kv_tile={kv_tile}")
+    for causal in (False, True):
+        out, lse, _, _ = _gpu(gpu, q, k, v, causal=causal, kv_tile=kv_tile, fp16_budget_pct=pct)
+        want, wlse = mcf.expected(q, k, v, a, causal, pct, 128, 1.0 / math.sqrt(d), kv_tile)
+        assert_close_attn(out.reshape(H, S, d), want, "mix zero keys")
+        np.testing.assert_allclose(lse.reshape(H, S), wlse, atol=1e-4)
 
 
 def test_full_budget_equals_textbook_fp16_attention(gpu):
@@ -117,28 +170,29 @@ def test_bf16_output_and_prequantized_operands(gpu):
     assert (o3.float() - o2).abs().max().item() <= 2 ** -8 * max(1.0, o2.abs().max().item())
 
 
-def test_prefill_workload_sampled_rows(gpu):
-    """B=1, H=32, S=8192, d=128, causal, ScaleSearch Q/K/V, two-level P, kv_tile 128."""
+def test_prefill_workload_all_heads(gpu):
+    """B=1, H=32, S=8192, d=128, causal, ScaleSearch Q/K/V, two-level P,
+    kv_tile 128: every row of every head against the oracle."""
     q, k, v = synth.prefill(S=8192)
-    rows = sorted(set([0, 1, 127, 128, 4095, 8191] + list(range(37, 8192, 523))))
-    heads = [0, 13, 31]
-    case("attn prefill 8K causal full size, sampled rows")
-    _check(gpu, q, k, v, causal=True, kv_tile=128, search=True, rows=rows, heads=heads)
+    case("attn prefill 8K causal full size, all rows of all 32 heads")
+    _check(gpu, q, k, v, causal=True, kv_tile=128, search=True)
 
 
-def test_selective_workload_sampled_rows(gpu):
-    """B=1, H=32, S=32768, causal, top 10% 128x128 block pairs on the FP16 path."""
+def test_selective_workload_two_heads(gpu):
+    """B=1, H=32, S=32768, causal, top 10% 128x128 block pairs on the FP16
+    path: all 32768 rows of heads 0 and 31 (workgroups of different XCDs)
+    against the oracle, and the selection of every head bit-exact."""
     q, k, v = synth.prefill(S=32768)
-    rows = [0, 130, 5000, 16383, 16384, 29999, 32767]
     heads = [0, 31]
-    case("attn selective 32K causal full size, sampled rows")
-    out, idx, cnt = _check(gpu, q, k, v, causal=True, kv_tile=128, search=True, pct=10, rows=rows, heads=heads)
-    for h in heads:
+    case("attn selective 32K causal full size, all rows of heads 0 and 31")
+    out, idx, cnt = _check(gpu, q, k, v, causal=True, kv_tile=128, search=True, pct=10, heads=heads)
+    for h in range(32):
         qm = oracle.block_means(q[0, h], 128)
         km = oracle.block_means(k[0, h], 128)
         ri, rc = oracle.block_topk(qm, km, True, 10)
         np.testing.assert_array_equal(idx[0, h].cpu().numpy(), ri)
         np.testing.assert_array_equal(cnt[0, h].cpu().numpy(), rc)
+    assert int(cnt[0].sum().item()) == 32 * 3406
 
 
 def test_deterministic(gpu):
@@ -192,3 +246,42 @@ def test_peaked_scores_move_the_reference(gpu, single):
         ref, rlse = oracle.attention_fwd(q, k, v, causal=causal, single_level_p=single)
         assert_close_attn(out.cpu().numpy().reshape(ref.shape), ref, "peaked scores")
         np.testing.assert_allclose(lse.cpu().numpy().reshape(rlse.shape), rlse, atol=1e-3)
+
+
+def test_given_selection_contract(gpu):
+    """A caller's selection list that repeats, disorders or pads entries, or
+    whose count runs past kmax, promotes exactly the entries that exceed every
+    entry before them (include/fp4.h): the output is bit-identical to the one
+    for that clean ascending list, and no key is counted twice."""
+    B, H, S, d, pct = 1, 2, 1024, 128, 50
+    q, k, v = synth.qkv(B, H, S, d, seed=140, k_outliers=4)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    nqb = nkb = S // 128
+    kmax = (pct * nkb + 99) // 100
+    rng = np.random.default_rng(140)
+    messy = np.full((B, H, nqb, kmax), -1, np.int32)
+    clean = np.full((B, H, nqb, kmax), -1, np.int32)
+    mcnt = np.zeros((B, H, nqb), np.int32)
+    ccnt = np.zeros((B, H, nqb), np.int32)
+    for h in range(H):
+        for i in range(nqb):
+            row = [int(x) for x in rng.integers(-2, i + 1, size=kmax)]  # causal: blocks 0..i visible
+            messy[0, h, i] = row
+            mcnt[0, h, i] = kmax + 3 if i % 2 else kmax  # odd rows: a count past kmax (clamped)
+            rec, top = [], -1
+            for x in row:
+                if x > top:
+                    rec.append(x)
+                    top = x
+            clean[0, h, i, :len(rec)] = rec
+            ccnt[0, h, i] = len(rec)
+    assert (mcnt > 0).all() and (ccnt < kmax).any()
+    t = lambda a: torch.from_numpy(a).cuda()
+    case("attn given selection: messy list vs its clean records")
+    o1, l1 = gpu.fp4_attention_fwd(qc, kc, vc, causal=True, fp16_budget_pct=pct, out_dtype=gpu.FP32,
+                                   selection=(t(messy), t(mcnt)))
+    o2, l2 = gpu.fp4_attention_fwd(qc, kc, vc, causal=True, fp16_budget_pct=pct, out_dtype=gpu.FP32,
+                                   selection=(t(clean), t(ccnt)))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.isfinite(o1).all()

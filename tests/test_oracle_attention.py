@@ -56,6 +56,21 @@ def test_two_level_p_worked_example():
     expect = phat / 2688.0 / l
     np.testing.assert_allclose(out[0, 0], expect, rtol=1e-6, atol=1e-9)
     assert abs(lse[0, 0] - math.log(l)) < 1e-6
+    # rounding ambiguity: keys 3 and 19 sit exactly on the E2M1 midpoint 0.75
+    # (ties to the even code, value 1; the other rounding is 0.5).  Under any
+    # positive slack each can move its weight by 0.5 * s2 (448 and 56), each V
+    # row has max 1, and no scale input (448, 56) is near an E4M3 boundary:
+    # amb = (0.5 * 448 + 0.5 * 56) / 2688 / l.  Zero slack leaves both closed.
+    *_, amb = oracle.attention_fwd(q, k, v, causal=False, softmax_scale=math.log(2.0), kv_tile=32,
+                                   tie_slack=(1e-6, 0.0))
+    assert abs(amb[0, 0] - (0.5 * 448 + 0.5 * 56) / 2688.0 / l) < 1e-12
+    *_, amb0 = oracle.attention_fwd(q, k, v, causal=False, softmax_scale=math.log(2.0), kv_tile=32,
+                                    tie_slack=(0.0, 0.0))
+    assert amb0[0, 0] == 0.0
+    # the output with key 3's code taken the other way moves by exactly its share of the bound
+    alt = expect.copy()
+    alt[3] = 0.5 * 448 / 2688.0 / l
+    assert abs(np.abs(alt - expect).max() - 0.5 * 448 / 2688.0 / l) < 1e-12
 
 
 def test_zero_keys_closed_form_mean_of_dequantized_v():
@@ -68,6 +83,11 @@ def test_zero_keys_closed_form_mean_of_dequantized_v():
     out, lse = oracle.attention_fwd(q, k[:, :, :200 + 8], v, causal=False, kv_tile=64)
     np.testing.assert_allclose(out[0], np.broadcast_to(vh.mean(0), (200, 64)), rtol=0, atol=2e-6)
     np.testing.assert_allclose(lse[0], math.log(208), atol=1e-5)
+    # every t is 6 and every block scale input 448: no decision is near a
+    # rounding boundary, so the ambiguity bound is exactly 0 under a slack far
+    # larger than any binary32 evaluation error
+    *_, amb = oracle.attention_fwd(q, k[:, :, :200 + 8], v, causal=False, kv_tile=64, tie_slack=(1e-3, 1e-4))
+    assert np.all(amb == 0.0)
     # causal: row i sees i+1 keys
     q2 = _rand((1, 1, 208, 64), 2)
     out, _ = oracle.attention_fwd(q2, k, v, causal=True, kv_tile=64)
@@ -203,3 +223,108 @@ def test_single_level_p_worked_example():
     two, _ = oracle.attention_fwd(q.to(torch.bfloat16), k.to(torch.bfloat16), v, kv_tile=64,
                                   softmax_scale=float(np.float32(math.log(2.0))))
     assert np.abs(two[0, 0] - want).max() > 1e-3
+
+
+# ---- the FP4/FP16 mix at a partial budget (ThriftAttention page, Metodologia /
+# 1 and 2): a closed form that does not go through the oracle's attention code
+# (tests/mix_closed_form.py explains the construction)
+
+import mix_closed_form as mcf  # noqa: E402
+
+
+def _mix_case(H, S, d, kv_tile, sel_block, causal, pct, seed, zero_keys=False):
+    q, k, v, a = mcf.construct(H, S, d, kv_tile, seed, zero_keys=zero_keys)
+    assert mcf.operands_exact(q, k)
+    scale = 0.25 / d
+    want, wlse = mcf.expected(q, k, v, a, causal, pct, sel_block, scale, kv_tile)
+    return q, k, v, a, scale, want, wlse
+
+
+@pytest.mark.parametrize("kv_tile,sel_block", [(64, 128), (128, 128), (64, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pct", [10, 34, 50])
+def test_partial_budget_mix_closed_form(kv_tile, sel_block, causal, pct):
+    H, S, d = 2, 704, 64  # 5.5 selection blocks of 128: a ragged last block
+    q, k, v, a, scale, want, wlse = _mix_case(H, S, d, kv_tile, sel_block, causal, pct, seed=pct + 7 * kv_tile)
+    out, lse, idx, cnt = oracle.attention_fwd(q, k, v, causal=causal, softmax_scale=scale, kv_tile=kv_tile,
+                                              pct=pct, sel_block=sel_block, with_topk=True)
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(lse, wlse, rtol=0, atol=1e-6)
+    # the oracle's selection is the construction's ranking
+    for h in range(H):
+        sel = mcf.selection(a[h], S, causal, pct, sel_block)
+        for i, s in enumerate(sel):
+            assert cnt[h, i] == len(s)
+            assert list(idx[h, i, : cnt[h, i]]) == s
+            assert all(x == -1 for x in idx[h, i, cnt[h, i]:])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_partial_budget_zero_keys_promote_lowest_blocks(causal):
+    """K = 0: every score ties, so the lowest visible blocks are promoted and
+    O_i is the mean of fp16(V) over their keys and of V^ over the rest."""
+    H, S, d, pct = 1, 640, 64, 34
+    q, k, v, a, scale, want, wlse = _mix_case(H, S, d, 64, 128, causal, pct, seed=3, zero_keys=True)
+    out, lse, idx, cnt = oracle.attention_fwd(q, k, v, causal=causal, softmax_scale=scale, kv_tile=64,
+                                              pct=pct, sel_block=128, with_topk=True)
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(lse[0], np.log(np.arange(1, S + 1) if causal else np.full(S, S)), atol=1e-6)
+    for i in range(5):
+        n = i + 1 if causal else 5
+        kc = -(-pct * n // 100)
+        assert list(idx[0, i, : cnt[0, i]]) == list(range(kc))
+    # the same mean written out directly for the last row
+    vb = v[0, 0]
+    r = oracle.quantize(vb, 1, True)
+    vh = oracle.dequantize(r["codes"], r["scales"], S, d, 1).astype(np.float64)
+    v16 = vb.to(torch.float16).double().numpy()
+    kc = -(-pct * 5 // 100)
+    w = np.concatenate([v16[: 128 * kc], vh[128 * kc:]])
+    np.testing.assert_allclose(out[0, S - 1], w.mean(0), atol=1e-6)
+
+
+def test_partial_budget_closed_form_tells_wrong_maps_apart():
+    """The closed form is sensitive to the mistakes it is meant to catch: a
+    tile index taken for the block index (identical at kv_tile = sel_block,
+    wrong at 64 against 128), a block shifted by one, and FP4 weights left in
+    units of 2688 e.  Each moves the output far beyond the pin's 1e-6."""
+    H, S, d, kv_tile, sel_block, pct = 2, 704, 64, 64, 128, 34
+    q, k, v, a, scale, want, _ = _mix_case(H, S, d, kv_tile, sel_block, True, pct, seed=5)
+    by_tile, _ = mcf.expected(q, k, v, a, True, pct, sel_block, scale, kv_tile, block_of_key=lambda j: j // kv_tile)
+    shifted, _ = mcf.expected(q, k, v, a, True, pct, sel_block, scale, kv_tile,
+                              block_of_key=lambda j: j // sel_block + 1)
+    assert np.abs(by_tile - want).max() > 1e-3
+    assert np.abs(shifted - want).max() > 1e-3
+    out, _ = oracle.attention_fwd(q, k, v, causal=True, softmax_scale=scale, kv_tile=kv_tile, pct=pct,
+                                  sel_block=sel_block)
+    assert np.abs(out - by_tile).max() > 1e-3 and np.abs(out - shifted).max() > 1e-3
+    # the units: with the FP4 weights 2688 times too large, rows mixing both paths move
+    _, Hn, Sn, dn = q.shape
+    qf, kf = q[0].float().double().numpy(), k[0].float().double().numpy()
+    c = float(np.float32(math.log2(math.e) * scale))
+    h, i = 0, S - 1
+    vb = v[0, h]
+    r = oracle.quantize(vb, 1, True)
+    vh = oracle.dequantize(r["codes"], r["scales"], S, d, 1).astype(np.float64)
+    v16 = vb.to(torch.float16).double().numpy()
+    x = (qf[h, i] @ kf[h].T).astype(np.float32) * np.float32(c)
+    p = np.exp2(x.astype(np.float64) - x.max())
+    chosen = set(mcf.selection(a[h], S, True, pct, sel_block)[i // sel_block])
+    prom = np.array([j // sel_block in chosen for j in range(S)])
+    p_bad = np.where(prom, p, 2688.0 * p)
+    w = np.where(prom[:, None], v16, vh)
+    bad = (p_bad[:, None] * w).sum(0) / p.sum()
+    assert np.abs(bad - out[h, i]).max() > 1e-3
+
+
+def test_rounding_ambiguity_bound_is_rare_and_grows_with_slack():
+    """On random inputs few rows have an open P decision under a slack of a
+    few binary32 ulps, the bound grows with the slack, and it vanishes at zero
+    slack (no input lands exactly on a boundary here)."""
+    q, k, v = _rand((1, 2, 512, 64), 31), _rand((1, 2, 512, 64), 32), _rand((1, 2, 512, 64), 33)
+    *_, a0 = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64, tie_slack=(0.0, 0.0))
+    *_, a1 = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64, tie_slack=(2.0 ** -20, 2.0 ** -22))
+    *_, a2 = oracle.attention_fwd(q, k, v, causal=True, kv_tile=64, tie_slack=(2.0 ** -10, 2.0 ** -12))
+    assert np.all(a0 == 0.0)
+    assert np.all(a2 >= a1) and np.count_nonzero(a1) <= 0.02 * a1.size
+    assert np.count_nonzero(a2) > np.count_nonzero(a1)
