@@ -87,7 +87,7 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 struct AttnPlan {
-  size_t qc, qs, kc, ks, vc, vs, qm, km, idx, cnt, total;
+  size_t qc, qs, kc, ks, vc, vs, qm, km, idx, cnt, keys, total;
   int nqb, nkb, kmax;
   bool need_quant, need_sel;
 };
@@ -116,6 +116,7 @@ AttnPlan plan_attn(const fp4_attn_problem* p, const fp4_attn_opts* o) {
     P.km = take((size_t)(B * Hkv * P.nkb * d) * sizeof(double));
     P.idx = take((size_t)(B * H * P.nqb * (P.kmax > 0 ? P.kmax : 1)) * sizeof(int32_t));
     P.cnt = take((size_t)(B * H * P.nqb) * sizeof(int32_t));
+    P.keys = take((size_t)(B * H * P.nqb) * (size_t)P.nkb * sizeof(uint64_t));
   }
   P.total = off;
   return P;
@@ -276,6 +277,7 @@ static int launch_selection(const fp4_attn_problem* p, const fp4_attn_opts* o, c
   T.kmeans = (double*)(ws_sel + (P.km - P.qm));
   T.idx = idx ? idx : (int32_t*)(ws_sel + (P.idx - P.qm));
   T.cnt = cnt ? cnt : (int32_t*)(ws_sel + (P.cnt - P.qm));
+  T.keys = (uint64_t*)(ws_sel + (P.keys - P.qm));
   return hip_status(fp4i_launch_topk(T, s), "block selection launch");
 }
 

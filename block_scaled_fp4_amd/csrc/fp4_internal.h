@@ -48,6 +48,7 @@ struct TopkLaunch {
   int nqb, nkb, kmax;
   double* qmeans;  // [B*H, nqb, d]
   double* kmeans;  // [B*Hkv, nkb, d]
+  uint64_t* keys;  // [B*H, nqb, nkb] order-preserving keys of the block scores
   int32_t* idx;    // [B*H, nqb, kmax]
   int32_t* cnt;    // [B*H, nqb]
 };

@@ -19,81 +19,155 @@ __device__ __forceinline__ double ld_elem<uint16_t>(const uint16_t* p) { return 
 template <>
 __device__ __forceinline__ double ld_elem<half_t>(const half_t* p) { return (double)(float)*p; }
 
-// grid: (heads * nblocks); block: d threads, one channel each.
+// Element e (0..7) of 8 consecutive bf16 / fp16 values in 16 bytes, exactly.
 template <typename T>
-__global__ void __launch_bounds__(128) block_means_kernel(const T* x, int64_t S, int d, int blk, int nb,
-                                                          double* means) {
-  const int64_t hb = blockIdx.x;
-  const int64_t head = hb / nb, ib = hb - head * nb;
-  const int c = threadIdx.x;
-  if (c >= d) return;
-  const int64_t t0 = ib * blk;
-  int64_t t1 = t0 + blk;
-  if (t1 > S) t1 = S;
-  const T* p = x + (head * S + t0) * d + c;
-  double s = 0.0;
-  int64_t n = t1 - t0;
-  int64_t t = 0;
-  for (; t + 8 <= n; t += 8) {
-    double v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ld_elem<T>(p + (t + u) * d);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s = s + v[u];
-  }
-  for (; t < n; ++t) s = s + ld_elem<T>(p + t * d);
-  means[hb * d + c] = s / (double)n;
+__device__ __forceinline__ double elem8(const uint4_t& w, int e);
+template <>
+__device__ __forceinline__ double elem8<uint16_t>(const uint4_t& w, int e) {
+  const uint32_t v = w[e >> 1];
+  return (double)__uint_as_float((e & 1) ? (v & 0xFFFF0000u) : (v << 16));
+}
+template <>
+__device__ __forceinline__ double elem8<half_t>(const uint4_t& w, int e) {
+  const uint32_t v = w[e >> 1];
+  return (double)(float)__builtin_bit_cast(half_t, (uint16_t)((e & 1) ? (v >> 16) : (v & 0xFFFFu)));
 }
 
-// grid: (B*H*nqb); block: 256 threads.  Scores every visible key block, ranks
-// them (descending score, ascending index on ties) and writes the kept ones in
-// ascending order, padded with -1.
-__global__ void __launch_bounds__(256) block_topk_kernel(const double* qm, const double* km, int64_t H,
-                                                         int64_t Hkv, int nqb, int nkb, int d, int causal,
-                                                         int pct, int kmax, int32_t* idx, int32_t* cnt) {
-  extern __shared__ double smem[];  // [d] query mean, [nkb] scores, [nkb] kept flags
-  double* qv = smem;
-  double* sc = smem + d;
-  int* kept = reinterpret_cast<int*>(smem + d + nkb);
-  const int64_t g = blockIdx.x;  // (b*H + h) * nqb + i
-  const int64_t bh = g / nqb;
-  const int i = (int)(g - bh * nqb);
-  const int64_t b = bh / H, h = bh - b * H;
-  const int64_t hk = h / (H / Hkv);
-  const double* kmh = km + (b * Hkv + hk) * (int64_t)nkb * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) qv[c] = qm[g * d + c];
-  __syncthreads();
-  const int nvis = causal ? (i + 1 < nkb ? i + 1 : nkb) : nkb;
-  const int k = (pct * nvis + 99) / 100;
-  for (int j = threadIdx.x; j < nvis; j += blockDim.x) {
-    double s = 0.0;
-    const double* kv = kmh + (int64_t)j * d;
-    for (int c = 0; c < d; ++c) {
-      double p = __dmul_rn(qv[c], kv[c]);
-      s = __dadd_rn(s, p);
+// Block means: one thread per 8 channels of one (head, block), 16-byte loads
+// (sixteen in flight), each channel summed over ascending tokens in binary64
+// and divided by the token count.  One launch covers the Q units and then the
+// K units; 256 threads cover 256 / (d / 8) units.
+template <typename T>
+struct MeansArgs {
+  const T *q, *k;
+  int64_t Sq, Sk, nunits_q, nunits_k;
+  int d, blk, nqb, nkb;
+  double *qmeans, *kmeans;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
+  const int per = A.d / 8;
+  int64_t u = (int64_t)blockIdx.x * (256 / per) + threadIdx.x / per;
+  const bool isq = u < A.nunits_q;
+  if (!isq) u -= A.nunits_q;
+  if (!isq && u >= A.nunits_k) return;
+  const T* x = isq ? A.q : A.k;
+  const int64_t S = isq ? A.Sq : A.Sk;
+  const int nb = isq ? A.nqb : A.nkb;
+  double* means = isq ? A.qmeans : A.kmeans;
+  const int d = A.d, blk = A.blk;
+  const int c0 = (threadIdx.x % per) * 8;
+  const int64_t head = u / nb, ib = u - head * nb;
+  const int64_t t0 = ib * blk;
+  const int64_t n = (t0 + blk < S ? t0 + blk : S) - t0;
+  const T* p = x + (head * S + t0) * d + c0;
+  double s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.0;
+  int64_t t = 0;
+  for (; t + 16 <= n; t += 16) {
+    uint4_t w[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) w[v] = *reinterpret_cast<const uint4_t*>(p + (t + v) * d);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = s[e] + elem8<T>(w[v], e);
+  }
+  for (; t < n; ++t) {
+    const uint4_t w = *reinterpret_cast<const uint4_t*>(p + t * d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = s[e] + elem8<T>(w, e);
+  }
+  double* out = means + u * d + c0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = s[e] / (double)n;
+}
+
+// Scores of a tile of 64 query blocks x 64 key blocks of one (batch, head):
+// Q and K means staged through LDS 32 channels at a time, every score summed
+// over ascending channels (binary64 products and sums, no fused multiply-add),
+// written as an order-preserving 64-bit key.  A tile wholly above the causal
+// diagonal does nothing; its keys are never read.
+constexpr int kScTQ = 64, kScTK = 64, kScTC = 32;
+
+// Scores as unsigned keys that order like the doubles (-0 folded into +0).
+__device__ __forceinline__ uint64_t score_key(double s) {
+  if (s == 0.0) s = 0.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(s);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__global__ void __launch_bounds__(256) block_scores_kernel(const double* qm, const double* km, int64_t H,
+                                                           int64_t Hkv, int nqb, int nkb, int d, int causal,
+                                                           int ntq, int ntk, uint64_t* keys) {
+  __shared__ double sq[kScTQ][kScTC + 1];
+  __shared__ double sk[kScTK][kScTC + 1];
+  const int64_t bh = blockIdx.x / (ntq * ntk);
+  const int tile = (int)(blockIdx.x - bh * ntq * ntk);
+  const int i0 = (tile / ntk) * kScTQ, j0 = (tile % ntk) * kScTK;
+  const int ilast = i0 + kScTQ - 1 < nqb - 1 ? i0 + kScTQ - 1 : nqb - 1;
+  if (causal && j0 > ilast) return;
+  const int64_t b = bh / H, h = bh - b * H, hk = h / (H / Hkv);
+  const double* qb = qm + bh * nqb * d;
+  const double* kb = km + (b * Hkv + hk) * nkb * d;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  // staging map: element e = tid + 256 u of a chunk -> row e / 32, channel e % 32
+  constexpr int NQ = kScTQ * kScTC / 256, NK = kScTK * kScTC / 256;
+  double rq[NQ], rk[NK];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = tid + 256 * u, r = e / kScTC, cc = e % kScTC;
+      rq[u] = i0 + r < nqb ? qb[(int64_t)(i0 + r) * d + c0 + cc] : 0.0;
     }
-    sc[j] = s;
-  }
-  __syncthreads();
-  int32_t* out = idx + g * kmax;
-  // rank of j = number of visible j' ahead of it; kept iff rank < k
-  for (int j = threadIdx.x; j < nvis; j += blockDim.x) {
-    const double sj = sc[j];
-    int rank = 0;
-    for (int jj = 0; jj < nvis; ++jj) {
-      const double so = sc[jj];
-      rank += (so > sj || (so == sj && jj < j)) ? 1 : 0;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + 256 * u, r = e / kScTC, cc = e % kScTC;
+      rk[u] = j0 + r < nkb ? kb[(int64_t)(j0 + r) * d + c0 + cc] : 0.0;
     }
-    kept[j] = rank < k ? 1 : 0;
+  };
+  double acc[4][4];  // rows ty + 16 r, columns tx + 16 c
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+  fetch(0);
+  for (int c0 = 0; c0 < d; c0 += kScTC) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = tid + 256 * u;
+      sq[e / kScTC][e % kScTC] = rq[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + 256 * u;
+      sk[e / kScTC][e % kScTC] = rk[u];
+    }
+    __syncthreads();
+    if (c0 + kScTC < d) fetch(c0 + kScTC);
+#pragma unroll 4
+    for (int cc = 0; cc < kScTC; ++cc) {
+      double a[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = sq[ty + 16 * r][cc];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = sk[tx + 16 * c][cc];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = __dadd_rn(acc[r][c], __dmul_rn(a[r], bv[c]));
+    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int w = 0;
-    for (int j = 0; j < nvis; ++j)
-      if (kept[j]) out[w++] = j;
-    for (int t = w; t < kmax; ++t) out[t] = -1;
-    cnt[g] = k;
-  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
+      if (i < nqb && j < nkb && (!causal || j <= i)) keys[(bh * nqb + i) * nkb + j] = score_key(acc[r][c]);
+    }
 }
 
 // ---- decode: promoted middle blocks of one query token per query head ----
@@ -114,12 +188,6 @@ __global__ void __launch_bounds__(256) block_topk_kernel(const double* qm, const
 constexpr int kScoreBlocks = 32;    // middle blocks per scoring workgroup
 constexpr int kSelLdsKeys = 4096;   // keys the select kernel keeps in LDS
 
-// Scores as unsigned keys that order like the doubles (-0 folded into +0).
-__device__ __forceinline__ uint64_t score_key(double s) {
-  if (s == 0.0) s = 0.0;
-  const uint64_t u = (uint64_t)__double_as_longlong(s);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
 
 struct DecSelArgs {
   const uint16_t* q;
@@ -204,24 +272,16 @@ __global__ void __launch_bounds__(256) decode_scores_kernel(DecSelArgs A) {
   }
 }
 
-// grid: B*Hkv; block: 256 threads.  KEYS_IN_LDS: nb <= kSelLdsKeys.
-template <bool KEYS_IN_LDS>
-__global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
-  __shared__ uint64_t lkeys[KEYS_IN_LDS ? kSelLdsKeys : 1];
+// The k largest of keys[0..nb) (ties: the lower index first), by a radix
+// select over 8-bit digits: the kept indices go to out[0..k) in ascending
+// order and out[k..kmax) gets -1; mask (nullable) gets the same set as bits.
+// Called by all 256 threads of the workgroup (block-wide barriers inside).
+__device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, int32_t* out, uint32_t* mask) {
   __shared__ int hist[256];
   __shared__ int wtot[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t bk = blockIdx.x;
-  const int64_t M = sel_mid_len(A, bk / A.Hkv);
-  const int nb = (int)((M + kDecSelBlock - 1) / kDecSelBlock);
-  const int k = (A.pct * nb + 99) / 100;
-  const uint64_t* gkeys = A.keys + bk * A.nbc;
-  if (KEYS_IN_LDS)
-    for (int j = tid; j < nb; j += 256) lkeys[j] = gkeys[j];
-  __syncthreads();
-  auto key = [&](int j) { return KEYS_IN_LDS ? lkeys[j] : gkeys[j]; };
   // k-th largest key: after the passes `prefix` is its value and `rem` the
-  // number of keys equal to it that are kept (the lowest blocks among them)
+  // number of keys equal to it that are kept (the lowest indices among them)
   uint64_t prefix = 0;
   int rem = k;
   if (k > 0) {
@@ -230,7 +290,7 @@ __global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
       __syncthreads();
       const uint64_t hi = shift == 56 ? 0ull : (~0ull << (shift + 8));
       for (int j = tid; j < nb; j += 256) {
-        const uint64_t u = key(j);
+        const uint64_t u = keys[j];
         if ((u & hi) == prefix) atomicAdd(&hist[(int)((u >> shift) & 255u)], 1);
       }
       __syncthreads();
@@ -269,14 +329,12 @@ __global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
       __syncthreads();
     }
   }
-  // kept blocks in ascending order, with the bit mask
-  int32_t* out = A.idx + bk * A.kmax;
-  uint32_t* mask = A.mask + bk * A.nbw;
+  // kept indices in ascending order (and the bit mask)
   const uint64_t below = (1ull << lane) - 1ull;
   int run_tie = 0, run_sel = 0;
   for (int base = 0; base < nb; base += 256) {
     const int j = base + tid;
-    const uint64_t u = j < nb ? key(j) : 0ull;
+    const uint64_t u = j < nb ? keys[j] : 0ull;
     const bool tie = k > 0 && j < nb && u == prefix;
     const unsigned long long bt = __ballot(tie);
     if (lane == 0) wtot[0][wave] = __popcll(bt);
@@ -296,13 +354,123 @@ __global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
       all_s += wtot[1][w];
     }
     if (sel) out[off_s + __popcll(bs & below)] = j;
-    if ((lane & 31) == 0 && j < nb) mask[j >> 5] = (uint32_t)(bs >> (lane & 32));
+    if (mask && (lane & 31) == 0 && j < nb) mask[j >> 5] = (uint32_t)(bs >> (lane & 32));
     run_tie += all_t;
     run_sel += all_s;
     __syncthreads();
   }
-  for (int p = k + tid; p < A.kmax; p += 256) out[p] = -1;
+  for (int p = k + tid; p < kmax; p += 256) out[p] = -1;
+}
+
+// grid: B*Hkv; block: 256 threads.  KEYS_IN_LDS: nb <= kSelLdsKeys.
+template <bool KEYS_IN_LDS>
+__global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
+  __shared__ uint64_t lkeys[KEYS_IN_LDS ? kSelLdsKeys : 1];
+  const int tid = threadIdx.x;
+  const int64_t bk = blockIdx.x;
+  const int64_t M = sel_mid_len(A, bk / A.Hkv);
+  const int nb = (int)((M + kDecSelBlock - 1) / kDecSelBlock);
+  const int k = (A.pct * nb + 99) / 100;
+  const uint64_t* gkeys = A.keys + bk * A.nbc;
+  if (KEYS_IN_LDS)
+    for (int j = tid; j < nb; j += 256) lkeys[j] = gkeys[j];
+  __syncthreads();
+  select_top_keys(KEYS_IN_LDS ? lkeys : gkeys, nb, k, A.kmax, A.idx + bk * A.kmax, A.mask + bk * A.nbw);
   if (tid == 0) A.cnt[bk] = k;
+}
+
+// Prefill selection, one wave per (batch, head, query block) row, no
+// workgroup barrier: a radix select over 8-bit digits of the row's visible
+// keys (from block_scores_kernel, read from memory each pass) with a per-wave
+// histogram in LDS, then the kept indices in ascending order (the k largest,
+// ties to the lower index), -1 padding and the count.
+__global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys, int64_t nrows, int nqb, int nkb,
+                                                           int causal, int pct, int kmax, int32_t* idx,
+                                                           int32_t* cnt) {
+  __shared__ int hist[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t g = (int64_t)blockIdx.x * 4 + wave;  // (b*H + h) * nqb + i
+  if (g >= nrows) return;
+  const int i = (int)(g % nqb);
+  const int nvis = causal ? (i + 1 < nkb ? i + 1 : nkb) : nkb;
+  const int k = (pct * nvis + 99) / 100;
+  const uint64_t* row = keys + g * nkb;
+  int* hw = hist[wave];
+  uint64_t prefix = 0;
+  int rem = k;
+  if (k > 0 && k < nvis) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hw[lane + 64 * q] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const uint64_t hi = shift == 56 ? 0ull : (~0ull << (shift + 8));
+      for (int j = lane; j < nvis; j += 64) {
+        const uint64_t u = row[j];
+        if ((u & hi) == prefix) atomicAdd(&hw[(int)((u >> shift) & 255u)], 1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // lane l holds bins 255-4l .. 252-4l (scanned from the top)
+      int c4[4], own = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c4[q] = hw[255 - 4 * lane - q];
+        own += c4[q];
+      }
+      int incl = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int excl = incl - own;
+      int found = -1, above = 0;
+      if (excl < rem && incl >= rem) {
+        int acc = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (found < 0 && acc + c4[q] >= rem) {
+            found = 255 - 4 * lane - q;
+            above = acc;
+          }
+          acc += c4[q];
+        }
+      }
+      const unsigned long long who = __ballot(found >= 0);
+      const int src = (int)__builtin_ctzll(who);
+      prefix |= (uint64_t)__shfl(found, src, 64) << shift;
+      rem -= __shfl(above, src, 64);
+      // the next pass clears this histogram: all reads of it are done first
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // kept: every visible block when k >= nvis; else keys above the threshold
+  // and the first rem ties
+  int32_t* out = idx + g * kmax;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int run_tie = 0, run_sel = 0;
+  for (int base = 0; base < nvis; base += 64) {
+    const int j = base + lane;
+    const bool in = j < nvis;
+    const uint64_t u = in ? row[j] : 0ull;
+    bool sel;
+    if (k >= nvis) {
+      sel = in;
+    } else {
+      const bool tie = k > 0 && in && u == prefix;
+      const unsigned long long bt = __ballot(tie);
+      sel = k > 0 && in && (u > prefix || (tie && run_tie + __popcll(bt & below) < rem));
+      run_tie += __popcll(bt);
+    }
+    const unsigned long long bs = __ballot(sel);
+    if (sel) out[run_sel + __popcll(bs & below)] = j;
+    run_sel += __popcll(bs);
+  }
+  for (int p = k + lane; p < kmax; p += 64) out[p] = -1;
+  if (lane == 0) cnt[g] = k;
 }
 
 }  // namespace fp4dev
@@ -338,22 +506,36 @@ hipError_t fp4i_launch_decode_select(const DecSelectLaunch& L, hipStream_t strea
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_means(const TopkLaunch& L, hipStream_t stream) {
+  MeansArgs<T> A;
+  A.q = (const T*)L.q;
+  A.k = (const T*)L.k;
+  A.Sq = L.Sq;
+  A.Sk = L.Sk;
+  A.nunits_q = L.B * L.H * L.nqb;
+  A.nunits_k = L.B * L.Hkv * L.nkb;
+  A.d = (int)L.d;
+  A.blk = L.sel_block;
+  A.nqb = L.nqb;
+  A.nkb = L.nkb;
+  A.qmeans = L.qmeans;
+  A.kmeans = L.kmeans;
+  const int upw = 256 / (A.d / 8);  // (head, block) units per workgroup
+  const int64_t units = A.nunits_q + A.nunits_k;
+  hipLaunchKernelGGL(block_means_kernel<T>, dim3((unsigned)((units + upw - 1) / upw)), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
+
 hipError_t fp4i_launch_topk(const TopkLaunch& L, hipStream_t stream) {
   const int d = (int)L.d;
-  const int64_t gq = L.B * L.H * L.nqb, gk = L.B * L.Hkv * L.nkb;
-  if (L.dtype == 0) {
-    hipLaunchKernelGGL(block_means_kernel<uint16_t>, dim3(gq), dim3(d), 0, stream, (const uint16_t*)L.q, L.Sq, d,
-                       L.sel_block, L.nqb, L.qmeans);
-    hipLaunchKernelGGL(block_means_kernel<uint16_t>, dim3(gk), dim3(d), 0, stream, (const uint16_t*)L.k, L.Sk, d,
-                       L.sel_block, L.nkb, L.kmeans);
-  } else {
-    hipLaunchKernelGGL(block_means_kernel<half_t>, dim3(gq), dim3(d), 0, stream, (const half_t*)L.q, L.Sq, d,
-                       L.sel_block, L.nqb, L.qmeans);
-    hipLaunchKernelGGL(block_means_kernel<half_t>, dim3(gk), dim3(d), 0, stream, (const half_t*)L.k, L.Sk, d,
-                       L.sel_block, L.nkb, L.kmeans);
-  }
-  size_t shm = sizeof(double) * (size_t)(d + L.nkb) + sizeof(int) * (size_t)L.nkb;
-  hipLaunchKernelGGL(block_topk_kernel, dim3(gq), dim3(256), shm, stream, L.qmeans, L.kmeans, L.H, L.Hkv, L.nqb,
-                     L.nkb, d, L.causal, L.pct, L.kmax, L.idx, L.cnt);
+  const int64_t gq = L.B * L.H * L.nqb;
+  const hipError_t e = L.dtype == 0 ? launch_means<uint16_t>(L, stream) : launch_means<half_t>(L, stream);
+  if (e != hipSuccess) return e;
+  const int ntq = (L.nqb + kScTQ - 1) / kScTQ, ntk = (L.nkb + kScTK - 1) / kScTK;
+  hipLaunchKernelGGL(block_scores_kernel, dim3((unsigned)(L.B * L.H * ntq * ntk)), dim3(256), 0, stream, L.qmeans,
+                     L.kmeans, L.H, L.Hkv, L.nqb, L.nkb, d, L.causal, ntq, ntk, L.keys);
+  hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((gq + 3) / 4)), dim3(256), 0, stream, L.keys, gq, L.nqb,
+                     L.nkb, L.causal, L.pct, L.kmax, L.idx, L.cnt);
   return hipGetLastError();
 }
