@@ -114,6 +114,8 @@ def load():
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
+    L.fp4_attention_decode_noalloc.argtypes = [vp, i64, C.POINTER(KVCacheStruct), C.c_float, i32, vp, vp, vp]
+    L.fp4_attention_decode_noalloc.restype = C.c_int
     L.fp4_mx_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
     L.fp4_mx_quantize.restype = C.c_int
     L.fp4_attention_fwd_mx.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, sz, vp]
@@ -460,6 +462,22 @@ def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, r
                                                 _ptr(scnt), _ptr(ws), nws, _stream(q.device)))
     if return_selection:
         return out, lse, sidx, scnt
+    return out, lse
+
+
+def fp4_attention_decode_noalloc(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, out=None, lse=None):
+    """fp4_attention_decode with the library's fixed device scratch array as
+    its workspace (no allocation inside the call).  q [B,Hq,d] bf16; out
+    [B,Hq,d] and lse [B,Hq] (float32, optional) are the caller's (allocated
+    here only when not given).  Returns (out, lse)."""
+    L = load()
+    _dev(q, "q")
+    B, Hq, d = q.shape
+    cs = cache.struct()
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
+    _check(L.fp4_attention_decode_noalloc(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out),
+                                          _ptr(lse), _stream(q.device)))
     return out, lse
 
 

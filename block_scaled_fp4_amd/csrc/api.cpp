@@ -172,6 +172,9 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
 
 }  // namespace
 
+// Error reporting for the library's other host sources (same message buffer).
+int fp4i_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 int fp4_version(void) { return 10000; }

@@ -170,3 +170,6 @@ size_t fp4i_kv_append_workspace(int64_t B, int64_t Hkv, int64_t n_recent, int64_
 hipError_t fp4i_launch_kv_append(const KvAppendLaunch& L, hipStream_t stream);
 int fp4i_decode_full_splits(int64_t n_full);
 hipError_t fp4i_launch_decode(const DecodeLaunch& L, hipStream_t stream);
+
+// Sets the thread's fp4_last_error message and returns code (api.cpp).
+int fp4i_fail(int code, const char* msg);

@@ -342,6 +342,25 @@ int fp4_attention_decode(const void* q, int64_t Hq, const fp4_kv_cache* cache, f
 
 size_t fp4_attention_decode_workspace_size(int64_t Hq, const fp4_kv_cache* cache);
 
+/* Bytes of the fixed device array behind fp4_attention_decode_noalloc (one
+   copy per GPU, held until the process ends). */
+#define FP4_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fp4_attention_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, with the workspace
+ * taken from a fixed device array of the library (FP4_NOALLOC_SCRATCH_BYTES
+ * per GPU) instead of a caller buffer.  The caller still owns q, the cache,
+ * out and lse.  Calls no allocating routine.  A problem whose workspace
+ * (fp4_attention_decode_workspace_size) exceeds the array is rejected with
+ * FP4_ERR_UNSUPPORTED before anything runs.  All calls on one GPU share its
+ * array: calls that overlap on a GPU (other streams, other threads) race and
+ * must be serialized by the caller.
+ */
+int fp4_attention_decode_noalloc(const void* q, int64_t Hq, const fp4_kv_cache* cache, float softmax_scale,
+                                 int32_t out_dtype, void* out, float* lse, void* stream);
+
 /*
  * Decode with selective promotion (ThriftAttention page, Metodologia / 1 and
  * / 2, applied to one query token).  For every (batch, kv head) the middle is

@@ -236,3 +236,20 @@ def test_backward_workspace_is_linear_in_length(L):
     # bf16 copies of Q^, K^, V^ and the two terms of an fp16 dO, the row term D, and the NVFP4
     # codes + scales of Q, K, V
     assert sizes[2] < 5 * n * 2 + 32 * 131072 * 4 + 3 * n * 9 // 16 + 65536
+
+
+def test_noalloc_decode_rejects_oversized_problems(L):
+    """The allocation-free decode refuses a problem whose workspace exceeds its
+    fixed array, before touching the device, with a message naming the sizes."""
+    import block_scaled_fp4_amd as fp4
+    cs = fp4.KVCacheStruct()
+    cs.struct_size = C.sizeof(cs)
+    cs.B, cs.Hkv, cs.d, cs.n_sink, cs.n_recent, cs.mid_cap = 4096, 8, 128, 128, 256, 1 << 20
+    need = L.fp4_attention_decode_workspace_size(32, C.byref(cs))
+    assert need > 16 << 20
+    fake = C.c_void_p(1 << 20)
+    st = L.fp4_attention_decode_noalloc(fake, 32, C.byref(cs), 0.0, 2, fake, None, None)
+    msg = L.fp4_last_error().decode()
+    assert st == -2 and "scratch" in msg and str(need) in msg
+    # invalid arguments are reported as by fp4_attention_decode
+    assert L.fp4_attention_decode_noalloc(fake, 0, C.byref(cs), 0.0, 2, fake, None, None) == -1
