@@ -169,6 +169,21 @@ def _dev(t, name):
         raise FP4Error(-1, f"{name} must be contiguous")
 
 
+def _out(out, shape, dtype, dev, name="out"):
+    """The output buffer: allocated when not given; a given one must be a
+    contiguous GPU tensor of exactly the dtype and element count the kernel
+    writes (the C ABI takes a bare pointer and cannot check)."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _dev(out, name)
+    n = 1
+    for x in shape:
+        n *= int(x)
+    if out.dtype != dtype or out.numel() != n:
+        raise FP4Error(-1, f"{name} must be {dtype} with {n} elements (got {out.dtype}, {out.numel()})")
+    return out
+
+
 def _stream(dev):
     return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -194,7 +209,10 @@ def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True
     else:
         cshape, sshape = (rows // 2, cols), (rows // 16, cols)
     if out is not None:
-        codes, scales, offs = out["codes"], out["scales"], out.get("offsets")
+        codes = _out(out["codes"], cshape, torch.uint8, dev, "codes")
+        scales = _out(out["scales"], sshape, torch.uint8, dev, "scales")
+        offs = out.get("offsets")
+        offs = _out(offs, sshape, torch.int8, dev, "offsets") if offs is not None else None
     else:
         codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
         scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
@@ -294,8 +312,7 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
     P = _problem(q, k, v, quantized)
     O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype,
               selection is not None, hadamard, hadamard_signs, single_level_p)
-    if out is None:
-        out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
+    out = _out(out, (B, H, Sq, d), _TORCH_DT[out_dtype], dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
     idx = cnt = None
     if selection is not None:
@@ -330,8 +347,7 @@ def fp4_attention_fwd_mx(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, 
     B, H, Sq, d = q.shape if q is not None else quantized["q_shape"]
     P = _problem(q, k, v, quantized)
     O = _opts(causal, softmax_scale, kv_tile, False, -2, 6, 0, 128, out_dtype, False)
-    if out is None:
-        out = torch.empty((B, H, Sq, d), dtype=_TORCH_DT[out_dtype], device=dev)
+    out = _out(out, (B, H, Sq, d), _TORCH_DT[out_dtype], dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
     nws = L.fp4_attention_fwd_mx_workspace_size(C.byref(P), C.byref(O))
     ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
@@ -440,8 +456,7 @@ def fp4_attention_decode(q, cache: KVCache, softmax_scale=0.0, out_dtype=BF16, r
     _dev(q, "q")
     B, Hq, d = q.shape
     cs = cache.struct()
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
+    out = _out(out, (B, Hq, d), _TORCH_DT[out_dtype], q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     pct = int(fp16_budget_pct)
     sidx = scnt = None
@@ -474,8 +489,8 @@ def fp4_attention_decode_noalloc(q, cache: KVCache, softmax_scale=0.0, out_dtype
     _dev(q, "q")
     B, Hq, d = q.shape
     cs = cache.struct()
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=_TORCH_DT[out_dtype], device=q.device)
+    out = _out(out, (B, Hq, d), _TORCH_DT[out_dtype], q.device)
+    lse = _out(lse, (B, Hq), torch.float32, q.device, "lse") if lse is not None else None
     _check(L.fp4_attention_decode_noalloc(_ptr(q), Hq, C.byref(cs), float(softmax_scale), out_dtype, _ptr(out),
                                           _ptr(lse), _stream(q.device)))
     return out, lse

@@ -285,3 +285,19 @@ def test_given_selection_contract(gpu):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.isfinite(o1).all()
+
+
+def test_binding_rejects_mismatched_out_buffer(gpu):
+    """The C ABI takes a bare output pointer, so the binding refuses a given
+    buffer whose dtype or size differs from what the kernel writes (it raises
+    before anything is launched)."""
+    q, k, v = synth.qkv(1, 1, 128, 64, seed=150)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    case("binding: output buffer checks (nothing launched)")
+    with pytest.raises(gpu.FP4Error):
+        gpu.fp4_attention_fwd(qc, kc, vc, out_dtype=gpu.FP32, out=torch.empty_like(qc))  # bf16 buffer, fp32 output
+    with pytest.raises(gpu.FP4Error):
+        gpu.fp4_attention_fwd(qc, kc, vc, out_dtype=gpu.BF16, out=torch.empty(10, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(gpu.FP4Error):
+        gpu.fp4_quantize(qc.view(-1, 64), 0, True, out=dict(codes=torch.empty(7, dtype=torch.uint8, device="cuda"),
+                                                            scales=torch.empty(512, dtype=torch.uint8, device="cuda")))
