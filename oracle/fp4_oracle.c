@@ -322,6 +322,44 @@ void orc_hadamard_rows(float* x, int64_t rows, int n, const uint32_t* signs) {
   }
 }
 
+/* Magnitude balance of Q and K (ScaleSearch page, Metodologia /
+   ScaleSearchAttention: besides the Hadamard rotation, a pair Q' = Q R^-T,
+   K' = K R keeps the scores Q K^T and lowers the mean squared magnitude of the
+   two tensors).  Reading: R is diagonal with power-of-two entries 2^e_c, one
+   vector per (batch, kv head), fitted to the call's own Q and K: with ms_q[c]
+   the mean of q^2 over the group's query heads and all query tokens and
+   ms_k[c] the mean of k^2 over the kv head's tokens (binary64 sums in
+   ascending head then token order, divided by the count), e_c is the integer
+   in [-8, 8] minimizing ms_q 4^-e + ms_k 4^e: the smallest e with
+   4^(2e+1) >= ms_q / ms_k (ties go to the lower e).  A channel whose mean
+   square is 0 on either side keeps e = 0.  Then Q'_c = Q_c 2^-e_c and
+   K'_c = K_c 2^e_c are exact in binary32 (away from overflow and underflow)
+   and Q' K'^T = Q K^T.  e: [B][Hkv][d]. */
+void orc_balance_exponents(const float* q, const float* k, int B, int H, int Hkv, int64_t Sq, int64_t Sk, int d,
+                           int32_t* e) {
+  const int G = H / Hkv;
+  for (int b = 0; b < B; ++b)
+    for (int hk = 0; hk < Hkv; ++hk)
+      for (int c = 0; c < d; ++c) {
+        double sq = 0.0, sk = 0.0;
+        for (int g = 0; g < G; ++g) {
+          const float* qh = q + (((int64_t)b * H + hk * G + g) * Sq) * d;
+          for (int64_t t = 0; t < Sq; ++t) sq += (double)qh[t * d + c] * (double)qh[t * d + c];
+        }
+        const float* kh = k + (((int64_t)b * Hkv + hk) * Sk) * d;
+        for (int64_t t = 0; t < Sk; ++t) sk += (double)kh[t * d + c] * (double)kh[t * d + c];
+        const double mq = sq / (double)(G * Sq), mk = sk / (double)Sk;
+        int ec = 0;
+        if (mq > 0.0 && mk > 0.0) {
+          const double A = mq / mk;
+          ec = 8;
+          for (int x = -8; x <= 8; ++x)
+            if (ldexp(1.0, 2 * (2 * x + 1)) >= A) { ec = x; break; }
+        }
+        e[((int64_t)b * Hkv + hk) * d + c] = ec;
+      }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Block selection ([Thrift] Metodologia / 1)                                */
 /* ------------------------------------------------------------------------ */

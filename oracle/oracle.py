@@ -21,7 +21,8 @@ _LIB = os.path.join(_LIB_DIR, "liboracle.so")
 __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
     "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
-    "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads",
+    "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads", "balance_exponents",
+    "balance_apply",
     "score_factor", "kv_append", "block_sums", "hadamard_rows", "attention_train", "mx_quantize",
     "mx_dequantize", "mx_scale_byte",
 ]
@@ -91,6 +92,9 @@ def lib():
     L.orc_mx_dequantize.restype = None
     L.orc_hadamard_rows.argtypes = [_f32p, C.c_int64, C.c_int, _vp]
     L.orc_hadamard_rows.restype = None
+    L.orc_balance_exponents.argtypes = [_f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int,
+                                        _i32p]
+    L.orc_balance_exponents.restype = None
     L.orc_attention_exact.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                       C.c_int64, C.c_int, C.c_int, C.c_double, _vp, C.c_int64,
                                       _vp, C.c_int, _f32p, _vp]
@@ -177,6 +181,27 @@ def hadamard_rows(x, signs=None):
         assert sg.size * 32 >= n
     lib().orc_hadamard_rows(x.reshape(-1), x.size // n, n, _ptr(sg))
     return x
+
+
+def balance_exponents(q, k):
+    """Exponents e [B, Hkv, d] (int32) of the diagonal power-of-two pair
+    Q' = Q 2^-e, K' = K 2^e (orc_balance_exponents): per (batch, kv head) and
+    channel, the integer in [-8, 8] minimizing ms_q 4^-e + ms_k 4^e."""
+    q, k = _f32(q), _f32(k)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    e = np.zeros(B * Hkv * d, np.int32)
+    lib().orc_balance_exponents(q.reshape(-1), k.reshape(-1), B, H, Hkv, Sq, Sk, d, e)
+    return e.reshape(B, Hkv, d)
+
+
+def balance_apply(q, k, e):
+    """Q' = Q 2^-e and K' = K 2^e in binary32 (exact away from overflow and
+    underflow); the exponent vector of kv head h serves its query heads."""
+    q, k = _f32(q), _f32(k)
+    G = q.shape[1] // k.shape[1]
+    eq = np.repeat(e, G, axis=1)[:, :, None, :]
+    return np.ldexp(q, -eq).astype(np.float32), np.ldexp(k, e[:, :, None, :]).astype(np.float32)
 
 
 def mx_quantize(x, block_axis=0):
@@ -271,12 +296,14 @@ def _sel(arr, dtype):
 def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True,
                   fmin=-2, fmax=6, pct=0, sel_block=128, rows=None, heads=None,
                   with_topk=False, hadamard=False, signs=None, single_level_p=False, with_probs=False,
-                  mx=False, tie_slack=None):
+                  mx=False, tie_slack=None, balance=False):
     """Fake-quant FP4 attention. q [B,H,Sq,d], k/v [B,Hkv,Sk,d].
 
     hadamard: the FP4 path quantizes Q and K after incoherence processing
     (hadamard_rows with the given signs); the FP16 path and the block means
-    use the original Q and K.  single_level_p quantizes P with the block
+    use the original Q and K.  balance: the FP4 path quantizes Q 2^-e and
+    K 2^e (balance_exponents, balance_apply), before the rotation when both
+    are on; the FP16 path and the block means again use the originals.  single_level_p quantizes P with the block
     scale alone, E4M3(amax(e)/6) per 16 keys, without the row level.
     mx: the MXFP4 variant (mx_quantize for Q, K, V; P in 32-key blocks with
     the same power-of-two scale rule).  with_probs also returns every row's
@@ -296,9 +323,13 @@ def attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_s
     B, H, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     qr = kr = None
+    qb, kb = q, k
+    if balance:
+        qb, kb = balance_apply(q, k, balance_exponents(q, k))
+        qr, kr = np.ascontiguousarray(qb.reshape(-1)), np.ascontiguousarray(kb.reshape(-1))
     if hadamard:
-        qr = np.ascontiguousarray(hadamard_rows(q, signs).reshape(-1))
-        kr = np.ascontiguousarray(hadamard_rows(k, signs).reshape(-1))
+        qr = np.ascontiguousarray(hadamard_rows(qb, signs).reshape(-1))
+        kr = np.ascontiguousarray(hadamard_rows(kb, signs).reshape(-1))
     ra, nr = _sel(rows, np.int64)
     ha, nh = _sel(heads, np.int32)
     nr = nr if ra is not None else Sq
