@@ -188,6 +188,36 @@ def bench_prefill8k(fp4, synth, torch, n):
                 attn_kernel_frac_fp16_mfma=round(fl / kern / 1e9 / FP16_MFMA_PEAK_TF, 4))
 
 
+def bench_balance(fp4, synth, torch, n):
+    """The balance pair Q 2^-e, K 2^e (and with the Hadamard rotation) on the
+    8K prefill workload: end-to-end time of the forward with and without it,
+    and the error of the FP4 output against exact attention on sampled rows
+    (heads 0 and 1, every 256th row; the oracle's exact attention)."""
+    import numpy as np
+
+    import oracle
+    B, H, S, d = 1, 32, 8192, 128
+    q, k, v = synth.prefill(S=S)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    out = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+    timer = Timer(torch)
+    signs = [0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0xD1B54A32]
+    rows = list(range(0, S, 256))
+    ex, _ = oracle.attention_exact(q, k, v, causal=True, heads=[0, 1], rows=rows)
+    res = {}
+    for name, kw in (("plain", {}), ("balance", dict(balance=True)), ("hadamard", dict(hadamard=True,
+                     hadamard_signs=signs)), ("balance_hadamard", dict(balance=True, hadamard=True,
+                                                                        hadamard_signs=signs))):
+        ms = timer.run(lambda: fp4.fp4_attention_fwd(qc, kc, vc, causal=True, out_dtype=fp4.FP32, return_lse=False,
+                                                     out=out, **kw), n)
+        got = out.cpu().numpy()[0, :2][:, rows]
+        res[name] = dict(end_to_end_ms=round(ms, 4),
+                         rel_l2_vs_exact=round(float(np.linalg.norm(got - ex) / np.linalg.norm(ex)), 5))
+    res["workload"] = ("prefill B=1 H=32 S=8192 d=128 causal with K outlier channels; end to end (exponents, "
+                       "quantization, attention); error on heads 0-1, every 256th row, against exact attention")
+    return res
+
+
 # The quantizer's search is bound by plain VALU work: per element and offset
 # candidate one multiply (element times reciprocal scale), one E2M1 convert
 # there and back (a packed pair per instruction: half an instruction each),
@@ -244,6 +274,12 @@ def bench_quantizer(fp4, synth, torch, n):
                                                     hadamard_signs=had_signs), max(3, n // 4))
     big_given_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, True, -2, 6, fp4.GLOBAL_GIVEN, g=g, out=bo),
                              max(3, n // 4))
+    # max-scaling only at 64x rows: one pass with a given per-tensor scale (the
+    # HBM-bound quantizer), and with the amax pass (reads the input twice)
+    big_max_given_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, False, -2, 6, fp4.GLOBAL_GIVEN, g=g, out=bo),
+                                 max(3, n // 4))
+    big_max_amax_ms = timer.run(lambda: fp4.fp4_quantize(big, 0, False, -2, 6, fp4.GLOBAL_AMAX, g=g, out=bo),
+                                max(3, n // 4))
     alu_tops = rows * 64 * cols * QUANT_LANE_OPS_PER_ELEM / big_ms / 1e9
     cold_gbps = algo / cold / 1e6
     return dict(workload="bf16 [32768,128], 2% outlier channels x20, ScaleSearch f in [-2,6], per-tensor amax scale",
@@ -260,7 +296,63 @@ def bench_quantizer(fp4, synth, torch, n):
                 rows_x64_ms=round(big_ms, 4), rows_x64_GBps=round(big_algo / big_ms / 1e6, 1),
                 rows_x64_frac_hbm=round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4),
                 rows_x64_given_scale_ms=round(big_given_ms, 4),
-                rows_x64_hadamard_given_scale_ms=round(big_had_ms, 4))
+                rows_x64_hadamard_given_scale_ms=round(big_had_ms, 4),
+                max_scaling_x64={
+                    "given_scale_ms": round(big_max_given_ms, 4),
+                    "given_scale_GBps": round(big_algo / big_max_given_ms / 1e6, 1),
+                    "given_scale_frac_hbm": round(big_algo / big_max_given_ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "amax_ms": round(big_max_amax_ms, 4),
+                    "amax_GBps": round(big_algo / big_max_amax_ms / 1e6, 1),
+                    "amax_frac_hbm": round(big_algo / big_max_amax_ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "note": "algorithmic bytes as above; the amax mode reads the input a second time"},
+                scalesearch_over_max_scaling_x64=round(big_given_ms / big_max_given_ms, 3),
+                scalesearch_over_max_scaling_pages="1.74x (0.0449 against 0.0258 ms on the pages' GPU, "
+                                                   "tensor size not stated; context only)")
+
+
+def bench_calibration(fp4, torch):
+    """Achievable peaks measured on this GPU (context for the fractions, which
+    stay against the published peaks): the fp16 MFMA rate with every SIMD
+    running independent 32x32x16 chains, a streaming HBM read of 4 GiB (beyond
+    the 256 MB Infinity Cache) and a 2 GiB device copy."""
+    timer = Timer(torch)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = cus * 8  # 8 workgroups of 4 waves per CU: 8 waves per SIMD
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    iters = 4096
+    ms = timer.run(lambda: fp4.calib_mfma_f16(iters, wg, sink), 5)
+    mfma_tf = wg * 4 * 4 * iters * 32768 / ms / 1e9
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    rwg = cus * 16  # 16 waves per SIMD, eight 16-byte loads in flight each
+    isink = torch.empty(rwg * 256, dtype=torch.int32, device="cuda")
+    ms_r = timer.run(lambda: fp4.calib_read(buf, rwg, isink), 5)
+    read_gbs = buf.numel() / ms_r / 1e6
+    del buf
+    a = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms_c = timer.run(lambda: b.copy_(a), 5)
+    copy_gbs = 2 * a.numel() / ms_c / 1e6
+    del a, b
+    return dict(fp16_mfma_tflops=round(mfma_tf, 1), fp16_mfma_frac_of_published=round(mfma_tf / FP16_MFMA_PEAK_TF, 4),
+                hbm_read_GBps=round(read_gbs, 1), hbm_read_frac_of_published=round(read_gbs / HBM_PEAK_GBS, 4),
+                hbm_copy_GBps=round(copy_gbs, 1),
+                note="fp4_calib_mfma_f16 (every SIMD, independent MFMA chains), fp4_calib_read (4 GiB streamed "
+                     "once), torch device copy of 2 GiB (bytes read + written)")
+
+
+def bench_tiny(fp4, synth, torch, n):
+    """The tiny configuration B=1 H=1 S=256 d=64 fp16 non-causal, max-scaling
+    only, no FP16 path, kv_tile 64: a parity case; its time (quantization plus
+    attention, launch-bound) is reported."""
+    q, k, v = (t.cuda() for t in synth.tiny())
+    out = torch.empty((1, 1, 256, 64), dtype=torch.float32, device="cuda")
+    timer = Timer(torch)
+    ms = timer.run(lambda: fp4.fp4_attention_fwd(q, k, v, causal=False, kv_tile=64, scale_search=False,
+                                                 out_dtype=fp4.FP32, return_lse=False, out=out), max(50, n))
+    fl = attn_flops(1, 1, 256, 64, causal=False)
+    return dict(workload="tiny B=1 H=1 S=256 d=64 fp16 non-causal, max-scaling, kv_tile 64",
+                end_to_end_us=round(ms * 1e3, 2), tflops=round(fl / ms / 1e9, 3),
+                note="three quantizer launches and the attention kernel; launch-bound at this size")
 
 
 def bench_decode(fp4, synth, torch, n, selective=True):
@@ -418,7 +510,8 @@ def bench_kv_append(fp4, torch, n):
     return dict(workload="append 16 tokens to batch 16 x 8 kv heads, d 128, 256-token bf16 window, ScaleSearch",
                 algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
                 roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": None})
+                          "frac": round(gbps / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("kv_append_b16_w256", "kvcache.hip")})
 
 
 def cpu_baseline(q, k, v):
@@ -461,6 +554,8 @@ def pmc_mode(mode, fp4, synth, torch):
         torch.cuda.synchronize()
     elif mode == "decode":
         bench_decode(fp4, synth, torch, 3, selective=False)
+    elif mode == "kvappend":
+        bench_kv_append(fp4, torch, 3)
     elif mode == "quant":
         x = synth.quant_tensor().cuda()
         for _ in range(3):
@@ -476,7 +571,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
-    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy", "decode"], default=None)
+    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy", "decode", "kvappend"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -495,6 +590,10 @@ def main():
     if args.pmc_mode:
         pmc_mode(args.pmc_mode, fp4, synth, torch)
         return
+    calib = None
+    if not args.no_components:
+        log("calibration: achievable fp16 MFMA rate and HBM bandwidth")
+        calib = bench_calibration(fp4, torch)
     res = bench_select32k(fp4, synth, torch, args.steps, args.warmup)
     value = res["flops"] / res["ms"] / 1e9
     kern_tf = res["flops"] / res["kernel_ms"] / 1e9
@@ -525,13 +624,31 @@ def main():
                      "algorithmic_flops": res["flops"], "traffic": traffic,
                      "mfma_busy": read_profile("attn_fwd_select32k_mfma.txt", "attn_fwd.hip", "mfma_busy_frac")},
     }
+    if calib:
+        line["roofline"]["frac_of_measured_peak"] = round(kern_tf / calib["fp16_mfma_tflops"], 4)
+        line["measured_peaks"] = calib
     if not args.no_components:
         log("components: prefill 8K")
         line["components"] = {"prefill_8k": bench_prefill8k(fp4, synth, torch, max(5, args.steps))}
+        log("components: balance pair")
+        line["components"]["balance_8k"] = bench_balance(fp4, synth, torch, max(5, args.steps))
+        log("components: tiny")
+        line["components"]["tiny"] = bench_tiny(fp4, synth, torch, args.steps)
         log("components: quantizer")
         line["components"]["quantizer"] = bench_quantizer(fp4, synth, torch, max(8, args.steps))
         log("components: decode")
         line["components"]["decode"] = bench_decode(fp4, synth, torch, max(5, args.steps))
+        if calib:
+            rd = calib["hbm_read_GBps"]
+            line["components"]["decode"]["roofline"]["frac_of_measured_read"] = round(
+                line["components"]["decode"]["GBps"] / rd, 4)
+            q8 = line["components"]["quantizer"]
+            q8["max_scaling_x64"]["given_scale_frac_of_measured_read"] = round(
+                q8["max_scaling_x64"]["given_scale_GBps"] / rd, 4)
+            q8["max_scaling_x64"]["given_scale_frac_of_measured_copy"] = round(
+                q8["max_scaling_x64"]["given_scale_GBps"] / calib["hbm_copy_GBps"], 4)
+            line["components"]["prefill_8k"]["attn_kernel_frac_of_measured_mfma"] = round(
+                line["components"]["prefill_8k"]["attn_kernel_tflops"] / calib["fp16_mfma_tflops"], 4)
         log("components: kv append")
         line["components"]["kv_append"] = bench_kv_append(fp4, torch, max(10, args.steps))
         log("components: MXFP4 prefill")

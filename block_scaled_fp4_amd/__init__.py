@@ -38,7 +38,8 @@ class FP4Error(RuntimeError):
 class QuantOpts(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
                 ("f_max", C.c_int32), ("global_scale", C.c_int32), ("block_axis", C.c_int32),
-                ("hadamard", C.c_int32), ("hadamard_signs", C.c_uint32 * 4)]
+                ("hadamard", C.c_int32), ("hadamard_signs", C.c_uint32 * 4), ("channel_exp", C.c_void_p),
+                ("exp_negate", C.c_int32), ("exp_rows", C.c_int64)]
 
 
 class AttnProblem(C.Structure):
@@ -54,7 +55,7 @@ class AttnOpts(C.Structure):
                 ("kv_tile", C.c_int32), ("scale_search", C.c_int32), ("f_min", C.c_int32),
                 ("f_max", C.c_int32), ("fp16_budget_pct", C.c_int32), ("sel_block", C.c_int32),
                 ("out_dtype", C.c_int32), ("selection_given", C.c_int32), ("hadamard_qk", C.c_int32),
-                ("hadamard_signs", C.c_uint32 * 4), ("p_single_level", C.c_int32)]
+                ("hadamard_signs", C.c_uint32 * 4), ("p_single_level", C.c_int32), ("balance_qk", C.c_int32)]
 
 
 def _sign_words(signs):
@@ -110,12 +111,20 @@ def load():
     L.fp4_block_topk.restype = C.c_int
     L.fp4_block_topk_workspace_size.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts)]
     L.fp4_block_topk_workspace_size.restype = sz
+    L.fp4_qk_balance.argtypes = [C.POINTER(AttnProblem), vp, vp, sz, vp]
+    L.fp4_qk_balance.restype = C.c_int
+    L.fp4_qk_balance_workspace_size.argtypes = [C.POINTER(AttnProblem)]
+    L.fp4_qk_balance_workspace_size.restype = sz
     L.fp4_attention_decode.argtypes = [vp, i64, C.POINTER(KVCacheStruct), C.c_float, i32, vp, vp, vp, sz, vp]
     L.fp4_attention_decode.restype = C.c_int
     L.fp4_attention_decode_workspace_size.argtypes = [i64, C.POINTER(KVCacheStruct)]
     L.fp4_attention_decode_workspace_size.restype = sz
     L.fp4_attention_decode_noalloc.argtypes = [vp, i64, C.POINTER(KVCacheStruct), C.c_float, i32, vp, vp, vp]
     L.fp4_attention_decode_noalloc.restype = C.c_int
+    L.fp4_calib_mfma_f16.argtypes = [i64, i32, vp, vp]
+    L.fp4_calib_mfma_f16.restype = C.c_int
+    L.fp4_calib_read.argtypes = [vp, sz, i32, vp, vp]
+    L.fp4_calib_read.restype = C.c_int
     L.fp4_mx_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
     L.fp4_mx_quantize.restype = C.c_int
     L.fp4_attention_fwd_mx.argtypes = [C.POINTER(AttnProblem), C.POINTER(AttnOpts), vp, vp, vp, sz, vp]
@@ -194,12 +203,15 @@ def _workspace(n, dev):
 
 def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True, f_min: int = -2,
                  f_max: int = 6, global_scale: int = GLOBAL_NONE, g: torch.Tensor | None = None,
-                 with_offsets: bool = True, out=None, hadamard: bool = False, hadamard_signs=None):
+                 with_offsets: bool = True, out=None, hadamard: bool = False, hadamard_signs=None,
+                 channel_exp=None, exp_negate: bool = False, exp_rows: int = 1):
     """Quantize a 2-D tensor (bf16/fp16/fp32, contiguous rows) to NVFP4 blocks.
 
     hadamard rotates each row first (incoherence processing; hadamard_signs:
-    up to four 32-bit words of sign bits).  Returns dict(codes, scales,
-    offsets, g); layouts as documented in fp4.h."""
+    up to four 32-bit words of sign bits).  channel_exp (int32 GPU tensor
+    [rows / exp_rows, cols], e.g. from fp4_qk_balance) first multiplies row r
+    by 2^(+-e[r // exp_rows]) (minus with exp_negate).  Returns dict(codes,
+    scales, offsets, g); layouts as documented in fp4.h."""
     L = load()
     _dev(x, "x")
     rows, cols = x.shape
@@ -219,8 +231,13 @@ def fp4_quantize(x: torch.Tensor, block_axis: int = 0, scale_search: bool = True
         offs = torch.empty(sshape, dtype=torch.int8, device=dev) if with_offsets else None
     if g is None and global_scale != GLOBAL_NONE:
         g = torch.empty(1, dtype=torch.float32, device=dev)
+    if channel_exp is not None:
+        _dev(channel_exp, "channel_exp")
+        if channel_exp.dtype != torch.int32 or channel_exp.numel() * int(exp_rows) != rows * cols:
+            raise FP4Error(-1, "channel_exp must be int32 with rows / exp_rows * cols elements")
     o = QuantOpts(C.sizeof(QuantOpts), int(bool(scale_search)), f_min, f_max, global_scale, block_axis,
-                  int(bool(hadamard)), _sign_words(hadamard_signs))
+                  int(bool(hadamard)), _sign_words(hadamard_signs), _ptr(channel_exp), int(bool(exp_negate)),
+                  int(exp_rows))
     nws = L.fp4_quantize_workspace_size(rows, cols, C.byref(o))
     ws = _workspace(nws, dev)
     st = L.fp4_quantize(_ptr(x), _DT[x.dtype], rows, cols, cols, C.byref(o), _ptr(codes), _ptr(scales),
@@ -259,10 +276,25 @@ def _problem(q, k, v, quant=None):
 
 
 def _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, pct, sel_block, out_dtype, given=False,
-          hadamard=False, hadamard_signs=None, single_level_p=False):
+          hadamard=False, hadamard_signs=None, single_level_p=False, balance=False):
     return AttnOpts(C.sizeof(AttnOpts), int(bool(causal)), float(softmax_scale), kv_tile,
                     int(bool(scale_search)), f_min, f_max, int(pct), sel_block, out_dtype, int(bool(given)),
-                    int(bool(hadamard)), _sign_words(hadamard_signs), int(bool(single_level_p)))
+                    int(bool(hadamard)), _sign_words(hadamard_signs), int(bool(single_level_p)), int(bool(balance)))
+
+
+def fp4_qk_balance(q, k):
+    """Exponents e [B, Hkv, d] (int32) of the balance pair Q 2^-e, K 2^e
+    (fp4.h: fp4_qk_balance).  q [B,H,Sq,d], k [B,Hkv,Sk,d] bf16 or fp16."""
+    L = load()
+    for t, n in ((q, "q"), (k, "k")):
+        _dev(t, n)
+    P = _problem(q, k, k)
+    B, Hkv, d = k.shape[0], k.shape[1], k.shape[3]
+    e = torch.empty((B, Hkv, d), dtype=torch.int32, device=q.device)
+    nws = L.fp4_qk_balance_workspace_size(C.byref(P))
+    ws = _workspace(nws, q.device)
+    _check(L.fp4_qk_balance(C.byref(P), _ptr(e), _ptr(ws), nws, _stream(q.device)))
+    return e
 
 
 def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile=128):
@@ -288,7 +320,7 @@ def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile
 def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, scale_search=True, f_min=-2,
                       f_max=6, fp16_budget_pct=0, sel_block=128, out_dtype=BF16, quantized=None,
                       return_lse=True, return_topk=False, workspace=None, out=None, selection=None,
-                      hadamard=False, hadamard_signs=None, single_level_p=False):
+                      hadamard=False, hadamard_signs=None, single_level_p=False, balance=False):
     """FP4 attention forward.  q [B,H,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp16).
 
     single_level_p: P is quantized with the NVFP4 block scale alone (no row
@@ -311,7 +343,7 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
         B, H, Sq, d = quantized["q_shape"]
     P = _problem(q, k, v, quantized)
     O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, fp16_budget_pct, sel_block, out_dtype,
-              selection is not None, hadamard, hadamard_signs, single_level_p)
+              selection is not None, hadamard, hadamard_signs, single_level_p, balance)
     out = _out(out, (B, H, Sq, d), _TORCH_DT[out_dtype], dev)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if return_lse else None
     idx = cnt = None
@@ -519,3 +551,27 @@ def fp4_kv_cache_append(cache: KVCache, k_new, v_new, workspace=None):
     _check(L.fp4_kv_cache_append(C.byref(cs), _ptr(k_new), _ptr(v_new), n_new, _ptr(overflow), _ptr(ws), nws,
                                  _stream(k_new.device)))
     return overflow
+
+
+def calib_mfma_f16(iters: int, workgroups: int, sink):
+    """Measurement helper (fp4_calib.h): `workgroups` x 4 waves of four
+    independent fp16 32x32x16 MFMA chains, `iters` rounds each.  sink: float32
+    GPU tensor of workgroups * 256 elements."""
+    L = load()
+    _out(sink, (workgroups * 256,), torch.float32, sink.device, "sink")
+    st = L.fp4_calib_mfma_f16(int(iters), int(workgroups), _ptr(sink), _stream(sink.device))
+    if st != 0:
+        raise FP4Error(st, "fp4_calib_mfma_f16 failed")
+
+
+def calib_read(buf, workgroups: int, sink):
+    """Measurement helper (fp4_calib.h): read buf (a contiguous GPU tensor,
+    byte size a multiple of 16) once.  sink: int32 GPU tensor of workgroups * 256."""
+    L = load()
+    _dev(buf, "buf")
+    _out(sink, (workgroups * 256,), torch.int32, sink.device, "sink")
+    st = L.fp4_calib_read(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups), _ptr(sink),
+                          _stream(buf.device))
+    if st != 0:
+        raise FP4Error(st, "fp4_calib_read failed")
+

@@ -12,7 +12,7 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.cpp", "quantize.hip", "topk.hip", "attn_fwd.hip", "attn_decode.hip", "kvcache.hip", "attn_train.hip", "attn_mx.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "calib.hip"]
 ARCH = "gfx950"
 # -ffp-contract=off: no multiply-add is fused unless written as fmaf (the
 # quantizer's error sums and scale decisions are defined without contraction).

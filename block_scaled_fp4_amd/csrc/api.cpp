@@ -68,6 +68,15 @@ int check_quant_opts(const fp4_quant_opts* o) {
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: hadamard needs block_axis 0");
   if (o->hadamard && o->global_scale == FP4_GLOBAL_AMAX)
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: hadamard with FP4_GLOBAL_AMAX is not supported");
+  if (o->channel_exp) {
+    if (o->block_axis != 0) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: channel_exp needs block_axis 0");
+    if (o->exp_negate != 0 && o->exp_negate != 1)
+      return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: exp_negate must be 0 or 1");
+    if (o->exp_rows < 1) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: exp_rows must be >= 1");
+    if (o->global_scale == FP4_GLOBAL_AMAX)
+      return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: channel_exp with FP4_GLOBAL_AMAX is not supported");
+    if (!aligned16(o->channel_exp)) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: channel_exp must be 16-byte aligned");
+  }
   return FP4_OK;
 }
 
@@ -87,7 +96,7 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 struct AttnPlan {
-  size_t qc, qs, kc, ks, vc, vs, qm, km, idx, cnt, keys, total;
+  size_t qc, qs, kc, ks, vc, vs, qm, km, idx, cnt, keys, bpart, bexp, total;
   int nqb, nkb, kmax;
   bool need_quant, need_sel;
 };
@@ -110,6 +119,10 @@ AttnPlan plan_attn(const fp4_attn_problem* p, const fp4_attn_opts* o) {
     P.ks = take((size_t)(B * Hkv * Sk * d / 16));
     P.vc = take((size_t)(B * Hkv * Sk * d / 2));
     P.vs = take((size_t)(B * Hkv * Sk * d / 16));
+    if (o->balance_qk) {
+      P.bpart = take(fp4i_balance_partials(B, H, Hkv, Sq, Sk, d) * sizeof(double));
+      P.bexp = take((size_t)(B * Hkv * d) * sizeof(int32_t));
+    }
   }
   if (P.need_sel) {
     P.qm = take((size_t)(B * H * P.nqb * d) * sizeof(double));
@@ -164,6 +177,9 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
     return fail(FP4_ERR_INVALID_ARG, "%s: p_single_level must be 0 or 1", fn);
   if (o->hadamard_qk && all_codes)
     return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk applies to the call's own quantization (no pre-quantized operands)", fn);
+  if (o->balance_qk != 0 && o->balance_qk != 1) return fail(FP4_ERR_INVALID_ARG, "%s: balance_qk must be 0 or 1", fn);
+  if (o->balance_qk && all_codes)
+    return fail(FP4_ERR_INVALID_ARG, "%s: balance_qk applies to the call's own quantization (no pre-quantized operands)", fn);
   const void* ptrs[] = {p->q, p->k, p->v, p->q_codes, p->q_scales, p->k_codes, p->k_scales, p->v_codes, p->v_scales};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
@@ -196,6 +212,8 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: bad shape/ld");
   if (opts->block_axis == 0 && cols % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: cols %% 16 != 0");
   if (opts->block_axis == 1 && rows % 16) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: rows %% 16 != 0");
+  if (opts->channel_exp && rows % opts->exp_rows)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: exp_rows must divide rows");
   if (opts->hadamard && !hadamard_size(cols))
     return fail(FP4_ERR_UNSUPPORTED, "fp4_quantize: hadamard needs cols in {16, 32, 64, 128}");
   if (rows > 0 && cols > 0 && (!x || !codes || !scales))
@@ -229,6 +247,9 @@ int fp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64
   L.hadamard = opts->hadamard;
   for (int i = 0; i < 4; ++i) L.hsigns[i] = opts->hadamard_signs[i];
   L.hscale = hadamard_scale(cols);
+  L.cexp = opts->channel_exp;
+  L.exp_negate = opts->exp_negate;
+  L.exp_rows = opts->exp_rows;
   return hip_status(fp4i_launch_quantize(L, (hipStream_t)stream), "fp4_quantize launch");
 }
 
@@ -284,6 +305,33 @@ static int launch_selection(const fp4_attn_problem* p, const fp4_attn_opts* o, c
   return hip_status(fp4i_launch_topk(T, s), "block selection launch");
 }
 
+size_t fp4_qk_balance_workspace_size(const fp4_attn_problem* prob) {
+  if (!prob || prob->struct_size < sizeof(fp4_attn_problem) || prob->B < 1 || prob->H < 1 || prob->Hkv < 1 ||
+      prob->Sq < 1 || prob->Sk < 1 || prob->H % prob->Hkv || (prob->d != 64 && prob->d != 128))
+    return 0;
+  return fp4i_balance_partials(prob->B, prob->H, prob->Hkv, prob->Sq, prob->Sk, prob->d) * sizeof(double);
+}
+
+int fp4_qk_balance(const fp4_attn_problem* prob, int32_t* exponents, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const char* fn = "fp4_qk_balance";
+  if (!prob || prob->struct_size < sizeof(fp4_attn_problem)) return fail(FP4_ERR_INVALID_ARG, "%s: bad problem", fn);
+  if (prob->B < 1 || prob->H < 1 || prob->Hkv < 1 || prob->Sq < 1 || prob->Sk < 1 || prob->H % prob->Hkv)
+    return fail(FP4_ERR_INVALID_ARG, "%s: bad B/H/Hkv/Sq/Sk", fn);
+  if (prob->d != 64 && prob->d != 128) return fail(FP4_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128", fn);
+  if (prob->dtype != FP4_BF16 && prob->dtype != FP4_FP16) return fail(FP4_ERR_UNSUPPORTED, "%s: bf16 or fp16", fn);
+  if (!prob->q || !prob->k || !exponents) return fail(FP4_ERR_INVALID_ARG, "%s: q, k and exponents are required", fn);
+  if (!aligned16(prob->q) || !aligned16(prob->k)) return fail(FP4_ERR_INVALID_ARG, "%s: q, k must be 16-byte aligned", fn);
+  const size_t need = fp4_qk_balance_workspace_size(prob);
+  if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  BalanceLaunch BL{};
+  BL.q = prob->q; BL.k = prob->k; BL.dtype = prob->dtype;
+  BL.B = prob->B; BL.H = prob->H; BL.Hkv = prob->Hkv; BL.Sq = prob->Sq; BL.Sk = prob->Sk; BL.d = prob->d;
+  BL.partial = (double*)workspace;
+  BL.exps = exponents;
+  return hip_status(fp4i_launch_balance(BL, (hipStream_t)stream), "fp4_qk_balance launch");
+}
+
 int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int32_t* topk_idx,
                    int32_t* topk_cnt, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_attn(prob, opts, "fp4_block_topk", true);
@@ -330,14 +378,29 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
     L.hadamard = opts->hadamard_qk;  // Q and K only; V is never rotated
     for (int i = 0; i < 4; ++i) L.hsigns[i] = opts->hadamard_signs[i];
     L.hscale = hadamard_scale(d);
-    hipError_t e = fp4i_launch_quantize(L, s);
+    hipError_t e = hipSuccess;
+    if (opts->balance_qk) {  // exponents of the pair Q 2^-e, K 2^e, applied by the row quantizer
+      BalanceLaunch BL{};
+      BL.q = prob->q; BL.k = prob->k; BL.dtype = prob->dtype;
+      BL.B = B; BL.H = H; BL.Hkv = Hkv; BL.Sq = Sq; BL.Sk = Sk; BL.d = d;
+      BL.partial = (double*)(ws + P.bpart);
+      BL.exps = (int32_t*)(ws + P.bexp);
+      e = fp4i_launch_balance(BL, s);
+      L.cexp = BL.exps;
+      L.exp_negate = 1;
+      L.exp_rows = (H / Hkv) * Sq;  // the query heads of a kv head are consecutive
+    }
+    if (e == hipSuccess) e = fp4i_launch_quantize(L, s);
     if (e == hipSuccess) {
       L.x = prob->k; L.rows = B * Hkv * Sk;
       L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
+      L.exp_negate = 0;
+      L.exp_rows = Sk;
       e = fp4i_launch_quantize(L, s);
     }
     if (e == hipSuccess) {
       L.x = prob->v; L.axis = 1; L.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
+      L.cexp = nullptr;
       L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
       e = fp4i_launch_quantize(L, s);
     }
@@ -413,6 +476,7 @@ int fp4_attention_fwd_mx(const fp4_attn_problem* prob, const fp4_attn_opts* opts
   if (st) return st;
   if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_INVALID_ARG, "%s: no FP16 path (fp16_budget_pct must be 0)", fn);
   if (opts->hadamard_qk) return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk must be 0", fn);
+  if (opts->balance_qk) return fail(FP4_ERR_INVALID_ARG, "%s: balance_qk must be 0", fn);
   if (prob->Sk % 32) return fail(FP4_ERR_INVALID_ARG, "%s: Sk %% 32 != 0", fn);
   if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "%s: out must be non-NULL and 16-byte aligned", fn);
   const size_t need = fp4_attention_fwd_mx_workspace_size(prob, opts);
@@ -465,6 +529,7 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
   if (st) return st;
   if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_UNSUPPORTED, "%s: training has no FP16 path (fp16_budget_pct must be 0)", fn);
   if (opts->hadamard_qk) return fail(FP4_ERR_UNSUPPORTED, "%s: the rotation is not supported in training", fn);
+  if (opts->balance_qk) return fail(FP4_ERR_UNSUPPORTED, "%s: the balance pair is not supported in training", fn);
   if (!out_hp || !lse || !dout || !dq || !dk || !dv) return fail(FP4_ERR_INVALID_ARG, "%s: out_hp, lse, dout, dq, dk, dv are required", fn);
   const void* ptrs[] = {out_hp, lse, dout, dq, dk, dv};
   for (const void* ptr : ptrs)

@@ -17,7 +17,23 @@ struct QuantLaunch {
   int hadamard;            // rotate rows (axis 0) before quantizing
   uint32_t hsigns[4];      // sign bits of the rotation
   float hscale;            // binary32 1/sqrt(cols)
+  const int32_t* cexp;     // balance exponents [rows / exp_rows][cols], or null (axis 0)
+  int exp_negate;          // 1: multiply by 2^-e (Q side)
+  int64_t exp_rows;        // rows sharing one exponent vector
 };
+
+// Balance exponents: per (batch, kv head) binary64 partial sums of squares of
+// Q (the group's heads) and K over chunks of rows, then the exponents.
+struct BalanceLaunch {
+  const void* q;  // [B, H, Sq, d]
+  const void* k;  // [B, Hkv, Sk, d]
+  int dtype;      // 0 bf16, 1 fp16
+  int64_t B, H, Hkv, Sq, Sk, d;
+  double* partial;  // fp4i_balance_partials doubles
+  int32_t* exps;    // [B, Hkv, d]
+};
+size_t fp4i_balance_partials(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t d);
+hipError_t fp4i_launch_balance(const BalanceLaunch& L, hipStream_t stream);
 
 int fp4i_amax_parts(int64_t rows, int64_t cols);
 hipError_t fp4i_launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,

@@ -39,7 +39,27 @@ struct QuantArgs {
   int search, fmin, fmax, gmode;
   uint32_t hsigns[4];  // incoherence processing: sign bits and 1/sqrt(cols)
   float hscale;
+  const int32_t* cexp;  // balance exponents [rows / exp_rows][cols] (BAL instances)
+  int exp_negate;
+  int64_t exp_rows;
 };
+
+// Magnitude balance of one block (ScaleSearch page, Metodologia /
+// ScaleSearchAttention, the pair Q' = Q R^-T, K' = K R with R = diag(2^e)):
+// element i of block cb of row r times 2^(+-e[r / exp_rows][16 cb + i]),
+// exact in binary32 (v_ldexp_f32).
+__device__ __forceinline__ void balance_block(float (&y)[16], const QuantArgs& A, int64_t r, int64_t cb) {
+  const uint4_t* ep = reinterpret_cast<const uint4_t*>(A.cexp + (r / A.exp_rows) * A.cols + cb * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4_t w = ep[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (int)w[i];
+      y[4 * j + i] = __builtin_ldexpf(y[4 * j + i], A.exp_negate ? -e : e);
+    }
+  }
+}
 
 // Incoherence processing of one row held by the bpr = cols/16 consecutive
 // lanes of its blocks (ScaleSearch page, Metodologia / ScaleSearchAttention):
@@ -147,7 +167,7 @@ __device__ __forceinline__ void raw_to_f32<float>(const RawBlock<float>& R, floa
 // consecutive blocks (2 KiB of bf16) and writes their 512 code bytes.  The
 // grid is a few workgroups per CU that stride over the blocks, each lane
 // loading its next block while it searches the current one.
-template <typename T, bool HAD>
+template <typename T, bool HAD, bool BAL>
 __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
   __shared__ float2_t tab[128];
   __shared__ float sh[8];
@@ -169,6 +189,7 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
     float y[16];
     raw_to_f32<T>(raw, y);
     if (blk + stride < nb) load_raw<T>(raw, src(blk + stride));
+    if (BAL) balance_block(y, A, blk / bpr, blk % bpr);
     if (HAD) hadamard_block(y, A, blk % bpr, (int)bpr);
     if (A.gmode != 0) {
 #pragma unroll
@@ -366,6 +387,96 @@ int fp4i_amax_parts(int64_t rows, int64_t cols) {
   return (int)p;
 }
 
+template <bool HAD, bool BAL>
+void launch_axis0(int dtype, int64_t grid, const QuantArgs& A, hipStream_t stream) {
+  if (dtype == 0) hipLaunchKernelGGL((quantize_axis0_kernel<uint16_t, HAD, BAL>), dim3(grid), dim3(256), 0, stream, A);
+  else if (dtype == 1) hipLaunchKernelGGL((quantize_axis0_kernel<half_t, HAD, BAL>), dim3(grid), dim3(256), 0, stream, A);
+  else hipLaunchKernelGGL((quantize_axis0_kernel<float, HAD, BAL>), dim3(grid), dim3(256), 0, stream, A);
+}
+
+// ---- magnitude balance exponents -----------------------------------------
+// Per (batch, kv head): the rows of Q of its group (G*Sq rows, contiguous) and
+// the rows of K (Sk rows, contiguous) are cut into chunks of kBalRows rows;
+// a workgroup forms one chunk's binary64 sums of squares per channel (one
+// thread per 8 channels and a subset of the rows, then the row groups added in
+// order); the finalize kernel adds the chunks in order, divides by the counts
+// and decides the exponents.
+constexpr int kBalRows = 256;
+
+template <typename T>
+__global__ void __launch_bounds__(256) balance_partial_kernel(const T* q, const T* k, int64_t H, int64_t Hkv,
+                                                              int64_t Sq, int64_t Sk, int d, int nchunk,
+                                                              double* partial) {
+  __shared__ double red[32][128];
+  const int64_t G = H / Hkv;
+  const int64_t gi = blockIdx.x;  // ((bk * 2 + side) * nchunk + chunk)
+  const int chunk = (int)(gi % nchunk);
+  const int side = (int)((gi / nchunk) % 2);
+  const int64_t bk = gi / (2 * nchunk);
+  const int64_t b = bk / Hkv, hk = bk - b * Hkv;
+  const int64_t nrows = side == 0 ? G * Sq : Sk;
+  const T* base = side == 0 ? q + (b * H + hk * G) * Sq * d : k + bk * Sk * d;
+  const int per = d / 8;                 // threads per row
+  const int rgroups = 256 / per;         // rows in flight per pass (16 or 32)
+  const int c0 = (threadIdx.x % per) * 8, rg = threadIdx.x / per;
+  double s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.0;
+  const int64_t r0 = (int64_t)chunk * kBalRows;
+  const int64_t r1 = r0 + kBalRows < nrows ? r0 + kBalRows : nrows;
+  for (int64_t r = r0 + rg; r < r1; r += rgroups) {
+    const uint4_t w = *reinterpret_cast<const uint4_t*>(base + r * d + c0);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (sizeof(T) == 2 && __is_same(T, uint16_t)) {
+        y[2 * e] = __uint_as_float(w[e] << 16);
+        y[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      } else {
+        const half2_t h = __builtin_bit_cast(half2_t, w[e]);
+        y[2 * e] = (float)h[0];
+        y[2 * e + 1] = (float)h[1];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = s[e] + (double)y[e] * (double)y[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][c0 + e] = s[e];
+  __syncthreads();
+  if (threadIdx.x < d) {
+    double t = 0.0;
+    for (int g = 0; g < rgroups; ++g) t = t + red[g][threadIdx.x];
+    partial[gi * d + threadIdx.x] = t;
+  }
+}
+
+// one thread per (batch, kv head, channel)
+__global__ void __launch_bounds__(128) balance_exp_kernel(const double* partial, int64_t n_bk, int64_t G,
+                                                          int64_t Sq, int64_t Sk, int d, int nchunk,
+                                                          int32_t* exps) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_bk * d) return;
+  const int64_t bk = i / d;
+  const int c = (int)(i - bk * d);
+  double sq = 0.0, sk = 0.0;
+  const int nq = (int)((G * Sq + kBalRows - 1) / kBalRows), nk = (int)((Sk + kBalRows - 1) / kBalRows);
+  for (int ch = 0; ch < nq; ++ch) sq = sq + partial[((bk * 2 + 0) * nchunk + ch) * d + c];
+  for (int ch = 0; ch < nk; ++ch) sk = sk + partial[((bk * 2 + 1) * nchunk + ch) * d + c];
+  const double mq = sq / (double)(G * Sq), mk = sk / (double)Sk;
+  int e = 0;
+  if (mq > 0.0 && mk > 0.0) {
+    const double A = mq / mk;
+    e = 8;
+    for (int x = -8; x <= 8; ++x)
+      if (__builtin_ldexp(1.0, 2 * (2 * x + 1)) >= A) {
+        e = x;
+        break;
+      }
+  }
+  exps[i] = e;
+}
+
 hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   QuantArgs A;
   A.x = L.x;
@@ -407,14 +518,15 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   if (grid < 1) grid = 1;
   for (int i = 0; i < 4; ++i) A.hsigns[i] = L.hsigns[i];
   A.hscale = L.hscale;
-  if (L.axis == 0 && L.hadamard) {
-    if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis0_kernel<uint16_t, true>), dim3(grid), dim3(256), 0, stream, A);
-    else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis0_kernel<half_t, true>), dim3(grid), dim3(256), 0, stream, A);
-    else hipLaunchKernelGGL((quantize_axis0_kernel<float, true>), dim3(grid), dim3(256), 0, stream, A);
-  } else if (L.axis == 0) {
-    if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis0_kernel<uint16_t, false>), dim3(grid), dim3(256), 0, stream, A);
-    else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis0_kernel<half_t, false>), dim3(grid), dim3(256), 0, stream, A);
-    else hipLaunchKernelGGL((quantize_axis0_kernel<float, false>), dim3(grid), dim3(256), 0, stream, A);
+  A.cexp = L.cexp;
+  A.exp_negate = L.exp_negate;
+  A.exp_rows = L.exp_rows > 0 ? L.exp_rows : 1;
+  if (L.axis == 0) {
+    const bool had = L.hadamard != 0, bal = L.cexp != nullptr;
+    if (had && bal) launch_axis0<true, true>(L.dtype, grid, A, stream);
+    else if (had) launch_axis0<true, false>(L.dtype, grid, A, stream);
+    else if (bal) launch_axis0<false, true>(L.dtype, grid, A, stream);
+    else launch_axis0<false, false>(L.dtype, grid, A, stream);
   } else {
     if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis1_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
     else if (L.dtype == 1) hipLaunchKernelGGL(quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
@@ -440,5 +552,29 @@ hipError_t fp4i_launch_mx_quantize(const void* x, int dtype, int64_t rows, int64
     else if (dtype == 1) hipLaunchKernelGGL(mx_quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
     else hipLaunchKernelGGL(mx_quantize_axis1_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
   }
+  return hipGetLastError();
+}
+
+size_t fp4i_balance_partials(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t d) {
+  const int64_t G = H / Hkv;
+  const int64_t nq = (G * Sq + kBalRows - 1) / kBalRows, nk = (Sk + kBalRows - 1) / kBalRows;
+  const int64_t nchunk = nq > nk ? nq : nk;
+  return (size_t)(B * Hkv * 2 * nchunk * d);
+}
+
+hipError_t fp4i_launch_balance(const BalanceLaunch& L, hipStream_t stream) {
+  const int64_t G = L.H / L.Hkv;
+  const int64_t nq = (G * L.Sq + kBalRows - 1) / kBalRows, nk = (L.Sk + kBalRows - 1) / kBalRows;
+  const int nchunk = (int)(nq > nk ? nq : nk);
+  const int64_t n_bk = L.B * L.Hkv;
+  const dim3 grid((unsigned)(n_bk * 2 * nchunk));
+  if (L.dtype == 0)
+    hipLaunchKernelGGL(balance_partial_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t*)L.q,
+                       (const uint16_t*)L.k, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
+  else
+    hipLaunchKernelGGL(balance_partial_kernel<half_t>, grid, dim3(256), 0, stream, (const half_t*)L.q,
+                       (const half_t*)L.k, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
+  hipLaunchKernelGGL(balance_exp_kernel, dim3((unsigned)((n_bk * L.d + 127) / 128)), dim3(128), 0, stream, L.partial,
+                     n_bk, G, L.Sq, L.Sk, (int)L.d, nchunk, L.exps);
   return hipGetLastError();
 }

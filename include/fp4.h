@@ -81,7 +81,7 @@ typedef struct fp4_quant_opts {
   int32_t global_scale; /* FP4_GLOBAL_* */
   int32_t block_axis;   /* 0: blocks of 16 consecutive columns; 1: of 16 consecutive rows */
   /* Incoherence processing (ScaleSearch page, Metodologia / ScaleSearchAttention:
-     Hadamard transforms before quantization, following QuIP#).  1: every row
+     Hadamard transforms before quantization, as in QuIP#).  1: every row
      is first replaced by H_n (s o row) / sqrt(n), n = cols, s_j = -1 where bit
      j of hadamard_signs is set (bit j % 32 of word j / 32), H_n the Sylvester
      Hadamard matrix applied by binary32 butterfly stages of span 1, 2, 4, ...
@@ -90,6 +90,17 @@ typedef struct fp4_quant_opts {
      scale mode other than FP4_GLOBAL_AMAX.  0: off. */
   int32_t hadamard;
   uint32_t hadamard_signs[4];
+  /* Magnitude balance (ScaleSearch page, Metodologia / ScaleSearchAttention:
+     a pair Q' = Q R^-T, K' = K R that keeps Q K^T, here with R = diag(2^e)).
+     NULL: off.  Otherwise a device array of int32 exponents
+     [rows / exp_rows][cols] (e.g. from fp4_qk_balance): every element of row
+     r is first multiplied by 2^(e[r / exp_rows][col]), by 2^-e when exp_negate
+     is 1 (the Q side), exactly in binary32, before the rotation and the
+     per-tensor factor.  Needs block_axis 0, exp_rows >= 1 dividing rows, and a
+     global scale mode other than FP4_GLOBAL_AMAX. */
+  const int32_t* channel_exp;
+  int32_t exp_negate;
+  int64_t exp_rows;
 } fp4_quant_opts;
 
 /*
@@ -192,6 +203,10 @@ typedef struct fp4_attn_opts {
                               s2 = E4M3(amax(e) / 6) per 16 keys and codes RNE_E2M1(e / s2)
                               (Attn-QAT page, Metodologia / B: no two-level step); 0: the
                               two-level P above */
+  int32_t balance_qk;      /* 1: the call quantizes Q' = Q 2^-e and K' = K 2^e with the
+                              exponents of fp4_qk_balance (before the rotation when hadamard_qk
+                              is on); QK^T is kept exactly, the FP16 path and the block means use
+                              the original Q and K.  Needs the call to quantize. */
 } fp4_attn_opts;
 
 /*
@@ -232,6 +247,26 @@ int fp4_block_topk(const fp4_attn_problem* prob, const fp4_attn_opts* opts, int3
                    int32_t* topk_cnt, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_attn_opts* opts);
+
+/*
+ * Exponents of the magnitude-balancing pair Q' = Q R^-T, K' = K R (ScaleSearch
+ * page, Metodologia / ScaleSearchAttention: a pair of linear maps that keeps
+ * the attention scores and lowers the mean squared magnitude of Q and K).
+ * R = diag(2^e) per (batch, kv head): ms_q[c] is the mean of q^2 over the
+ * group's Hq/Hkv query heads and all Sq tokens, ms_k[c] the mean of k^2 over
+ * the kv head's Sk tokens (binary64 sums), and e_c is the integer in [-8, 8]
+ * minimizing ms_q 4^-e + ms_k 4^e: the smallest e with 4^(2e+1) >= ms_q/ms_k
+ * (0 when either mean square is 0).  Because the entries are powers of two,
+ * Q' and K' are exact in binary32 and Q' K'^T = Q K^T.
+ * exponents: device int32 [B, Hkv, d] (written).  Needs prob->q and prob->k
+ * (bf16 or fp16, dense).  The binary64 sums are reduced in a parallel order;
+ * an exponent can depend on that order only when ms_q/ms_k lies within a few
+ * units in the last place of a boundary 4^(2e+1).
+ */
+int fp4_qk_balance(const fp4_attn_problem* prob, int32_t* exponents, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+size_t fp4_qk_balance_workspace_size(const fp4_attn_problem* prob);
 
 /*
  * MXFP4 variant of the forward (blocks of 32 with power-of-two scales, the

@@ -7,13 +7,18 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp4.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text)))
+    """Every function declared by a header under include/."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +31,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert {"fp4_quantize", "fp4_attention_fwd", "fp4_attention_decode", "fp4_block_topk"} <= set(names)
+    assert {"fp4_quantize", "fp4_attention_fwd", "fp4_attention_decode", "fp4_block_topk",
+            "fp4_calib_mfma_f16", "fp4_calib_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.fp4_version() == 10000
@@ -253,3 +259,34 @@ def test_noalloc_decode_rejects_oversized_problems(L):
     assert st == -2 and "scratch" in msg and str(need) in msg
     # invalid arguments are reported as by fp4_attention_decode
     assert L.fp4_attention_decode_noalloc(fake, 0, C.byref(cs), 0.0, 2, fake, None, None) == -1
+
+
+def test_balance_options_are_validated(L):
+    """The balance pair's options are refused before any launch when they do
+    not fit (ScaleSearch page, Metodologia / ScaleSearchAttention)."""
+    import block_scaled_fp4_amd as fp4
+    fake = C.c_void_p(1 << 20)
+    # quantizer: channel exponents need block_axis 0, exp_rows dividing rows, no AMAX mode, 0/1 negate
+    ax1 = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 1, 0, (C.c_uint32 * 4)(), fake, 0, 16)
+    assert L.fp4_quantize(fake, 0, 32, 32, 32, C.byref(ax1), fake, fake, None, None, None, 0, None) == -1
+    rows = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 0, 0, (C.c_uint32 * 4)(), fake, 0, 3)
+    assert L.fp4_quantize(fake, 0, 32, 32, 32, C.byref(rows), fake, fake, None, None, None, 0, None) == -1
+    assert "exp_rows" in L.fp4_last_error().decode()
+    amax = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 1, 0, 0, (C.c_uint32 * 4)(), fake, 0, 16)
+    assert L.fp4_quantize(fake, 0, 32, 32, 32, C.byref(amax), fake, fake, None, fake, fake, 1 << 20, None) == -1
+    neg = fp4.QuantOpts(C.sizeof(fp4.QuantOpts), 1, -2, 6, 0, 0, 0, (C.c_uint32 * 4)(), fake, 2, 16)
+    assert L.fp4_quantize(fake, 0, 32, 32, 32, C.byref(neg), fake, fake, None, None, None, 0, None) == -1
+    # attention: balance_qk needs the call's own quantization
+    quant = dict(q_codes=fake, q_scales=fake, k_codes=fake, k_scales=fake, v_codes=fake, v_scales=fake)
+    P = _prob(fp4, **quant)
+    O = fp4._opts(True, 0.0, 128, True, -2, 6, 0, 128, fp4.FP32, balance=True)
+    assert L.fp4_attention_fwd(C.byref(P), C.byref(O), fake, None, None, None, fake, 1 << 30, None) == -1
+    assert "balance_qk" in L.fp4_last_error().decode()
+    # the exponent entry point: shapes, dtype and workspace
+    Pq = _prob(fp4)
+    need = L.fp4_qk_balance_workspace_size(C.byref(Pq))
+    assert need > 0
+    assert L.fp4_qk_balance(C.byref(Pq), fake, fake, need - 1, None) == -3
+    assert L.fp4_qk_balance(C.byref(Pq), None, fake, need, None) == -1
+    P64 = _prob(fp4, d=96)
+    assert L.fp4_qk_balance(C.byref(P64), fake, fake, 1 << 30, None) == -2

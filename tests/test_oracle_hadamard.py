@@ -1,6 +1,6 @@
 """Pins of the oracle's incoherence processing (ScaleSearch page, Metodologia /
 ScaleSearchAttention: Hadamard transforms of Q and K before quantization,
-following QuIP#; a rotation R applied to both keeps Q K^T).
+as QuIP# does; a rotation R applied to both keeps Q K^T).
 
 The transform is R = diag(s) H_n / sqrt(n) with H_n the Sylvester Hadamard
 matrix; the pins compare it with scipy's Hadamard matrix, check the
