@@ -303,41 +303,74 @@ __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S)
   }
 }
 
-// FP16 path staging: original bf16/fp16 K and V of the tile (buffer loads, so
-// keys past Sk read as zero), converted to fp16.
-template <int D, int BC, typename IT>
-__device__ __forceinline__ void stage_fp16(Smem<D, BC>& S, rsrc_t kr16, rsrc_t vr16, int64_t key0) {
-  // K: BC rows x D; 8 elements (16 bytes) per step
-  constexpr int NK = BC * D / 8;
-  for (int q = threadIdx.x; q < NK; q += 256) {
-    const int kr = q / (D / 8), dc = q % (D / 8);
-    const uint32_t key = (uint32_t)key0 + kr;
-    const uint4_t w = buf_load16(kr16, (key * D + dc * 8) * 2);
-    half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
-    S.k[kr * Smem<D, BC>::KS8 + dc] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+// FP16 path: the original bf16/fp16 K and V of one step of keys (32 at
+// d = 128, 64 at d = 64: the most whose registers fit beside the wave's
+// state), fetched into registers (buffer loads, so keys past Sk read as zero)
+// one step ahead of their use and then converted to fp16 into the first keys
+// of the tile layout.  K: rows x D, 16 bytes per load.  V: a chunk is a token
+// pair x 8 columns going to V^T; as in the FP4 staging, a half-wave's chunks
+// sit in d-groups 32 rows apart (conflict-free writes).
+template <int D>
+constexpr int kStepKeys = D == 128 ? 32 : 64;
+
+template <int D>
+struct Fetch16 {
+  static constexpr int NK = kStepKeys<D>;
+  static constexpr int NKU = NK * D / 8 / 256;         // K loads per thread
+  static constexpr int NVU = (NK / 2) * (D / 8) / 256;  // V chunks per thread (two loads each)
+  static_assert(NKU * 256 == NK * D / 8 && NVU * 256 == (NK / 2) * (D / 8) && NVU >= 1, "whole rounds");
+  uint4_t k[NKU];
+  uint4_t v0[NVU], v1[NVU];
+};
+
+template <int D>
+struct Stage16Map {
+  static constexpr int PPW = 1024 / D;  // token pairs per half-wave row of chunks
+  static __device__ __forceinline__ int k_row(int u) { return (threadIdx.x + 256 * u) / (D / 8); }
+  static __device__ __forceinline__ int k_dc(int u) { return (threadIdx.x + 256 * u) % (D / 8); }
+  static __device__ __forceinline__ int v_pair(int it) {
+    const int z = (threadIdx.x >> 6) + 4 * it, lp = threadIdx.x & 31;
+    return PPW * (z >> 1) + lp % PPW;
   }
-  // V: a chunk is a token pair x 8 columns -> V^T.  As in the FP4 staging, a
-  // half-wave's chunks sit in d-groups 32 rows apart (conflict-free writes).
-  constexpr int NC8 = D / 8, PPW = 1024 / D;
-  constexpr int NV = (BC / 2) * NC8;
-  static_assert(NV % 256 == 0, "whole rounds of 256 chunks");
-  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6, lp = l & 31;
+  static __device__ __forceinline__ int v_grp() { return ((threadIdx.x & 63) >> 5) + 2 * ((threadIdx.x & 31) / PPW); }
+  static __device__ __forceinline__ int v_c8(int it) { return 2 * v_grp() + ((((threadIdx.x >> 6) + 4 * it)) & 1); }
+};
+
+template <int D>
+__device__ __forceinline__ void fetch16(Fetch16<D>& G, rsrc_t kr16, rsrc_t vr16, int64_t key0) {
+  using M = Stage16Map<D>;
+#pragma unroll
+  for (int u = 0; u < Fetch16<D>::NKU; ++u) {
+    const uint32_t key = (uint32_t)key0 + M::k_row(u);
+    G.k[u] = buf_load16(kr16, (key * D + M::k_dc(u) * 8) * 2);
+  }
+#pragma unroll
+  for (int it = 0; it < Fetch16<D>::NVU; ++it) {
+    const uint32_t key = (uint32_t)key0 + 2 * M::v_pair(it);
+    const int c8 = M::v_c8(it);
+    G.v0[it] = buf_load16(vr16, (key * D + c8 * 8) * 2);
+    G.v1[it] = buf_load16(vr16, ((key + 1) * D + c8 * 8) * 2);
+  }
+}
+
+template <int D, int BC, typename IT>
+__device__ __forceinline__ void stage16(const Fetch16<D>& G, Smem<D, BC>& S) {
+  using M = Stage16Map<D>;
+#pragma unroll
+  for (int u = 0; u < Fetch16<D>::NKU; ++u) {
+    const uint4_t w = G.k[u];
+    half2_t a = to_half2<IT>(w[0]), b = to_half2<IT>(w[1]), c = to_half2<IT>(w[2]), d2 = to_half2<IT>(w[3]);
+    S.k[M::k_row(u) * Smem<D, BC>::KS8 + M::k_dc(u)] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+  }
   half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
   constexpr int VS2 = Smem<D, BC>::VS8 * 4;
 #pragma unroll
-  for (int it = 0; it < NV / 256; ++it) {
-    const int z = wv + 4 * it;
-    const int pr = PPW * (z >> 1) + lp % PPW;
-    const int grp = (l >> 5) + 2 * (lp / PPW);
-    const int c8 = 2 * grp + (z & 1);
-    const uint32_t key = (uint32_t)key0 + 2 * pr;
-    const uint4_t w0 = buf_load16(vr16, (key * D + c8 * 8) * 2);
-    const uint4_t w1 = buf_load16(vr16, ((key + 1) * D + c8 * 8) * 2);
-    const int pos = vpos(2 * pr);
-    half2_t* dst = v2 + 8 * c8 * VS2 + 4 * Smem<D, BC>::vpad(grp) + pos / 2;
+  for (int it = 0; it < Fetch16<D>::NVU; ++it) {
+    const int pos = vpos(2 * M::v_pair(it));
+    half2_t* dst = v2 + 8 * M::v_c8(it) * VS2 + 4 * Smem<D, BC>::vpad(M::v_grp()) + pos / 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      half2_t a = to_half2<IT>(w0[j]), b = to_half2<IT>(w1[j]);
+      half2_t a = to_half2<IT>(G.v0[it][j]), b = to_half2<IT>(G.v1[it][j]);
       dst[(2 * j) * VS2] = half2_t{a[0], b[0]};
       dst[(2 * j + 1) * VS2] = half2_t{a[1], b[1]};
     }
@@ -385,12 +418,16 @@ __device__ __forceinline__ float max16(const float16_t& a) {
 // each exponent is one fused x*c - offset.  Each lane holds 16 consecutive
 // keys of one query row per 32-key subtile, i.e. exactly one level-2 block of
 // P, so the block scale is lane-local.
-template <int D, int BC, bool FP4, bool MASK, bool SINGLE>
+//
+// NK: keys processed, the first NK of the tile's LDS layout (the FP16 path
+// runs steps of 32 or 64 keys).
+template <int D, int BC, bool FP4, bool MASK, bool SINGLE, int NK = BC>
 __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
                                           int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
+  static_assert(NK % 32 == 0 && NK <= BC, "whole 32-key subtiles of the layout");
   const int lane = threadIdx.x & 63;
   const int hi = lane >> 5;  // which 16-key half of each 32-key group this lane holds
-  constexpr int NG = BC / 32;
+  constexpr int NG = NK / 32;
   constexpr int NS = D / 16;
   float16_t acc[NG];
   float bmax[NG];
@@ -571,6 +608,79 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
 
+// One FP16-path step of ST keys at k0 (staged at the start of the tile
+// layout) for this wave's rows [wrow0, wrow0 + 32).
+template <int D, int BC, int ST>
+__device__ __forceinline__ void fp16_step(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
+                                          int64_t k0, int64_t wrow0, int64_t qrow, int64_t Sk, int causal, float c) {
+  if (causal && k0 > wrow0 + 31) return;  // every key after this wave's rows
+  const bool need_mask = (k0 + ST > Sk) || (causal && k0 + ST - 1 > wrow0);
+  if (need_mask) wave_tile<D, BC, false, true, false, ST>(S, qf, R, k0, qrow, Sk, causal, c);
+  else wave_tile<D, BC, false, false, false, ST>(S, qf, R, k0, qrow, Sk, causal, c);
+}
+
+// The selection list of a query block, read 64 entries at a time into one
+// register (lane i holds entry base + i) and looked up with readlane: the tile
+// loops make no memory access and no wait for it.  Entries past the count n
+// read as INT32_MAX (above every block index).
+struct SelList {
+  const int32_t* sel;
+  int n, cap, base, chunk;  // n: entries in use; cap: entries the list holds (reads stay below it)
+  __device__ __forceinline__ void init(const int32_t* s, int capacity) {
+    sel = s;
+    n = capacity;
+    cap = capacity;
+    base = 0;
+    chunk = fetch(0);
+  }
+  __device__ __forceinline__ int fetch(int b) const {
+    const int i = b + (int)(threadIdx.x & 63);
+    return i < cap ? sel[i] : 0x7fffffff;
+  }
+  // entry i (wave-uniform), INT32_MAX past the count
+  __device__ __forceinline__ int get(int i) {
+    if (i >= n) return 0x7fffffff;
+    if (i < base || i >= base + 64) {
+      base = i & ~63;
+      chunk = fetch(base);
+    }
+    return __builtin_amdgcn_readlane(chunk, i - base);
+  }
+};
+
+// The FP16 pass's walk over the selected blocks: steps of STEP keys in list
+// order.  An entry not above every earlier entry is skipped (negative ones
+// included); once a block starts at or past kend the walk ends, since every
+// later entry that is not skipped lies further out.
+template <int STEP>
+struct SelCursor {
+  SelList* list;
+  int halves, sel_block;  // halves: steps per block
+  int64_t kend;
+  int s_i = -1, hh = 0, prev = -1;
+  int64_t base = 0;
+  // key0 of the next step, or -1
+  __device__ __forceinline__ int64_t next() {
+    const int nsel = list->n;
+    if (s_i >= 0 && s_i < nsel) {
+      ++hh;
+      if (hh < halves && base + (int64_t)STEP * hh < kend) return base + (int64_t)STEP * hh;
+    }
+    int v = 0;
+    while (++s_i < nsel && (v = list->get(s_i)) <= prev) {
+    }
+    if (s_i >= nsel) return -1;
+    prev = v;
+    hh = 0;
+    base = (int64_t)prev * sel_block;
+    if (base >= kend) {
+      s_i = nsel;
+      return -1;
+    }
+    return base;
+  }
+};
+
 // PM: P on the FP4 tiles -- 0 two-level, 1 single-level, 2 unquantized
 // (fp16 probabilities with the FP4 operands: the high-precision output O' of
 // training, Attn-QAT page, Metodologia / A).
@@ -599,22 +709,48 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   const int64_t qrow = q0 + 32 * wave + (lane & 31);
   const int64_t Sk = P.Sk;
 
-  if (threadIdx.x < 128) S.pt[threadIdx.x] = PM == 1 ? kPScale1.v[threadIdx.x] : kPScale.v[threadIdx.x];
+  // selection of this query block (sel_block is a multiple of kBr); its list
+  // and count load while the Q fragment below does
+  const int32_t* sel = nullptr;
+  int nsel = 0;
+  SelList list;
+  if (P.pct > 0) {
+    const int64_t qb = q0 / P.sel_block;
+    sel = P.idx + (bh * P.nqb + qb) * P.kmax;
+    nsel = P.cnt[bh * P.nqb + qb];
+    list.init(sel, P.kmax);
+    nsel = nsel < 0 ? 0 : (nsel > P.kmax ? P.kmax : nsel);  // a given count never reaches the padding
+  } else {
+    list.init(nullptr, 0);
+  }
+  list.n = nsel;
+  const float4_t ptv = PM == 1 ? kPScale1.v[threadIdx.x & 127] : kPScale.v[threadIdx.x & 127];
   // Q^ fragment (B operand): query qrow, d = 16 s + 8 hi .. +8
   half8_t qf[D / 16];
   {
+    // rows past Sq read row 0 (every load in bounds and in flight together)
+    // and are zeroed
     const bool ok = qrow < P.Sq;
     const uint8_t* qcr = P.qc + (bh * P.Sq + (ok ? qrow : 0)) * (D / 2);
     const uint8_t* qsr = P.qs + (bh * P.Sq + (ok ? qrow : 0)) * (D / 16);
+    uint32_t cws[D / 16];
+    uint8_t scs[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const uint32_t cw = ok ? *reinterpret_cast<const uint32_t*>(qcr + 8 * s + 4 * hi) : 0u;
-      const half_t sc = (half_t)e4m3_to_f32(ok ? qsr[s] : 0u);
+      cws[s] = *reinterpret_cast<const uint32_t*>(qcr + 8 * s + 4 * hi);
+      scs[s] = qsr[s];
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t cw = ok ? cws[s] : 0u;
+      const half_t sc = (half_t)e4m3_to_f32(ok ? scs[s] : 0u);
       half2_t a = scale_pair(cvt_pk_f16_fp4<0>(cw), sc), bb = scale_pair(cvt_pk_f16_fp4<1>(cw), sc);
       half2_t cc = scale_pair(cvt_pk_f16_fp4<2>(cw), sc), dd = scale_pair(cvt_pk_f16_fp4<3>(cw), sc);
       qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
     }
   }
+  // level-2 P scale table (read after the first barrier of the tile loop)
+  if (threadIdx.x < 128) S.pt[threadIdx.x] = ptv;
   RowState<D> R;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) R.o[t] = float16_t{0};
@@ -625,15 +761,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   int64_t kend = Sk;
   if (P.causal && qend < kend) kend = qend;
   const int ntile = (int)((kend + BC - 1) / BC);
-  // selection of this query block (sel_block is a multiple of kBr)
-  const int32_t* sel = nullptr;
-  int nsel = 0;
-  if (P.pct > 0) {
-    const int64_t qb = q0 / P.sel_block;
-    sel = P.idx + (bh * P.nqb + qb) * P.kmax;
-    nsel = P.cnt[bh * P.nqb + qb];
-    nsel = nsel < 0 ? 0 : (nsel > P.kmax ? P.kmax : nsel);  // a given count never reaches the padding
-  }
   const int tiles_per_block = P.sel_block / BC;
 
   const int64_t bhk = b * P.Hkv + hk;
@@ -649,12 +776,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   // pass below takes exactly these entries, so a given list that is unsorted
   // or repeats an index never counts a key twice or skips it.
   Fetch<D, BC> F;
-  int si = 0;  // cursor into the selection list
+  int si = 0, sv = list.get(0);  // cursor into the selection list and its entry
   auto selected = [&](int tile) {
     if (nsel == 0) return false;
     const int blk = tile / tiles_per_block;
-    while (si < nsel && sel[si] < blk) ++si;
-    return si < nsel && sel[si] == blk;
+    while (sv < blk) sv = list.get(++si);
+    return sv == blk;
   };
   int cur = 0;
   while (cur < ntile && selected(cur)) ++cur;
@@ -690,34 +817,34 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     // fp16 Q fragment from the original input
     const IT* qp = reinterpret_cast<const IT*>(P.q) + bh * P.Sq * D;
     const bool ok = qrow < P.Sq;
+    uint4_t qw[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qw[s] = *reinterpret_cast<const uint4_t*>(qp + (ok ? qrow : 0) * D + 16 * s + 8 * hi);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      uint4_t w = ok ? *reinterpret_cast<const uint4_t*>(qp + qrow * D + 16 * s + 8 * hi) : uint4_t{0, 0, 0, 0};
+      uint4_t w = ok ? qw[s] : uint4_t{0, 0, 0, 0};
       half2_t a = to_half2<IT>(w[0]), bb = to_half2<IT>(w[1]), cc = to_half2<IT>(w[2]), dd = to_half2<IT>(w[3]);
       qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
     }
     const rsrc_t kr16 = make_rsrc(reinterpret_cast<const IT*>(P.k) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
     const rsrc_t vr16 = make_rsrc(reinterpret_cast<const IT*>(P.v) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
-    int prev = -1;  // entries not above every earlier entry are skipped (negative ones included)
-    for (int s_i = 0; s_i < nsel; ++s_i) {
-      const int blk = sel[s_i];
-      if (blk <= prev) continue;
-      prev = blk;
-      for (int tt = 0; tt < tiles_per_block; ++tt) {
-        const int tile = blk * tiles_per_block + tt;
-        if (tile >= ntile) break;
-        const int64_t key0 = (int64_t)tile * BC;
-        __syncthreads();
-        stage_fp16<D, BC, IT>(S, kr16, vr16, key0);
-        __syncthreads();
-        const int64_t wrow0 = q0 + 32 * wave;
-        const bool wave_dead = P.causal && key0 > wrow0 + 31;
-        if (!wave_dead) {
-          const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
-          if (need_mask) wave_tile<D, BC, false, true, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-          else wave_tile<D, BC, false, false, false>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-        }
-      }
+    // steps of the selected blocks in list order, each fetched into
+    // registers while the step before it computes
+    constexpr int ST = kStepKeys<D>;
+    SelCursor<ST> cur{&list, P.sel_block / ST, P.sel_block, kend};
+    const int64_t wrow0 = q0 + 32 * wave;
+    Fetch16<D> G;
+    int64_t key0 = cur.next();
+    if (key0 >= 0) fetch16<D>(G, kr16, vr16, key0);
+    while (key0 >= 0) {
+      const int64_t nxt = cur.next();
+      __syncthreads();  // previous step's LDS reads are done
+      stage16<D, BC, IT>(G, S);
+      if (nxt >= 0) fetch16<D>(G, kr16, vr16, nxt);
+      __syncthreads();
+      fp16_step<D, BC, ST>(S, qf, R, key0, wrow0, qrow, Sk, P.causal, P.c);
+      key0 = nxt;
     }
   }
 

@@ -89,8 +89,11 @@ __global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
 // Q and K means staged through LDS 32 channels at a time, every score summed
 // over ascending channels (binary64 products and sums, no fused multiply-add),
 // written as an order-preserving 64-bit key.  A tile wholly above the causal
-// diagonal does nothing; its keys are never read.
+// diagonal does nothing; its keys are never read.  (Measured on a causal 32K
+// prefill: 64 x 64, 32 x 64 and 64 x 32 tiles take 34-36 us; 32 x 32 tiles,
+// at one LDS read per multiply-add, 42 us.)
 constexpr int kScTQ = 64, kScTK = 64, kScTC = 32;
+constexpr int kScR = kScTQ / 16, kScC = kScTK / 16;  // scores per thread: kScR x kScC
 
 // Scores as unsigned keys that order like the doubles (-0 folded into +0).
 __device__ __forceinline__ uint64_t score_key(double s) {
@@ -128,11 +131,11 @@ __global__ void __launch_bounds__(256) block_scores_kernel(const double* qm, con
       rk[u] = j0 + r < nkb ? kb[(int64_t)(j0 + r) * d + c0 + cc] : 0.0;
     }
   };
-  double acc[4][4];  // rows ty + 16 r, columns tx + 16 c
+  double acc[kScR][kScC];  // rows ty + 16 r, columns tx + 16 c
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < kScR; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+    for (int c = 0; c < kScC; ++c) acc[r][c] = 0.0;
   fetch(0);
   for (int c0 = 0; c0 < d; c0 += kScTC) {
     __syncthreads();  // the previous chunk's reads are done
@@ -148,23 +151,23 @@ __global__ void __launch_bounds__(256) block_scores_kernel(const double* qm, con
     }
     __syncthreads();
     if (c0 + kScTC < d) fetch(c0 + kScTC);
-#pragma unroll 4
+#pragma unroll 8
     for (int cc = 0; cc < kScTC; ++cc) {
-      double a[4], bv[4];
+      double a[kScR], bv[kScC];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = sq[ty + 16 * r][cc];
+      for (int r = 0; r < kScR; ++r) a[r] = sq[ty + 16 * r][cc];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = sk[tx + 16 * c][cc];
+      for (int c = 0; c < kScC; ++c) bv[c] = sk[tx + 16 * c][cc];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < kScR; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = __dadd_rn(acc[r][c], __dmul_rn(a[r], bv[c]));
+        for (int c = 0; c < kScC; ++c) acc[r][c] = __dadd_rn(acc[r][c], __dmul_rn(a[r], bv[c]));
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < kScR; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kScC; ++c) {
       const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
       if (i < nqb && j < nkb && (!causal || j <= i)) keys[(bh * nqb + i) * nkb + j] = score_key(acc[r][c]);
     }
@@ -381,9 +384,49 @@ __global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
 
 // Prefill selection, one wave per (batch, head, query block) row, no
 // workgroup barrier: a radix select over 8-bit digits of the row's visible
-// keys (from block_scores_kernel, read from memory each pass) with a per-wave
-// histogram in LDS, then the kept indices in ascending order (the k largest,
-// ties to the lower index), -1 padding and the count.
+// keys (from block_scores_kernel) with a per-wave histogram in LDS, stopping
+// at the first digit whose threshold bin is kept whole, then the kept indices
+// in ascending order (the k largest, ties to the lower index), -1 padding and
+// the count.  Rows of at most kSelRegKeys visible blocks are
+// read once into registers (four keys per lane); longer rows are read from
+// memory in every pass.
+constexpr int kSelRegKeys = 256;
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
+// 16-lane row, then row 0's total into row 1 and row 2's into row 3, then
+// the total of rows 0-1 into rows 2-3 (lanes whose source is out of range add
+// zero).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// One 64-key chunk of the final emission: keys whose bits from `shift` up
+// exceed the threshold's, and ties there while fewer than rem have been
+// kept (the lower indices first).
+__device__ __forceinline__ void select_emit(uint64_t u, bool in, int j, int k, int nvis, uint64_t prefix, int shift,
+                                            int rem, int lane, int& run_tie, int& run_sel, int32_t* out) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool sel;
+  if (k >= nvis) {
+    sel = in;
+  } else {
+    const uint64_t uh = u >> shift, ph = prefix >> shift;
+    const bool tie = k > 0 && in && uh == ph;
+    const unsigned long long bt = __ballot(tie);
+    sel = k > 0 && in && (uh > ph || (tie && run_tie + __popcll(bt & below) < rem));
+    run_tie += __popcll(bt);
+  }
+  const unsigned long long bs = __ballot(sel);
+  if (sel) out[run_sel + __popcll(bs & below)] = j;
+  run_sel += __popcll(bs);
+}
+
 __global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys, int64_t nrows, int nqb, int nkb,
                                                            int causal, int pct, int kmax, int32_t* idx,
                                                            int32_t* cnt) {
@@ -395,9 +438,17 @@ __global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys,
   const int nvis = causal ? (i + 1 < nkb ? i + 1 : nkb) : nkb;
   const int k = (pct * nvis + 99) / 100;
   const uint64_t* row = keys + g * nkb;
+  const bool inreg = nvis <= kSelRegKeys;
+  constexpr int NR = kSelRegKeys / 64;
+  uint64_t kv[NR];
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    const int j = lane + 64 * q;
+    kv[q] = inreg && j < nvis ? row[j] : 0ull;
+  }
   int* hw = hist[wave];
   uint64_t prefix = 0;
-  int rem = k;
+  int rem = k, fshift = 0;  // the threshold is decided on the key bits from fshift up
   if (k > 0 && k < nvis) {
     for (int shift = 56; shift >= 0; shift -= 8) {
 #pragma unroll
@@ -406,9 +457,17 @@ __global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const uint64_t hi = shift == 56 ? 0ull : (~0ull << (shift + 8));
-      for (int j = lane; j < nvis; j += 64) {
-        const uint64_t u = row[j];
-        if ((u & hi) == prefix) atomicAdd(&hw[(int)((u >> shift) & 255u)], 1);
+      if (inreg) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          const uint64_t u = kv[q];
+          if (lane + 64 * q < nvis && (u & hi) == prefix) atomicAdd(&hw[(int)((u >> shift) & 255u)], 1);
+        }
+      } else {
+        for (int j = lane; j < nvis; j += 64) {
+          const uint64_t u = row[j];
+          if ((u & hi) == prefix) atomicAdd(&hw[(int)((u >> shift) & 255u)], 1);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
@@ -420,14 +479,9 @@ __global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys,
         c4[q] = hw[255 - 4 * lane - q];
         own += c4[q];
       }
-      int incl = own;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
+      const int incl = wave_incl_scan(own);
       const int excl = incl - own;
-      int found = -1, above = 0;
+      int found = -1, above = 0, fcnt = 0;
       if (excl < rem && incl >= rem) {
         int acc = excl;
 #pragma unroll
@@ -435,39 +489,38 @@ __global__ void __launch_bounds__(256) block_select_kernel(const uint64_t* keys,
           if (found < 0 && acc + c4[q] >= rem) {
             found = 255 - 4 * lane - q;
             above = acc;
+            fcnt = c4[q];
           }
           acc += c4[q];
         }
       }
       const unsigned long long who = __ballot(found >= 0);
       const int src = (int)__builtin_ctzll(who);
-      prefix |= (uint64_t)__shfl(found, src, 64) << shift;
-      rem -= __shfl(above, src, 64);
+      prefix |= (uint64_t)__builtin_amdgcn_readlane(found, src) << shift;
+      rem -= __builtin_amdgcn_readlane(above, src);
+      fshift = shift;
       // the next pass clears this histogram: all reads of it are done first
       __builtin_amdgcn_wave_barrier();
+      // every key of the threshold's bin is kept: no lower digit can matter
+      if (__builtin_amdgcn_readlane(fcnt, src) == rem) break;
     }
   }
   // kept: every visible block when k >= nvis; else keys above the threshold
   // and the first rem ties
   int32_t* out = idx + g * kmax;
-  const uint64_t below = (1ull << lane) - 1ull;
   int run_tie = 0, run_sel = 0;
-  for (int base = 0; base < nvis; base += 64) {
-    const int j = base + lane;
-    const bool in = j < nvis;
-    const uint64_t u = in ? row[j] : 0ull;
-    bool sel;
-    if (k >= nvis) {
-      sel = in;
-    } else {
-      const bool tie = k > 0 && in && u == prefix;
-      const unsigned long long bt = __ballot(tie);
-      sel = k > 0 && in && (u > prefix || (tie && run_tie + __popcll(bt & below) < rem));
-      run_tie += __popcll(bt);
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int j = 64 * q + lane;
+      select_emit(kv[q], j < nvis, j, k, nvis, prefix, fshift, rem, lane, run_tie, run_sel, out);
     }
-    const unsigned long long bs = __ballot(sel);
-    if (sel) out[run_sel + __popcll(bs & below)] = j;
-    run_sel += __popcll(bs);
+  } else {
+    for (int base = 0; base < nvis; base += 64) {
+      const int j = base + lane;
+      const bool in = j < nvis;
+      select_emit(in ? row[j] : 0ull, in, j, k, nvis, prefix, fshift, rem, lane, run_tie, run_sel, out);
+    }
   }
   for (int p = k + lane; p < kmax; p += 64) out[p] = -1;
   if (lane == 0) cnt[g] = k;
