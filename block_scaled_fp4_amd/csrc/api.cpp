@@ -287,8 +287,9 @@ size_t fp4_block_topk_workspace_size(const fp4_attn_problem* prob, const fp4_att
 }
 
 static int launch_selection(const fp4_attn_problem* p, const fp4_attn_opts* o, const AttnPlan& P, char* ws_sel,
-                            int32_t* idx, int32_t* cnt, hipStream_t s) {
+                            int32_t* idx, int32_t* cnt, hipStream_t s, bool means_ready = false) {
   TopkLaunch T;
+  T.means_ready = means_ready ? 1 : 0;
   T.q = p->q;
   T.k = p->k;
   T.dtype = p->dtype;
@@ -390,17 +391,31 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
       L.exp_negate = 1;
       L.exp_rows = (H / Hkv) * Sq;  // the query heads of a kv head are consecutive
     }
+    // with the selection computed here, the Q and K launches also write the
+    // selection's block means (from the unrotated, unbalanced input)
+    if (P.need_sel) {
+      L.means = (double*)(ws + P.qm);
+      L.mS = Sq;
+      L.mblk = opts->sel_block;
+      L.mnb = P.nqb;
+    }
     if (e == hipSuccess) e = fp4i_launch_quantize(L, s);
     if (e == hipSuccess) {
       L.x = prob->k; L.rows = B * Hkv * Sk;
       L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
       L.exp_negate = 0;
       L.exp_rows = Sk;
+      if (P.need_sel) {
+        L.means = (double*)(ws + P.km);
+        L.mS = Sk;
+        L.mnb = P.nkb;
+      }
       e = fp4i_launch_quantize(L, s);
     }
     if (e == hipSuccess) {
       L.x = prob->v; L.axis = 1; L.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
       L.cexp = nullptr;
+      L.means = nullptr;
       L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
       e = fp4i_launch_quantize(L, s);
     }
@@ -417,7 +432,7 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
     idx = topk_idx;
     cnt = topk_cnt;
   } else if (P.need_sel) {
-    const int st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s);
+    const int st = launch_selection(prob, opts, P, ws + P.qm, topk_idx, topk_cnt, s, P.need_quant);
     if (st) return st;
     idx = topk_idx ? topk_idx : (const int32_t*)(ws + P.idx);
     cnt = topk_cnt ? topk_cnt : (const int32_t*)(ws + P.cnt);

@@ -20,6 +20,12 @@ struct QuantLaunch {
   const int32_t* cexp;     // balance exponents [rows / exp_rows][cols], or null (axis 0)
   int exp_negate;          // 1: multiply by 2^-e (Q side)
   int64_t exp_rows;        // rows sharing one exponent vector
+  // block means of the input, written in the same launch (axis 0, bf16/fp16,
+  // cols <= 128, gmode 0): rows are heads of mS rows cut into mnb blocks of
+  // mblk; means [rows / mS][mnb][cols] in binary64.  Null: none.
+  double* means = nullptr;
+  int64_t mS = 0;
+  int mblk = 0, mnb = 0;
 };
 
 // Balance exponents: per (batch, kv head) binary64 partial sums of squares of
@@ -64,6 +70,7 @@ struct TopkLaunch {
   int nqb, nkb, kmax;
   double* qmeans;  // [B*H, nqb, d]
   double* kmeans;  // [B*Hkv, nkb, d]
+  int means_ready = 0;  // 1: the quantizer already wrote both
   uint64_t* keys;  // [B*H, nqb, nkb] order-preserving keys of the block scores
   int32_t* idx;    // [B*H, nqb, kmax]
   int32_t* cnt;    // [B*H, nqb]

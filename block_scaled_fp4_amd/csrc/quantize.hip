@@ -42,6 +42,9 @@ struct QuantArgs {
   const int32_t* cexp;  // balance exponents [rows / exp_rows][cols] (BAL instances)
   int exp_negate;
   int64_t exp_rows;
+  double* means;  // block means of the input (quantize_means_kernel): [rows / mS][mnb][cols]
+  int64_t mS;     // rows per head
+  int mblk, mnb;  // rows per selection block, blocks per head
 };
 
 // Magnitude balance of one block (ScaleSearch page, Metodologia /
@@ -202,6 +205,78 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
     A.scales[blk] = (uint8_t)scale;
     if (A.offsets) A.offsets[blk] = (int8_t)off;
   }
+}
+
+// Axis-0 quantization fused with the block means of the FP16 path's block
+// selection (ThriftAttention page, Metodologia / 1): one workgroup per
+// (head, selection block) unit.  The unit's rows are quantized kMeansRows at a
+// time exactly as quantize_axis0_kernel does (whole rows per lane group, so
+// the Hadamard butterflies find their partners), and the raw input rows are
+// kept in LDS, where one thread per channel adds them in binary64 over
+// ascending tokens and divides by the token count: the order and arithmetic
+// of block_means_kernel, so the selection is unchanged, without a second pass
+// over Q and K.
+constexpr int kMeansRows = 128;
+
+template <typename T, bool HAD, bool BAL>
+__global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
+  __shared__ float2_t tab[128];
+  __shared__ __align__(16) T raw_rows[kMeansRows * 128];  // [row][channel], cols <= 128
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const int64_t bpr = A.cols / 16;
+  const int64_t u = blockIdx.x, head = u / A.mnb, ib = u - head * A.mnb;
+  const int64_t t0 = ib * A.mblk;
+  const int64_t n = (t0 + A.mblk < A.mS ? t0 + A.mblk : A.mS) - t0;
+  const int64_t row0 = head * A.mS + t0;
+  const T* x = reinterpret_cast<const T*>(A.x);
+  const int c = threadIdx.x;
+  double sum = 0.0;
+  constexpr int kMaxPer = kMeansRows * 8 / 256;  // blocks per thread and chunk at cols = 128
+  for (int64_t r0 = 0; r0 < n; r0 += kMeansRows) {
+    const int64_t nr = n - r0 < kMeansRows ? n - r0 : kMeansRows;
+    const int64_t nblk = nr * bpr;
+    RawBlock<T> raw[kMaxPer];
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int64_t i = threadIdx.x + 256 * j;
+      if (i < nblk) load_raw<T>(raw[j], x + (row0 + r0 + i / bpr) * A.ld + (i % bpr) * 16);
+    }
+    __syncthreads();  // the previous chunk's sums have read the rows; the table is in place
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int64_t i = threadIdx.x + 256 * j;
+      if (i < nblk) {
+        const int64_t rl = i / bpr, cb = i % bpr;
+        uint4_t* dst = reinterpret_cast<uint4_t*>(raw_rows + rl * A.cols + cb * 16);
+#pragma unroll
+        for (int w = 0; w < RawBlock<T>::N; ++w) dst[w] = raw[j].w[w];
+        float y[16];
+        raw_to_f32<T>(raw[j], y);
+        const int64_t r = row0 + r0 + rl, blk = r * bpr + cb;
+        if (BAL) balance_block(y, A, r, cb);
+        if (HAD) hadamard_block(y, A, cb, (int)bpr);
+        uint32_t codes[2], scale;
+        int off;
+        quantize_block(y, A.search, A.fmin, A.fmax, tab, codes, scale, off);
+        A.codes[blk] = uint2_t{codes[0], codes[1]};
+        A.scales[blk] = (uint8_t)scale;
+        if (A.offsets) A.offsets[blk] = (int8_t)off;
+      }
+    }
+    __syncthreads();
+    if (c < A.cols) {
+      int64_t t = 0;
+      for (; t + 8 <= nr; t += 8) {
+        double v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (double)load_elem<T>(raw_rows + (t + e) * A.cols + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum = sum + v[e];
+      }
+      for (; t < nr; ++t) sum = sum + (double)load_elem<T>(raw_rows + t * A.cols + c);
+    }
+  }
+  if (c < A.cols) A.means[u * A.cols + c] = sum / (double)n;
 }
 
 // block_axis 1: one lane per block of 16 rows of one column; consecutive
@@ -521,6 +596,26 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   A.cexp = L.cexp;
   A.exp_negate = L.exp_negate;
   A.exp_rows = L.exp_rows > 0 ? L.exp_rows : 1;
+  A.means = L.means;
+  A.mS = L.mS;
+  A.mblk = L.mblk;
+  A.mnb = L.mnb;
+  if (L.means) {  // axis 0, bf16/fp16, cols <= 128, no per-tensor scale (checked by the caller)
+    const bool had = L.hadamard != 0, bal = L.cexp != nullptr;
+    const dim3 g((unsigned)((L.rows / L.mS) * L.mnb));
+    if (L.dtype == 0) {
+      if (had && bal) hipLaunchKernelGGL((quantize_means_kernel<uint16_t, true, true>), g, dim3(256), 0, stream, A);
+      else if (had) hipLaunchKernelGGL((quantize_means_kernel<uint16_t, true, false>), g, dim3(256), 0, stream, A);
+      else if (bal) hipLaunchKernelGGL((quantize_means_kernel<uint16_t, false, true>), g, dim3(256), 0, stream, A);
+      else hipLaunchKernelGGL((quantize_means_kernel<uint16_t, false, false>), g, dim3(256), 0, stream, A);
+    } else {
+      if (had && bal) hipLaunchKernelGGL((quantize_means_kernel<half_t, true, true>), g, dim3(256), 0, stream, A);
+      else if (had) hipLaunchKernelGGL((quantize_means_kernel<half_t, true, false>), g, dim3(256), 0, stream, A);
+      else if (bal) hipLaunchKernelGGL((quantize_means_kernel<half_t, false, true>), g, dim3(256), 0, stream, A);
+      else hipLaunchKernelGGL((quantize_means_kernel<half_t, false, false>), g, dim3(256), 0, stream, A);
+    }
+    return hipGetLastError();
+  }
   if (L.axis == 0) {
     const bool had = L.hadamard != 0, bal = L.cexp != nullptr;
     if (had && bal) launch_axis0<true, true>(L.dtype, grid, A, stream);

@@ -583,8 +583,10 @@ hipError_t launch_means(const TopkLaunch& L, hipStream_t stream) {
 hipError_t fp4i_launch_topk(const TopkLaunch& L, hipStream_t stream) {
   const int d = (int)L.d;
   const int64_t gq = L.B * L.H * L.nqb;
-  const hipError_t e = L.dtype == 0 ? launch_means<uint16_t>(L, stream) : launch_means<half_t>(L, stream);
-  if (e != hipSuccess) return e;
+  if (!L.means_ready) {
+    const hipError_t e = L.dtype == 0 ? launch_means<uint16_t>(L, stream) : launch_means<half_t>(L, stream);
+    if (e != hipSuccess) return e;
+  }
   const int ntq = (L.nqb + kScTQ - 1) / kScTQ, ntk = (L.nkb + kScTK - 1) / kScTK;
   hipLaunchKernelGGL(block_scores_kernel, dim3((unsigned)(L.B * L.H * ntq * ntk)), dim3(256), 0, stream, L.qmeans,
                      L.kmeans, L.H, L.Hkv, L.nqb, L.nkb, d, L.causal, ntq, ntk, L.keys);

@@ -49,3 +49,39 @@ def test_selective_workload_full_size(gpu):
     np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
     np.testing.assert_array_equal(idx.cpu().numpy(), ri)
     assert int(rc.sum()) == 32 * 3406  # sum over query blocks of ceil(10 * (i+1) / 100)
+
+
+@pytest.mark.parametrize("dtype,d,sel_block,causal,hadamard,balance", [
+    (torch.bfloat16, 128, 128, True, False, False),
+    (torch.float16, 64, 256, False, False, False),
+    (torch.bfloat16, 128, 256, True, True, False),
+    (torch.float16, 128, 128, False, False, True),
+])
+def test_forward_selection_bit_exact(gpu, dtype, d, sel_block, causal, hadamard, balance):
+    """The selection the forward computes itself (its Q and K quantization
+    launches also write the block means, from the input before any rotation or
+    balance) equals the oracle's: ragged last blocks, GQA, selection blocks of
+    one and of two 128-row chunks."""
+    S = 1040 if causal else 1008
+    q, k, v = synth.qkv(2, 4, S, d, dtype, seed=5, Hkv=2, k_outliers=2)
+    case(f"forward selection {dtype} d={d} sel_block={sel_block} causal={causal} had={hadamard} bal={balance}")
+    _, _, idx, cnt = gpu.fp4_attention_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, fp16_budget_pct=10,
+                                           sel_block=sel_block, return_topk=True, hadamard=hadamard,
+                                           balance=balance)
+    torch.cuda.synchronize()
+    ri, rc = _oracle_topk(q, k, causal, 10, sel_block)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+
+
+def test_forward_selection_full_size(gpu):
+    """The 32K selective workload: the selection inside fp4_attention_fwd equals
+    the oracle's, bit for bit."""
+    q, k, v = synth.prefill(S=32768)
+    case("forward selection full 32K")
+    _, _, idx, cnt = gpu.fp4_attention_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, fp16_budget_pct=10,
+                                           return_topk=True, return_lse=False)
+    torch.cuda.synchronize()
+    ri, rc = _oracle_topk(q, k, True, 10, 128)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
