@@ -11,7 +11,10 @@
 // n_recent tokens of T, and mid_len[b] grows by n_new.  A batch whose NVFP4
 // region has no room is left unchanged and flagged.
 //
-// Two launches, so that nothing is overwritten while it may still be read:
+// When T of one operand and 64 channels fits in LDS (the usual case: a
+// window of a few hundred tokens), kv_append_fast_kernel does it all in one
+// pass and kv_append_finish_kernel updates mid_len and the flags.  Otherwise,
+// two launches, so that nothing is overwritten while it may still be read:
 //   1. kv_append_quant_kernel: one workgroup per (batch, kv head, 16-token
 //      group): one lane per 16-element block (K: 16 tokens x d/16 blocks; V: d
 //      channel blocks), the same block quantizer as fp4_quantize; the same
@@ -195,6 +198,120 @@ __global__ void __launch_bounds__(256) kv_append_commit_kernel(AppendArgs A) {
   }
 }
 
+// ---- one-pass append: the sequence T of one (batch, kv head), one operand
+// (K or V) and 64 channels fits in LDS (kFastLds bytes), so a workgroup reads
+// T once, quantizes its first n_new tokens from LDS and writes the new window
+// back over the old one in place (nothing else reads that window), with no
+// workspace round trip.  mid_len is read, never written, here; a second
+// launch of one thread per batch then updates it and the flags, so every
+// workgroup decides on the same value.
+constexpr int kFastCh = 64;              // channels per workgroup
+constexpr int kFastLds = 62 * 1024;      // bytes of T staged per workgroup (496 tokens)
+constexpr int kFastTok = kFastLds / (kFastCh * 2);
+
+// grid: B*Hkv*2*(d/64): (bk, operand, channel half); block 256.
+__global__ void __launch_bounds__(256) kv_append_fast_kernel(AppendArgs A) {
+  __shared__ float2_t tab[128];
+  __shared__ __align__(16) uint16_t Tl[kFastTok * kFastCh];  // [token][channel of this half]
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const int nh = (int)(A.d / kFastCh);
+  const int64_t gi = blockIdx.x;
+  const int half = (int)(gi % nh);
+  const bool isv = (gi / nh) % 2 == 1;
+  const int64_t bk = gi / (2 * nh), b = bk / A.Hkv;
+  const int64_t mid = used_mid(A, b);
+  if (mid + A.n_new > A.mid_cap) return;  // no room: the batch stays as it is
+  const int d = (int)A.d, c0 = half * kFastCh;
+  const int nt = A.n_recent + A.n_new;
+  const uint16_t* recent = isv ? A.v_recent : A.k_recent;
+  const uint16_t* fresh = isv ? A.v_new : A.k_new;
+  // T into LDS: 8 channels (16 bytes) per step
+  for (int i = threadIdx.x; i < nt * (kFastCh / 8); i += 256) {
+    const int t = i / (kFastCh / 8), c8 = (i % (kFastCh / 8)) * 8;
+    *reinterpret_cast<uint4_t*>(Tl + t * kFastCh + c8) =
+        *reinterpret_cast<const uint4_t*>(seq_row(recent, fresh, A, bk, t) + c0 + c8);
+  }
+  __syncthreads();
+  // the first n_new tokens of T into the NVFP4 region at mid
+  if (!isv) {
+    // K: token t, channels 16 cb .. +16 of this half
+    for (int i = threadIdx.x; i < A.n_new * (kFastCh / 16); i += 256) {
+      const int t = i / (kFastCh / 16), cb = i % (kFastCh / 16);
+      float y[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[e] = bf16_to_f32(Tl[t * kFastCh + 16 * cb + e]);
+      uint32_t codes[2], scale;
+      int off;
+      quantize_block(y, 1, -2, 6, tab, codes, scale, off);
+      const int64_t row = bk * A.mid_cap + mid + t;
+      const int gcb = c0 / 16 + cb;
+      *reinterpret_cast<uint2_t*>(A.kc + row * (d / 2) + 8 * gcb) = uint2_t{codes[0], codes[1]};
+      A.ks[row * (d / 16) + gcb] = (uint8_t)scale;
+      if (A.k_mid) {
+        const uint4_t* s4 = reinterpret_cast<const uint4_t*>(Tl + t * kFastCh + 16 * cb);
+        uint4_t* d4 = reinterpret_cast<uint4_t*>(A.k_mid + row * d + c0 + 16 * cb);
+        d4[0] = s4[0];
+        d4[1] = s4[1];
+      }
+    }
+  } else {
+    // V: channel c of a group of 16 tokens
+    for (int i = threadIdx.x; i < (A.n_new / 16) * kFastCh; i += 256) {
+      const int g = i / kFastCh, c = i % kFastCh;
+      float y[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) y[k] = bf16_to_f32(Tl[(16 * g + k) * kFastCh + c]);
+      uint32_t codes[2], scale;
+      int off;
+      quantize_block(y, 1, -2, 6, tab, codes, scale, off);
+      const int64_t tok = mid + 16 * g;
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        A.vc[(bk * (A.mid_cap / 2) + tok / 2 + p) * d + c0 + c] = (uint8_t)((codes[p >> 2] >> (8 * (p & 3))) & 0xFFu);
+      A.vs[(bk * (A.mid_cap / 16) + tok / 16) * d + c0 + c] = (uint8_t)scale;
+      if (A.v_mid) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) A.v_mid[(bk * A.mid_cap + tok + k) * d + c0 + c] = Tl[(16 * g + k) * kFastCh + c];
+      }
+    }
+  }
+  // the new window: T[n_new + j], j < n_recent, over the old one
+  uint16_t* win = isv ? A.v_recent : A.k_recent;
+  for (int i = threadIdx.x; i < A.n_recent * (kFastCh / 8); i += 256) {
+    const int j = i / (kFastCh / 8), c8 = (i % (kFastCh / 8)) * 8;
+    *reinterpret_cast<uint4_t*>(win + (bk * A.n_recent + j) * d + c0 + c8) =
+        *reinterpret_cast<const uint4_t*>(Tl + (A.n_new + j) * kFastCh + c8);
+  }
+  // key-block sums of the moved tokens (K side with the full-precision copy):
+  // channel c in token order, a block's sum restarting at its first token
+  if (!isv && A.k_mid && threadIdx.x < kFastCh) {
+    const int c = threadIdx.x;
+    double* sums = A.k_sum + bk * (int64_t)A.nbc * d + c0 + c;
+    int64_t j = mid / kDecSelBlock;
+    double acc = mid % kDecSelBlock == 0 ? 0.0 : sums[j * d];
+    for (int t = 0; t < A.n_new; ++t) {
+      if (t > 0 && (mid + t) % kDecSelBlock == 0) {
+        sums[j * d] = acc;
+        ++j;
+        acc = 0.0;
+      }
+      acc = __dadd_rn(acc, (double)bf16_to_f32(Tl[t * kFastCh + c]));
+    }
+    sums[j * d] = acc;
+  }
+}
+
+// grid: ceil(B/256); one thread per batch: mid_len and the flag, decided on
+// the mid_len the fast kernel read (it does not write it).
+__global__ void __launch_bounds__(256) kv_append_finish_kernel(AppendArgs A, int64_t B) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int64_t mid = used_mid(A, b);
+  const bool room = mid + A.n_new <= A.mid_cap;
+  if (room) A.mid_len[b] = (int32_t)(mid + A.n_new);
+  if (A.overflow) A.overflow[b] = room ? 0 : 1;
+}
+
 // grid: B*Hkv*nbc; block: d lanes, one channel each.  Block j's sum over its
 // tokens below mid_len, ascending (0 for a block with none).
 __global__ void __launch_bounds__(128) kv_block_sums_kernel(const uint16_t* k_mid, const int32_t* mid_len,
@@ -272,6 +389,12 @@ hipError_t fp4i_launch_kv_append(const KvAppendLaunch& L, hipStream_t st) {
   A.k_sum = L.k_sum;
   A.nbc = (int)((L.mid_cap + kDecSelBlock - 1) / kDecSelBlock);
   A.nsum = L.k_mid ? 1 : 0;
+  if (L.n_recent + L.n_new <= kFastTok && L.d % kFastCh == 0) {
+    const int nh = (int)(L.d / kFastCh);
+    hipLaunchKernelGGL(kv_append_fast_kernel, dim3((unsigned)(L.B * L.Hkv * 2 * nh)), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(kv_append_finish_kernel, dim3((unsigned)((L.B + 255) / 256)), dim3(256), 0, st, A, L.B);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kv_append_quant_kernel, dim3((unsigned)(L.B * L.Hkv * (A.ngroups + A.ncopy + A.nsum))), dim3(256),
                      0, st, A);
   const int nc = A.ncopy > 0 ? A.ncopy : 1;

@@ -30,10 +30,16 @@ def _cache(fp4, B, H, d, n_sink, n_recent, cap, seed, mid):
     return host, dev
 
 
-@pytest.mark.parametrize("d,n_recent,n_new", [(64, 48, 16), (128, 32, 32), (128, 0, 16), (128, 16, 48)])
+@pytest.mark.parametrize("d,n_recent,n_new", [(64, 48, 16), (128, 32, 32), (128, 0, 16), (128, 16, 48),
+                                              (128, 480, 16), (64, 496, 16), (128, 256, 256)])
 def test_append_bit_exact(gpu, d, n_recent, n_new):
-    B, H, cap = 3, 2, 96
-    mid = [16, 96 - n_new, 90]  # room, exactly full after, no room (90 -> 80; 80 + n_new > 96 for n_new >= 32)
+    # windows plus new tokens up to 496 take the one-pass kernel (the sequence of
+    # one operand and 64 channels in LDS); (64, 496, 16) and (128, 256, 256) the
+    # two-launch path
+    B, H = 3, 2
+    cap = max(96, 2 * n_new + 32)
+    # room, exactly full after, no room (rounded down to a multiple of 16: cap - 6 -> cap - 16)
+    mid = [16, cap - n_new, cap - 6] if n_new >= 32 else [16, cap - n_new, 90]
     host, dev = _cache(gpu, B, H, d, 16, n_recent, cap, seed=30 + d + n_recent, mid=mid)
     g = torch.Generator().manual_seed(7)
     kn = torch.randn(B, H, n_new, d, generator=g).to(torch.bfloat16)
