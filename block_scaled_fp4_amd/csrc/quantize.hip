@@ -246,10 +246,30 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
     for (int j = 0; j < kMaxPer; ++j) {
       const int64_t i = threadIdx.x + 256 * j;
       if (i < nblk) {
-        const int64_t rl = i / bpr, cb = i % bpr;
-        uint4_t* dst = reinterpret_cast<uint4_t*>(raw_rows + rl * A.cols + cb * 16);
+        uint4_t* dst = reinterpret_cast<uint4_t*>(raw_rows + (i / bpr) * A.cols + (i % bpr) * 16);
 #pragma unroll
         for (int w = 0; w < RawBlock<T>::N; ++w) dst[w] = raw[j].w[w];
+      }
+    }
+    __syncthreads();
+    // the channel sums first: their waves' dependent binary64 adds overlap the
+    // other waves' quantization
+    if (c < A.cols) {
+      int64_t t = 0;
+      for (; t + 8 <= nr; t += 8) {
+        double v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (double)load_elem<T>(raw_rows + (t + e) * A.cols + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum = sum + v[e];
+      }
+      for (; t < nr; ++t) sum = sum + (double)load_elem<T>(raw_rows + t * A.cols + c);
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int64_t i = threadIdx.x + 256 * j;
+      if (i < nblk) {
+        const int64_t rl = i / bpr, cb = i % bpr;
         float y[16];
         raw_to_f32<T>(raw[j], y);
         const int64_t r = row0 + r0 + rl, blk = r * bpr + cb;
@@ -262,18 +282,6 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
         A.scales[blk] = (uint8_t)scale;
         if (A.offsets) A.offsets[blk] = (int8_t)off;
       }
-    }
-    __syncthreads();
-    if (c < A.cols) {
-      int64_t t = 0;
-      for (; t + 8 <= nr; t += 8) {
-        double v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (double)load_elem<T>(raw_rows + (t + e) * A.cols + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum = sum + v[e];
-      }
-      for (; t < nr; ++t) sum = sum + (double)load_elem<T>(raw_rows + t * A.cols + c);
     }
   }
   if (c < A.cols) A.means[u * A.cols + c] = sum / (double)n;
