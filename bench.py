@@ -222,13 +222,14 @@ def bench_balance(fp4, synth, torch, n):
 # candidate one multiply (element times reciprocal scale), one E2M1 convert
 # there and back (a packed pair per instruction: half an instruction each),
 # one fused error term, one square and one tree addition -- 5 lane operations,
-# 45 per element for the 9 offsets.  The ALU peak: an unpacked 32-bit VALU
-# instruction processes 16 lanes per clock on each SIMD (a wave of 64 in 4
-# clocks): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.  (The
-# published 157.3 TFLOP/s fp32 counts an FMA as two flops and packed FP32 as
-# two lanes; packed FP32 is not used here.)
+# 45 per element for the 9 offsets.  The ALU peak is the published fp32 vector
+# rate counted in lane operations: 157.3 TFLOP/s counts an FMA as two flops,
+# i.e. 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T lane-ops/s.  gfx950
+# reaches it without packed FP32: unpacked adds, multiplies and FMAs from
+# several waves issued at 51-57 T lane-ops/s on the GPU (about 2.1 GHz under
+# load), while the E2M1 encode convert issues at a quarter of that rate.
 QUANT_LANE_OPS_PER_ELEM = 45
-VALU_PEAK_TOPS = 39.3
+VALU_PEAK_TOPS = 78.6
 
 
 def bench_quantizer(fp4, synth, torch, n):
