@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(256) block_scores_kernel(const double* qm, con
 //     in LDS when they fit, then the kept blocks in ascending order and a bit
 //     mask of the same set.
 
-constexpr int kScoreBlocks = 32;    // middle blocks per scoring workgroup
+constexpr int kScoreBlocks = 16;    // middle blocks per scoring workgroup (17 KB of LDS: eight workgroups per CU)
 constexpr int kSelLdsKeys = 4096;   // keys the select kernel keeps in LDS
 
 
@@ -275,10 +275,25 @@ __global__ void __launch_bounds__(256) decode_scores_kernel(DecSelArgs A) {
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
+// 16-lane row, then row 0's total into row 1 and row 2's into row 3, then
+// the total of rows 0-1 into rows 2-3 (lanes whose source is out of range add
+// zero).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // The k largest of keys[0..nb) (ties: the lower index first), by a radix
-// select over 8-bit digits: the kept indices go to out[0..k) in ascending
-// order and out[k..kmax) gets -1; mask (nullable) gets the same set as bits.
-// Called by all 256 threads of the workgroup (block-wide barriers inside).
+// select over 8-bit digits, stopping at the first digit whose threshold bin
+// is kept whole: the kept indices go to out[0..k) in ascending order and
+// out[k..kmax) gets -1; mask (nullable) gets the same set as bits.  Called by
+// all 256 threads of the workgroup (block-wide barriers inside).
 __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, int32_t* out, uint32_t* mask) {
   __shared__ int hist[256];
   __shared__ int wtot[2][4];
@@ -286,7 +301,7 @@ __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, i
   // k-th largest key: after the passes `prefix` is its value and `rem` the
   // number of keys equal to it that are kept (the lowest indices among them)
   uint64_t prefix = 0;
-  int rem = k;
+  int rem = k, fshift = 0;  // the threshold is decided on the key bits from fshift up
   if (k > 0) {
     for (int shift = 56; shift >= 0; shift -= 8) {
       hist[tid] = 0;
@@ -304,15 +319,10 @@ __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, i
         c4[i] = hist[255 - 4 * lane - i];
         own += c4[i];
       }
-      int incl = own;  // inclusive prefix over lanes (descending bins)
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
+      const int incl = wave_incl_scan(own);  // inclusive prefix over lanes (descending bins)
       const int excl = incl - own;
       // the lane whose range crosses rem finds the bin
-      int found = -1, above = 0;
+      int found = -1, above = 0, fcnt = 0;
       if (excl < rem && incl >= rem) {
         int acc = excl;
 #pragma unroll
@@ -320,16 +330,21 @@ __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, i
           if (found < 0 && acc + c4[i] >= rem) {
             found = 255 - 4 * lane - i;
             above = acc;
+            fcnt = c4[i];
           }
           acc += c4[i];
         }
       }
       const unsigned long long who = __ballot(found >= 0);
       const int src = (int)__builtin_ctzll(who);
-      const int bin = __shfl(found, src, 64);
-      rem -= __shfl(above, src, 64);
+      const int bin = __builtin_amdgcn_readlane(found, src);
+      rem -= __builtin_amdgcn_readlane(above, src);
       prefix |= (uint64_t)bin << shift;
+      fshift = shift;
       __syncthreads();
+      // every key of the threshold's bin is kept: no lower digit can matter
+      // (every wave scanned the same histogram, so all leave together)
+      if (__builtin_amdgcn_readlane(fcnt, src) == rem) break;
     }
   }
   // kept indices in ascending order (and the bit mask)
@@ -338,7 +353,8 @@ __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, i
   for (int base = 0; base < nb; base += 256) {
     const int j = base + tid;
     const uint64_t u = j < nb ? keys[j] : 0ull;
-    const bool tie = k > 0 && j < nb && u == prefix;
+    const uint64_t uh = u >> fshift, ph = prefix >> fshift;
+    const bool tie = k > 0 && j < nb && uh == ph;
     const unsigned long long bt = __ballot(tie);
     if (lane == 0) wtot[0][wave] = __popcll(bt);
     __syncthreads();
@@ -347,7 +363,7 @@ __device__ void select_top_keys(const uint64_t* keys, int nb, int k, int kmax, i
       off_t += w < wave ? wtot[0][w] : 0;
       all_t += wtot[0][w];
     }
-    const bool sel = k > 0 && j < nb && (u > prefix || (tie && off_t + __popcll(bt & below) < rem));
+    const bool sel = k > 0 && j < nb && (uh > ph || (tie && off_t + __popcll(bt & below) < rem));
     const unsigned long long bs = __ballot(sel);
     if (lane == 0) wtot[1][wave] = __popcll(bs);
     __syncthreads();
@@ -391,20 +407,6 @@ __global__ void __launch_bounds__(256) decode_select_kernel(DecSelArgs A) {
 // read once into registers (four keys per lane); longer rows are read from
 // memory in every pass.
 constexpr int kSelRegKeys = 256;
-
-// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
-// 16-lane row, then row 0's total into row 1 and row 2's into row 3, then
-// the total of rows 0-1 into rows 2-3 (lanes whose source is out of range add
-// zero).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
-  return v;
-}
 
 // One 64-key chunk of the final emission: keys whose bits from `shift` up
 // exceed the threshold's, and ties there while fewer than rem have been
