@@ -232,7 +232,7 @@ struct Problem {
 // (their scores are masked), and no branch or clamp sits between the loads,
 // so the next tile's codes stay in flight while the current tile computes.
 template <int D, int BC>
-__device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const HeadBufs& hb, int64_t key0) {
+__device__ __forceinline__ void fetch_k(Fetch<D, BC>& F, const HeadBufs& hb, int64_t key0) {
   using M = StageMap<D>;
   const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -243,6 +243,15 @@ __device__ __forceinline__ void fetch_fp4(Fetch<D, BC>& F, const HeadBufs& hb, i
       F.kc[u] = buf_load16(hb.kc, key * (D / 2) + dc * 16);
       F.ks[u] = buf_load2(hb.ks, key * (D / 16) + dc * 2);
     }
+  }
+}
+
+template <int D, int BC>
+__device__ __forceinline__ void fetch_v(Fetch<D, BC>& F, const HeadBufs& hb, int64_t key0) {
+  using M = StageMap<D>;
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
     const int pr = M::v_pair(wv, l, u), cc = M::v_cc(l);
     if (Fetch<D, BC>::NCH % 256 == 0 || pr < BC / 2) {
       const uint32_t pair = (uint32_t)(key0 / 2) + pr;
@@ -270,10 +279,9 @@ __device__ __forceinline__ half8_t deq8(uint32_t cw, half_t s) {
 }
 
 template <int D, int BC>
-__device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S) {
+__device__ __forceinline__ void stage_k(const Fetch<D, BC>& F, Smem<D, BC>& S) {
   using M = StageMap<D>;
   const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
 #pragma unroll
   for (int u = 0; u < Fetch<D, BC>::PER; ++u) {
     const int kr = M::k_row(wv, l, u), dc = M::k_dc(l);
@@ -283,24 +291,37 @@ __device__ __forceinline__ void stage_fp4(const Fetch<D, BC>& F, Smem<D, BC>& S)
 #pragma unroll
       for (int w = 0; w < 4; ++w) dst[w] = deq8(F.kc[u][w], w < 2 ? ks2[0] : ks2[1]);
     }
-    // V: byte j of dword w = column 16*cc + 4*w + j, tokens (2*pr, 2*pr+1)
-    const int pr = M::v_pair(wv, l, u), cc = M::v_cc(l);
-    if (Fetch<D, BC>::NCH % 256 == 0 || pr < BC / 2) {
-      const int pos = vpos(2 * pr);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t cw = F.vc[u][w], sw = F.vs[u][w];
-        const half2_t sa = e4m3x2_to_half2(sw), sb = e4m3x2_hi_to_half2(sw);
-        const int col = 16 * cc + 4 * w;
-        constexpr int VS2 = Smem<D, BC>::VS8 * 4;  // half2 units per V^T row
-        half2_t* dst = v2 + col * VS2 + 4 * Smem<D, BC>::vpad(cc) + pos / 2;
-        dst[0 * VS2] = scale_pair(cvt_pk_f16_fp4<0>(cw), sa[0]);
-        dst[1 * VS2] = scale_pair(cvt_pk_f16_fp4<1>(cw), sa[1]);
-        dst[2 * VS2] = scale_pair(cvt_pk_f16_fp4<2>(cw), sb[0]);
-        dst[3 * VS2] = scale_pair(cvt_pk_f16_fp4<3>(cw), sb[1]);
-      }
-    }
   }
+}
+
+// Word w of V chunk u (four columns of a token pair): byte j of the code word
+// is column 16*cc + 4*w + j, tokens (2*pr, 2*pr+1).
+template <int D, int BC>
+__device__ __forceinline__ void stage_v_word(const Fetch<D, BC>& F, Smem<D, BC>& S, int u, int w) {
+  using M = StageMap<D>;
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int pr = M::v_pair(wv, l, u), cc = M::v_cc(l);
+  if (Fetch<D, BC>::NCH % 256 == 0 || pr < BC / 2) {
+    half2_t* v2 = reinterpret_cast<half2_t*>(S.v);
+    const int pos = vpos(2 * pr);
+    const uint32_t cw = F.vc[u][w], sw = F.vs[u][w];
+    const half2_t sa = e4m3x2_to_half2(sw), sb = e4m3x2_hi_to_half2(sw);
+    const int col = 16 * cc + 4 * w;
+    constexpr int VS2 = Smem<D, BC>::VS8 * 4;  // half2 units per V^T row
+    half2_t* dst = v2 + col * VS2 + 4 * Smem<D, BC>::vpad(cc) + pos / 2;
+    dst[0 * VS2] = scale_pair(cvt_pk_f16_fp4<0>(cw), sa[0]);
+    dst[1 * VS2] = scale_pair(cvt_pk_f16_fp4<1>(cw), sa[1]);
+    dst[2 * VS2] = scale_pair(cvt_pk_f16_fp4<2>(cw), sb[0]);
+    dst[3 * VS2] = scale_pair(cvt_pk_f16_fp4<3>(cw), sb[1]);
+  }
+}
+
+template <int D, int BC>
+__device__ __forceinline__ void stage_v(const Fetch<D, BC>& F, Smem<D, BC>& S) {
+#pragma unroll
+  for (int u = 0; u < Fetch<D, BC>::PER; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) stage_v_word<D, BC>(F, S, u, w);
 }
 
 // FP16 path: the original bf16/fp16 K and V of one step of keys (32 at
@@ -411,7 +432,7 @@ __device__ __forceinline__ float max16(const float16_t& a) {
   return __builtin_fmaxf(m0, m3);
 }
 
-// Process one tile for one wave.  FP4: two-level P; else fp16(2^(x - m)).
+// One tile for one wave, in two phases.  FP4: two-level P; else fp16(2^(x - m)).
 //
 // Scores stay raw (S = q.k) until the exponential: with c > 0 the largest
 // fl32(S c) is fl32(max(S) c), so the tile maximum is taken on raw scores and
@@ -421,35 +442,44 @@ __device__ __forceinline__ float max16(const float16_t& a) {
 //
 // NK: keys processed, the first NK of the tile's LDS layout (the FP16 path
 // runs steps of 32 or 64 keys).
-template <int D, int BC, bool FP4, bool MASK, bool SINGLE, int NK = BC>
-__device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
-                                          int64_t key0, int64_t qrow, int64_t Sk, int causal, float c) {
+template <int NG>
+struct ScoreTile {
+  float16_t acc[NG];  // S^T of the wave's rows, 32 keys per subtile
+  float bmax[NG];     // this lane's block maximum (raw scores) per subtile
+};
+
+// Scores: S^T = K Q^T, one 32-key subtile at a time; the mask-and-max of the
+// previous subtile runs on the VALU while this subtile's MFMAs execute.  VST:
+// this thread's share of the tile's V staging (from F) also runs between the
+// MFMAs, in issue slots the scores leave free (the caller orders it before
+// the P V phase with a barrier).
+template <int D, int BC, bool MASK, int NK, bool VST>
+__device__ __forceinline__ void s_phase(Smem<D, BC>& S, const half8_t (&qf)[D / 16], ScoreTile<NK / 32>& T,
+                                        const Fetch<D, BC>* F, int64_t key0, int64_t qrow, int64_t Sk, int causal) {
   static_assert(NK % 32 == 0 && NK <= BC, "whole 32-key subtiles of the layout");
   const int lane = threadIdx.x & 63;
   const int hi = lane >> 5;  // which 16-key half of each 32-key group this lane holds
   constexpr int NG = NK / 32;
   constexpr int NS = D / 16;
-  float16_t acc[NG];
-  float bmax[NG];
-  // ---- S^T = K Q^T, one 32-key subtile at a time; the mask-and-max of the
-  // previous subtile runs on the VALU while this subtile's MFMAs execute
   const half8_t* kbase = S.k + krow_of_lane(lane & 31) * Smem<D, BC>::KS8 + hi;
   auto mask_max = [&](int g) {
     if (MASK) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int64_t key = key0 + 32 * g + 16 * hi + i;
-        if (key >= Sk || (causal && key > qrow)) acc[g][i] = -__builtin_inff();
+        if (key >= Sk || (causal && key > qrow)) T.acc[g][i] = -__builtin_inff();
       }
     }
-    bmax[g] = max16(acc[g]);
+    T.bmax[g] = max16(T.acc[g]);
   };
   // Fragment reads run kAhead MFMAs ahead of their use (LDS latency is
   // several MFMA lengths) through a register ring; the fences keep reads and
   // MFMAs in this order and let only ALU work (the mask-and-max of the
-  // previous subtile) move between them.
+  // previous subtile) move between them; the V staging words sit at fixed
+  // iterations, spread over the loop.
   {
     constexpr int NM = NG * NS, kAhead = 4, kRing = kAhead + 2;
+    constexpr int NW = Fetch<D, BC>::PER * 4;  // V staging words of this thread
     half8_t ring[kRing];
     auto kfrag = [&](int i) { return kbase[32 * (i / NS) * Smem<D, BC>::KS8 + 2 * (i % NS)]; };
 #pragma unroll
@@ -460,10 +490,15 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int g = i / NS, s = i % NS;
-      if (s == 0) acc[g] = float16_t{0};
-      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], qf[s], acc[g], 0, 0, 0);
+      if (s == 0) T.acc[g] = float16_t{0};
+      T.acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[i % kRing], qf[s], T.acc[g], 0, 0, 0);
       if (i + kAhead < NM) ring[(i + kAhead) % kRing] = kfrag(i + kAhead);
       if (s == 0 && g > 0) mask_max(g - 1);
+      if (VST) {
+#pragma unroll
+        for (int q = 0; q < NW; ++q)
+          if (i == (q * NM) / NW + 1) stage_v_word<D, BC>(*F, S, q / 4, q % 4);
+      }
       __builtin_amdgcn_sched_barrier(0x0406);  // VALU, SALU and transcendental ops may cross (not MFMA, not LDS)
     }
   }
@@ -471,6 +506,16 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
   mask_max(NG - 1);
+}
+
+// Softmax, P and U^T += V^T P^T of a tile whose scores are in T.
+template <int D, int BC, bool FP4, bool SINGLE, int NK>
+__device__ __forceinline__ void pv_phase(const Smem<D, BC>& S, RowState<D>& R, ScoreTile<NK / 32>& T, float c) {
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5;
+  constexpr int NG = NK / 32;
+  float16_t (&acc)[NG] = T.acc;
+  float (&bmax)[NG] = T.bmax;
   float smax = bmax[0];
 #pragma unroll
   for (int g = 1; g < NG; ++g) smax = __builtin_fmaxf(smax, bmax[g]);
@@ -608,10 +653,19 @@ __device__ __forceinline__ void wave_tile(const Smem<D, BC>& S, const half8_t (&
   R.l += FP4 ? lsum * __builtin_amdgcn_exp2f(use ? tm - R.m : ninf) : lsum;
 }
 
+// Both phases of one tile (the FP16 path: its staging is done before).
+template <int D, int BC, bool FP4, bool MASK, bool SINGLE, int NK = BC>
+__device__ __forceinline__ void wave_tile(Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R, int64_t key0,
+                                          int64_t qrow, int64_t Sk, int causal, float c) {
+  ScoreTile<NK / 32> T;
+  s_phase<D, BC, MASK, NK, false>(S, qf, T, static_cast<const Fetch<D, BC>*>(nullptr), key0, qrow, Sk, causal);
+  pv_phase<D, BC, FP4, SINGLE, NK>(S, R, T, c);
+}
+
 // One FP16-path step of ST keys at k0 (staged at the start of the tile
 // layout) for this wave's rows [wrow0, wrow0 + 32).
 template <int D, int BC, int ST>
-__device__ __forceinline__ void fp16_step(const Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
+__device__ __forceinline__ void fp16_step(Smem<D, BC>& S, const half8_t (&qf)[D / 16], RowState<D>& R,
                                           int64_t k0, int64_t wrow0, int64_t qrow, int64_t Sk, int causal, float c) {
   if (causal && k0 > wrow0 + 31) return;  // every key after this wave's rows
   const bool need_mask = (k0 + ST > Sk) || (causal && k0 + ST - 1 > wrow0);
@@ -785,23 +839,37 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   };
   int cur = 0;
   while (cur < ntile && selected(cur)) ++cur;
-  if (cur < ntile) fetch_fp4<D, BC>(F, hb, (int64_t)cur * BC);
+  if (cur < ntile) {
+    fetch_k<D, BC>(F, hb, (int64_t)cur * BC);
+    fetch_v<D, BC>(F, hb, (int64_t)cur * BC);
+  }
+  // per tile: K staged between the first two barriers, V between the scores'
+  // MFMAs (a wave with no visible key in the tile stages its V share alone),
+  // and the third barrier before any wave reads V.  Every barrier is reached
+  // by every wave.
   while (cur < ntile) {
     int nxt = cur + 1;
     while (nxt < ntile && selected(nxt)) ++nxt;
-    __syncthreads();  // previous tile's LDS reads are done
-    stage_fp4<D, BC>(F, S);
     // always prefetch (past the last tile this is a harmless cached reload)
-    fetch_fp4<D, BC>(F, hb, (int64_t)(nxt < ntile ? nxt : cur) * BC);
+    const int64_t knext = (int64_t)(nxt < ntile ? nxt : cur) * BC;
+    __syncthreads();  // previous tile's LDS reads are done
+    stage_k<D, BC>(F, S);
+    fetch_k<D, BC>(F, hb, knext);
     __syncthreads();
     const int64_t key0 = (int64_t)cur * BC;
     const int64_t wrow0 = q0 + 32 * wave;
     const bool wave_dead = P.causal && key0 > wrow0 + 31;  // every key of the tile is after this wave's rows
+    ScoreTile<BC / 32> T;
     if (!wave_dead) {
       const bool need_mask = (key0 + BC > Sk) || (P.causal && key0 + BC - 1 > wrow0);
-      if (need_mask) wave_tile<D, BC, PM != 2, true, PM == 1>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
-      else wave_tile<D, BC, PM != 2, false, PM == 1>(S, qf, R, key0, qrow, Sk, P.causal, P.c);
+      if (need_mask) s_phase<D, BC, true, BC, true>(S, qf, T, &F, key0, qrow, Sk, P.causal);
+      else s_phase<D, BC, false, BC, true>(S, qf, T, &F, key0, qrow, Sk, P.causal);
+    } else {
+      stage_v<D, BC>(F, S);
     }
+    fetch_v<D, BC>(F, hb, knext);
+    __syncthreads();  // V is staged
+    if (!wave_dead) pv_phase<D, BC, PM != 2, PM == 1, BC>(S, R, T, P.c);
     cur = nxt;
   }
 
