@@ -203,34 +203,20 @@ struct KvArgs {
 
 __device__ __forceinline__ int krow2(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-  return __builtin_fmaxf(v, o);
-}
+// dV pass: K rows fed to S^T = K^ Q^T in this order leave lane (query, h)
+// holding keys 16h .. 16h+15 of the wave, consecutive (the output rows of a
+// 32x32 MFMA lane are 4h + 8j + i, i < 4, j < 4)
+__device__ __forceinline__ int krow16(int r) { return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 4); }
 
-// maximum over the 16 lanes of a DPP row (mirror, half mirror, then the two quad swaps)
-__device__ __forceinline__ float rowmax16(float v) {
-  v = dpp_max<0x140>(v);
-  v = dpp_max<0x141>(v);
-  v = dpp_max<0xB1>(v);
-  return dpp_max<0x4E>(v);
-}
-
-// lane n of each 16-lane DPP row, broadcast to the row
-template <int N>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
-}
-
-// dst[k][n] = src[k] of lane n of this lane's row, for n = 0..15
-template <int K, int N = 0>
-__device__ __forceinline__ void row_bcast_all(const float (&src)[K], float (&dst)[K][16]) {
-  if constexpr (N < 16) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) dst[k][N] = row_bcast<N>(src[k]);
-    row_bcast_all<K, N + 1>(src, dst);
-  }
+__device__ __forceinline__ float max16v(const float (&a)[16]) {
+  float m0 = __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]);
+  float m1 = __builtin_fmaxf(__builtin_fmaxf(a[3], a[4]), a[5]);
+  float m2 = __builtin_fmaxf(__builtin_fmaxf(a[6], a[7]), a[8]);
+  float m3 = __builtin_fmaxf(__builtin_fmaxf(a[9], a[10]), a[11]);
+  float m4 = __builtin_fmaxf(__builtin_fmaxf(a[12], a[13]), a[14]);
+  m0 = __builtin_fmaxf(__builtin_fmaxf(m0, m1), m2);
+  m3 = __builtin_fmaxf(__builtin_fmaxf(m3, m4), a[15]);
+  return __builtin_fmaxf(m0, m3);
 }
 
 // Two binary32 values -> two bf16 (round to nearest even) in one dword, low
@@ -278,6 +264,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
   __shared__ __align__(16) float D_s[QB];
   __shared__ __align__(16) float tmx[DV ? 8 : 1][QB];  // block maxima: [2 wave + row of the wave][query]
   __shared__ float2_t ptab[DV ? 128 : 1];             // the P-scale table of the chosen scheme
+  // dV: P^ of the wave's 32 keys x the step's 32 queries as bf16 hi and lo
+  // terms, [query][key] rows (padded to 40), written by (query, key half)
+  // lanes and read back by (key, query half) lanes
+  constexpr int RPT = 40;
+  __shared__ __align__(16) uint16_t pth[DV ? 4 * QB * RPT : 1], ptl[DV ? 4 * QB * RPT : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
   const int64_t BHkv = gridDim.x / A.nkt;
   const int64_t bhk = blockIdx.x % BHkv;
@@ -287,10 +278,13 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
   const int64_t key0 = (int64_t)kt * kGT;
   const int64_t key = key0 + 32 * wave + r32;
   const bool kok = key < A.Sk;
+  // the K^ row this lane feeds: key r32 (dK: B operand), key krow16(r32) (dV: A operand of S^T)
+  const int64_t kfeed = key0 + 32 * wave + (DV ? krow16(r32) : r32);
+  const bool fok = kfeed < A.Sk;
   uint4_t kf[D / 16], vf[DV ? 1 : D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    kf[s] = fragb(A.k + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok);
+    kf[s] = fragb(A.k + (bhk * A.Sk + (fok ? kfeed : 0)) * D + 16 * s + 8 * hi, fok);
     if (!DV) vf[DV ? 0 : s] = fragb(A.v + (bhk * A.Sk + (kok ? key : 0)) * D + 16 * s + 8 * hi, kok);
   }
   float16_t acc[D / 32];
@@ -374,85 +368,116 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
     stage();
     if (step + 1 < nsteps) fetch(step + 1);  // in flight during this step's products
     __syncthreads();
-    // S = Q^ K^T (and dP = dO V^T): lane holds key r32 of the wave and the 16 queries qof(v)
-    float16_t sacc = float16_t{0}, dp = float16_t{0};
+    if constexpr (DV) {
+      // S^T = K^ Q^T: lane (query r32 of the step, h) holds keys 16h + v of the wave
+      float16_t sacc = float16_t{0};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      sacc = mfma_bf16(*reinterpret_cast<const uint4_t*>(Qa + qr * RA + 16 * s + 8 * hi), kf[s], sacc);
-    if (!DV) {
+      for (int s = 0; s < D / 16; ++s)
+        sacc = mfma_bf16(kf[s], *reinterpret_cast<const uint4_t*>(Qa + r32 * RA + 16 * s + 8 * hi), sacc);
+      const int64_t qq = q0 + r32;
+      const int64_t kb = key0 + 32 * wave + 16 * hi;  // this lane's first key
+      float x[16];
+      const int64_t wkey1 = key0 + 32 * wave + 31;  // the wave's last key
+      const bool full = wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0);
+      if (full) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = sacc[v] * A.c;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const bool vis = kb + v < A.Sk && qq < A.Sq && (!A.causal || kb + v <= qq);
+          x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+        }
+      }
+      // the lane's 16 keys are one level-2 block of its query: block maximum
+      // in registers, tile maximum over kv_tile keys through LDS
+      const float bm = max16v(x);
+      tmx[2 * wave + hi][r32] = bm;
+      __syncthreads();
+      const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
+      const int ne = A.kv_tile == 128 ? 8 : 4;
+      float tmi = tmx[e0][r32];
+      for (int e = 1; e < ne; ++e) tmi = __builtin_fmaxf(tmi, tmx[e0 + e][r32]);
+      const bool live = bm != -__builtin_inff();  // a block with no visible key gets scale 0
+      const float emax = live ? __builtin_amdgcn_exp2f(bm - tmi) : 0.0f;
+      const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
+      const float2_t fs = ptab[byte];
+      const float sh = live ? tmi : 0.0f;
+      const float f0 = live ? fs[0] : 0.0f;  // (an empty block: 2^-inf times 0)
+      // s2 times the tile weight, rounded once before the product with the code value
+      const float s2w =
+          live ? fs[1] * (__builtin_amdgcn_exp2f(tmi - lse_s[r32]) * (A.single ? 1.0f : 1.0f / 2688.0f)) : 0.0f;
+      float w16[16];
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float t0 = __builtin_amdgcn_exp2f(x[v] - sh) * f0;
+        const float t1 = __builtin_amdgcn_exp2f(x[v + 1] - sh) * f0;
+        const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t0, t1));
+        w16[v] = cv[0] * s2w;  // (s2 times the weight is rounded once, then the product)
+        w16[v + 1] = cv[1] * s2w;
+      }
+      // hi = the top 16 bits, lo = the rest rounded to bf16 (as pack8), written
+      // as [query][key] and read back as the A operand of dV += P^T X: lane
+      // (key r32, h) takes queries 16 ks + 8 h .. +8
+      uint16_t* ph = pth + (wave * QB + r32) * RPT + 16 * hi;
+      uint16_t* pl = ptl + (wave * QB + r32) * RPT + 16 * hi;
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        uint4_t wh, wl;
+        pack8<true>(w16 + 8 * hv, wh, wl);
+        *reinterpret_cast<uint4_t*>(ph + 8 * hv) = wh;
+        *reinterpret_cast<uint4_t*>(pl + 8 * hv) = wl;
+      }
+      // the wave reads what its own lanes wrote (LDS operations of a wave stay in order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* rh = pth + (wave * QB + 16 * ks + 8 * hi) * RPT + r32;
+        const uint16_t* rl = ptl + (wave * QB + 16 * ks + 8 * hi) * RPT + r32;
+        uint4_t wa, wl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wa[j] = (uint32_t)rh[(2 * j) * RPT] | ((uint32_t)rh[(2 * j + 1) * RPT] << 16);
+          wl[j] = (uint32_t)rl[(2 * j) * RPT] | ((uint32_t)rl[(2 * j + 1) * RPT] << 16);
+        }
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
+          const uint4_t xb = *reinterpret_cast<const uint4_t*>(Xb + row);
+          acc[t] = mfma_bf16(wa, xb, acc[t]);
+          acc[t] = mfma_bf16(wl, xb, acc[t]);
+          if (SPL) acc[t] = mfma_bf16(wa, *reinterpret_cast<const uint4_t*>(Xbl + row), acc[t]);
+        }
+      }
+    } else {
+      // S = Q^ K^T and dP = dO V^T: lane holds key r32 of the wave and the 16 queries qof(v)
+      float16_t sacc = float16_t{0}, dp = float16_t{0};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        sacc = mfma_bf16(*reinterpret_cast<const uint4_t*>(Qa + qr * RA + 16 * s + 8 * hi), kf[s], sacc);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oa + qr * RA + 16 * s + 8 * hi), vf[DV ? 0 : s], dp);
         if (SPL) dp = mfma_bf16(*reinterpret_cast<const uint4_t*>(Oal + qr * RA + 16 * s + 8 * hi), vf[DV ? 0 : s], dp);
       }
-    }
-    float x[16];
-    // every (key, query) pair of the wave's step visible: no mask (the common case)
-    const int64_t wkey1 = key0 + 32 * wave + 31;  // the wave's last key
-    const bool full = wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0);
-    if (full) {
+      float x[16];
+      // every (key, query) pair of the wave's step visible: no mask (the common case)
+      const int64_t wkey1 = key0 + 32 * wave + 31;  // the wave's last key
+      const bool full = wkey1 < A.Sk && q0 + QB <= A.Sq && (!A.causal || wkey1 <= q0);
+      if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] = sacc[v] * A.c;
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t qq = q0 + qof(v);
-        const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
-        x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
-      }
-    }
-    float w16[16];  // the A operand values of this step: P^ (dV) or dS (dK)
-    if (DV) {
-      float bm[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) bm[v] = rowmax16(x[v]);  // this query's 16-key block
-      if ((r32 & 15) == 0) {  // one writer per DPP row: entry 2 wave + row of the wave
-        float* dst = &tmx[DV ? 2 * wave + (r32 >> 4) : 0][0];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          *reinterpret_cast<float4_t*>(dst + 8 * hi + 16 * h) = float4_t{bm[8 * h], bm[8 * h + 1], bm[8 * h + 2], bm[8 * h + 3]};
-          *reinterpret_cast<float4_t*>(dst + 8 * hi + 16 * h + 4) =
-              float4_t{bm[8 * h + 4], bm[8 * h + 5], bm[8 * h + 6], bm[8 * h + 7]};
-        }
-      }
-      __syncthreads();
-      // The scale data of a (query, 16-key block) is the same in all 16 lanes of the block's DPP
-      // row: lane i of each row works it out for value i (query qof(i)), then each value is
-      // broadcast across the row.
-      const int e0 = A.kv_tile == 128 ? 0 : 2 * (wave & 2);
-      const int ne = A.kv_tile == 128 ? 8 : 4;
-      float sd[3];  // this lane's value: tile maximum, element factor, s2 times the tile weight
-      {
-        const int qi = qof(r32 & 15);
-        const float bmi = tmx[2 * wave + (r32 >> 4)][qi];
-        float tmi = tmx[e0][qi];
-        for (int e = 1; e < ne; ++e) tmi = __builtin_fmaxf(tmi, tmx[e0 + e][qi]);
-        const bool live = bmi != -__builtin_inff();  // a block with no visible key gets scale 0
-        const float emax = live ? __builtin_amdgcn_exp2f(bmi - tmi) : 0.0f;
-        const uint32_t byte = f32_to_e4m3(A.single ? div6_rn(emax) : emax * 448.0f);
-        const float2_t fs = ptab[DV ? byte : 0];
-        sd[0] = live ? tmi : 0.0f;
-        sd[1] = fs[0];
-        sd[2] = live ? fs[1] * (__builtin_amdgcn_exp2f(tmi - lse_s[qi]) * (A.single ? 1.0f : 1.0f / 2688.0f)) : 0.0f;
-      }
-      float bc[3][16];
-      row_bcast_all(sd, bc);
-      float t[16];
-      if (full) {  // no block is empty
-#pragma unroll
-        for (int v = 0; v < 16; ++v) t[v] = __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v];
+        for (int v = 0; v < 16; ++v) x[v] = sacc[v] * A.c;
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          t[v] = bm[v] != -__builtin_inff() ? __builtin_amdgcn_exp2f(x[v] - bc[0][v]) * bc[1][v] : 0.0f;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t qq = q0 + qof(v);
+          const bool vis = kok && qq < A.Sq && (!A.causal || key <= qq);
+          x[v] = vis ? sacc[v] * A.c : -__builtin_inff();
+        }
       }
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float2_t cv = cvt_pk_f32_fp4<0>(cvt_pk_fp4<0>(0u, t[v], t[v + 1]));
-        w16[v] = cv[0] * bc[2][v];  // (s2 times the weight is rounded once, then the product)
-        w16[v + 1] = cv[1] * bc[2][v + 1];
-      }
-    } else {
+      float w16[16];  // dS of this lane's key and queries
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int qb = 8 * hi + 16 * h;
@@ -466,20 +491,19 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
           w16[8 * h + 4 + j] = A.alpha * __builtin_amdgcn_exp2f(x[8 * h + 4 + j] - lc[j]) * (dp[8 * h + 4 + j] - dc[j]);
         }
       }
-    }
-    // acc += w^T X: A = this lane's values (k-step ks: values 8 ks .. 8 ks + 7), B = the
-    // [d][query] image (dO for dV, Q^ for dK)
+      // acc += dS^T Q^: A = this lane's values (k-step ks: values 8 ks .. 8 ks + 7), B = the
+      // [d][query] image of Q^
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4_t wa, wl;
-      pack8<true>(w16 + 8 * ks, wa, wl);
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4_t wa, wl;
+        pack8<true>(w16 + 8 * ks, wa, wl);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
-        const uint4_t xb = *reinterpret_cast<const uint4_t*>(Xb + row);
-        acc[t] = mfma_bf16(wa, xb, acc[t]);
-        acc[t] = mfma_bf16(wl, xb, acc[t]);
-        if (DV && SPL) acc[t] = mfma_bf16(wa, *reinterpret_cast<const uint4_t*>(Xbl + row), acc[t]);
+        for (int t = 0; t < D / 32; ++t) {
+          const int row = (32 * t + r32) * RB + 16 * ks + 8 * hi;
+          const uint4_t xb = *reinterpret_cast<const uint4_t*>(Xb + row);
+          acc[t] = mfma_bf16(wa, xb, acc[t]);
+          acc[t] = mfma_bf16(wl, xb, acc[t]);
+        }
       }
     }
   }
