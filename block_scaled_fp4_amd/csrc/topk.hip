@@ -85,15 +85,18 @@ __global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
   for (int e = 0; e < 8; ++e) out[e] = s[e] / (double)n;
 }
 
-// Scores of a tile of 64 query blocks x 64 key blocks of one (batch, head):
-// Q and K means staged through LDS 32 channels at a time, every score summed
-// over ascending channels (binary64 products and sums, no fused multiply-add),
-// written as an order-preserving 64-bit key.  A tile wholly above the causal
-// diagonal does nothing; its keys are never read.  (Measured on a causal 32K
-// prefill: 64 x 64, 32 x 64 and 64 x 32 tiles take 34-36 us; 32 x 32 tiles,
-// at one LDS read per multiply-add, 42 us.)
-constexpr int kScTQ = 64, kScTK = 64, kScTC = 32;
-constexpr int kScR = kScTQ / 16, kScC = kScTK / 16;  // scores per thread: kScR x kScC
+// Scores of 16 query blocks x 64 key blocks of one (batch, head) per
+// workgroup.  Wave w takes query blocks i0 + 4w .. +3, whose means are the
+// same for all its lanes and are read through the scalar unit; lane l takes
+// key block j0 + l, from a transposed LDS image of the 64 key means (32
+// channels at a time, staged from coalesced reads).  Every score is one
+// binary64 fused multiply-add per channel in ascending channel order, written
+// as an order-preserving 64-bit key.  A tile wholly above the causal
+// diagonal does nothing; its keys are never read.  The fixed channel order
+// makes every score one chain of d dependent fused multiply-adds: a causal 32K
+// prefill has about 20 such chains per SIMD in all, where the fp64 unit needs
+// about 64 in flight to run at its rate, so the chains' latency sets the time.
+constexpr int kScQ = 16, kScK = 64, kScC = 32;
 
 // Scores as unsigned keys that order like the doubles (-0 folded into +0).
 __device__ __forceinline__ uint64_t score_key(double s) {
@@ -102,87 +105,104 @@ __device__ __forceinline__ uint64_t score_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-__global__ void __launch_bounds__(256) block_scores_kernel(const double* qm, const double* km, int64_t H,
-                                                           int64_t Hkv, int nqb, int nkb, int d, int causal,
-                                                           int ntq, int ntk, uint64_t* keys) {
-  __shared__ double sq[kScTQ][kScTC + 1];
-  __shared__ double sk[kScTK][kScTC + 1];
-  const int64_t bh = blockIdx.x / (ntq * ntk);
-  const int tile = (int)(blockIdx.x - bh * ntq * ntk);
-  const int i0 = (tile / ntk) * kScTQ, j0 = (tile % ntk) * kScTK;
-  const int ilast = i0 + kScTQ - 1 < nqb - 1 ? i0 + kScTQ - 1 : nqb - 1;
+__global__ void __launch_bounds__(256) block_scores_kernel(const double* __restrict__ qm,
+                                                           const double* __restrict__ km, int64_t H, int64_t Hkv,
+                                                           int nqb, int nkb, int d, int causal, int ntq, int ntk,
+                                                           uint64_t* __restrict__ keys) {
+  __shared__ double skt[kScC][kScK + 1];  // [channel][key block]
+  // Workgroups go to the 8 XCDs in turn (blockIdx modulo 8): consecutive
+  // tiles -- one head's -- are given to one XCD, so the key means its tiles
+  // all re-read stay in that XCD's L2.
+  const unsigned per = gridDim.x / 8;
+  const unsigned lin = blockIdx.x < 8 * per ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+  const int64_t bh = lin / (ntq * ntk);
+  const int tile = (int)(lin - bh * ntq * ntk);
+  const int i0 = (tile / ntk) * kScQ, j0 = (tile % ntk) * kScK;
+  const int ilast = i0 + kScQ - 1 < nqb - 1 ? i0 + kScQ - 1 : nqb - 1;
   if (causal && j0 > ilast) return;
   const int64_t b = bh / H, h = bh - b * H, hk = h / (H / Hkv);
   const double* qb = qm + bh * nqb * d;
   const double* kb = km + (b * Hkv + hk) * nkb * d;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  // staging map: element e = tid + 256 u of a chunk -> row e / 32, channel e % 32
-  constexpr int NQ = kScTQ * kScTC / 256, NK = kScTK * kScTC / 256;
-  double rq[NQ], rk[NK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int iw = i0 + 4 * __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's first query block
+  const int iwl = iw + 3 < nqb - 1 ? iw + 3 : nqb - 1;                // its last one that exists
+  const bool live = iw < nqb && (!causal || j0 <= iwl);
+  // query blocks past the last one read the last one (their scores are not written)
+  const double* qr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) qr[r] = qb + (int64_t)(iw + r < nqb ? iw + r : nqb - 1) * d;
+  // staging: element e = tid + 256 u of a chunk -> key block e / 32, channel e % 32
+  constexpr int NK = kScK * kScC / 256;
+  double rk[NK];
   auto fetch = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = tid + 256 * u, r = e / kScTC, cc = e % kScTC;
-      rq[u] = i0 + r < nqb ? qb[(int64_t)(i0 + r) * d + c0 + cc] : 0.0;
-    }
-#pragma unroll
     for (int u = 0; u < NK; ++u) {
-      const int e = tid + 256 * u, r = e / kScTC, cc = e % kScTC;
+      const int e = tid + 256 * u, r = e / kScC, cc = e % kScC;
       rk[u] = j0 + r < nkb ? kb[(int64_t)(j0 + r) * d + c0 + cc] : 0.0;
     }
   };
-  double acc[kScR][kScC];  // rows ty + 16 r, columns tx + 16 c
-#pragma unroll
-  for (int r = 0; r < kScR; ++r)
-#pragma unroll
-    for (int c = 0; c < kScC; ++c) acc[r][c] = 0.0;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
   fetch(0);
-  for (int c0 = 0; c0 < d; c0 += kScTC) {
+  for (int c0 = 0; c0 < d; c0 += kScC) {
     __syncthreads();  // the previous chunk's reads are done
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = tid + 256 * u;
-      sq[e / kScTC][e % kScTC] = rq[u];
-    }
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int e = tid + 256 * u;
-      sk[e / kScTC][e % kScTC] = rk[u];
+      skt[e % kScC][e / kScC] = rk[u];
     }
     __syncthreads();
-    if (c0 + kScTC < d) fetch(c0 + kScTC);
-#pragma unroll 8
-    for (int cc = 0; cc < kScTC; ++cc) {
-      double a[kScR], bv[kScC];
+    if (c0 + kScC < d) fetch(c0 + kScC);
+    if (live) {
+      // eight channels at a time (each score takes them in ascending
+      // order); the query means of the next eight are loaded before this
+      // group's arithmetic
+      double qv[4][8], qn[4][8];
 #pragma unroll
-      for (int r = 0; r < kScR; ++r) a[r] = sq[ty + 16 * r][cc];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < kScC; ++c) bv[c] = sk[tx + 16 * c][cc];
+        for (int j = 0; j < 8; ++j) qv[r][j] = qr[r][c0 + j];
 #pragma unroll
-      for (int r = 0; r < kScR; ++r)
+      for (int c8 = 0; c8 < kScC; c8 += 8) {
+        if (c8 + 8 < kScC) {
 #pragma unroll
-        for (int c = 0; c < kScC; ++c) acc[r][c] = __dadd_rn(acc[r][c], __dmul_rn(a[r], bv[c]));
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qn[r][j] = qr[r][c0 + c8 + 8 + j];
+        }
+        double kv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[j] = skt[c8 + j][lane];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = __fma_rn(qv[r][j], kv[j], acc[r]);
+        if (c8 + 8 < kScC) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qv[r][j] = qn[r][j];
+        }
+      }
     }
   }
+  const int j = j0 + lane;
 #pragma unroll
-  for (int r = 0; r < kScR; ++r)
-#pragma unroll
-    for (int c = 0; c < kScC; ++c) {
-      const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
-      if (i < nqb && j < nkb && (!causal || j <= i)) keys[(bh * nqb + i) * nkb + j] = score_key(acc[r][c]);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int i = iw + r;
+    if (live && i < nqb && j < nkb && (!causal || j <= i)) keys[(bh * nqb + i) * nkb + j] = score_key(acc[r]);
+  }
 }
 
 // ---- decode: promoted middle blocks of one query token per query head ----
 //
 // The query block of a kv head is its G query vectors; its mean and the
 // key-block means (cached binary64 sums over each block's tokens, divided by
-// their count) give one binary64 score per middle block, summed over
-// ascending channels.  The ceil(pct * n / 100) best blocks (descending score,
-// lower block first on ties) are kept.
-//   decode_scores_kernel: 32 blocks per workgroup; the sums are read
-//     coalesced (a wavefront reads 512 contiguous bytes), each channel's
-//     product goes to LDS, then one lane per block adds its row in order;
+// their count) give one binary64 score per middle block, one fused
+// multiply-add per channel in ascending order.  The ceil(pct * n / 100) best
+// blocks (descending score, lower block first on ties) are kept.
+//   decode_scores_kernel: 16 blocks per workgroup; the sums are read
+//     coalesced (a wavefront reads 512 contiguous bytes), each block's mean
+//     goes to LDS, then one lane per block runs its row in channel order;
 //   decode_select_kernel: one workgroup per (batch, kv head): a radix select
 //     (8 passes of 8 bits) on order-preserving 64-bit keys of the scores, kept
 //     in LDS when they fit, then the kept blocks in ascending order and a bit
@@ -214,7 +234,7 @@ __device__ __forceinline__ int64_t sel_mid_len(const DecSelArgs& A, int64_t b) {
 // grid: B*Hkv*ceil(nbc/32); block: 256 threads.
 __global__ void __launch_bounds__(256) decode_scores_kernel(DecSelArgs A) {
   __shared__ double qm[128];
-  __shared__ double prod[kScoreBlocks][129];  // one pad column: lanes summing rows hit distinct banks
+  __shared__ double kmr[kScoreBlocks][129];  // block means; one pad column: lanes reading rows hit distinct banks
   const int tid = threadIdx.x;
   const int nchunk = (A.nbc + kScoreBlocks - 1) / kScoreBlocks;
   const int64_t bk = blockIdx.x / nchunk;
@@ -256,20 +276,20 @@ __global__ void __launch_bounds__(256) decode_scores_kernel(DecSelArgs A) {
       m0 = __ddiv_rn(w[i][0], (double)n);
       m1 = __ddiv_rn(w[i][1], (double)n);
     }
-    prod[jb][c] = __dmul_rn(qm[c], m0);
-    prod[jb][c + 1] = __dmul_rn(qm[c + 1], m1);
+    kmr[jb][c] = m0;
+    kmr[jb][c + 1] = m1;
   }
   __syncthreads();
   if (tid < nloc) {
-    // 16 row entries are read ahead of each run of additions (the adds stay
-    // in channel order)
+    // one fused multiply-add per channel in ascending order; 16 row entries
+    // are read ahead of each run
     double s = 0.0;
     for (int c0 = 0; c0 < d; c0 += 16) {
       double r[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = prod[tid][c0 + i];
+      for (int i = 0; i < 16; ++i) r[i] = kmr[tid][c0 + i];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s = __dadd_rn(s, r[i]);
+      for (int i = 0; i < 16; ++i) s = __fma_rn(qm[c0 + i], r[i], s);
     }
     A.keys[bk * A.nbc + j0 + tid] = score_key(s);
   }
@@ -589,7 +609,7 @@ hipError_t fp4i_launch_topk(const TopkLaunch& L, hipStream_t stream) {
     const hipError_t e = L.dtype == 0 ? launch_means<uint16_t>(L, stream) : launch_means<half_t>(L, stream);
     if (e != hipSuccess) return e;
   }
-  const int ntq = (L.nqb + kScTQ - 1) / kScTQ, ntk = (L.nkb + kScTK - 1) / kScTK;
+  const int ntq = (L.nqb + kScQ - 1) / kScQ, ntk = (L.nkb + kScK - 1) / kScK;
   hipLaunchKernelGGL(block_scores_kernel, dim3((unsigned)(L.B * L.H * ntq * ntk)), dim3(256), 0, stream, L.qmeans,
                      L.kmeans, L.H, L.Hkv, L.nqb, L.nkb, d, L.causal, ntq, ntk, L.keys);
   hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((gq + 3) / 4)), dim3(256), 0, stream, L.keys, gq, L.nqb,

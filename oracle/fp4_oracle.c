@@ -397,10 +397,25 @@ void orc_block_sums(const float* x, int64_t S, int d, int blk, double* sums) {
    ceil(pct * n / 100) in integers. */
 int orc_topk_count(int pct, int n) { return (pct * n + 99) / 100; }
 
+/* Score of a block pair: the binary64 dot product of the two block means,
+   one fused multiply-add per channel in ascending channel order (each step
+   is the exact s + q_c k_c rounded once; the page fixes the dot product, not
+   its rounding). */
+static double block_score(const double* q, const double* k, int d) {
+  double s = 0.0;
+  for (int c = 0; c < d; ++c) s = fma(q[c], k[c], s);
+  return s;
+}
+
+/* Every score of query blocks x key blocks (out [nqb, nkb]). */
+void orc_block_scores(const double* qm, const double* km, int nqb, int nkb, int d, double* out) {
+  for (int i = 0; i < nqb; ++i)
+    for (int j = 0; j < nkb; ++j) out[(int64_t)i * nkb + j] = block_score(qm + (int64_t)i * d, km + (int64_t)j * d, d);
+}
+
 /* For every query block i: score each visible key block j (j <= i when
-   causal) with the binary64 dot product of the block means (ascending
-   channel order), keep the k_i highest (ties: lower j first), and write
-   them in ascending j order, padded with -1 to kmax entries. */
+   causal), keep the k_i highest (ties: lower j first), and write them in
+   ascending j order, padded with -1 to kmax entries. */
 void orc_block_topk(const double* qm, const double* km, int nqb, int nkb, int d, int causal,
                     int pct, int kmax, int32_t* idx, int32_t* cnt) {
   double* sc = (double*)malloc(sizeof(double) * (size_t)nkb);
@@ -408,12 +423,7 @@ void orc_block_topk(const double* qm, const double* km, int nqb, int nkb, int d,
   for (int i = 0; i < nqb; ++i) {
     int nvis = causal ? (i + 1 < nkb ? i + 1 : nkb) : nkb;
     for (int j = 0; j < nvis; ++j) {
-      double s = 0.0;
-      for (int c = 0; c < d; ++c) {
-        double p = qm[(int64_t)i * d + c] * km[(int64_t)j * d + c];
-        s = s + p;
-      }
-      sc[j] = s;
+      sc[j] = block_score(qm + (int64_t)i * d, km + (int64_t)j * d, d);
       taken[j] = 0;
     }
     int k = orc_topk_count(pct, nvis);

@@ -20,7 +20,7 @@ _LIB = os.path.join(_LIB_DIR, "liboracle.so")
 
 __all__ = [
     "build", "lib", "e2m1_value", "e4m3_value", "e4m3_encode", "e2m1_encode", "recip",
-    "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_topk",
+    "round_fp16", "quantize_block", "quantize", "dequantize", "block_means", "block_scores", "block_topk",
     "topk_count", "attention_fwd", "attention_exact", "attention_decode", "num_threads", "balance_exponents",
     "balance_apply",
     "score_factor", "kv_append", "block_sums", "hadamard_rows", "attention_train", "mx_quantize",
@@ -79,6 +79,8 @@ def lib():
     L.orc_block_topk.argtypes = [_f64p, _f64p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                  C.c_int, _i32p, _i32p]
     L.orc_block_topk.restype = None
+    L.orc_block_scores.argtypes = [_f64p, _f64p, C.c_int, C.c_int, C.c_int, _f64p]
+    L.orc_block_scores.restype = None
     L.orc_attention_fwd.argtypes = [_f32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int64,
                                     C.c_int64, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int,
                                     C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64, _vp,
@@ -271,6 +273,17 @@ def block_means(x, blk=128):
 
 def topk_count(pct: int, n: int) -> int:
     return lib().orc_topk_count(int(pct), int(n))
+
+
+def block_scores(qm, km):
+    """Scores of every (query block, key block) pair [nqb, nkb] (ThriftAttention
+    page, Metodologia / 1): binary64 dot products of the block means, one fused
+    multiply-add per channel in ascending order."""
+    qm = np.ascontiguousarray(qm, np.float64)
+    km = np.ascontiguousarray(km, np.float64)
+    out = np.zeros((qm.shape[0], km.shape[0]), np.float64)
+    lib().orc_block_scores(qm.reshape(-1), km.reshape(-1), qm.shape[0], km.shape[0], qm.shape[1], out.reshape(-1))
+    return out
 
 
 def block_topk(qm, km, causal, pct):

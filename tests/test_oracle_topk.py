@@ -4,6 +4,8 @@ ThriftAttention page, Metodologia / 1: Q and K split into blocks; the score of a
 block pair is the dot product of the blocks' mean token vectors; the top-k
 pairs go to the FP16 path.  Resultados: budgets are a percentage of blocks.
 """
+from fractions import Fraction
+
 import numpy as np
 import torch
 
@@ -26,6 +28,27 @@ def test_means_exact_on_integer_data():
     assert m.shape == (3, 16)
     assert np.array_equal(m[0], x[:128].astype(np.float64).sum(0) / 128)
     assert np.array_equal(m[2], x[256:].astype(np.float64).sum(0) / 44)
+
+
+def test_scores_one_rounding_per_channel():
+    # each step of the dot product is the exact s + q_c k_c rounded once to
+    # binary64 (float() of a Fraction rounds to nearest, ties to even), in
+    # ascending channel order
+    rng = np.random.default_rng(7)
+    qm = rng.standard_normal((5, 24))
+    km = rng.standard_normal((6, 24)) * np.exp2(rng.integers(-20, 20, size=(6, 1)))
+    got = oracle.block_scores(qm, km)
+    separate = 0
+    for i in range(5):
+        for j in range(6):
+            s = 0.0
+            t = 0.0
+            for c in range(24):
+                s = float(Fraction(s) + Fraction(float(qm[i, c])) * Fraction(float(km[j, c])))
+                t = t + float(qm[i, c]) * float(km[j, c])  # product rounded, then the sum
+            assert got[i, j] == s, (i, j)
+            separate += got[i, j] != t
+    assert separate > 0  # the fused form is the one pinned, not the two-rounding one
 
 
 def _brute(qm, km, causal, pct):
