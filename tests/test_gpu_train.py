@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from block_scaled_fp4_amd import synth
-from gpu_helpers import assert_close_attn, case
+from gpu_helpers import TIE_SLACK, assert_close_attn, assert_close_attn_rows, case
 
 pytestmark = pytest.mark.gpu
 
@@ -50,3 +50,31 @@ def test_train_step(gpu, S, d, H, Hkv, causal, kv_tile, single, dt):
     _close_grad(dv.cpu().numpy(), r["dv"], "dv")
     _close_grad(dq.cpu().numpy(), r["dq"], "dq")
     _close_grad(dk.cpu().numpy(), r["dk"], "dk")
+
+
+def test_train_step_full_size(gpu):
+    # the training workload as timed (B=1 H=32 S=4096 d=128 causal, bf16, two-level P,
+    # kv_tile 128, one launch of each kernel over all heads); heads 0, 13 and 31 are
+    # compared with the oracle, which runs one head at a time
+    S, H, d = 4096, 32, 128
+    q, k, v = synth.qkv(1, H, S, d, torch.bfloat16, seed=0, k_outliers=4)
+    g = torch.Generator().manual_seed(5)
+    do = torch.randn(1, H, S, d, generator=g).to(torch.bfloat16)
+    case(f"train step full size S={S} d={d} H={H}")
+    out, out_hp, lse = gpu.fp4_attention_fwd_train(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    dq, dk, dv = gpu.fp4_attention_bwd(q.cuda(), k.cuda(), v.cuda(), out_hp, lse, do.cuda(), causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 13, 31):
+        sl = slice(h, h + 1)
+        r = oracle.attention_train(q[:, sl], k[:, sl], v[:, sl], do[:, sl], causal=True, kv_tile=128)
+        # the FP4 output against the forward oracle's rows with their rounding-ambiguity bounds
+        # (peaked rows whose P codes sit on a rounding boundary, from the outlier channels)
+        ref, _, amb = oracle.attention_fwd(q[:, sl], k[:, sl], v[:, sl], causal=True, kv_tile=128,
+                                           tie_slack=TIE_SLACK)
+        assert_close_attn_rows(out[:, sl].cpu().numpy().reshape(-1, d), ref.reshape(-1, d), amb.reshape(-1),
+                               f"out head {h}")
+        assert_close_attn(out_hp[:, sl].cpu().numpy().reshape(-1, d), r["out_hp"].reshape(-1, d), f"out_hp head {h}")
+        np.testing.assert_allclose(lse[:, sl].cpu().numpy().reshape(-1), r["lse"].reshape(-1), atol=1e-3)
+        _close_grad(dv[:, sl].cpu().numpy(), r["dv"], f"dv head {h}")
+        _close_grad(dq[:, sl].cpu().numpy(), r["dq"], f"dq head {h}")
+        _close_grad(dk[:, sl].cpu().numpy(), r["dk"], f"dk head {h}")
