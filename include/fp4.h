@@ -220,7 +220,8 @@ typedef struct fp4_attn_opts {
  * denominator sums the unquantized e.  lse [B,H,Sq] (nullable) receives the
  * natural-log sum of exp of the scaled scores.
  * Selection (fp16_budget_pct > 0): per query block i of sel_block rows, the
- * visible key blocks j are scored by mean(q_i) . mean(k_j) in binary64 and the
+ * visible key blocks j are scored by mean(q_i) . mean(k_j) in binary64 (one
+ * fused multiply-add per channel, ascending channels) and the
  * ceil(pct * n_i / 100) best are kept (ties: lower j).  topk_idx
  * [B,H,ceil(Sq/sel_block),kmax] (ascending, -1 padded, kmax =
  * ceil(pct * ceil(Sk/sel_block) / 100)) and topk_cnt [B,H,ceil(Sq/sel_block)]
@@ -401,7 +402,8 @@ int fp4_attention_decode_noalloc(const void* q, int64_t Hq, const fp4_kv_cache* 
  * / 2, applied to one query token).  For every (batch, kv head) the middle is
  * cut into blocks of FP4_DECODE_SEL_BLOCK tokens from its first token (the
  * last one may be short: n_b = ceil(mid_len[b] / 128) blocks).  Block j is
- * scored by qbar . (k_sum[j] / tokens in j) in binary64, ascending channels,
+ * scored by qbar . (k_sum[j] / tokens in j) in binary64, one fused multiply-add
+ * per channel in ascending order,
  * where qbar is the mean of the kv head's G query vectors (reading: the query
  * block of a kv head is the G query tokens that read it).  The
  * ceil(fp16_budget_pct * n_b / 100) best blocks (ties: lower j) are read from
