@@ -47,7 +47,8 @@ class AttnProblem(C.Structure):
                 ("Sq", C.c_int64), ("Sk", C.c_int64), ("d", C.c_int64), ("dtype", C.c_int32),
                 ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
                 ("q_codes", C.c_void_p), ("q_scales", C.c_void_p), ("k_codes", C.c_void_p),
-                ("k_scales", C.c_void_p), ("v_codes", C.c_void_p), ("v_scales", C.c_void_p)]
+                ("k_scales", C.c_void_p), ("v_codes", C.c_void_p), ("v_scales", C.c_void_p),
+                ("q_strides", C.c_int64 * 3), ("k_strides", C.c_int64 * 3), ("v_strides", C.c_int64 * 3)]
 
 
 class AttnOpts(C.Structure):
@@ -178,6 +179,33 @@ def _dev(t, name):
         raise FP4Error(-1, f"{name} must be contiguous")
 
 
+def _dev_rows(t, name):
+    """A 4-D attention input [B, heads, S, d]: a GPU tensor whose rows of d
+    elements are contiguous (other strides are passed to the library)."""
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise FP4Error(-1, f"{name} must be a GPU tensor")
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise FP4Error(-1, f"{name} must be 4-D with contiguous rows (last stride 1)")
+
+
+def _strides(t):
+    """{batch, head, token} element strides of a 4-D input, or zeros when it
+    is dense (the library's default).  Strides of size-1 dimensions never
+    multiply a non-zero index; they are normalized so the library's checks see
+    whole rows."""
+    w = (C.c_int64 * 3)()
+    if t is None or t.is_contiguous():
+        return w
+    B, Hn, S, d = t.shape
+    sb, sh, ss, _ = t.stride()
+    w[0] = 0 if B == 1 else sb
+    w[1] = 0 if Hn == 1 else sh
+    w[2] = d if S == 1 else ss
+    return w
+
+
 def _out(out, shape, dtype, dev, name="out"):
     """The output buffer: allocated when not given; a given one must be a
     contiguous GPU tensor of exactly the dtype and element count the kernel
@@ -269,6 +297,7 @@ def _problem(q, k, v, quant=None):
     Hkv, Sk = (k.shape[1], k.shape[2]) if k is not None else quant["kv_shape"]
     dt = _DT[q.dtype] if q is not None else BF16
     P = AttnProblem(C.sizeof(AttnProblem), B, H, Hkv, Sq, Sk, d, dt, _ptr(q), _ptr(k), _ptr(v))
+    P.q_strides, P.k_strides, P.v_strides = _strides(q), _strides(k), _strides(v)
     if quant is not None:
         for name in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales"):
             setattr(P, name, _ptr(quant[name]))
@@ -287,7 +316,7 @@ def fp4_qk_balance(q, k):
     (fp4.h: fp4_qk_balance).  q [B,H,Sq,d], k [B,Hkv,Sk,d] bf16 or fp16."""
     L = load()
     for t, n in ((q, "q"), (k, "k")):
-        _dev(t, n)
+        _dev_rows(t, n)
     P = _problem(q, k, k)
     B, Hkv, d = k.shape[0], k.shape[1], k.shape[3]
     e = torch.empty((B, Hkv, d), dtype=torch.int32, device=q.device)
@@ -301,7 +330,7 @@ def fp4_block_topk(q, k, causal=True, fp16_budget_pct=10, sel_block=128, kv_tile
     """Block selection alone: returns (idx [B,H,nqb,kmax], cnt [B,H,nqb])."""
     L = load()
     for t, n in ((q, "q"), (k, "k")):
-        _dev(t, n)
+        _dev_rows(t, n)
     P = _problem(q, k, k)
     O = _opts(causal, 0.0, kv_tile, True, -2, 6, fp16_budget_pct, sel_block, FP32)
     B, H, Sq = q.shape[:3]
@@ -334,7 +363,7 @@ def fp4_attention_fwd(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, sca
     fp4_block_topk, used instead of computing one.  Returns (out, lse[, idx, cnt])."""
     L = load()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+        _dev_rows(t, n)
     ref = q if q is not None else quantized["q_codes"]
     dev = ref.device
     if q is not None:
@@ -373,7 +402,7 @@ def fp4_attention_fwd_mx(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, 
     fp4_mx_quantize plus q_shape/kv_shape.  Returns (out, lse)."""
     L = load()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+        _dev_rows(t, n)  # (the library rejects strided inputs here)
     ref = q if q is not None else quantized["q_codes"]
     dev = ref.device
     B, H, Sq, d = q.shape if q is not None else quantized["q_shape"]
@@ -393,7 +422,7 @@ def fp4_attention_fwd_train(q, k, v, causal=False, softmax_scale=0.0, kv_tile=12
     out_hp the high-precision output O' kept for the backward."""
     L = load()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
+        _dev_rows(t, n)
     B, H, Sq, d = q.shape
     P = _problem(q, k, v)
     O = _opts(causal, softmax_scale, kv_tile, scale_search, f_min, f_max, 0, 128, out_dtype,
@@ -413,8 +442,10 @@ def fp4_attention_bwd(q, k, v, out_hp, lse, dout, causal=False, softmax_scale=0.
     """Training backward: (dq, dk, dv) in float32 from fp4_attention_fwd_train's
     out_hp and lse and the output gradient dout (q's dtype)."""
     L = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out_hp, "out_hp"), (lse, "lse"), (dout, "dout")):
+    for t, n in ((out_hp, "out_hp"), (lse, "lse"), (dout, "dout")):
         _dev(t, n)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_rows(t, n)
     B, H, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     hp_dtype = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}[out_hp.dtype]

@@ -135,6 +135,45 @@ AttnPlan plan_attn(const fp4_attn_problem* p, const fp4_attn_opts* o) {
   return P;
 }
 
+// Row maps of q, k and v: the problem's strides, or dense where all three of a
+// tensor's strides are zero.
+struct Maps {
+  TokMap q, k, v;
+  bool strided = false;  // some tensor is not dense
+};
+
+Maps maps_of(const fp4_attn_problem* p) {
+  Maps m;
+  m.q = dense_map(p->H, p->Sq, p->d);
+  m.k = dense_map(p->Hkv, p->Sk, p->d);
+  m.v = dense_map(p->Hkv, p->Sk, p->d);
+  auto set = [&](TokMap& t, const int64_t st[3]) {
+    if (!st[0] && !st[1] && !st[2]) return;
+    if (st[0] != t.bs || st[1] != t.hs || st[2] != t.ts) m.strided = true;
+    t.bs = st[0];
+    t.hs = st[1];
+    t.ts = st[2];
+  };
+  set(m.q, p->q_strides);
+  set(m.k, p->k_strides);
+  set(m.v, p->v_strides);
+  return m;
+}
+
+// Strides of one high-precision input: none, or all three with whole 16-byte
+// rows (multiples of 8 elements), token rows at least d apart, and (k, v) one
+// head's rows within 32-bit byte offsets.
+int check_strides(const int64_t st[3], int64_t S, int64_t d, bool kv, const char* fn, const char* name) {
+  if (!st[0] && !st[1] && !st[2]) return FP4_OK;
+  if (st[0] < 0 || st[1] < 0 || st[2] < d)
+    return fail(FP4_ERR_INVALID_ARG, "%s: %s strides must be >= 0 with the token stride >= d", fn, name);
+  if (st[0] % 8 || st[1] % 8 || st[2] % 8)
+    return fail(FP4_ERR_INVALID_ARG, "%s: %s strides must be multiples of 8 elements (16-byte rows)", fn, name);
+  if (kv && ((S - 1) * st[2] + d) * 2 >= ((int64_t)1 << 31))
+    return fail(FP4_ERR_UNSUPPORTED, "%s: %s token stride too large for one head's 32-bit offsets", fn, name);
+  return FP4_OK;
+}
+
 int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn, bool for_topk) {
   if (!p || !o) return fail(FP4_ERR_INVALID_ARG, "%s: problem or opts is NULL", fn);
   if (p->struct_size < sizeof(fp4_attn_problem) || o->struct_size < sizeof(fp4_attn_opts))
@@ -183,7 +222,10 @@ int check_attn(const fp4_attn_problem* p, const fp4_attn_opts* o, const char* fn
   const void* ptrs[] = {p->q, p->k, p->v, p->q_codes, p->q_scales, p->k_codes, p->k_scales, p->v_codes, p->v_scales};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(FP4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-  return FP4_OK;
+  int st = check_strides(p->q_strides, p->Sq, p->d, false, fn, "q");
+  if (!st) st = check_strides(p->k_strides, p->Sk, p->d, true, fn, "k");
+  if (!st) st = check_strides(p->v_strides, p->Sk, p->d, true, fn, "v");
+  return st;
 }
 
 }  // namespace
@@ -298,6 +340,9 @@ static int launch_selection(const fp4_attn_problem* p, const fp4_attn_opts* o, c
   T.pct = o->fp16_budget_pct;
   T.sel_block = o->sel_block;
   T.nqb = P.nqb; T.nkb = P.nkb; T.kmax = P.kmax;
+  const Maps m = maps_of(p);
+  T.qmap = m.q;
+  T.kmap = m.k;
   T.qmeans = (double*)(ws_sel);
   T.kmeans = (double*)(ws_sel + (P.km - P.qm));
   T.idx = idx ? idx : (int32_t*)(ws_sel + (P.idx - P.qm));
@@ -325,9 +370,14 @@ int fp4_qk_balance(const fp4_attn_problem* prob, int32_t* exponents, void* works
   if (!aligned16(prob->q) || !aligned16(prob->k)) return fail(FP4_ERR_INVALID_ARG, "%s: q, k must be 16-byte aligned", fn);
   const size_t need = fp4_qk_balance_workspace_size(prob);
   if (workspace_bytes < need || !workspace) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  int st = check_strides(prob->q_strides, prob->Sq, prob->d, false, fn, "q");
+  if (!st) st = check_strides(prob->k_strides, prob->Sk, prob->d, true, fn, "k");
+  if (st) return st;
+  const Maps m = maps_of(prob);
   BalanceLaunch BL{};
   BL.q = prob->q; BL.k = prob->k; BL.dtype = prob->dtype;
   BL.B = prob->B; BL.H = prob->H; BL.Hkv = prob->Hkv; BL.Sq = prob->Sq; BL.Sk = prob->Sk; BL.d = prob->d;
+  BL.qmap = m.q; BL.kmap = m.k;
   BL.partial = (double*)workspace;
   BL.exps = exponents;
   return hip_status(fp4i_launch_balance(BL, (hipStream_t)stream), "fp4_qk_balance launch");
@@ -365,6 +415,7 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
   const int64_t B = prob->B, H = prob->H, Hkv = prob->Hkv, Sq = prob->Sq, Sk = prob->Sk, d = prob->d;
   const uint8_t *qc = prob->q_codes, *qs = prob->q_scales, *kc = prob->k_codes, *ks = prob->k_scales,
                 *vc = prob->v_codes, *vs = prob->v_scales;
+  const Maps maps = maps_of(prob);
   if (P.need_quant) {
     QuantLaunch L{};
     L.dtype = prob->dtype;
@@ -374,6 +425,8 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
     L.gmode = 0;
     L.cols = d;
     L.ld = d;
+    L.strided = maps.strided ? 1 : 0;
+    L.map = maps.q;
     L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
     L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
     L.hadamard = opts->hadamard_qk;  // Q and K only; V is never rotated
@@ -384,6 +437,7 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
       BalanceLaunch BL{};
       BL.q = prob->q; BL.k = prob->k; BL.dtype = prob->dtype;
       BL.B = B; BL.H = H; BL.Hkv = Hkv; BL.Sq = Sq; BL.Sk = Sk; BL.d = d;
+      BL.qmap = maps.q; BL.kmap = maps.k;
       BL.partial = (double*)(ws + P.bpart);
       BL.exps = (int32_t*)(ws + P.bexp);
       e = fp4i_launch_balance(BL, s);
@@ -402,6 +456,7 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
     if (e == hipSuccess) e = fp4i_launch_quantize(L, s);
     if (e == hipSuccess) {
       L.x = prob->k; L.rows = B * Hkv * Sk;
+      L.map = maps.k;
       L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
       L.exp_negate = 0;
       L.exp_rows = Sk;
@@ -414,6 +469,7 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
     }
     if (e == hipSuccess) {
       L.x = prob->v; L.axis = 1; L.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
+      L.map = maps.v;
       L.cexp = nullptr;
       L.means = nullptr;
       L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
@@ -441,6 +497,8 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
   A.B = B; A.H = H; A.Hkv = Hkv; A.Sq = Sq; A.Sk = Sk; A.d = d;
   A.dtype = prob->dtype;
   A.q = prob->q; A.k = prob->k; A.v = prob->v;
+  A.qmap = maps.q; A.kmap = maps.k; A.vmap = maps.v;
+  A.strided = maps.strided ? 1 : 0;
   A.qc = qc; A.qs = qs; A.kc = kc; A.ks = ks; A.vc = vc; A.vs = vs;
   A.causal = opts->causal;
   A.c = score_factor(opts->softmax_scale, d);
@@ -493,6 +551,7 @@ int fp4_attention_fwd_mx(const fp4_attn_problem* prob, const fp4_attn_opts* opts
   if (opts->hadamard_qk) return fail(FP4_ERR_INVALID_ARG, "%s: hadamard_qk must be 0", fn);
   if (opts->balance_qk) return fail(FP4_ERR_INVALID_ARG, "%s: balance_qk must be 0", fn);
   if (prob->Sk % 32) return fail(FP4_ERR_INVALID_ARG, "%s: Sk %% 32 != 0", fn);
+  if (maps_of(prob).strided) return fail(FP4_ERR_UNSUPPORTED, "%s: q, k, v must be dense", fn);
   if (!out || !aligned16(out)) return fail(FP4_ERR_INVALID_ARG, "%s: out must be non-NULL and 16-byte aligned", fn);
   const size_t need = fp4_attention_fwd_mx_workspace_size(prob, opts);
   if (workspace_bytes < need || (need && !workspace)) return fail(FP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
@@ -558,6 +617,7 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
   const uint8_t *qc = prob->q_codes, *qs = prob->q_scales, *kc = prob->k_codes, *ks = prob->k_scales,
                 *vc = prob->v_codes, *vs = prob->v_scales;
   if (P.need_quant) {  // the forward's quantization, repeated
+    const Maps maps = maps_of(prob);
     QuantLaunch L{};
     L.dtype = prob->dtype;
     L.search = opts->scale_search;
@@ -565,16 +625,20 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
     L.fmax = opts->f_max;
     L.cols = d;
     L.ld = d;
+    L.strided = maps.strided ? 1 : 0;
+    L.map = maps.q;
     L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
     L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
     hipError_t e = fp4i_launch_quantize(L, s);
     if (e == hipSuccess) {
       L.x = prob->k; L.rows = B * Hkv * Sk;
+      L.map = maps.k;
       L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
       e = fp4i_launch_quantize(L, s);
     }
     if (e == hipSuccess) {
       L.x = prob->v; L.axis = 1;
+      L.map = maps.v;
       L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
       e = fp4i_launch_quantize(L, s);
     }

@@ -221,6 +221,7 @@ struct Problem {
   int64_t H, Hkv, Sq, Sk;
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
   const void *q, *k, *v;
+  TokMap qmap, kmap, vmap;  // token rows of q, k, v (the FP16 path)
   const int32_t *idx, *cnt;
   int causal, pct, sel_block, nqb, kmax, nqt;
   float c;
@@ -357,20 +358,22 @@ struct Stage16Map {
   static __device__ __forceinline__ int v_c8(int it) { return 2 * v_grp() + ((((threadIdx.x >> 6) + 4 * it)) & 1); }
 };
 
+// kts, vts: elements between consecutive tokens of K and V
 template <int D>
-__device__ __forceinline__ void fetch16(Fetch16<D>& G, rsrc_t kr16, rsrc_t vr16, int64_t key0) {
+__device__ __forceinline__ void fetch16(Fetch16<D>& G, rsrc_t kr16, rsrc_t vr16, uint32_t kts, uint32_t vts,
+                                        int64_t key0) {
   using M = Stage16Map<D>;
 #pragma unroll
   for (int u = 0; u < Fetch16<D>::NKU; ++u) {
     const uint32_t key = (uint32_t)key0 + M::k_row(u);
-    G.k[u] = buf_load16(kr16, (key * D + M::k_dc(u) * 8) * 2);
+    G.k[u] = buf_load16(kr16, (key * kts + M::k_dc(u) * 8) * 2);
   }
 #pragma unroll
   for (int it = 0; it < Fetch16<D>::NVU; ++it) {
     const uint32_t key = (uint32_t)key0 + 2 * M::v_pair(it);
     const int c8 = M::v_c8(it);
-    G.v0[it] = buf_load16(vr16, (key * D + c8 * 8) * 2);
-    G.v1[it] = buf_load16(vr16, ((key + 1) * D + c8 * 8) * 2);
+    G.v0[it] = buf_load16(vr16, (key * vts + c8 * 8) * 2);
+    G.v1[it] = buf_load16(vr16, ((key + 1) * vts + c8 * 8) * 2);
   }
 }
 
@@ -738,7 +741,9 @@ struct SelCursor {
 // PM: P on the FP4 tiles -- 0 two-level, 1 single-level, 2 unquantized
 // (fp16 probabilities with the FP4 operands: the high-precision output O' of
 // training, Attn-QAT page, Metodologia / A).
-template <int D, int BC, typename IT, typename OT, int PM>
+// STR: q, k, v rows through their row maps (strided inputs; only the FP16
+// path reads them), else dense.
+template <int D, int BC, typename IT, typename OT, int PM, bool STR>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   __shared__ Smem<D, BC> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
@@ -883,20 +888,25 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   // ---- FP16 pass over the selected blocks
   if (nsel > 0) {
     // fp16 Q fragment from the original input
-    const IT* qp = reinterpret_cast<const IT*>(P.q) + bh * P.Sq * D;
+    const IT* qp = reinterpret_cast<const IT*>(P.q) + (STR ? P.qmap.head_off(bh) : bh * P.Sq * D);
+    const int64_t qts = STR ? P.qmap.ts : D;
     const bool ok = qrow < P.Sq;
     uint4_t qw[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qw[s] = *reinterpret_cast<const uint4_t*>(qp + (ok ? qrow : 0) * D + 16 * s + 8 * hi);
+      qw[s] = *reinterpret_cast<const uint4_t*>(qp + (ok ? qrow : 0) * qts + 16 * s + 8 * hi);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       uint4_t w = ok ? qw[s] : uint4_t{0, 0, 0, 0};
       half2_t a = to_half2<IT>(w[0]), bb = to_half2<IT>(w[1]), cc = to_half2<IT>(w[2]), dd = to_half2<IT>(w[3]);
       qf[s] = half8_t{a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
     }
-    const rsrc_t kr16 = make_rsrc(reinterpret_cast<const IT*>(P.k) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
-    const rsrc_t vr16 = make_rsrc(reinterpret_cast<const IT*>(P.v) + bhk * Sk * D, (uint32_t)(Sk * D * 2));
+    // one head's token rows (the host checks that (Sk - 1) ts + D elements fit 32-bit byte offsets)
+    const uint32_t kts = STR ? (uint32_t)P.kmap.ts : D, vts = STR ? (uint32_t)P.vmap.ts : D;
+    const rsrc_t kr16 = make_rsrc(reinterpret_cast<const IT*>(P.k) + (STR ? P.kmap.head_off(bhk) : bhk * Sk * D),
+                                  (uint32_t)(((Sk - 1) * kts + D) * 2));
+    const rsrc_t vr16 = make_rsrc(reinterpret_cast<const IT*>(P.v) + (STR ? P.vmap.head_off(bhk) : bhk * Sk * D),
+                                  (uint32_t)(((Sk - 1) * vts + D) * 2));
     // steps of the selected blocks in list order, each fetched into
     // registers while the step before it computes
     constexpr int ST = kStepKeys<D>;
@@ -904,12 +914,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
     const int64_t wrow0 = q0 + 32 * wave;
     Fetch16<D> G;
     int64_t key0 = cur.next();
-    if (key0 >= 0) fetch16<D>(G, kr16, vr16, key0);
+    if (key0 >= 0) fetch16<D>(G, kr16, vr16, kts, vts, key0);
     while (key0 >= 0) {
       const int64_t nxt = cur.next();
       __syncthreads();  // previous step's LDS reads are done
       stage16<D, BC, IT>(G, S);
-      if (nxt >= 0) fetch16<D>(G, kr16, vr16, nxt);
+      if (nxt >= 0) fetch16<D>(G, kr16, vr16, kts, vts, nxt);
       __syncthreads();
       fp16_step<D, BC, ST>(S, qf, R, key0, wrow0, qrow, Sk, P.causal, P.c);
       key0 = nxt;
@@ -934,12 +944,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(Problem P) {
   }
 }
 
+template <int D, int BC, typename IT, int PM, bool STR>
+hipError_t launch_str(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
+  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float, PM, STR>), grid, dim3(256), 0, st, P);
+  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t, PM, STR>), grid, dim3(256), 0, st, P);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t, PM, STR>), grid, dim3(256), 0, st, P);
+  return hipGetLastError();
+}
+
+// The strided instances only where the FP16 path runs (a budget; P modes 0
+// and 1): without it the kernel reads only the quantized operands.
 template <int D, int BC, typename IT, int PM>
 hipError_t launch_out(const AttnLaunch& L, const Problem& P, dim3 grid, hipStream_t st) {
-  if (L.out_dtype == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, float, PM>), grid, dim3(256), 0, st, P);
-  else if (L.out_dtype == 1) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, half_t, PM>), grid, dim3(256), 0, st, P);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, IT, uint16_t, PM>), grid, dim3(256), 0, st, P);
-  return hipGetLastError();
+  if constexpr (PM != 2) {
+    if (L.strided && L.pct > 0) return launch_str<D, BC, IT, PM, true>(L, P, grid, st);
+  }
+  return launch_str<D, BC, IT, PM, false>(L, P, grid, st);
 }
 
 template <int D, int BC>
@@ -966,6 +986,7 @@ hipError_t fp4i_launch_attn_fwd(const AttnLaunch& L, hipStream_t st) {
   P.H = L.H; P.Hkv = L.Hkv; P.Sq = L.Sq; P.Sk = L.Sk;
   P.qc = L.qc; P.qs = L.qs; P.kc = L.kc; P.ks = L.ks; P.vc = L.vc; P.vs = L.vs;
   P.q = L.q; P.k = L.k; P.v = L.v;
+  P.qmap = L.qmap; P.kmap = L.kmap; P.vmap = L.vmap;
   P.idx = L.idx; P.cnt = L.cnt;
   P.causal = L.causal; P.pct = L.pct; P.sel_block = L.pct > 0 ? L.sel_block : 128;
   P.nqb = L.nqb; P.kmax = L.kmax;

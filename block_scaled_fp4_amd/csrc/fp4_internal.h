@@ -3,6 +3,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Element offsets of the token rows of a [B, Hn, S, d] tensor with strides
+// (token ts, head hs, batch bs; the d elements of a row are contiguous).
+// Dense: ts = d, hs = S d, bs = Hn S d.
+struct TokMap {
+  int64_t ts = 0, hs = 0, bs = 0;
+  int64_t S = 1, Hn = 1;
+  __host__ __device__ int64_t head_off(int64_t bh) const { return (bh / Hn) * bs + (bh % Hn) * hs; }
+  __host__ __device__ int64_t row_off(int64_t r) const {
+    const int64_t bh = r / S;
+    return head_off(bh) + (r - bh * S) * ts;
+  }
+};
+
+inline TokMap dense_map(int64_t Hn, int64_t S, int64_t d) {
+  TokMap m;
+  m.ts = d;
+  m.hs = S * d;
+  m.bs = Hn * S * d;
+  m.S = S;
+  m.Hn = Hn;
+  return m;
+}
+
 struct QuantLaunch {
   const void* x;
   int dtype;  // 0 bf16, 1 fp16, 2 fp32
@@ -26,6 +49,9 @@ struct QuantLaunch {
   double* means = nullptr;
   int64_t mS = 0;
   int mblk = 0, mnb = 0;
+  // strided rows (attention inputs): row r at map.row_off(r) instead of r * ld
+  int strided = 0;
+  TokMap map;
 };
 
 // Balance exponents: per (batch, kv head) binary64 partial sums of squares of
@@ -35,6 +61,7 @@ struct BalanceLaunch {
   const void* k;  // [B, Hkv, Sk, d]
   int dtype;      // 0 bf16, 1 fp16
   int64_t B, H, Hkv, Sq, Sk, d;
+  TokMap qmap, kmap;  // row offsets of q and k
   double* partial;  // fp4i_balance_partials doubles
   int32_t* exps;    // [B, Hkv, d]
 };
@@ -71,6 +98,7 @@ struct TopkLaunch {
   double* qmeans;  // [B*H, nqb, d]
   double* kmeans;  // [B*Hkv, nkb, d]
   int means_ready = 0;  // 1: the quantizer already wrote both
+  TokMap qmap, kmap;    // row offsets of q and k (for the means)
   uint64_t* keys;  // [B*H, nqb, nkb] order-preserving keys of the block scores
   int32_t* idx;    // [B*H, nqb, kmax]
   int32_t* cnt;    // [B*H, nqb]
@@ -84,6 +112,8 @@ struct AttnLaunch {
   const void* q;
   const void* k;
   const void* v;
+  TokMap qmap, kmap, vmap;  // row offsets of q, k, v (the FP16 path reads them)
+  int strided = 0;          // some of them is not dense
   const uint8_t* qc;
   const uint8_t* qs;
   const uint8_t* kc;

@@ -45,6 +45,10 @@ struct QuantArgs {
   double* means;  // block means of the input (quantize_means_kernel): [rows / mS][mnb][cols]
   int64_t mS;     // rows per head
   int mblk, mnb;  // rows per selection block, blocks per head
+  int strided;    // rows at map.row_off(r) (attention inputs with strides), else r * ld
+  TokMap map;
+  __device__ __forceinline__ int64_t row_off(int64_t r) const { return strided ? map.row_off(r) : r * ld; }
+  __device__ __forceinline__ int64_t row_step() const { return strided ? map.ts : ld; }
 };
 
 // Magnitude balance of one block (ScaleSearch page, Metodologia /
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   auto src = [&](int64_t blk) {
     const int64_t r = blk / bpr, cb = blk - r * bpr;
-    return x + r * A.ld + cb * 16;
+    return x + A.row_off(r) + cb * 16;
   };
   int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   RawBlock<T> raw;
@@ -228,7 +232,9 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
   const int64_t t0 = ib * A.mblk;
   const int64_t n = (t0 + A.mblk < A.mS ? t0 + A.mblk : A.mS) - t0;
   const int64_t row0 = head * A.mS + t0;
-  const T* x = reinterpret_cast<const T*>(A.x);
+  // the unit's rows lie in one head: the first at row_off(row0), then a fixed step
+  const T* x = reinterpret_cast<const T*>(A.x) + A.row_off(row0);
+  const int64_t step = A.row_step();
   const int c = threadIdx.x;
   double sum = 0.0;
   constexpr int kMaxPer = kMeansRows * 8 / 256;  // blocks per thread and chunk at cols = 128
@@ -239,7 +245,7 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
       const int64_t i = threadIdx.x + 256 * j;
-      if (i < nblk) load_raw<T>(raw[j], x + (row0 + r0 + i / bpr) * A.ld + (i % bpr) * 16);
+      if (i < nblk) load_raw<T>(raw[j], x + (r0 + i / bpr) * step + (i % bpr) * 16);
     }
     __syncthreads();  // the previous chunk's sums have read the rows; the table is in place
 #pragma unroll
@@ -302,10 +308,13 @@ __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
   for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nb;
        blk += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rb = blk / A.cols, c = blk - rb * A.cols;
+    // the block's 16 rows lie in one head (heads hold whole blocks)
+    const T* xb = x + A.row_off(rb * 16) + c;
+    const int64_t step = A.row_step();
     float y[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float v = load_elem<T>(x + (rb * 16 + k) * A.ld + c);
+      const float v = load_elem<T>(xb + k * step);
       y[k] = A.gmode != 0 ? v * ginv : v;
     }
     uint32_t codes[2], scale;
@@ -487,9 +496,9 @@ void launch_axis0(int dtype, int64_t grid, const QuantArgs& A, hipStream_t strea
 constexpr int kBalRows = 256;
 
 template <typename T>
-__global__ void __launch_bounds__(256) balance_partial_kernel(const T* q, const T* k, int64_t H, int64_t Hkv,
-                                                              int64_t Sq, int64_t Sk, int d, int nchunk,
-                                                              double* partial) {
+__global__ void __launch_bounds__(256) balance_partial_kernel(const T* q, const T* k, TokMap qmap, TokMap kmap,
+                                                              int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int d,
+                                                              int nchunk, double* partial) {
   __shared__ double red[32][128];
   const int64_t G = H / Hkv;
   const int64_t gi = blockIdx.x;  // ((bk * 2 + side) * nchunk + chunk)
@@ -498,7 +507,14 @@ __global__ void __launch_bounds__(256) balance_partial_kernel(const T* q, const 
   const int64_t bk = gi / (2 * nchunk);
   const int64_t b = bk / Hkv, hk = bk - b * Hkv;
   const int64_t nrows = side == 0 ? G * Sq : Sk;
-  const T* base = side == 0 ? q + (b * H + hk * G) * Sq * d : k + bk * Sk * d;
+  // row r of the side: query head b H + hk G + r / Sq, token r % Sq (Q), or token r of kv head bk (K)
+  auto row_ptr = [&](int64_t r) {
+    if (side == 0) {
+      const int64_t g = r / Sq;
+      return q + qmap.head_off(b * H + hk * G + g) + (r - g * Sq) * qmap.ts;
+    }
+    return k + kmap.head_off(bk) + r * kmap.ts;
+  };
   const int per = d / 8;                 // threads per row
   const int rgroups = 256 / per;         // rows in flight per pass (16 or 32)
   const int c0 = (threadIdx.x % per) * 8, rg = threadIdx.x / per;
@@ -508,7 +524,7 @@ __global__ void __launch_bounds__(256) balance_partial_kernel(const T* q, const 
   const int64_t r0 = (int64_t)chunk * kBalRows;
   const int64_t r1 = r0 + kBalRows < nrows ? r0 + kBalRows : nrows;
   for (int64_t r = r0 + rg; r < r1; r += rgroups) {
-    const uint4_t w = *reinterpret_cast<const uint4_t*>(base + r * d + c0);
+    const uint4_t w = *reinterpret_cast<const uint4_t*>(row_ptr(r) + c0);
     float y[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -581,6 +597,7 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
     if (L.g && L.gmode != 2) hipLaunchKernelGGL(set_one_kernel, dim3(1), dim3(1), 0, stream, L.g);
     return hipGetLastError();
   }
+  if (L.strided && L.gmode == 1) return hipErrorInvalidValue;  // the amax pass reads dense rows
   if (L.gmode == 1) {
     A.n_part = fp4i_amax_parts(L.rows, L.cols);
     if (L.dtype == 0)
@@ -608,6 +625,8 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
   A.mS = L.mS;
   A.mblk = L.mblk;
   A.mnb = L.mnb;
+  A.strided = L.strided;
+  A.map = L.map;
   if (L.means) {  // axis 0, bf16/fp16, cols <= 128, no per-tensor scale (checked by the caller)
     const bool had = L.hadamard != 0, bal = L.cexp != nullptr;
     const dim3 g((unsigned)((L.rows / L.mS) * L.mnb));
@@ -673,10 +692,10 @@ hipError_t fp4i_launch_balance(const BalanceLaunch& L, hipStream_t stream) {
   const dim3 grid((unsigned)(n_bk * 2 * nchunk));
   if (L.dtype == 0)
     hipLaunchKernelGGL(balance_partial_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t*)L.q,
-                       (const uint16_t*)L.k, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
+                       (const uint16_t*)L.k, L.qmap, L.kmap, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
   else
     hipLaunchKernelGGL(balance_partial_kernel<half_t>, grid, dim3(256), 0, stream, (const half_t*)L.q,
-                       (const half_t*)L.k, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
+                       (const half_t*)L.k, L.qmap, L.kmap, L.H, L.Hkv, L.Sq, L.Sk, (int)L.d, nchunk, L.partial);
   hipLaunchKernelGGL(balance_exp_kernel, dim3((unsigned)((n_bk * L.d + 127) / 128)), dim3(128), 0, stream, L.partial,
                      n_bk, G, L.Sq, L.Sk, (int)L.d, nchunk, L.exps);
   return hipGetLastError();

@@ -40,6 +40,7 @@ __device__ __forceinline__ double elem8<half_t>(const uint4_t& w, int e) {
 template <typename T>
 struct MeansArgs {
   const T *q, *k;
+  TokMap qmap, kmap;  // row offsets of q and k
   int64_t Sq, Sk, nunits_q, nunits_k;
   int d, blk, nqb, nkb;
   double *qmeans, *kmeans;
@@ -53,6 +54,7 @@ __global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
   if (!isq) u -= A.nunits_q;
   if (!isq && u >= A.nunits_k) return;
   const T* x = isq ? A.q : A.k;
+  const TokMap& map = isq ? A.qmap : A.kmap;
   const int64_t S = isq ? A.Sq : A.Sk;
   const int nb = isq ? A.nqb : A.nkb;
   double* means = isq ? A.qmeans : A.kmeans;
@@ -61,7 +63,8 @@ __global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
   const int64_t head = u / nb, ib = u - head * nb;
   const int64_t t0 = ib * blk;
   const int64_t n = (t0 + blk < S ? t0 + blk : S) - t0;
-  const T* p = x + (head * S + t0) * d + c0;
+  const T* p = x + map.head_off(head) + t0 * map.ts + c0;
+  const int64_t ts = map.ts;
   double s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0;
@@ -69,14 +72,14 @@ __global__ void __launch_bounds__(256) block_means_kernel(MeansArgs<T> A) {
   for (; t + 16 <= n; t += 16) {
     uint4_t w[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) w[v] = *reinterpret_cast<const uint4_t*>(p + (t + v) * d);
+    for (int v = 0; v < 16; ++v) w[v] = *reinterpret_cast<const uint4_t*>(p + (t + v) * ts);
 #pragma unroll
     for (int v = 0; v < 16; ++v)
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] = s[e] + elem8<T>(w[v], e);
   }
   for (; t < n; ++t) {
-    const uint4_t w = *reinterpret_cast<const uint4_t*>(p + t * d);
+    const uint4_t w = *reinterpret_cast<const uint4_t*>(p + t * ts);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = s[e] + elem8<T>(w, e);
   }
@@ -594,6 +597,8 @@ hipError_t launch_means(const TopkLaunch& L, hipStream_t stream) {
   A.blk = L.sel_block;
   A.nqb = L.nqb;
   A.nkb = L.nkb;
+  A.qmap = L.qmap;
+  A.kmap = L.kmap;
   A.qmeans = L.qmeans;
   A.kmeans = L.kmeans;
   const int upw = 256 / (A.d / 8);  // (head, block) units per workgroup

@@ -163,9 +163,10 @@ typedef struct fp4_attn_problem {
   int64_t B, H, Hkv;    /* batch, query heads, key/value heads (H % Hkv == 0) */
   int64_t Sq, Sk, d;    /* query / key lengths, head dimension (64 or 128) */
   int32_t dtype;        /* FP4_BF16 or FP4_FP16 for q, k, v */
-  /* high-precision inputs, dense: q [B,H,Sq,d], k and v [B,Hkv,Sk,d].
-     Needed unless all six quantized arrays below are given; always needed
-     when fp16_budget_pct > 0 (block means and the FP16 path read them). */
+  /* high-precision inputs: q [B,H,Sq,d], k and v [B,Hkv,Sk,d], dense unless
+     their strides below are given.  Needed unless all six quantized arrays
+     below are given; always needed when fp16_budget_pct > 0 (block means and
+     the FP16 path read them). */
   const void* q;
   const void* k;
   const void* v;
@@ -180,6 +181,18 @@ typedef struct fp4_attn_problem {
   const uint8_t* k_scales;
   const uint8_t* v_codes;
   const uint8_t* v_scales;
+  /* Element strides {batch, head, token} of q, k and v; all three zero means
+     dense.  A token's d elements stay contiguous.  Strides must be >= 0, the
+     token stride >= d, all multiples of 8 elements (whole 16-byte rows), and
+     for k and v ((S - 1) * token stride + d) * 2 < 2^31.  Example, a fused
+     projection [B, S, H + 2 Hkv, d]: q = base, k = base + H d,
+     v = base + (H + Hkv) d, each with strides {S (H + 2 Hkv) d, d,
+     (H + 2 Hkv) d}.  Read by the call's own quantization, the block means,
+     the balance exponents and the FP16 path, in the same launches as dense
+     inputs (no copy); fp4_attention_fwd_mx needs dense inputs. */
+  int64_t q_strides[3];
+  int64_t k_strides[3];
+  int64_t v_strides[3];
 } fp4_attn_problem;
 
 typedef struct fp4_attn_opts {

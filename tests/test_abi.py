@@ -290,3 +290,48 @@ def test_balance_options_are_validated(L):
     assert L.fp4_qk_balance(C.byref(Pq), None, fake, need, None) == -1
     P64 = _prob(fp4, d=96)
     assert L.fp4_qk_balance(C.byref(P64), fake, fake, 1 << 30, None) == -2
+
+
+def test_strides_are_validated(L):
+    """Strided q, k, v (fp4.h, fp4_attn_problem strides): token rows at least d
+    apart, whole 16-byte rows, non-negative strides, one K/V head within 32-bit
+    offsets; the MXFP4 entry point takes dense inputs only."""
+    import block_scaled_fp4_amd as fp4
+    fake = C.c_void_p(1 << 20)
+    O = fp4._opts(True, 0.0, 128, True, -2, 6, 0, 128, fp4.FP32)
+
+    def run(**st):
+        P = _prob(fp4)
+        for name, val in st.items():
+            setattr(P, name, (C.c_int64 * 3)(*val))
+        return L.fp4_attention_fwd(C.byref(P), C.byref(O), fake, None, None, None, fake, 1 << 40, None)
+
+    d = 128
+    assert run(q_strides=(0, d, d - 8)) == -1           # token stride below d
+    assert "token stride" in L.fp4_last_error().decode()
+    assert run(k_strides=(0, d, 3 * d + 4)) == -1       # rows not 16-byte aligned
+    assert "multiples of 8" in L.fp4_last_error().decode()
+    assert run(v_strides=(-8, d, 3 * d)) == -1          # negative stride
+    assert run(k_strides=(0, 0, 1 << 30)) == -2         # one head past 32-bit offsets
+    O_mx = fp4._opts(True, 0.0, 128, False, -2, 6, 0, 128, fp4.FP32)
+    P = _prob(fp4)
+    P.q_strides = (C.c_int64 * 3)(0, d, 3 * d)
+    assert L.fp4_attention_fwd_mx(C.byref(P), C.byref(O_mx), fake, None, fake, 1 << 40, None) == -2
+    assert "dense" in L.fp4_last_error().decode()
+
+
+def test_binding_strides_of_views():
+    """The binding passes a view's {batch, head, token} strides (zeros when
+    dense; size-1 dimensions normalized) and refuses rows that are not
+    contiguous."""
+    import torch
+    import block_scaled_fp4_amd as fp4
+    B, S, H, Hkv, d = 2, 64, 4, 2, 128
+    buf = torch.zeros((B, S, H + 2 * Hkv, d), dtype=torch.bfloat16)
+    q = buf[:, :, :H].transpose(1, 2)
+    assert list(fp4._strides(q)) == [S * (H + 2 * Hkv) * d, d, (H + 2 * Hkv) * d]
+    assert list(fp4._strides(q.contiguous())) == [0, 0, 0]
+    one = torch.zeros((1, 40, 1, d), dtype=torch.bfloat16)[:, ::2]  # B = 1, one token per head
+    assert list(fp4._strides(one)) == [0, 2 * d, d]
+    with pytest.raises(fp4.FP4Error, match="GPU"):
+        fp4._dev_rows(q, "q")
