@@ -293,41 +293,92 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
   if (c < A.cols) A.means[u * A.cols + c] = sum / (double)n;
 }
 
-// block_axis 1: one lane per block of 16 rows of one column; consecutive
-// lanes take consecutive columns, so each row load of a wavefront is one
-// contiguous segment.
-template <typename T>
+// block_axis 1: one lane per VEC consecutive columns of a group of 16 rows
+// (VEC blocks, searched one after the other); consecutive lanes take
+// consecutive column groups, so each row load of a wavefront is one
+// contiguous segment, and a lane's VEC code bytes of a row pair, scales and
+// offsets go out as one store each (VEC 4: whole columns groups of 4, with
+// cols and the row step multiples of 4; else VEC 1).
+template <typename T, int VEC>
+__device__ __forceinline__ void load_cols(const T* p, float (&v)[VEC]);
+template <>
+__device__ __forceinline__ void load_cols<uint16_t, 1>(const uint16_t* p, float (&v)[1]) { v[0] = bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ void load_cols<half_t, 1>(const half_t* p, float (&v)[1]) { v[0] = (float)*p; }
+template <>
+__device__ __forceinline__ void load_cols<float, 1>(const float* p, float (&v)[1]) { v[0] = *p; }
+template <>
+__device__ __forceinline__ void load_cols<uint16_t, 4>(const uint16_t* p, float (&v)[4]) {
+  const uint2_t w = *reinterpret_cast<const uint2_t*>(p);
+  v[0] = __uint_as_float(w[0] << 16);
+  v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  v[2] = __uint_as_float(w[1] << 16);
+  v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void load_cols<half_t, 4>(const half_t* p, float (&v)[4]) {
+  const half4_t w = *reinterpret_cast<const half4_t*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = (float)w[j];
+}
+template <>
+__device__ __forceinline__ void load_cols<float, 4>(const float* p, float (&v)[4]) {
+  const float4_t w = *reinterpret_cast<const float4_t*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = w[j];
+}
+
+// VEC bytes (byte j from value j) as one store
+template <int VEC>
+__device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&b)[VEC]) {
+  if constexpr (VEC == 1) {
+    *p = (uint8_t)b[0];
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  }
+}
+
+template <typename T, int VEC>
 __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
   __shared__ float2_t tab[128];
   __shared__ float sh[8];
   if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
   const float ginv = global_factor(A, sh);
   __syncthreads();
-  const int64_t nb = (A.rows / 16) * A.cols;
+  const int64_t cv = A.cols / VEC;  // column groups per row
+  const int64_t nu = (A.rows / 16) * cv;
   const T* x = reinterpret_cast<const T*>(A.x);
-  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nb;
-       blk += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t rb = blk / A.cols, c = blk - rb * A.cols;
-    // the block's 16 rows lie in one head (heads hold whole blocks)
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nu; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rb = u / cv, c = (u - rb * cv) * VEC;
+    // the blocks' 16 rows lie in one head (heads hold whole blocks)
     const T* xb = x + A.row_off(rb * 16) + c;
     const int64_t step = A.row_step();
-    float y[16];
+    float y[VEC][16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float v = load_elem<T>(xb + k * step);
-      y[k] = A.gmode != 0 ? v * ginv : v;
+      float v[VEC];
+      load_cols<T, VEC>(xb + k * step, v);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) y[j][k] = A.gmode != 0 ? v[j] * ginv : v[j];
     }
-    uint32_t codes[2], scale;
-    int off;
-    quantize_block(y, A.search, A.fmin, A.fmax, tab, codes, scale, off);
-    // row pair (2i, 2i+1) -> byte i of the block's 8 bytes, at codes8[(rb*8+i)*cols + c]
+    uint32_t codes[VEC][2], scale[VEC], offb[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      int off;
+      quantize_block(y[j], A.search, A.fmin, A.fmax, tab, codes[j], scale[j], off);
+      offb[j] = (uint32_t)(off & 0xFF);
+    }
+    // row pair (2i, 2i+1) of column c + j -> byte i of that block's 8 bytes, at codes8[(rb*8+i)*cols + c + j]
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t byte = (codes[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      A.codes8[(rb * 8 + i) * A.cols + c] = (uint8_t)byte;
+      uint32_t b[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) b[j] = (codes[j][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      store_bytes<VEC>(A.codes8 + (rb * 8 + i) * A.cols + c, b);
     }
-    A.scales[blk] = (uint8_t)scale;
-    if (A.offsets) A.offsets[blk] = (int8_t)off;
+    const int64_t blk = rb * A.cols + c;
+    store_bytes<VEC>(A.scales + blk, scale);
+    if (A.offsets) store_bytes<VEC>(reinterpret_cast<uint8_t*>(A.offsets) + blk, offb);
   }
 }
 
@@ -650,9 +701,21 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
     else if (bal) launch_axis0<false, true>(L.dtype, grid, A, stream);
     else launch_axis0<false, false>(L.dtype, grid, A, stream);
   } else {
-    if (L.dtype == 0) hipLaunchKernelGGL(quantize_axis1_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, A);
-    else if (L.dtype == 1) hipLaunchKernelGGL(quantize_axis1_kernel<half_t>, dim3(grid), dim3(256), 0, stream, A);
-    else hipLaunchKernelGGL(quantize_axis1_kernel<float>, dim3(grid), dim3(256), 0, stream, A);
+    // four columns per lane when whole groups of 4 stay aligned (codes, scales and offsets rows
+    // are cols bytes apart; input rows ld or the map's token stride elements apart)
+    const bool v4 = L.cols % 4 == 0 && (L.strided ? L.map.ts % 4 == 0 : L.ld % 4 == 0) &&
+                    (reinterpret_cast<uintptr_t>(L.offsets) & 3u) == 0;
+    if (v4) {
+      const int64_t g4 = ((L.rows / 16) * (L.cols / 4) + 255) / 256;
+      const dim3 g((unsigned)(g4 > 2048 ? 2048 : (g4 < 1 ? 1 : g4)));
+      if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis1_kernel<uint16_t, 4>), g, dim3(256), 0, stream, A);
+      else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis1_kernel<half_t, 4>), g, dim3(256), 0, stream, A);
+      else hipLaunchKernelGGL((quantize_axis1_kernel<float, 4>), g, dim3(256), 0, stream, A);
+    } else {
+      if (L.dtype == 0) hipLaunchKernelGGL((quantize_axis1_kernel<uint16_t, 1>), dim3(grid), dim3(256), 0, stream, A);
+      else if (L.dtype == 1) hipLaunchKernelGGL((quantize_axis1_kernel<half_t, 1>), dim3(grid), dim3(256), 0, stream, A);
+      else hipLaunchKernelGGL((quantize_axis1_kernel<float, 1>), dim3(grid), dim3(256), 0, stream, A);
+    }
   }
   return hipGetLastError();
 }
