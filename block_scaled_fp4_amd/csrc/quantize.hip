@@ -296,9 +296,9 @@ __global__ void __launch_bounds__(256) quantize_means_kernel(QuantArgs A) {
 // block_axis 1: one lane per VEC consecutive columns of a group of 16 rows
 // (VEC blocks, searched one after the other); consecutive lanes take
 // consecutive column groups, so each row load of a wavefront is one
-// contiguous segment, and a lane's VEC code bytes of a row pair, scales and
-// offsets go out as one store each (VEC 4: whole columns groups of 4, with
-// cols and the row step multiples of 4; else VEC 1).
+// contiguous segment, and a lane's VEC code bytes of a row pair, its VEC
+// scales and its VEC offsets go out as one store each.  VEC is 4 when cols
+// and the row step are multiples of 4, else 1.
 template <typename T, int VEC>
 __device__ __forceinline__ void load_cols(const T* p, float (&v)[VEC]);
 template <>
