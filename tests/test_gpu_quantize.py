@@ -39,6 +39,17 @@ def test_small_shapes_bit_exact(gpu, dtype, axis, search):
     _run(gpu, x, axis, search)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("cols", [18, 84, 4])
+def test_rows_axis_column_groups(gpu, dtype, cols):
+    # blocks along rows: four columns per lane when cols is a multiple of 4 (84, 4),
+    # one column per lane otherwise (18); both bit-exact
+    g = torch.Generator().manual_seed(13 + cols)
+    x = (torch.randn(64, cols, generator=g) * torch.logspace(-2, 2, cols)).to(dtype)
+    case(f"quantize axis=1 {dtype} cols={cols}")
+    _run(gpu, x, 1, True)
+
+
 @pytest.mark.parametrize("gmode", [1, 2])
 def test_global_scale_modes(gpu, gmode):
     g = torch.Generator().manual_seed(12)
