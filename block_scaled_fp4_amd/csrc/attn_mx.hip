@@ -310,11 +310,17 @@ template <int D, int BC, typename OT>
 __global__ void __launch_bounds__(256, 2) mx_attn_kernel(MxProblem P) {
   __shared__ MxSmem<D, BC> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
-  // workgroup -> (batch*head, query tile), XCD-aware as in the NVFP4 kernel
+  // workgroup -> (batch*head, query tile).  Workgroups go round-robin to the
+  // 8 XCDs.  Where a head's K and V codes fill an L2 (Sk d >= 4 Mi bytes), each
+  // XCD takes whole heads, one after the other (their codes stay in its L2),
+  // the heaviest causal tiles of a head first; below that, heads are
+  // interleaved over the XCDs and the heaviest tiles of all heads come first
+  // (measured at 32 heads, d 128, causal: 8K 10-12% faster interleaved, 32K
+  // up to 2.5% faster with whole heads).
   const int64_t BH = gridDim.x / P.nqt;
   int64_t bh, qrank;
   const int64_t gi = blockIdx.x;
-  if (BH % 8 == 0) {
+  if (BH % 8 == 0 && P.Sk * D >= ((int64_t)4 << 20)) {
     const int64_t xcd = gi % 8, slot = gi / 8;
     qrank = slot % P.nqt;
     bh = (slot / P.nqt) * 8 + xcd;
