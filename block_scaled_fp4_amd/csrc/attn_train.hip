@@ -93,17 +93,53 @@ __global__ void __launch_bounds__(256) split_f16_kernel(const half_t* x, int64_t
   lo[i] = (uint16_t)bf16_rne_bits(v - __uint_as_float(h << 16));
 }
 
-// D[row] = sum_d dO[row][d] O'[row][d] in binary32, one wave per row.
+// 8 consecutive elements (16-byte aligned) as binary32
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8f<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  const uint4_t w = *reinterpret_cast<const uint4_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8f<half_t>(const half_t* p, float (&v)[8]) {
+  const half8_t w = *reinterpret_cast<const half8_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)w[i];
+}
+template <>
+__device__ __forceinline__ void load8f<float>(const float* p, float (&v)[8]) {
+  const float4_t a = *reinterpret_cast<const float4_t*>(p), b = *reinterpret_cast<const float4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+// D[row] = sum_d dO[row][d] O'[row][d] in binary32: 16 lanes per row, each
+// with 8 consecutive elements (16-byte loads), then a sum over the 16 lanes.
 template <typename TD, typename TO>
 __global__ void __launch_bounds__(256) row_dot_kernel(const TD* dout, const TO* ohp, int64_t rows, int d, float* D) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  const int sub = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   float s = 0.0f;
-  for (int c = lane; c < d; c += 64) s = __builtin_fmaf(to_f32<TD>(dout[row * d + c]), to_f32<TO>(ohp[row * d + c]), s);
+  if (row < rows) {
+    for (int c = 8 * sub; c < d; c += 128) {
+      float a[8], b[8];
+      load8f<TD>(dout + row * d + c, a);
+      load8f<TO>(ohp + row * d + c, b);
 #pragma unroll
-  for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
-  if (lane == 0) D[row] = s;
+      for (int e = 0; e < 8; ++e) s = __builtin_fmaf(a[e], b[e], s);
+    }
+  }
+#pragma unroll
+  for (int k = 8; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);  // within the row's 16 lanes
+  if (sub == 0 && row < rows) D[row] = s;
 }
 
 // ---- probabilities --------------------------------------------------------
@@ -694,7 +730,7 @@ hipError_t fp4i_launch_attn_bwd(const AttnBwdLaunch& L, hipStream_t st) {
     dO_hi = doh;
     dO_lo = dol;
   }
-  const dim3 rd((unsigned)((nq + 3) / 4));
+  const dim3 rd((unsigned)((nq + 15) / 16));
   if (fp16_do) {
     const half_t* dO = (const half_t*)L.dout;
     if (L.hp_dtype == 2) hipLaunchKernelGGL((row_dot_kernel<half_t, float>), rd, dim3(256), 0, st, dO, (const float*)L.out_hp, (int64_t)nq, (int)d, Dv);
