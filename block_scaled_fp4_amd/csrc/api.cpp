@@ -453,27 +453,32 @@ int attention_fwd_impl(const fp4_attn_problem* prob, const fp4_attn_opts* opts, 
       L.mblk = opts->sel_block;
       L.mnb = P.nqb;
     }
-    if (e == hipSuccess) e = fp4i_launch_quantize(L, s);
-    if (e == hipSuccess) {
-      L.x = prob->k; L.rows = B * Hkv * Sk;
-      L.map = maps.k;
-      L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
-      L.exp_negate = 0;
-      L.exp_rows = Sk;
-      if (P.need_sel) {
-        L.means = (double*)(ws + P.km);
-        L.mS = Sk;
-        L.mnb = P.nkb;
-      }
-      e = fp4i_launch_quantize(L, s);
+    QuantLaunch LK = L;
+    LK.x = prob->k; LK.rows = B * Hkv * Sk;
+    LK.map = maps.k;
+    LK.codes = (uint8_t*)(ws + P.kc); LK.scales = (uint8_t*)(ws + P.ks);
+    LK.exp_negate = 0;
+    LK.exp_rows = Sk;
+    if (P.need_sel) {
+      LK.means = (double*)(ws + P.km);
+      LK.mS = Sk;
+      LK.mnb = P.nkb;
     }
+    QuantLaunch LV = LK;
+    LV.x = prob->v; LV.axis = 1; LV.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
+    LV.map = maps.v;
+    LV.cexp = nullptr;
+    LV.means = nullptr;
+    LV.codes = (uint8_t*)(ws + P.vc); LV.scales = (uint8_t*)(ws + P.vs);
     if (e == hipSuccess) {
-      L.x = prob->v; L.axis = 1; L.hadamard = 0;  // V blocks run along tokens (16-token blocks never straddle heads: Sk % 16 == 0)
-      L.map = maps.v;
-      L.cexp = nullptr;
-      L.means = nullptr;
-      L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
-      e = fp4i_launch_quantize(L, s);
+      // the plain case (no rotation, balance or block means) in one launch
+      if (!L.hadamard && !L.cexp && !L.means) {
+        e = fp4i_launch_quantize_qkv(L, LK, LV, s);
+      } else {
+        e = fp4i_launch_quantize(L, s);
+        if (e == hipSuccess) e = fp4i_launch_quantize(LK, s);
+        if (e == hipSuccess) e = fp4i_launch_quantize(LV, s);
+      }
     }
     if (e != hipSuccess) return hip_status(e, "fp4_attention_fwd quantize launch");
     qc = (uint8_t*)(ws + P.qc); qs = (uint8_t*)(ws + P.qs);
@@ -629,19 +634,15 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
     L.map = maps.q;
     L.x = prob->q; L.rows = B * H * Sq; L.axis = 0;
     L.codes = (uint8_t*)(ws + P.qc); L.scales = (uint8_t*)(ws + P.qs);
-    hipError_t e = fp4i_launch_quantize(L, s);
-    if (e == hipSuccess) {
-      L.x = prob->k; L.rows = B * Hkv * Sk;
-      L.map = maps.k;
-      L.codes = (uint8_t*)(ws + P.kc); L.scales = (uint8_t*)(ws + P.ks);
-      e = fp4i_launch_quantize(L, s);
-    }
-    if (e == hipSuccess) {
-      L.x = prob->v; L.axis = 1;
-      L.map = maps.v;
-      L.codes = (uint8_t*)(ws + P.vc); L.scales = (uint8_t*)(ws + P.vs);
-      e = fp4i_launch_quantize(L, s);
-    }
+    QuantLaunch LK = L;
+    LK.x = prob->k; LK.rows = B * Hkv * Sk;
+    LK.map = maps.k;
+    LK.codes = (uint8_t*)(ws + P.kc); LK.scales = (uint8_t*)(ws + P.ks);
+    QuantLaunch LV = LK;
+    LV.x = prob->v; LV.axis = 1;
+    LV.map = maps.v;
+    LV.codes = (uint8_t*)(ws + P.vc); LV.scales = (uint8_t*)(ws + P.vs);
+    const hipError_t e = fp4i_launch_quantize_qkv(L, LK, LV, s);
     if (e != hipSuccess) return hip_status(e, "fp4_attention_bwd quantize launch");
     qc = (uint8_t*)(ws + P.qc); qs = (uint8_t*)(ws + P.qs);
     kc = (uint8_t*)(ws + P.kc); ks = (uint8_t*)(ws + P.ks);

@@ -72,6 +72,11 @@ int fp4i_amax_parts(int64_t rows, int64_t cols);
 hipError_t fp4i_launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
                                    uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream);
+// Q and K (axis 0) and V (axis 1) in one launch; only for gmode 0 with no
+// per-tensor scale, rotation, balance exponents or block means, bf16/fp16
+// (hipErrorInvalidValue otherwise).  Same results as three fp4i_launch_quantize.
+hipError_t fp4i_launch_quantize_qkv(const QuantLaunch& q, const QuantLaunch& k, const QuantLaunch& v,
+                                    hipStream_t stream);
 
 // MXFP4 attention forward: Q, K codes [.., d/2] with E8M0 scales [.., d/32]
 // (blocks along d), V codes [.., Sk/2, d] with scales [.., Sk/32, d] (blocks

@@ -174,22 +174,20 @@ __device__ __forceinline__ void raw_to_f32<float>(const RawBlock<float>& R, floa
 // consecutive blocks (2 KiB of bf16) and writes their 512 code bytes.  The
 // grid is a few workgroups per CU that stride over the blocks, each lane
 // loading its next block while it searches the current one.
+// The work of workgroup wg of nwg (grid-stride over the blocks), with the
+// scale table in LDS and the per-tensor factor ginv.
 template <typename T, bool HAD, bool BAL>
-__global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
-  __shared__ float2_t tab[128];
-  __shared__ float sh[8];
-  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
-  const float ginv = global_factor(A, sh);
-  __syncthreads();
+__device__ __forceinline__ void axis0_body(const QuantArgs& A, const float2_t* tab, float ginv, int64_t wg,
+                                           int64_t nwg) {
   const int64_t bpr = A.cols / 16;  // blocks per row
   const int64_t nb = A.rows * bpr;
   const T* x = reinterpret_cast<const T*>(A.x);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t stride = nwg * blockDim.x;
   auto src = [&](int64_t blk) {
     const int64_t r = blk / bpr, cb = blk - r * bpr;
     return x + A.row_off(r) + cb * 16;
   };
-  int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t blk = wg * blockDim.x + threadIdx.x;
   RawBlock<T> raw;
   if (blk < nb) load_raw<T>(raw, src(blk));
   for (; blk < nb; blk += stride) {
@@ -209,6 +207,16 @@ __global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
     A.scales[blk] = (uint8_t)scale;
     if (A.offsets) A.offsets[blk] = (int8_t)off;
   }
+}
+
+template <typename T, bool HAD, bool BAL>
+__global__ void __launch_bounds__(256) quantize_axis0_kernel(QuantArgs A) {
+  __shared__ float2_t tab[128];
+  __shared__ float sh[8];
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const float ginv = global_factor(A, sh);
+  __syncthreads();
+  axis0_body<T, HAD, BAL>(A, tab, ginv, blockIdx.x, gridDim.x);
 }
 
 // Axis-0 quantization fused with the block means of the FP16 path's block
@@ -339,16 +347,12 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&b)[VEC]
 }
 
 template <typename T, int VEC>
-__global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
-  __shared__ float2_t tab[128];
-  __shared__ float sh[8];
-  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
-  const float ginv = global_factor(A, sh);
-  __syncthreads();
+__device__ __forceinline__ void axis1_body(const QuantArgs& A, const float2_t* tab, float ginv, int64_t wg,
+                                           int64_t nwg) {
   const int64_t cv = A.cols / VEC;  // column groups per row
   const int64_t nu = (A.rows / 16) * cv;
   const T* x = reinterpret_cast<const T*>(A.x);
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nu; u += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t u = wg * blockDim.x + threadIdx.x; u < nu; u += nwg * blockDim.x) {
     const int64_t rb = u / cv, c = (u - rb * cv) * VEC;
     // the blocks' 16 rows lie in one head (heads hold whole blocks)
     const T* xb = x + A.row_off(rb * 16) + c;
@@ -379,6 +383,44 @@ __global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
     const int64_t blk = rb * A.cols + c;
     store_bytes<VEC>(A.scales + blk, scale);
     if (A.offsets) store_bytes<VEC>(reinterpret_cast<uint8_t*>(A.offsets) + blk, offb);
+  }
+}
+
+template <typename T, int VEC>
+__global__ void __launch_bounds__(256) quantize_axis1_kernel(QuantArgs A) {
+  __shared__ float2_t tab[128];
+  __shared__ float sh[8];
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  const float ginv = global_factor(A, sh);
+  __syncthreads();
+  axis1_body<T, VEC>(A, tab, ginv, blockIdx.x, gridDim.x);
+}
+
+// Q and K (blocks along d) and V (blocks along rows) of an attention call in
+// one launch, when none needs the per-tensor scale, the rotation, the balance
+// exponents or the block means: workgroups [0, gq) take Q, [gq, gq + gk) K,
+// the rest V, each range striding over its tensor's blocks as its own launch
+// would.
+struct QkvArgs {
+  QuantArgs q, k, v;
+  int64_t gq, gk;
+  int v4;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) quantize_qkv_kernel(QkvArgs A) {
+  __shared__ float2_t tab[128];
+  if (threadIdx.x < 128) tab[threadIdx.x] = kScaleTab.v[threadIdx.x];
+  __syncthreads();
+  const int64_t b = blockIdx.x;
+  if (b < A.gq) {
+    axis0_body<T, false, false>(A.q, tab, 1.0f, b, A.gq);
+  } else if (b < A.gq + A.gk) {
+    axis0_body<T, false, false>(A.k, tab, 1.0f, b - A.gq, A.gk);
+  } else {
+    const int64_t gv = (int64_t)gridDim.x - A.gq - A.gk;
+    if (A.v4) axis1_body<T, 4>(A.v, tab, 1.0f, b - A.gq - A.gk, gv);
+    else axis1_body<T, 1>(A.v, tab, 1.0f, b - A.gq - A.gk, gv);
   }
 }
 
@@ -717,6 +759,66 @@ hipError_t fp4i_launch_quantize(const QuantLaunch& L, hipStream_t stream) {
       else hipLaunchKernelGGL((quantize_axis1_kernel<float, 1>), dim3(grid), dim3(256), 0, stream, A);
     }
   }
+  return hipGetLastError();
+}
+
+namespace {
+QuantArgs plain_args(const QuantLaunch& L) {
+  QuantArgs A;
+  A.x = L.x;
+  A.rows = L.rows;
+  A.cols = L.cols;
+  A.ld = L.ld;
+  A.codes = reinterpret_cast<uint2_t*>(L.codes);
+  A.codes8 = L.codes;
+  A.scales = L.scales;
+  A.offsets = L.offsets;
+  A.g = nullptr;
+  A.search = L.search;
+  A.fmin = L.fmin;
+  A.fmax = L.fmax;
+  A.gmode = 0;
+  A.amax_part = nullptr;
+  A.n_part = 0;
+  for (int i = 0; i < 4; ++i) A.hsigns[i] = 0;
+  A.hscale = 1.0f;
+  A.cexp = nullptr;
+  A.exp_negate = 0;
+  A.exp_rows = 1;
+  A.means = nullptr;
+  A.mS = 0;
+  A.mblk = 0;
+  A.mnb = 0;
+  A.strided = L.strided;
+  A.map = L.map;
+  return A;
+}
+
+int64_t part_grid(int64_t work) {
+  const int64_t g = (work + 255) / 256;
+  return g > 2048 ? 2048 : g;
+}
+}  // namespace
+
+hipError_t fp4i_launch_quantize_qkv(const QuantLaunch& q, const QuantLaunch& k, const QuantLaunch& v,
+                                    hipStream_t stream) {
+  for (const QuantLaunch* L : {&q, &k, &v})
+    if (L->gmode != 0 || L->g || L->hadamard || L->cexp || L->means || L->dtype != q.dtype || L->dtype == 2)
+      return hipErrorInvalidValue;
+  if (q.axis != 0 || k.axis != 0 || v.axis != 1) return hipErrorInvalidValue;
+  QkvArgs A;
+  A.q = plain_args(q);
+  A.k = plain_args(k);
+  A.v = plain_args(v);
+  A.v4 = v.cols % 4 == 0 && (v.strided ? v.map.ts % 4 == 0 : v.ld % 4 == 0) &&
+         (reinterpret_cast<uintptr_t>(v.offsets) & 3u) == 0;
+  A.gq = part_grid(q.rows * (q.cols / 16));
+  A.gk = part_grid(k.rows * (k.cols / 16));
+  const int64_t gv = part_grid((v.rows / 16) * (A.v4 ? v.cols / 4 : v.cols));
+  const int64_t grid = A.gq + A.gk + gv;
+  if (grid == 0) return hipSuccess;
+  if (q.dtype == 0) hipLaunchKernelGGL(quantize_qkv_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, A);
+  else hipLaunchKernelGGL(quantize_qkv_kernel<half_t>, dim3((unsigned)grid), dim3(256), 0, stream, A);
   return hipGetLastError();
 }
 

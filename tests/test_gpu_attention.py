@@ -170,6 +170,28 @@ def test_bf16_output_and_prequantized_operands(gpu):
     assert (o3.float() - o2).abs().max().item() <= 2 ** -8 * max(1.0, o2.abs().max().item())
 
 
+@pytest.mark.parametrize("B,H,Hkv,S,d,dt", [
+    (2, 4, 2, 384, 64, torch.float16),
+    (1, 8, 2, 8192, 128, torch.bfloat16),  # Q alone fills the 2048 workgroups of its range
+])
+def test_one_launch_quantization_equals_separate(gpu, B, H, Hkv, S, d, dt):
+    # without rotation, balance or selection the forward quantizes Q, K and V in
+    # one launch; its codes must be those of three standalone quantizer calls
+    q, k, v = synth.qkv(B, H, S, d, dt, seed=90 + d, Hkv=Hkv, k_outliers=2)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    case(f"attn one-launch quantization B={B} H={H}/{Hkv} S={S} d={d} {dt}")
+    rq = gpu.fp4_quantize(qc.view(-1, d), 0, True, with_offsets=False)
+    rk = gpu.fp4_quantize(kc.view(-1, d), 0, True, with_offsets=False)
+    rv = gpu.fp4_quantize(vc.view(-1, d), 1, True, with_offsets=False)
+    quant = dict(q_codes=rq["codes"], q_scales=rq["scales"], k_codes=rk["codes"], k_scales=rk["scales"],
+                 v_codes=rv["codes"], v_scales=rv["scales"])
+    kw = dict(causal=True, kv_tile=128, out_dtype=gpu.FP32)
+    o1, l1 = gpu.fp4_attention_fwd(qc, kc, vc, quantized=quant, **kw)
+    o2, l2 = gpu.fp4_attention_fwd(qc, kc, vc, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_prefill_workload_all_heads(gpu):
     """B=1, H=32, S=8192, d=128, causal, ScaleSearch Q/K/V, two-level P,
     kv_tile 128: every row of every head against the oracle."""
