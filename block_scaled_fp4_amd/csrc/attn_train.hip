@@ -556,9 +556,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
 
 // ---- dQ without materialized scores -----------------------------------------
 //
-// One workgroup per 128 query rows (4 waves x 32), looping over 64-key tiles.
-// Per 32-key subtile the wave recomputes S^T = K^ Q^T and dP^T = V^ dO^T with
-// K^ and V^ rows fed in the krow2 order, so that lane (query, h) holds keys
+// One workgroup per 128 query rows (4 waves x 32), looping over key tiles (32
+// keys at d = 128, 64 at d = 64), each fetched into registers while the tile
+// before it computes.  Per 32-key subtile the wave recomputes S^T = K^ Q^T
+// and dP^T = V^ dO^T with K^ and V^ rows fed in the krow2 order, so that
+// lane (query, h) holds keys
 // 8h..8h+7 and 16+8h..16+8h+7 -- the k order of the B operand of
 // dQ^T += K^T dS^T -- forms dS = s P (dP - D) with P = 2^(x - lse2) (dQ needs
 // no P^), and accumulates dQ^T with K^T staged transposed in LDS.
@@ -574,7 +576,7 @@ struct QArgs {
 
 template <int D, bool SPLIT_DO>
 __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
-  constexpr int KT = 64;       // keys per tile
+  constexpr int KT = 4096 / D;  // keys per tile: one 4 x 4 block of K and of V per thread
   constexpr int RA = D + 8;    // [key][d] rows, bf16
   constexpr int RT = KT + 8;   // [d][key] rows, bf16
   __shared__ uint16_t Ka[KT * RA], Va[KT * RA], Kt[D * RT];
@@ -606,35 +608,44 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
   const uint16_t* kb = A.k + bhk * A.Sk * D;
   const uint16_t* vb = A.v + bhk * A.Sk * D;
   const int kr = krow2(r32);
+  // K^ and V^ rows of a tile, fetched into registers one tile ahead (thread
+  // (key group, d group) moves 4 keys x 4 d of each) and staged as [key][d]
+  // images and a [d][key] image of K^
+  constexpr int NU = KT * D / 16 / 256;
+  uint2_t xk[NU][4], xv[NU][4];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int id = (int)threadIdx.x + 256 * u;
+      const int kg = id % (KT / 4), dg = id / (KT / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t kk = k0 + 4 * kg + i;
+        const bool ok = kk < A.Sk;
+        xk[u][i] = ok ? *reinterpret_cast<const uint2_t*>(kb + kk * D + 4 * dg) : uint2_t{0, 0};
+        xv[u][i] = ok ? *reinterpret_cast<const uint2_t*>(vb + kk * D + 4 * dg) : uint2_t{0, 0};
+      }
+    }
+  };
+  if (ntile > 0) fetch(0);
   for (int tile = 0; tile < ntile; ++tile) {
     const int64_t key0 = (int64_t)tile * KT;
     __syncthreads();  // the previous tile's LDS reads are done
-    {
-      // K^ and V^ rows as [key][d]; K^ also as [d][key]: thread (key group, d group) moves 4 x 4
-      const int t = threadIdx.x;
 #pragma unroll
-      for (int u = 0; u < KT * D / 16 / 256; ++u) {
-        const int id = t + 256 * u;
-        const int kg = id % (KT / 4), dg = id / (KT / 4);
-        uint2_t xk[4], xv[4];
+    for (int u = 0; u < NU; ++u) {
+      const int id = (int)threadIdx.x + 256 * u;
+      const int kg = id % (KT / 4), dg = id / (KT / 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t kk = key0 + 4 * kg + i;
-          const bool ok = kk < A.Sk;
-          xk[i] = ok ? *reinterpret_cast<const uint2_t*>(kb + kk * D + 4 * dg) : uint2_t{0, 0};
-          xv[i] = ok ? *reinterpret_cast<const uint2_t*>(vb + kk * D + 4 * dg) : uint2_t{0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<uint2_t*>(Ka + (4 * kg + i) * RA + 4 * dg) = xk[i];
-          *reinterpret_cast<uint2_t*>(Va + (4 * kg + i) * RA + 4 * dg) = xv[i];
-        }
-        uint2_t tr[4];
-        transpose4x4_16(xk, tr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2_t*>(Kt + (4 * dg + j) * RT + 4 * kg) = tr[j];
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint2_t*>(Ka + (4 * kg + i) * RA + 4 * dg) = xk[u][i];
+        *reinterpret_cast<uint2_t*>(Va + (4 * kg + i) * RA + 4 * dg) = xv[u][i];
       }
+      uint2_t tr[4];
+      transpose4x4_16(xk[u], tr);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2_t*>(Kt + (4 * dg + j) * RT + 4 * kg) = tr[j];
     }
+    if (tile + 1 < ntile) fetch(key0 + KT);  // in flight during this tile's products
     __syncthreads();
 #pragma unroll
     for (int g = 0; g < KT / 32; ++g) {
