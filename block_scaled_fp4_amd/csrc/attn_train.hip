@@ -560,10 +560,10 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
 // keys at d = 128, 64 at d = 64), each fetched into registers while the tile
 // before it computes.  Per 32-key subtile the wave recomputes S^T = K^ Q^T
 // and dP^T = V^ dO^T with K^ and V^ rows fed in the krow2 order, so that
-// lane (query, h) holds keys
-// 8h..8h+7 and 16+8h..16+8h+7 -- the k order of the B operand of
-// dQ^T += K^T dS^T -- forms dS = s P (dP - D) with P = 2^(x - lse2) (dQ needs
-// no P^), and accumulates dQ^T with K^T staged transposed in LDS.
+// lane (query, h) holds keys 8h..8h+7 and 16+8h..16+8h+7 -- the k order of
+// the B operand of dQ^T += K^T dS^T -- forms dS = s P (dP - D) with
+// P = 2^(x - lse2) (dQ needs no P^), and accumulates dQ^T with K^T staged
+// transposed in LDS.
 
 struct QArgs {
   const uint16_t *q, *k, *v, *doh, *dol;
