@@ -116,6 +116,35 @@ class Timer:
         return sorted(a.elapsed_time(b) for a, b in ev)
 
 
+def graph_ms(torch, fn, calls, reps=5):
+    """GPU time per call of fn alone: `calls` calls captured in one HIP graph
+    (torch.cuda.graph) and the graph replayed `reps` times between events.
+    For calls whose kernels take less time than Python needs to issue them,
+    where back-to-back calls measure the host.  fn must be capturable: the
+    library makes no memset or host synchronization, and the binding only
+    allocates (from the graph's pool)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * calls)
+
+
 def bench_select32k(fp4, synth, torch, steps, warmup):
     B, H, S, d = 1, 32, 32768, 128
     log("generating selective workload S=32768")
@@ -348,12 +377,21 @@ def bench_tiny(fp4, synth, torch, n):
     q, k, v = (t.cuda() for t in synth.tiny())
     out = torch.empty((1, 1, 256, 64), dtype=torch.float32, device="cuda")
     timer = Timer(torch)
-    ms = timer.run(lambda: fp4.fp4_attention_fwd(q, k, v, causal=False, kv_tile=64, scale_search=False,
-                                                 out_dtype=fp4.FP32, return_lse=False, out=out), max(50, n))
+    call = lambda: fp4.fp4_attention_fwd(q, k, v, causal=False, kv_tile=64, scale_search=False,  # noqa: E731
+                                         out_dtype=fp4.FP32, return_lse=False, out=out)
+    ms = timer.run(call, max(50, n))
+    try:
+        gms = graph_ms(torch, call, 50)
+    except Exception as e:  # capture refused: report the host-bound figure only
+        log(f"graph timing of the tiny configuration failed: {e}")
+        gms = float("nan")
     fl = attn_flops(1, 1, 256, 64, causal=False)
     return dict(workload="tiny B=1 H=1 S=256 d=64 fp16 non-causal, max-scaling, kv_tile 64",
                 end_to_end_us=round(ms * 1e3, 2), tflops=round(fl / ms / 1e9, 3),
-                note="three quantizer launches and the attention kernel; launch-bound at this size")
+                gpu_us_graph=None if gms != gms else round(gms * 1e3, 2),
+                note="one quantizer launch (Q, K and V) and the attention kernel; launch-bound at this size "
+                     "(end_to_end_us: calls from Python back to back; gpu_us_graph: the same calls replayed "
+                     "from a HIP graph, the GPU's own time)")
 
 
 def bench_decode(fp4, synth, torch, n, selective=True):
@@ -505,13 +543,30 @@ def bench_kv_append(fp4, torch, n):
                      device="cuda")
     timer = Timer(torch)
     ms = timer.run(lambda: fp4.fp4_kv_cache_append(cache, kn, vn, workspace=ws), n, warm=2)
+    # the GPU's own time: 32 appends replayed from a HIP graph (room made for every one of them;
+    # mid_len must advance by 16 per append)
+    gcalls, greps = 32, 5
+    start = cap - 16 * (gcalls * (greps + 2) + 2)
+    ml.fill_(start)
+    torch.cuda.synchronize()
+    try:
+        gms = graph_ms(torch, lambda: fp4.fp4_kv_cache_append(cache, kn, vn, workspace=ws), gcalls, greps)
+        appended = int((ml[0] - start).item()) // 16
+        assert appended == 1 + gcalls * (greps + 1), f"graph replay appended {appended} groups"
+    except Exception as e:  # capture refused or replays incomplete: the host-bound figure only
+        log(f"graph timing of the cache append failed: {e}")
+        gms = ms
     # read the window and the new tokens once, write the window and the NVFP4 group once
     algo = B * Hkv * ((n_recent + 16) * d * 2 * 2 + n_recent * d * 2 * 2 + 16 * (d // 2 + d // 16) * 2)
     gbps = algo / ms / 1e6
+    ggbps = algo / gms / 1e6
     return dict(workload="append 16 tokens to batch 16 x 8 kv heads, d 128, 256-token bf16 window, ScaleSearch",
                 algorithmic_bytes=algo, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
-                roofline={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbps / HBM_PEAK_GBS, 4),
+                gpu_us_graph=round(gms * 1e3, 2), gpu_GBps_graph=round(ggbps, 1),
+                note="us: calls from Python back to back (the host's per-call time exceeds the kernels'); "
+                     "gpu_us_graph: the same call replayed from a HIP graph; the roofline uses the latter",
+                roofline={"bound": "hbm", "achieved": round(ggbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(ggbps / HBM_PEAK_GBS, 4),
                           "traffic": read_traffic("kv_append_b16_w256", "kvcache.hip")})
 
 
