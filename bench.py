@@ -630,8 +630,8 @@ def main():
     ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy", "decode", "kvappend"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md but not run", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path's sharding over several GPUs is designed but not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 
