@@ -609,6 +609,8 @@ int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, c
   if (opts->fp16_budget_pct != 0) return fail(FP4_ERR_UNSUPPORTED, "%s: training has no FP16 path (fp16_budget_pct must be 0)", fn);
   if (opts->hadamard_qk) return fail(FP4_ERR_UNSUPPORTED, "%s: the rotation is not supported in training", fn);
   if (opts->balance_qk) return fail(FP4_ERR_UNSUPPORTED, "%s: the balance pair is not supported in training", fn);
+  // the dK/dV kernels address one head's query rows through 32-bit buffer offsets
+  if (prob->Sq * prob->d * 2 >= ((int64_t)1 << 31)) return fail(FP4_ERR_UNSUPPORTED, "%s: Sq * d too large", fn);
   if (!out_hp || !lse || !dout || !dq || !dk || !dv) return fail(FP4_ERR_INVALID_ARG, "%s: out_hp, lse, dout, dq, dk, dv are required", fn);
   const void* ptrs[] = {out_hp, lse, dout, dq, dk, dv};
   for (const void* ptr : ptrs)

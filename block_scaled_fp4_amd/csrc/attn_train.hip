@@ -338,22 +338,25 @@ __global__ void __launch_bounds__(256, 2) bwd_kv_kernel(KvArgs A) {
   constexpr int NOP = NT == 256 ? 2 : 1;
   uint2_t fx[NOP][4], fxl[SPL ? 4 : 1];
   float fl = 0.0f, fd = 0.0f;
+  // rows go through buffer resources of the step's query head: rows past Sq
+  // read as zero with no branch (the host keeps Sq * d * 2 below 2^31)
+  const uint32_t head_bytes = (uint32_t)(A.Sq * D * 2);
   auto fetch = [&](int step) {
     const int64_t bh = b * A.H + hk * A.G + step / nqb;
-    const int64_t q0 = qstart + (int64_t)(step % nqb) * QB;
+    const int q0 = (int)(qstart + (int64_t)(step % nqb) * QB);
+    const rsrc_t rq = make_rsrc(A.q + bh * A.Sq * D, head_bytes);
+    const rsrc_t rdo = make_rsrc(A.doh + bh * A.Sq * D, head_bytes);
 #pragma unroll
     for (int o = 0; o < NOP; ++o) {
       const int op = NOP == 2 ? o : (int)(threadIdx.x / NT);
       const int t = (int)(threadIdx.x % NT);
       const int qg = t % 8, dg = t / 8;
-      const uint16_t* src = op == 0 ? A.q : A.doh;
+      const rsrc_t src = op == 0 ? rq : rdo;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t qq = q0 + 4 * qg + i;
-        const bool ok = qq < A.Sq;
-        fx[o][i] = ok ? *reinterpret_cast<const uint2_t*>(src + (bh * A.Sq + qq) * D + 4 * dg) : uint2_t{0, 0};
-        if (SPL && op == 1)
-          fxl[SPL ? i : 0] = ok ? *reinterpret_cast<const uint2_t*>(A.dol + (bh * A.Sq + qq) * D + 4 * dg) : uint2_t{0, 0};
+        const uint32_t off = (uint32_t)((((int64_t)q0 + 4 * qg + i) * D + 4 * dg) * 2);
+        fx[o][i] = buf_load8(src, off);
+        if (SPL && op == 1) fxl[SPL ? i : 0] = buf_load8(make_rsrc(A.dol + bh * A.Sq * D, head_bytes), off);
       }
     }
     if (threadIdx.x < QB) {
@@ -613,6 +616,9 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
   // images and a [d][key] image of K^
   constexpr int NU = KT * D / 16 / 256;
   uint2_t xk[NU][4], xv[NU][4];
+  // rows through buffer resources of the kv head: keys past Sk read as zero
+  // with no branch (the host keeps Sk * d * 2 below 2^31)
+  const rsrc_t rk = make_rsrc(kb, (uint32_t)(A.Sk * D * 2)), rv = make_rsrc(vb, (uint32_t)(A.Sk * D * 2));
   auto fetch = [&](int64_t k0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -620,10 +626,9 @@ __global__ void __launch_bounds__(256, 2) bwd_q_kernel(QArgs A) {
       const int kg = id % (KT / 4), dg = id / (KT / 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t kk = k0 + 4 * kg + i;
-        const bool ok = kk < A.Sk;
-        xk[u][i] = ok ? *reinterpret_cast<const uint2_t*>(kb + kk * D + 4 * dg) : uint2_t{0, 0};
-        xv[u][i] = ok ? *reinterpret_cast<const uint2_t*>(vb + kk * D + 4 * dg) : uint2_t{0, 0};
+        const uint32_t off = (uint32_t)(((k0 + 4 * kg + i) * D + 4 * dg) * 2);
+        xk[u][i] = buf_load8(rk, off);
+        xv[u][i] = buf_load8(rv, off);
       }
     }
   };

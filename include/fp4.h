@@ -335,6 +335,8 @@ int fp4_attention_fwd_train(const fp4_attn_problem* prob, const fp4_attn_opts* o
  * K^ and V^ (exact, as every E2M1 x E4M3 product has at most six significant
  * bits), dO as one bfloat16 term or, for binary16 dO, as two bfloat16 terms
  * whose sum is exact, and one float per query row (see the query).
+ * FP4_ERR_UNSUPPORTED when Sq * d * 2 >= 2^31 (one head's query rows are
+ * addressed through 32-bit byte offsets), as for Sk * d.
  */
 int fp4_attention_bwd(const fp4_attn_problem* prob, const fp4_attn_opts* opts, const void* out_hp, const float* lse,
                       const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
