@@ -229,6 +229,19 @@ def test_log_switch_reports_errors(L, capfd, monkeypatch):
     assert "[fp4]" not in capfd.readouterr().err
 
 
+def test_backward_rejects_query_rows_past_32_bit_offsets(L):
+    """The dK/dV kernels address one head's query rows through 32-bit buffer
+    offsets: Sq * d * 2 must stay below 2^31 (as Sk * d does for every call)."""
+    import block_scaled_fp4_amd as fp4
+    f = C.c_void_p(1 << 20)
+
+    def call(P):  # no workspace: a call past every other check stops there, before any launch
+        return L.fp4_attention_bwd(C.byref(P), C.byref(_opts(fp4, causal=0)), f, f, f, f, f, f, f, 0, None)
+
+    assert call(_prob(fp4, Sq=1 << 23, Sk=256)) == -2          # 2^23 * 128 * 2 = 2^31
+    assert call(_prob(fp4, Sq=(1 << 23) - 16, Sk=256)) == -3   # below the limit: the workspace check
+
+
 def test_backward_workspace_is_linear_in_length(L):
     """The backward recomputes the scores: its workspace holds per-row operand copies only."""
     import block_scaled_fp4_amd as fp4
