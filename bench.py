@@ -315,8 +315,13 @@ def bench_quantizer(fp4, synth, torch, n):
     return dict(workload="bf16 [32768,128], 2% outlier channels x20, ScaleSearch f in [-2,6], per-tensor amax scale",
                 roofline={"bound": "alu", "achieved": round(alu_tops, 2), "peak": VALU_PEAK_TOPS,
                           "unit": "T lane-ops/s", "frac": round(alu_tops / VALU_PEAK_TOPS, 4),
-                          "note": "64x rows, algorithmic 45 lane-ops per element",
+                          "note": "64x rows; 45 lane-ops per element: for each of the 9 candidate scales, "
+                                  "the product with the reciprocal, the E2M1 rounding, the error (one fused "
+                                  "multiply-add with the exact dequantized value), its square and its add in "
+                                  "the sum tree; the SIMDs' VALU issue is saturated (one wave-instruction per "
+                                  "~4 clocks in the counters), so the HBM fractions below are what it reaches",
                           "hbm_frac_cold": round(cold_gbps / HBM_PEAK_GBS, 4),
+                          "hbm_frac_x64": round(big_algo / big_ms / 1e6 / HBM_PEAK_GBS, 4),
                           "traffic": read_traffic("quantizer_32768x128", "quantize.hip")},
                 algorithmic_bytes=algo,
                 cold_us=round(cold * 1e3, 2), cold_GBps=round(algo / cold / 1e6, 1),
