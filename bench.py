@@ -622,6 +622,17 @@ def pmc_mode(mode, fp4, synth, torch):
         for _ in range(3):
             fp4.fp4_quantize(x, 0, True, -2, 6, fp4.GLOBAL_AMAX, with_offsets=False)
         torch.cuda.synchronize()
+    elif mode == "quant64":
+        # the quantizer workload at 64x rows with a given per-tensor scale: the search kernel alone
+        x = synth.quant_tensor(rows=32768 * 64).cuda()
+        g = torch.full((1,), 0.01, dtype=torch.float32, device="cuda")
+        out = dict(codes=torch.empty((x.shape[0], 64), dtype=torch.uint8, device="cuda"),
+                   scales=torch.empty((x.shape[0], 8), dtype=torch.uint8, device="cuda"), offsets=None)
+        for _ in range(3):
+            fp4.fp4_quantize(x, 0, True, -2, 6, fp4.GLOBAL_GIVEN, g=g, out=out)
+        torch.cuda.synchronize()
+    elif mode == "train":
+        bench_train(fp4, synth, torch, 2)
     print(json.dumps({"pmc_mode": mode}))
 
 
@@ -632,7 +643,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
-    ap.add_argument("--pmc-mode", choices=["attn", "quant", "copy", "decode", "kvappend"], default=None)
+    ap.add_argument("--pmc-mode", choices=["attn", "quant", "quant64", "train", "copy", "decode", "kvappend"],
+                    default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
